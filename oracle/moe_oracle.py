@@ -1,0 +1,353 @@
+"""CPU reference (oracle) for one MoE layer forward: router -> top-K with
+renormalised softmax -> per-expert counts and offsets -> expert-grouped rows
+-> SwiGLU experts -> route-weighted combine.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  It shares no code with the GPU path
+and imports nothing from it.
+
+Written from the definitions on the pages, in plain numpy:
+  * float64 for every floating-point value it computes, except the router
+    logits, which are rounded to fp32 because the routing decision is defined
+    on fp32 logits (the GPU takes the same decision in fp32);
+  * no blocking, fusion or reordering beyond what the definition states.
+
+Pages cited (titles and sections):
+  [vllbc]  vllbc blog, "MoE inference and expert parallelism" -- routing /
+           expert-FFN / "fused MoE" section with Table 3-1, and the vLLM
+           forward-path section (topk -> align/sort -> GEMM1 -> act -> GEMM2
+           -> moe_sum).
+  [infra5] "推理 INFRA 方法论(5)" -- C(B), DeepGEMM (masked layout,
+           masked_m, pad waste) sections.
+  [eplb]   vLLM EPLB explainer -- section 1.2 (basic concepts: the three maps).
+  [moonep] "MoonEP: dynamic redundant experts" -- the routing-count identity
+           (sum_e T_e = RSK), the redundant-expert semantics (ids, weights and
+           combine positions unchanged), the online-plan data flow (counts ->
+           token offsets -> expert-grouped slots) and the zero-copy section.
+
+Readings taken where the pages leave a step open (each is listed in the
+design notes with its reason):
+  R1 ties in top-K go to the lower expert id; -0.0 equals +0.0; a NaN logit
+     ranks below every number (including -inf).
+  R2 slot order inside a token's K choices is descending logit.
+  R3 rows inside an expert group are in ascending token order (a stable
+     counting sort by expert).
+  R4 the shared expert has weight 1 and is added outside the top-K.
+  R5 SwiGLU = SiLU(x W1^T) * (x W3^T), then W2^T; weights are stored
+     [out, in] (W1, W3: [I, H]; W2: [H, I]).
+  R6 masked overflow is never dropped: rows past M_max go to a spill region.
+  R7 a replicated expert's tokens, in ascending token order, go round-robin
+     over its replicas in logical_to_physical order.
+  R8 an invalid replica entry (count < 1, or a slot outside [0, E_phys))
+     sends that expert's tokens to its home slot (= its logical id) and sets
+     status bit 1.
+
+Parity pins: see tests/test_oracle_pins.py (brute force, a third-party
+Mixtral MoE block, textbook sorts, page worked examples, closed forms).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+STATUS_SPILL = 1        # bit 0: masked overflow went to the spill region
+STATUS_BAD_REPLICA = 2  # bit 1: replica map entry invalid, home slot used
+STATUS_NONFINITE = 4    # bit 2: a logit was NaN or infinite
+
+
+# --------------------------------------------------------------------------
+# Number formats (decoders written from the format definitions)
+# --------------------------------------------------------------------------
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64.  A bf16 value is the upper
+    16 bits of the IEEE binary32 value with the same bits."""
+    b = np.asarray(bits).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+def decode_e4m3fn(q: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3FN bytes -> float64: 1 sign bit, 4 exponent bits (bias 7),
+    3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN;
+    there is no infinity."""
+    q = np.asarray(q).astype(np.int64)
+    sign = np.where(q & 0x80, -1.0, 1.0)
+    e = (q >> 3) & 0xF
+    m = (q & 0x7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    val = np.where((e == 15) & ((q & 7) == 7), np.nan, val)
+    return sign * val
+
+
+def dequant_block128(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """value[i, j] = e4m3(q[i, j]) * s[i // 128, j // 128], exact in float64
+    (a 4-bit by 24-bit significand product).  [infra5] DeepGEMM section:
+    128-wide blocks, each with one fp32 scale."""
+    v = decode_e4m3fn(q)
+    sf = np.asarray(s, dtype=np.float64)
+    return v * np.repeat(np.repeat(sf, 128, axis=0), 128, axis=1)
+
+
+# --------------------------------------------------------------------------
+# Router
+# --------------------------------------------------------------------------
+
+def router_logits(x: np.ndarray, w_router: np.ndarray, bias: np.ndarray | None) -> np.ndarray:
+    """logits[t, e] = sum_h x[t, h] * W_r[e, h] (+ bias[e]), returned as fp32.
+    [vllbc] routing section: the router gives one logit per expert per token.
+    The bias is added before selection and weighting (workload reading)."""
+    lg = np.asarray(x, np.float64) @ np.asarray(w_router, np.float64).T
+    if bias is not None:
+        lg = lg + np.asarray(bias, np.float64)[None, :]
+    return lg.astype(np.float32)
+
+
+def topk_route(logits: np.ndarray, K: int):
+    """Per token: the K largest fp32 logits (R1, R2) and their renormalised
+    softmax weights  w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0)  over the K
+    chosen logits (l_0 the largest).  This equals the softmax over all experts
+    renormalised over the K chosen ([vllbc] routing section and Table 3-1:
+    top-2 then softmax for Mixtral; softmax then renormalize in vLLM).
+
+    Returns ids [T, K] int32, weights [T, K] float64, status bits."""
+    lg = np.asarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    assert 1 <= K <= E
+    v = lg.astype(np.float64) + 0.0            # -0.0 + 0.0 == +0.0
+    nan = np.isnan(v)
+    v = np.where(nan, 0.0, v)
+    eid = np.broadcast_to(np.arange(E), (T, E))
+    # lexsort: last key is primary -> not-NaN first, then value descending,
+    # then id ascending
+    order = np.lexsort((eid, -v, nan.astype(np.int8)), axis=-1)
+    ids = order[:, :K].astype(np.int32)
+    sel = np.take_along_axis(v, order[:, :K], axis=1)
+    z = np.exp(sel - sel[:, :1])
+    w = z / z.sum(axis=1, keepdims=True)
+    status = STATUS_NONFINITE if (~np.isfinite(lg)).any() else 0
+    return ids, w, status
+
+
+# --------------------------------------------------------------------------
+# Replica maps  ([eplb] section 1.2; [moonep] redundant-expert semantics)
+# --------------------------------------------------------------------------
+
+def replica_tables(p2l: np.ndarray, E: int, max_replicas: int | None = None):
+    """physical_to_logical_map [E_phys] -> (logical_to_physical_map
+    [E, max_replicas] padded with -1, logical_replica_count [E]).  The
+    replicas of a logical expert are listed in ascending physical slot."""
+    p2l = np.asarray(p2l, dtype=np.int64)
+    count = np.zeros(E, dtype=np.int32)
+    for l in p2l:
+        count[l] += 1
+    R = int(count.max()) if max_replicas is None else max_replicas
+    l2p = np.full((E, R), -1, dtype=np.int32)
+    fill = np.zeros(E, dtype=np.int64)
+    for p, l in enumerate(p2l):
+        l2p[l, fill[l]] = p
+        fill[l] += 1
+    return l2p, count
+
+
+def assign_physical(ids: np.ndarray, E_phys: int, l2p: np.ndarray | None = None,
+                    count: np.ndarray | None = None):
+    """Physical slot of every (token, k) choice.  Without a map the slot is
+    the logical id.  With a map (R7): the tokens that chose logical expert l,
+    taken in ascending token order, are numbered j = 0, 1, ...; choice j goes
+    to l2p[l][j mod R_l].  Invalid entries follow R8."""
+    ids = np.asarray(ids)
+    T, K = ids.shape
+    if l2p is None:
+        return ids.astype(np.int32).copy(), 0
+    status = 0
+    phys = np.empty_like(ids, dtype=np.int32)
+    seen: dict[int, int] = {}
+    for t in range(T):
+        for k in range(K):
+            l = int(ids[t, k])
+            j = seen.get(l, 0)
+            seen[l] = j + 1
+            R = int(count[l])
+            p = int(l2p[l, j % R]) if R >= 1 else -1
+            if R < 1 or not (0 <= p < E_phys):
+                status |= STATUS_BAD_REPLICA
+                p = l
+            phys[t, k] = p
+    return phys, status
+
+
+# --------------------------------------------------------------------------
+# Counts, offsets and the expert-grouped order
+# --------------------------------------------------------------------------
+
+def group_rows(phys: np.ndarray, E_phys: int):
+    """counts T_p = #{(t, k): phys = p}; offsets = exclusive prefix sum
+    (E_phys + 1 entries, the cu_seqlens of [moonep] online plan);
+    src_of[row] = token of each row of the expert-grouped order, a stable sort
+    by slot (R3); row_of[t, k] = the row of choice (t, k).  [vllbc] vLLM
+    forward path: sort token/expert pairs by expert."""
+    T, K = phys.shape
+    flat = phys.reshape(-1).astype(np.int64)
+    counts = np.bincount(flat, minlength=E_phys).astype(np.int32)
+    offsets = np.zeros(E_phys + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    order = np.argsort(flat, kind="stable")
+    src_of = (order // K).astype(np.int32)
+    row_of = np.empty(T * K, dtype=np.int32)
+    row_of[order] = np.arange(T * K, dtype=np.int32)
+    return counts, offsets.astype(np.int32), row_of.reshape(T, K), src_of
+
+
+def layout_masked(counts, offsets, row_of, phys, M_max: int, E_phys: int):
+    """Static [E_phys, M_max] buffer with device-side valid counts masked_m
+    ([infra5] DeepGEMM section) and, under R6, a spill region after it.
+    rank = row_of - offsets[p]; slot = p*M_max + rank if rank < M_max, else
+    E_phys*M_max + spill_off[p] + rank - M_max."""
+    counts = np.asarray(counts, np.int64)
+    masked_m = np.minimum(counts, M_max)
+    spill_m = counts - masked_m
+    spill_off = np.zeros(E_phys + 1, dtype=np.int64)
+    spill_off[1:] = np.cumsum(spill_m)
+    rank = row_of - offsets[phys]
+    slot = np.where(rank < M_max, phys.astype(np.int64) * M_max + rank,
+                    E_phys * M_max + spill_off[phys] + rank - M_max)
+    status = STATUS_SPILL if spill_m.sum() > 0 else 0
+    return (masked_m.astype(np.int32), spill_off.astype(np.int32),
+            slot.astype(np.int32), status)
+
+
+def layout_contig(counts, offsets, row_of, phys, BM: int):
+    """Expert-grouped rows with each slot's segment padded to a multiple of BM
+    ([vllbc] forward path: block-aligned and padded).  pad_off = exclusive
+    prefix sum of ceil(T_p / BM) * BM; slot = pad_off[p] + rank."""
+    counts = np.asarray(counts, np.int64)
+    padded = (counts + BM - 1) // BM * BM
+    pad_off = np.zeros(len(counts) + 1, dtype=np.int64)
+    pad_off[1:] = np.cumsum(padded)
+    rank = row_of - offsets[phys]
+    slot = pad_off[phys] + rank
+    return pad_off.astype(np.int32), slot.astype(np.int32)
+
+
+# --------------------------------------------------------------------------
+# Experts and combine
+# --------------------------------------------------------------------------
+
+def silu(g: np.ndarray) -> np.ndarray:
+    return g / (1.0 + np.exp(-g))
+
+
+def swiglu_expert(X: np.ndarray, W1: np.ndarray, W3: np.ndarray, W2: np.ndarray) -> np.ndarray:
+    """(SiLU(X W1^T) * (X W3^T)) W2^T in float64 (R5; [vllbc] expert FFN:
+    W1/W3 are gate/up, W2 is down)."""
+    G = X @ W1.T
+    U = X @ W3.T
+    return (silu(G) * U) @ W2.T
+
+
+def moe_forward(x, w_router, bias, K, E_phys, expert_weights, shared_weights=None,
+                p2l=None, layout="contig", M_max=0, BM=16, logits=None,
+                tokens=None):
+    """The layer forward as defined: returns a dict with every intermediate.
+
+    x [T, H] (values exactly as the layer receives them); w_router [E, H];
+    expert_weights(p) -> (W1 [I,H], W3 [I,H], W2 [H,I]) float64 for physical
+    slot p; shared_weights the same triple or None.  ``logits`` (fp32), if
+    given, replaces the router step (routing parity is defined on the same
+    fp32 logits).  ``tokens`` restricts the FFN and combine to a sample of
+    token ids (routing still covers every token, as it must).
+
+    out[t] = S[t] + sum_k w[t, k] * Y[row_of[t, k]]   ([vllbc] combine:
+    weight by g_i then sum the K results; R4 for S)."""
+    x = np.asarray(x, dtype=np.float64)
+    T, H = x.shape
+    E = np.asarray(w_router).shape[0]
+    if logits is None:
+        logits = router_logits(x, w_router, bias)
+    ids, w, status = topk_route(logits, K)
+    l2p = count = None
+    if p2l is not None:
+        l2p, count = replica_tables(p2l, E)
+    phys, st = assign_physical(ids, E_phys, l2p, count)
+    status |= st
+    counts, offsets, row_of, src_of = group_rows(phys, E_phys)
+    res = dict(logits=logits, ids=ids, w=w, phys=phys, counts=counts,
+               offsets=offsets, row_of=row_of, src_of=src_of)
+    if layout == "masked":
+        masked_m, spill_off, slot_of, st = layout_masked(counts, offsets, row_of, phys, M_max, E_phys)
+        status |= st
+        res.update(masked_m=masked_m, spill_off=spill_off, slot_of=slot_of)
+    else:
+        pad_off, slot_of = layout_contig(counts, offsets, row_of, phys, BM)
+        res.update(pad_off=pad_off, slot_of=slot_of)
+    res["status"] = status
+
+    want = np.arange(T) if tokens is None else np.asarray(tokens)
+    need = np.zeros(T, dtype=bool)
+    need[want] = True
+    Y = np.zeros((T * K, H), dtype=np.float64)
+    for p in range(E_phys):
+        lo, hi = int(offsets[p]), int(offsets[p + 1])
+        if hi == lo:
+            continue
+        rows = np.arange(lo, hi)
+        rows = rows[need[src_of[lo:hi]]]
+        if rows.size == 0:
+            continue
+        W1, W3, W2 = expert_weights(p)
+        Y[rows] = swiglu_expert(x[src_of[rows]], W1, W3, W2)
+    out = np.zeros((len(want), H), dtype=np.float64)
+    if shared_weights is not None:
+        out += swiglu_expert(x[want], *shared_weights)
+    for k in range(K):
+        out += w[want, k][:, None] * Y[row_of[want, k]]
+    res["out"] = out
+    res["tokens"] = want
+    return res
+
+
+def bruteforce_forward(x, w_router, bias, K, expert_weights_logical, shared_weights=None,
+                       logits=None):
+    """Dense evaluation: every logical expert on every token, then a mask of
+    route weights (m[t, e] = w[t, k] where ids[t, k] = e, else 0):
+    out = S + sum_e m[:, e] * F_e(x).  Replicas do not appear: by the
+    redundant-expert semantics ([moonep]) they leave the function unchanged."""
+    x = np.asarray(x, dtype=np.float64)
+    T, H = x.shape
+    E = np.asarray(w_router).shape[0]
+    if logits is None:
+        logits = router_logits(x, w_router, bias)
+    ids, w, _ = topk_route(logits, K)
+    m = np.zeros((T, E))
+    for t in range(T):
+        for k in range(K):
+            m[t, ids[t, k]] = w[t, k]
+    out = np.zeros((T, H))
+    if shared_weights is not None:
+        out += swiglu_expert(x, *shared_weights)
+    for e in range(E):
+        out += m[:, e:e + 1] * swiglu_expert(x, *expert_weights_logical(e))
+    return out
+
+
+# --------------------------------------------------------------------------
+# Accounting ([infra5] C(B) and DeepGEMM sections)
+# --------------------------------------------------------------------------
+
+def coverage(B: int, K: int, E: int) -> float:
+    """C(B) = 1 - (1 - k/E)^B: expected fraction of experts a batch of B
+    tokens touches when each token picks k of E uniformly."""
+    return 1.0 - (1.0 - K / E) ** B
+
+
+def pad_waste(M_e: int, BM: int) -> float:
+    """FLOP waste of a tile-granular skip: ceil(M_e / BM) * BM / M_e."""
+    return -(-M_e // BM) * BM / M_e
+
+
+def expert_bytes(H: int, I: int, w_dtype: str) -> int:
+    """Bytes of one SwiGLU expert (3 matrices of H*I) with block-128 scales
+    for fp8."""
+    if w_dtype == "bf16":
+        return 3 * H * I * 2
+    return 3 * H * I + 3 * (H // 128) * (I // 128) * 4

@@ -1,0 +1,47 @@
+"""Adapters from the synthetic-input tensors (torch, CPU) to the numpy arrays
+the CPU reference takes.  Test infrastructure: decoding uses the reference's
+own bf16 / e4m3 decoders."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import moe_oracle as O
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return O.decode_bf16(t.contiguous().view(torch.int16).numpy().view(np.uint16))
+    if t.dtype == torch.float32:
+        return t.numpy().astype(np.float64)
+    raise TypeError(t.dtype)
+
+
+def expert_f64(ew, w_dtype: str):
+    if w_dtype == "bf16":
+        return to_f64(ew.w1), to_f64(ew.w3), to_f64(ew.w2)
+    return (O.dequant_block128(ew.w1.numpy(), ew.s1.numpy()),
+            O.dequant_block128(ew.w3.numpy(), ew.s3.numpy()),
+            O.dequant_block128(ew.w2.numpy(), ew.s2.numpy()))
+
+
+def oracle_forward(inp, logits=None, tokens=None, layout=None):
+    """Runs the reference on workload inputs ``inp`` (workloads.generate)."""
+    cfg = inp.cfg
+    cache = {}
+
+    def slot_weights(p):
+        l = inp.slot_logical(p)
+        if l not in cache:
+            if len(cache) > 2:
+                cache.pop(next(iter(cache)))
+            cache[l] = expert_f64(inp.expert(l), cfg.w_dtype)
+        return cache[l]
+
+    shared = expert_f64(inp.shared(), cfg.w_dtype) if cfg.n_shared else None
+    return O.moe_forward(
+        to_f64(inp.x), to_f64(inp.w_router),
+        None if inp.bias is None else inp.bias.numpy(),
+        cfg.K, cfg.E_phys, slot_weights, shared, p2l=inp.p2l,
+        layout=layout or cfg.layout, M_max=cfg.M_max, BM=cfg.BM,
+        logits=logits, tokens=tokens)

@@ -1,0 +1,393 @@
+"""Pins for the CPU reference: every check compares it with something other
+than itself -- textbook sorts, brute force, a third-party implementation of
+the Mixtral MoE block, closed forms, and values the pages print."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from workloads import configs, generate
+from oracle_adapt import oracle_forward, to_f64, expert_f64
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- formats
+
+def test_bf16_decoder_matches_torch():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 1 << 16, size=50000, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+    got = O.decode_bf16(bits)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+def test_e4m3_decoder_spec_values():
+    # values fixed by the OCP 8-bit floating point format (E4M3FN)
+    spec = {0x00: 0.0, 0x38: 1.0, 0x7E: 448.0, 0xFE: -448.0, 0x01: 2.0 ** -9,
+            0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x40: 2.0, 0x3C: 1.5, 0xB8: -1.0}
+    for code, val in spec.items():
+        assert O.decode_e4m3fn(np.array([code], np.uint8))[0] == val, hex(code)
+    assert np.isnan(O.decode_e4m3fn(np.array([0x7F, 0xFF], np.uint8))).all()
+    assert np.signbit(O.decode_e4m3fn(np.array([0x80], np.uint8))[0])
+
+
+def test_e4m3_decoder_matches_torch_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = O.decode_e4m3fn(codes)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all()
+
+
+def test_block_dequant_against_loop():
+    rng = np.random.default_rng(2)
+    q = rng.integers(0, 256, size=(256, 384), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x11      # no NaN codes
+    s = rng.uniform(0.5, 2.0, size=(2, 3)).astype(np.float32)
+    got = O.dequant_block128(q, s)
+    for i in (0, 127, 128, 255):
+        for j in (0, 129, 300, 383):
+            assert got[i, j] == O.decode_e4m3fn(q[i:i + 1, j])[0] * float(s[i // 128, j // 128])
+
+
+def test_synthetic_fp8_roundtrip_is_close():
+    w = torch.randn(256, 256, generator=torch.Generator().manual_seed(0)) * 0.02
+    q, s = generate.quantize_e4m3_block128(w)
+    back = O.dequant_block128(q.numpy(), s.numpy())
+    # e4m3 has 3 mantissa bits: relative rounding error <= 2^-4 on normals
+    err = np.abs(back - w.double().numpy())
+    assert err.max() <= 2 ** -4 * np.abs(w.double().numpy()).max() + 1e-12
+
+
+# ---------------------------------------------------------------- top-K
+
+def _topk_textbook(row, K):
+    """Python's sorted() on (-value, id), NaN last: the definition of R1/R2."""
+    items = []
+    for e, v in enumerate(row):
+        v = float(v)
+        items.append(((1 if math.isnan(v) else 0), 0.0 if math.isnan(v) else -(v + 0.0), e))
+    return [e for _, _, e in sorted(items)[:K]]
+
+
+@pytest.mark.parametrize("E,K", [(8, 2), (8, 8), (16, 5), (64, 8), (33, 1)])
+def test_topk_ids_match_textbook_sort_with_ties(E, K):
+    rng = np.random.default_rng(E * 100 + K)
+    for trial in range(40):
+        # integer-valued logits force many exact ties
+        lg = rng.integers(-3, 4, size=(7, E)).astype(np.float32)
+        if trial % 2:
+            lg = rng.standard_normal((7, E)).astype(np.float32)
+        ids, w, _ = O.topk_route(lg, K)
+        for t in range(lg.shape[0]):
+            assert list(ids[t]) == _topk_textbook(lg[t], K)
+
+
+def test_topk_signed_zero_and_nan():
+    lg = np.array([[-0.0, 0.0, -1.0, np.nan, -np.inf, 0.0]], np.float32)
+    ids, _, st = O.topk_route(lg, 6)
+    assert list(ids[0]) == [0, 1, 5, 2, 4, 3]
+    assert st & O.STATUS_NONFINITE
+
+
+def test_topk_all_equal_and_full():
+    lg = np.full((3, 8), 0.25, np.float32)
+    ids, w, _ = O.topk_route(lg, 3)
+    assert (ids == np.arange(3)).all() and (w == 1.0 / 3).all()
+    lg = np.random.default_rng(3).standard_normal((5, 8)).astype(np.float32)
+    ids, _, _ = O.topk_route(lg, 8)
+    assert (ids == np.argsort(-lg, axis=1, kind="stable")).all()
+
+
+def test_topk_weights_closed_forms():
+    rng = np.random.default_rng(4)
+    lg = rng.standard_normal((50, 16)).astype(np.float32)
+    ids1, w1, _ = O.topk_route(lg, 1)
+    assert (w1 == 1.0).all()
+    ids2, w2, _ = O.topk_route(lg, 2)
+    l0 = np.take_along_axis(lg, ids2[:, :1], 1)[:, 0].astype(np.float64)
+    l1 = np.take_along_axis(lg, ids2[:, 1:], 1)[:, 0].astype(np.float64)
+    assert np.allclose(w2[:, 0], 1.0 / (1.0 + np.exp(l1 - l0)), rtol=0, atol=1e-15)
+    _, w8, _ = O.topk_route(lg, 8)
+    assert np.allclose(w8.sum(1), 1.0, atol=1e-14)
+    assert (np.diff(w8, axis=1) <= 0).all()
+
+
+def test_topk_weights_equal_full_softmax_renormalised():
+    """Mixtral's top-K-then-softmax equals vLLM's softmax-then-renormalize."""
+    rng = np.random.default_rng(5)
+    lg = (rng.standard_normal((30, 12)) * 3).astype(np.float32)
+    ids, w, _ = O.topk_route(lg, 4)
+    p = torch.softmax(torch.from_numpy(lg).double(), dim=1).numpy()
+    sel = np.take_along_axis(p, ids, 1)
+    assert np.allclose(w, sel / sel.sum(1, keepdims=True), rtol=1e-13, atol=0)
+
+
+# ---------------------------------------------------------------- grouping
+
+def _phys_random(T, K, E, seed):
+    rng = np.random.default_rng(seed)
+    return np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+
+
+def test_counts_offsets_src_row_against_textbook():
+    T, K, E = 37, 3, 11
+    phys = _phys_random(T, K, E, 6)
+    counts, offsets, row_of, src_of = O.group_rows(phys, E)
+    assert counts.sum() == T * K                                  # sum_e T_e = B*K
+    assert (counts == np.bincount(phys.ravel(), minlength=E)).all()
+    assert offsets[0] == 0 and (np.diff(offsets) == counts).all()
+    pairs = sorted((int(phys[t, k]), t, k) for t in range(T) for k in range(K))
+    assert list(src_of) == [t for _, t, _ in pairs]
+    for r, (_, t, k) in enumerate(pairs):
+        assert row_of[t, k] == r
+    # permute then unpermute is the identity
+    x = np.random.default_rng(7).standard_normal((T, 5))
+    xg = x[src_of]
+    for k in range(K):
+        assert (xg[row_of[:, k]] == x).all()
+
+
+def test_masked_layout_tables():
+    T, K, E, M_max = 40, 4, 6, 5
+    phys = _phys_random(T, K, E, 8)
+    counts, offsets, row_of, _ = O.group_rows(phys, E)
+    masked_m, spill_off, slot, st = O.layout_masked(counts, offsets, row_of, phys, M_max, E)
+    assert (masked_m == np.minimum(counts, M_max)).all()
+    assert spill_off[-1] == np.maximum(counts - M_max, 0).sum()
+    assert st == (O.STATUS_SPILL if spill_off[-1] else 0)
+    # slots are distinct, inside the static buffer + spill region, and each
+    # masked slot lies inside its expert's valid rows
+    assert len(set(slot.ravel().tolist())) == T * K
+    cap = E * M_max + K * max(0, T - M_max)
+    assert slot.min() >= 0 and slot.max() < cap
+    for t in range(T):
+        for k in range(K):
+            p, s = phys[t, k], slot[t, k]
+            if s < E * M_max:
+                assert s // M_max == p and s % M_max < masked_m[p]
+            else:
+                assert spill_off[p] <= s - E * M_max < spill_off[p + 1]
+
+
+def test_contig_layout_tables():
+    T, K, E, BM = 33, 2, 7, 8
+    phys = _phys_random(T, K, E, 9)
+    counts, offsets, row_of, _ = O.group_rows(phys, E)
+    pad_off, slot = O.layout_contig(counts, offsets, row_of, phys, BM)
+    assert (pad_off % BM == 0).all() and (np.diff(pad_off) >= counts).all()
+    assert (np.diff(pad_off) < counts + BM).all()
+    for t in range(T):
+        for k in range(K):
+            p = phys[t, k]
+            assert pad_off[p] <= slot[t, k] < pad_off[p] + counts[p]
+
+
+# ---------------------------------------------------------------- replicas
+
+def test_replica_tables_page_example():
+    g = _gold("replica_map_eplb.json")
+    l2p, count = O.replica_tables(np.array(g["physical_to_logical_map"]), 4)
+    assert l2p.tolist() == g["logical_to_physical_map"]
+    assert count.tolist() == g["logical_replica_count"]
+
+
+def test_replica_round_robin_split():
+    T, K, E = 50, 3, 6
+    p2l = np.array([0, 1, 2, 3, 4, 5, 0, 0, 2], np.int32)
+    l2p, count = O.replica_tables(p2l, E)
+    ids = _phys_random(T, K, E, 10)
+    phys, st = O.assign_physical(ids, len(p2l), l2p, count)
+    assert st == 0
+    assert (p2l[phys] == ids).all()                         # ids unchanged
+    pc = np.bincount(phys.ravel(), minlength=len(p2l))
+    lc = np.bincount(ids.ravel(), minlength=E)
+    for l in range(E):
+        reps = l2p[l, :count[l]]
+        assert pc[reps].sum() == lc[l]                      # counts conserved
+        assert pc[reps].max() - pc[reps].min() <= 1         # even split
+        # round robin over ascending tokens
+        toks = [t for t in range(T) for k in range(K) if ids[t, k] == l]
+        got = [phys[t, list(ids[t]).index(l)] for t in toks]
+        assert got == [reps[j % count[l]] for j in range(len(toks))]
+
+
+def test_replica_invalid_entry_falls_back_home():
+    ids = np.array([[0, 1], [1, 0]], np.int32)
+    l2p = np.array([[0, 9], [1, -1]], np.int32)
+    count = np.array([2, 0], np.int32)
+    phys, st = O.assign_physical(ids, 3, l2p, count)
+    assert st & O.STATUS_BAD_REPLICA
+    assert phys.tolist() == [[0, 1], [1, 0]]
+
+
+# ---------------------------------------------------------------- FFN + combine
+
+def _tiny_inputs(**kw):
+    cfg = configs.tiny().with_(**kw)
+    return generate.make_inputs(cfg)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(K=1), dict(K=8), dict(E=5, E_phys=5, K=3, T=9),
+                                dict(n_shared=1), dict(layout="contig", BM=4)])
+def test_oracle_matches_bruteforce(kw):
+    inp = _tiny_inputs(**kw)
+    cfg = inp.cfg
+    res = oracle_forward(inp)
+    ew = lambda l: expert_f64(inp.expert(l), cfg.w_dtype)
+    sh = expert_f64(inp.shared(), cfg.w_dtype) if cfg.n_shared else None
+    bf = O.bruteforce_forward(to_f64(inp.x), to_f64(inp.w_router), None, cfg.K, ew, sh)
+    assert np.allclose(res["out"], bf, rtol=1e-12, atol=1e-12)
+
+
+def test_oracle_matches_transformers_mixtral_block():
+    """Third-party pin: Hugging Face's Mixtral sparse-MoE block (router
+    softmax -> top-k -> renormalise, SiLU(gate) * up -> down, weighted sum),
+    run in float64 on the same weights."""
+    from transformers import MixtralConfig
+    from transformers.models.mixtral.modeling_mixtral import MixtralSparseMoeBlock
+    inp = _tiny_inputs()
+    cfg = inp.cfg
+    hf = MixtralConfig(hidden_size=cfg.H, intermediate_size=cfg.I, num_local_experts=cfg.E,
+                       num_experts_per_tok=cfg.K, hidden_act="silu")
+    blk = MixtralSparseMoeBlock(hf).double().eval()
+    with torch.no_grad():
+        blk.gate.weight.copy_(torch.from_numpy(to_f64(inp.w_router)))
+        for e in range(cfg.E):
+            W1, W3, W2 = expert_f64(inp.expert(e), cfg.w_dtype)
+            blk.experts.gate_up_proj[e].copy_(torch.from_numpy(np.concatenate([W1, W3], 0)))
+            blk.experts.down_proj[e].copy_(torch.from_numpy(W2))
+        _, _, hf_ids = blk.gate(torch.from_numpy(to_f64(inp.x)))
+        ref = blk(torch.from_numpy(to_f64(inp.x))[None])[0].numpy()
+    res = oracle_forward(inp)
+    assert (np.sort(res["ids"], 1) == np.sort(hf_ids.numpy(), 1)).all()
+    # the HF router takes its softmax in fp32: agreement to fp32 rounding
+    assert np.abs(res["out"] - ref).max() <= 1e-6 * np.abs(ref).max()
+
+
+def test_single_expert_reduces_to_dense_swiglu_and_shared_matches_mlp():
+    """E=1, K=1: the layer is one dense SwiGLU FFN (torch linear + silu).
+    The shared expert equals Hugging Face's DeepseekV3MLP on its weights."""
+    inp = _tiny_inputs(E=1, E_phys=1, K=1)
+    W1, W3, W2 = expert_f64(inp.expert(0), "bf16")
+    x = torch.from_numpy(to_f64(inp.x))
+    F = torch.nn.functional
+    dense = F.linear(F.silu(F.linear(x, torch.from_numpy(W1))) * F.linear(x, torch.from_numpy(W3)),
+                     torch.from_numpy(W2)).numpy()
+    assert np.allclose(oracle_forward(inp)["out"], dense, rtol=1e-12, atol=1e-13)
+
+    from transformers import DeepseekV3Config
+    from transformers.models.deepseek_v3.modeling_deepseek_v3 import DeepseekV3MLP
+    inp = _tiny_inputs(n_shared=1)
+    S1, S3, S2 = expert_f64(inp.shared(), "bf16")
+    mlp = DeepseekV3MLP(DeepseekV3Config(hidden_size=inp.cfg.H, intermediate_size=inp.cfg.I,
+                                         hidden_act="silu")).double()
+    with torch.no_grad():
+        mlp.gate_proj.weight.copy_(torch.from_numpy(S1))
+        mlp.up_proj.weight.copy_(torch.from_numpy(S3))
+        mlp.down_proj.weight.copy_(torch.from_numpy(S2))
+        shared_ref = mlp(torch.from_numpy(to_f64(inp.x))).numpy()
+    with_sh = oracle_forward(inp)["out"]
+    without = oracle_forward(generate.make_inputs(inp.cfg.with_(n_shared=0)))["out"]
+    assert np.allclose(with_sh - without, shared_ref, rtol=1e-10, atol=1e-12)
+
+
+def test_replica_map_leaves_output_unchanged():
+    """Redundant-expert semantics: ids, weights and combine positions are
+    unchanged, so the output must not change."""
+    base = configs.tiny().with_(E=6, E_phys=6, K=2, T=24, layout="contig")
+    rep = base.with_(E_phys=9)
+    a = generate.make_inputs(base)
+    b = generate.make_inputs(rep)
+    b.p2l = np.array([0, 1, 2, 3, 4, 5, 2, 2, 0], np.int32)
+    ra, rb = oracle_forward(a), oracle_forward(b)
+    assert (ra["ids"] == rb["ids"]).all() and (ra["w"] == rb["w"]).all()
+    assert np.allclose(ra["out"], rb["out"], rtol=1e-13, atol=1e-14)
+    assert rb["counts"][[2, 6, 7]].sum() == ra["counts"][2]
+
+
+def test_layouts_agree():
+    inp = _tiny_inputs(T=16, M_max=3)        # forces spill
+    rm = oracle_forward(inp, layout="masked")
+    rc = oracle_forward(inp, layout="contig")
+    assert rm["status"] & O.STATUS_SPILL
+    assert np.array_equal(rm["out"], rc["out"])
+
+
+def test_token_sample_matches_full_run():
+    inp = _tiny_inputs(n_shared=1)
+    full = oracle_forward(inp)
+    part = oracle_forward(inp, tokens=[3, 0, 15])
+    assert np.allclose(part["out"], full["out"][[3, 0, 15]], rtol=1e-13, atol=1e-14)
+
+
+def test_fp8_weights_path():
+    inp = _tiny_inputs(w_dtype="fp8", H=256, I=256)
+    cfg = inp.cfg
+    res = oracle_forward(inp)
+    ew = lambda l: expert_f64(inp.expert(l), "fp8")
+    bf = O.bruteforce_forward(to_f64(inp.x), to_f64(inp.w_router), None, cfg.K, ew)
+    assert np.allclose(res["out"], bf, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- accounting
+
+def test_accounting_pins_from_pages():
+    g = _gold("accounting_pins.json")
+    a = g["expert_bytes_fp8_dsv3_x8"]
+    w_only = 3 * a["H"] * a["I"] * a["bytes_per_weight"] * a["n_experts"]
+    assert round(w_only / 1e6) == a["total_mb_decimal"]
+    for lat, tbs in zip(g["triton_bm_sweep"]["latency_us"], g["triton_bm_sweep"]["tb_per_s"]):
+        assert round(w_only / (lat * 1e-6) / 1e12, 1) == tbs
+    pw = g["pad_waste"]
+    for c in pw["cases"]:
+        assert O.pad_waste(pw["M_e"], c["BM"]) == pytest.approx(c["waste"])
+    m = g["mixtral_expert_params"]
+    assert O.expert_bytes(m["H"], m["I"], "bf16") // 2 * m["E"] * m["n_layers"] == m["total"]
+    act = g["mixtral_active_params"]
+    active = 2 * 4096 * 14336 * 3 * 32 + act["replicated"]
+    assert round(active / 1e9, 2) == act["active_billions_2dp"]
+
+
+def test_coverage_closed_form():
+    # C(B) limits and a direct count over all k-subsets for a tiny case:
+    # probability that a given expert is untouched by B tokens choosing
+    # uniform k-subsets of E is ((E-k)/E)^B.
+    assert O.coverage(0, 2, 8) == 0.0
+    assert O.coverage(10 ** 6, 8, 256) == pytest.approx(1.0)
+    E, k, B = 5, 2, 3
+    subsets = list(itertools.combinations(range(E), k))
+    miss = sum(1 for ch in itertools.product(subsets, repeat=B) if all(0 not in s for s in ch))
+    assert miss / len(subsets) ** B == pytest.approx(1 - O.coverage(B, k, E))
+
+
+@pytest.mark.parametrize("cfgf,B", [(configs.mixtral_decode, 8), (configs.dsv3_decode, 32),
+                                    (configs.dsv3_decode, 128)])
+def test_distinct_experts_track_coverage(cfgf, B):
+    """The synthetic router is close to uniform, so the number of distinct
+    experts a batch touches should sit near E*C(B).  Each seed redraws x and
+    W_r; a non-uniform router would sit below E*C(B)."""
+    counts = []
+    for seed in range(24):
+        cfg = cfgf(B).with_(seed=seed)
+        inp = generate.make_inputs(cfg)
+        lg = O.router_logits(to_f64(inp.x), to_f64(inp.w_router), None)
+        ids, _, _ = O.topk_route(lg, cfg.K)
+        counts.append(len(np.unique(ids)))
+    exp = cfg.E * O.coverage(B, cfg.K, cfg.E)
+    mean = float(np.mean(counts))
+    se = float(np.std(counts, ddof=1) / np.sqrt(len(counts))) if np.std(counts) > 0 else 0.0
+    assert mean <= exp + 3 * se + 1e-9
+    assert mean >= exp * 0.97 - 3 * se
