@@ -1,0 +1,234 @@
+"""Benchmark of the single-GPU MoE layer forward on MI355X.
+
+One step = one pass of the whole layer over one batch: router logits ->
+route (top-K, counts, offsets, grouped order) -> permute -> expert gate/up
+(+SwiGLU) -> expert down -> combine, all HIP kernels through the C ABI, on
+one stream, with inputs and weights already resident in HBM.
+
+Default workload: the Mixtral-8x7B-shaped decode layer (E=8, K=2, H=4096,
+I=14336, bf16) at B=64 tokens; the other batch sizes of that workload are
+timed too and reported under "batches".  ``--workload`` picks another one.
+
+Metric: decode MoE-layer latency (us), lower is better, with the expert-weight
+HBM bandwidth it implies: touched weight bytes (slots with >= 1 token, plus
+the shared expert and the router) / latency.  The roofline object is for the
+dominant kernel (expert gate/up): algorithmic bytes per launch (W1 + W3 of
+every touched slot) / its mean duration, measured with HIP events on the
+launch stream over the timed region.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixtral_decode_b64")
+    ap.add_argument("--no-sweep", action="store_true", help="time only the named workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU reference timing")
+    return ap.parse_args()
+
+
+def weight_bytes_per_slot(cfg):
+    """Bytes of one SwiGLU expert: 3 matrices of H x I, plus one fp32 scale
+    per 128x128 block for fp8."""
+    if cfg.w_dtype == "bf16":
+        return 3 * cfg.H * cfg.I * 2
+    return 3 * cfg.H * cfg.I + 3 * (cfg.H // 128) * (cfg.I // 128) * 4
+
+
+class Setup:
+    def __init__(self, cfg):
+        import torch
+        from routing_grouped_expert_router_amd import binding as B
+        from workloads import generate
+        self.cfg = cfg
+        self.inp = generate.make_inputs(cfg, wdevice="cuda")
+        self.w = generate.upload_weights(self.inp, "cuda")
+        l2p = rc = None
+        max_rep = 1
+        if self.inp.p2l is not None:
+            import numpy as np
+            counts = np.bincount(self.inp.p2l, minlength=cfg.E)
+            max_rep = int(counts.max())
+            l2p_t, rc_t = B.moe_replica_map_from_p2l(self.inp.p2l, cfg.E, max_rep)
+            l2p, rc = l2p_t.cuda(), rc_t.cuda()
+        self.d = B.Desc.from_config(cfg, max_replicas=max_rep)
+        self.x = self.inp.x.cuda()
+        self.wr = self.inp.w_router.cuda()
+        self.bias = None if self.inp.bias is None else self.inp.bias.cuda()
+        self.layer = B.MoELayer(self.d, self.w, self.wr, self.bias, l2p, rc, "cuda")
+        self.B = B
+        torch.cuda.synchronize()
+
+    def step(self, ev=None):
+        B, L, d, T = self.B, self.layer, self.d, self.cfg.T
+        B.moe_router_logits(d, self.x, self.wr, self.bias, T, L.logits)
+        B.moe_route(d, L.logits, T, L.rt, L.ws, L.l2p, L.rcount)
+        B.moe_permute(d, self.x, T, L.rt, L.xg)
+        if ev is not None:
+            ev[0].record()
+        B.moe_expert_gate_up(d, L.weights, L.rt, T, L.xg, L.h)
+        if ev is not None:
+            ev[1].record()
+        B.moe_expert_down(d, L.weights, L.rt, T, L.h, L.y)
+        B.moe_combine(d, L.rt, T, L.y, L.out)
+
+    def touched(self):
+        """(touched slots, touched routed-weight bytes, gate/up bytes, all bytes)"""
+        import numpy as np
+        cfg = self.cfg
+        counts = self.layer.rt.counts.cpu().numpy()
+        slots = int((counts > 0).sum())
+        per = weight_bytes_per_slot(cfg)
+        bpp = 2 if cfg.w_dtype == "bf16" else 1
+        scale_gu = 0 if cfg.w_dtype == "bf16" else 2 * (cfg.I // 128) * (cfg.H // 128) * 4
+        gu = (slots + cfg.n_shared) * (2 * cfg.I * cfg.H * bpp + scale_gu)
+        routed = slots * per
+        total = routed + cfg.n_shared * per + cfg.E * cfg.H * 2
+        return slots, routed, gu, total
+
+
+def time_workload(cfg, steps, warmup):
+    import torch
+    s = Setup(cfg)
+    for _ in range(warmup):
+        s.step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        s.step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / steps
+    gu_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    slots, routed, gu_bytes, total = s.touched()
+    status = int(s.layer.rt.status.item())
+    res = dict(cfg=cfg, ms=ms, gu_ms=gu_ms, wall=wall, slots=slots, routed_bytes=routed,
+               gu_bytes=gu_bytes, total_bytes=total, status=status, setup=s)
+    return res
+
+
+def cpu_baseline(s, budget_s=30.0):
+    """The CPU reference, as it stands, on a bounded sample of the workload:
+    all routing for the whole batch plus the expert FFN and combine for a
+    sample of tokens.  Returns (us per full layer call, sample description)."""
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle import moe_oracle as O
+    from oracle_adapt import oracle_forward
+    cfg = s.cfg
+    inp = s.inp
+    # copy every expert the batch touches to host memory first (not timed)
+    counts = s.layer.rt.counts.cpu().numpy()
+    inp.prefetch(sorted({inp.slot_logical(p) for p in np.nonzero(counts)[0]}))
+    T = cfg.T
+    for n in (T, max(1, T // 4), max(1, T // 16), 1):
+        toks = np.arange(0, T, max(1, T // n))[:n]
+        t0 = time.perf_counter()
+        oracle_forward(inp, tokens=toks)
+        dt = time.perf_counter() - t0
+        if dt <= budget_s or n == 1:
+            break
+    # scale: routing is over the full batch; the FFN part is per token
+    frac = len(toks) / T
+    est = dt / frac if frac > 0 else dt
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    return est * 1e6, f"{len(toks)} of {T} tokens (routing over all {T}); fp64 numpy; " \
+                      f"measured {dt:.1f} s, scaled by tokens", cores
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the MoE layer here runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from workloads import configs
+    cfg = configs.by_name(args.workload)
+    names = [cfg.name]
+    if not args.no_sweep and cfg.name.startswith("mixtral_decode_b"):
+        names = [f"mixtral_decode_b{b}" for b in (1, 8, 32, 64)]
+    results = {}
+    for n in names:
+        c = configs.by_name(n)
+        r = time_workload(c, args.steps, args.warmup)
+        results[n] = r
+        print(f"# {n}: {r['ms']*1e3:.1f} us/layer, gate/up {r['gu_ms']*1e3:.1f} us, "
+              f"slots {r['slots']}, touched {r['total_bytes']/1e9:.3f} GB -> "
+              f"{r['total_bytes']/(r['ms']*1e-3)/1e9:.0f} GB/s, status {r['status']}",
+              file=sys.stderr, flush=True)
+        if n != cfg.name:
+            del r["setup"]
+            torch.cuda.empty_cache()
+    head = results[cfg.name]
+    lat_us = head["ms"] * 1e3
+    gb_s = head["total_bytes"] / (head["ms"] * 1e-3) / 1e9
+    gu_gbs = head["gu_bytes"] / (head["gu_ms"] * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu:
+        us, sample, cores = cpu_baseline(head["setup"])
+        cpu = {"value": round(us, 1), "unit": "us", "cores": cores, "kind": "oracle",
+               "sample": sample}
+    out = {
+        "metric": "decode MoE-layer latency (us) + expert-weight HBM GB/s; prefill TFLOP/s",
+        "value": round(lat_us, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms"], 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.w_dtype == "bf16" else "fp8-e4m3-b128 weights, bf16 activations",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
+                   "E_phys": cfg.E_phys, "K": cfg.K, "n_shared": cfg.n_shared,
+                   "layout": cfg.layout, "M_max": cfg.M_max, "w_dtype": cfg.w_dtype},
+        "expert_weight_hbm_gbs": round(gb_s, 1),
+        "touched_slots": head["slots"],
+        "touched_bytes": head["total_bytes"],
+        "roofline": {"bound": "hbm", "kernel": "ffn_stream gate/up (W1+W3, SwiGLU)",
+                     "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel_us": round(head["gu_ms"] * 1e3, 2),
+                     "algorithmic_bytes": head["gu_bytes"]},
+        "cpu_baseline": cpu,
+        "batches": {n: {"latency_us": round(r["ms"] * 1e3, 2),
+                        "gbs": round(r["total_bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
+                        "gate_up_us": round(r["gu_ms"] * 1e3, 2),
+                        "touched_slots": r["slots"]} for n, r in results.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

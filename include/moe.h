@@ -1,0 +1,243 @@
+/*
+ * moe.h -- C ABI of a single-GPU fused MoE layer forward for MI355X (gfx950).
+ *
+ * The layer, as the pages define it:
+ *   router logits -> top-K experts per token with renormalised softmax
+ *   weights -> per-expert token counts T_e and prefix-sum offsets ->
+ *   tokens permuted into expert-grouped rows -> grouped SwiGLU expert GEMMs
+ *   (gate W1 / up W3, SiLU(gate)*up, down W2) -> route-weighted combine back
+ *   into token order, plus an always-on shared expert of weight 1.
+ * Sources: vllbc blog "MoE inference and expert parallelism" (routing and
+ * expert-FFN section, Table 3-1; vLLM forward-path section), "推理 INFRA
+ * 方法论(5)" (DeepGEMM section: static [E_loc, M_max, K] buffer with a
+ * device-side masked_m), vLLM EPLB explainer section 1.2 (the three replica
+ * maps), "MoonEP" (online-plan data flow; zero-copy lifetime).
+ *
+ * Conventions for every call below:
+ *   - Memory: every pointer argument is caller-owned.  Arguments documented
+ *     as "device" are device memory on the current HIP device; "host" are
+ *     host memory.  The library never allocates, frees or synchronises.
+ *   - Launches: calls only enqueue kernels on `stream`.  Grids depend on
+ *     (desc, T) only, never on device-side counts, so a call sequence can be
+ *     captured in a HIP graph.  No call records a memset.
+ *   - Errors: argument errors are detected on the host before anything is
+ *     enqueued and returned as MOE_ERR_ARG / MOE_ERR_UNSUPPORTED.  A failed
+ *     kernel launch returns MOE_ERR_HIP.  Data-dependent conditions never
+ *     trap: moe_route writes a status word (MOE_STATUS_* bits) that the
+ *     caller may read after synchronising.
+ *   - Validity: outputs stay valid until the next call writing the same
+ *     buffers.  Rows of the grouped buffers (xg, h, y) that hold no token --
+ *     masked rows past masked_m[p], contiguous pad rows -- are undefined and
+ *     are never read into `out` (MoonEP zero-copy section: padding and the
+ *     undefined tail are described by the plan).
+ *   - Determinism: identical inputs give bit-identical outputs; no result
+ *     depends on the order of atomic operations.
+ *   - Thread safety: the library keeps no state; concurrent calls on
+ *     distinct buffers are safe.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = 1,          /* NULL required pointer, bad size, T > T_max ... */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. H % 128 != 0) */
+  MOE_ERR_WORKSPACE = 3,    /* workspace smaller than moe_route_workspace_bytes */
+  MOE_ERR_HIP = 4           /* a HIP launch failed */
+} moe_status_t;
+
+typedef enum {
+  MOE_F32 = 0,              /* IEEE binary32 */
+  MOE_BF16 = 1,             /* bfloat16 */
+  MOE_FP8E4M3_B128 = 2      /* OCP E4M3FN bytes + one fp32 scale per 128x128
+                               block (DeepGEMM section: block-128 fp8) */
+} moe_dtype_t;
+
+typedef enum {
+  MOE_CONTIG = 0,           /* expert-grouped rows, each segment padded to BM */
+  MOE_MASKED = 1            /* static [E_phys, M_max] rows + spill region */
+} moe_layout_t;
+
+/* Bits of the device status word written by moe_route. */
+#define MOE_STATUS_SPILL       1u  /* some T_p > M_max: rows went to the spill
+                                      region (result still exact, no drop) */
+#define MOE_STATUS_BAD_REPLICA 2u  /* replica map invalid (count outside
+                                      [1, max_replicas], slot outside
+                                      [0, E_phys), or a slot listed twice):
+                                      the whole map is ignored and expert l
+                                      uses slot l */
+#define MOE_STATUS_NONFINITE   4u  /* a logit was NaN or +-inf; NaN ranks
+                                      below every number, output unspecified */
+#define MOE_STATUS_INTERNAL    8u  /* an index fell outside its buffer and the
+                                      access was skipped (never expected) */
+
+/* Layer description (host struct, copied by value into every call). */
+typedef struct {
+  int32_t T_max;        /* largest token count any call will pass */
+  int32_t H;            /* hidden size; multiple of 128 */
+  int32_t I;            /* expert intermediate size; multiple of 128 */
+  int32_t E;            /* logical routed experts, 1..4096 */
+  int32_t E_phys;       /* physical slots (>= E; == E without replicas) */
+  int32_t K;            /* experts per token, 1..min(E, 16) */
+  int32_t n_shared;     /* 0 or 1 always-on shared expert */
+  int32_t max_replicas; /* columns of logical_to_physical_map (>= 1) */
+  int32_t act_dtype;    /* moe_dtype_t of x and out: MOE_F32 or MOE_BF16 */
+  int32_t w_dtype;      /* moe_dtype_t of expert weights: MOE_BF16 or
+                           MOE_FP8E4M3_B128 (router weights are always bf16) */
+  int32_t layout;       /* moe_layout_t */
+  int32_t M_max;        /* masked rows per slot, >= 1 (MOE_MASKED) */
+  int32_t BM;           /* segment padding, >= 1 (MOE_CONTIG) */
+} moe_desc_t;
+
+/* Routing tables, all device int32/float/uint32 arrays, caller-allocated.
+ * Sizes: TK = T_max*K.  Choice i = t*K + k (k-th choice of token t). */
+typedef struct {
+  int32_t* topk_ids;   /* [TK] logical expert of choice i; per token in
+                          descending logit order, ties to the lower id */
+  float*   topk_w;     /* [TK] w = exp(l_k - l_0) / sum_j exp(l_j - l_0) */
+  int32_t* topk_phys;  /* [TK] physical slot of choice i */
+  int32_t* row_of;     /* [TK] row of choice i in the unpadded grouped order */
+  int32_t* slot_of;    /* [TK] row of choice i in the layout's buffer */
+  int32_t* src_of;     /* [TK] token of each unpadded grouped row */
+  int32_t* counts;     /* [E_phys] T_p, tokens per physical slot */
+  int32_t* offsets;    /* [E_phys+1] exclusive prefix sum of counts */
+  int32_t* masked_m;   /* [E_phys] min(T_p, M_max)   (MOE_MASKED; else NULL ok) */
+  int32_t* spill_off;  /* [E_phys+1] prefix sum of T_p - masked_m (MOE_MASKED) */
+  int32_t* pad_off;    /* [E_phys+1] prefix sum of ceil(T_p/BM)*BM (MOE_CONTIG) */
+  uint32_t* status;    /* [1] MOE_STATUS_* bits of the last moe_route */
+} moe_route_t;
+
+/* Expert weights, device memory, layout [out, in] (row = output feature):
+ *   w1, w3: [E_phys, I, H]   (gate, up)     w2: [E_phys, H, I]   (down)
+ *   bf16, or E4M3FN bytes with fp32 scales
+ *   s1, s3: [E_phys, I/128, H/128]          s2: [E_phys, H/128, I/128]
+ * Slot p holds the weights of logical expert physical_to_logical_map[p].
+ * sw1/sw3/sw2 (+ ss*) are the shared expert ([I,H], [I,H], [H,I]), used when
+ * n_shared == 1.  Scale pointers are ignored for bf16 weights. */
+typedef struct {
+  const void* w1; const void* w3; const void* w2;
+  const float* s1; const float* s3; const float* s2;
+  const void* sw1; const void* sw3; const void* sw2;
+  const float* ss1; const float* ss3; const float* ss2;
+} moe_weights_t;
+
+/* ---- sizing (host, pure) ------------------------------------------------ */
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_string(moe_status_t s);
+
+/* Validates a description; MOE_OK or the error the calls would return. */
+moe_status_t moe_check_desc(const moe_desc_t* d);
+
+/* Bytes of scratch device memory moe_route needs (for T = T_max). */
+size_t moe_route_workspace_bytes(const moe_desc_t* d);
+
+/* Rows of the grouped buffers xg [rows, H], h [rows, I] and y: routed rows
+ * (masked: E_phys*M_max + K*max(0, T_max - M_max) spill rows; contiguous:
+ * T_max*K + E_phys*(BM-1)), then n_shared*T_max shared-expert rows. */
+int64_t moe_buffer_rows(const moe_desc_t* d);
+
+/* Row where the shared expert's rows start (= routed row capacity). */
+int64_t moe_shared_base(const moe_desc_t* d);
+
+/* Number of K-splits the down projection uses for T tokens.  With 1 split
+ * y is bf16 [rows, H]; with S > 1 it is S fp32 partial sums [S, rows, H],
+ * summed in split order by moe_combine. */
+int32_t moe_down_splits(const moe_desc_t* d, int32_t T);
+
+/* Bytes of y for T tokens. */
+size_t moe_y_bytes(const moe_desc_t* d, int32_t T);
+
+/* ---- the hot path -------------------------------------------------------- */
+
+/* a1. logits[t, e] = sum_h x[t, h] * w_router[e, h] (+ bias[e]), fp32
+ * accumulation.  x: device [T, H] act_dtype; w_router: device [E, H] bf16;
+ * bias: device [E] fp32 or NULL; logits: device [T, E] fp32.
+ * (vllbc blog, routing section: one logit per expert per token.) */
+moe_status_t moe_router_logits(const moe_desc_t* d, const void* x, const void* w_router,
+                               const float* bias, int32_t T, float* logits,
+                               hipStream_t stream);
+
+/* a2-a4. From fp32 logits [T, E] (device): top-K ids and weights, per-slot
+ * counts and offsets, the stable expert-grouped order (ascending token
+ * inside each slot), and the layout tables.  With a replica map
+ * (l2p: device [E, max_replicas] logical_to_physical_map, -1 padded;
+ * replica_count: device [E] logical_replica_count; both NULL for none) the
+ * tokens of logical expert l, in ascending token order, go round-robin over
+ * l2p[l][0..count-1] (vLLM EPLB explainer 1.2; MoonEP: ids, weights and
+ * combine positions unchanged).  ws: device scratch of at least
+ * moe_route_workspace_bytes(d) bytes.  0 <= T <= T_max. */
+moe_status_t moe_route(const moe_desc_t* d, const float* logits, int32_t T,
+                       const int32_t* l2p, const int32_t* replica_count,
+                       const moe_route_t* r, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* a5. Gathers token rows into the grouped buffer: xg[slot_of[t*K+k]] = x[t]
+ * (cast to bf16 if x is fp32) and, with a shared expert,
+ * xg[moe_shared_base + t] = x[t].  x: device [T, H] act_dtype;
+ * xg: device [moe_buffer_rows, H] bf16. */
+moe_status_t moe_permute(const moe_desc_t* d, const void* x, int32_t T,
+                         const moe_route_t* r, void* xg, hipStream_t stream);
+
+/* a6 (+a8). Gate/up projection with the SwiGLU activation for every slot
+ * with tokens, and for the shared expert over all T tokens:
+ * h[row] = SiLU(xg[row] W1^T) * (xg[row] W3^T), fp32 accumulation, stored
+ * bf16.  Slots with no token, and row tiles holding no valid row, issue no
+ * MFMA and read no weights ("推理 INFRA 方法论(5)", DeepGEMM section: a tile
+ * with m_blk*BM >= masked_m[e] is skipped).  fp8 weights are promoted with
+ * their block scale every 128 K (the same section's two-level
+ * accumulation).  xg: device [moe_buffer_rows, H] bf16;
+ * h: device [moe_buffer_rows, I] bf16. */
+moe_status_t moe_expert_gate_up(const moe_desc_t* d, const moe_weights_t* w,
+                                const moe_route_t* r, int32_t T, const void* xg,
+                                void* h, hipStream_t stream);
+
+/* a7 (+a8). Down projection y[row] = h[row] W2^T for the same rows.
+ * y: device, moe_y_bytes(d, T) bytes: bf16 [moe_buffer_rows, H] when
+ * moe_down_splits(d, T) == 1, else that many fp32 partial planes. */
+moe_status_t moe_expert_down(const moe_desc_t* d, const moe_weights_t* w,
+                             const moe_route_t* r, int32_t T, const void* h, void* y,
+                             hipStream_t stream);
+
+/* a6-a8 in one call: moe_expert_gate_up then moe_expert_down. */
+moe_status_t moe_grouped_ffn(const moe_desc_t* d, const moe_weights_t* w,
+                             const moe_route_t* r, int32_t T, const void* xg,
+                             void* h, void* y, hipStream_t stream);
+
+/* a9. out[t] = sum_k topk_w[t,k] * y[slot_of[t*K+k]] (+ y[shared_base + t]),
+ * in fp32 with k ascending, then rounded to act_dtype (RNE).
+ * (vllbc blog, combine: weight by g_i, then sum the K results.)
+ * y: device as produced by moe_grouped_ffn; out: device [T, H] act_dtype. */
+moe_status_t moe_combine(const moe_desc_t* d, const moe_route_t* r, int32_t T,
+                         const void* y, void* out, hipStream_t stream);
+
+/* All five steps in order on one stream (same arguments as above). */
+moe_status_t moe_forward(const moe_desc_t* d, const void* x, const void* w_router,
+                         const float* bias, const int32_t* l2p, const int32_t* replica_count,
+                         const moe_weights_t* w, int32_t T, float* logits,
+                         const moe_route_t* r, void* ws, size_t ws_bytes,
+                         void* xg, void* h, void* y, void* out, hipStream_t stream);
+
+/* ---- replica maps (host, pure) ------------------------------------------- */
+
+/* physical_to_logical_map p2l [E_phys] (host) -> logical_to_physical_map
+ * l2p_out [E, max_replicas] (host, -1 padded, replicas in ascending slot) and
+ * logical_replica_count count_out [E] (host).  MOE_ERR_ARG if an entry is
+ * outside [0, E), a logical expert has no slot, or has more than
+ * max_replicas.  (vLLM EPLB explainer, section 1.2.) */
+moe_status_t moe_replica_map_from_p2l(const int32_t* p2l, int32_t E, int32_t E_phys,
+                                      int32_t max_replicas, int32_t* l2p_out,
+                                      int32_t* count_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

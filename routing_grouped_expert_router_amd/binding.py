@@ -1,0 +1,301 @@
+"""ctypes binding of libmoe.so (include/moe.h).  Argument marshalling only:
+every step of the layer runs in the library's HIP kernels; PyTorch supplies
+device memory and the current stream.
+
+The library must be built (``python -m routing_grouped_expert_router_amd.build``);
+loading fails loudly when it is missing.  There is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16, MOE_FP8E4M3_B128 = 0, 1, 2
+MOE_CONTIG, MOE_MASKED = 0, 1
+MOE_STATUS_SPILL, MOE_STATUS_BAD_REPLICA, MOE_STATUS_NONFINITE, MOE_STATUS_INTERNAL = 1, 2, 4, 8
+
+EXPORTED = [
+    "moe_status_string", "moe_check_desc", "moe_route_workspace_bytes", "moe_buffer_rows",
+    "moe_shared_base", "moe_down_splits", "moe_y_bytes", "moe_router_logits", "moe_route",
+    "moe_permute", "moe_expert_gate_up", "moe_expert_down", "moe_grouped_ffn", "moe_combine",
+    "moe_forward", "moe_replica_map_from_p2l",
+]
+
+
+class moe_desc_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "T_max", "H", "I", "E", "E_phys", "K", "n_shared", "max_replicas",
+        "act_dtype", "w_dtype", "layout", "M_max", "BM")]
+
+
+_P = ctypes.c_void_p
+
+
+class moe_route_t(ctypes.Structure):
+    _fields_ = [(n, _P) for n in (
+        "topk_ids", "topk_w", "topk_phys", "row_of", "slot_of", "src_of", "counts",
+        "offsets", "masked_m", "spill_off", "pad_off", "status")]
+
+
+class moe_weights_t(ctypes.Structure):
+    _fields_ = [(n, _P) for n in (
+        "w1", "w3", "w2", "s1", "s3", "s2", "sw1", "sw3", "sw2", "ss1", "ss3", "ss2")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m routing_grouped_expert_router_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        D = ctypes.POINTER(moe_desc_t)
+        R = ctypes.POINTER(moe_route_t)
+        W = ctypes.POINTER(moe_weights_t)
+        i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        sig = {
+            "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "moe_check_desc": (ctypes.c_int, [D]),
+            "moe_route_workspace_bytes": (sz, [D]),
+            "moe_buffer_rows": (i64, [D]),
+            "moe_shared_base": (i64, [D]),
+            "moe_down_splits": (i32, [D, i32]),
+            "moe_y_bytes": (sz, [D, i32]),
+            "moe_router_logits": (ctypes.c_int, [D, _P, _P, _P, i32, _P, _P]),
+            "moe_route": (ctypes.c_int, [D, _P, i32, _P, _P, R, _P, sz, _P]),
+            "moe_permute": (ctypes.c_int, [D, _P, i32, R, _P, _P]),
+            "moe_expert_gate_up": (ctypes.c_int, [D, W, R, i32, _P, _P, _P]),
+            "moe_expert_down": (ctypes.c_int, [D, W, R, i32, _P, _P, _P]),
+            "moe_grouped_ffn": (ctypes.c_int, [D, W, R, i32, _P, _P, _P, _P]),
+            "moe_combine": (ctypes.c_int, [D, R, i32, _P, _P, _P]),
+            "moe_forward": (ctypes.c_int, [D, _P, _P, _P, _P, _P, W, i32, _P, R, _P, sz,
+                                           _P, _P, _P, _P, _P]),
+            "moe_replica_map_from_p2l": (ctypes.c_int, [_P, i32, i32, i32, _P, _P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+class MoEError(RuntimeError):
+    pass
+
+
+def _check(code: int, what: str):
+    if code != MOE_OK:
+        msg = lib().moe_status_string(code).decode()
+        raise MoEError(f"{what}: {msg} (status {code})")
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+@dataclass
+class Desc:
+    T_max: int
+    H: int
+    I: int
+    E: int
+    E_phys: int
+    K: int
+    n_shared: int = 0
+    max_replicas: int = 1
+    act_dtype: int = MOE_BF16
+    w_dtype: int = MOE_BF16
+    layout: int = MOE_CONTIG
+    M_max: int = 1
+    BM: int = 16
+
+    def c(self) -> moe_desc_t:
+        return moe_desc_t(*[int(getattr(self, f)) for f, _ in moe_desc_t._fields_])
+
+    @staticmethod
+    def from_config(cfg, max_replicas: int = 1) -> "Desc":
+        return Desc(T_max=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, E_phys=cfg.E_phys, K=cfg.K,
+                    n_shared=cfg.n_shared, max_replicas=max_replicas,
+                    act_dtype=MOE_F32 if cfg.act_dtype == "f32" else MOE_BF16,
+                    w_dtype=MOE_BF16 if cfg.w_dtype == "bf16" else MOE_FP8E4M3_B128,
+                    layout=MOE_MASKED if cfg.layout == "masked" else MOE_CONTIG,
+                    M_max=max(1, cfg.M_max), BM=max(1, cfg.BM))
+
+
+# ---- sizing -------------------------------------------------------------------
+
+def check_desc(d: Desc) -> int:
+    return lib().moe_check_desc(ctypes.byref(d.c()))
+
+
+def route_workspace_bytes(d: Desc) -> int:
+    return lib().moe_route_workspace_bytes(ctypes.byref(d.c()))
+
+
+def buffer_rows(d: Desc) -> int:
+    return lib().moe_buffer_rows(ctypes.byref(d.c()))
+
+
+def shared_base(d: Desc) -> int:
+    return lib().moe_shared_base(ctypes.byref(d.c()))
+
+
+def down_splits(d: Desc, T: int) -> int:
+    return lib().moe_down_splits(ctypes.byref(d.c()), T)
+
+
+def y_bytes(d: Desc, T: int) -> int:
+    return lib().moe_y_bytes(ctypes.byref(d.c()), T)
+
+
+# ---- buffers ------------------------------------------------------------------
+
+class RouteTables:
+    """Device tensors behind a moe_route_t (allocated with torch)."""
+
+    def __init__(self, d: Desc, device="cuda"):
+        TK = max(1, d.T_max * d.K)
+        i32 = dict(dtype=torch.int32, device=device)
+        self.topk_ids = torch.zeros(TK, **i32)
+        self.topk_w = torch.zeros(TK, dtype=torch.float32, device=device)
+        self.topk_phys = torch.zeros(TK, **i32)
+        self.row_of = torch.zeros(TK, **i32)
+        self.slot_of = torch.zeros(TK, **i32)
+        self.src_of = torch.zeros(TK, **i32)
+        self.counts = torch.zeros(d.E_phys, **i32)
+        self.offsets = torch.zeros(d.E_phys + 1, **i32)
+        self.masked_m = torch.zeros(d.E_phys, **i32)
+        self.spill_off = torch.zeros(d.E_phys + 1, **i32)
+        self.pad_off = torch.zeros(d.E_phys + 1, **i32)
+        self.status = torch.zeros(1, **i32)
+        self.c = moe_route_t(*[_ptr(getattr(self, f)) for f, _ in moe_route_t._fields_])
+
+
+class Weights:
+    """moe_weights_t over torch tensors (kept alive here)."""
+
+    def __init__(self, w: dict, shared: dict | None = None):
+        self._keep = (w, shared)
+        s = shared or {}
+        self.c = moe_weights_t(
+            _ptr(w["w1"]), _ptr(w["w3"]), _ptr(w["w2"]),
+            _ptr(w.get("s1")), _ptr(w.get("s3")), _ptr(w.get("s2")),
+            _ptr(s.get("w1")), _ptr(s.get("w3")), _ptr(s.get("w2")),
+            _ptr(s.get("s1")), _ptr(s.get("s3")), _ptr(s.get("s2")))
+
+
+# ---- the five steps (same names as the C ABI) ------------------------------------
+
+def moe_router_logits(d: Desc, x, w_router, bias, T, logits, stream=None):
+    _check(lib().moe_router_logits(ctypes.byref(d.c()), _ptr(x), _ptr(w_router), _ptr(bias),
+                                   T, _ptr(logits), _stream(stream)), "moe_router_logits")
+
+
+def moe_route(d: Desc, logits, T, rt: RouteTables, ws, l2p=None, replica_count=None, stream=None):
+    _check(lib().moe_route(ctypes.byref(d.c()), _ptr(logits), T, _ptr(l2p), _ptr(replica_count),
+                           ctypes.byref(rt.c), _ptr(ws), ws.numel() * ws.element_size(),
+                           _stream(stream)), "moe_route")
+
+
+def moe_permute(d: Desc, x, T, rt: RouteTables, xg, stream=None):
+    _check(lib().moe_permute(ctypes.byref(d.c()), _ptr(x), T, ctypes.byref(rt.c), _ptr(xg),
+                             _stream(stream)), "moe_permute")
+
+
+def moe_grouped_ffn(d: Desc, w: Weights, rt: RouteTables, T, xg, h, y, stream=None):
+    _check(lib().moe_grouped_ffn(ctypes.byref(d.c()), ctypes.byref(w.c), ctypes.byref(rt.c), T,
+                                 _ptr(xg), _ptr(h), _ptr(y), _stream(stream)), "moe_grouped_ffn")
+
+
+def moe_expert_gate_up(d: Desc, w: Weights, rt: RouteTables, T, xg, h, stream=None):
+    _check(lib().moe_expert_gate_up(ctypes.byref(d.c()), ctypes.byref(w.c), ctypes.byref(rt.c), T,
+                                    _ptr(xg), _ptr(h), _stream(stream)), "moe_expert_gate_up")
+
+
+def moe_expert_down(d: Desc, w: Weights, rt: RouteTables, T, h, y, stream=None):
+    _check(lib().moe_expert_down(ctypes.byref(d.c()), ctypes.byref(w.c), ctypes.byref(rt.c), T,
+                                 _ptr(h), _ptr(y), _stream(stream)), "moe_expert_down")
+
+
+def moe_combine(d: Desc, rt: RouteTables, T, y, out, stream=None):
+    _check(lib().moe_combine(ctypes.byref(d.c()), ctypes.byref(rt.c), T, _ptr(y), _ptr(out),
+                             _stream(stream)), "moe_combine")
+
+
+def moe_replica_map_from_p2l(p2l, E: int, max_replicas: int):
+    """Host helper: physical_to_logical_map -> (logical_to_physical_map,
+    logical_replica_count) as CPU int32 tensors."""
+    p2l = torch.as_tensor(p2l, dtype=torch.int32).contiguous()
+    l2p = torch.empty((E, max_replicas), dtype=torch.int32)
+    cnt = torch.empty(E, dtype=torch.int32)
+    _check(lib().moe_replica_map_from_p2l(_ptr(p2l), E, p2l.numel(), max_replicas,
+                                          _ptr(l2p), _ptr(cnt)), "moe_replica_map_from_p2l")
+    return l2p, cnt
+
+
+class MoELayer:
+    """One layer's device buffers and the C calls in order.  Weights are a
+    dict of device tensors as produced for the C ABI layout
+    (w1/w3 [E_phys(+1 shared), I, H], w2 [.., H, I], fp8 scales s1/s3/s2);
+    the shared expert, if any, is the last slot."""
+
+    def __init__(self, d: Desc, weights: dict, w_router, bias=None, l2p=None,
+                 replica_count=None, device="cuda"):
+        self.d = d
+        self.device = device
+        self.rt = RouteTables(d, device)
+        self.ws = torch.zeros(route_workspace_bytes(d), dtype=torch.uint8, device=device)
+        rows = buffer_rows(d)
+        self.xg = torch.zeros((rows, d.H), dtype=torch.bfloat16, device=device)
+        self.h = torch.zeros((rows, d.I), dtype=torch.bfloat16, device=device)
+        # the down projection splits K more for fewer tokens: size y for the worst T
+        ymax = max(y_bytes(d, t) for t in {1, d.T_max} if t <= max(1, d.T_max))
+        self.y = torch.zeros(ymax, dtype=torch.uint8, device=device)
+        self.logits = torch.zeros((max(1, d.T_max), d.E), dtype=torch.float32, device=device)
+        self.w_router = w_router
+        self.bias = bias
+        self.l2p = l2p
+        self.rcount = replica_count
+        G = d.E_phys
+        routed = {k: (v[:G] if v is not None else None) for k, v in weights.items()}
+        shared = None
+        if d.n_shared:
+            shared = {k: v[G] for k, v in weights.items() if v is not None}
+        self.weights = Weights(routed, shared)
+        odt = torch.float32 if d.act_dtype == MOE_F32 else torch.bfloat16
+        self.out = torch.zeros((max(1, d.T_max), d.H), dtype=odt, device=device)
+
+    def y_for(self, T: int) -> torch.Tensor:
+        return self.y[: y_bytes(self.d, T)]
+
+    def forward(self, x, T=None, logits=None, stream=None):
+        """Runs the five steps; ``logits`` (fp32 [T, E]) replaces the router
+        step when given.  Returns the output view [T, H]."""
+        d = self.d
+        T = x.shape[0] if T is None else T
+        if logits is None:
+            moe_router_logits(d, x, self.w_router, self.bias, T, self.logits, stream)
+            logits = self.logits
+        moe_route(d, logits, T, self.rt, self.ws, self.l2p, self.rcount, stream)
+        moe_permute(d, x, T, self.rt, self.xg, stream)
+        moe_grouped_ffn(d, self.weights, self.rt, T, self.xg, self.h, self.y, stream)
+        moe_combine(d, self.rt, T, self.y, self.out, stream)
+        return self.out[:T]

@@ -1,0 +1,127 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kMaxK = 16;      // experts per token supported by the router
+constexpr int kMaxE = 4096;    // logical / physical experts supported
+constexpr int kBlockTokens = 64;  // tokens per routing block (one u64 mask)
+
+// ---- bf16 ---------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(uint32_t(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN (quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+// ---- OCP E4M3FN -> bf16 (exact: every E4M3 value is a bf16 value) ---------
+// Four fp8 bytes of `w` -> four bf16 in two dwords, byte order preserved.
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  u32x2 r;
+  r.x = __builtin_bit_cast(uint32_t, lo);
+  r.y = __builtin_bit_cast(uint32_t, hi);
+  return r;
+}
+
+// 16 fp8 bytes -> two bf16x8 MFMA operands (bytes 0..7, bytes 8..15).
+__device__ __forceinline__ void fp8x16_to_bf16(const u32x4 q, bf16x8& a0, bf16x8& a1) {
+  u32x2 p0 = fp8x4_to_bf16x4(q.x), p1 = fp8x4_to_bf16x4(q.y);
+  u32x2 p2 = fp8x4_to_bf16x4(q.z), p3 = fp8x4_to_bf16x4(q.w);
+  u32x4 v0 = {p0.x, p0.y, p1.x, p1.y};
+  u32x4 v1 = {p2.x, p2.y, p3.x, p3.y};
+  a0 = __builtin_bit_cast(bf16x8, v0);
+  a1 = __builtin_bit_cast(bf16x8, v1);
+}
+
+// ---- MFMA ---------------------------------------------------------------
+// v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16].
+// Lane l supplies A row (l % 16), B column (l % 16), each with 8 K values
+// (the K set of lane group l / 16); lane l receives D rows 4*(l/16)+0..3 of
+// column l % 16.  Any K assignment works as long as A and B agree on it.
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 a, const bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- ordering key for top-K ------------------------------------------------
+// Monotone map fp32 -> u32 with -0 == +0 and NaN below -inf (key 0).
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// (value, id) packed so that a larger key is a larger value, ties to the
+// lower id.  A removed entry is 0, below every real key.
+__device__ __forceinline__ uint64_t topk_key(float v, int id) {
+  return (uint64_t(order_key(v)) << 32) | uint64_t(0xffffffffu - uint32_t(id));
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t lo = __shfl_xor((unsigned)(v & 0xffffffffu), off, kWave);
+    uint32_t hi = __shfl_xor((unsigned)(v >> 32), off, kWave);
+    uint64_t o = (uint64_t(hi) << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Exclusive scan of n (<= 4 * blockDim.x) ints in LDS `a`, in place, by the
+// whole workgroup; returns the total.  `tmp` needs blockDim.x/64 + 1 ints.
+__device__ inline int block_exclusive_scan(int* a, int n, int* tmp) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int per = (n + nt - 1) / nt;
+  const int lo = tid * per, hi = min(lo + per, n);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += a[i];
+  // inclusive scan of s across the workgroup
+  const int lane = tid & 63, wv = tid >> 6;
+  int x = s;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) tmp[wv] = x;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < nt / 64; ++w) { int c = tmp[w]; tmp[w] = run; run += c; }
+    tmp[nt / 64] = run;
+  }
+  __syncthreads();
+  int base = tmp[wv] + x - s;
+  for (int i = lo; i < hi; ++i) { int c = a[i]; a[i] = base; base += c; }
+  int total = tmp[nt / 64];
+  __syncthreads();
+  return total;
+}
+
+}  // namespace moe

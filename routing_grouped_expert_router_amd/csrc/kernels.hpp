@@ -1,0 +1,79 @@
+// Internal launch interface between the C ABI (moe_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- routing ----------------------------------------------------------------
+
+struct RouteWs {            // views into the caller's route workspace
+  int32_t* local_rank;      // [T_max*K] rank of choice i among earlier tokens
+                            //           of its 64-token block that chose the
+                            //           same logical expert
+  int32_t* blk;             // [nblk*E] per-block counts -> exclusive prefixes
+  int32_t* blk_flags;       // [nblk] non-finite flag per block
+  int32_t* map_valid;       // [1] 1 when a replica map is given and valid
+};
+
+struct RouteArgs {
+  const float* logits; int T, E, E_phys, K;
+  const int32_t* l2p; const int32_t* rcount; int max_replicas;
+  int layout, M_max, BM;
+  int64_t routed_cap;       // rows of the routed part of the grouped buffer
+  // outputs
+  int32_t* topk_ids; float* topk_w; int32_t* topk_phys; int32_t* row_of;
+  int32_t* slot_of; int32_t* src_of; int32_t* counts; int32_t* offsets;
+  int32_t* masked_m; int32_t* spill_off; int32_t* pad_off; uint32_t* status;
+  RouteWs ws;
+};
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+// ---- permute / combine -------------------------------------------------------
+
+struct PermuteArgs {
+  const void* x; int act_f32; int T, K, H;
+  const int32_t* slot_of; int64_t shared_base; int n_shared; int64_t rows;
+  uint16_t* xg;
+};
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t s);
+
+struct CombineArgs {
+  const void* y; int y_f32; int splits; int64_t split_stride;  // elements
+  int T, K, H; int64_t rows;
+  const int32_t* slot_of; const float* topk_w;
+  int n_shared; int64_t shared_base;
+  void* out; int out_f32;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+// ---- streaming grouped GEMM (decode FFN and router logits) ---------------------
+
+enum { MODE_GATEUP = 0, MODE_DOWN = 1, MODE_ROUTER = 2 };
+
+struct StreamArgs {
+  const uint16_t* X; int64_t ldx;   // bf16 rows
+  int Kdim, N;                       // reduction length, output features
+  int E_phys, T, layout, M_max; int64_t shared_base;
+  const int32_t* counts; const int32_t* masked_m; const int32_t* spill_off;
+  const int32_t* pad_off;
+  const void* W; const void* W3; const float* S; const float* S3;        // routed
+  const void* SW; const void* SW3; const float* SS; const float* SS3;    // shared
+  void* out; int64_t ldo; int64_t split_stride; int out_f32;
+  const float* bias;
+  int ksplit;      // grid.z = ksplit * mchunks
+  int mchunks;     // row-tile passes dealt round-robin over grid.z
+};
+
+hipError_t launch_ffn_stream(const StreamArgs& a, int fp8, int mode, int mt, dim3 grid,
+                             hipStream_t s);
+
+// router logits for fp32 activations: plain fp32 dot products
+struct RouterF32Args {
+  const float* x; const uint16_t* w; const float* bias; int T, E, H; float* logits;
+};
+hipError_t launch_router_f32(const RouterF32Args& a, hipStream_t s);
+
+}  // namespace moe

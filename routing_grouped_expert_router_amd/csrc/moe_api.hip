@@ -1,0 +1,307 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// buffer sizing, and the choice of kernel variants and grids.  Grids depend
+// only on (desc, T), never on device-side counts.
+#include <string.h>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline int64_t nblk_of(int64_t T) { return (T + kBlockTokens - 1) / kBlockTokens; }
+
+struct WsLayout { size_t local_rank, blk, flags, map_valid, total; };
+
+WsLayout ws_layout(const moe_desc_t* d) {
+  WsLayout w;
+  const int64_t TK = (int64_t)d->T_max * d->K;
+  const int64_t nb = nblk_of(d->T_max);
+  w.local_rank = 0;
+  w.blk = w.local_rank + align_up(sizeof(int32_t) * (size_t)(TK > 0 ? TK : 1));
+  w.flags = w.blk + align_up(sizeof(int32_t) * (size_t)((nb > 0 ? nb : 1) * d->E));
+  w.map_valid = w.flags + align_up(sizeof(int32_t) * (size_t)(nb > 0 ? nb : 1));
+  w.total = w.map_valid + kAlign;
+  return w;
+}
+
+int64_t routed_cap(const moe_desc_t* d) {
+  if (d->layout == MOE_MASKED) {
+    const int64_t spill = (int64_t)d->K * (d->T_max > d->M_max ? d->T_max - d->M_max : 0);
+    return (int64_t)d->E_phys * d->M_max + spill;
+  }
+  return (int64_t)d->T_max * d->K + (int64_t)d->E_phys * (d->BM - 1);
+}
+
+bool route_ptrs_ok(const moe_desc_t* d, const moe_route_t* r) {
+  if (!r) return false;
+  if (!r->topk_ids || !r->topk_w || !r->topk_phys || !r->row_of || !r->slot_of || !r->src_of ||
+      !r->counts || !r->offsets || !r->status)
+    return false;
+  if (d->layout == MOE_MASKED) return r->masked_m && r->spill_off;
+  return r->pad_off != nullptr;
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// row tiles held in registers per pass of the streaming GEMM
+int stream_mt(const moe_desc_t* d, int T) {
+  int rows;
+  if (d->layout == MOE_MASKED) rows = d->M_max;
+  else rows = (int)(((int64_t)T * d->K + d->E_phys - 1) / d->E_phys);
+  if (rows <= 16) return 1;
+  if (rows <= 32) return 2;
+  return 4;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+moe_status_t moe_check_desc(const moe_desc_t* d) {
+  if (!d) return MOE_ERR_ARG;
+  if (d->T_max < 0 || d->H <= 0 || d->I <= 0 || d->E < 1 || d->K < 1 || d->K > d->E) return MOE_ERR_ARG;
+  if (d->E_phys < d->E || d->n_shared < 0 || d->n_shared > 1 || d->max_replicas < 1) return MOE_ERR_ARG;
+  if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_ERR_ARG;
+  if (d->w_dtype != MOE_BF16 && d->w_dtype != MOE_FP8E4M3_B128) return MOE_ERR_ARG;
+  if (d->layout == MOE_MASKED) { if (d->M_max < 1) return MOE_ERR_ARG; }
+  else if (d->layout == MOE_CONTIG) { if (d->BM < 1) return MOE_ERR_ARG; }
+  else return MOE_ERR_ARG;
+  if (d->H % 128 || d->I % 128) return MOE_ERR_UNSUPPORTED;
+  if (d->E > 1024 || d->E_phys > kMaxE || d->K > kMaxK) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)d->T_max * d->K > (int64_t)INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t moe_route_workspace_bytes(const moe_desc_t* d) {
+  if (moe_check_desc(d) != MOE_OK) return 0;
+  return ws_layout(d).total;
+}
+
+int64_t moe_shared_base(const moe_desc_t* d) {
+  if (moe_check_desc(d) != MOE_OK) return -1;
+  return routed_cap(d);
+}
+
+int64_t moe_buffer_rows(const moe_desc_t* d) {
+  if (moe_check_desc(d) != MOE_OK) return -1;
+  return routed_cap(d) + (int64_t)d->n_shared * d->T_max;
+}
+
+int32_t moe_down_splits(const moe_desc_t* d, int32_t T) {
+  if (moe_check_desc(d) != MOE_OK) return 0;
+  const int steps = d->I / 128;
+  const int64_t groups = ((int64_t)T * d->K < d->E_phys ? (int64_t)T * d->K : d->E_phys) + d->n_shared;
+  const int64_t wgs = groups * (d->H / 64);
+  int s = 1;
+  while (wgs * s < 1024 && steps % (2 * s) == 0 && s < 8) s *= 2;
+  return s;
+}
+
+size_t moe_y_bytes(const moe_desc_t* d, int32_t T) {
+  const int32_t s = moe_down_splits(d, T);
+  if (s <= 0) return 0;
+  const size_t plane = (size_t)moe_buffer_rows(d) * d->H;
+  return s == 1 ? plane * 2 : plane * 4 * s;
+}
+
+moe_status_t moe_router_logits(const moe_desc_t* d, const void* x, const void* w_router,
+                               const float* bias, int32_t T, float* logits, hipStream_t stream) {
+  moe_status_t st = moe_check_desc(d);
+  if (st != MOE_OK) return st;
+  if (T < 0 || T > d->T_max) return MOE_ERR_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !w_router || !logits) return MOE_ERR_ARG;
+  if (d->act_dtype == MOE_F32) {
+    RouterF32Args f = {static_cast<const float*>(x), static_cast<const uint16_t*>(w_router), bias,
+                       T, d->E, d->H, logits};
+    return hip_status(launch_router_f32(f, stream));
+  }
+  StreamArgs a = {};
+  a.X = static_cast<const uint16_t*>(x); a.ldx = d->H;
+  a.Kdim = d->H; a.N = d->E; a.T = T; a.E_phys = d->E_phys;
+  a.W = w_router; a.out = logits; a.ldo = d->E; a.bias = bias; a.ksplit = 1;
+  const int mt = 4;
+  const int tiles = (T + 15) / 16;
+  a.mchunks = (tiles + mt - 1) / mt;
+  dim3 grid((d->E + 63) / 64, 1, a.mchunks);
+  return hip_status(launch_ffn_stream(a, 0, MODE_ROUTER, mt, grid, stream));
+}
+
+moe_status_t moe_route(const moe_desc_t* d, const float* logits, int32_t T, const int32_t* l2p,
+                       const int32_t* replica_count, const moe_route_t* r, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = moe_check_desc(d);
+  if (st != MOE_OK) return st;
+  if (T < 0 || T > d->T_max || !route_ptrs_ok(d, r)) return MOE_ERR_ARG;
+  if (T > 0 && !logits) return MOE_ERR_ARG;
+  if ((l2p == nullptr) != (replica_count == nullptr)) return MOE_ERR_ARG;
+  const WsLayout wl = ws_layout(d);
+  if (!ws || ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  RouteArgs a = {};
+  a.logits = logits; a.T = T; a.E = d->E; a.E_phys = d->E_phys; a.K = d->K;
+  a.l2p = l2p; a.rcount = replica_count; a.max_replicas = d->max_replicas;
+  a.layout = d->layout; a.M_max = d->M_max; a.BM = d->BM; a.routed_cap = routed_cap(d);
+  a.topk_ids = r->topk_ids; a.topk_w = r->topk_w; a.topk_phys = r->topk_phys;
+  a.row_of = r->row_of; a.slot_of = r->slot_of; a.src_of = r->src_of;
+  a.counts = r->counts; a.offsets = r->offsets; a.masked_m = r->masked_m;
+  a.spill_off = r->spill_off; a.pad_off = r->pad_off; a.status = r->status;
+  a.ws.local_rank = reinterpret_cast<int32_t*>(base + wl.local_rank);
+  a.ws.blk = reinterpret_cast<int32_t*>(base + wl.blk);
+  a.ws.blk_flags = reinterpret_cast<int32_t*>(base + wl.flags);
+  a.ws.map_valid = reinterpret_cast<int32_t*>(base + wl.map_valid);
+  return hip_status(launch_route(a, stream));
+}
+
+moe_status_t moe_permute(const moe_desc_t* d, const void* x, int32_t T, const moe_route_t* r,
+                         void* xg, hipStream_t stream) {
+  moe_status_t st = moe_check_desc(d);
+  if (st != MOE_OK) return st;
+  if (T < 0 || T > d->T_max || !route_ptrs_ok(d, r)) return MOE_ERR_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !xg) return MOE_ERR_ARG;
+  PermuteArgs a = {};
+  a.x = x; a.act_f32 = d->act_dtype == MOE_F32; a.T = T; a.K = d->K; a.H = d->H;
+  a.slot_of = r->slot_of; a.shared_base = routed_cap(d); a.n_shared = d->n_shared;
+  a.rows = moe_buffer_rows(d); a.xg = static_cast<uint16_t*>(xg);
+  return hip_status(launch_permute(a, stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+moe_status_t ffn_common_checks(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
+                               int32_t T) {
+  moe_status_t st = moe_check_desc(d);
+  if (st != MOE_OK) return st;
+  if (T < 0 || T > d->T_max || !route_ptrs_ok(d, r) || !w) return MOE_ERR_ARG;
+  const bool fp8 = d->w_dtype == MOE_FP8E4M3_B128;
+  if (d->n_shared && fp8 && (!w->ss1 || !w->ss3 || !w->ss2)) return MOE_ERR_ARG;
+  return MOE_OK;
+}
+
+StreamArgs ffn_base_args(const moe_desc_t* d, const moe_route_t* r, int32_t T) {
+  StreamArgs a = {};
+  a.E_phys = d->E_phys; a.T = T; a.layout = d->layout; a.M_max = d->M_max;
+  a.shared_base = routed_cap(d);
+  a.counts = r->counts; a.masked_m = r->masked_m; a.spill_off = r->spill_off; a.pad_off = r->pad_off;
+  a.ksplit = 1; a.mchunks = 1;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_expert_gate_up(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
+                                int32_t T, const void* xg, void* h, hipStream_t stream) {
+  moe_status_t st = ffn_common_checks(d, w, r, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  const bool fp8 = d->w_dtype == MOE_FP8E4M3_B128;
+  if (!xg || !h || !w->w1 || !w->w3) return MOE_ERR_ARG;
+  if (fp8 && (!w->s1 || !w->s3)) return MOE_ERR_ARG;
+  if (d->n_shared && (!w->sw1 || !w->sw3)) return MOE_ERR_ARG;
+  StreamArgs g1 = ffn_base_args(d, r, T);
+  g1.X = static_cast<const uint16_t*>(xg); g1.ldx = d->H; g1.Kdim = d->H; g1.N = d->I;
+  g1.W = w->w1; g1.W3 = w->w3; g1.S = w->s1; g1.S3 = w->s3;
+  g1.SW = w->sw1; g1.SW3 = w->sw3; g1.SS = w->ss1; g1.SS3 = w->ss3;
+  g1.out = h; g1.ldo = d->I;
+  const int G = d->E_phys + d->n_shared;
+  return hip_status(launch_ffn_stream(g1, fp8, MODE_GATEUP, stream_mt(d, T), dim3(d->I / 64, G, 1), stream));
+}
+
+moe_status_t moe_expert_down(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
+                             int32_t T, const void* h, void* y, hipStream_t stream) {
+  moe_status_t st = ffn_common_checks(d, w, r, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  const bool fp8 = d->w_dtype == MOE_FP8E4M3_B128;
+  if (!h || !y || !w->w2) return MOE_ERR_ARG;
+  if (fp8 && !w->s2) return MOE_ERR_ARG;
+  if (d->n_shared && !w->sw2) return MOE_ERR_ARG;
+  const int splits = moe_down_splits(d, T);
+  StreamArgs g2 = ffn_base_args(d, r, T);
+  g2.X = static_cast<const uint16_t*>(h); g2.ldx = d->I; g2.Kdim = d->I; g2.N = d->H;
+  g2.W = w->w2; g2.S = w->s2; g2.SW = w->sw2; g2.SS = w->ss2;
+  g2.out = y; g2.ldo = d->H; g2.ksplit = splits; g2.out_f32 = splits > 1;
+  g2.split_stride = moe_buffer_rows(d) * d->H;
+  const int G = d->E_phys + d->n_shared;
+  return hip_status(launch_ffn_stream(g2, fp8, MODE_DOWN, stream_mt(d, T), dim3(d->H / 64, G, splits), stream));
+}
+
+moe_status_t moe_grouped_ffn(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
+                             int32_t T, const void* xg, void* h, void* y, hipStream_t stream) {
+  moe_status_t st = moe_expert_gate_up(d, w, r, T, xg, h, stream);
+  if (st != MOE_OK) return st;
+  return moe_expert_down(d, w, r, T, h, y, stream);
+}
+
+moe_status_t moe_combine(const moe_desc_t* d, const moe_route_t* r, int32_t T, const void* y,
+                         void* out, hipStream_t stream) {
+  moe_status_t st = moe_check_desc(d);
+  if (st != MOE_OK) return st;
+  if (T < 0 || T > d->T_max || !route_ptrs_ok(d, r)) return MOE_ERR_ARG;
+  if (T == 0) return MOE_OK;
+  if (!y || !out) return MOE_ERR_ARG;
+  const int splits = moe_down_splits(d, T);
+  CombineArgs a = {};
+  a.y = y; a.y_f32 = splits > 1; a.splits = splits; a.split_stride = moe_buffer_rows(d) * d->H;
+  a.T = T; a.K = d->K; a.H = d->H; a.rows = moe_buffer_rows(d);
+  a.slot_of = r->slot_of; a.topk_w = r->topk_w;
+  a.n_shared = d->n_shared; a.shared_base = routed_cap(d);
+  a.out = out; a.out_f32 = d->act_dtype == MOE_F32;
+  return hip_status(launch_combine(a, stream));
+}
+
+moe_status_t moe_forward(const moe_desc_t* d, const void* x, const void* w_router,
+                         const float* bias, const int32_t* l2p, const int32_t* replica_count,
+                         const moe_weights_t* w, int32_t T, float* logits, const moe_route_t* r,
+                         void* ws, size_t ws_bytes, void* xg, void* h, void* y, void* out,
+                         hipStream_t stream) {
+  moe_status_t st = moe_router_logits(d, x, w_router, bias, T, logits, stream);
+  if (st != MOE_OK) return st;
+  st = moe_route(d, logits, T, l2p, replica_count, r, ws, ws_bytes, stream);
+  if (st != MOE_OK) return st;
+  st = moe_permute(d, x, T, r, xg, stream);
+  if (st != MOE_OK) return st;
+  st = moe_grouped_ffn(d, w, r, T, xg, h, y, stream);
+  if (st != MOE_OK) return st;
+  return moe_combine(d, r, T, y, out, stream);
+}
+
+moe_status_t moe_replica_map_from_p2l(const int32_t* p2l, int32_t E, int32_t E_phys,
+                                      int32_t max_replicas, int32_t* l2p_out, int32_t* count_out) {
+  if (!p2l || !l2p_out || !count_out || E < 1 || E_phys < E || max_replicas < 1) return MOE_ERR_ARG;
+  for (int64_t i = 0; i < (int64_t)E * max_replicas; ++i) l2p_out[i] = -1;
+  for (int l = 0; l < E; ++l) count_out[l] = 0;
+  for (int p = 0; p < E_phys; ++p) {
+    const int l = p2l[p];
+    if (l < 0 || l >= E) return MOE_ERR_ARG;
+    if (count_out[l] >= max_replicas) return MOE_ERR_ARG;
+    l2p_out[(int64_t)l * max_replicas + count_out[l]] = p;
+    count_out[l] += 1;
+  }
+  for (int l = 0; l < E; ++l)
+    if (count_out[l] < 1) return MOE_ERR_ARG;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+"""Helpers for the GPU parity tests: build a layer on the device from the
+synthetic workload, and compare against the CPU reference."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import moe_oracle as O
+from routing_grouped_expert_router_amd import binding as B
+from workloads import generate
+from oracle_adapt import to_f64, oracle_forward
+
+DEV = "cuda"
+
+# max|d| / max|ref| bars for the layer output, by weight format
+TOL = {"bf16": 1e-2, "fp8": 3e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+_DEFAULT = object()
+
+
+class Built:
+    """A workload on the GPU: inputs, uploaded weights and a MoELayer."""
+
+    def __init__(self, cfg, T=None, layout=None, M_max=None, p2l=_DEFAULT):
+        if layout is not None:
+            cfg = cfg.with_(layout=layout)
+        if M_max is not None:
+            cfg = cfg.with_(M_max=M_max)
+        self.cfg = cfg
+        self.inp = generate.make_inputs(cfg, wdevice=DEV)
+        if p2l is not _DEFAULT:
+            self.inp.p2l = p2l
+        self.T = cfg.T if T is None else T
+        self.inp.x = self.inp.x[: self.T].contiguous()   # the reference sees T tokens
+        self.weights = generate.upload_weights(self.inp, DEV)
+        self.l2p = self.rcount = None
+        max_rep = 1
+        if self.inp.p2l is not None:
+            l2p, cnt = O.replica_tables(self.inp.p2l, cfg.E)
+            max_rep = l2p.shape[1]
+            self.l2p = torch.from_numpy(l2p).to(DEV)
+            self.rcount = torch.from_numpy(cnt).to(DEV)
+        self.d = B.Desc.from_config(cfg, max_replicas=max_rep)
+        self.x = self.inp.x.to(DEV)
+        self.wr = self.inp.w_router.to(DEV)
+        self.bias = None if self.inp.bias is None else self.inp.bias.to(DEV)
+        self.layer = B.MoELayer(self.d, self.weights, self.wr, self.bias, self.l2p, self.rcount, DEV)
+
+    def oracle_logits(self) -> np.ndarray:
+        return O.router_logits(to_f64(self.inp.x), to_f64(self.inp.w_router),
+                               None if self.inp.bias is None else self.inp.bias.numpy())
+
+    def run(self, logits_np=None):
+        lg = None if logits_np is None else torch.from_numpy(np.ascontiguousarray(logits_np)).to(DEV)
+        out = self.layer.forward(self.x[: self.T], self.T, logits=lg)
+        torch.cuda.synchronize()
+        return out
+
+    def oracle(self, logits_np=None, tokens=None):
+        return oracle_forward(self.inp, logits=logits_np, tokens=tokens)
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def out_np(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def route_np(rt: B.RouteTables, T: int, K: int) -> dict:
+    g = lambda t, n: t[:n].cpu().numpy()
+    return dict(ids=g(rt.topk_ids, T * K).reshape(T, K), w=g(rt.topk_w, T * K).reshape(T, K),
+                phys=g(rt.topk_phys, T * K).reshape(T, K),
+                row_of=g(rt.row_of, T * K).reshape(T, K), slot_of=g(rt.slot_of, T * K).reshape(T, K),
+                src_of=g(rt.src_of, T * K), counts=rt.counts.cpu().numpy(),
+                offsets=rt.offsets.cpu().numpy(), masked_m=rt.masked_m.cpu().numpy(),
+                spill_off=rt.spill_off.cpu().numpy(), pad_off=rt.pad_off.cpu().numpy(),
+                status=int(rt.status.cpu().numpy()[0]))
+
+
+def weight_tol(K: int) -> float:
+    """Bound on |w_gpu - w_ref| for the renormalised weights: each of the K
+    fp32 exponentials carries <= 2 ulp, the sum K-1 roundings, the quotient
+    one: (K + 4) * 2^-23 relative, on weights <= 1."""
+    return (K + 4) * 2.0 ** -23

@@ -1,0 +1,376 @@
+"""GPU parity: the HIP path through the C ABI against the CPU reference.
+
+Routing tables must be bit-exact when both sides start from the same fp32
+logits; layer outputs must satisfy max|d| / max|ref| <= 1e-2 (bf16 weights)
+or 3e-2 (fp8 block-128 weights).  Small shapes span several tiles and a
+ragged tail and are compared on every token; the full workload shapes are
+compared on sampled tokens, in the launch configuration the benchmark uses.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from routing_grouped_expert_router_amd import binding as B
+from workloads import configs, generate
+from gpu_util import Built, TOL, rel_err, out_np, route_np, say, weight_tol, DEV
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu_hygiene(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    say(f"[gpu] {request.node.name}")
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+# small shapes: several 64-row weight blocks, several 16-row tiles, ragged tails
+def small_configs():
+    base = configs.tiny()
+    return [
+        base,
+        base.with_(name="mixtral_small_masked", T=37, H=512, I=768, act_dtype="bf16", M_max=37),
+        base.with_(name="mixtral_small_spill", T=37, H=512, I=768, act_dtype="bf16", M_max=5),
+        base.with_(name="dsv3_small_fp8", T=45, H=1024, I=256, E=64, E_phys=64, K=8, n_shared=1,
+                   act_dtype="bf16", w_dtype="fp8", M_max=45 * 8 // 64 * 4),
+        base.with_(name="dsv3_small_fp8_contig", T=45, H=1024, I=256, E=64, E_phys=64, K=8,
+                   n_shared=1, act_dtype="bf16", w_dtype="fp8", layout="contig", BM=16),
+        base.with_(name="prefill_small", T=200, H=512, I=256, E=16, E_phys=16, K=4, n_shared=1,
+                   act_dtype="bf16", layout="contig", BM=128, bias="normal0.5"),
+        base.with_(name="replica_small", T=70, H=256, I=128, E=32, E_phys=40, K=4,
+                   act_dtype="bf16", layout="contig", BM=16, bias="zipf1.1"),
+    ]
+
+
+SMALL = small_configs()
+FULL = [configs.mixtral_decode(1), configs.mixtral_decode(8), configs.mixtral_decode(64),
+        configs.dsv3_decode(32), configs.dsv3_decode(256), configs.dsv3_prefill(),
+        configs.replica_decode()]
+
+ROUTE_KEYS = ["ids", "phys", "row_of", "slot_of", "src_of", "counts", "offsets"]
+
+
+def check_route(b: Built, res: dict):
+    T, K = b.T, b.cfg.K
+    g = route_np(b.layer.rt, T, K)
+    for k in ROUTE_KEYS:
+        assert np.array_equal(g[k], np.asarray(res[k]).reshape(g[k].shape)), k
+    if b.cfg.layout == "masked":
+        assert np.array_equal(g["masked_m"], res["masked_m"])
+        assert np.array_equal(g["spill_off"], res["spill_off"])
+    else:
+        assert np.array_equal(g["pad_off"], res["pad_off"])
+    assert np.abs(g["w"] - res["w"]).max() <= weight_tol(K)
+    assert g["status"] == res["status"], (g["status"], res["status"])
+    return g
+
+
+def test_mfma_operand_layout_probe():
+    """The one-expert, one-token layer is a dense SwiGLU of one row; exercising
+    it at H = I = 128 checks the MFMA lane layout end to end on the smallest
+    case (a wrong D layout scrambles columns; a wrong K pairing scrambles sums)."""
+    cfg = configs.tiny().with_(name="probe", T=1, H=128, I=128, E=1, E_phys=1, K=1, act_dtype="bf16")
+    b = Built(cfg)
+    lg = b.oracle_logits()
+    out = out_np(b.run(lg))
+    ref = b.oracle(lg)["out"]
+    assert rel_err(out, ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_route_and_layer_small(cfg):
+    b = Built(cfg)
+    lg = b.oracle_logits()
+    out = out_np(b.run(lg))
+    res = b.oracle(lg)
+    check_route(b, res)
+    e = rel_err(out, res["out"])
+    say(f"  {cfg.name}: rel err {e:.3e}  status {res['status']}")
+    assert e <= TOL[cfg.w_dtype]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_router_logits(cfg):
+    b = Built(cfg)
+    ref = b.oracle_logits().astype(np.float64)
+    B.moe_router_logits(b.d, b.x, b.wr, b.bias, b.T, b.layer.logits)
+    got = b.layer.logits[: b.T].cpu().numpy().astype(np.float64)
+    from oracle_adapt import to_f64
+    absdot = np.abs(to_f64(b.inp.x)) @ np.abs(to_f64(b.inp.w_router)).T
+    bound = cfg.H * 2.0 ** -24 * absdot + 2.0 ** -24 * np.abs(ref) + 1e-30
+    assert (np.abs(got - ref) <= bound).all(), float((np.abs(got - ref) / bound).max())
+
+
+def test_permute_copies_rows_exactly():
+    cfg = SMALL[3]   # fp8 + shared + masked
+    b = Built(cfg)
+    lg = b.oracle_logits()
+    b.run(lg)
+    g = route_np(b.layer.rt, b.T, cfg.K)
+    xg = b.layer.xg.cpu()
+    xb = b.inp.x.to(torch.bfloat16)
+    for t in range(b.T):
+        for k in range(cfg.K):
+            assert torch.equal(xg[g["slot_of"][t, k]], xb[t])
+    base = B.shared_base(b.d)
+    assert torch.equal(xg[base: base + b.T], xb)
+
+
+def test_f32_activations_cast_to_bf16_in_permute():
+    b = Built(configs.tiny())
+    b.run(b.oracle_logits())
+    g = route_np(b.layer.rt, b.T, 2)
+    xg = b.layer.xg.cpu()
+    assert torch.equal(xg[g["slot_of"][:, 0]], b.inp.x.to(torch.bfloat16))
+
+
+# ---------------------------------------------------------------- routing edge cases
+
+def _route_only(b: Built, lg: np.ndarray, l2p=None, cnt=None):
+    t = torch.from_numpy(np.ascontiguousarray(lg.astype(np.float32))).to(DEV)
+    B.moe_route(b.d, t, lg.shape[0], b.layer.rt, b.layer.ws, l2p, cnt)
+    torch.cuda.synchronize()
+    return route_np(b.layer.rt, lg.shape[0], b.cfg.K)
+
+
+def _ref_route(cfg, lg, p2l=None):
+    ids, w, st = O.topk_route(lg, cfg.K)
+    l2p = cnt = None
+    if p2l is not None:
+        l2p, cnt = O.replica_tables(p2l, cfg.E)
+    phys, st2 = O.assign_physical(ids, cfg.E_phys, l2p, cnt)
+    counts, offsets, row_of, src_of = O.group_rows(phys, cfg.E_phys)
+    res = dict(ids=ids, w=w, phys=phys, counts=counts, offsets=offsets, row_of=row_of, src_of=src_of,
+               status=st | st2)
+    if cfg.layout == "masked":
+        mm, so, slot, st3 = O.layout_masked(counts, offsets, row_of, phys, cfg.M_max, cfg.E_phys)
+        res.update(masked_m=mm, spill_off=so, slot_of=slot)
+        res["status"] |= st3
+    else:
+        po, slot = O.layout_contig(counts, offsets, row_of, phys, cfg.BM)
+        res.update(pad_off=po, slot_of=slot)
+    return res
+
+
+@pytest.mark.parametrize("case", ["ties", "all_equal", "signed_zero", "nan_inf", "K_eq_E", "T1",
+                                  "T65", "spill_all"])
+def test_route_edge_cases(case):
+    cfg = configs.tiny().with_(T=130, M_max=40)
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
+    T = cfg.T
+    if case == "ties":
+        lg = rng.integers(-2, 3, size=(T, cfg.E)).astype(np.float32)
+    elif case == "all_equal":
+        lg = np.full((T, cfg.E), 0.5, np.float32)
+    elif case == "signed_zero":
+        lg = np.where(rng.random((T, cfg.E)) < 0.5, -0.0, 0.0).astype(np.float32)
+        lg[:, 5] = -1.0
+    elif case == "nan_inf":
+        lg = rng.standard_normal((T, cfg.E)).astype(np.float32)
+        lg[3, 2] = np.nan
+        lg[7, :] = np.nan
+        lg[9, 4] = np.inf
+        lg[11, 6] = -np.inf
+    elif case == "K_eq_E":
+        cfg = cfg.with_(K=8)
+        lg = rng.standard_normal((T, cfg.E)).astype(np.float32)
+    elif case == "T1":
+        lg = rng.standard_normal((1, cfg.E)).astype(np.float32)
+    elif case == "T65":
+        lg = rng.standard_normal((65, cfg.E)).astype(np.float32)
+    elif case == "spill_all":
+        cfg = cfg.with_(M_max=1)
+        lg = np.tile(np.arange(cfg.E, dtype=np.float32)[::-1], (T, 1))   # every token picks 0, 1
+    b = Built(cfg)
+    g = _route_only(b, lg)
+    ref = _ref_route(cfg, lg)
+    for k in ROUTE_KEYS:
+        assert np.array_equal(g[k], np.asarray(ref[k]).reshape(g[k].shape)), k
+    if cfg.layout == "masked":
+        assert np.array_equal(g["masked_m"], ref["masked_m"]) and np.array_equal(g["spill_off"], ref["spill_off"])
+    assert g["status"] == ref["status"]
+    fin = np.isfinite(lg).all(axis=1)        # weights of non-finite rows are unspecified
+    assert np.abs(g["w"][fin] - ref["w"][fin]).max(initial=0) <= weight_tol(cfg.K)
+
+
+def test_route_zero_tokens():
+    b = Built(configs.tiny())
+    lg = np.zeros((0, 8), np.float32)
+    B.moe_route(b.d, b.layer.logits, 0, b.layer.rt, b.layer.ws)
+    torch.cuda.synchronize()
+    g = route_np(b.layer.rt, 0, 2)
+    assert (g["counts"] == 0).all() and (g["offsets"] == 0).all() and g["status"] == 0
+    out = b.layer.forward(b.x[:0], 0)
+    torch.cuda.synchronize()
+    assert out.shape[0] == 0
+
+
+@pytest.mark.parametrize("kind", ["out_of_range", "zero_count", "duplicate", "too_many"])
+def test_invalid_replica_map_is_ignored(kind):
+    cfg = configs.tiny().with_(E_phys=10, layout="contig")
+    b = Built(cfg, p2l=np.array([0, 1, 2, 3, 4, 5, 6, 7, 0, 1], np.int32))
+    l2p, cnt = O.replica_tables(b.inp.p2l, cfg.E)
+    if kind == "out_of_range":
+        l2p[0, 1] = 12
+    elif kind == "zero_count":
+        cnt[3] = 0
+    elif kind == "duplicate":
+        l2p[1, 1] = 8
+    else:
+        cnt[0] = 3
+    lg = b.oracle_logits()
+    g = _route_only(b, lg, torch.from_numpy(l2p).to(DEV), torch.from_numpy(cnt).to(DEV))
+    ids, _, _ = O.topk_route(lg, cfg.K)
+    phys, st = O.assign_physical(ids, cfg.E_phys, l2p, cnt)
+    assert st & O.STATUS_BAD_REPLICA and g["status"] & B.MOE_STATUS_BAD_REPLICA
+    assert np.array_equal(g["phys"], phys) and np.array_equal(g["phys"], ids)
+
+
+# ---------------------------------------------------------------- layer-level properties
+
+def test_layouts_give_identical_outputs():
+    cfg = SMALL[1]
+    a = Built(cfg, layout="masked", M_max=3)     # heavy spill
+    c = Built(cfg, layout="contig")
+    lg = a.oracle_logits()
+    oa, oc = a.run(lg).clone(), c.run(lg).clone()
+    assert int(a.layer.rt.status.item()) & B.MOE_STATUS_SPILL
+    assert torch.equal(oa, oc)
+
+
+def test_replica_map_leaves_output_unchanged():
+    cfg = SMALL[6]
+    with_map = Built(cfg)
+    no_map = Built(cfg.with_(E_phys=cfg.E))
+    lg = with_map.oracle_logits()
+    a, b = with_map.run(lg).clone(), no_map.run(lg).clone()
+    g = route_np(with_map.layer.rt, cfg.T, cfg.K)
+    assert (g["phys"] >= cfg.E).any()            # replicas really used
+    assert torch.equal(a, b)
+
+
+def test_determinism_bit_identical():
+    cfg = SMALL[3]
+    b = Built(cfg)
+    o1 = b.run(None).clone()
+    t1 = {k: v.copy() for k, v in route_np(b.layer.rt, b.T, cfg.K).items() if isinstance(v, np.ndarray)}
+    o2 = b.run(None).clone()
+    t2 = route_np(b.layer.rt, b.T, cfg.K)
+    assert torch.equal(o1, o2)
+    for k, v in t1.items():
+        assert np.array_equal(v, t2[k]), k
+
+
+def test_fewer_tokens_than_T_max():
+    cfg = SMALL[1]
+    b = Built(cfg, T=9)
+    lg = b.oracle_logits()
+    out = out_np(b.run(lg))
+    res = b.oracle(lg)
+    check_route(b, res)
+    assert rel_err(out, res["out"]) <= TOL["bf16"]
+
+
+def test_forward_chain_with_gpu_router():
+    """GPU router -> route -> ... compared with the reference on its own
+    logits.  Where the two fp32 logit vectors order a near-tie differently
+    the token is skipped, and such tokens must be rare and genuine ties."""
+    for cfg in (SMALL[0], SMALL[3], SMALL[5]):
+        b = Built(cfg)
+        out = out_np(b.run(None))
+        res = b.oracle()
+        g = route_np(b.layer.rt, b.T, cfg.K)
+        same = (np.sort(g["ids"], 1) == np.sort(res["ids"], 1)).all(1)
+        lg = res["logits"].astype(np.float64)
+        for t in np.nonzero(~same)[0]:
+            srt = np.sort(lg[t])[::-1]
+            assert srt[cfg.K - 1] - srt[cfg.K] <= 1e-5 * max(1.0, abs(srt[0])), t
+        assert same.mean() >= 0.95
+        assert rel_err(out[same], res["out"][same]) <= TOL[cfg.w_dtype]
+
+
+class _Guarded:
+    """Device buffers with guard bands before and after; writes outside the
+    documented extent change the guard bytes."""
+    G = 4096
+
+    def __init__(self):
+        self.bufs = []
+
+    def make(self, n, dtype):
+        esz = torch.tensor([], dtype=dtype).element_size()
+        g = self.G // esz
+        full = torch.full((n + 2 * g,), 0, dtype=dtype, device=DEV)
+        full.view(torch.uint8)[:] = 0xA5
+        self.bufs.append((full, g, n))
+        return full[g: g + n]
+
+    def intact(self):
+        for full, g, n in self.bufs:
+            u = full.view(torch.uint8)
+            esz = full.element_size()
+            if not (bool((u[: g * esz] == 0xA5).all()) and bool((u[(g + n) * esz:] == 0xA5).all())):
+                return False
+        return True
+
+
+def test_canaries_around_every_buffer():
+    for cfg in (SMALL[2], SMALL[4], SMALL[6]):
+        b = Built(cfg)
+        d, T, K = b.d, b.T, cfg.K
+        gd = _Guarded()
+        rt = B.RouteTables(d, DEV)
+        TK = T * K
+        for name, n, dt in [("topk_ids", TK, torch.int32), ("topk_w", TK, torch.float32),
+                            ("topk_phys", TK, torch.int32), ("row_of", TK, torch.int32),
+                            ("slot_of", TK, torch.int32), ("src_of", TK, torch.int32),
+                            ("counts", d.E_phys, torch.int32), ("offsets", d.E_phys + 1, torch.int32),
+                            ("masked_m", d.E_phys, torch.int32), ("spill_off", d.E_phys + 1, torch.int32),
+                            ("pad_off", d.E_phys + 1, torch.int32), ("status", 1, torch.int32)]:
+            setattr(rt, name, gd.make(n, dt))
+        rt.c = B.moe_route_t(*[B._ptr(getattr(rt, f)) for f, _ in B.moe_route_t._fields_])
+        rows = B.buffer_rows(d)
+        ws = gd.make(B.route_workspace_bytes(d), torch.uint8)
+        xg = gd.make(rows * d.H, torch.bfloat16)
+        h = gd.make(rows * d.I, torch.bfloat16)
+        y = gd.make(B.y_bytes(d, T), torch.uint8)
+        out = gd.make(T * d.H, torch.bfloat16)
+        logits = gd.make(T * d.E, torch.float32)
+        L = b.layer
+        B.moe_router_logits(d, b.x, b.wr, b.bias, T, logits)
+        B.moe_route(d, logits, T, rt, ws, b.l2p, b.rcount)
+        B.moe_permute(d, b.x, T, rt, xg)
+        B.moe_grouped_ffn(d, L.weights, rt, T, xg, h, y)
+        B.moe_combine(d, rt, T, y, out)
+        torch.cuda.synchronize()
+        assert gd.intact(), cfg.name
+        ref = L.forward(b.x, T)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(T, d.H), ref)
+
+
+# ---------------------------------------------------------------- full workload shapes
+
+def _sample(T, n, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=min(n, T), replace=False)]))
+
+
+@pytest.mark.parametrize("cfg", FULL, ids=lambda c: c.name)
+def test_full_size_sampled(cfg):
+    b = Built(cfg)
+    say(f"  built {cfg.name}")
+    lg = b.oracle_logits()
+    out = out_np(b.run(lg))
+    toks = _sample(b.T, 6 if cfg.T > 64 else 4)
+    res = b.oracle(lg, tokens=toks)
+    check_route(b, res)
+    e = rel_err(out[toks], res["out"])
+    say(f"  {cfg.name}: sampled tokens {list(toks)} rel err {e:.3e} status {res['status']}")
+    assert e <= TOL[cfg.w_dtype]

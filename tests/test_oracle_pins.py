@@ -224,13 +224,19 @@ def test_replica_round_robin_split():
         assert got == [reps[j % count[l]] for j in range(len(toks))]
 
 
-def test_replica_invalid_entry_falls_back_home():
+@pytest.mark.parametrize("l2p,count", [
+    ([[0, 9], [1, -1]], [2, 1]),      # slot outside [0, E_phys)
+    ([[0, 2], [1, -1]], [2, 0]),      # a logical expert with no replica
+    ([[0, 2], [2, -1]], [2, 1]),      # slot 2 listed twice
+    ([[0, 2], [1, -1]], [3, 1]),      # count above max_replicas
+])
+def test_replica_invalid_map_is_ignored(l2p, count):
     ids = np.array([[0, 1], [1, 0]], np.int32)
-    l2p = np.array([[0, 9], [1, -1]], np.int32)
-    count = np.array([2, 0], np.int32)
-    phys, st = O.assign_physical(ids, 3, l2p, count)
+    phys, st = O.assign_physical(ids, 3, np.array(l2p, np.int32), np.array(count, np.int32))
     assert st & O.STATUS_BAD_REPLICA
     assert phys.tolist() == [[0, 1], [1, 0]]
+    ok, st = O.assign_physical(ids, 3, np.array([[0, 2], [1, -1]], np.int32), np.array([2, 1], np.int32))
+    assert st == 0 and ok.tolist() == [[0, 1], [1, 2]]
 
 
 # ---------------------------------------------------------------- FFN + combine

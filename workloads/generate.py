@@ -139,12 +139,25 @@ class MoEInputs:
     wdevice: str = "cpu"                 # where expert weights are drawn
     _cache: dict = field(default_factory=dict, repr=False)
 
+    def prefetch(self, ids) -> None:
+        """Keeps the CPU copies of these logical experts (and the shared one)
+        resident, so later reads do no generation or device copy."""
+        pinned = self._cache.setdefault("pinned", {})
+        for l in ids:
+            if l not in pinned:
+                pinned[l] = _to_cpu(make_expert(self.cfg, _TAG_EXPERT, int(l), self.wdevice))
+        self.shared()
+
     def expert(self, l: int) -> ExpertWeights:
         """Weights of logical expert l as CPU tensors (drawn on ``wdevice``,
         regenerated on demand, small LRU)."""
+        pinned = self._cache.get("pinned", {})
+        if l in pinned:
+            return pinned[l]
         if l not in self._cache:
-            if len(self._cache) >= 4:
-                self._cache.pop(next(iter(self._cache)))
+            lru = [k for k in self._cache if k not in ("pinned", "shared")]
+            if len(lru) >= 4:
+                self._cache.pop(lru[0])
             self._cache[l] = _to_cpu(make_expert(self.cfg, _TAG_EXPERT, l, self.wdevice))
         return self._cache[l]
 
