@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--workload", default="mixtral_decode_b64")
     ap.add_argument("--no-sweep", action="store_true", help="time only the named workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU reference timing")
+    ap.add_argument("--row-major", action="store_true",
+                    help="stream the row-major weights instead of the packed layout")
     return ap.parse_args()
 
 
@@ -53,7 +55,7 @@ def weight_bytes_per_slot(cfg):
 
 
 class Setup:
-    def __init__(self, cfg):
+    def __init__(self, cfg, packed=True):
         import torch
         from routing_grouped_expert_router_amd import binding as B
         from workloads import generate
@@ -68,7 +70,12 @@ class Setup:
             max_rep = int(counts.max())
             l2p_t, rc_t = B.moe_replica_map_from_p2l(self.inp.p2l, cfg.E, max_rep)
             l2p, rc = l2p_t.cuda(), rc_t.cuda()
-        self.d = B.Desc.from_config(cfg, max_replicas=max_rep)
+        self.d = B.Desc.from_config(cfg, max_replicas=max_rep, w_packed=int(packed))
+        if packed:   # one-time repack into the streamed layout; free the row-major copy
+            w = B.pack_expert_weights(self.d, self.w)
+            del self.w
+            torch.cuda.empty_cache()
+            self.w = w
         self.x = self.inp.x.cuda()
         self.wr = self.inp.w_router.cuda()
         self.bias = None if self.inp.bias is None else self.inp.bias.cuda()
@@ -89,6 +96,18 @@ class Setup:
         B.moe_expert_down(d, L.weights, L.rt, T, L.h, L.y)
         B.moe_combine(d, L.rt, T, L.y, L.out)
 
+    def gate_up_flops(self):
+        """Algorithmic FLOPs of the gate/up kernel: 2 * rows * 2I * H over the
+        token rows (T*K routed + n_shared*T shared); pad rows not counted."""
+        cfg = self.cfg
+        rows = cfg.T * cfg.K + cfg.n_shared * cfg.T
+        return 2.0 * rows * 2 * cfg.I * cfg.H
+
+    def layer_flops(self):
+        cfg = self.cfg
+        rows = cfg.T * cfg.K + cfg.n_shared * cfg.T
+        return 2.0 * rows * 3 * cfg.I * cfg.H + 2.0 * cfg.T * cfg.E * cfg.H
+
     def touched(self):
         """(touched slots, touched routed-weight bytes, gate/up bytes, all bytes)"""
         import numpy as np
@@ -104,9 +123,12 @@ class Setup:
         return slots, routed, gu, total
 
 
-def time_workload(cfg, steps, warmup):
+def time_workload(cfg, steps, warmup, packed=True):
+    """Eager steps (HIP events around the gate/up kernel on the launch
+    stream), then the same step captured once in a HIP graph and replayed
+    ``steps`` times (the layer latency reported)."""
     import torch
-    s = Setup(cfg)
+    s = Setup(cfg, packed)
     for _ in range(warmup):
         s.step()
     torch.cuda.synchronize()
@@ -115,20 +137,56 @@ def time_workload(cfg, steps, warmup):
            for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     start.record(stream)
     for i in range(steps):
         s.step(evs[i])
     end.record(stream)
     torch.cuda.synchronize()
+    eager_ms = start.elapsed_time(end) / steps
+    gu_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    ref = s.layer.out.clone()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        s.step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(s.layer.out, ref), "graph replay differs from the eager step"
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(end) / steps
-    gu_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
     slots, routed, gu_bytes, total = s.touched()
     status = int(s.layer.rt.status.item())
-    res = dict(cfg=cfg, ms=ms, gu_ms=gu_ms, wall=wall, slots=slots, routed_bytes=routed,
-               gu_bytes=gu_bytes, total_bytes=total, status=status, setup=s)
+    res = dict(cfg=cfg, ms=ms, eager_ms=eager_ms, gu_ms=gu_ms, wall=wall, slots=slots,
+               routed_bytes=routed, gu_bytes=gu_bytes, total_bytes=total, status=status, setup=s,
+               gu_flops=s.gate_up_flops(), layer_flops=s.layer_flops())
+    del graph
     return res
+
+
+PREFILL_MIN_T = 1024   # token counts from here on are timed against the MFMA peak
+
+
+def roofline(cfg, r):
+    """The dominant kernel (expert gate/up + SwiGLU) against its bound: HBM
+    bytes for decode, bf16 MFMA FLOPs for prefill."""
+    kernel = "ffn_stream gate/up (W1+W3, SwiGLU)"
+    if cfg.T >= PREFILL_MIN_T:
+        tf = r["gu_flops"] / (r["gu_ms"] * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": kernel, "achieved": round(tf, 1),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                "traffic": None, "kernel_us": round(r["gu_ms"] * 1e3, 2),
+                "algorithmic_flops": r["gu_flops"]}
+    gbs = r["gu_bytes"] / (r["gu_ms"] * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel_us": round(r["gu_ms"] * 1e3, 2), "algorithmic_bytes": r["gu_bytes"]}
 
 
 def cpu_baseline(s, budget_s=30.0):
@@ -179,9 +237,11 @@ def main():
     results = {}
     for n in names:
         c = configs.by_name(n)
-        r = time_workload(c, args.steps, args.warmup)
+        r = time_workload(c, args.steps, args.warmup, packed=not args.row_major)
         results[n] = r
-        print(f"# {n}: {r['ms']*1e3:.1f} us/layer, gate/up {r['gu_ms']*1e3:.1f} us, "
+        print(f"# {n}: {r['ms']*1e3:.1f} us/layer (graph), {r['eager_ms']*1e3:.1f} eager, "
+              f"gate/up {r['gu_ms']*1e3:.1f} us ({r['gu_flops']/(r['gu_ms']*1e-3)/1e12:.0f} TFLOP/s), "
+              f"layer {r['layer_flops']/(r['ms']*1e-3)/1e12:.0f} TFLOP/s, "
               f"slots {r['slots']}, touched {r['total_bytes']/1e9:.3f} GB -> "
               f"{r['total_bytes']/(r['ms']*1e-3)/1e9:.0f} GB/s, status {r['status']}",
               file=sys.stderr, flush=True)
@@ -191,7 +251,6 @@ def main():
     head = results[cfg.name]
     lat_us = head["ms"] * 1e3
     gb_s = head["total_bytes"] / (head["ms"] * 1e-3) / 1e9
-    gu_gbs = head["gu_bytes"] / (head["gu_ms"] * 1e-3) / 1e9
     cpu = None
     if not args.no_cpu:
         us, sample, cores = cpu_baseline(head["setup"])
@@ -212,17 +271,19 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
                    "E_phys": cfg.E_phys, "K": cfg.K, "n_shared": cfg.n_shared,
-                   "layout": cfg.layout, "M_max": cfg.M_max, "w_dtype": cfg.w_dtype},
+                   "layout": cfg.layout, "M_max": cfg.M_max, "w_dtype": cfg.w_dtype,
+                   "weights": "row-major" if args.row_major else "packed"},
         "expert_weight_hbm_gbs": round(gb_s, 1),
+        "layer_tflops": round(head["layer_flops"] / (head["ms"] * 1e-3) / 1e12, 2),
         "touched_slots": head["slots"],
         "touched_bytes": head["total_bytes"],
-        "roofline": {"bound": "hbm", "kernel": "ffn_stream gate/up (W1+W3, SwiGLU)",
-                     "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel_us": round(head["gu_ms"] * 1e3, 2),
-                     "algorithmic_bytes": head["gu_bytes"]},
+        "roofline": roofline(cfg, head),
         "cpu_baseline": cpu,
+        "eager_latency_us": round(head["eager_ms"] * 1e3, 2),
+        "timing": "HIP graph of one layer step replayed `steps` times between HIP events "
+                  "on the launch stream; eager_latency_us is the same step launched directly",
         "batches": {n: {"latency_us": round(r["ms"] * 1e3, 2),
+                        "eager_latency_us": round(r["eager_ms"] * 1e3, 2),
                         "gbs": round(r["total_bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
                         "gate_up_us": round(r["gu_ms"] * 1e3, 2),
                         "touched_slots": r["slots"]} for n, r in results.items()},

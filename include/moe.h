@@ -84,7 +84,7 @@ typedef struct {
   int32_t T_max;        /* largest token count any call will pass */
   int32_t H;            /* hidden size; multiple of 128 */
   int32_t I;            /* expert intermediate size; multiple of 128 */
-  int32_t E;            /* logical routed experts, 1..4096 */
+  int32_t E;            /* logical routed experts, 1..1024 */
   int32_t E_phys;       /* physical slots (>= E; == E without replicas) */
   int32_t K;            /* experts per token, 1..min(E, 16) */
   int32_t n_shared;     /* 0 or 1 always-on shared expert */
@@ -95,6 +95,8 @@ typedef struct {
   int32_t layout;       /* moe_layout_t */
   int32_t M_max;        /* masked rows per slot, >= 1 (MOE_MASKED) */
   int32_t BM;           /* segment padding, >= 1 (MOE_CONTIG) */
+  int32_t w_packed;     /* 0: expert weights row-major [out, in];
+                           1: packed by moe_pack_weights */
 } moe_desc_t;
 
 /* Routing tables, all device int32/float/uint32 arrays, caller-allocated.
@@ -115,7 +117,8 @@ typedef struct {
   uint32_t* status;    /* [1] MOE_STATUS_* bits of the last moe_route */
 } moe_route_t;
 
-/* Expert weights, device memory, layout [out, in] (row = output feature):
+/* Expert weights, device memory.  Row-major layout [out, in] (row = output
+ * feature), or the packed layout of moe_pack_weights when desc->w_packed:
  *   w1, w3: [E_phys, I, H]   (gate, up)     w2: [E_phys, H, I]   (down)
  *   bf16, or E4M3FN bytes with fp32 scales
  *   s1, s3: [E_phys, I/128, H/128]          s2: [E_phys, H/128, I/128]
@@ -225,6 +228,20 @@ moe_status_t moe_forward(const moe_desc_t* d, const void* x, const void* w_route
                          const moe_weights_t* w, int32_t T, float* logits,
                          const moe_route_t* r, void* ws, size_t ws_bytes,
                          void* xg, void* h, void* y, void* out, hipStream_t stream);
+
+/* ---- weight layout ------------------------------------------------------ */
+
+/* Repacks G expert matrices from row-major [G, N, Kdim] (row = output
+ * feature) into the layout the expert kernels stream: for every 16-row panel
+ * and 128-wide K block, the 16-byte pieces each lane loads, in lane order, so
+ * every load instruction of a wave reads 1 KiB of contiguous memory.
+ * Same size as the input.  which = 0 for W1 or W3 (N = I, Kdim = H), 1 for
+ * W2 (N = H, Kdim = I); element type from desc->w_dtype (fp8 scales are not
+ * repacked).  src, dst: device, distinct; a one-time step, not on the hot
+ * path.  Weights are an input the pages treat as given; packing changes
+ * only their order in memory. */
+moe_status_t moe_pack_weights(const moe_desc_t* d, int32_t which, int32_t G, const void* src,
+                              void* dst, hipStream_t stream);
 
 /* ---- replica maps (host, pure) ------------------------------------------- */
 

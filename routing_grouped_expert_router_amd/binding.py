@@ -25,14 +25,14 @@ EXPORTED = [
     "moe_status_string", "moe_check_desc", "moe_route_workspace_bytes", "moe_buffer_rows",
     "moe_shared_base", "moe_down_splits", "moe_y_bytes", "moe_router_logits", "moe_route",
     "moe_permute", "moe_expert_gate_up", "moe_expert_down", "moe_grouped_ffn", "moe_combine",
-    "moe_forward", "moe_replica_map_from_p2l",
+    "moe_forward", "moe_pack_weights", "moe_replica_map_from_p2l",
 ]
 
 
 class moe_desc_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T_max", "H", "I", "E", "E_phys", "K", "n_shared", "max_replicas",
-        "act_dtype", "w_dtype", "layout", "M_max", "BM")]
+        "act_dtype", "w_dtype", "layout", "M_max", "BM", "w_packed")]
 
 
 _P = ctypes.c_void_p
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "moe_combine": (ctypes.c_int, [D, R, i32, _P, _P, _P]),
             "moe_forward": (ctypes.c_int, [D, _P, _P, _P, _P, _P, W, i32, _P, R, _P, sz,
                                            _P, _P, _P, _P, _P]),
+            "moe_pack_weights": (ctypes.c_int, [D, i32, i32, _P, _P, _P]),
             "moe_replica_map_from_p2l": (ctypes.c_int, [_P, i32, i32, i32, _P, _P]),
         }
         for name, (res, args) in sig.items():
@@ -126,18 +127,19 @@ class Desc:
     layout: int = MOE_CONTIG
     M_max: int = 1
     BM: int = 16
+    w_packed: int = 0
 
     def c(self) -> moe_desc_t:
         return moe_desc_t(*[int(getattr(self, f)) for f, _ in moe_desc_t._fields_])
 
     @staticmethod
-    def from_config(cfg, max_replicas: int = 1) -> "Desc":
+    def from_config(cfg, max_replicas: int = 1, w_packed: int = 0) -> "Desc":
         return Desc(T_max=cfg.T, H=cfg.H, I=cfg.I, E=cfg.E, E_phys=cfg.E_phys, K=cfg.K,
                     n_shared=cfg.n_shared, max_replicas=max_replicas,
                     act_dtype=MOE_F32 if cfg.act_dtype == "f32" else MOE_BF16,
                     w_dtype=MOE_BF16 if cfg.w_dtype == "bf16" else MOE_FP8E4M3_B128,
                     layout=MOE_MASKED if cfg.layout == "masked" else MOE_CONTIG,
-                    M_max=max(1, cfg.M_max), BM=max(1, cfg.BM))
+                    M_max=max(1, cfg.M_max), BM=max(1, cfg.BM), w_packed=w_packed)
 
 
 # ---- sizing -------------------------------------------------------------------
@@ -238,6 +240,26 @@ def moe_expert_down(d: Desc, w: Weights, rt: RouteTables, T, h, y, stream=None):
 def moe_combine(d: Desc, rt: RouteTables, T, y, out, stream=None):
     _check(lib().moe_combine(ctypes.byref(d.c()), ctypes.byref(rt.c), T, _ptr(y), _ptr(out),
                              _stream(stream)), "moe_combine")
+
+
+def moe_pack_weights(d: Desc, which: int, src, dst, stream=None):
+    """Packs G row-major expert matrices (src [G, N, Kdim]) into dst (same
+    shape and dtype) in the layout the expert kernels stream."""
+    G = src.shape[0] if src.dim() == 3 else 1
+    _check(lib().moe_pack_weights(ctypes.byref(d.c()), which, G, _ptr(src), _ptr(dst),
+                                  _stream(stream)), "moe_pack_weights")
+
+
+def pack_expert_weights(d: Desc, weights: dict) -> dict:
+    """A copy of a weight dict (w1, w3 [G, I, H], w2 [G, H, I], fp8 scales)
+    with the matrices packed; scales are shared unchanged."""
+    out = dict(weights)
+    for name, which in (("w1", 0), ("w3", 0), ("w2", 1)):
+        src = weights[name].contiguous()
+        dst = torch.empty_like(src)
+        moe_pack_weights(d, which, src, dst)
+        out[name] = dst
+    return out
 
 
 def moe_replica_map_from_p2l(p2l, E: int, max_replicas: int):

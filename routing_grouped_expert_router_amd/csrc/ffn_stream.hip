@@ -1,66 +1,87 @@
-// Streaming grouped GEMM for decode-sized groups on gfx950 (CDNA4).
+// Streaming grouped GEMM for decode-sized expert groups on gfx950 (CDNA4).
 //
 // One workgroup (4 waves) owns 64 output features (weight rows) of one group
-// (a physical expert slot, the shared expert, or the router) and all of that
-// group's token rows.  Decode moves far more weight bytes than activation
-// bytes ("推理 INFRA 方法论(5)": the weight traffic is
-// [C(B) W_routed + W_shared] * bpp), so the design streams every weight byte
-// from HBM exactly once, straight into registers in the MFMA operand layout,
-// and keeps the small activation tile in LDS where the four waves share it.
+// (a physical expert slot or the shared expert) and all of that group's
+// token rows.  Decode moves far more weight bytes than activation bytes
+// ("推理 INFRA 方法论(5)", C(B) section: the weight traffic is
+// [C(B) W_routed + W_shared] * bpp), so every weight byte is streamed from
+// HBM exactly once, straight into registers in the MFMA operand layout, while
+// the small activation tile sits in LDS where the four waves share it.
 //
-//  * Weights W [N, Kdim] (row = output feature, K contiguous).  Lane l of a
-//    wave loads row n0 + l%16; the four lane groups l/16 take consecutive
-//    16-byte pieces, so each load instruction reads 64 contiguous bytes of
-//    16 rows.  The next 128-wide K step is loaded while the current one is
-//    multiplied.
+//  * Weights, per 16-row panel and 128-wide K step, are read by one wave as
+//    NI 16-byte loads per lane (bf16: NI = 4, fp8: NI = 2).  In the packed
+//    layout (moe_pack_weights) each load instruction reads 1 KiB of
+//    contiguous memory and a panel is one contiguous stream; in the row-major
+//    [out, in] layout each instruction reads 64 bytes of 16 rows.  Two K steps
+//    are in flight while the current one is multiplied (three register
+//    buffers in rotation).
 //  * Activations X [rows, Kdim] bf16: the group's row tiles (16 rows each,
 //    up to MT tiles per pass) are staged per K step in a double-buffered LDS
 //    tile and read as the MFMA B operand.
-//  * v_mfma_f32_16x16x32_bf16 computes D[n, m] = sum_k W[n, k] X[m, k].
-//  * Masked layout ("推理 INFRA 方法论(5)", DeepGEMM section): the valid rows of
-//    slot p are masked_m[p] rows at p*M_max, plus any spill rows; row tiles
-//    that hold no valid row are never formed, so a slot without tokens
-//    issues no weight load and no MFMA.
+//  * v_mfma_f32_16x16x32_bf16 computes D[n, m] = sum_k W[n, k] X[m, k]; lane l
+//    supplies weight row l % 16 and activation row l % 16 with the K values
+//    of lane group l / 16, and receives D rows 4*(l/16)+0..3 of column l % 16.
+//  * Masked layout ("推理 INFRA 方法论(5)", DeepGEMM section): the valid rows
+//    of slot p are masked_m[p] rows at p*M_max, plus any spill rows; a row
+//    tile with no valid row is never formed, so a slot without tokens issues
+//    no weight load and no MFMA.
 //  * fp8 weights (OCP E4M3FN + one fp32 scale per 128x128 block): 16 bytes
 //    become two bf16x8 operands by an exact conversion; the four MFMAs of a
-//    128-wide K block start from zero and their sum is scaled and added to an
-//    fp32 accumulator (the same page's two-level accumulation: promote every
+//    128-wide K block start from zero and their sum is scaled into an fp32
+//    accumulator (the same section's two-level accumulation: promote every
 //    128 K with the block scale).
-//  * MODE_GATEUP: both W1 (gate) and W3 (up); epilogue h = SiLU(g) * u in
-//    bf16.  MODE_DOWN: W2; bf16 output, or fp32 partials when K is split
-//    over grid.z.  MODE_ROUTER: router weight [E, H], fp32 logits + bias.
+//  * MODE_GATEUP: W1 (gate) and W3 (up); epilogue h = SiLU(g) * u in bf16.
+//    MODE_DOWN: W2; bf16 output, or fp32 partial planes when K is split over
+//    grid.z (summed in split order by the combine).
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
-constexpr int kThreads = 256;      // 4 waves
-constexpr int kBN = 64;            // weight rows per workgroup
-constexpr int kKS = 128;           // K per pipeline step
+constexpr int kThreads = 256;        // 4 waves
+constexpr int kBN = 64;              // weight rows per workgroup
+constexpr int kKS = 128;             // K per pipeline step
 constexpr int kLdsStride = kKS + 8;  // bf16 elements per LDS row (pad vs bank conflicts)
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
 template <bool FP8>
 struct WFrag {
-  // bf16: 4 x 16 B per 128 K (K offsets 32j + 8*lg); fp8: 2 x 16 B (64i + 16*lg)
-  static constexpr int N = FP8 ? 2 : 4;
-  u32x4 v[N];
+  static constexpr int NI = FP8 ? 2 : 4;
+  u32x4 v[NI];
+};
+
+// Byte addressing of one wave's weight stream:
+//   address(kstep, i) = base + kstep * step_bytes + i * instr_bytes + lane_bytes
+struct WStream {
+  const char* base;
+  int step_bytes, instr_bytes, lane_bytes;
 };
 
 template <bool FP8>
-__device__ __forceinline__ void load_w(WFrag<FP8>& f, const void* wrow, int k0, int lg, bool ok) {
-  if (FP8) {
-    const uint8_t* p = static_cast<const uint8_t*>(wrow) + k0 + 16 * lg;
+__device__ __forceinline__ void load_w(WFrag<FP8>& f, const WStream& w, int kstep) {
+  const char* p = w.base + (int64_t)kstep * w.step_bytes + w.lane_bytes;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      f.v[i] = ok ? *reinterpret_cast<const u32x4*>(p + 64 * i) : u32x4{0, 0, 0, 0};
+  for (int i = 0; i < WFrag<FP8>::NI; ++i) f.v[i] = *reinterpret_cast<const u32x4*>(p + i * w.instr_bytes);
+}
+
+template <bool FP8, bool PACKED>
+__device__ __forceinline__ WStream make_stream(const void* Wg, int n_w0, int lane, int Kdim) {
+  constexpr int wbytes = FP8 ? 1 : 2;
+  WStream s;
+  if (PACKED) {
+    // panel n_w0/16 holds 16*Kdim weights; each K step is one block of 16*128
+    s.base = static_cast<const char*>(Wg) + (int64_t)(n_w0 / 16) * 16 * Kdim * wbytes;
+    s.step_bytes = 16 * kKS * wbytes;
+    s.instr_bytes = 1024;
+    s.lane_bytes = 16 * lane;
   } else {
-    const uint16_t* p = static_cast<const uint16_t*>(wrow) + k0 + 8 * lg;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      f.v[j] = ok ? *reinterpret_cast<const u32x4*>(p + 32 * j) : u32x4{0, 0, 0, 0};
+    s.base = static_cast<const char*>(Wg) + (int64_t)(n_w0 + (lane & 15)) * Kdim * wbytes;
+    s.step_bytes = kKS * wbytes;
+    s.instr_bytes = 64;
+    s.lane_bytes = 16 * (lane >> 4);
   }
+  return s;
 }
 
 template <int MT>
@@ -77,7 +98,7 @@ __device__ __forceinline__ void tile_rows(int tile, int64_t s0, int c0, int nt0,
   else { const int u = tile - nt0; start = s1 + 16 * u; valid = min(16, c1 - 16 * u); }
 }
 
-template <bool FP8, int MODE, int MT>
+template <bool FP8, int MODE, int MT, bool PACKED>
 __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
   constexpr bool TWO = MODE == MODE_GATEUP;
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT * 16][kLdsStride];
@@ -88,9 +109,8 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
   // ---- the group's row segments
   int64_t s0 = 0, s1 = 0;
   int c0 = 0, c1 = 0;
-  const bool shared = (MODE != MODE_ROUTER) && g == a.E_phys;
-  if (MODE == MODE_ROUTER) { c0 = a.T; }
-  else if (shared) { s0 = a.shared_base; c0 = a.T; }
+  const bool shared = g == a.E_phys;
+  if (shared) { s0 = a.shared_base; c0 = a.T; }
   else if (a.layout == MOE_MASKED) {
     const int mm = a.masked_m[g];
     s0 = (int64_t)g * a.M_max; c0 = mm;
@@ -104,13 +124,11 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
   const int n_w0 = blockIdx.x * kBN + wave * 16;   // first weight row of this wave
-  const int nrow = n_w0 + lr;
-  const bool nok = nrow < a.N;
   const int Kdim = a.Kdim;
   const int kb_per_row = Kdim / kKS;
 
   // ---- weights of this group
-  const size_t wbytes = FP8 ? 1 : 2;
+  constexpr int wbytes = FP8 ? 1 : 2;
   const void* Wg;
   const void* W3g = nullptr;
   const float* Sg = nullptr;
@@ -118,21 +136,19 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
   if (shared) {
     Wg = a.SW; W3g = a.SW3; Sg = a.SS; S3g = a.SS3;
   } else {
-    const int64_t gi = (MODE == MODE_ROUTER) ? 0 : g;
-    Wg = static_cast<const char*>(a.W) + gi * (int64_t)a.N * Kdim * wbytes;
-    if (TWO) W3g = static_cast<const char*>(a.W3) + gi * (int64_t)a.N * Kdim * wbytes;
+    Wg = static_cast<const char*>(a.W) + (int64_t)g * a.N * Kdim * wbytes;
+    if (TWO) W3g = static_cast<const char*>(a.W3) + (int64_t)g * a.N * Kdim * wbytes;
     if (FP8) {
-      Sg = a.S + gi * (int64_t)(a.N / 128) * kb_per_row;
-      if (TWO) S3g = a.S3 + gi * (int64_t)(a.N / 128) * kb_per_row;
+      Sg = a.S + (int64_t)g * (a.N / 128) * kb_per_row;
+      if (TWO) S3g = a.S3 + (int64_t)g * (a.N / 128) * kb_per_row;
     }
   }
-  const void* wrow = static_cast<const char*>(Wg) + (int64_t)(nok ? nrow : 0) * Kdim * wbytes;
-  const void* w3row = TWO ? static_cast<const char*>(W3g) + (int64_t)nrow * Kdim * wbytes : nullptr;
+  const WStream w1s = make_stream<FP8, PACKED>(Wg, n_w0, lane, Kdim);
+  const WStream w3s = TWO ? make_stream<FP8, PACKED>(W3g, n_w0, lane, Kdim) : w1s;
   const int sb_row = (n_w0 / 128) * kb_per_row;    // scale row of this wave's 16 rows
 
   // ---- K range of this split
-  const int steps_all = kb_per_row;
-  const int steps = steps_all / a.ksplit;
+  const int steps = kb_per_row / a.ksplit;
   const int kstep0 = ks * steps;
 
   // staging assignment: thread -> (row r of a 16-row tile, 16-byte chunk c)
@@ -147,15 +163,19 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
       if (m < ps.n) tile_rows(tile0 + m, s0, c0, nt0, s1, c1, ps.start[m], ps.valid[m]);
     }
 
+    // Activation rows, clamped into the tile's valid rows (rows past the valid
+    // count only feed MFMA columns that are never stored).  The loads sit
+    // outside any divergent branch so the compiler never waits on them early.
+    const uint16_t* xsrc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int64_t row = (m < ps.n && ps.valid[m] > 0) ? ps.start[m] + min(sr, ps.valid[m] - 1) : s0;
+      xsrc[m] = a.X + row * a.ldx + 8 * sc;
+    }
     auto load_x = [&](int kstep, u32x4* xr) {
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        xr[m] = u32x4{0, 0, 0, 0};
-        if (m < ps.n && sr < ps.valid[m]) {
-          const uint16_t* src = a.X + (ps.start[m] + sr) * a.ldx + (int64_t)kstep * kKS + 8 * sc;
-          xr[m] = *reinterpret_cast<const u32x4*>(src);
-        }
-      }
+      for (int m = 0; m < MT; ++m)
+        xr[m] = *reinterpret_cast<const u32x4*>(xsrc[m] + (int64_t)kstep * kKS);
     };
     auto store_x = [&](int buf, const u32x4* xr) {
 #pragma unroll
@@ -167,29 +187,11 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) { acc[m] = f32x4{0, 0, 0, 0}; acc3[m] = f32x4{0, 0, 0, 0}; }
 
-    WFrag<FP8> wa, wb;
-    load_w<FP8>(wa, wrow, kstep0 * kKS, lg, nok);
-    if (TWO) load_w<FP8>(wb, w3row, kstep0 * kKS, lg, true);
-    {
-      u32x4 xr[MT];
-      load_x(kstep0, xr);
-      store_x(0, xr);
-    }
-    __syncthreads();
-
-    for (int s = 0; s < steps; ++s) {
-      const int buf = s & 1;
-      const bool more = s + 1 < steps;
-      WFrag<FP8> na, nb;
-      u32x4 xr[MT];
-      if (more) {
-        load_w<FP8>(na, wrow, (kstep0 + s + 1) * kKS, lg, nok);
-        if (TWO) load_w<FP8>(nb, w3row, (kstep0 + s + 1) * kKS, lg, true);
-        load_x(kstep0 + s + 1, xr);
-      }
+    // one K step: multiply the weights in (wa, wb) with the staged tile
+    auto compute = [&](const WFrag<FP8>& wa, const WFrag<FP8>& wb, int buf, int kstep) {
       if (FP8) {
-        float sc1 = Sg[sb_row + kstep0 + s];
-        float sc3 = TWO ? S3g[sb_row + kstep0 + s] : 0.f;
+        const float sc1 = Sg[sb_row + kstep];
+        const float sc3 = TWO ? S3g[sb_row + kstep] : 0.f;
         bf16x8 a1[4], a3[4];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -225,9 +227,40 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
           }
         }
       }
-      if (more) store_x(buf ^ 1, xr);
-      __syncthreads();
-      if (more) { wa = na; if (TWO) wb = nb; }
+    };
+
+    // Pipeline: at step s the weights of steps s+1, s+2 and the activations of
+    // step s+2 are in flight while step s is multiplied and the (already
+    // arrived) activations of step s+1 are staged.  Loads are issued
+    // activations-first: vector-memory counters drain in order, so waiting for
+    // an activation tile never waits for weights issued after it.  Steps past
+    // the end re-load the last K block (clamped) instead of branching around
+    // the loads; that data is never multiplied.
+    const int klast = kstep0 + steps - 1;
+    WFrag<FP8> w1b[3], w3b[3];
+    u32x4 xb[3][MT];
+    load_x(kstep0, xb[0]);
+    load_w<FP8>(w1b[0], w1s, kstep0);
+    if (TWO) load_w<FP8>(w3b[0], w3s, kstep0);
+    load_x(min(kstep0 + 1, klast), xb[1]);
+    load_w<FP8>(w1b[1], w1s, min(kstep0 + 1, klast));
+    if (TWO) load_w<FP8>(w3b[1], w3s, min(kstep0 + 1, klast));
+    store_x(0, xb[0]);
+    __syncthreads();
+
+    for (int s0 = 0; s0 < steps; s0 += 3) {
+#pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int s = s0 + u;
+        if (s < steps) {
+          load_x(min(kstep0 + s + 2, klast), xb[(u + 2) % 3]);
+          load_w<FP8>(w1b[(u + 2) % 3], w1s, min(kstep0 + s + 2, klast));
+          if (TWO) load_w<FP8>(w3b[(u + 2) % 3], w3s, min(kstep0 + s + 2, klast));
+          compute(w1b[u], w3b[u], s & 1, kstep0 + s);
+          store_x((s + 1) & 1, xb[(u + 1) % 3]);
+          __syncthreads();
+        }
+      }
     }
 
     // ---- epilogue: lane holds D[n = n_w0 + 4*lg + j][m = lr], j = 0..3
@@ -241,45 +274,82 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
           u32x2 o = {pack_bf16x2(silu(gt.x) * up.x, silu(gt.y) * up.y),
                      pack_bf16x2(silu(gt.z) * up.z, silu(gt.w) * up.w)};
           *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
-        } else if (MODE == MODE_DOWN) {
-          if (a.out_f32) {
-            float* o = static_cast<float*>(a.out) + ks * a.split_stride + row * a.ldo + ncol;
-            *reinterpret_cast<f32x4*>(o) = acc[m];
-          } else {
-            u32x2 o = {pack_bf16x2(acc[m].x, acc[m].y), pack_bf16x2(acc[m].z, acc[m].w)};
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
-          }
+        } else if (a.out_f32) {
+          float* o = static_cast<float*>(a.out) + ks * a.split_stride + row * a.ldo + ncol;
+          *reinterpret_cast<f32x4*>(o) = acc[m];
         } else {
-          float* o = static_cast<float*>(a.out) + row * a.ldo;
-          const float v[4] = {acc[m].x, acc[m].y, acc[m].z, acc[m].w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (ncol + j < a.N) o[ncol + j] = v[j] + (a.bias ? a.bias[ncol + j] : 0.f);
+          u32x2 o = {pack_bf16x2(acc[m].x, acc[m].y), pack_bf16x2(acc[m].z, acc[m].w)};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
         }
       }
     }
   }
 }
 
-template <bool FP8, int MODE>
+template <bool FP8, int MODE, bool PACKED>
 static hipError_t launch_mt(const StreamArgs& a, int mt, dim3 grid, hipStream_t s) {
   switch (mt) {
-    case 1: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 1>), grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 2>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 4>), grid, dim3(kThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 1, PACKED>), grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 2, PACKED>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 4, PACKED>), grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_stream(const StreamArgs& a, int fp8, int mode, int mt, dim3 grid, hipStream_t s) {
+template <int MODE>
+static hipError_t launch_mode(const StreamArgs& a, int fp8, int packed, int mt, dim3 grid, hipStream_t s) {
+  if (fp8) return packed ? launch_mt<true, MODE, true>(a, mt, grid, s) : launch_mt<true, MODE, false>(a, mt, grid, s);
+  return packed ? launch_mt<false, MODE, true>(a, mt, grid, s) : launch_mt<false, MODE, false>(a, mt, grid, s);
+}
+
+hipError_t launch_ffn_stream(const StreamArgs& a, int fp8, int packed, int mode, int mt, dim3 grid,
+                             hipStream_t s) {
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
-  if (mode == MODE_GATEUP) return fp8 ? launch_mt<true, MODE_GATEUP>(a, mt, grid, s)
-                                      : launch_mt<false, MODE_GATEUP>(a, mt, grid, s);
-  if (mode == MODE_DOWN) return fp8 ? launch_mt<true, MODE_DOWN>(a, mt, grid, s)
-                                    : launch_mt<false, MODE_DOWN>(a, mt, grid, s);
-  if (mode == MODE_ROUTER && !fp8) return launch_mt<false, MODE_ROUTER>(a, mt, grid, s);
+  if (mode == MODE_GATEUP) return launch_mode<MODE_GATEUP>(a, fp8, packed, mt, grid, s);
+  if (mode == MODE_DOWN) return launch_mode<MODE_DOWN>(a, fp8, packed, mt, grid, s);
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Weight packing: row-major [G, N, Kdim] -> per 16-row panel and 128-wide K
+// step, the NI 1-KiB blocks the expert kernels load, in lane order.
+// Element (n, k) of one matrix goes to
+//   panel n/16, step k/128, then (bf16) block kk/32 lane 16*((kk%32)/8) + n%16
+//   element kk%8, or (fp8) block kk/64 lane 16*((kk%64)/16) + n%16 byte kk%16,
+// with kk = k % 128.  One thread moves one 16-byte piece.
+template <bool FP8>
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                   int64_t pieces, int N, int Kdim) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= pieces) return;
+  constexpr int wbytes = FP8 ? 1 : 2;
+  constexpr int NI = FP8 ? 2 : 4;
+  // destination order: [g][panel][step][instr][lane] pieces of 16 bytes
+  const int lane = int(i % 64);
+  int64_t r = i / 64;
+  const int instr = int(r % NI); r /= NI;
+  const int steps = Kdim / kKS;
+  const int step = int(r % steps); r /= steps;
+  const int64_t panel = r % (N / 16);
+  const int64_t g = r / (N / 16);
+  const int64_t n = panel * 16 + (lane & 15);
+  const int kk = FP8 ? 64 * instr + 16 * (lane >> 4) : 32 * instr + 8 * (lane >> 4);
+  const int64_t k = (int64_t)step * kKS + kk;
+  const int64_t soff = ((g * N + n) * Kdim + k) * wbytes;
+  *reinterpret_cast<u32x4*>(dst + i * 16) = *reinterpret_cast<const u32x4*>(src + soff);
+}
+
+hipError_t launch_pack(const void* src, void* dst, int G, int N, int Kdim, int fp8, hipStream_t s) {
+  const int64_t bytes = (int64_t)G * N * Kdim * (fp8 ? 1 : 2);
+  const int64_t pieces = bytes / 16;
+  if (pieces == 0) return hipSuccess;
+  const dim3 grid((unsigned)((pieces + 255) / 256));
+  if (fp8) hipLaunchKernelGGL((pack_kernel<true>), grid, dim3(256), 0, s,
+                              static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), pieces, N, Kdim);
+  else hipLaunchKernelGGL((pack_kernel<false>), grid, dim3(256), 0, s,
+                          static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst), pieces, N, Kdim);
+  return hipGetLastError();
 }
 
 }  // namespace moe

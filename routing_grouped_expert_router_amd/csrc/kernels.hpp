@@ -22,6 +22,7 @@ struct RouteArgs {
   const int32_t* l2p; const int32_t* rcount; int max_replicas;
   int layout, M_max, BM;
   int64_t routed_cap;       // rows of the routed part of the grouped buffer
+  int topk_lanes;           // lanes per token in the top-K kernel
   // outputs
   int32_t* topk_ids; float* topk_w; int32_t* topk_phys; int32_t* row_of;
   int32_t* slot_of; int32_t* src_of; int32_t* counts; int32_t* offsets;
@@ -51,7 +52,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
 // ---- streaming grouped GEMM (decode FFN and router logits) ---------------------
 
-enum { MODE_GATEUP = 0, MODE_DOWN = 1, MODE_ROUTER = 2 };
+enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
 
 struct StreamArgs {
   const uint16_t* X; int64_t ldx;   // bf16 rows
@@ -62,18 +63,21 @@ struct StreamArgs {
   const void* W; const void* W3; const float* S; const float* S3;        // routed
   const void* SW; const void* SW3; const float* SS; const float* SS3;    // shared
   void* out; int64_t ldo; int64_t split_stride; int out_f32;
-  const float* bias;
   int ksplit;      // grid.z = ksplit * mchunks
   int mchunks;     // row-tile passes dealt round-robin over grid.z
 };
 
-hipError_t launch_ffn_stream(const StreamArgs& a, int fp8, int mode, int mt, dim3 grid,
+hipError_t launch_ffn_stream(const StreamArgs& a, int fp8, int packed, int mode, int mt, dim3 grid,
                              hipStream_t s);
 
-// router logits for fp32 activations: plain fp32 dot products
-struct RouterF32Args {
-  const float* x; const uint16_t* w; const float* bias; int T, E, H; float* logits;
+// row-major [G, N, Kdim] weights -> the packed layout the kernels stream
+hipError_t launch_pack(const void* src, void* dst, int G, int N, int Kdim, int fp8, hipStream_t s);
+
+// ---- router logits --------------------------------------------------------------
+
+struct RouterArgs {
+  const void* x; int x_f32; const uint16_t* w; const float* bias; int T, E, H; float* logits;
 };
-hipError_t launch_router_f32(const RouterF32Args& a, hipStream_t s);
+hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 
 }  // namespace moe

@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/moe.h: argument validation,
 // buffer sizing, and the choice of kernel variants and grids.  Grids depend
 // only on (desc, T), never on device-side counts.
+#include <math.h>
 #include <string.h>
 
 #include "common.hpp"
@@ -48,11 +49,15 @@ bool route_ptrs_ok(const moe_desc_t* d, const moe_route_t* r) {
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// row tiles held in registers per pass of the streaming GEMM
+// Row tiles held in registers per pass of the streaming GEMM: enough for a
+// slot's expected rows plus four standard deviations (tokens choose a slot
+// with probability about K/E_phys), capped by M_max in the masked layout.
+// Larger groups take further passes.
 int stream_mt(const moe_desc_t* d, int T) {
-  int rows;
-  if (d->layout == MOE_MASKED) rows = d->M_max;
-  else rows = (int)(((int64_t)T * d->K + d->E_phys - 1) / d->E_phys);
+  const double p = (double)d->K / d->E_phys;
+  const double mean = (double)T * p;
+  double rows = mean + 4.0 * sqrt(mean * (1.0 - p)) + 1.0;
+  if (d->layout == MOE_MASKED && rows > d->M_max) rows = d->M_max;
   if (rows <= 16) return 1;
   if (rows <= 32) return 2;
   return 4;
@@ -79,6 +84,7 @@ moe_status_t moe_check_desc(const moe_desc_t* d) {
   if (d->E_phys < d->E || d->n_shared < 0 || d->n_shared > 1 || d->max_replicas < 1) return MOE_ERR_ARG;
   if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_ERR_ARG;
   if (d->w_dtype != MOE_BF16 && d->w_dtype != MOE_FP8E4M3_B128) return MOE_ERR_ARG;
+  if (d->w_packed != 0 && d->w_packed != 1) return MOE_ERR_ARG;
   if (d->layout == MOE_MASKED) { if (d->M_max < 1) return MOE_ERR_ARG; }
   else if (d->layout == MOE_CONTIG) { if (d->BM < 1) return MOE_ERR_ARG; }
   else return MOE_ERR_ARG;
@@ -127,20 +133,9 @@ moe_status_t moe_router_logits(const moe_desc_t* d, const void* x, const void* w
   if (T < 0 || T > d->T_max) return MOE_ERR_ARG;
   if (T == 0) return MOE_OK;
   if (!x || !w_router || !logits) return MOE_ERR_ARG;
-  if (d->act_dtype == MOE_F32) {
-    RouterF32Args f = {static_cast<const float*>(x), static_cast<const uint16_t*>(w_router), bias,
-                       T, d->E, d->H, logits};
-    return hip_status(launch_router_f32(f, stream));
-  }
-  StreamArgs a = {};
-  a.X = static_cast<const uint16_t*>(x); a.ldx = d->H;
-  a.Kdim = d->H; a.N = d->E; a.T = T; a.E_phys = d->E_phys;
-  a.W = w_router; a.out = logits; a.ldo = d->E; a.bias = bias; a.ksplit = 1;
-  const int mt = 4;
-  const int tiles = (T + 15) / 16;
-  a.mchunks = (tiles + mt - 1) / mt;
-  dim3 grid((d->E + 63) / 64, 1, a.mchunks);
-  return hip_status(launch_ffn_stream(a, 0, MODE_ROUTER, mt, grid, stream));
+  RouterArgs a = {x, d->act_dtype == MOE_F32, static_cast<const uint16_t*>(w_router), bias,
+                  T, d->E, d->H, logits};
+  return hip_status(launch_router(a, stream));
 }
 
 moe_status_t moe_route(const moe_desc_t* d, const float* logits, int32_t T, const int32_t* l2p,
@@ -225,7 +220,8 @@ moe_status_t moe_expert_gate_up(const moe_desc_t* d, const moe_weights_t* w, con
   g1.SW = w->sw1; g1.SW3 = w->sw3; g1.SS = w->ss1; g1.SS3 = w->ss3;
   g1.out = h; g1.ldo = d->I;
   const int G = d->E_phys + d->n_shared;
-  return hip_status(launch_ffn_stream(g1, fp8, MODE_GATEUP, stream_mt(d, T), dim3(d->I / 64, G, 1), stream));
+  return hip_status(launch_ffn_stream(g1, fp8, d->w_packed, MODE_GATEUP, stream_mt(d, T),
+                                      dim3(d->I / 64, G, 1), stream));
 }
 
 moe_status_t moe_expert_down(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
@@ -244,7 +240,8 @@ moe_status_t moe_expert_down(const moe_desc_t* d, const moe_weights_t* w, const 
   g2.out = y; g2.ldo = d->H; g2.ksplit = splits; g2.out_f32 = splits > 1;
   g2.split_stride = moe_buffer_rows(d) * d->H;
   const int G = d->E_phys + d->n_shared;
-  return hip_status(launch_ffn_stream(g2, fp8, MODE_DOWN, stream_mt(d, T), dim3(d->H / 64, G, splits), stream));
+  return hip_status(launch_ffn_stream(g2, fp8, d->w_packed, MODE_DOWN, stream_mt(d, T),
+                                      dim3(d->H / 64, G, splits), stream));
 }
 
 moe_status_t moe_grouped_ffn(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
@@ -285,6 +282,15 @@ moe_status_t moe_forward(const moe_desc_t* d, const void* x, const void* w_route
   st = moe_grouped_ffn(d, w, r, T, xg, h, y, stream);
   if (st != MOE_OK) return st;
   return moe_combine(d, r, T, y, out, stream);
+}
+
+moe_status_t moe_pack_weights(const moe_desc_t* d, int32_t which, int32_t G, const void* src,
+                              void* dst, hipStream_t stream) {
+  moe_status_t st = moe_check_desc(d);
+  if (st != MOE_OK) return st;
+  if ((which != 0 && which != 1) || G < 0 || (G > 0 && (!src || !dst)) || src == dst) return MOE_ERR_ARG;
+  const int N = which == 0 ? d->I : d->H, Kdim = which == 0 ? d->H : d->I;
+  return hip_status(launch_pack(src, dst, G, N, Kdim, d->w_dtype == MOE_FP8E4M3_B128, stream));
 }
 
 moe_status_t moe_replica_map_from_p2l(const int32_t* p2l, int32_t E, int32_t E_phys,

@@ -5,9 +5,11 @@
 // Method (vllbc blog "MoE inference and expert parallelism", routing section
 // and Table 3-1; vLLM forward path: top-k, then sort token/expert pairs by
 // expert; MoonEP online plan: counts -> offsets -> expert-grouped slots):
-//   kernel 1, one workgroup per 64-token block: each wave takes a token and
-//     finds its K largest logits by K rounds of a wave-wide max over packed
-//     (value, ~id) keys; the block's choices set bits in one 64-bit mask per
+//   kernel 1, one workgroup per 64-token block: a subgroup of lanes (the
+//     power of two >= E, 8..64) takes a token and finds its K largest logits
+//     by K rounds of a subgroup max over packed (value, ~id) keys; several
+//     tokens share a wave when E is small.  The block's choices set bits in
+//     one 64-bit mask per
 //     logical expert, from which each choice's rank among earlier tokens of
 //     the block and the block's count per expert follow by popcount.  OR is
 //     order-independent, so the result is deterministic.
@@ -24,36 +26,49 @@
 namespace moe {
 
 constexpr int kRouteThreads = 256;
+constexpr int kTopkThreads = 1024;   // 16 waves per 64-token block
 
-__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(RouteArgs a) {
+// lanes per token: the smallest power of two >= E, between 8 and 64
+inline int topk_lanes(int E) {
+  int l = 8;
+  while (l < E && l < 64) l <<= 1;
+  return l;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
   __shared__ unsigned long long mask[1024];
   __shared__ int ids_s[kBlockTokens * kMaxK];
   __shared__ int flag_s;
   const int E = a.E, K = a.K, T = a.T;
   const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += kRouteThreads) mask[e] = 0ull;
+  for (int e = tid; e < E; e += kTopkThreads) mask[e] = 0ull;
   if (tid == 0) flag_s = 0;
   __syncthreads();
 
-  const int npl = (E + kWave - 1) / kWave;   // logits per lane
-  for (int tl = wave; tl < kBlockTokens; tl += kRouteThreads / kWave) {
+  // a token is handled by a subgroup of LPT lanes; a wave holds 64/LPT tokens
+  const int LPT = a.topk_lanes;
+  const int tpw = kWave / LPT;
+  const int sub = lane / LPT, sl = lane % LPT, sbase = sub * LPT;
+  const int npl = (E + LPT - 1) / LPT;           // logits per lane (<= 16)
+  for (int tl0 = wave * tpw; tl0 < kBlockTokens; tl0 += (kTopkThreads / kWave) * tpw) {
+    const int tl = tl0 + sub;
     const int t = b * kBlockTokens + tl;
-    if (t >= T) break;
-    const float* row = a.logits + (int64_t)t * E;
+    const bool valid = t < T;
+    const float* row = a.logits + (int64_t)(valid ? t : 0) * E;
     uint64_t keys[16];
     bool bad = false;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int e = lane + j * kWave;
+      const int e = sl + j * LPT;
       keys[j] = 0ull;
-      if (j < npl && e < E) {
+      if (valid && j < npl && e < E) {
         const float v = row[e];
         bad |= !__builtin_isfinite(v);
         keys[j] = topk_key(v, e);
       }
     }
-    if (__any(bad) && lane == 0) atomicOr(&flag_s, 1);
+    if (bad) atomicOr(&flag_s, 1);
     uint64_t prev = ~0ull;
     int my_id = -1;
     for (int k = 0; k < K; ++k) {
@@ -63,32 +78,38 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(RouteArgs a) 
         const uint64_t c = keys[j] < prev ? keys[j] : 0ull;
         best = c > best ? c : best;
       }
-      best = wave_max_u64(best);
+      // max over the LPT lanes of this subgroup
+      for (int off = LPT >> 1; off >= 1; off >>= 1) {
+        const uint32_t lo = __shfl_xor((unsigned)(best & 0xffffffffu), off, kWave);
+        const uint32_t hi = __shfl_xor((unsigned)(best >> 32), off, kWave);
+        const uint64_t o = (uint64_t(hi) << 32) | lo;
+        best = o > best ? o : best;
+      }
       prev = best;
       const int id = int(0xffffffffu - uint32_t(best & 0xffffffffu));
-      if (lane == k) my_id = id;
+      if (sl == k) my_id = id;
     }
     // weights: w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0), sum in k order
-    const int id0 = __shfl(my_id, 0, kWave);
-    const float l0 = row[id0];
+    const int id0 = __shfl(my_id, sbase, kWave);
+    const float l0 = valid ? row[id0] : 0.f;
     float ek = 0.f, sum = 0.f;
     for (int k = 0; k < K; ++k) {
-      const int idk = __shfl(my_id, k, kWave);
-      const float e = expf(row[idk] - l0);
+      const int idk = __shfl(my_id, sbase + k, kWave);
+      const float e = valid ? expf(row[idk] - l0) : 0.f;
       sum += e;
-      if (lane == k) ek = e;
+      if (sl == k) ek = e;
     }
-    if (lane < K) {
+    if (valid && sl < K) {
       // K <= E distinct positive keys always exist, so my_id is in [0, E)
       const int id = (my_id >= 0 && my_id < E) ? my_id : 0;
-      a.topk_ids[(int64_t)t * K + lane] = id;
-      a.topk_w[(int64_t)t * K + lane] = ek / sum;
-      ids_s[tl * K + lane] = id;
+      a.topk_ids[(int64_t)t * K + sl] = id;
+      a.topk_w[(int64_t)t * K + sl] = ek / sum;
+      ids_s[tl * K + sl] = id;
       atomicOr(&mask[id], 1ull << tl);
     }
   }
   __syncthreads();
-  for (int i = tid; i < kBlockTokens * K; i += kRouteThreads) {
+  for (int i = tid; i < kBlockTokens * K; i += kTopkThreads) {
     const int tl = i / K, t = b * kBlockTokens + tl;
     if (t < T) {
       const int e = ids_s[i];
@@ -96,7 +117,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(RouteArgs a) 
       a.ws.local_rank[(int64_t)t * K + (i - tl * K)] = __popcll(below);
     }
   }
-  for (int e = tid; e < E; e += kRouteThreads)
+  for (int e = tid; e < E; e += kTopkThreads)
     a.ws.blk[(int64_t)b * E + e] = __popcll(mask[e]);
   if (tid == 0) a.ws.blk_flags[b] = flag_s;
 }
@@ -225,7 +246,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_assign_kernel(RouteArgs a
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const int nblk = (a.T + kBlockTokens - 1) / kBlockTokens;
   if (nblk > 0) {
-    hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kRouteThreads), 0, s, a);
+    RouteArgs b = a;
+    b.topk_lanes = topk_lanes(a.E);
+    hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kTopkThreads), 0, s, b);
   }
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
   const int64_t TK = (int64_t)a.T * a.K;

@@ -26,7 +26,7 @@ _DEFAULT = object()
 class Built:
     """A workload on the GPU: inputs, uploaded weights and a MoELayer."""
 
-    def __init__(self, cfg, T=None, layout=None, M_max=None, p2l=_DEFAULT):
+    def __init__(self, cfg, T=None, layout=None, M_max=None, p2l=_DEFAULT, packed=False):
         if layout is not None:
             cfg = cfg.with_(layout=layout)
         if M_max is not None:
@@ -45,7 +45,9 @@ class Built:
             max_rep = l2p.shape[1]
             self.l2p = torch.from_numpy(l2p).to(DEV)
             self.rcount = torch.from_numpy(cnt).to(DEV)
-        self.d = B.Desc.from_config(cfg, max_replicas=max_rep)
+        self.d = B.Desc.from_config(cfg, max_replicas=max_rep, w_packed=int(packed))
+        if packed:
+            self.weights = B.pack_expert_weights(self.d, self.weights)
         self.x = self.inp.x.to(DEV)
         self.wr = self.inp.w_router.to(DEV)
         self.bias = None if self.inp.bias is None else self.inp.bias.to(DEV)

@@ -83,9 +83,10 @@ def test_mfma_operand_layout_probe():
     assert rel_err(out, ref) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
-def test_route_and_layer_small(cfg):
-    b = Built(cfg)
+def test_route_and_layer_small(cfg, packed):
+    b = Built(cfg, packed=packed)
     lg = b.oracle_logits()
     out = out_np(b.run(lg))
     res = b.oracle(lg)
@@ -255,6 +256,45 @@ def test_replica_map_leaves_output_unchanged():
     assert torch.equal(a, b)
 
 
+def test_packed_weights_give_identical_outputs():
+    """Packing only reorders weight bytes: every row's reduction runs in the
+    same order, so outputs must match the row-major run bit for bit."""
+    for cfg in (SMALL[1], SMALL[3], SMALL[6]):
+        a = Built(cfg)
+        p = Built(cfg, packed=True)
+        lg = a.oracle_logits()
+        assert torch.equal(a.run(lg).clone(), p.run(lg).clone()), cfg.name
+
+
+def test_pack_layout_matches_definition():
+    """moe_pack_weights places element (n, k) where the layout definition
+    says: panel n/16, K block k/128, then the lane piece of kk = k % 128."""
+    for w_dtype, dt in (("bf16", torch.bfloat16), ("fp8", torch.uint8)):
+        cfg = configs.tiny().with_(H=256, I=384, w_dtype=w_dtype)
+        d = B.Desc.from_config(cfg)
+        G, N, Kd = 2, cfg.I, cfg.H
+        src = torch.arange(G * N * Kd, dtype=torch.int64) % 251
+        src = src.to(torch.int16).view(torch.bfloat16) if dt == torch.bfloat16 else src.to(torch.uint8)
+        src = src.reshape(G, N, Kd).to(DEV)
+        dst = torch.empty_like(src)
+        B.moe_pack_weights(d, 0, src, dst)
+        s_ = src.cpu().view(torch.int16 if dt == torch.bfloat16 else torch.uint8).numpy()
+        d_ = dst.cpu().view(torch.int16 if dt == torch.bfloat16 else torch.uint8).numpy().reshape(-1)
+        esz = 2 if dt == torch.bfloat16 else 1
+        per_piece = 16 // esz
+        NI = 4 if esz == 2 else 2
+        rng = np.random.default_rng(0)
+        for _ in range(2000):
+            g, n, k = int(rng.integers(G)), int(rng.integers(N)), int(rng.integers(Kd))
+            kk = k % 128
+            instr = kk // (32 if esz == 2 else 64)
+            within = kk % (32 if esz == 2 else 64)
+            lane = 16 * (within // per_piece) + n % 16
+            e = within % per_piece
+            piece = ((((g * (N // 16) + n // 16) * (Kd // 128) + k // 128) * NI + instr) * 64 + lane)
+            assert d_[piece * per_piece + e] == s_[g, n, k]
+
+
 def test_determinism_bit_identical():
     cfg = SMALL[3]
     b = Built(cfg)
@@ -364,7 +404,7 @@ def _sample(T, n, seed=0):
 
 @pytest.mark.parametrize("cfg", FULL, ids=lambda c: c.name)
 def test_full_size_sampled(cfg):
-    b = Built(cfg)
+    b = Built(cfg, packed=True)          # the layout the benchmark times
     say(f"  built {cfg.name}")
     lg = b.oracle_logits()
     out = out_np(b.run(lg))
@@ -374,3 +414,26 @@ def test_full_size_sampled(cfg):
     e = rel_err(out[toks], res["out"])
     say(f"  {cfg.name}: sampled tokens {list(toks)} rel err {e:.3e} status {res['status']}")
     assert e <= TOL[cfg.w_dtype]
+
+
+def test_graph_replays_match_eager():
+    """The five calls captured in a HIP graph, replayed several times with
+    eager work and synchronisations in between; every replay must equal the
+    eager result bit for bit (no call records a memset)."""
+    for cfg in (SMALL[2], SMALL[3], SMALL[6]):
+        b = Built(cfg)
+        other = Built(SMALL[0])
+        eager = b.run(None).clone()
+        g = torch.cuda.CUDAGraph()
+        b.layer.out.zero_()
+        with torch.cuda.graph(g):
+            b.layer.forward(b.x, b.T)
+        for i in range(3):
+            b.layer.out.zero_()
+            b.layer.xg.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(b.layer.out[: b.T], eager), (cfg.name, i)
+            other.run(None)                       # eager work between replays
+            torch.cuda.synchronize()
+        del g
