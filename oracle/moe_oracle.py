@@ -38,9 +38,9 @@ design notes with its reason):
   R6 masked overflow is never dropped: rows past M_max go to a spill region.
   R7 a replicated expert's tokens, in ascending token order, go round-robin
      over its replicas in logical_to_physical order.
-  R8 an invalid replica entry (count < 1, or a slot outside [0, E_phys))
-     sends that expert's tokens to its home slot (= its logical id) and sets
-     status bit 1.
+  R8 an invalid replica map (a count outside [1, max_replicas], a slot
+     outside [0, E_phys), or one slot listed twice) is ignored as a whole:
+     every expert uses slot = its logical id, and status bit 1 is set.
 
 Parity pins: see tests/test_oracle_pins.py (brute force, a third-party
 Mixtral MoE block, textbook sorts, page worked examples, closed forms).
@@ -149,17 +149,34 @@ def replica_tables(p2l: np.ndarray, E: int, max_replicas: int | None = None):
     return l2p, count
 
 
+def replica_map_valid(l2p: np.ndarray, count: np.ndarray, E_phys: int) -> bool:
+    """R8: counts in [1, max_replicas], slots in [0, E_phys), no slot twice."""
+    l2p = np.asarray(l2p)
+    seen = set()
+    for l in range(l2p.shape[0]):
+        R = int(count[l])
+        if R < 1 or R > l2p.shape[1]:
+            return False
+        for r in range(R):
+            p = int(l2p[l, r])
+            if not (0 <= p < E_phys) or p in seen:
+                return False
+            seen.add(p)
+    return True
+
+
 def assign_physical(ids: np.ndarray, E_phys: int, l2p: np.ndarray | None = None,
                     count: np.ndarray | None = None):
     """Physical slot of every (token, k) choice.  Without a map the slot is
     the logical id.  With a map (R7): the tokens that chose logical expert l,
     taken in ascending token order, are numbered j = 0, 1, ...; choice j goes
-    to l2p[l][j mod R_l].  Invalid entries follow R8."""
+    to l2p[l][j mod R_l].  An invalid map follows R8."""
     ids = np.asarray(ids)
     T, K = ids.shape
     if l2p is None:
         return ids.astype(np.int32).copy(), 0
-    status = 0
+    if not replica_map_valid(l2p, count, E_phys):
+        return ids.astype(np.int32).copy(), STATUS_BAD_REPLICA
     phys = np.empty_like(ids, dtype=np.int32)
     seen: dict[int, int] = {}
     for t in range(T):
@@ -167,13 +184,8 @@ def assign_physical(ids: np.ndarray, E_phys: int, l2p: np.ndarray | None = None,
             l = int(ids[t, k])
             j = seen.get(l, 0)
             seen[l] = j + 1
-            R = int(count[l])
-            p = int(l2p[l, j % R]) if R >= 1 else -1
-            if R < 1 or not (0 <= p < E_phys):
-                status |= STATUS_BAD_REPLICA
-                p = l
-            phys[t, k] = p
-    return phys, status
+            phys[t, k] = l2p[l, j % int(count[l])]
+    return phys, 0
 
 
 # --------------------------------------------------------------------------
