@@ -114,6 +114,9 @@ typedef struct {
   int32_t* masked_m;   /* [E_phys] min(T_p, M_max)   (MOE_MASKED; else NULL ok) */
   int32_t* spill_off;  /* [E_phys+1] prefix sum of T_p - masked_m (MOE_MASKED) */
   int32_t* pad_off;    /* [E_phys+1] prefix sum of ceil(T_p/BM)*BM (MOE_CONTIG) */
+  int32_t* tile_off;   /* [E_phys+2] work list of the tiled expert kernel:
+                          prefix sum of ceil(T_p/128) over slots, then the
+                          shared expert's ceil(T/128) tiles (n_shared = 1) */
   uint32_t* status;    /* [1] MOE_STATUS_* bits of the last moe_route */
 } moe_route_t;
 

@@ -41,7 +41,7 @@ _P = ctypes.c_void_p
 class moe_route_t(ctypes.Structure):
     _fields_ = [(n, _P) for n in (
         "topk_ids", "topk_w", "topk_phys", "row_of", "slot_of", "src_of", "counts",
-        "offsets", "masked_m", "spill_off", "pad_off", "status")]
+        "offsets", "masked_m", "spill_off", "pad_off", "tile_off", "status")]
 
 
 class moe_weights_t(ctypes.Structure):
@@ -187,6 +187,7 @@ class RouteTables:
         self.masked_m = torch.zeros(d.E_phys, **i32)
         self.spill_off = torch.zeros(d.E_phys + 1, **i32)
         self.pad_off = torch.zeros(d.E_phys + 1, **i32)
+        self.tile_off = torch.zeros(d.E_phys + 2, **i32)
         self.status = torch.zeros(1, **i32)
         self.c = moe_route_t(*[_ptr(getattr(self, f)) for f, _ in moe_route_t._fields_])
 

@@ -120,6 +120,8 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
   }
   const int nt0 = (c0 + 15) >> 4, nt1 = (c1 + 15) >> 4, ntiles = nt0 + nt1;
   if (ntiles == 0) return;   // no token: no weight load, no MFMA
+  // size classes: another launch owns groups outside (min_rows, max_rows]
+  if (c0 + c1 <= a.min_rows || (a.max_rows > 0 && c0 + c1 > a.max_rows)) return;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;

@@ -26,7 +26,8 @@ struct RouteArgs {
   // outputs
   int32_t* topk_ids; float* topk_w; int32_t* topk_phys; int32_t* row_of;
   int32_t* slot_of; int32_t* src_of; int32_t* counts; int32_t* offsets;
-  int32_t* masked_m; int32_t* spill_off; int32_t* pad_off; uint32_t* status;
+  int32_t* masked_m; int32_t* spill_off; int32_t* pad_off; int32_t* tile_off; uint32_t* status;
+  int n_shared;
   RouteWs ws;
 };
 
@@ -65,10 +66,25 @@ struct StreamArgs {
   void* out; int64_t ldo; int64_t split_stride; int out_f32;
   int ksplit;      // grid.z = ksplit * mchunks
   int mchunks;     // row-tile passes dealt round-robin over grid.z
+  int min_rows;    // groups with at most this many rows are left to another launch
+  int max_rows;    // groups with more rows are left to another launch (0: no limit)
 };
 
 hipError_t launch_ffn_stream(const StreamArgs& a, int fp8, int packed, int mode, int mt, dim3 grid,
                              hipStream_t s);
+
+// ---- LDS-tiled grouped GEMM (large groups) ------------------------------------
+
+constexpr int kTileRows = 128;     // token rows per tile of the tiled kernel
+
+struct TiledArgs {
+  StreamArgs s;
+  const int32_t* tile_off;   // [E_phys + 2] prefix of ceil(rows / 128) per group
+  int min_rows;              // groups with at most this many rows are skipped
+};
+bool tiled_supported(int mode, int fp8, int N, int Kdim, int ksplit);
+hipError_t launch_ffn_tiled(const TiledArgs& a, int fp8, int packed, int mode, int max_tiles,
+                            hipStream_t s);
 
 // row-major [G, N, Kdim] weights -> the packed layout the kernels stream
 hipError_t launch_pack(const void* src, void* dst, int G, int N, int Kdim, int fp8, hipStream_t s);

@@ -41,7 +41,7 @@ int64_t routed_cap(const moe_desc_t* d) {
 bool route_ptrs_ok(const moe_desc_t* d, const moe_route_t* r) {
   if (!r) return false;
   if (!r->topk_ids || !r->topk_w || !r->topk_phys || !r->row_of || !r->slot_of || !r->src_of ||
-      !r->counts || !r->offsets || !r->status)
+      !r->counts || !r->offsets || !r->tile_off || !r->status)
     return false;
   if (d->layout == MOE_MASKED) return r->masked_m && r->spill_off;
   return r->pad_off != nullptr;
@@ -49,14 +49,14 @@ bool route_ptrs_ok(const moe_desc_t* d, const moe_route_t* r) {
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// Row tiles held in registers per pass of the streaming GEMM: enough for a
-// slot's expected rows plus four standard deviations (tokens choose a slot
-// with probability about K/E_phys), capped by M_max in the masked layout.
-// Larger groups take further passes.
+// Row tiles held in registers per pass of the streaming GEMM for the bulk of
+// the groups: a slot's expected rows plus two standard deviations (tokens
+// choose a slot with probability about K/E_phys), capped by M_max in the
+// masked layout.  Larger groups go to the larger size classes below.
 int stream_mt(const moe_desc_t* d, int T) {
   const double p = (double)d->K / d->E_phys;
   const double mean = (double)T * p;
-  double rows = mean + 4.0 * sqrt(mean * (1.0 - p)) + 1.0;
+  double rows = mean + 2.0 * sqrt(mean * (1.0 - p)) + 1.0;
   if (d->layout == MOE_MASKED && rows > d->M_max) rows = d->M_max;
   if (rows <= 16) return 1;
   if (rows <= 32) return 2;
@@ -156,7 +156,8 @@ moe_status_t moe_route(const moe_desc_t* d, const float* logits, int32_t T, cons
   a.topk_ids = r->topk_ids; a.topk_w = r->topk_w; a.topk_phys = r->topk_phys;
   a.row_of = r->row_of; a.slot_of = r->slot_of; a.src_of = r->src_of;
   a.counts = r->counts; a.offsets = r->offsets; a.masked_m = r->masked_m;
-  a.spill_off = r->spill_off; a.pad_off = r->pad_off; a.status = r->status;
+  a.spill_off = r->spill_off; a.pad_off = r->pad_off; a.tile_off = r->tile_off;
+  a.status = r->status; a.n_shared = d->n_shared;
   a.ws.local_rank = reinterpret_cast<int32_t*>(base + wl.local_rank);
   a.ws.blk = reinterpret_cast<int32_t*>(base + wl.blk);
   a.ws.blk_flags = reinterpret_cast<int32_t*>(base + wl.flags);
@@ -192,6 +193,45 @@ moe_status_t ffn_common_checks(const moe_desc_t* d, const moe_weights_t* w, cons
   return MOE_OK;
 }
 
+// One expert projection, dispatched by each group's row count (read on the
+// device; every grid depends on (desc, T) only):
+//   class A  rows <= 16*mt         streaming kernel, mt row tiles per pass
+//   class B  16*mt < rows <= 64    streaming kernel, 4 row tiles per pass
+//   class C  rows > 64             LDS-tiled kernel (when the shape allows it;
+//                                  otherwise class B takes these groups too)
+// A class is launched only if T allows a group of its size (a routed group
+// has at most T rows, the shared group exactly T).
+moe_status_t launch_expert_gemm(const moe_desc_t* d, const moe_route_t* r, int32_t T, StreamArgs a,
+                                bool fp8, int mode, dim3 stream_grid, hipStream_t stream) {
+  const int mt = stream_mt(d, T);
+  const bool tiled = tiled_supported(mode, fp8, a.N, a.Kdim, a.ksplit);
+  const int a_max = 16 * mt;
+  const bool need_b = mt < 4 && T > a_max;
+  const bool need_c = tiled && T > 64;
+  a.min_rows = 0;
+  a.max_rows = (need_b || need_c) ? a_max : 0;
+  hipError_t e = launch_ffn_stream(a, fp8, d->w_packed, mode, mt, stream_grid, stream);
+  if (e != hipSuccess) return hip_status(e);
+  if (need_b) {
+    StreamArgs b = a;
+    b.min_rows = a_max;
+    b.max_rows = need_c ? 64 : 0;
+    e = launch_ffn_stream(b, fp8, d->w_packed, mode, 4, stream_grid, stream);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (!need_c) return MOE_OK;
+  TiledArgs ta;
+  ta.s = a;
+  ta.s.min_rows = 0;
+  ta.s.max_rows = 0;
+  ta.tile_off = r->tile_off;
+  ta.min_rows = (mt < 4) ? 64 : a_max;
+  const int64_t TK = (int64_t)T * d->K;
+  const int64_t max_tiles = (TK + kTileRows - 1) / kTileRows + d->E_phys +
+                            (d->n_shared ? (T + kTileRows - 1) / kTileRows : 0);
+  return hip_status(launch_ffn_tiled(ta, fp8, d->w_packed, mode, (int)max_tiles, stream));
+}
+
 StreamArgs ffn_base_args(const moe_desc_t* d, const moe_route_t* r, int32_t T) {
   StreamArgs a = {};
   a.E_phys = d->E_phys; a.T = T; a.layout = d->layout; a.M_max = d->M_max;
@@ -219,9 +259,8 @@ moe_status_t moe_expert_gate_up(const moe_desc_t* d, const moe_weights_t* w, con
   g1.W = w->w1; g1.W3 = w->w3; g1.S = w->s1; g1.S3 = w->s3;
   g1.SW = w->sw1; g1.SW3 = w->sw3; g1.SS = w->ss1; g1.SS3 = w->ss3;
   g1.out = h; g1.ldo = d->I;
-  const int G = d->E_phys + d->n_shared;
-  return hip_status(launch_ffn_stream(g1, fp8, d->w_packed, MODE_GATEUP, stream_mt(d, T),
-                                      dim3(d->I / 64, G, 1), stream));
+  return launch_expert_gemm(d, r, T, g1, fp8, MODE_GATEUP, dim3(d->I / 64, d->E_phys + d->n_shared, 1),
+                            stream);
 }
 
 moe_status_t moe_expert_down(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
@@ -239,9 +278,8 @@ moe_status_t moe_expert_down(const moe_desc_t* d, const moe_weights_t* w, const 
   g2.W = w->w2; g2.S = w->s2; g2.SW = w->sw2; g2.SS = w->ss2;
   g2.out = y; g2.ldo = d->H; g2.ksplit = splits; g2.out_f32 = splits > 1;
   g2.split_stride = moe_buffer_rows(d) * d->H;
-  const int G = d->E_phys + d->n_shared;
-  return hip_status(launch_ffn_stream(g2, fp8, d->w_packed, MODE_DOWN, stream_mt(d, T),
-                                      dim3(d->H / 64, G, splits), stream));
+  return launch_expert_gemm(d, r, T, g2, fp8, MODE_DOWN, dim3(d->H / 64, d->E_phys + d->n_shared, splits),
+                            stream);
 }
 
 moe_status_t moe_grouped_ffn(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,

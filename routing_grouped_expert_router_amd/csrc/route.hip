@@ -200,7 +200,19 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(RouteArgs a) {
     if (masked) a.spill_off[p] = aux[p];
     else a.pad_off[p] = aux[p];
   }
+  __syncthreads();
+  // tiles of kTileRows rows per slot for the tiled expert kernel (aux reused;
+  // cnt holds the exclusive offsets, so slot p has cnt[p+1] - cnt[p] rows)
+  for (int p = tid; p < P; p += kScanThreads) {
+    const int rows = (p + 1 < P ? cnt[p + 1] : total) - cnt[p];
+    aux[p] = (rows + kTileRows - 1) / kTileRows;
+  }
+  __syncthreads();
+  const int ttotal = block_exclusive_scan(aux, P, tmp);
+  for (int p = tid; p < P; p += kScanThreads) a.tile_off[p] = aux[p];
   if (tid == 0) {
+    a.tile_off[P] = ttotal;
+    a.tile_off[P + 1] = ttotal + (a.n_shared ? (a.T + kTileRows - 1) / kTileRows : 0);
     a.offsets[P] = total;
     if (masked) a.spill_off[P] = total2;
     else a.pad_off[P] = total2;

@@ -66,7 +66,7 @@ def test_calls_reject_bad_arguments_before_enqueueing():
     assert L.moe_combine(dc, ctypes.byref(rt), 4, null, null, null) == B.MOE_ERR_ARG
     # workspace too small (table pointers non-null but never used)
     fake = ctypes.c_void_p(16)
-    rt2 = B.moe_route_t(*([fake] * 12))
+    rt2 = B.moe_route_t(*([fake] * len(B.moe_route_t._fields_)))
     assert L.moe_route(dc, fake, 4, null, null, ctypes.byref(rt2), fake, 1, null) == B.MOE_ERR_WORKSPACE
     # only one of the two replica arrays
     assert L.moe_route(dc, fake, 4, fake, null, ctypes.byref(rt2), fake, 1 << 20, null) == B.MOE_ERR_ARG

@@ -45,6 +45,12 @@ def small_configs():
                    act_dtype="bf16", layout="contig", BM=128, bias="normal0.5"),
         base.with_(name="replica_small", T=70, H=256, I=128, E=32, E_phys=40, K=4,
                    act_dtype="bf16", layout="contig", BM=16, bias="zipf1.1"),
+        # groups of ~150 rows: two 128-row tiles each in the tiled kernel, with
+        # the masked/spill boundary falling inside a tile
+        base.with_(name="tiled_masked_spill", T=300, H=256, I=256, E=4, E_phys=4, K=2,
+                   act_dtype="bf16", M_max=100),
+        base.with_(name="tiled_contig_shared", T=300, H=512, I=384, E=4, E_phys=4, K=2, n_shared=1,
+                   act_dtype="bf16", layout="contig", BM=128, bias="normal0.5"),
     ]
 
 
@@ -361,7 +367,7 @@ class _Guarded:
 
 
 def test_canaries_around_every_buffer():
-    for cfg in (SMALL[2], SMALL[4], SMALL[6]):
+    for cfg in (SMALL[2], SMALL[4], SMALL[6], SMALL[7], SMALL[8]):
         b = Built(cfg)
         d, T, K = b.d, b.T, cfg.K
         gd = _Guarded()
@@ -372,7 +378,8 @@ def test_canaries_around_every_buffer():
                             ("slot_of", TK, torch.int32), ("src_of", TK, torch.int32),
                             ("counts", d.E_phys, torch.int32), ("offsets", d.E_phys + 1, torch.int32),
                             ("masked_m", d.E_phys, torch.int32), ("spill_off", d.E_phys + 1, torch.int32),
-                            ("pad_off", d.E_phys + 1, torch.int32), ("status", 1, torch.int32)]:
+                            ("pad_off", d.E_phys + 1, torch.int32), ("tile_off", d.E_phys + 2, torch.int32),
+                            ("status", 1, torch.int32)]:
             setattr(rt, name, gd.make(n, dt))
         rt.c = B.moe_route_t(*[B._ptr(getattr(rt, f)) for f, _ in B.moe_route_t._fields_])
         rows = B.buffer_rows(d)
@@ -420,7 +427,7 @@ def test_graph_replays_match_eager():
     """The five calls captured in a HIP graph, replayed several times with
     eager work and synchronisations in between; every replay must equal the
     eager result bit for bit (no call records a memset)."""
-    for cfg in (SMALL[2], SMALL[3], SMALL[6]):
+    for cfg in (SMALL[2], SMALL[3], SMALL[6], SMALL[8]):
         b = Built(cfg)
         other = Built(SMALL[0])
         eager = b.run(None).clone()
