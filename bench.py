@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU reference timing")
     ap.add_argument("--row-major", action="store_true",
                     help="stream the row-major weights instead of the packed layout")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 512 MiB device copy three times (a kernel of known "
+                         "traffic for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -172,6 +175,39 @@ def time_workload(cfg, steps, warmup, packed=True):
 
 PREFILL_MIN_T = 1024   # token counts from here on are timed against the MFMA peak
 
+KERNEL_SOURCES = ("common.hpp", "kernels.hpp", "ffn_stream.hip", "ffn_tiled.hip", "moe_api.hip")
+
+
+def kernel_sources_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "routing_grouped_expert_router_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the gate/up kernel from the committed counter
+    summary (profiles/gate_up_traffic_<workload>.md: FETCH_SIZE and
+    WRITE_SIZE passes scaled by a plain copy of known size), or None when
+    there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"gate_up_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "*", "#")):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_sources_sha256_16") != kernel_sources_hash():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
 
 def roofline(cfg, r):
     """The dominant kernel (expert gate/up + SwiGLU) against its bound: HBM
@@ -185,7 +221,8 @@ def roofline(cfg, r):
                 "algorithmic_flops": r["gu_flops"]}
     gbs = r["gu_bytes"] / (r["gu_ms"] * 1e-3) / 1e9
     return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(cfg.name),
             "kernel_us": round(r["gu_ms"] * 1e3, 2), "algorithmic_bytes": r["gu_bytes"]}
 
 
@@ -230,6 +267,13 @@ def main():
         sys.exit(2)
     import torch
     from workloads import configs
+    if args.copy_calibration:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cfg = configs.by_name(args.workload)
     names = [cfg.name]
     if not args.no_sweep and cfg.name.startswith("mixtral_decode_b"):
