@@ -235,9 +235,13 @@ moe_status_t moe_forward(const moe_desc_t* d, const void* x, const void* w_route
 /* ---- weight layout ------------------------------------------------------ */
 
 /* Repacks G expert matrices from row-major [G, N, Kdim] (row = output
- * feature) into the layout the expert kernels stream: for every 16-row panel
- * and 128-wide K block, the 16-byte pieces each lane loads, in lane order, so
- * every load instruction of a wave reads 1 KiB of contiguous memory.
+ * feature) into the layout the expert kernels stream: for every 128-wide K
+ * block (outer) and 16-row panel (inner), the 16-byte pieces each lane loads,
+ * in lane order, so every load instruction of a wave reads 1 KiB of
+ * contiguous memory.  The 16-byte piece of element (n, k) is
+ *   ((g*(Kdim/128) + k/128)*(N/16) + n/16)*NI*64 + (kk/c)*64 + 16*((kk%c)/e) + n%16
+ * with kk = k%128, c = 32 (bf16) or 64 (fp8), e = 8 or 16 elements per piece,
+ * NI = 128/c, and the element sits at position kk%e inside the piece.
  * Same size as the input.  which = 0 for W1 or W3 (N = I, Kdim = H), 1 for
  * W2 (N = H, Kdim = I); element type from desc->w_dtype (fp8 scales are not
  * repacked).  src, dst: device, distinct; a one-time step, not on the hot

@@ -15,9 +15,11 @@
 //    [out, in] layout each instruction reads 64 bytes of 16 rows.  Two K steps
 //    are in flight while the current one is multiplied (three register
 //    buffers in rotation).
-//  * Activations X [rows, Kdim] bf16: the group's row tiles (16 rows each,
-//    up to MT tiles per pass) are staged per K step in a double-buffered LDS
-//    tile and read as the MFMA B operand.
+//  * Activations X [rows, Kdim] bf16: with one 16-row tile per pass (MT = 1,
+//    the common decode case) each lane loads its row's fragments straight
+//    into registers two K steps ahead and the waves never synchronise; with
+//    MT > 1 the group's row tiles are staged per K step in a double-buffered
+//    LDS tile shared by the four waves.
 //  * v_mfma_f32_16x16x32_bf16 computes D[n, m] = sum_k W[n, k] X[m, k]; lane l
 //    supplies weight row l % 16 and activation row l % 16 with the K values
 //    of lane group l / 16, and receives D rows 4*(l/16)+0..3 of column l % 16.
@@ -58,21 +60,26 @@ struct WStream {
   int step_bytes, instr_bytes, lane_bytes;
 };
 
+// Weights are read once per call and never again by this kernel, so the
+// loads are non-temporal: streamed past the caches instead of evicting the
+// activations and routing tables other workgroups still read.
 template <bool FP8>
 __device__ __forceinline__ void load_w(WFrag<FP8>& f, const WStream& w, int kstep) {
   const char* p = w.base + (int64_t)kstep * w.step_bytes + w.lane_bytes;
 #pragma unroll
-  for (int i = 0; i < WFrag<FP8>::NI; ++i) f.v[i] = *reinterpret_cast<const u32x4*>(p + i * w.instr_bytes);
+  for (int i = 0; i < WFrag<FP8>::NI; ++i)
+    f.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + i * w.instr_bytes));
 }
 
 template <bool FP8, bool PACKED>
-__device__ __forceinline__ WStream make_stream(const void* Wg, int n_w0, int lane, int Kdim) {
+__device__ __forceinline__ WStream make_stream(const void* Wg, int n_w0, int lane, int N, int Kdim) {
   constexpr int wbytes = FP8 ? 1 : 2;
   WStream s;
   if (PACKED) {
-    // panel n_w0/16 holds 16*Kdim weights; each K step is one block of 16*128
-    s.base = static_cast<const char*>(Wg) + (int64_t)(n_w0 / 16) * 16 * Kdim * wbytes;
-    s.step_bytes = 16 * kKS * wbytes;
+    // K step s of panel n_w0/16 is the 16x128 block (s, panel) of the
+    // step-major packed matrix
+    s.base = static_cast<const char*>(Wg) + (int64_t)(n_w0 / 16) * 16 * kKS * wbytes;
+    s.step_bytes = (N / 16) * 16 * kKS * wbytes;
     s.instr_bytes = 1024;
     s.lane_bytes = 16 * lane;
   } else {
@@ -98,10 +105,11 @@ __device__ __forceinline__ void tile_rows(int tile, int64_t s0, int c0, int nt0,
   else { const int u = tile - nt0; start = s1 + 16 * u; valid = min(16, c1 - 16 * u); }
 }
 
-template <bool FP8, int MODE, int MT, bool PACKED>
+template <bool FP8, int MODE, int MT, bool PACKED, bool XDIRECT>
 __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
   constexpr bool TWO = MODE == MODE_GATEUP;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT * 16][kLdsStride];
+  static_assert(!XDIRECT || MT == 1, "register-staged activations hold one row tile");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[XDIRECT ? 1 : 2][XDIRECT ? 1 : MT * 16][kLdsStride];
 
   const int g = blockIdx.y;
   const int ks = blockIdx.z % a.ksplit;
@@ -145,8 +153,8 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
       if (TWO) S3g = a.S3 + (int64_t)g * (a.N / 128) * kb_per_row;
     }
   }
-  const WStream w1s = make_stream<FP8, PACKED>(Wg, n_w0, lane, Kdim);
-  const WStream w3s = TWO ? make_stream<FP8, PACKED>(W3g, n_w0, lane, Kdim) : w1s;
+  const WStream w1s = make_stream<FP8, PACKED>(Wg, n_w0, lane, a.N, Kdim);
+  const WStream w3s = TWO ? make_stream<FP8, PACKED>(W3g, n_w0, lane, a.N, Kdim) : w1s;
   const int sb_row = (n_w0 / 128) * kb_per_row;    // scale row of this wave's 16 rows
 
   // ---- K range of this split
@@ -163,6 +171,81 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
     for (int m = 0; m < MT; ++m) {
       ps.start[m] = 0; ps.valid[m] = 0;
       if (m < ps.n) tile_rows(tile0 + m, s0, c0, nt0, s1, c1, ps.start[m], ps.valid[m]);
+    }
+
+    if constexpr (XDIRECT) {
+      // One 16-row tile; each lane streams its own activation row (clamped
+      // into the valid rows) straight into registers, two K steps ahead like
+      // the weights.  Waves never synchronise.
+      const uint16_t* xrow = a.X + (ps.start[0] + min(lr, ps.valid[0] - 1)) * a.ldx;
+      auto xoff = [&](int q) { return FP8 ? 64 * (q >> 1) + 16 * lg + 8 * (q & 1) : 32 * q + 8 * lg; };
+      auto load_xd = [&](u32x4* v, int kstep) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v[q] = *reinterpret_cast<const u32x4*>(xrow + (int64_t)kstep * kKS + xoff(q));
+      };
+      f32x4 acc1 = {0, 0, 0, 0}, acc3d = {0, 0, 0, 0};
+      const int klast = kstep0 + steps - 1;
+      WFrag<FP8> w1b[3], w3b[3];
+      u32x4 xb[3][4];
+      load_xd(xb[0], kstep0);
+      load_w<FP8>(w1b[0], w1s, kstep0);
+      if (TWO) load_w<FP8>(w3b[0], w3s, kstep0);
+      load_xd(xb[1], min(kstep0 + 1, klast));
+      load_w<FP8>(w1b[1], w1s, min(kstep0 + 1, klast));
+      if (TWO) load_w<FP8>(w3b[1], w3s, min(kstep0 + 1, klast));
+      for (int s0 = 0; s0 < steps; s0 += 3) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+          const int s = s0 + u;
+          if (s < steps) {
+            load_xd(xb[(u + 2) % 3], min(kstep0 + s + 2, klast));
+            load_w<FP8>(w1b[(u + 2) % 3], w1s, min(kstep0 + s + 2, klast));
+            if (TWO) load_w<FP8>(w3b[(u + 2) % 3], w3s, min(kstep0 + s + 2, klast));
+            if (FP8) {
+              const float sc1 = Sg[sb_row + kstep0 + s];
+              const float sc3 = TWO ? S3g[sb_row + kstep0 + s] : 0.f;
+              bf16x8 a1[4], a3[4];
+#pragma unroll
+              for (int i = 0; i < 2; ++i) {
+                fp8x16_to_bf16(w1b[u].v[i], a1[2 * i], a1[2 * i + 1]);
+                if (TWO) fp8x16_to_bf16(w3b[u].v[i], a3[2 * i], a3[2 * i + 1]);
+              }
+              f32x4 p1 = {0, 0, 0, 0}, p3 = {0, 0, 0, 0};
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const bf16x8 b = __builtin_bit_cast(bf16x8, xb[u][q]);
+                p1 = mfma16x16x32(a1[q], b, p1);
+                if (TWO) p3 = mfma16x16x32(a3[q], b, p3);
+              }
+              acc1 += p1 * sc1;
+              if (TWO) acc3d += p3 * sc3;
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const bf16x8 b = __builtin_bit_cast(bf16x8, xb[u][q]);
+                acc1 = mfma16x16x32(__builtin_bit_cast(bf16x8, w1b[u].v[q]), b, acc1);
+                if (TWO) acc3d = mfma16x16x32(__builtin_bit_cast(bf16x8, w3b[u].v[q]), b, acc3d);
+              }
+            }
+          }
+        }
+      }
+      const int ncol = n_w0 + 4 * lg;
+      if (lr < ps.valid[0]) {
+        const int64_t row = ps.start[0] + lr;
+        if (MODE == MODE_GATEUP) {
+          u32x2 o = {pack_bf16x2(silu(acc1.x) * acc3d.x, silu(acc1.y) * acc3d.y),
+                     pack_bf16x2(silu(acc1.z) * acc3d.z, silu(acc1.w) * acc3d.w)};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
+        } else if (a.out_f32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ks * a.split_stride + row * a.ldo + ncol) = acc1;
+        } else {
+          u32x2 o = {pack_bf16x2(acc1.x, acc1.y), pack_bf16x2(acc1.z, acc1.w)};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
+        }
+      }
+      continue;
     }
 
     // Activation rows, clamped into the tile's valid rows (rows past the valid
@@ -290,10 +373,12 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
 
 template <bool FP8, int MODE, bool PACKED>
 static hipError_t launch_mt(const StreamArgs& a, int mt, dim3 grid, hipStream_t s) {
+  // one row tile: activations staged in registers, no barriers; more tiles
+  // share an LDS activation tile between the four waves
   switch (mt) {
-    case 1: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 1, PACKED>), grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 2, PACKED>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 4, PACKED>), grid, dim3(kThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 1, PACKED, true>), grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 2, PACKED, false>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 4, PACKED, false>), grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -314,12 +399,15 @@ hipError_t launch_ffn_stream(const StreamArgs& a, int fp8, int packed, int mode,
 }
 
 // ---------------------------------------------------------------------------
-// Weight packing: row-major [G, N, Kdim] -> per 16-row panel and 128-wide K
-// step, the NI 1-KiB blocks the expert kernels load, in lane order.
-// Element (n, k) of one matrix goes to
-//   panel n/16, step k/128, then (bf16) block kk/32 lane 16*((kk%32)/8) + n%16
+// Weight packing: row-major [G, N, Kdim] -> per 128-wide K step and 16-row
+// panel (step-major: the blocks of one K step of all panels are adjacent), the
+// NI 1-KiB blocks the expert kernels load, in lane order.  Element (n, k) of
+// one matrix goes to
+//   step k/128, panel n/16, then (bf16) block kk/32 lane 16*((kk%32)/8) + n%16
 //   element kk%8, or (fp8) block kk/64 lane 16*((kk%64)/16) + n%16 byte kk%16,
-// with kk = k % 128.  One thread moves one 16-byte piece.
+// with kk = k % 128.  Workgroups that stream different panels advance through
+// K at about the same pace, so at any moment the reads of the whole grid fall
+// in a compact window of memory.  One thread moves one 16-byte piece.
 template <bool FP8>
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                                    int64_t pieces, int N, int Kdim) {
@@ -327,14 +415,14 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ s
   if (i >= pieces) return;
   constexpr int wbytes = FP8 ? 1 : 2;
   constexpr int NI = FP8 ? 2 : 4;
-  // destination order: [g][panel][step][instr][lane] pieces of 16 bytes
+  // destination order: [g][step][panel][instr][lane] pieces of 16 bytes
   const int lane = int(i % 64);
   int64_t r = i / 64;
   const int instr = int(r % NI); r /= NI;
+  const int64_t panel = r % (N / 16); r /= (N / 16);
   const int steps = Kdim / kKS;
-  const int step = int(r % steps); r /= steps;
-  const int64_t panel = r % (N / 16);
-  const int64_t g = r / (N / 16);
+  const int step = int(r % steps);
+  const int64_t g = r / steps;
   const int64_t n = panel * 16 + (lane & 15);
   const int kk = FP8 ? 64 * instr + 16 * (lane >> 4) : 32 * instr + 8 * (lane >> 4);
   const int64_t k = (int64_t)step * kKS + kk;

@@ -121,12 +121,12 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(TiledArgs ta) {
     const char* base;
     if (MODE == MODE_GATEUP) { row0 = n0 + 32 * wave + 16 * (n & 1); base = n < 2 ? Wa : Wb; }
     else { row0 = n0 + 64 * wave + 16 * n; base = Wa; }
-    if (PACKED) wsrc[n] = base + (int64_t)(row0 / 16) * 16 * Kdim * 2 + lane * 16;
+    if (PACKED) wsrc[n] = base + (int64_t)(row0 / 16) * 16 * 128 * 2 + lane * 16;
     else wsrc[n] = base + (int64_t)(row0 + (lane & 15)) * Kdim * 2 + 16 * (lane >> 4);
   }
   // byte offset of 32-wide K chunk kc (K = 32 kc) in a weight stream
   auto wk = [&](int kc) -> int64_t {
-    if (PACKED) return (int64_t)(kc >> 2) * 4096 + (kc & 3) * 1024;
+    if (PACKED) return (int64_t)(kc >> 2) * (a.N / 16) * 4096 + (kc & 3) * 1024;   // step-major
     return (int64_t)kc * 64;
   };
 

@@ -20,6 +20,7 @@
 //   kernel 3, one thread per choice: the choice's rank j among all tokens of
 //     its logical expert, its replica l2p[l][j mod R] and rank j / R inside
 //     that slot, its row, its buffer slot, and src_of.
+//   For T <= 64 (one block) the three run back to back in one workgroup.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -35,12 +36,12 @@ inline int topk_lanes(int E) {
   return l;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
+// one 64-token block b, by a workgroup of kTopkThreads threads
+__device__ __forceinline__ void topk_block(const RouteArgs& a, int b) {
   __shared__ unsigned long long mask[1024];
   __shared__ int ids_s[kBlockTokens * kMaxK];
   __shared__ int flag_s;
   const int E = a.E, K = a.K, T = a.T;
-  const int b = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += kTopkThreads) mask[e] = 0ull;
   if (tid == 0) flag_s = 0;
@@ -58,15 +59,16 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
     const float* row = a.logits + (int64_t)(valid ? t : 0) * E;
     uint64_t keys[16];
     bool bad = false;
+    // all loads issued unconditionally (clamped column), masked afterwards
+    float lv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) lv[j] = row[min(sl + j * LPT, E - 1)];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int e = sl + j * LPT;
-      keys[j] = 0ull;
-      if (valid && j < npl && e < E) {
-        const float v = row[e];
-        bad |= !__builtin_isfinite(v);
-        keys[j] = topk_key(v, e);
-      }
+      const bool in = valid && j < npl && e < E;
+      bad |= in && !__builtin_isfinite(lv[j]);
+      keys[j] = in ? topk_key(lv[j], e) : 0ull;
     }
     if (bad) atomicOr(&flag_s, 1);
     uint64_t prev = ~0ull;
@@ -122,9 +124,12 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) {
   if (tid == 0) a.ws.blk_flags[b] = flag_s;
 }
 
-constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) { topk_block(a, blockIdx.x); }
 
-__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(RouteArgs a) {
+constexpr int kScanThreads = 1024;
+static_assert(kScanThreads == kTopkThreads, "the fused route kernel runs both phases in one workgroup");
+
+__device__ __forceinline__ void scan_all(const RouteArgs& a) {
   __shared__ int cnt[kMaxE + 1];
   __shared__ int aux[kMaxE + 1];
   __shared__ int tl_s[1024];
@@ -225,10 +230,11 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(RouteArgs a) {
   }
 }
 
-__global__ __launch_bounds__(kRouteThreads) void route_assign_kernel(RouteArgs a) {
+__global__ __launch_bounds__(kScanThreads) void route_scan_kernel(RouteArgs a) { scan_all(a); }
+
+// choice i = t*K + k
+__device__ __forceinline__ void assign_one(const RouteArgs& a, int64_t i) {
   const int64_t TK = (int64_t)a.T * a.K;
-  const int64_t i = (int64_t)blockIdx.x * kRouteThreads + threadIdx.x;
-  if (i >= TK) return;
   const int t = int(i / a.K);
   const int l = a.topk_ids[i];
   const int b = t / kBlockTokens;
@@ -255,13 +261,32 @@ __global__ __launch_bounds__(kRouteThreads) void route_assign_kernel(RouteArgs a
   if (!ok) atomicOr(a.status, MOE_STATUS_INTERNAL);
 }
 
+__global__ __launch_bounds__(kRouteThreads) void route_assign_kernel(RouteArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * kRouteThreads + threadIdx.x;
+  if (i < (int64_t)a.T * a.K) assign_one(a, i);
+}
+
+// T <= 64: the three phases in one workgroup (one launch instead of three).
+// The barrier between phases orders the global-memory tables each phase
+// writes before the next one reads them.
+__global__ __launch_bounds__(kTopkThreads) void route_fused_kernel(RouteArgs a) {
+  if (a.T > 0) topk_block(a, 0);
+  __syncthreads();
+  scan_all(a);
+  __syncthreads();
+  const int64_t TK = (int64_t)a.T * a.K;
+  for (int64_t i = threadIdx.x; i < TK; i += kTopkThreads) assign_one(a, i);
+}
+
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const int nblk = (a.T + kBlockTokens - 1) / kBlockTokens;
-  if (nblk > 0) {
-    RouteArgs b = a;
-    b.topk_lanes = topk_lanes(a.E);
-    hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kTopkThreads), 0, s, b);
+  RouteArgs b = a;
+  b.topk_lanes = topk_lanes(a.E);
+  if (nblk <= 1) {
+    hipLaunchKernelGGL(route_fused_kernel, dim3(1), dim3(kTopkThreads), 0, s, b);
+    return hipGetLastError();
   }
+  hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kTopkThreads), 0, s, b);
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
   const int64_t TK = (int64_t)a.T * a.K;
   if (TK > 0) {

@@ -39,19 +39,19 @@ __global__ __launch_bounds__(256) void router_small_kernel(RouterArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) { xv[2 * q] = __uint_as_float(w[q] << 16); xv[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u); }
     }
+    // every W_r load is issued (rows past E re-read the last row, their sums
+    // are never stored), so none waits behind a branch
 #pragma unroll
     for (int e = 0; e < EB; ++e) {
-      if (e < ne) {
-        const u32x4 u = *reinterpret_cast<const u32x4*>(a.w + (int64_t)(eb + e) * a.H + h0);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-        float s = part[e];
+      const u32x4 u = *reinterpret_cast<const u32x4*>(a.w + (int64_t)(eb + min(e, ne - 1)) * a.H + h0);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      float s = part[e];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          s += xv[2 * q] * __uint_as_float(w[q] << 16);
-          s += xv[2 * q + 1] * __uint_as_float(w[q] & 0xffff0000u);
-        }
-        part[e] = s;
+      for (int q = 0; q < 4; ++q) {
+        s += xv[2 * q] * __uint_as_float(w[q] << 16);
+        s += xv[2 * q + 1] * __uint_as_float(w[q] & 0xffff0000u);
       }
+      part[e] = s;
     }
   }
 #pragma unroll

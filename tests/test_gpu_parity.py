@@ -274,7 +274,8 @@ def test_packed_weights_give_identical_outputs():
 
 def test_pack_layout_matches_definition():
     """moe_pack_weights places element (n, k) where the layout definition
-    says: panel n/16, K block k/128, then the lane piece of kk = k % 128."""
+    says: K block k/128, panel n/16 (step-major), then the lane piece of
+    kk = k % 128."""
     for w_dtype, dt in (("bf16", torch.bfloat16), ("fp8", torch.uint8)):
         cfg = configs.tiny().with_(H=256, I=384, w_dtype=w_dtype)
         d = B.Desc.from_config(cfg)
@@ -297,7 +298,7 @@ def test_pack_layout_matches_definition():
             within = kk % (32 if esz == 2 else 64)
             lane = 16 * (within // per_piece) + n % 16
             e = within % per_piece
-            piece = ((((g * (N // 16) + n // 16) * (Kd // 128) + k // 128) * NI + instr) * 64 + lane)
+            piece = ((((g * (Kd // 128) + k // 128) * (N // 16) + n // 16) * NI + instr) * 64 + lane)
             assert d_[piece * per_piece + e] == s_[g, n, k]
 
 
