@@ -76,6 +76,13 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of order_key on finite values (key 0, the NaN class, maps back to
+// NaN; -0 comes back as +0, which no arithmetic here tells apart).
+__device__ __forceinline__ float order_key_value(uint32_t k) {
+  if (k == 0u) return __uint_as_float(0x7fc00000u);
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // (value, id) packed so that a larger key is a larger value, ties to the
 // lower id.  A removed entry is 0, below every real key.
 __device__ __forceinline__ uint64_t topk_key(float v, int id) {

@@ -60,15 +60,18 @@ struct WStream {
   int step_bytes, instr_bytes, lane_bytes;
 };
 
-// Weights are read once per call and never again by this kernel, so the
-// loads are non-temporal: streamed past the caches instead of evicting the
-// activations and routing tables other workgroups still read.
-template <bool FP8>
+// NT: the weights are read once per call and never again, so the loads are
+// non-temporal, streamed past the caches instead of evicting the activations
+// and tables other workgroups still read.  Groups whose row-tile passes run
+// on several workgroups (region B) re-read their weights and load normally.
+template <bool FP8, bool NT>
 __device__ __forceinline__ void load_w(WFrag<FP8>& f, const WStream& w, int kstep) {
   const char* p = w.base + (int64_t)kstep * w.step_bytes + w.lane_bytes;
 #pragma unroll
-  for (int i = 0; i < WFrag<FP8>::NI; ++i)
-    f.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + i * w.instr_bytes));
+  for (int i = 0; i < WFrag<FP8>::NI; ++i) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(p + i * w.instr_bytes);
+    f.v[i] = NT ? __builtin_nontemporal_load(q) : *q;
+  }
 }
 
 template <bool FP8, bool PACKED>
@@ -105,15 +108,31 @@ __device__ __forceinline__ void tile_rows(int tile, int64_t s0, int c0, int nt0,
   else { const int u = tile - nt0; start = s1 + 16 * u; valid = min(16, c1 - 16 * u); }
 }
 
-template <bool FP8, int MODE, int MT, bool PACKED, bool XDIRECT>
-__global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
-  constexpr bool TWO = MODE == MODE_GATEUP;
-  static_assert(!XDIRECT || MT == 1, "register-staged activations hold one row tile");
-  __shared__ __attribute__((aligned(16))) uint16_t xs[XDIRECT ? 1 : 2][XDIRECT ? 1 : MT * 16][kLdsStride];
+// LDS activation tile of the MT > 1 passes: two buffers of MT*16 rows
+template <int MT>
+constexpr int lds_elems() { return MT > 1 ? 2 * MT * 16 * kLdsStride : 1; }
 
-  const int g = blockIdx.y;
-  const int ks = blockIdx.z % a.ksplit;
-  const int mc = blockIdx.z / a.ksplit;
+// Pipeline depth of the main size class: NB register banks, NB - 1 K steps
+// in flight.  An fp8 down step moves a quarter of the bytes of a bf16 gate/up
+// step and its registers leave room, so it keeps three steps in flight.  The
+// large-group class (region B) shares the kernel and its register count, so
+// with fp8, where the main class needs every register to keep three waves
+// per SIMD, it takes two row tiles per pass and one step in flight; with
+// bf16 it takes four tiles and two steps, like a launch of its own.
+template <bool FP8, int MODE>
+constexpr int banks_a() { return (FP8 && MODE == MODE_DOWN) ? 4 : 3; }
+template <bool FP8>
+constexpr int banks_b() { return FP8 ? 2 : 3; }
+template <bool FP8>
+constexpr int tiles_b() { return FP8 ? 2 : 4; }
+
+// The rows of group g if its row count is in (lo, hi] (hi = 0: no limit):
+// row-tile passes mc, mc + mch, ... of it, K split ks.
+template <bool FP8, int MODE, int MT, bool PACKED, int NB, bool NT>
+__device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks, int mc, int mch, int lo,
+                                             int hi, uint16_t* __restrict__ xs_raw) {
+  constexpr bool TWO = MODE == MODE_GATEUP;
+  constexpr bool XDIRECT = MT == 1;
   // ---- the group's row segments
   int64_t s0 = 0, s1 = 0;
   int c0 = 0, c1 = 0;
@@ -128,8 +147,8 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
   }
   const int nt0 = (c0 + 15) >> 4, nt1 = (c1 + 15) >> 4, ntiles = nt0 + nt1;
   if (ntiles == 0) return;   // no token: no weight load, no MFMA
-  // size classes: another launch owns groups outside (min_rows, max_rows]
-  if (c0 + c1 <= a.min_rows || (a.max_rows > 0 && c0 + c1 > a.max_rows)) return;
+  // size class: another part of the grid (or another launch) owns the rest
+  if (c0 + c1 <= lo || (hi > 0 && c0 + c1 > hi)) return;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
@@ -160,11 +179,14 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
   // ---- K range of this split
   const int steps = kb_per_row / a.ksplit;
   const int kstep0 = ks * steps;
+  const int klast = kstep0 + steps - 1;
 
-  // staging assignment: thread -> (row r of a 16-row tile, 16-byte chunk c)
+  using XS = uint16_t[MT * 16][kLdsStride];
+  XS* xs = reinterpret_cast<XS*>(xs_raw);
+  // staging assignment (MT > 1): thread -> (row r of a 16-row tile, 16-byte chunk c)
   const int sr = tid >> 4, sc = tid & 15;
 
-  for (int tile0 = mc * MT; tile0 < ntiles; tile0 += a.mchunks * MT) {
+  for (int tile0 = mc * MT; tile0 < ntiles; tile0 += mch * MT) {
     Pass<MT> ps;
     ps.n = min(MT, ntiles - tile0);
 #pragma unroll
@@ -173,107 +195,52 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
       if (m < ps.n) tile_rows(tile0 + m, s0, c0, nt0, s1, c1, ps.start[m], ps.valid[m]);
     }
 
-    if constexpr (XDIRECT) {
-      // One 16-row tile; each lane streams its own activation row (clamped
-      // into the valid rows) straight into registers, two K steps ahead like
-      // the weights.  Waves never synchronise.
-      const uint16_t* xrow = a.X + (ps.start[0] + min(lr, ps.valid[0] - 1)) * a.ldx;
-      auto xoff = [&](int q) { return FP8 ? 64 * (q >> 1) + 16 * lg + 8 * (q & 1) : 32 * q + 8 * lg; };
-      auto load_xd = [&](u32x4* v, int kstep) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          v[q] = *reinterpret_cast<const u32x4*>(xrow + (int64_t)kstep * kKS + xoff(q));
-      };
-      f32x4 acc1 = {0, 0, 0, 0}, acc3d = {0, 0, 0, 0};
-      const int klast = kstep0 + steps - 1;
-      WFrag<FP8> w1b[3], w3b[3];
-      u32x4 xb[3][4];
-      load_xd(xb[0], kstep0);
-      load_w<FP8>(w1b[0], w1s, kstep0);
-      if (TWO) load_w<FP8>(w3b[0], w3s, kstep0);
-      load_xd(xb[1], min(kstep0 + 1, klast));
-      load_w<FP8>(w1b[1], w1s, min(kstep0 + 1, klast));
-      if (TWO) load_w<FP8>(w3b[1], w3s, min(kstep0 + 1, klast));
-      for (int s0 = 0; s0 < steps; s0 += 3) {
-#pragma unroll
-        for (int u = 0; u < 3; ++u) {
-          const int s = s0 + u;
-          if (s < steps) {
-            load_xd(xb[(u + 2) % 3], min(kstep0 + s + 2, klast));
-            load_w<FP8>(w1b[(u + 2) % 3], w1s, min(kstep0 + s + 2, klast));
-            if (TWO) load_w<FP8>(w3b[(u + 2) % 3], w3s, min(kstep0 + s + 2, klast));
-            if (FP8) {
-              const float sc1 = Sg[sb_row + kstep0 + s];
-              const float sc3 = TWO ? S3g[sb_row + kstep0 + s] : 0.f;
-              bf16x8 a1[4], a3[4];
-#pragma unroll
-              for (int i = 0; i < 2; ++i) {
-                fp8x16_to_bf16(w1b[u].v[i], a1[2 * i], a1[2 * i + 1]);
-                if (TWO) fp8x16_to_bf16(w3b[u].v[i], a3[2 * i], a3[2 * i + 1]);
-              }
-              f32x4 p1 = {0, 0, 0, 0}, p3 = {0, 0, 0, 0};
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const bf16x8 b = __builtin_bit_cast(bf16x8, xb[u][q]);
-                p1 = mfma16x16x32(a1[q], b, p1);
-                if (TWO) p3 = mfma16x16x32(a3[q], b, p3);
-              }
-              acc1 += p1 * sc1;
-              if (TWO) acc3d += p3 * sc3;
-            } else {
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const bf16x8 b = __builtin_bit_cast(bf16x8, xb[u][q]);
-                acc1 = mfma16x16x32(__builtin_bit_cast(bf16x8, w1b[u].v[q]), b, acc1);
-                if (TWO) acc3d = mfma16x16x32(__builtin_bit_cast(bf16x8, w3b[u].v[q]), b, acc3d);
-              }
-            }
-          }
-        }
-      }
-      const int ncol = n_w0 + 4 * lg;
-      if (lr < ps.valid[0]) {
-        const int64_t row = ps.start[0] + lr;
-        if (MODE == MODE_GATEUP) {
-          u32x2 o = {pack_bf16x2(silu(acc1.x) * acc3d.x, silu(acc1.y) * acc3d.y),
-                     pack_bf16x2(silu(acc1.z) * acc3d.z, silu(acc1.w) * acc3d.w)};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
-        } else if (a.out_f32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ks * a.split_stride + row * a.ldo + ncol) = acc1;
-        } else {
-          u32x2 o = {pack_bf16x2(acc1.x, acc1.y), pack_bf16x2(acc1.z, acc1.w)};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
-        }
-      }
-      continue;
-    }
-
-    // Activation rows, clamped into the tile's valid rows (rows past the valid
-    // count only feed MFMA columns that are never stored).  The loads sit
-    // outside any divergent branch so the compiler never waits on them early.
+    // Activation sources, clamped into the tile's valid rows (rows past the
+    // valid count only feed MFMA columns that are never stored).  All loads
+    // sit outside any branch so the compiler never waits on them early.
+    // MT == 1: each lane streams its own row's MFMA fragments straight into
+    // registers and the waves never synchronise.  MT > 1: the workgroup
+    // stages the tiles into LDS, one 16-byte chunk per thread and tile.
     const uint16_t* xsrc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const int64_t row = (m < ps.n && ps.valid[m] > 0) ? ps.start[m] + min(sr, ps.valid[m] - 1) : s0;
-      xsrc[m] = a.X + row * a.ldx + 8 * sc;
+      const int r = XDIRECT ? lr : sr;
+      const int64_t row = (m < ps.n && ps.valid[m] > 0) ? ps.start[m] + min(r, ps.valid[m] - 1) : s0;
+      xsrc[m] = a.X + row * a.ldx + (XDIRECT ? 0 : 8 * sc);
     }
+    // K offset of MFMA operand q inside a 128-wide step for this lane:
+    // bf16 operand q covers 32q + 8*lg .. +8; an fp8 step's 16-byte weight
+    // piece i expands to operands 2i, 2i+1 covering 64i + 16*lg + 8*(q%2).
+    auto xoff = [&](int q) { return FP8 ? 64 * (q >> 1) + 16 * lg + 8 * (q & 1) : 32 * q + 8 * lg; };
+    constexpr int XV = XDIRECT ? 4 : MT;     // 16-byte activation loads per thread and step
     auto load_x = [&](int kstep, u32x4* xr) {
+      if constexpr (XDIRECT) {
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
-        xr[m] = *reinterpret_cast<const u32x4*>(xsrc[m] + (int64_t)kstep * kKS);
+        for (int q = 0; q < 4; ++q)
+          xr[q] = *reinterpret_cast<const u32x4*>(xsrc[0] + (int64_t)kstep * kKS + xoff(q));
+      } else {
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          xr[m] = *reinterpret_cast<const u32x4*>(xsrc[m] + (int64_t)kstep * kKS);
+      }
     };
     auto store_x = [&](int buf, const u32x4* xr) {
 #pragma unroll
       for (int m = 0; m < MT; ++m)
         *reinterpret_cast<u32x4*>(&xs[buf][m * 16 + sr][8 * sc]) = xr[m];
     };
+    // B operand q of tile m at K step buffer buf (MT > 1) or bank xr (MT == 1)
+    auto bop = [&](const u32x4* xr, int buf, int m, int q) -> bf16x8 {
+      if constexpr (XDIRECT) return __builtin_bit_cast(bf16x8, xr[q]);
+      else return *reinterpret_cast<const bf16x8*>(&xs[buf][m * 16 + lr][xoff(q)]);
+    };
 
     f32x4 acc[MT], acc3[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) { acc[m] = f32x4{0, 0, 0, 0}; acc3[m] = f32x4{0, 0, 0, 0}; }
 
-    // one K step: multiply the weights in (wa, wb) with the staged tile
-    auto compute = [&](const WFrag<FP8>& wa, const WFrag<FP8>& wb, int buf, int kstep) {
+    // one K step: multiply the weights in (wa, wb) with the step's activations
+    auto compute = [&](const WFrag<FP8>& wa, const WFrag<FP8>& wb, const u32x4* xr, int buf, int kstep) {
       if (FP8) {
         const float sc1 = Sg[sb_row + kstep];
         const float sc3 = TWO ? S3g[sb_row + kstep] : 0.f;
@@ -289,9 +256,7 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
             f32x4 p1 = {0, 0, 0, 0}, p3 = {0, 0, 0, 0};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              // operand q covers K offsets 64*(q/2) + 16*lg + 8*(q%2) .. +8
-              const bf16x8 b = *reinterpret_cast<const bf16x8*>(
-                  &xs[buf][m * 16 + lr][64 * (q >> 1) + 16 * lg + 8 * (q & 1)]);
+              const bf16x8 b = bop(xr, buf, m, q);
               p1 = mfma16x16x32(a1[q], b, p1);
               if (TWO) p3 = mfma16x16x32(a3[q], b, p3);
             }
@@ -304,46 +269,50 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
         for (int m = 0; m < MT; ++m) {
           if (m < ps.n) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const bf16x8 b = *reinterpret_cast<const bf16x8*>(&xs[buf][m * 16 + lr][32 * j + 8 * lg]);
-              acc[m] = mfma16x16x32(__builtin_bit_cast(bf16x8, wa.v[j]), b, acc[m]);
-              if (TWO) acc3[m] = mfma16x16x32(__builtin_bit_cast(bf16x8, wb.v[j]), b, acc3[m]);
+            for (int q = 0; q < 4; ++q) {
+              const bf16x8 b = bop(xr, buf, m, q);
+              acc[m] = mfma16x16x32(__builtin_bit_cast(bf16x8, wa.v[q]), b, acc[m]);
+              if (TWO) acc3[m] = mfma16x16x32(__builtin_bit_cast(bf16x8, wb.v[q]), b, acc3[m]);
             }
           }
         }
       }
     };
 
-    // Pipeline: at step s the weights of steps s+1, s+2 and the activations of
-    // step s+2 are in flight while step s is multiplied and the (already
-    // arrived) activations of step s+1 are staged.  Loads are issued
+    // Pipeline: at step s the weights (and activations) of steps s+1 ..
+    // s+NB-1 are in flight while step s is multiplied.  Loads are issued
     // activations-first: vector-memory counters drain in order, so waiting for
-    // an activation tile never waits for weights issued after it.  Steps past
-    // the end re-load the last K block (clamped) instead of branching around
-    // the loads; that data is never multiplied.
-    const int klast = kstep0 + steps - 1;
-    WFrag<FP8> w1b[3], w3b[3];
-    u32x4 xb[3][MT];
-    load_x(kstep0, xb[0]);
-    load_w<FP8>(w1b[0], w1s, kstep0);
-    if (TWO) load_w<FP8>(w3b[0], w3s, kstep0);
-    load_x(min(kstep0 + 1, klast), xb[1]);
-    load_w<FP8>(w1b[1], w1s, min(kstep0 + 1, klast));
-    if (TWO) load_w<FP8>(w3b[1], w3s, min(kstep0 + 1, klast));
-    store_x(0, xb[0]);
-    __syncthreads();
-
-    for (int s0 = 0; s0 < steps; s0 += 3) {
+    // an activation block never waits for weights issued after it.  Steps
+    // past the end re-load the last K block (clamped) instead of branching
+    // around the loads; that data is never multiplied.  MT > 1 stages step
+    // s+1's (already arrived) activations into the other LDS buffer and
+    // synchronises once per step.
+    WFrag<FP8> w1b[NB], w3b[NB];
+    u32x4 xb[NB][XV];
 #pragma unroll
-      for (int u = 0; u < 3; ++u) {
-        const int s = s0 + u;
+    for (int p = 0; p < NB - 1; ++p) {
+      load_x(min(kstep0 + p, klast), xb[p]);
+      load_w<FP8, NT>(w1b[p], w1s, min(kstep0 + p, klast));
+      if (TWO) load_w<FP8, NT>(w3b[p], w3s, min(kstep0 + p, klast));
+    }
+    if constexpr (!XDIRECT) {
+      store_x(0, xb[0]);
+      __syncthreads();
+    }
+    for (int s0i = 0; s0i < steps; s0i += NB) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int s = s0i + u;
         if (s < steps) {
-          load_x(min(kstep0 + s + 2, klast), xb[(u + 2) % 3]);
-          load_w<FP8>(w1b[(u + 2) % 3], w1s, min(kstep0 + s + 2, klast));
-          if (TWO) load_w<FP8>(w3b[(u + 2) % 3], w3s, min(kstep0 + s + 2, klast));
-          compute(w1b[u], w3b[u], s & 1, kstep0 + s);
-          store_x((s + 1) & 1, xb[(u + 1) % 3]);
-          __syncthreads();
+          const int nxt = (u + NB - 1) % NB;
+          load_x(min(kstep0 + s + NB - 1, klast), xb[nxt]);
+          load_w<FP8, NT>(w1b[nxt], w1s, min(kstep0 + s + NB - 1, klast));
+          if (TWO) load_w<FP8, NT>(w3b[nxt], w3s, min(kstep0 + s + NB - 1, klast));
+          compute(w1b[u], w3b[u], xb[u], s & 1, kstep0 + s);
+          if constexpr (!XDIRECT) {
+            store_x((s + 1) & 1, xb[(u + 1) % NB]);
+            __syncthreads();
+          }
         }
       }
     }
@@ -368,17 +337,45 @@ __global__ __launch_bounds__(kThreads) void ffn_stream_kernel(StreamArgs a) {
         }
       }
     }
+    if constexpr (!XDIRECT) __syncthreads();   // LDS buffer reuse by the next pass
   }
+}
+
+// grid (N / 64, b_rows + E_phys + n_shared, ksplit); region B exists only
+// when region A takes fewer than four tiles per pass.
+// fp8 single-tile launches fit three waves per SIMD (168 registers) once the
+// compiler is asked to
+template <bool FP8, int MTA>
+constexpr int min_waves() { return (FP8 && MTA == 1) ? 3 : 1; }
+
+template <bool FP8, int MODE, int MTA, bool PACKED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves<FP8, MTA>())))
+void ffn_stream_kernel(StreamArgs a) {
+  constexpr int TB = tiles_b<FP8>();
+  constexpr int LDS = lds_elems<(MTA < 4 && MTA < TB) ? TB : MTA>();
+  __shared__ __attribute__((aligned(16))) uint16_t xs_raw[LDS];
+  const int ks = blockIdx.z;
+  int y = blockIdx.y;
+  if constexpr (MTA < 4) {
+    if (y < a.b_rows) {
+      const int sh = a.b_rows - a.E_phys;   // n_shared * shared_chunks rows of the shared expert
+      if (y < sh) stream_group<FP8, MODE, TB, PACKED, banks_b<FP8>(), false>(a, a.E_phys, ks, y, a.shared_chunks,
+                                                                          a.max_rows, a.b_max_rows, xs_raw);
+      else stream_group<FP8, MODE, TB, PACKED, banks_b<FP8>(), true>(a, y - sh, ks, 0, 1, a.max_rows,
+                                                                   a.b_max_rows, xs_raw);
+      return;
+    }
+    y -= a.b_rows;
+  }
+  stream_group<FP8, MODE, MTA, PACKED, banks_a<FP8, MODE>(), true>(a, y, ks, 0, 1, 0, a.max_rows, xs_raw);
 }
 
 template <bool FP8, int MODE, bool PACKED>
 static hipError_t launch_mt(const StreamArgs& a, int mt, dim3 grid, hipStream_t s) {
-  // one row tile: activations staged in registers, no barriers; more tiles
-  // share an LDS activation tile between the four waves
   switch (mt) {
-    case 1: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 1, PACKED, true>), grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 2, PACKED, false>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 4, PACKED, false>), grid, dim3(kThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 1, PACKED>), grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 2, PACKED>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 4, PACKED>), grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -393,6 +390,8 @@ static hipError_t launch_mode(const StreamArgs& a, int fp8, int packed, int mt, 
 hipError_t launch_ffn_stream(const StreamArgs& a, int fp8, int packed, int mode, int mt, dim3 grid,
                              hipStream_t s) {
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
+  if (mt == 4 && a.b_rows != 0) return hipErrorInvalidValue;
+  if (a.b_rows != 0 && a.b_rows < a.E_phys) return hipErrorInvalidValue;
   if (mode == MODE_GATEUP) return launch_mode<MODE_GATEUP>(a, fp8, packed, mt, grid, s);
   if (mode == MODE_DOWN) return launch_mode<MODE_DOWN>(a, fp8, packed, mt, grid, s);
   return hipErrorInvalidValue;

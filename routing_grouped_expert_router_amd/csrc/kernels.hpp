@@ -14,6 +14,7 @@ struct RouteWs {            // views into the caller's route workspace
                             //           same logical expert
   int32_t* blk;             // [nblk*E] per-block counts -> exclusive prefixes
   int32_t* blk_flags;       // [nblk] non-finite flag per block
+  int32_t* tok_flag;        // [T_max] non-finite flag per token
   int32_t* map_valid;       // [1] 1 when a replica map is given and valid
 };
 
@@ -22,7 +23,6 @@ struct RouteArgs {
   const int32_t* l2p; const int32_t* rcount; int max_replicas;
   int layout, M_max, BM;
   int64_t routed_cap;       // rows of the routed part of the grouped buffer
-  int topk_lanes;           // lanes per token in the top-K kernel
   // outputs
   int32_t* topk_ids; float* topk_w; int32_t* topk_phys; int32_t* row_of;
   int32_t* slot_of; int32_t* src_of; int32_t* counts; int32_t* offsets;
@@ -64,12 +64,21 @@ struct StreamArgs {
   const void* W; const void* W3; const float* S; const float* S3;        // routed
   const void* SW; const void* SW3; const float* SS; const float* SS3;    // shared
   void* out; int64_t ldo; int64_t split_stride; int out_f32;
-  int ksplit;      // grid.z = ksplit * mchunks
-  int mchunks;     // row-tile passes dealt round-robin over grid.z
-  int min_rows;    // groups with at most this many rows are left to another launch
-  int max_rows;    // groups with more rows are left to another launch (0: no limit)
+  int ksplit;         // K splits over grid.z
+  // Two size classes share one launch; grid.y = b_rows + E_phys + n_shared.
+  // Region B, the first b_rows rows of grid.y (dispatched first): groups with
+  // more than max_rows rows (and at most b_max_rows; 0 = no limit),
+  // stream_tiles_b(fp8) row tiles per pass; its first n_shared * shared_chunks
+  // rows are the shared expert, whose passes are dealt over shared_chunks
+  // workgroup rows.
+  // Region A, the rest: groups with at most max_rows rows (0 = no limit).
+  int max_rows;
+  int b_rows, shared_chunks, b_max_rows;
 };
 
+// row tiles per pass of region B
+inline int stream_tiles_b(int fp8) { return fp8 ? 2 : 4; }
+// mt: row tiles per pass of region A (1, 2 or 4); grid.x = N / 64
 hipError_t launch_ffn_stream(const StreamArgs& a, int fp8, int packed, int mode, int mt, dim3 grid,
                              hipStream_t s);
 

@@ -16,7 +16,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 inline int64_t nblk_of(int64_t T) { return (T + kBlockTokens - 1) / kBlockTokens; }
 
-struct WsLayout { size_t local_rank, blk, flags, map_valid, total; };
+struct WsLayout { size_t local_rank, blk, flags, tok_flag, map_valid, total; };
 
 WsLayout ws_layout(const moe_desc_t* d) {
   WsLayout w;
@@ -25,7 +25,8 @@ WsLayout ws_layout(const moe_desc_t* d) {
   w.local_rank = 0;
   w.blk = w.local_rank + align_up(sizeof(int32_t) * (size_t)(TK > 0 ? TK : 1));
   w.flags = w.blk + align_up(sizeof(int32_t) * (size_t)((nb > 0 ? nb : 1) * d->E));
-  w.map_valid = w.flags + align_up(sizeof(int32_t) * (size_t)(nb > 0 ? nb : 1));
+  w.tok_flag = w.flags + align_up(sizeof(int32_t) * (size_t)(nb > 0 ? nb : 1));
+  w.map_valid = w.tok_flag + align_up(sizeof(int32_t) * (size_t)(d->T_max > 0 ? d->T_max : 1));
   w.total = w.map_valid + kAlign;
   return w;
 }
@@ -161,6 +162,7 @@ moe_status_t moe_route(const moe_desc_t* d, const float* logits, int32_t T, cons
   a.ws.local_rank = reinterpret_cast<int32_t*>(base + wl.local_rank);
   a.ws.blk = reinterpret_cast<int32_t*>(base + wl.blk);
   a.ws.blk_flags = reinterpret_cast<int32_t*>(base + wl.flags);
+  a.ws.tok_flag = reinterpret_cast<int32_t*>(base + wl.tok_flag);
   a.ws.map_valid = reinterpret_cast<int32_t*>(base + wl.map_valid);
   return hip_status(launch_route(a, stream));
 }
@@ -206,24 +208,28 @@ moe_status_t launch_expert_gemm(const moe_desc_t* d, const moe_route_t* r, int32
   const int mt = stream_mt(d, T);
   const bool tiled = tiled_supported(mode, fp8, a.N, a.Kdim, a.ksplit);
   const int a_max = 16 * mt;
-  const bool need_b = mt < 4 && T > a_max;
-  const bool need_c = tiled && T > 64;
-  a.min_rows = 0;
+  const bool need_b = mt < 4 && T > a_max;   // a group may outgrow region A
+  const bool need_c = tiled && T > 64;       // a group may outgrow the streaming kernel
   a.max_rows = (need_b || need_c) ? a_max : 0;
-  hipError_t e = launch_ffn_stream(a, fp8, d->w_packed, mode, mt, stream_grid, stream);
-  if (e != hipSuccess) return hip_status(e);
+  a.b_rows = 0;
+  a.shared_chunks = 1;
+  a.b_max_rows = 0;
+  dim3 grid = stream_grid;
   if (need_b) {
-    StreamArgs b = a;
-    b.min_rows = a_max;
-    b.max_rows = need_c ? 64 : 0;
-    e = launch_ffn_stream(b, fp8, d->w_packed, mode, 4, stream_grid, stream);
-    if (e != hipSuccess) return hip_status(e);
+    a.b_max_rows = need_c ? 64 : 0;
+    // the shared expert's T rows, when region B takes them, are split into
+    // passes on separate workgroup rows
+    const bool shared_in_b = d->n_shared && (a.b_max_rows == 0 || T <= a.b_max_rows);
+    const int tb = stream_tiles_b(fp8);
+    a.shared_chunks = shared_in_b ? ((T + 15) / 16 + tb - 1) / tb : 1;
+    a.b_rows = d->E_phys + d->n_shared * a.shared_chunks;
+    grid.y += a.b_rows;
   }
+  hipError_t e = launch_ffn_stream(a, fp8, d->w_packed, mode, mt, grid, stream);
+  if (e != hipSuccess) return hip_status(e);
   if (!need_c) return MOE_OK;
   TiledArgs ta;
   ta.s = a;
-  ta.s.min_rows = 0;
-  ta.s.max_rows = 0;
   ta.tile_off = r->tile_off;
   ta.min_rows = (mt < 4) ? 64 : a_max;
   const int64_t TK = (int64_t)T * d->K;
@@ -237,7 +243,7 @@ StreamArgs ffn_base_args(const moe_desc_t* d, const moe_route_t* r, int32_t T) {
   a.E_phys = d->E_phys; a.T = T; a.layout = d->layout; a.M_max = d->M_max;
   a.shared_base = routed_cap(d);
   a.counts = r->counts; a.masked_m = r->masked_m; a.spill_off = r->spill_off; a.pad_off = r->pad_off;
-  a.ksplit = 1; a.mchunks = 1;
+  a.ksplit = 1;
   return a;
 }
 

@@ -5,129 +5,145 @@
 // Method (vllbc blog "MoE inference and expert parallelism", routing section
 // and Table 3-1; vLLM forward path: top-k, then sort token/expert pairs by
 // expert; MoonEP online plan: counts -> offsets -> expert-grouped slots):
-//   kernel 1, one workgroup per 64-token block: a subgroup of lanes (the
-//     power of two >= E, 8..64) takes a token and finds its K largest logits
-//     by K rounds of a subgroup max over packed (value, ~id) keys; several
-//     tokens share a wave when E is small.  The block's choices set bits in
-//     one 64-bit mask per
-//     logical expert, from which each choice's rank among earlier tokens of
-//     the block and the block's count per expert follow by popcount.  OR is
-//     order-independent, so the result is deterministic.
-//   kernel 2, one workgroup: per-expert exclusive scan of the block counts,
+//   select, grid over tokens: a subgroup of LPT lanes (the power of two >= E,
+//     8..64) takes a token; each lane holds NPL = ceil(E / LPT) packed
+//     (value, ~id) keys, sorts them once, and each of the K rounds takes the
+//     subgroup max of the lanes' heads and pops it from its lane.  Several
+//     tokens share a wave when E is small.
+//   rank, one workgroup per 64-token block: the block's choices set bits in
+//     one 64-bit mask per logical expert, from which each choice's rank among
+//     earlier tokens of the block and the block's count per expert follow by
+//     popcount.  OR is order-independent, so the result is deterministic.
+//   scan, one workgroup: per-expert exclusive scan of the block counts,
 //     replica-map validation and the round-robin split into physical counts,
 //     then scans for offsets, spill offsets (masked) or padded offsets
 //     (contiguous), and the status word.
-//   kernel 3, one thread per choice: the choice's rank j among all tokens of
+//   assign, one thread per choice: the choice's rank j among all tokens of
 //     its logical expert, its replica l2p[l][j mod R] and rank j / R inside
 //     that slot, its row, its buffer slot, and src_of.
-//   For T <= 64 (one block) the three run back to back in one workgroup.
+//   For T <= 64 (one block) the four run back to back in one workgroup.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
 constexpr int kRouteThreads = 256;
-constexpr int kTopkThreads = 1024;   // 16 waves per 64-token block
+constexpr int kSelectThreads = 256;
+constexpr int kFusedThreads = 1024;   // 16 waves
 
-// lanes per token: the smallest power of two >= E, between 8 and 64
-inline int topk_lanes(int E) {
-  int l = 8;
-  while (l < E && l < 64) l <<= 1;
-  return l;
-}
+__device__ __forceinline__ uint64_t max_u64(uint64_t x, uint64_t y) { return x > y ? x : y; }
 
-// one 64-token block b, by a workgroup of kTopkThreads threads
-__device__ __forceinline__ void topk_block(const RouteArgs& a, int b) {
-  __shared__ unsigned long long mask[1024];
-  __shared__ int ids_s[kBlockTokens * kMaxK];
-  __shared__ int flag_s;
-  const int E = a.E, K = a.K, T = a.T;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += kTopkThreads) mask[e] = 0ull;
-  if (tid == 0) flag_s = 0;
-  __syncthreads();
-
-  // a token is handled by a subgroup of LPT lanes; a wave holds 64/LPT tokens
-  const int LPT = a.topk_lanes;
-  const int tpw = kWave / LPT;
+// Top-K of tokens t0 .. t0+count-1 (clamped to T), by `nwaves` waves of which
+// this is `wave`.  Writes topk_ids, topk_w and the per-token non-finite flag.
+template <int LPT, int NPL>
+__device__ __forceinline__ void select_tokens(const RouteArgs& a, int t0, int count, int wave, int nwaves) {
+  constexpr int TPW = kWave / LPT;   // tokens per wave and pass
+  const int E = a.E, K = a.K;
+  const int lane = threadIdx.x & (kWave - 1);
   const int sub = lane / LPT, sl = lane % LPT, sbase = sub * LPT;
-  const int npl = (E + LPT - 1) / LPT;           // logits per lane (<= 16)
-  for (int tl0 = wave * tpw; tl0 < kBlockTokens; tl0 += (kTopkThreads / kWave) * tpw) {
-    const int tl = tl0 + sub;
-    const int t = b * kBlockTokens + tl;
-    const bool valid = t < T;
+  for (int base = wave * TPW; base < count; base += nwaves * TPW) {
+    const int t = t0 + base + sub;
+    const bool valid = base + sub < count && t < a.T;
     const float* row = a.logits + (int64_t)(valid ? t : 0) * E;
-    uint64_t keys[16];
-    bool bad = false;
     // all loads issued unconditionally (clamped column), masked afterwards
-    float lv[16];
+    float lv[NPL];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) lv[j] = row[min(sl + j * LPT, E - 1)];
+    for (int j = 0; j < NPL; ++j) lv[j] = row[min(sl + j * LPT, E - 1)];
+    uint64_t keys[NPL];
+    bool bad = false;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < NPL; ++j) {
       const int e = sl + j * LPT;
-      const bool in = valid && j < npl && e < E;
+      const bool in = valid && e < E;
       bad |= in && !__builtin_isfinite(lv[j]);
       keys[j] = in ? topk_key(lv[j], e) : 0ull;
     }
-    if (bad) atomicOr(&flag_s, 1);
-    uint64_t prev = ~0ull;
-    int my_id = -1;
-    for (int k = 0; k < K; ++k) {
-      uint64_t best = 0ull;
+    // descending order inside the lane (keys are distinct unless 0)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint64_t c = keys[j] < prev ? keys[j] : 0ull;
-        best = c > best ? c : best;
+    for (int i = 1; i < NPL; ++i)
+#pragma unroll
+      for (int j = i; j > 0; --j) {
+        const uint64_t hi = max_u64(keys[j - 1], keys[j]);
+        const uint64_t lo = keys[j - 1] ^ keys[j] ^ hi;
+        keys[j - 1] = hi;
+        keys[j] = lo;
       }
-      // max over the LPT lanes of this subgroup
+    uint64_t my_key = 0ull;
+    for (int k = 0; k < K; ++k) {
+      uint64_t best = keys[0];
+#pragma unroll
       for (int off = LPT >> 1; off >= 1; off >>= 1) {
         const uint32_t lo = __shfl_xor((unsigned)(best & 0xffffffffu), off, kWave);
         const uint32_t hi = __shfl_xor((unsigned)(best >> 32), off, kWave);
-        const uint64_t o = (uint64_t(hi) << 32) | lo;
-        best = o > best ? o : best;
+        best = max_u64(best, (uint64_t(hi) << 32) | lo);
       }
-      prev = best;
-      const int id = int(0xffffffffu - uint32_t(best & 0xffffffffu));
-      if (sl == k) my_id = id;
+      if (sl == k) my_key = best;
+      // the lane holding the winner pops it (best == 0: nothing left, a no-op)
+      const bool win = keys[0] == best;
+#pragma unroll
+      for (int j = 0; j < NPL - 1; ++j) keys[j] = win ? keys[j + 1] : keys[j];
+      keys[NPL - 1] = win ? 0ull : keys[NPL - 1];
     }
+    // lane sl < K holds selection sl; its logit comes back out of the key
+    const int my_id = int(0xffffffffu - uint32_t(my_key & 0xffffffffu));
+    const float my_l = order_key_value(uint32_t(my_key >> 32));
     // weights: w_k = exp(l_k - l_0) / sum_j exp(l_j - l_0), sum in k order
-    const int id0 = __shfl(my_id, sbase, kWave);
-    const float l0 = valid ? row[id0] : 0.f;
-    float ek = 0.f, sum = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int idk = __shfl(my_id, sbase + k, kWave);
-      const float e = valid ? expf(row[idk] - l0) : 0.f;
-      sum += e;
-      if (sl == k) ek = e;
-    }
+    const float l0 = __shfl(my_l, sbase, kWave);
+    const float ek = (valid && sl < K) ? expf(my_l - l0) : 0.f;
+    float sum = 0.f;
+    for (int k = 0; k < K; ++k) sum += __shfl(ek, sbase + k, kWave);
+    const uint64_t badm = __ballot(bad);
     if (valid && sl < K) {
       // K <= E distinct positive keys always exist, so my_id is in [0, E)
       const int id = (my_id >= 0 && my_id < E) ? my_id : 0;
       a.topk_ids[(int64_t)t * K + sl] = id;
       a.topk_w[(int64_t)t * K + sl] = ek / sum;
-      ids_s[tl * K + sl] = id;
-      atomicOr(&mask[id], 1ull << tl);
     }
+    if (valid && sl == 0)
+      a.ws.tok_flag[t] = ((badm >> sbase) & (LPT == 64 ? ~0ull : ((1ull << LPT) - 1ull))) ? 1 : 0;
   }
+}
+
+template <int LPT, int NPL>
+__global__ __launch_bounds__(kSelectThreads) void route_select_kernel(RouteArgs a) {
+  constexpr int per_wg = (kSelectThreads / kWave) * (kWave / LPT);
+  select_tokens<LPT, NPL>(a, blockIdx.x * per_wg, per_wg, threadIdx.x / kWave, kSelectThreads / kWave);
+}
+
+// 64-token block b: masks per logical expert from topk_ids, then each
+// choice's rank inside the block, the block's counts and its non-finite flag.
+// Any workgroup size.
+__device__ __forceinline__ void rank_block(const RouteArgs& a, int b) {
+  __shared__ unsigned long long mask[1024];
+  __shared__ int flag_s;
+  const int E = a.E, K = a.K;
+  const int tid = threadIdx.x, nth = blockDim.x;
+  const int t0 = b * kBlockTokens;
+  const int nt = min(kBlockTokens, a.T - t0);
+  for (int e = tid; e < E; e += nth) mask[e] = 0ull;
+  if (tid == 0) flag_s = 0;
   __syncthreads();
-  for (int i = tid; i < kBlockTokens * K; i += kTopkThreads) {
-    const int tl = i / K, t = b * kBlockTokens + tl;
-    if (t < T) {
-      const int e = ids_s[i];
-      const unsigned long long below = tl ? (mask[e] & ((1ull << tl) - 1ull)) : 0ull;
-      a.ws.local_rank[(int64_t)t * K + (i - tl * K)] = __popcll(below);
-    }
+  for (int i = tid; i < nt * K; i += nth) {
+    const int id = a.topk_ids[(int64_t)t0 * K + i];
+    atomicOr(&mask[id], 1ull << (i / K));
   }
-  for (int e = tid; e < E; e += kTopkThreads)
-    a.ws.blk[(int64_t)b * E + e] = __popcll(mask[e]);
+  for (int tl = tid; tl < nt; tl += nth)
+    if (a.ws.tok_flag[t0 + tl]) atomicOr(&flag_s, 1);
+  __syncthreads();
+  for (int i = tid; i < nt * K; i += nth) {
+    const int tl = i / K;
+    const int id = a.topk_ids[(int64_t)t0 * K + i];
+    const unsigned long long below = tl ? (mask[id] & ((1ull << tl) - 1ull)) : 0ull;
+    a.ws.local_rank[(int64_t)t0 * K + i] = __popcll(below);
+  }
+  for (int e = tid; e < E; e += nth) a.ws.blk[(int64_t)b * E + e] = __popcll(mask[e]);
   if (tid == 0) a.ws.blk_flags[b] = flag_s;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(RouteArgs a) { topk_block(a, blockIdx.x); }
+__global__ __launch_bounds__(kRouteThreads) void route_rank_kernel(RouteArgs a) { rank_block(a, blockIdx.x); }
 
 constexpr int kScanThreads = 1024;
-static_assert(kScanThreads == kTopkThreads, "the fused route kernel runs both phases in one workgroup");
+static_assert(kScanThreads == kFusedThreads, "the fused route kernel runs every phase in one workgroup");
 
 __device__ __forceinline__ void scan_all(const RouteArgs& a) {
   __shared__ int cnt[kMaxE + 1];
@@ -266,33 +282,57 @@ __global__ __launch_bounds__(kRouteThreads) void route_assign_kernel(RouteArgs a
   if (i < (int64_t)a.T * a.K) assign_one(a, i);
 }
 
-// T <= 64: the three phases in one workgroup (one launch instead of three).
+// T <= 64: the four phases in one workgroup (one launch instead of four).
 // The barrier between phases orders the global-memory tables each phase
 // writes before the next one reads them.
-__global__ __launch_bounds__(kTopkThreads) void route_fused_kernel(RouteArgs a) {
-  if (a.T > 0) topk_block(a, 0);
+template <int LPT, int NPL>
+__global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(RouteArgs a) {
+  if (a.T > 0) {
+    select_tokens<LPT, NPL>(a, 0, a.T, threadIdx.x / kWave, kFusedThreads / kWave);
+    __syncthreads();
+    rank_block(a, 0);
+  }
   __syncthreads();
   scan_all(a);
   __syncthreads();
   const int64_t TK = (int64_t)a.T * a.K;
-  for (int64_t i = threadIdx.x; i < TK; i += kTopkThreads) assign_one(a, i);
+  for (int64_t i = threadIdx.x; i < TK; i += kFusedThreads) assign_one(a, i);
+}
+
+template <int LPT, int NPL>
+static void launch_shape(const RouteArgs& a, int nblk, hipStream_t s) {
+  // one block: a single launch, unless 16 keys per lane would not fit the
+  // registers of a 1024-thread workgroup
+  if (nblk <= 1 && NPL <= 8) {
+    hipLaunchKernelGGL((route_fused_kernel<LPT, NPL>), dim3(1), dim3(kFusedThreads), 0, s, a);
+    return;
+  }
+  constexpr int per_wg = (kSelectThreads / kWave) * (kWave / LPT);
+  if (a.T > 0)
+    hipLaunchKernelGGL((route_select_kernel<LPT, NPL>), dim3((a.T + per_wg - 1) / per_wg), dim3(kSelectThreads),
+                       0, s, a);
+  hipLaunchKernelGGL(route_rank_kernel, dim3(nblk > 0 ? nblk : 1), dim3(kRouteThreads), 0, s, a);
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
+  const int64_t TK = (int64_t)a.T * a.K;
+  if (TK > 0)
+    hipLaunchKernelGGL(route_assign_kernel, dim3((TK + kRouteThreads - 1) / kRouteThreads), dim3(kRouteThreads),
+                       0, s, a);
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   const int nblk = (a.T + kBlockTokens - 1) / kBlockTokens;
-  RouteArgs b = a;
-  b.topk_lanes = topk_lanes(a.E);
-  if (nblk <= 1) {
-    hipLaunchKernelGGL(route_fused_kernel, dim3(1), dim3(kTopkThreads), 0, s, b);
-    return hipGetLastError();
-  }
-  hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(kTopkThreads), 0, s, b);
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
-  const int64_t TK = (int64_t)a.T * a.K;
-  if (TK > 0) {
-    hipLaunchKernelGGL(route_assign_kernel, dim3((TK + kRouteThreads - 1) / kRouteThreads),
-                       dim3(kRouteThreads), 0, s, a);
-  }
+  // lanes per token: the smallest power of two >= E between 8 and 64; keys
+  // per lane: ceil(E / lanes) (E <= 1024)
+  const int E = a.E;
+  if (E <= 8) launch_shape<8, 1>(a, nblk, s);
+  else if (E <= 16) launch_shape<16, 1>(a, nblk, s);
+  else if (E <= 32) launch_shape<32, 1>(a, nblk, s);
+  else if (E <= 64) launch_shape<64, 1>(a, nblk, s);
+  else if (E <= 128) launch_shape<64, 2>(a, nblk, s);
+  else if (E <= 256) launch_shape<64, 4>(a, nblk, s);
+  else if (E <= 512) launch_shape<64, 8>(a, nblk, s);
+  else if (E <= 1024) launch_shape<64, 16>(a, nblk, s);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -51,6 +51,10 @@ def small_configs():
                    act_dtype="bf16", M_max=100),
         base.with_(name="tiled_contig_shared", T=300, H=512, I=384, E=4, E_phys=4, K=2, n_shared=1,
                    act_dtype="bf16", layout="contig", BM=128, bias="normal0.5"),
+        # fp8 with skewed groups: single-tile groups, hot groups of several
+        # tiles (the large-group class) and a shared expert split over chunks
+        base.with_(name="fp8_skewed_classes", T=100, H=512, I=256, E=32, E_phys=32, K=2, n_shared=1,
+                   act_dtype="bf16", w_dtype="fp8", M_max=64, bias="zipf1.1"),
     ]
 
 
