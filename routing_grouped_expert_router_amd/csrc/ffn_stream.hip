@@ -53,10 +53,12 @@ struct WFrag {
   u32x4 v[NI];
 };
 
-// Byte addressing of one wave's weight stream:
-//   address(kstep, i) = base + kstep * step_bytes + i * instr_bytes + lane_bytes
+// Byte addressing of one wave's weight stream, for the wave's 16 rows in the
+// j-th 64-row block of its workgroup:
+//   address(j, kstep, i) = base + j * blk_bytes + kstep * step_bytes + i * instr_bytes + lane_bytes
 struct WStream {
   const char* base;
+  int64_t blk_bytes;
   int step_bytes, instr_bytes, lane_bytes;
 };
 
@@ -65,8 +67,8 @@ struct WStream {
 // and tables other workgroups still read.  Groups whose row-tile passes run
 // on several workgroups (region B) re-read their weights and load normally.
 template <bool FP8, bool NT>
-__device__ __forceinline__ void load_w(WFrag<FP8>& f, const WStream& w, int kstep) {
-  const char* p = w.base + (int64_t)kstep * w.step_bytes + w.lane_bytes;
+__device__ __forceinline__ void load_w(WFrag<FP8>& f, const WStream& w, int j, int kstep) {
+  const char* p = w.base + j * w.blk_bytes + (int64_t)kstep * w.step_bytes + w.lane_bytes;
 #pragma unroll
   for (int i = 0; i < WFrag<FP8>::NI; ++i) {
     const u32x4* q = reinterpret_cast<const u32x4*>(p + i * w.instr_bytes);
@@ -83,11 +85,13 @@ __device__ __forceinline__ WStream make_stream(const void* Wg, int n_w0, int lan
     // step-major packed matrix
     s.base = static_cast<const char*>(Wg) + (int64_t)(n_w0 / 16) * 16 * kKS * wbytes;
     s.step_bytes = (N / 16) * 16 * kKS * wbytes;
+    s.blk_bytes = (int64_t)kBN * kKS * wbytes;      // four panels further
     s.instr_bytes = 1024;
     s.lane_bytes = 16 * lane;
   } else {
     s.base = static_cast<const char*>(Wg) + (int64_t)(n_w0 + (lane & 15)) * Kdim * wbytes;
     s.step_bytes = kKS * wbytes;
+    s.blk_bytes = (int64_t)kBN * Kdim * wbytes;     // 64 rows further
     s.instr_bytes = 64;
     s.lane_bytes = 16 * (lane >> 4);
   }
@@ -116,13 +120,13 @@ constexpr int lds_elems() { return MT > 1 ? 2 * MT * 16 * kLdsStride : 1; }
 // in flight.  An fp8 down step moves a quarter of the bytes of a bf16 gate/up
 // step and its registers leave room, so it keeps three steps in flight.  The
 // large-group class (region B) shares the kernel and its register count, so
-// with fp8, where the main class needs every register to keep three waves
-// per SIMD, it takes two row tiles per pass and one step in flight; with
-// bf16 it takes four tiles and two steps, like a launch of its own.
+// it never sets that count: with fp8 it takes two row tiles per pass and one
+// step in flight; with bf16 four tiles, and two steps in flight for gate/up
+// (whose main class needs more registers anyway) or one for down.
 template <bool FP8, int MODE>
 constexpr int banks_a() { return (FP8 && MODE == MODE_DOWN) ? 4 : 3; }
-template <bool FP8>
-constexpr int banks_b() { return FP8 ? 2 : 3; }
+template <bool FP8, int MODE>
+constexpr int banks_b() { return (FP8 || MODE == MODE_DOWN) ? 2 : 3; }
 template <bool FP8>
 constexpr int tiles_b() { return FP8 ? 2 : 4; }
 
@@ -152,7 +156,10 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const int n_w0 = blockIdx.x * kBN + wave * 16;   // first weight row of this wave
+  // the workgroup owns a.nblk consecutive 64-row blocks; first row of this
+  // wave in the first of them
+  const int nblk = a.nblk;
+  const int n_w0 = blockIdx.x * (kBN * nblk) + wave * 16;
   const int Kdim = a.Kdim;
   const int kb_per_row = Kdim / kKS;
 
@@ -174,12 +181,12 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
   }
   const WStream w1s = make_stream<FP8, PACKED>(Wg, n_w0, lane, a.N, Kdim);
   const WStream w3s = TWO ? make_stream<FP8, PACKED>(W3g, n_w0, lane, a.N, Kdim) : w1s;
-  const int sb_row = (n_w0 / 128) * kb_per_row;    // scale row of this wave's 16 rows
+  // scale row of this wave's 16 rows in block j
+  auto sb_row = [&](int j) { return ((n_w0 + kBN * j) / 128) * kb_per_row; };
 
   // ---- K range of this split
   const int steps = kb_per_row / a.ksplit;
   const int kstep0 = ks * steps;
-  const int klast = kstep0 + steps - 1;
 
   using XS = uint16_t[MT * 16][kLdsStride];
   XS* xs = reinterpret_cast<XS*>(xs_raw);
@@ -240,10 +247,10 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
     for (int m = 0; m < MT; ++m) { acc[m] = f32x4{0, 0, 0, 0}; acc3[m] = f32x4{0, 0, 0, 0}; }
 
     // one K step: multiply the weights in (wa, wb) with the step's activations
-    auto compute = [&](const WFrag<FP8>& wa, const WFrag<FP8>& wb, const u32x4* xr, int buf, int kstep) {
+    auto compute = [&](const WFrag<FP8>& wa, const WFrag<FP8>& wb, const u32x4* xr, int buf, int j, int kstep) {
       if (FP8) {
-        const float sc1 = Sg[sb_row + kstep];
-        const float sc3 = TWO ? S3g[sb_row + kstep] : 0.f;
+        const float sc1 = Sg[sb_row(j) + kstep];
+        const float sc3 = TWO ? S3g[sb_row(j) + kstep] : 0.f;
         bf16x8 a1[4], a3[4];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -279,64 +286,88 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
       }
     };
 
-    // Pipeline: at step s the weights (and activations) of steps s+1 ..
-    // s+NB-1 are in flight while step s is multiplied.  Loads are issued
-    // activations-first: vector-memory counters drain in order, so waiting for
-    // an activation block never waits for weights issued after it.  Steps
-    // past the end re-load the last K block (clamped) instead of branching
-    // around the loads; that data is never multiplied.  MT > 1 stages step
-    // s+1's (already arrived) activations into the other LDS buffer and
-    // synchronises once per step.
+    // ---- epilogue of block j: lane holds D[n = n_w0 + 64j + 4*lg + i][m = lr], i = 0..3
+    auto epilogue = [&](int j) {
+      const int ncol = n_w0 + kBN * j + 4 * lg;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m < ps.n && lr < ps.valid[m]) {
+          const int64_t row = ps.start[m] + lr;
+          if (MODE == MODE_GATEUP) {
+            const f32x4 gt = acc[m], up = acc3[m];
+            u32x2 o = {pack_bf16x2(silu(gt.x) * up.x, silu(gt.y) * up.y),
+                       pack_bf16x2(silu(gt.z) * up.z, silu(gt.w) * up.w)};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
+          } else if (a.out_f32) {
+            float* o = static_cast<float*>(a.out) + ks * a.split_stride + row * a.ldo + ncol;
+            *reinterpret_cast<f32x4*>(o) = acc[m];
+          } else {
+            u32x2 o = {pack_bf16x2(acc[m].x, acc[m].y), pack_bf16x2(acc[m].z, acc[m].w)};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
+          }
+        }
+        acc[m] = f32x4{0, 0, 0, 0};
+        acc3[m] = f32x4{0, 0, 0, 0};
+      }
+    };
+
+    // Pipeline.  The single-tile path (MT == 1) runs the workgroup's nblk
+    // blocks x steps K steps as one stream: at step v the weights and
+    // activations of steps v+1 .. v+NB-1 are in flight while step v is
+    // multiplied, across block boundaries too, so a short K range does not
+    // pay the load latency once per block.  MT > 1 runs one such stream per
+    // block (its registers are spent on row tiles), stages step v+1's
+    // (already arrived) activations into the other LDS buffer and
+    // synchronises once per step.  Loads are issued activations-first:
+    // vector-memory counters drain in order, so waiting for an activation
+    // block never waits for weights issued after it.  Steps past the end of
+    // a stream re-load its last step (clamped) instead of branching around
+    // the loads; that data is never multiplied.
+    constexpr bool FLAT = XDIRECT;
+    const int span = FLAT ? nblk : 1;       // blocks per stream
+    const int vsteps = span * steps;
     WFrag<FP8> w1b[NB], w3b[NB];
     u32x4 xb[NB][XV];
+    for (int jb = 0; jb < nblk; jb += span) {
+      int lj = jb, lk = 0;   // block and K step of the next loads
+      auto issue = [&](int bank) {
+        const bool in = lj < jb + span;
+        const int j = in ? lj : jb + span - 1;
+        const int k = kstep0 + (in ? lk : steps - 1);
+        load_x(k, xb[bank]);
+        load_w<FP8, NT>(w1b[bank], w1s, j, k);
+        if (TWO) load_w<FP8, NT>(w3b[bank], w3s, j, k);
+        if (++lk == steps) { lk = 0; ++lj; }
+      };
 #pragma unroll
-    for (int p = 0; p < NB - 1; ++p) {
-      load_x(min(kstep0 + p, klast), xb[p]);
-      load_w<FP8, NT>(w1b[p], w1s, min(kstep0 + p, klast));
-      if (TWO) load_w<FP8, NT>(w3b[p], w3s, min(kstep0 + p, klast));
-    }
-    if constexpr (!XDIRECT) {
-      store_x(0, xb[0]);
-      __syncthreads();
-    }
-    for (int s0i = 0; s0i < steps; s0i += NB) {
+      for (int p = 0; p < NB - 1; ++p) issue(p);
+      if constexpr (!XDIRECT) {
+        store_x(0, xb[0]);
+        __syncthreads();
+      }
+      int cj = jb, ck = 0;   // block and K step being multiplied
+      for (int v0 = 0; v0 < vsteps; v0 += NB) {
 #pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int s = s0i + u;
-        if (s < steps) {
-          const int nxt = (u + NB - 1) % NB;
-          load_x(min(kstep0 + s + NB - 1, klast), xb[nxt]);
-          load_w<FP8, NT>(w1b[nxt], w1s, min(kstep0 + s + NB - 1, klast));
-          if (TWO) load_w<FP8, NT>(w3b[nxt], w3s, min(kstep0 + s + NB - 1, klast));
-          compute(w1b[u], w3b[u], xb[u], s & 1, kstep0 + s);
-          if constexpr (!XDIRECT) {
-            store_x((s + 1) & 1, xb[(u + 1) % NB]);
-            __syncthreads();
+        for (int u = 0; u < NB; ++u) {
+          const int v = v0 + u;
+          if (v < vsteps) {
+            issue((u + NB - 1) % NB);
+            compute(w1b[u], w3b[u], xb[u], v & 1, cj, kstep0 + ck);
+            if constexpr (!XDIRECT) {
+              store_x((v + 1) & 1, xb[(u + 1) % NB]);
+              __syncthreads();
+            }
+            if constexpr (FLAT) {
+              if (++ck == steps) { epilogue(cj); ck = 0; ++cj; }
+            } else {
+              ++ck;
+            }
           }
         }
       }
+      if constexpr (!FLAT) epilogue(jb);
     }
 
-    // ---- epilogue: lane holds D[n = n_w0 + 4*lg + j][m = lr], j = 0..3
-    const int ncol = n_w0 + 4 * lg;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m < ps.n && lr < ps.valid[m]) {
-        const int64_t row = ps.start[m] + lr;
-        if (MODE == MODE_GATEUP) {
-          const f32x4 gt = acc[m], up = acc3[m];
-          u32x2 o = {pack_bf16x2(silu(gt.x) * up.x, silu(gt.y) * up.y),
-                     pack_bf16x2(silu(gt.z) * up.z, silu(gt.w) * up.w)};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
-        } else if (a.out_f32) {
-          float* o = static_cast<float*>(a.out) + ks * a.split_stride + row * a.ldo + ncol;
-          *reinterpret_cast<f32x4*>(o) = acc[m];
-        } else {
-          u32x2 o = {pack_bf16x2(acc[m].x, acc[m].y), pack_bf16x2(acc[m].z, acc[m].w)};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
-        }
-      }
-    }
     if constexpr (!XDIRECT) __syncthreads();   // LDS buffer reuse by the next pass
   }
 }
@@ -359,9 +390,9 @@ void ffn_stream_kernel(StreamArgs a) {
   if constexpr (MTA < 4) {
     if (y < a.b_rows) {
       const int sh = a.b_rows - a.E_phys;   // n_shared * shared_chunks rows of the shared expert
-      if (y < sh) stream_group<FP8, MODE, TB, PACKED, banks_b<FP8>(), false>(a, a.E_phys, ks, y, a.shared_chunks,
+      if (y < sh) stream_group<FP8, MODE, TB, PACKED, banks_b<FP8, MODE>(), false>(a, a.E_phys, ks, y, a.shared_chunks,
                                                                           a.max_rows, a.b_max_rows, xs_raw);
-      else stream_group<FP8, MODE, TB, PACKED, banks_b<FP8>(), true>(a, y - sh, ks, 0, 1, a.max_rows,
+      else stream_group<FP8, MODE, TB, PACKED, banks_b<FP8, MODE>(), true>(a, y - sh, ks, 0, 1, a.max_rows,
                                                                    a.b_max_rows, xs_raw);
       return;
     }
@@ -390,6 +421,7 @@ static hipError_t launch_mode(const StreamArgs& a, int fp8, int packed, int mt, 
 hipError_t launch_ffn_stream(const StreamArgs& a, int fp8, int packed, int mode, int mt, dim3 grid,
                              hipStream_t s) {
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
+  if (a.nblk < 1 || a.nblk > 8 || (int64_t)grid.x * 64 * a.nblk != a.N) return hipErrorInvalidValue;
   if (mt == 4 && a.b_rows != 0) return hipErrorInvalidValue;
   if (a.b_rows != 0 && a.b_rows < a.E_phys) return hipErrorInvalidValue;
   if (mode == MODE_GATEUP) return launch_mode<MODE_GATEUP>(a, fp8, packed, mt, grid, s);

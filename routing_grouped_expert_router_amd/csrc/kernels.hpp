@@ -65,6 +65,7 @@ struct StreamArgs {
   const void* SW; const void* SW3; const float* SS; const float* SS3;    // shared
   void* out; int64_t ldo; int64_t split_stride; int out_f32;
   int ksplit;         // K splits over grid.z
+  int nblk;           // consecutive 64-row output blocks per workgroup (1..8); grid.x = N / (64 * nblk)
   // Two size classes share one launch; grid.y = b_rows + E_phys + n_shared.
   // Region B, the first b_rows rows of grid.y (dispatched first): groups with
   // more than max_rows rows (and at most b_max_rows; 0 = no limit),
@@ -78,7 +79,7 @@ struct StreamArgs {
 
 // row tiles per pass of region B
 inline int stream_tiles_b(int fp8) { return fp8 ? 2 : 4; }
-// mt: row tiles per pass of region A (1, 2 or 4); grid.x = N / 64
+// mt: row tiles per pass of region A (1, 2 or 4); grid.x = N / (64 * nblk)
 hipError_t launch_ffn_stream(const StreamArgs& a, int fp8, int packed, int mode, int mt, dim3 grid,
                              hipStream_t s);
 

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <cstdlib>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -203,9 +205,36 @@ moe_status_t ffn_common_checks(const moe_desc_t* d, const moe_weights_t* w, cons
 //                                  otherwise class B takes these groups too)
 // A class is launched only if T allows a group of its size (a routed group
 // has at most T rows, the shared group exactly T).
+// 64-row output blocks per streaming workgroup.  With fp8 weights and a
+// short K range (an fp8 K step is half the bytes of a bf16 one) a workgroup
+// would spend a large share of its life waiting for its first loads, so it
+// walks several blocks as one pipelined stream, up to 64 K steps, while at
+// least 6144 workgroups (about eight rounds of the chip) remain; fewer,
+// longer workgroups would leave the chip idle at the end of the launch.
+// Measured: it pays for fp8 down projections with K = 2048 and costs time for
+// bf16 ones.  MOE_STREAM_NBLK (1..8, dividing N/64) overrides the choice.
+int stream_nblk(const moe_desc_t* d, int32_t T, const StreamArgs& a, bool fp8) {
+  const int nblocks = a.N / 64;
+  const int steps = a.Kdim / 128 / a.ksplit;
+  if (const char* env = getenv("MOE_STREAM_NBLK")) {
+    const int v = atoi(env);
+    if (v >= 1 && v <= 8 && nblocks % v == 0) return v;
+  }
+  if (!fp8) return 1;
+  const int64_t TK = (int64_t)T * d->K;
+  const int64_t groups = (TK < d->E_phys ? TK : d->E_phys) + d->n_shared;
+  int nb = 1;
+  while (nb < 8 && steps * nb * 2 <= 64 && nblocks % (nb * 2) == 0 &&
+         groups * (nblocks / (nb * 2)) * a.ksplit >= 6144)
+    nb *= 2;
+  return nb;
+}
+
 moe_status_t launch_expert_gemm(const moe_desc_t* d, const moe_route_t* r, int32_t T, StreamArgs a,
                                 bool fp8, int mode, dim3 stream_grid, hipStream_t stream) {
   const int mt = stream_mt(d, T);
+  a.nblk = stream_nblk(d, T, a, fp8);
+  stream_grid.x = a.N / (64 * a.nblk);
   const bool tiled = tiled_supported(mode, fp8, a.N, a.Kdim, a.ksplit);
   const int a_max = 16 * mt;
   const bool need_b = mt < 4 && T > a_max;   // a group may outgrow region A
@@ -244,6 +273,7 @@ StreamArgs ffn_base_args(const moe_desc_t* d, const moe_route_t* r, int32_t T) {
   a.shared_base = routed_cap(d);
   a.counts = r->counts; a.masked_m = r->masked_m; a.spill_off = r->spill_off; a.pad_off = r->pad_off;
   a.ksplit = 1;
+  a.nblk = 1;
   return a;
 }
 

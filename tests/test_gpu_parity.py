@@ -276,6 +276,24 @@ def test_packed_weights_give_identical_outputs():
         assert torch.equal(a.run(lg).clone(), p.run(lg).clone()), cfg.name
 
 
+@pytest.mark.parametrize("nblk", [2, 4])
+def test_block_walk_gives_identical_outputs(nblk, monkeypatch):
+    """A streaming workgroup that walks several 64-row output blocks as one
+    pipelined stream (MOE_STREAM_NBLK forces the count) reduces every output
+    over the same K steps in the same order: bit-identical outputs."""
+    for cfg in (SMALL[1], SMALL[3], SMALL[9]):
+        for packed in (False, True):
+            b = Built(cfg, packed=packed)
+            lg = b.oracle_logits()
+            ref = b.run(lg).clone()
+            monkeypatch.setenv("MOE_STREAM_NBLK", str(nblk))
+            try:
+                out = b.run(lg).clone()
+            finally:
+                monkeypatch.delenv("MOE_STREAM_NBLK")
+            assert torch.equal(ref, out), (cfg.name, packed, nblk)
+
+
 def test_pack_layout_matches_definition():
     """moe_pack_weights places element (n, k) where the layout definition
     says: K block k/128, panel n/16 (step-major), then the lane piece of
