@@ -175,7 +175,9 @@ def time_workload(cfg, steps, warmup, packed=True):
 
 PREFILL_MIN_T = 1024   # token counts from here on are timed against the MFMA peak
 
-KERNEL_SOURCES = ("common.hpp", "kernels.hpp", "ffn_stream.hip", "ffn_tiled.hip", "moe_api.hip")
+# sources of the decode gate/up kernel and its launch (the decode path never
+# launches the tiled kernel)
+KERNEL_SOURCES = ("common.hpp", "kernels.hpp", "ffn_stream.hip", "moe_api.hip")
 
 
 def kernel_sources_hash() -> str:
