@@ -8,8 +8,9 @@
 //
 //  * Workgroup tile: 128 token rows x 256 weight rows (MODE_GATEUP: 128 gate
 //    rows of W1 + the same 128 rows of W3, so SiLU(g) * u pairs sit in one
-//    wave; MODE_DOWN: 256 rows of W2).  Four waves as 2 (rows) x 2 (weight
-//    rows); each wave owns 64 x 128 outputs = 4 x 8 MFMA tiles of 16 x 16.
+//    wave; MODE_DOWN: 256 rows of W2).  Four waves split the weight rows; each
+//    wave owns all 128 token rows x 64 weight rows = 8 x 4 MFMA
+//    tiles of 16 x 16.
 //  * K advances in 64-wide stages, double-buffered in LDS.  Both operands are
 //    stored in MFMA fragment order (per 16-row tile and 32-wide K step, the
 //    16-byte piece of each lane, slots rotated by swz() against bank
@@ -18,9 +19,15 @@
 //    memory latency.
 //  * Work list: slot p owns ceil(T_p / 128) row tiles, the shared expert
 //    ceil(T / 128), in the prefix tile_off; each row tile pairs with every
-//    weight-row tile.  The list is dealt to the XCDs in contiguous chunks so
-//    an XCD's L2 holds one group's tiles at a time.  Groups with at most
-//    `min_rows` rows are left to the streaming kernel, launched alongside.
+//    weight-row tile.  The list is ordered (group, weight tile, row tile) and
+//    dealt to the XCDs in contiguous chunks, so the row tiles that share a
+//    weight tile run back to back on one XCD and the later ones find it in
+//    that XCD's L2.  Groups with at most `min_rows` rows are left to the
+//    streaming kernel.
+//  * A group's last row tile is usually partly empty (groups are 28..961
+//    rows at the prefill workload): the tile is run with only its non-empty
+//    32-row sub-tiles (a compile-time count, one instance per count), so no
+//    MFMA, LDS read or activation load is spent on whole pad sub-tiles.
 //  * Each output element accumulates its K range in 32-wide MFMA steps in
 //    ascending order, exactly as the streaming kernel does, so the split of
 //    groups between the two kernels does not change any bit of the result.
@@ -28,6 +35,9 @@
 #include "kernels.hpp"
 
 namespace moe {
+
+template <int V>
+struct IntC { static constexpr int value = V; };
 
 constexpr int kTM = 128;     // token rows per tile
 constexpr int kTN = 256;     // weight rows per tile
@@ -58,7 +68,7 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(TiledArgs ta) {
   // ---- work item.  The hardware deals workgroups round-robin over the 8 XCDs
   // (linear id L goes to XCD L % 8).  The live work list -- tile_off's
   // ceil(rows/128) tiles per group times the weight-row tiles -- is cut into 8
-  // contiguous chunks, one per XCD, ordered (group, row tile, weight tile), so
+  // contiguous chunks, one per XCD, ordered (group, weight tile, row tile), so
   // the workgroups an XCD runs together share one group's weight and
   // activation tiles in that XCD's L2.
   const int ngroups = a.E_phys + 1;
@@ -70,15 +80,16 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(TiledArgs ta) {
   if (k_in >= chunk) return;
   const int64_t wi = (L % 8) * chunk + k_in;
   if (wi >= work) return;
-  const int i = int(wi / ntiles_n);          // row tile in the work list
-  const int nt = int(wi % ntiles_n);         // weight-row tile
-  int lo = 0, hi = ngroups;                  // largest g with tile_off[g] <= i
+  int lo = 0, hi = ngroups;                  // largest g with tile_off[g] * ntiles_n <= wi
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (ta.tile_off[mid] <= i) lo = mid; else hi = mid;
+    if ((int64_t)ta.tile_off[mid] * ntiles_n <= wi) lo = mid; else hi = mid;
   }
   const int g = lo;
-  const int mt = i - ta.tile_off[g];
+  const int mtiles = ta.tile_off[g + 1] - ta.tile_off[g];
+  const int64_t o = wi - (int64_t)ta.tile_off[g] * ntiles_n;
+  const int nt = int(o / mtiles);            // weight-row tile
+  const int mt = int(o % mtiles);            // row tile within the group
   int64_t s0 = 0, s1 = 0;
   int c0 = 0, c1 = 0;
   const bool shared = g == a.E_phys;
@@ -144,96 +155,109 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(TiledArgs ta) {
     xdst[q] = (((r >> 4) * 2 + (xc >> 2)) * 64 + swz(16 * (xc & 3) + (r & 15), xc >> 2)) * 16;
   }
 
-  // Global loads run two stages ahead through three register banks (per
-  // stage: the activation pieces first, then the weights; vector-memory
-  // counters drain in order, so staging the activations never waits for the
-  // weights issued after them).
-  u32x4 xr[3][4], wr[3][4][2];
-  auto gload = [&](int bank, int stage) {
-    const int k0 = kbeg + stage * kTK;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xr[bank][q] = *reinterpret_cast<const u32x4*>(xsrc[q] + (int64_t)k0 * 2);
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        wr[bank][n][j] = *reinterpret_cast<const u32x4*>(wsrc[n] + wk(k0 / 32 + j));
-  };
-  auto lstore = [&](int bank, int buf) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) *reinterpret_cast<u32x4*>(xsm + buf * kXStage + xdst[q]) = xr[bank][q];
-  };
+  // the tile's non-empty 16-row tiles, rounded up to 32-row sub-tiles
+  const int rows_here = min(kTM, R - m0);
+  const int mv = ((rows_here + 31) / 32) * 2;
+  auto run = [&](auto mvc) {
+    // Global loads run two stages ahead through three register banks (per
+    // stage: the activation pieces first, then the weights; vector-memory
+    // counters drain in order, so staging the activations never waits for the
+    // weights issued after them).
+    constexpr int MV = decltype(mvc)::value;    // non-empty 16-row tiles (even)
+    constexpr int XQ = MV / 2;                   // activation pieces per thread and stage
+    u32x4 xr[3][XQ], wr[3][4][2];
+    auto gload = [&](int bank, int stage) {
+      const int k0 = kbeg + stage * kTK;
+  #pragma unroll
+      for (int q = 0; q < XQ; ++q) xr[bank][q] = *reinterpret_cast<const u32x4*>(xsrc[q] + (int64_t)k0 * 2);
+  #pragma unroll
+      for (int n = 0; n < 4; ++n)
+  #pragma unroll
+        for (int j = 0; j < 2; ++j)
+          wr[bank][n][j] = *reinterpret_cast<const u32x4*>(wsrc[n] + wk(k0 / 32 + j));
+    };
+    auto lstore = [&](int bank, int buf) {
+  #pragma unroll
+      for (int q = 0; q < XQ; ++q) *reinterpret_cast<u32x4*>(xsm + buf * kXStage + xdst[q]) = xr[bank][q];
+    };
 
-  f32x4 acc[8][4];
-#pragma unroll
-  for (int m = 0; m < 8; ++m)
-#pragma unroll
-    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0, 0, 0, 0};
+    f32x4 acc[MV][4];
+  #pragma unroll
+    for (int m = 0; m < MV; ++m)
+  #pragma unroll
+      for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0, 0, 0, 0};
 
-  auto compute = [&](int bank, int buf) {
-    const char* xb = xsm + buf * kXStage;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      bf16x8 xf[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-        xf[m] = *reinterpret_cast<const bf16x8*>(xb + ((m * 2 + j) * 64 + swz(lane, j)) * 16);
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-          acc[m][n] = mfma16x16x32(__builtin_bit_cast(bf16x8, wr[bank][n][j]), xf[m], acc[m][n]);
-    }
-  };
-
-  // Stages past the end re-load the last stage (clamped) instead of branching
-  // around loads; the extra LDS copy goes to the buffer not being read.
-  const int slast = nstages - 1;
-  gload(0, 0);
-  gload(1, min(1, slast));
-  lstore(0, 0);
-  __syncthreads();
-  for (int s0 = 0; s0 < nstages; s0 += 3) {
-#pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      const int st = s0 + u;
-      if (st < nstages) {
-        gload((u + 2) % 3, min(st + 2, slast));
-        compute(u, st & 1);
-        lstore((u + 1) % 3, (st + 1) & 1);   // that buffer was last read before the previous barrier
-        __syncthreads();
+    auto compute = [&](int bank, int buf) {
+      const char* xb = xsm + buf * kXStage;
+  #pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bf16x8 xf[MV];
+  #pragma unroll
+        for (int m = 0; m < MV; ++m)
+          xf[m] = *reinterpret_cast<const bf16x8*>(xb + ((m * 2 + j) * 64 + swz(lane, j)) * 16);
+  #pragma unroll
+        for (int m = 0; m < MV; ++m)
+  #pragma unroll
+          for (int n = 0; n < 4; ++n)
+            acc[m][n] = mfma16x16x32(__builtin_bit_cast(bf16x8, wr[bank][n][j]), xf[m], acc[m][n]);
       }
-    }
-  }
+    };
 
-  // ---- epilogue: acc[m][n] holds D[w-row 4*(lane/16)+j of tile n][token lane%16 of tile m]
-  const int lr = lane & 15, lg = lane >> 4;
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int gr = m0 + m * 16 + lr;                    // row within the group
-    if (gr >= R) continue;
-    const int64_t row = gr < c0 ? s0 + gr : s1 + (gr - c0);
-    if (MODE == MODE_GATEUP) {
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const f32x4 gt = acc[m][n], up = acc[m][n + 2];
-        const int ncol = n0 + 32 * wave + 16 * n + 4 * lg;
-        u32x2 o = {pack_bf16x2(silu_t(gt.x) * up.x, silu_t(gt.y) * up.y),
-                   pack_bf16x2(silu_t(gt.z) * up.z, silu_t(gt.w) * up.w)};
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
-      }
-    } else {
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const int ncol = n0 + 64 * wave + 16 * n + 4 * lg;
-        if (a.out_f32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ks * a.split_stride + row * a.ldo + ncol) = acc[m][n];
-        } else {
-          u32x2 o = {pack_bf16x2(acc[m][n].x, acc[m][n].y), pack_bf16x2(acc[m][n].z, acc[m][n].w)};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
+    // Stages past the end re-load the last stage (clamped) instead of branching
+    // around loads; the extra LDS copy goes to the buffer not being read.
+    const int slast = nstages - 1;
+    gload(0, 0);
+    gload(1, min(1, slast));
+    lstore(0, 0);
+    __syncthreads();
+    for (int s0 = 0; s0 < nstages; s0 += 3) {
+  #pragma unroll
+      for (int u = 0; u < 3; ++u) {
+        const int st = s0 + u;
+        if (st < nstages) {
+          gload((u + 2) % 3, min(st + 2, slast));
+          compute(u, st & 1);
+          lstore((u + 1) % 3, (st + 1) & 1);   // that buffer was last read before the previous barrier
+          __syncthreads();
         }
       }
     }
+
+    // ---- epilogue: acc[m][n] holds D[w-row 4*(lane/16)+j of tile n][token lane%16 of tile m]
+    const int lr = lane & 15, lg = lane >> 4;
+  #pragma unroll
+    for (int m = 0; m < MV; ++m) {
+      const int gr = m0 + m * 16 + lr;                    // row within the group
+      if (gr >= R) continue;
+      const int64_t row = gr < c0 ? s0 + gr : s1 + (gr - c0);
+      if (MODE == MODE_GATEUP) {
+  #pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const f32x4 gt = acc[m][n], up = acc[m][n + 2];
+          const int ncol = n0 + 32 * wave + 16 * n + 4 * lg;
+          u32x2 o = {pack_bf16x2(silu_t(gt.x) * up.x, silu_t(gt.y) * up.y),
+                     pack_bf16x2(silu_t(gt.z) * up.z, silu_t(gt.w) * up.w)};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
+        }
+      } else {
+  #pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const int ncol = n0 + 64 * wave + 16 * n + 4 * lg;
+          if (a.out_f32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ks * a.split_stride + row * a.ldo + ncol) = acc[m][n];
+          } else {
+            u32x2 o = {pack_bf16x2(acc[m][n].x, acc[m][n].y), pack_bf16x2(acc[m][n].z, acc[m][n].w)};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
+          }
+        }
+      }
+    }
+  };
+  switch (mv) {
+    case 2: run(IntC<2>{}); break;
+    case 4: run(IntC<4>{}); break;
+    case 6: run(IntC<6>{}); break;
+    default: run(IntC<8>{}); break;
   }
 }
 
