@@ -14,9 +14,9 @@
 //  * K advances in 64-wide stages, double-buffered in LDS.  Both operands are
 //    stored in MFMA fragment order (per 16-row tile and 32-wide K step, the
 //    16-byte piece of each lane, slots rotated by swz() against bank
-//    conflicts), so every operand read is one conflict-free ds_read_b128.  Global loads run two stages ahead through
-//    three register banks, so a stage's MFMAs overlap the next two stages'
-//    memory latency.
+//    conflicts), so every operand read is one conflict-free ds_read_b128.
+//    Global loads run kTBanks - 1 stages ahead through kTBanks register
+//    banks, so a stage's MFMAs overlap the following stages' memory latency.
 //  * Work list: slot p owns ceil(T_p / 128) row tiles, the shared expert
 //    ceil(T / 128), in the prefix tile_off; each row tile pairs with every
 //    weight-row tile.  The list is ordered (group, weight tile, row tile) and
@@ -43,6 +43,11 @@ constexpr int kTM = 128;     // token rows per tile
 constexpr int kTN = 256;     // weight rows per tile
 constexpr int kTK = 64;      // K per stage
 constexpr int kTThreads = 256;
+// register banks of the global-load pipeline: kTBanks - 1 stages in flight
+// (a stage is 64 MFMAs per wave, about 0.43 us at full rate).  The kernel
+// runs one wave per SIMD at any depth here; four banks measured fastest
+// (five spill into accumulation registers and gain nothing).
+constexpr int kTBanks = 4;
 
 // LDS bytes per stage: the 128 x 64 bf16 activation tile
 constexpr int kXStage = kTM * kTK * 2;   // 16 KiB
@@ -159,45 +164,45 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(TiledArgs ta) {
   const int rows_here = min(kTM, R - m0);
   const int mv = ((rows_here + 31) / 32) * 2;
   auto run = [&](auto mvc) {
-    // Global loads run two stages ahead through three register banks (per
+    // Global loads run kTBanks - 1 stages ahead (per
     // stage: the activation pieces first, then the weights; vector-memory
     // counters drain in order, so staging the activations never waits for the
     // weights issued after them).
     constexpr int MV = decltype(mvc)::value;    // non-empty 16-row tiles (even)
     constexpr int XQ = MV / 2;                   // activation pieces per thread and stage
-    u32x4 xr[3][XQ], wr[3][4][2];
+    u32x4 xr[kTBanks][XQ], wr[kTBanks][4][2];
     auto gload = [&](int bank, int stage) {
       const int k0 = kbeg + stage * kTK;
-  #pragma unroll
+#pragma unroll
       for (int q = 0; q < XQ; ++q) xr[bank][q] = *reinterpret_cast<const u32x4*>(xsrc[q] + (int64_t)k0 * 2);
-  #pragma unroll
+#pragma unroll
       for (int n = 0; n < 4; ++n)
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < 2; ++j)
           wr[bank][n][j] = *reinterpret_cast<const u32x4*>(wsrc[n] + wk(k0 / 32 + j));
     };
     auto lstore = [&](int bank, int buf) {
-  #pragma unroll
+#pragma unroll
       for (int q = 0; q < XQ; ++q) *reinterpret_cast<u32x4*>(xsm + buf * kXStage + xdst[q]) = xr[bank][q];
     };
 
     f32x4 acc[MV][4];
-  #pragma unroll
+#pragma unroll
     for (int m = 0; m < MV; ++m)
-  #pragma unroll
+#pragma unroll
       for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0, 0, 0, 0};
 
     auto compute = [&](int bank, int buf) {
       const char* xb = xsm + buf * kXStage;
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < 2; ++j) {
         bf16x8 xf[MV];
-  #pragma unroll
+#pragma unroll
         for (int m = 0; m < MV; ++m)
           xf[m] = *reinterpret_cast<const bf16x8*>(xb + ((m * 2 + j) * 64 + swz(lane, j)) * 16);
-  #pragma unroll
+#pragma unroll
         for (int m = 0; m < MV; ++m)
-  #pragma unroll
+#pragma unroll
           for (int n = 0; n < 4; ++n)
             acc[m][n] = mfma16x16x32(__builtin_bit_cast(bf16x8, wr[bank][n][j]), xf[m], acc[m][n]);
       }
@@ -206,18 +211,18 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(TiledArgs ta) {
     // Stages past the end re-load the last stage (clamped) instead of branching
     // around loads; the extra LDS copy goes to the buffer not being read.
     const int slast = nstages - 1;
-    gload(0, 0);
-    gload(1, min(1, slast));
+#pragma unroll
+    for (int p = 0; p < kTBanks - 1; ++p) gload(p, min(p, slast));
     lstore(0, 0);
     __syncthreads();
-    for (int s0 = 0; s0 < nstages; s0 += 3) {
-  #pragma unroll
-      for (int u = 0; u < 3; ++u) {
+    for (int s0 = 0; s0 < nstages; s0 += kTBanks) {
+#pragma unroll
+      for (int u = 0; u < kTBanks; ++u) {
         const int st = s0 + u;
         if (st < nstages) {
-          gload((u + 2) % 3, min(st + 2, slast));
+          gload((u + kTBanks - 1) % kTBanks, min(st + kTBanks - 1, slast));
           compute(u, st & 1);
-          lstore((u + 1) % 3, (st + 1) & 1);   // that buffer was last read before the previous barrier
+          lstore((u + 1) % kTBanks, (st + 1) & 1);   // that buffer was last read before the previous barrier
           __syncthreads();
         }
       }
@@ -225,13 +230,13 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(TiledArgs ta) {
 
     // ---- epilogue: acc[m][n] holds D[w-row 4*(lane/16)+j of tile n][token lane%16 of tile m]
     const int lr = lane & 15, lg = lane >> 4;
-  #pragma unroll
+#pragma unroll
     for (int m = 0; m < MV; ++m) {
       const int gr = m0 + m * 16 + lr;                    // row within the group
       if (gr >= R) continue;
       const int64_t row = gr < c0 ? s0 + gr : s1 + (gr - c0);
       if (MODE == MODE_GATEUP) {
-  #pragma unroll
+#pragma unroll
         for (int n = 0; n < 2; ++n) {
           const f32x4 gt = acc[m][n], up = acc[m][n + 2];
           const int ncol = n0 + 32 * wave + 16 * n + 4 * lg;
@@ -240,7 +245,7 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(TiledArgs ta) {
           *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
         }
       } else {
-  #pragma unroll
+#pragma unroll
         for (int n = 0; n < 4; ++n) {
           const int ncol = n0 + 64 * wave + 16 * n + 4 * lg;
           if (a.out_f32) {

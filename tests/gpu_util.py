@@ -83,7 +83,20 @@ def route_np(rt: B.RouteTables, T: int, K: int) -> dict:
                 src_of=g(rt.src_of, T * K), counts=rt.counts.cpu().numpy(),
                 offsets=rt.offsets.cpu().numpy(), masked_m=rt.masked_m.cpu().numpy(),
                 spill_off=rt.spill_off.cpu().numpy(), pad_off=rt.pad_off.cpu().numpy(),
-                status=int(rt.status.cpu().numpy()[0]))
+                tile_off=rt.tile_off.cpu().numpy(), status=int(rt.status.cpu().numpy()[0]))
+
+
+TILE_ROWS = 128   # token rows per tile of the tiled expert kernel (moe_route_t.tile_off)
+
+
+def tile_off_expected(counts, T: int, n_shared: int):
+    """tile_off as moe.h defines it: exclusive prefix sum of ceil(count/128)
+    over the slots, the total, then the total plus the shared expert's
+    ceil(T/128) tiles."""
+    t = -(-np.asarray(counts, dtype=np.int64) // TILE_ROWS)
+    pre = np.concatenate([[0], np.cumsum(t)])
+    shared = -(-T // TILE_ROWS) if n_shared else 0
+    return np.concatenate([pre, [pre[-1] + shared]]).astype(np.int32)
 
 
 def weight_tol(K: int) -> float:

@@ -15,7 +15,7 @@ import torch
 from oracle import moe_oracle as O
 from routing_grouped_expert_router_amd import binding as B
 from workloads import configs, generate
-from gpu_util import Built, TOL, rel_err, out_np, route_np, say, weight_tol, DEV
+from gpu_util import Built, TOL, rel_err, out_np, route_np, say, tile_off_expected, weight_tol, DEV
 
 pytestmark = pytest.mark.gpu
 
@@ -45,8 +45,8 @@ def small_configs():
                    act_dtype="bf16", layout="contig", BM=128, bias="normal0.5"),
         base.with_(name="replica_small", T=70, H=256, I=128, E=32, E_phys=40, K=4,
                    act_dtype="bf16", layout="contig", BM=16, bias="zipf1.1"),
-        # groups of ~150 rows: two 128-row tiles each in the tiled kernel, with
-        # the masked/spill boundary falling inside a tile
+        # groups of ~150 rows (masked: the masked/spill boundary falls inside
+        # a tile of the tiled kernel)
         base.with_(name="tiled_masked_spill", T=300, H=256, I=256, E=4, E_phys=4, K=2,
                    act_dtype="bf16", M_max=100),
         base.with_(name="tiled_contig_shared", T=300, H=512, I=384, E=4, E_phys=4, K=2, n_shared=1,
@@ -76,6 +76,7 @@ def check_route(b: Built, res: dict):
         assert np.array_equal(g["spill_off"], res["spill_off"])
     else:
         assert np.array_equal(g["pad_off"], res["pad_off"])
+    assert np.array_equal(g["tile_off"], tile_off_expected(np.asarray(res["counts"]), T, b.cfg.n_shared))
     assert np.abs(g["w"] - res["w"]).max() <= weight_tol(K)
     assert g["status"] == res["status"], (g["status"], res["status"])
     return g
