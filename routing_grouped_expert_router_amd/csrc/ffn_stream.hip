@@ -35,6 +35,8 @@
 //  * MODE_GATEUP: W1 (gate) and W3 (up); epilogue h = SiLU(g) * u in bf16.
 //    MODE_DOWN: W2; bf16 output, or fp32 partial planes when K is split over
 //    grid.z (summed in split order by the combine).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -44,6 +46,7 @@ constexpr int kThreads = 256;        // 4 waves
 constexpr int kBN = 64;              // weight rows per workgroup
 constexpr int kKS = 128;             // K per pipeline step
 constexpr int kLdsStride = kKS + 8;  // bf16 elements per LDS row (pad vs bank conflicts)
+constexpr int kXlSteps = 16;         // K steps of LDS-resident activations (16 x 4 KiB)
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
@@ -129,14 +132,24 @@ template <bool FP8, int MODE>
 constexpr int banks_b() { return (FP8 || MODE == MODE_DOWN) ? 2 : 3; }
 template <bool FP8>
 constexpr int tiles_b() { return FP8 ? 2 : 4; }
+// LDS-resident activations (fp8 down projection, one row tile, K range of at
+// most kXlSteps steps = 64 KiB): with no activation registers the weight
+// stream keeps NB - 1 = 11 steps (2 KiB a step and wave) in flight
+template <bool FP8>
+constexpr int banks_xl() { return FP8 ? 12 : 6; }
 
 // The rows of group g if its row count is in (lo, hi] (hi = 0: no limit):
 // row-tile passes mc, mc + mch, ... of it, K split ks.
-template <bool FP8, int MODE, int MT, bool PACKED, int NB, bool NT>
+// XL (single-tile passes only): the tile's activations for the split's whole
+// K range (at most kXlSteps steps) are staged once into LDS, in MFMA fragment
+// order, before the weight stream starts; the stream then carries weights
+// only and never synchronises.
+template <bool FP8, int MODE, int MT, bool PACKED, int NB, bool NT, bool XL = false>
 __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks, int mc, int mch, int lo,
                                              int hi, uint16_t* __restrict__ xs_raw) {
   constexpr bool TWO = MODE == MODE_GATEUP;
   constexpr bool XDIRECT = MT == 1;
+  static_assert(!XL || MT == 1, "LDS-resident activations hold one row tile");
   // ---- the group's row segments
   int64_t s0 = 0, s1 = 0;
   int c0 = 0, c1 = 0;
@@ -218,10 +231,13 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
     // K offset of MFMA operand q inside a 128-wide step for this lane:
     // bf16 operand q covers 32q + 8*lg .. +8; an fp8 step's 16-byte weight
     // piece i expands to operands 2i, 2i+1 covering 64i + 16*lg + 8*(q%2).
-    auto xoff = [&](int q) { return FP8 ? 64 * (q >> 1) + 16 * lg + 8 * (q & 1) : 32 * q + 8 * lg; };
-    constexpr int XV = XDIRECT ? 4 : MT;     // 16-byte activation loads per thread and step
+    auto xoff_g = [&](int q, int grp) { return FP8 ? 64 * (q >> 1) + 16 * grp + 8 * (q & 1) : 32 * q + 8 * grp; };
+    auto xoff = [&](int q) { return xoff_g(q, lg); };
+    constexpr int XV = XL ? 1 : (XDIRECT ? 4 : MT);   // 16-byte activation loads per thread and step
     auto load_x = [&](int kstep, u32x4* xr) {
-      if constexpr (XDIRECT) {
+      if constexpr (XL) {
+        (void)kstep; (void)xr;
+      } else if constexpr (XDIRECT) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           xr[q] = *reinterpret_cast<const u32x4*>(xsrc[0] + (int64_t)kstep * kKS + xoff(q));
@@ -236,9 +252,12 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
       for (int m = 0; m < MT; ++m)
         *reinterpret_cast<u32x4*>(&xs[buf][m * 16 + sr][8 * sc]) = xr[m];
     };
-    // B operand q of tile m at K step buffer buf (MT > 1) or bank xr (MT == 1)
-    auto bop = [&](const u32x4* xr, int buf, int m, int q) -> bf16x8 {
-      if constexpr (XDIRECT) return __builtin_bit_cast(bf16x8, xr[q]);
+    // B operand q of tile m at K step kstep: LDS-resident piece (XL), bank xr
+    // (MT == 1) or LDS buffer buf (MT > 1)
+    const u32x4* xl = reinterpret_cast<const u32x4*>(xs_raw);
+    auto bop = [&](const u32x4* xr, int buf, int m, int q, int kstep) -> bf16x8 {
+      if constexpr (XL) return __builtin_bit_cast(bf16x8, xl[((kstep - kstep0) * 4 + q) * 64 + lane]);
+      else if constexpr (XDIRECT) return __builtin_bit_cast(bf16x8, xr[q]);
       else return *reinterpret_cast<const bf16x8*>(&xs[buf][m * 16 + lr][xoff(q)]);
     };
 
@@ -263,7 +282,7 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
             f32x4 p1 = {0, 0, 0, 0}, p3 = {0, 0, 0, 0};
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const bf16x8 b = bop(xr, buf, m, q);
+              const bf16x8 b = bop(xr, buf, m, q, kstep);
               p1 = mfma16x16x32(a1[q], b, p1);
               if (TWO) p3 = mfma16x16x32(a3[q], b, p3);
             }
@@ -277,7 +296,7 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
           if (m < ps.n) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const bf16x8 b = bop(xr, buf, m, q);
+              const bf16x8 b = bop(xr, buf, m, q, kstep);
               acc[m] = mfma16x16x32(__builtin_bit_cast(bf16x8, wa.v[q]), b, acc[m]);
               if (TWO) acc3[m] = mfma16x16x32(__builtin_bit_cast(bf16x8, wb.v[q]), b, acc3[m]);
             }
@@ -339,8 +358,30 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
         if (TWO) load_w<FP8, NT>(w3b[bank], w3s, j, k);
         if (++lk == steps) { lk = 0; ++lj; }
       };
+      // XL: piece p = (s*4 + q)*64 + l of the LDS tile is operand q of K
+      // step s for lane l (row l%16, K group l/16); thread t moves pieces
+      // t + 256i.  The activation loads are issued before the weights so the
+      // wait for them leaves the weight loads in flight.
+      u32x4 xst[XL ? kXlSteps : 1];
+      if constexpr (XL) {
+        const int vrow = ps.valid[0] - 1;
+#pragma unroll
+        for (int i = 0; i < kXlSteps; ++i) {
+          const int pc = tid + 256 * i, l = pc & 63, q = (pc >> 6) & 3, st = pc >> 8;
+          const int64_t row = ps.start[0] + min(l & 15, vrow);
+          const int k = kstep0 + (st < steps ? st : 0);
+          xst[i] = *reinterpret_cast<const u32x4*>(a.X + row * a.ldx + (int64_t)k * kKS + xoff_g(q, l >> 4));
+        }
+      }
 #pragma unroll
       for (int p = 0; p < NB - 1; ++p) issue(p);
+      if constexpr (XL) {
+        u32x4* xw = reinterpret_cast<u32x4*>(xs_raw);
+#pragma unroll
+        for (int i = 0; i < kXlSteps; ++i)
+          if (((tid + 256 * i) >> 8) < steps) xw[tid + 256 * i] = xst[i];
+        __syncthreads();
+      }
       if constexpr (!XDIRECT) {
         store_x(0, xb[0]);
         __syncthreads();
@@ -368,7 +409,7 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
       if constexpr (!FLAT) epilogue(jb);
     }
 
-    if constexpr (!XDIRECT) __syncthreads();   // LDS buffer reuse by the next pass
+    if constexpr (!XDIRECT || XL) __syncthreads();   // LDS buffer reuse by the next pass
   }
 }
 
@@ -379,12 +420,16 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
 template <bool FP8, int MTA>
 constexpr int min_waves() { return (FP8 && MTA == 1) ? 3 : 1; }
 
-template <bool FP8, int MODE, int MTA, bool PACKED>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves<FP8, MTA>())))
+// XLK: region A keeps its activations in LDS (dynamic shared memory sized by
+// the launch to cover both the K range and region B's tiles).
+template <bool FP8, int MODE, int MTA, bool PACKED, bool XLK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves<FP8, MTA>() * !XLK + XLK)))
 void ffn_stream_kernel(StreamArgs a) {
   constexpr int TB = tiles_b<FP8>();
-  constexpr int LDS = lds_elems<(MTA < 4 && MTA < TB) ? TB : MTA>();
-  __shared__ __attribute__((aligned(16))) uint16_t xs_raw[LDS];
+  constexpr int LDS = XLK ? 1 : lds_elems<(MTA < 4 && MTA < TB) ? TB : MTA>();
+  __shared__ __attribute__((aligned(16))) uint16_t xs_static[LDS];
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs_dynamic[];
+  uint16_t* xs_raw = XLK ? xs_dynamic : xs_static;
   const int ks = blockIdx.z;
   int y = blockIdx.y;
   if constexpr (MTA < 4) {
@@ -398,15 +443,29 @@ void ffn_stream_kernel(StreamArgs a) {
     }
     y -= a.b_rows;
   }
-  stream_group<FP8, MODE, MTA, PACKED, banks_a<FP8, MODE>(), true>(a, y, ks, 0, 1, 0, a.max_rows, xs_raw);
+  if constexpr (XLK)
+    stream_group<FP8, MODE, 1, PACKED, banks_xl<FP8>(), true, true>(a, y, ks, 0, 1, 0, a.max_rows, xs_raw);
+  else
+    stream_group<FP8, MODE, MTA, PACKED, banks_a<FP8, MODE>(), true>(a, y, ks, 0, 1, 0, a.max_rows, xs_raw);
 }
 
 template <bool FP8, int MODE, bool PACKED>
 static hipError_t launch_mt(const StreamArgs& a, int mt, dim3 grid, hipStream_t s) {
+  if constexpr (MODE == MODE_DOWN && FP8) {
+    // measured: pays for fp8 down projections (K = 2048), costs time for bf16
+    const int steps = a.Kdim / kKS / a.ksplit;
+    if (mt == 1 && steps <= kXlSteps) {
+      // bytes: the K range's activation pieces, and region B's LDS tiles
+      constexpr int TB = tiles_b<FP8>();
+      const size_t lds = std::max<size_t>((size_t)steps * 256 * 16, sizeof(uint16_t) * lds_elems<TB>());
+      hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 1, PACKED, true>), grid, dim3(kThreads), lds, s, a);
+      return hipGetLastError();
+    }
+  }
   switch (mt) {
-    case 1: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 1, PACKED>), grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 2, PACKED>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 4, PACKED>), grid, dim3(kThreads), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 1, PACKED, false>), grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 2, PACKED, false>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((ffn_stream_kernel<FP8, MODE, 4, PACKED, false>), grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -7,7 +7,8 @@
 //    up to 64 experts; thread i takes 8 consecutive h per 2048-wide stride and
 //    keeps one partial sum per expert, then a wave butterfly and a fixed-order
 //    sum over the four waves.  W_r rows are read from L2 by every workgroup.
-//  * router_mfma (E > 64, bf16 x): a workgroup owns 16 experts x 64 tokens;
+//  * router_mfma (E > 64, bf16 x): a workgroup owns 16 experts x 16*MR tokens
+//    (MR = 1, 2 or 4 picked so the grid has at least 256 workgroups);
 //    its 16 waves split H, each runs v_mfma_f32_16x16x32_bf16 over its slice
 //    with operands loaded straight to registers (next slice in flight), and
 //    the 16 partial tiles are summed in wave order through LDS.
@@ -70,18 +71,19 @@ __global__ __launch_bounds__(256) void router_small_kernel(RouterArgs a) {
 
 constexpr int kRouterWaves = 16;
 
+template <int MR>
 __global__ __launch_bounds__(kRouterWaves * 64) void router_mfma_kernel(RouterArgs a) {
-  __shared__ f32x4 red[kRouterWaves][4][64];
+  __shared__ f32x4 red[kRouterWaves][MR][64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 64;
+  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16 * MR;
   const int erow = e0 + lr;
   const bool eok = erow < a.E;
   const uint16_t* wrow = a.w + (int64_t)(eok ? erow : 0) * a.H;
-  const uint16_t* xrow[4];
-  bool xok[4];
+  const uint16_t* xrow[MR];
+  bool xok[MR];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < MR; ++m) {
     const int t = t0 + 16 * m + lr;
     xok[m] = t < a.T;
     xrow[m] = static_cast<const uint16_t*>(a.x) + (int64_t)(xok[m] ? t : 0) * a.H;
@@ -89,10 +91,10 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_mfma_kernel(RouterAr
   // this wave's slice of H, in 64-wide chunks (two MFMA K steps)
   const int kw = a.H / kRouterWaves;          // multiple of 64 (H % 1024 == 0)
   const int kbeg = wave * kw;
-  f32x4 acc[4];
+  f32x4 acc[MR];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) acc[m] = f32x4{0, 0, 0, 0};
-  u32x4 wc[2], xc[4][2];
+  for (int m = 0; m < MR; ++m) acc[m] = f32x4{0, 0, 0, 0};
+  u32x4 wc[2], xc[MR][2];
   auto load = [&](int k0, u32x4* wv, u32x4 (*xv)[2]) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -100,32 +102,32 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_mfma_kernel(RouterAr
       // rows past E or T read row 0; their results are never written
       wv[j] = *reinterpret_cast<const u32x4*>(wrow + k);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) xv[m][j] = *reinterpret_cast<const u32x4*>(xrow[m] + k);
+      for (int m = 0; m < MR; ++m) xv[m][j] = *reinterpret_cast<const u32x4*>(xrow[m] + k);
     }
   };
   load(kbeg, wc, xc);
   for (int k0 = kbeg; k0 < kbeg + kw; k0 += 64) {
-    u32x4 wn[2], xn[4][2];
+    u32x4 wn[2], xn[MR][2];
     const bool more = k0 + 64 < kbeg + kw;
     if (more) load(k0 + 64, wn, xn);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < MR; ++m)
         acc[m] = mfma16x16x32(__builtin_bit_cast(bf16x8, wc[j]), __builtin_bit_cast(bf16x8, xc[m][j]), acc[m]);
     if (more) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         wc[j] = wn[j];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) xc[m][j] = xn[m][j];
+        for (int m = 0; m < MR; ++m) xc[m][j] = xn[m][j];
       }
     }
   }
 #pragma unroll
-  for (int m = 0; m < 4; ++m) red[wave][m][lane] = acc[m];
+  for (int m = 0; m < MR; ++m) red[wave][m][lane] = acc[m];
   __syncthreads();
-  if (tid < 256) {
+  if (tid < 64 * MR) {
     const int m = tid >> 6, l = tid & 63;
     f32x4 s = red[0][m][l];
     for (int w = 1; w < kRouterWaves; ++w) s += red[w][m][l];
@@ -147,7 +149,16 @@ bool router_uses_mfma(int E, int H, int x_f32) { return E > 64 && !x_f32 && H % 
 hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (router_uses_mfma(a.E, a.H, a.x_f32)) {
-    hipLaunchKernelGGL(router_mfma_kernel, dim3((a.E + 15) / 16, (a.T + 63) / 64), dim3(kRouterWaves * 64), 0, s, a);
+    // 16*MR tokens per workgroup: the largest MR that still gives >= 256
+    // workgroups (weights are re-read once per token block, activations once
+    // per 16-expert block either way)
+    const int eb = (a.E + 15) / 16;
+    if ((int64_t)eb * ((a.T + 63) / 64) >= 256)
+      hipLaunchKernelGGL(router_mfma_kernel<4>, dim3(eb, (a.T + 63) / 64), dim3(kRouterWaves * 64), 0, s, a);
+    else if ((int64_t)eb * ((a.T + 31) / 32) >= 256)
+      hipLaunchKernelGGL(router_mfma_kernel<2>, dim3(eb, (a.T + 31) / 32), dim3(kRouterWaves * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL(router_mfma_kernel<1>, dim3(eb, (a.T + 15) / 16), dim3(kRouterWaves * 64), 0, s, a);
   } else {
     const dim3 g(a.T, a.E > 32 ? (a.E + 63) / 64 : 1), b(256);
     if (a.x_f32) {
