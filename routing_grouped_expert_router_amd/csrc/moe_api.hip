@@ -238,7 +238,11 @@ moe_status_t launch_expert_gemm(const moe_desc_t* d, const moe_route_t* r, int32
   const bool tiled = tiled_supported(mode, fp8, a.N, a.Kdim, a.ksplit);
   const int a_max = 16 * mt;
   const bool need_b = mt < 4 && T > a_max;   // a group may outgrow region A
-  const bool need_c = tiled && T > 64;       // a group may outgrow the streaming kernel
+  // The tiled kernel pays only when groups are large on average (T*K/E_phys
+  // >= 64 rows, prefill); at decode sizes a few hot groups above 64 rows
+  // occupy too few workgroups in a launch of their own (measured on the
+  // replica workload: 1036 -> 970 us), so region B streams them, in passes.
+  const bool need_c = tiled && T > 64 && (int64_t)T * d->K >= (int64_t)64 * d->E_phys;
   a.max_rows = (need_b || need_c) ? a_max : 0;
   a.b_rows = 0;
   a.shared_chunks = 1;
