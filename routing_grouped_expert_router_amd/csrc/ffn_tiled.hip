@@ -45,9 +45,9 @@ constexpr int kTK = 64;      // K per stage
 constexpr int kTThreads = 256;
 // register banks of the global-load pipeline: kTBanks - 1 stages in flight
 // (a stage is 64 MFMAs per wave, about 0.43 us at full rate).  The kernel
-// runs one wave per SIMD at any depth here; four banks measured fastest
-// (five spill into accumulation registers and gain nothing).
-constexpr int kTBanks = 4;
+// runs one wave per SIMD; three banks leave the registers for two sets of
+// operand fragments (the LDS reads run one K step ahead of the MFMAs).
+constexpr int kTBanks = 3;
 
 // LDS bytes per stage: the 128 x 64 bf16 activation tile
 constexpr int kXStage = kTM * kTK * 2;   // 16 KiB
@@ -192,38 +192,48 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(TiledArgs ta) {
 #pragma unroll
       for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0, 0, 0, 0};
 
-    auto compute = [&](int bank, int buf) {
+    // operand fragments of one 32-wide K step j of LDS buffer buf
+    auto lread = [&](bf16x8* xf, int buf, int j) {
       const char* xb = xsm + buf * kXStage;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        bf16x8 xf[MV];
+      for (int m = 0; m < MV; ++m)
+        xf[m] = *reinterpret_cast<const bf16x8*>(xb + ((m * 2 + j) * 64 + swz(lane, j)) * 16);
+    };
+    auto mma = [&](int bank, const bf16x8* xf, int j) {
 #pragma unroll
-        for (int m = 0; m < MV; ++m)
-          xf[m] = *reinterpret_cast<const bf16x8*>(xb + ((m * 2 + j) * 64 + swz(lane, j)) * 16);
+      for (int m = 0; m < MV; ++m)
 #pragma unroll
-        for (int m = 0; m < MV; ++m)
-#pragma unroll
-          for (int n = 0; n < 4; ++n)
-            acc[m][n] = mfma16x16x32(__builtin_bit_cast(bf16x8, wr[bank][n][j]), xf[m], acc[m][n]);
-      }
+        for (int n = 0; n < 4; ++n)
+          acc[m][n] = mfma16x16x32(__builtin_bit_cast(bf16x8, wr[bank][n][j]), xf[m], acc[m][n]);
     };
 
-    // Stages past the end re-load the last stage (clamped) instead of branching
+    // Operand reads are software-pipelined against the MFMAs: with one wave
+    // per SIMD nothing else hides their latency.  Per stage st: the reads of
+    // K step 1 are issued, then the global loads; K step 0's MFMAs run on
+    // fragments read at the end of the previous stage; the next stage's
+    // activations are stored to the other LDS buffer; K step 1's MFMAs run;
+    // barrier; the next stage's K step 0 reads are issued at once.  Stages
+    // past the end re-load the last stage (clamped) instead of branching
     // around loads; the extra LDS copy goes to the buffer not being read.
+    bf16x8 xa[MV], xbv[MV];
     const int slast = nstages - 1;
 #pragma unroll
     for (int p = 0; p < kTBanks - 1; ++p) gload(p, min(p, slast));
     lstore(0, 0);
     __syncthreads();
+    lread(xa, 0, 0);
     for (int s0 = 0; s0 < nstages; s0 += kTBanks) {
 #pragma unroll
       for (int u = 0; u < kTBanks; ++u) {
         const int st = s0 + u;
         if (st < nstages) {
+          lread(xbv, st & 1, 1);
           gload((u + kTBanks - 1) % kTBanks, min(st + kTBanks - 1, slast));
-          compute(u, st & 1);
+          mma(u, xa, 0);
           lstore((u + 1) % kTBanks, (st + 1) & 1);   // that buffer was last read before the previous barrier
+          mma(u, xbv, 1);
           __syncthreads();
+          lread(xa, (st + 1) & 1, 0);                 // after the last stage: unused reads of written LDS
         }
       }
     }
