@@ -206,6 +206,17 @@ moe_status_t moe_expert_gate_up(const moe_desc_t* d, const moe_weights_t* w,
                                 const moe_route_t* r, int32_t T, const void* xg,
                                 void* h, hipStream_t stream);
 
+/* a5 + a6 (+a8) in one call, for bf16 activations: as moe_expert_gate_up,
+ * but each group's rows are read straight from the layer input instead of a
+ * grouped buffer -- rank r of slot p is token src_of[offsets[p] + r], rank
+ * r of the shared expert token r -- so moe_permute and its buffer are not
+ * needed (the gather of vllbc blog's forward path, fused into the expert
+ * kernel).  x: device [T, H] bf16.  h as for moe_expert_gate_up (same
+ * values).  MOE_ERR_UNSUPPORTED unless act_dtype is MOE_BF16. */
+moe_status_t moe_expert_gate_up_x(const moe_desc_t* d, const moe_weights_t* w,
+                                  const moe_route_t* r, int32_t T, const void* x,
+                                  void* h, hipStream_t stream);
+
 /* a7 (+a8). Down projection y[row] = h[row] W2^T for the same rows.
  * y: device, moe_y_bytes(d, T) bytes: bf16 [moe_buffer_rows, H] when
  * moe_down_splits(d, T) == 1, else that many fp32 partial planes. */
@@ -218,6 +229,11 @@ moe_status_t moe_grouped_ffn(const moe_desc_t* d, const moe_weights_t* w,
                              const moe_route_t* r, int32_t T, const void* xg,
                              void* h, void* y, hipStream_t stream);
 
+/* a5-a8 in one call: moe_expert_gate_up_x then moe_expert_down. */
+moe_status_t moe_grouped_ffn_x(const moe_desc_t* d, const moe_weights_t* w,
+                               const moe_route_t* r, int32_t T, const void* x,
+                               void* h, void* y, hipStream_t stream);
+
 /* a9. out[t] = sum_k topk_w[t,k] * y[slot_of[t*K+k]] (+ y[shared_base + t]),
  * in fp32 with k ascending, then rounded to act_dtype (RNE).
  * (vllbc blog, combine: weight by g_i, then sum the K results.)
@@ -225,7 +241,9 @@ moe_status_t moe_grouped_ffn(const moe_desc_t* d, const moe_weights_t* w,
 moe_status_t moe_combine(const moe_desc_t* d, const moe_route_t* r, int32_t T,
                          const void* y, void* out, hipStream_t stream);
 
-/* All five steps in order on one stream (same arguments as above). */
+/* All five steps in order on one stream (same arguments as above).  With
+ * bf16 activations the permute is fused into the expert kernel
+ * (moe_grouped_ffn_x) and xg is not used (may be NULL). */
 moe_status_t moe_forward(const moe_desc_t* d, const void* x, const void* w_router,
                          const float* bias, const int32_t* l2p, const int32_t* replica_count,
                          const moe_weights_t* w, int32_t T, float* logits,

@@ -24,8 +24,9 @@ MOE_STATUS_SPILL, MOE_STATUS_BAD_REPLICA, MOE_STATUS_NONFINITE, MOE_STATUS_INTER
 EXPORTED = [
     "moe_status_string", "moe_check_desc", "moe_route_workspace_bytes", "moe_buffer_rows",
     "moe_shared_base", "moe_down_splits", "moe_y_bytes", "moe_router_logits", "moe_route",
-    "moe_permute", "moe_expert_gate_up", "moe_expert_down", "moe_grouped_ffn", "moe_combine",
-    "moe_forward", "moe_pack_weights", "moe_replica_map_from_p2l",
+    "moe_permute", "moe_expert_gate_up", "moe_expert_gate_up_x", "moe_expert_down",
+    "moe_grouped_ffn", "moe_grouped_ffn_x", "moe_combine", "moe_forward", "moe_pack_weights",
+    "moe_replica_map_from_p2l",
 ]
 
 
@@ -76,8 +77,10 @@ def lib() -> ctypes.CDLL:
             "moe_route": (ctypes.c_int, [D, _P, i32, _P, _P, R, _P, sz, _P]),
             "moe_permute": (ctypes.c_int, [D, _P, i32, R, _P, _P]),
             "moe_expert_gate_up": (ctypes.c_int, [D, W, R, i32, _P, _P, _P]),
+            "moe_expert_gate_up_x": (ctypes.c_int, [D, W, R, i32, _P, _P, _P]),
             "moe_expert_down": (ctypes.c_int, [D, W, R, i32, _P, _P, _P]),
             "moe_grouped_ffn": (ctypes.c_int, [D, W, R, i32, _P, _P, _P, _P]),
+            "moe_grouped_ffn_x": (ctypes.c_int, [D, W, R, i32, _P, _P, _P, _P]),
             "moe_combine": (ctypes.c_int, [D, R, i32, _P, _P, _P]),
             "moe_forward": (ctypes.c_int, [D, _P, _P, _P, _P, _P, W, i32, _P, R, _P, sz,
                                            _P, _P, _P, _P, _P]),
@@ -228,6 +231,16 @@ def moe_grouped_ffn(d: Desc, w: Weights, rt: RouteTables, T, xg, h, y, stream=No
                                  _ptr(xg), _ptr(h), _ptr(y), _stream(stream)), "moe_grouped_ffn")
 
 
+def moe_grouped_ffn_x(d: Desc, w: Weights, rt: RouteTables, T, x, h, y, stream=None):
+    _check(lib().moe_grouped_ffn_x(ctypes.byref(d.c()), ctypes.byref(w.c), ctypes.byref(rt.c), T,
+                                   _ptr(x), _ptr(h), _ptr(y), _stream(stream)), "moe_grouped_ffn_x")
+
+
+def moe_expert_gate_up_x(d: Desc, w: Weights, rt: RouteTables, T, x, h, stream=None):
+    _check(lib().moe_expert_gate_up_x(ctypes.byref(d.c()), ctypes.byref(w.c), ctypes.byref(rt.c), T,
+                                      _ptr(x), _ptr(h), _stream(stream)), "moe_expert_gate_up_x")
+
+
 def moe_expert_gate_up(d: Desc, w: Weights, rt: RouteTables, T, xg, h, stream=None):
     _check(lib().moe_expert_gate_up(ctypes.byref(d.c()), ctypes.byref(w.c), ctypes.byref(rt.c), T,
                                     _ptr(xg), _ptr(h), _stream(stream)), "moe_expert_gate_up")
@@ -309,16 +322,21 @@ class MoELayer:
     def y_for(self, T: int) -> torch.Tensor:
         return self.y[: y_bytes(self.d, T)]
 
-    def forward(self, x, T=None, logits=None, stream=None):
+    def forward(self, x, T=None, logits=None, stream=None, fused_gather=True):
         """Runs the five steps; ``logits`` (fp32 [T, E]) replaces the router
-        step when given.  Returns the output view [T, H]."""
+        step when given.  With bf16 activations the permute is fused into the
+        expert kernel (moe_grouped_ffn_x) unless ``fused_gather`` is False.
+        Returns the output view [T, H]."""
         d = self.d
         T = x.shape[0] if T is None else T
         if logits is None:
             moe_router_logits(d, x, self.w_router, self.bias, T, self.logits, stream)
             logits = self.logits
         moe_route(d, logits, T, self.rt, self.ws, self.l2p, self.rcount, stream)
-        moe_permute(d, x, T, self.rt, self.xg, stream)
-        moe_grouped_ffn(d, self.weights, self.rt, T, self.xg, self.h, self.y, stream)
+        if fused_gather and d.act_dtype == MOE_BF16:
+            moe_grouped_ffn_x(d, self.weights, self.rt, T, x, self.h, self.y, stream)
+        else:
+            moe_permute(d, x, T, self.rt, self.xg, stream)
+            moe_grouped_ffn(d, self.weights, self.rt, T, self.xg, self.h, self.y, stream)
         moe_combine(d, self.rt, T, self.y, self.out, stream)
         return self.out[:T]

@@ -221,11 +221,19 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
     // MT == 1: each lane streams its own row's MFMA fragments straight into
     // registers and the waves never synchronise.  MT > 1: the workgroup
     // stages the tiles into LDS, one 16-byte chunk per thread and tile.
+    // With a gather the source row is the token of the row's rank in the
+    // group: ranks of segment 0 are 0 .. c0-1, of segment 1 c0 .. c0+c1-1.
     const uint16_t* xsrc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       const int r = XDIRECT ? lr : sr;
-      const int64_t row = (m < ps.n && ps.valid[m] > 0) ? ps.start[m] + min(r, ps.valid[m] - 1) : s0;
+      const bool live = m < ps.n && ps.valid[m] > 0;
+      int64_t row = live ? ps.start[m] + min(r, ps.valid[m] - 1) : s0;
+      if (a.gather_src) {
+        const int tile = tile0 + (live ? m : 0);
+        const int rank = (tile < nt0 ? 16 * tile : c0 + 16 * (tile - nt0)) + (live ? min(r, ps.valid[m] - 1) : 0);
+        row = shared ? rank : a.gather_src[a.gather_off[g] + rank];
+      }
       xsrc[m] = a.X + row * a.ldx + (XDIRECT ? 0 : 8 * sc);
     }
     // K offset of MFMA operand q inside a 128-wide step for this lane:

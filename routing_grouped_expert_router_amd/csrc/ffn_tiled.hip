@@ -156,6 +156,10 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(TiledArgs ta) {
     const int r = (tid >> 3) + 32 * q;
     const int gr = m0 + r;                               // row within the group
     int64_t row = gr < c0 ? s0 + gr : (gr < R ? s1 + (gr - c0) : s0);   // pad rows read a valid row
+    if (a.gather_src) {                                  // the token of rank gr (pad rows: rank 0)
+      const int rank = gr < R ? gr : 0;
+      row = shared ? rank : a.gather_src[a.gather_off[g] + rank];
+    }
     xsrc[q] = reinterpret_cast<const char*>(a.X + row * a.ldx) + 16 * xc;
     xdst[q] = (((r >> 4) * 2 + (xc >> 2)) * 64 + swz(16 * (xc & 3) + (r & 15), xc >> 2)) * 16;
   }

@@ -57,6 +57,11 @@ enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
 
 struct StreamArgs {
   const uint16_t* X; int64_t ldx;   // bf16 rows
+  // Gather (gate/up only): when gather_src is set, X is the layer input
+  // [T, H] and rank r of routed group g reads row gather_src[gather_off[g] + r]
+  // (the route tables' src_of and offsets); rank r of the shared expert
+  // reads row r.  Otherwise X is the grouped buffer, indexed by slot.
+  const int32_t* gather_src; const int32_t* gather_off;
   int Kdim, N;                       // reduction length, output features
   int E_phys, T, layout, M_max; int64_t shared_base;
   const int32_t* counts; const int32_t* masked_m; const int32_t* spill_off;

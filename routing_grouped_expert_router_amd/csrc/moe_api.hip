@@ -281,26 +281,40 @@ StreamArgs ffn_base_args(const moe_desc_t* d, const moe_route_t* r, int32_t T) {
   return a;
 }
 
+// gate/up from the grouped buffer (gather = false: X = xg, by slot) or
+// straight from the layer input (gather = true: X = x, by token)
+moe_status_t gate_up_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
+                          int32_t T, const void* X, bool gather, void* h, hipStream_t stream) {
+  moe_status_t st = ffn_common_checks(d, w, r, T);
+  if (st != MOE_OK) return st;
+  if (gather && d->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  const bool fp8 = d->w_dtype == MOE_FP8E4M3_B128;
+  if (!X || !h || !w->w1 || !w->w3) return MOE_ERR_ARG;
+  if (fp8 && (!w->s1 || !w->s3)) return MOE_ERR_ARG;
+  if (d->n_shared && (!w->sw1 || !w->sw3)) return MOE_ERR_ARG;
+  StreamArgs g1 = ffn_base_args(d, r, T);
+  g1.X = static_cast<const uint16_t*>(X); g1.ldx = d->H; g1.Kdim = d->H; g1.N = d->I;
+  if (gather) { g1.gather_src = r->src_of; g1.gather_off = r->offsets; }
+  g1.W = w->w1; g1.W3 = w->w3; g1.S = w->s1; g1.S3 = w->s3;
+  g1.SW = w->sw1; g1.SW3 = w->sw3; g1.SS = w->ss1; g1.SS3 = w->ss3;
+  g1.out = h; g1.ldo = d->I;
+  return launch_expert_gemm(d, r, T, g1, fp8, MODE_GATEUP, dim3(d->I / 64, d->E_phys + d->n_shared, 1),
+                            stream);
+}
+
 }  // namespace
 
 extern "C" {
 
 moe_status_t moe_expert_gate_up(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
                                 int32_t T, const void* xg, void* h, hipStream_t stream) {
-  moe_status_t st = ffn_common_checks(d, w, r, T);
-  if (st != MOE_OK) return st;
-  if (T == 0) return MOE_OK;
-  const bool fp8 = d->w_dtype == MOE_FP8E4M3_B128;
-  if (!xg || !h || !w->w1 || !w->w3) return MOE_ERR_ARG;
-  if (fp8 && (!w->s1 || !w->s3)) return MOE_ERR_ARG;
-  if (d->n_shared && (!w->sw1 || !w->sw3)) return MOE_ERR_ARG;
-  StreamArgs g1 = ffn_base_args(d, r, T);
-  g1.X = static_cast<const uint16_t*>(xg); g1.ldx = d->H; g1.Kdim = d->H; g1.N = d->I;
-  g1.W = w->w1; g1.W3 = w->w3; g1.S = w->s1; g1.S3 = w->s3;
-  g1.SW = w->sw1; g1.SW3 = w->sw3; g1.SS = w->ss1; g1.SS3 = w->ss3;
-  g1.out = h; g1.ldo = d->I;
-  return launch_expert_gemm(d, r, T, g1, fp8, MODE_GATEUP, dim3(d->I / 64, d->E_phys + d->n_shared, 1),
-                            stream);
+  return gate_up_impl(d, w, r, T, xg, false, h, stream);
+}
+
+moe_status_t moe_expert_gate_up_x(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
+                                  int32_t T, const void* x, void* h, hipStream_t stream) {
+  return gate_up_impl(d, w, r, T, x, true, h, stream);
 }
 
 moe_status_t moe_expert_down(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
@@ -325,6 +339,13 @@ moe_status_t moe_expert_down(const moe_desc_t* d, const moe_weights_t* w, const 
 moe_status_t moe_grouped_ffn(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
                              int32_t T, const void* xg, void* h, void* y, hipStream_t stream) {
   moe_status_t st = moe_expert_gate_up(d, w, r, T, xg, h, stream);
+  if (st != MOE_OK) return st;
+  return moe_expert_down(d, w, r, T, h, y, stream);
+}
+
+moe_status_t moe_grouped_ffn_x(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
+                               int32_t T, const void* x, void* h, void* y, hipStream_t stream) {
+  moe_status_t st = moe_expert_gate_up_x(d, w, r, T, x, h, stream);
   if (st != MOE_OK) return st;
   return moe_expert_down(d, w, r, T, h, y, stream);
 }
@@ -355,9 +376,14 @@ moe_status_t moe_forward(const moe_desc_t* d, const void* x, const void* w_route
   if (st != MOE_OK) return st;
   st = moe_route(d, logits, T, l2p, replica_count, r, ws, ws_bytes, stream);
   if (st != MOE_OK) return st;
-  st = moe_permute(d, x, T, r, xg, stream);
-  if (st != MOE_OK) return st;
-  st = moe_grouped_ffn(d, w, r, T, xg, h, y, stream);
+  if (d->act_dtype == MOE_BF16) {
+    // the expert kernel gathers its rows from x; xg is not used
+    st = moe_grouped_ffn_x(d, w, r, T, x, h, y, stream);
+  } else {
+    st = moe_permute(d, x, T, r, xg, stream);
+    if (st != MOE_OK) return st;
+    st = moe_grouped_ffn(d, w, r, T, xg, h, y, stream);
+  }
   if (st != MOE_OK) return st;
   return moe_combine(d, r, T, y, out, stream);
 }

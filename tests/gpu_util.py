@@ -57,9 +57,9 @@ class Built:
         return O.router_logits(to_f64(self.inp.x), to_f64(self.inp.w_router),
                                None if self.inp.bias is None else self.inp.bias.numpy())
 
-    def run(self, logits_np=None):
+    def run(self, logits_np=None, fused_gather=True):
         lg = None if logits_np is None else torch.from_numpy(np.ascontiguousarray(logits_np)).to(DEV)
-        out = self.layer.forward(self.x[: self.T], self.T, logits=lg)
+        out = self.layer.forward(self.x[: self.T], self.T, logits=lg, fused_gather=fused_gather)
         torch.cuda.synchronize()
         return out
 

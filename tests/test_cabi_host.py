@@ -70,6 +70,10 @@ def test_calls_reject_bad_arguments_before_enqueueing():
     assert L.moe_route(dc, fake, 4, null, null, ctypes.byref(rt2), fake, 1, null) == B.MOE_ERR_WORKSPACE
     # only one of the two replica arrays
     assert L.moe_route(dc, fake, 4, fake, null, ctypes.byref(rt2), fake, 1 << 20, null) == B.MOE_ERR_ARG
+    # the fused gather needs bf16 activations (the tiny descriptor's are fp32)
+    w0 = B.moe_weights_t(fake, fake, fake, None, None, None, None, None, None, None, None, None)
+    assert L.moe_expert_gate_up_x(dc, ctypes.byref(w0), ctypes.byref(rt2), 4, fake, fake,
+                                  null) == B.MOE_ERR_UNSUPPORTED
     # fp8 weights without scales
     d8 = _d(w_dtype=B.MOE_FP8E4M3_B128)
     w = B.moe_weights_t(fake, fake, fake, None, None, None, None, None, None, None, None, None)

@@ -123,7 +123,7 @@ def test_permute_copies_rows_exactly():
     cfg = SMALL[3]   # fp8 + shared + masked
     b = Built(cfg)
     lg = b.oracle_logits()
-    b.run(lg)
+    b.run(lg, fused_gather=False)             # the chain with moe_permute
     g = route_np(b.layer.rt, b.T, cfg.K)
     xg = b.layer.xg.cpu()
     xb = b.inp.x.to(torch.bfloat16)
@@ -275,6 +275,24 @@ def test_packed_weights_give_identical_outputs():
         p = Built(cfg, packed=True)
         lg = a.oracle_logits()
         assert torch.equal(a.run(lg).clone(), p.run(lg).clone()), cfg.name
+
+
+def test_fused_gather_gives_identical_outputs():
+    """moe_grouped_ffn_x reads each group's rows straight from x (token
+    src_of[offsets[p] + rank]) instead of a permuted buffer; the expert
+    arithmetic is unchanged, so outputs match moe_permute + moe_grouped_ffn
+    bit for bit -- masked with spill, contiguous, shared expert, both size
+    classes of the streaming kernel and the tiled kernel."""
+    for cfg in SMALL[1:]:
+        assert cfg.act_dtype == "bf16", cfg.name
+        b = Built(cfg, packed=True)
+        lg = b.oracle_logits()
+        ref = b.run(lg, fused_gather=False).clone()
+        out = b.run(lg).clone()
+        assert torch.equal(ref, out), cfg.name
+    b = Built(SMALL[6])                      # row-major weights, replica map
+    lg = b.oracle_logits()
+    assert torch.equal(b.run(lg, fused_gather=False).clone(), b.run(lg).clone())
 
 
 @pytest.mark.parametrize("nblk", [2, 4])
