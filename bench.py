@@ -3,7 +3,9 @@
 One step = one pass of the whole layer over one batch: router logits ->
 route (top-K, counts, offsets, grouped order) -> permute -> expert gate/up
 (+SwiGLU) -> expert down -> combine, all HIP kernels through the C ABI, on
-one stream, with inputs and weights already resident in HBM.
+one stream, with inputs and weights already resident in HBM.  With bf16
+activations the permute is done by the gate/up kernel itself (it gathers
+each group's rows from x through the route tables).
 
 Default workload: the Mixtral-8x7B-shaped decode layer (E=8, K=2, H=4096,
 I=14336, bf16) at B=64 tokens; the other batch sizes of that workload are
@@ -90,10 +92,15 @@ class Setup:
         B, L, d, T = self.B, self.layer, self.d, self.cfg.T
         B.moe_router_logits(d, self.x, self.wr, self.bias, T, L.logits)
         B.moe_route(d, L.logits, T, L.rt, L.ws, L.l2p, L.rcount)
-        B.moe_permute(d, self.x, T, L.rt, L.xg)
+        gather = d.act_dtype == B.MOE_BF16     # the gate/up kernel gathers rows from x itself
+        if not gather:
+            B.moe_permute(d, self.x, T, L.rt, L.xg)
         if ev is not None:
             ev[0].record()
-        B.moe_expert_gate_up(d, L.weights, L.rt, T, L.xg, L.h)
+        if gather:
+            B.moe_expert_gate_up_x(d, L.weights, L.rt, T, self.x, L.h)
+        else:
+            B.moe_expert_gate_up(d, L.weights, L.rt, T, L.xg, L.h)
         if ev is not None:
             ev[1].record()
         B.moe_expert_down(d, L.weights, L.rt, T, L.h, L.y)
