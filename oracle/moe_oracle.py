@@ -41,6 +41,19 @@ design notes with its reason):
   R8 an invalid replica map (a count outside [1, max_replicas], a slot
      outside [0, E_phys), or one slot listed twice) is ignored as a whole:
      every expert uses slot = its logical id, and status bit 1 is set.
+  R13 grouped sigmoid router ([vllbc] routing section and Table 3-1: sigmoid
+     scores, the correction bias only for choosing experts, weights from the
+     unbiased scores; grouped top-k: first the best groups, then experts
+     inside them): a score is the fp64 sigmoid of the fp32 logit rounded to
+     fp32; the selection key is the fp32 sum score + bias.
+  R14 groups are n_group runs of E/n_group consecutive expert ids; a group's
+     score is the fp32 sum, in descending order, of its group_k largest
+     selection keys (DeepSeek-V3's node-limited rule sums the K/M largest
+     affinities of a node); the topk_group best groups are kept (ties to
+     the lower group id), then the K best keys among their experts (ties to
+     the lower expert id), in descending key order.
+  R15 the weights are the chosen unbiased scores, divided by their sum when
+     renormalising, times a scale factor (the routed scaling factor).
 
 Parity pins: see tests/test_oracle_pins.py (brute force, a third-party
 Mixtral MoE block, textbook sorts, page worked examples, closed forms).
@@ -124,6 +137,63 @@ def topk_route(logits: np.ndarray, K: int):
     sel = np.take_along_axis(v, order[:, :K], axis=1)
     z = np.exp(sel - sel[:, :1])
     w = z / z.sum(axis=1, keepdims=True)
+    status = STATUS_NONFINITE if (~np.isfinite(lg)).any() else 0
+    return ids, w, status
+
+
+def sigmoid_scores_fp32(logits: np.ndarray) -> np.ndarray:
+    """R13: s = 1 / (1 + exp(-l)) evaluated in fp64 on the fp32 logit, then
+    rounded to fp32 (both sides of a routing comparison use these values)."""
+    l = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    with np.errstate(over="ignore"):
+        return (1.0 / (1.0 + np.exp(-l))).astype(np.float32)
+
+
+def _desc_order(v: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """Indices of v sorted by value descending (NaN last, -0 == +0), ties to
+    the lower id: R1's order."""
+    v64 = np.asarray(v, np.float64) + 0.0
+    nan = np.isnan(v64)
+    v64 = np.where(nan, 0.0, v64)
+    return np.lexsort((ids, -v64, nan.astype(np.int8)))
+
+
+def grouped_topk_route(logits: np.ndarray, K: int, n_group: int, topk_group: int, group_k: int,
+                       score_bias: np.ndarray | None = None, renormalize: bool = True,
+                       scale: float = 1.0):
+    """Grouped sigmoid routing per token (R13-R15): scores, selection keys
+    with the correction bias, group scores, the kept groups, the K chosen
+    experts and their weights from the unbiased scores.
+
+    Returns ids [T, K] int32, weights [T, K] float64, status bits."""
+    lg = np.asarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    assert E % n_group == 0 and 1 <= topk_group <= n_group
+    gsize = E // n_group
+    assert 1 <= group_k <= gsize and 1 <= K <= topk_group * gsize
+    s = sigmoid_scores_fp32(lg)
+    b = np.zeros(E, np.float32) if score_bias is None else np.asarray(score_bias, np.float32)
+    key = (s + b[None, :]).astype(np.float32)          # fp32 addition
+    ids = np.empty((T, K), np.int32)
+    w = np.empty((T, K), np.float64)
+    for t in range(T):
+        # group scores: the group_k largest keys of each group, summed in fp32
+        # in descending order
+        gscore = np.empty(n_group, np.float32)
+        for g in range(n_group):
+            vals = key[t, g * gsize:(g + 1) * gsize]
+            top = vals[_desc_order(vals, np.arange(gsize))[:group_k]]
+            acc = np.float32(top[0])
+            for v in top[1:]:
+                acc = np.float32(acc + v)
+            gscore[g] = acc
+        kept = _desc_order(gscore, np.arange(n_group))[:topk_group]
+        cand = np.concatenate([np.arange(g * gsize, (g + 1) * gsize) for g in sorted(kept)])
+        chosen = cand[_desc_order(key[t, cand], cand)[:K]]
+        ids[t] = chosen
+        sw = s[t, chosen].astype(np.float64)
+        wt = sw / sw.sum() if renormalize else sw
+        w[t] = wt * scale
     status = STATUS_NONFINITE if (~np.isfinite(lg)).any() else 0
     return ids, w, status
 
@@ -259,7 +329,7 @@ def swiglu_expert(X: np.ndarray, W1: np.ndarray, W3: np.ndarray, W2: np.ndarray)
 
 def moe_forward(x, w_router, bias, K, E_phys, expert_weights, shared_weights=None,
                 p2l=None, layout="contig", M_max=0, BM=16, logits=None,
-                tokens=None):
+                tokens=None, grouped=None):
     """The layer forward as defined: returns a dict with every intermediate.
 
     x [T, H] (values exactly as the layer receives them); w_router [E, H];
@@ -267,7 +337,10 @@ def moe_forward(x, w_router, bias, K, E_phys, expert_weights, shared_weights=Non
     slot p; shared_weights the same triple or None.  ``logits`` (fp32), if
     given, replaces the router step (routing parity is defined on the same
     fp32 logits).  ``tokens`` restricts the FFN and combine to a sample of
-    token ids (routing still covers every token, as it must).
+    token ids (routing still covers every token, as it must).  ``grouped``,
+    a dict of grouped_topk_route's keyword arguments (n_group, topk_group,
+    group_k, score_bias, renormalize, scale), selects the grouped sigmoid
+    router instead of the softmax top-K.
 
     out[t] = S[t] + sum_k w[t, k] * Y[row_of[t, k]]   ([vllbc] combine:
     weight by g_i then sum the K results; R4 for S)."""
@@ -276,7 +349,10 @@ def moe_forward(x, w_router, bias, K, E_phys, expert_weights, shared_weights=Non
     E = np.asarray(w_router).shape[0]
     if logits is None:
         logits = router_logits(x, w_router, bias)
-    ids, w, status = topk_route(logits, K)
+    if grouped is None:
+        ids, w, status = topk_route(logits, K)
+    else:
+        ids, w, status = grouped_topk_route(logits, K, **grouped)
     l2p = count = None
     if p2l is not None:
         l2p, count = replica_tables(p2l, E)

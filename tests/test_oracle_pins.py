@@ -397,3 +397,105 @@ def test_distinct_experts_track_coverage(cfgf, B):
     se = float(np.std(counts, ddof=1) / np.sqrt(len(counts))) if np.std(counts) > 0 else 0.0
     assert mean <= exp + 3 * se + 1e-9
     assert mean >= exp * 0.97 - 3 * se
+
+
+# ------------------------------------------------- grouped sigmoid router (R13-R15)
+
+def _grouped_logits(T=64, E=64, seed=3):
+    rng = np.random.default_rng(seed)
+    return rng.normal(scale=1.5, size=(T, E)).astype(np.float32), rng
+
+
+def test_grouped_router_matches_transformers_deepseek_v3_router():
+    """Hugging Face's DeepSeek-V3 router (sigmoid scores, correction bias for
+    the choice only, best groups by the sum of their two largest biased
+    scores, then top-k inside them, weights from the unbiased scores,
+    normalised and scaled) -- a third-party implementation -- chooses the
+    same experts and gives the same weights from its own fp32 logits."""
+    from transformers import DeepseekV3Config
+    from transformers.models.deepseek_v3.modeling_deepseek_v3 import DeepseekV3TopkRouter
+    H, E, K, G, TG, scale = 96, 64, 8, 8, 4, 2.5
+    hf = DeepseekV3Config(hidden_size=H, n_routed_experts=E, num_experts_per_tok=K, n_group=G,
+                          topk_group=TG, norm_topk_prob=True, routed_scaling_factor=scale)
+    gate = DeepseekV3TopkRouter(hf).eval()
+    rng = np.random.default_rng(7)
+    x = torch.from_numpy(rng.normal(size=(48, H)).astype(np.float32))
+    bias = rng.normal(scale=0.3, size=E).astype(np.float32)
+    with torch.no_grad():
+        gate.weight.copy_(torch.from_numpy(rng.normal(scale=0.15, size=(E, H)).astype(np.float32)))
+        gate.e_score_correction_bias.copy_(torch.from_numpy(bias))
+        logits, hf_w, hf_ids = gate(x)
+    logits = logits.float().numpy().reshape(-1, E)
+    ids, w, st = O.grouped_topk_route(logits, K, G, TG, 2, bias, True, scale)
+    hf_ids, hf_w = hf_ids.numpy().reshape(-1, K), hf_w.float().numpy().reshape(-1, K)
+    assert st == 0
+    for t in range(ids.shape[0]):
+        assert set(ids[t].tolist()) == set(hf_ids[t].tolist()), t
+        mine = dict(zip(ids[t].tolist(), w[t]))
+        for e, v in zip(hf_ids[t].tolist(), hf_w[t]):
+            # HF takes its sigmoid in fp32; the reading rounds an fp64 sigmoid
+            assert abs(mine[e] - v) <= 1e-6 * scale, (t, e)
+
+
+def test_grouped_router_one_group_is_sigmoid_topk():
+    """One group kept out of one, no bias: the choice is the K largest
+    scores, i.e. (sigmoid being increasing) the K largest logits -- the
+    softmax router's choice -- and the renormalised weights are torch's
+    sigmoid of those logits over their sum."""
+    lg, _ = _grouped_logits()
+    ids, w, _ = O.grouped_topk_route(lg, 6, 1, 1, 1, None, True, 1.0)
+    ref_ids, _, _ = O.topk_route(lg, 6)
+    assert (ids == ref_ids).all()
+    s = torch.sigmoid(torch.from_numpy(lg).double()).numpy()
+    sel = np.take_along_axis(s, ids, 1)
+    assert np.allclose(w, sel / sel.sum(1, keepdims=True), rtol=1e-6, atol=0)
+
+
+def test_grouped_router_all_groups_kept_is_global_topk_of_biased_scores():
+    """Keeping every group leaves a plain top-K of score + bias over all
+    experts (any group size, any group_k): Python's sorted() on
+    (-(s + b), id)."""
+    lg, rng = _grouped_logits()
+    b = rng.normal(scale=0.2, size=lg.shape[1]).astype(np.float32)
+    s = O.sigmoid_scores_fp32(lg)
+    key = (s + b[None, :]).astype(np.float32)
+    for G, gk in ((4, 1), (8, 3), (16, 2)):
+        ids, _, _ = O.grouped_topk_route(lg, 8, G, G, gk, b, True, 1.0)
+        for t in range(lg.shape[0]):
+            ref = [e for _, e in sorted((-float(key[t, e]), e) for e in range(lg.shape[1]))[:8]]
+            assert ids[t].tolist() == ref
+
+
+def test_grouped_router_bias_steers_choice_not_weights():
+    """The correction bias only decides which experts are chosen: the
+    weights are always the chosen experts' unbiased sigmoid scores over
+    their sum, times the scale; a large bias on expert 5 forces it into
+    every token's choice with its own (unbiased) score as weight."""
+    lg, rng = _grouped_logits()
+    E = lg.shape[1]
+    s = torch.sigmoid(torch.from_numpy(lg).double()).numpy()
+    for b in (rng.normal(scale=0.5, size=E).astype(np.float32), None):
+        ids, w, _ = O.grouped_topk_route(lg, 8, 8, 4, 2, b, True, 2.5)
+        sel = np.take_along_axis(s, ids, 1)
+        assert np.allclose(w, 2.5 * sel / sel.sum(1, keepdims=True), rtol=1e-6, atol=0)
+    b = np.zeros(E, np.float32)
+    b[5] = 100.0
+    ids, w, _ = O.grouped_topk_route(lg, 8, 8, 4, 2, b, False, 1.0)
+    assert (ids[:, 0] == 5).all()
+    assert np.allclose(w[:, 0], s[:, 5], rtol=1e-6, atol=0)
+
+
+def test_grouped_router_keeps_only_the_best_groups():
+    """Every chosen expert lies in one of the topk_group groups whose sums of
+    group_k largest biased scores are highest (a brute force over the group
+    subsets: the kept set has the largest score total among all subsets of
+    that size)."""
+    lg, rng = _grouped_logits(T=32, E=32)
+    b = rng.normal(scale=0.3, size=32).astype(np.float32)
+    key = (O.sigmoid_scores_fp32(lg) + b[None, :]).astype(np.float32).astype(np.float64)
+    G, TG, gk, K = 8, 3, 2, 6
+    ids, _, _ = O.grouped_topk_route(lg, K, G, TG, gk, b, True, 1.0)
+    for t in range(32):
+        gs = [np.sort(key[t, g * 4:(g + 1) * 4])[::-1][:gk].sum() for g in range(G)]
+        best = max(itertools.combinations(range(G), TG), key=lambda c: sum(gs[g] for g in c))
+        assert {int(e) // 4 for e in ids[t]} <= set(best), t
