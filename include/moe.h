@@ -186,6 +186,36 @@ moe_status_t moe_route(const moe_desc_t* d, const float* logits, int32_t T,
                        const moe_route_t* r, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* Grouped sigmoid router (DeepSeek style; vllbc blog, routing section and
+ * Table 3-1: sigmoid scores, a correction bias used only to choose experts,
+ * weights from the unbiased scores, best groups first, then experts inside
+ * them).  Per token: s_e = fp32 of the fp64 sigmoid of the fp32 logit;
+ * selection key c_e = fp32(s_e + score_bias[e]); the E experts form n_group
+ * groups of E/n_group consecutive ids, each scored by the fp32 sum, in
+ * descending order, of its group_k largest keys; the topk_group best groups
+ * are kept (ties to the lower group id) and the K largest keys among their
+ * experts chosen (ties to the lower id), in descending key order; weight k
+ * = s of choice k, divided by the sum of the K chosen s when renormalize is
+ * set, times scale. */
+typedef struct {
+  const float* score_bias;   /* [E] device fp32, or NULL for none */
+  int32_t n_group;           /* >= 1, divides E; E/n_group divides 64 */
+  int32_t topk_group;        /* 1 .. n_group */
+  int32_t group_k;           /* 1 .. min(8, E/n_group) */
+  int32_t renormalize;       /* 0 or 1 */
+  float scale;               /* finite */
+} moe_grouped_router_t;
+
+/* moe_route with the grouped sigmoid router in place of the softmax top-K:
+ * same tables, conventions and errors; also MOE_ERR_ARG for a NULL g or
+ * parameters outside the ranges above, MOE_ERR_UNSUPPORTED for K >
+ * topk_group * E/n_group. */
+moe_status_t moe_route_grouped(const moe_desc_t* d, const float* logits, int32_t T,
+                               const moe_grouped_router_t* g,
+                               const int32_t* l2p, const int32_t* replica_count,
+                               const moe_route_t* r, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
 /* a5. Gathers token rows into the grouped buffer: xg[slot_of[t*K+k]] = x[t]
  * (cast to bf16 if x is fp32) and, with a shared expert,
  * xg[moe_shared_base + t] = x[t].  x: device [T, H] act_dtype;

@@ -24,6 +24,7 @@ MOE_STATUS_SPILL, MOE_STATUS_BAD_REPLICA, MOE_STATUS_NONFINITE, MOE_STATUS_INTER
 EXPORTED = [
     "moe_status_string", "moe_check_desc", "moe_route_workspace_bytes", "moe_buffer_rows",
     "moe_shared_base", "moe_down_splits", "moe_y_bytes", "moe_router_logits", "moe_route",
+    "moe_route_grouped",
     "moe_permute", "moe_expert_gate_up", "moe_expert_gate_up_x", "moe_expert_down",
     "moe_grouped_ffn", "moe_grouped_ffn_x", "moe_combine", "moe_forward", "moe_pack_weights",
     "moe_replica_map_from_p2l",
@@ -45,6 +46,11 @@ class moe_route_t(ctypes.Structure):
         "offsets", "masked_m", "spill_off", "pad_off", "tile_off", "status")]
 
 
+class moe_grouped_router_t(ctypes.Structure):
+    _fields_ = [("score_bias", _P), ("n_group", ctypes.c_int32), ("topk_group", ctypes.c_int32),
+                ("group_k", ctypes.c_int32), ("renormalize", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
 class moe_weights_t(ctypes.Structure):
     _fields_ = [(n, _P) for n in (
         "w1", "w3", "w2", "s1", "s3", "s2", "sw1", "sw3", "sw2", "ss1", "ss3", "ss2")]
@@ -64,6 +70,7 @@ def lib() -> ctypes.CDLL:
         D = ctypes.POINTER(moe_desc_t)
         R = ctypes.POINTER(moe_route_t)
         W = ctypes.POINTER(moe_weights_t)
+        GR = ctypes.POINTER(moe_grouped_router_t)
         i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         sig = {
             "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -75,6 +82,7 @@ def lib() -> ctypes.CDLL:
             "moe_y_bytes": (sz, [D, i32]),
             "moe_router_logits": (ctypes.c_int, [D, _P, _P, _P, i32, _P, _P]),
             "moe_route": (ctypes.c_int, [D, _P, i32, _P, _P, R, _P, sz, _P]),
+            "moe_route_grouped": (ctypes.c_int, [D, _P, i32, GR, _P, _P, R, _P, sz, _P]),
             "moe_permute": (ctypes.c_int, [D, _P, i32, R, _P, _P]),
             "moe_expert_gate_up": (ctypes.c_int, [D, W, R, i32, _P, _P, _P]),
             "moe_expert_gate_up_x": (ctypes.c_int, [D, W, R, i32, _P, _P, _P]),
@@ -221,6 +229,23 @@ def moe_route(d: Desc, logits, T, rt: RouteTables, ws, l2p=None, replica_count=N
                            _stream(stream)), "moe_route")
 
 
+class GroupedRouter:
+    """Parameters of the grouped sigmoid router (moe_grouped_router_t);
+    ``score_bias`` is a device fp32 tensor [E] or None."""
+
+    def __init__(self, n_group, topk_group, group_k, renormalize=True, scale=1.0, score_bias=None):
+        self.score_bias = score_bias
+        self.c = moe_grouped_router_t(_ptr(score_bias), n_group, topk_group, group_k,
+                                      int(bool(renormalize)), float(scale))
+
+
+def moe_route_grouped(d: Desc, logits, T, rt: RouteTables, ws, router: GroupedRouter, l2p=None,
+                      replica_count=None, stream=None):
+    _check(lib().moe_route_grouped(ctypes.byref(d.c()), _ptr(logits), T, ctypes.byref(router.c),
+                                   _ptr(l2p), _ptr(replica_count), ctypes.byref(rt.c), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream)), "moe_route_grouped")
+
+
 def moe_permute(d: Desc, x, T, rt: RouteTables, xg, stream=None):
     _check(lib().moe_permute(ctypes.byref(d.c()), _ptr(x), T, ctypes.byref(rt.c), _ptr(xg),
                              _stream(stream)), "moe_permute")
@@ -294,8 +319,9 @@ class MoELayer:
     the shared expert, if any, is the last slot."""
 
     def __init__(self, d: Desc, weights: dict, w_router, bias=None, l2p=None,
-                 replica_count=None, device="cuda"):
+                 replica_count=None, device="cuda", router: GroupedRouter | None = None):
         self.d = d
+        self.router = router           # None: softmax top-K (moe_route)
         self.device = device
         self.rt = RouteTables(d, device)
         self.ws = torch.zeros(route_workspace_bytes(d), dtype=torch.uint8, device=device)
@@ -332,7 +358,10 @@ class MoELayer:
         if logits is None:
             moe_router_logits(d, x, self.w_router, self.bias, T, self.logits, stream)
             logits = self.logits
-        moe_route(d, logits, T, self.rt, self.ws, self.l2p, self.rcount, stream)
+        if self.router is None:
+            moe_route(d, logits, T, self.rt, self.ws, self.l2p, self.rcount, stream)
+        else:
+            moe_route_grouped(d, logits, T, self.rt, self.ws, self.router, self.l2p, self.rcount, stream)
         if fused_gather and d.act_dtype == MOE_BF16:
             moe_grouped_ffn_x(d, self.weights, self.rt, T, x, self.h, self.y, stream)
         else:

@@ -29,6 +29,9 @@ struct RouteArgs {
   int32_t* masked_m; int32_t* spill_off; int32_t* pad_off; int32_t* tile_off; uint32_t* status;
   int n_shared;
   RouteWs ws;
+  // grouped sigmoid router (selection phase only); grouped == 0: softmax top-K
+  int grouped, n_group, topk_group, group_k, renormalize;
+  const float* score_bias; float scale;
 };
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <cmath>
 #include <cstdlib>
 
 #include "common.hpp"
@@ -141,11 +142,24 @@ moe_status_t moe_router_logits(const moe_desc_t* d, const void* x, const void* w
   return hip_status(launch_router(a, stream));
 }
 
-moe_status_t moe_route(const moe_desc_t* d, const float* logits, int32_t T, const int32_t* l2p,
-                       const int32_t* replica_count, const moe_route_t* r, void* ws,
-                       size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status_t route_impl(const moe_desc_t* d, const float* logits, int32_t T, const moe_grouped_router_t* g,
+                        const int32_t* l2p, const int32_t* replica_count, const moe_route_t* r, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
   moe_status_t st = moe_check_desc(d);
   if (st != MOE_OK) return st;
+  if (g) {
+    const int G = g->n_group;
+    if (G < 1 || d->E % G) return MOE_ERR_ARG;
+    const int gs = d->E / G;
+    if (64 % gs || g->topk_group < 1 || g->topk_group > G || g->group_k < 1 || g->group_k > 8 ||
+        g->group_k > gs || (g->renormalize != 0 && g->renormalize != 1) || !std::isfinite(g->scale))
+      return MOE_ERR_ARG;
+    if (d->K > g->topk_group * gs) return MOE_ERR_UNSUPPORTED;
+  }
   if (T < 0 || T > d->T_max || !route_ptrs_ok(d, r)) return MOE_ERR_ARG;
   if (T > 0 && !logits) return MOE_ERR_ARG;
   if ((l2p == nullptr) != (replica_count == nullptr)) return MOE_ERR_ARG;
@@ -166,7 +180,29 @@ moe_status_t moe_route(const moe_desc_t* d, const float* logits, int32_t T, cons
   a.ws.blk_flags = reinterpret_cast<int32_t*>(base + wl.flags);
   a.ws.tok_flag = reinterpret_cast<int32_t*>(base + wl.tok_flag);
   a.ws.map_valid = reinterpret_cast<int32_t*>(base + wl.map_valid);
+  if (g) {
+    a.grouped = 1; a.n_group = g->n_group; a.topk_group = g->topk_group; a.group_k = g->group_k;
+    a.renormalize = g->renormalize; a.score_bias = g->score_bias; a.scale = g->scale;
+  }
   return hip_status(launch_route(a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_route(const moe_desc_t* d, const float* logits, int32_t T, const int32_t* l2p,
+                       const int32_t* replica_count, const moe_route_t* r, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  return route_impl(d, logits, T, nullptr, l2p, replica_count, r, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_route_grouped(const moe_desc_t* d, const float* logits, int32_t T,
+                               const moe_grouped_router_t* g, const int32_t* l2p,
+                               const int32_t* replica_count, const moe_route_t* r, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  if (!g) return MOE_ERR_ARG;
+  return route_impl(d, logits, T, g, l2p, replica_count, r, ws, ws_bytes, stream);
 }
 
 moe_status_t moe_permute(const moe_desc_t* d, const void* x, int32_t T, const moe_route_t* r,

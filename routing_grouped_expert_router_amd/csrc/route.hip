@@ -104,6 +104,130 @@ __device__ __forceinline__ void select_tokens(const RouteArgs& a, int t0, int co
   }
 }
 
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
+  const uint32_t lo = __shfl_xor((unsigned)(v & 0xffffffffu), off, kWave);
+  const uint32_t hi = __shfl_xor((unsigned)(v >> 32), off, kWave);
+  return (uint64_t(hi) << 32) | lo;
+}
+
+// Grouped sigmoid router (DeepSeek style), one wave per token: lane l holds
+// experts l + 64j.  The group size gs = E / n_group divides 64, so the lanes
+// of key slot j fall into 64/gs whole groups and a group's reductions are
+// xor-shuffles inside gs-lane segments.
+//   s_e = fp32(1 / (1 + exp(-l_e))) in fp64; key c_e = fp32(s_e + bias_e)
+//   group score = sum of its group_k largest keys, fp32, descending order
+//   keep the topk_group best groups (ties to the lower group id), choose the
+//   K largest keys among their experts (ties to the lower id)
+//   weight = s of the choice (/ sum of the K chosen s) * scale
+template <int NPL>
+__device__ __forceinline__ void select_tokens_grouped(const RouteArgs& a, int t0, int count, int wave, int nwaves) {
+  const int E = a.E, K = a.K, G = a.n_group;
+  const int gs = E / G;
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int base = wave; base < count; base += nwaves) {
+    const int t = t0 + base;
+    const bool valid = t < a.T;
+    const float* row = a.logits + (int64_t)(valid ? t : 0) * E;
+    // all loads issued unconditionally (clamped column), masked afterwards
+    float lv[NPL], bv[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int ec = min(lane + kWave * j, E - 1);
+      lv[j] = row[ec];
+      bv[j] = a.score_bias ? a.score_bias[ec] : 0.f;
+    }
+    float sc[NPL];
+    uint64_t key[NPL];
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int e = lane + kWave * j;
+      const bool in = valid && e < E;
+      bad |= in && !__builtin_isfinite(lv[j]);
+      sc[j] = (float)(1.0 / (1.0 + exp(-(double)lv[j])));
+      key[j] = in ? topk_key(sc[j] + bv[j], e) : 0ull;
+    }
+    // ---- group scores: per slot, group_k rounds of a segmented max (the
+    // segment's winner pops its key), summed in descending order
+    float gsum[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      uint64_t kk = key[j];
+      float acc = 0.f;
+      for (int r = 0; r < a.group_k; ++r) {
+        uint64_t best = kk;
+        for (int off = gs >> 1; off >= 1; off >>= 1) {
+          const uint64_t o = shfl_xor_u64(best, off);
+          best = o > best ? o : best;
+        }
+        const float v = order_key_value(uint32_t(best >> 32));
+        acc = r == 0 ? v : acc + v;
+        kk = kk == best ? 0ull : kk;
+      }
+      gsum[j] = acc;
+    }
+    // ---- group g's score onto lane g: slot (g*gs)/64, segment lane (g*gs)%64
+    float my_g = 0.f;
+    const int gj = (lane * gs) >> 6, gl = (lane * gs) & (kWave - 1);
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const float v = __shfl(gsum[j], gl, kWave);
+      my_g = j == gj ? v : my_g;
+    }
+    uint64_t gkey = (valid && lane < G) ? topk_key(my_g, lane) : 0ull;
+    uint64_t gmask = 0ull;
+    for (int r = 0; r < a.topk_group; ++r) {
+      const uint64_t best = wave_max_u64(gkey);
+      gmask |= 1ull << (int(0xffffffffu - uint32_t(best & 0xffffffffu)) & 63);
+      gkey = gkey == best ? 0ull : gkey;
+    }
+    // ---- experts of the kept groups, sorted inside the lane with their scores
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int e = lane + kWave * j;
+      key[j] = ((gmask >> ((e / gs) & 63)) & 1ull) ? key[j] : 0ull;
+    }
+#pragma unroll
+    for (int i = 1; i < NPL; ++i)
+#pragma unroll
+      for (int j = i; j > 0; --j) {
+        const bool sw = key[j] > key[j - 1];
+        const uint64_t k0 = sw ? key[j] : key[j - 1], k1 = sw ? key[j - 1] : key[j];
+        const float s0 = sw ? sc[j] : sc[j - 1], s1 = sw ? sc[j - 1] : sc[j];
+        key[j - 1] = k0; key[j] = k1; sc[j - 1] = s0; sc[j] = s1;
+      }
+    uint64_t my_key = 0ull;
+    float my_s = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const uint64_t best = wave_max_u64(key[0]);
+      const int id = int(0xffffffffu - uint32_t(best & 0xffffffffu));
+      const float sb = __shfl(sc[0], id & (kWave - 1), kWave);   // the winner's lane is id % 64
+      if (lane == k) { my_key = best; my_s = sb; }
+      const bool win = key[0] == best;
+#pragma unroll
+      for (int j = 0; j < NPL - 1; ++j) { key[j] = win ? key[j + 1] : key[j]; sc[j] = win ? sc[j + 1] : sc[j]; }
+      key[NPL - 1] = win ? 0ull : key[NPL - 1];
+    }
+    const int my_id = int(0xffffffffu - uint32_t(my_key & 0xffffffffu));
+    const float ek = (valid && lane < K) ? my_s : 0.f;
+    float sum = 0.f;
+    for (int k = 0; k < K; ++k) sum += __shfl(ek, k, kWave);
+    const uint64_t badm = __ballot(bad);
+    if (valid && lane < K) {
+      const int id = (my_id >= 0 && my_id < E) ? my_id : 0;
+      a.topk_ids[(int64_t)t * K + lane] = id;
+      a.topk_w[(int64_t)t * K + lane] = (a.renormalize ? ek / sum : ek) * a.scale;
+    }
+    if (valid && lane == 0) a.ws.tok_flag[t] = badm ? 1 : 0;
+  }
+}
+
+template <int NPL>
+__global__ __launch_bounds__(kSelectThreads) void route_select_grouped_kernel(RouteArgs a) {
+  constexpr int per_wg = kSelectThreads / kWave;   // one token per wave
+  select_tokens_grouped<NPL>(a, blockIdx.x * per_wg, per_wg, threadIdx.x / kWave, per_wg);
+}
+
 template <int LPT, int NPL>
 __global__ __launch_bounds__(kSelectThreads) void route_select_kernel(RouteArgs a) {
   constexpr int per_wg = (kSelectThreads / kWave) * (kWave / LPT);
@@ -285,10 +409,11 @@ __global__ __launch_bounds__(kRouteThreads) void route_assign_kernel(RouteArgs a
 // T <= 64: the four phases in one workgroup (one launch instead of four).
 // The barrier between phases orders the global-memory tables each phase
 // writes before the next one reads them.
-template <int LPT, int NPL>
+template <int LPT, int NPL, bool GROUPED>
 __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(RouteArgs a) {
   if (a.T > 0) {
-    select_tokens<LPT, NPL>(a, 0, a.T, threadIdx.x / kWave, kFusedThreads / kWave);
+    if constexpr (GROUPED) select_tokens_grouped<NPL>(a, 0, a.T, threadIdx.x / kWave, kFusedThreads / kWave);
+    else select_tokens<LPT, NPL>(a, 0, a.T, threadIdx.x / kWave, kFusedThreads / kWave);
     __syncthreads();
     rank_block(a, 0);
   }
@@ -299,18 +424,26 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(RouteArgs a)
   for (int64_t i = threadIdx.x; i < TK; i += kFusedThreads) assign_one(a, i);
 }
 
-template <int LPT, int NPL>
+template <int LPT, int NPL, bool GROUPED = false>
 static void launch_shape(const RouteArgs& a, int nblk, hipStream_t s) {
   // one block: a single launch, unless 16 keys per lane would not fit the
   // registers of a 1024-thread workgroup
-  if (nblk <= 1 && NPL <= 8) {
-    hipLaunchKernelGGL((route_fused_kernel<LPT, NPL>), dim3(1), dim3(kFusedThreads), 0, s, a);
+  constexpr bool kFusedFits = GROUPED ? NPL <= 4 : NPL <= 8;
+  if (nblk <= 1 && kFusedFits) {
+    hipLaunchKernelGGL((route_fused_kernel<LPT, NPL, GROUPED>), dim3(1), dim3(kFusedThreads), 0, s, a);
     return;
   }
-  constexpr int per_wg = (kSelectThreads / kWave) * (kWave / LPT);
-  if (a.T > 0)
-    hipLaunchKernelGGL((route_select_kernel<LPT, NPL>), dim3((a.T + per_wg - 1) / per_wg), dim3(kSelectThreads),
-                       0, s, a);
+  if (a.T > 0) {
+    if constexpr (GROUPED) {
+      constexpr int per_wg = kSelectThreads / kWave;
+      hipLaunchKernelGGL((route_select_grouped_kernel<NPL>), dim3((a.T + per_wg - 1) / per_wg),
+                         dim3(kSelectThreads), 0, s, a);
+    } else {
+      constexpr int per_wg = (kSelectThreads / kWave) * (kWave / LPT);
+      hipLaunchKernelGGL((route_select_kernel<LPT, NPL>), dim3((a.T + per_wg - 1) / per_wg), dim3(kSelectThreads),
+                         0, s, a);
+    }
+  }
   hipLaunchKernelGGL(route_rank_kernel, dim3(nblk > 0 ? nblk : 1), dim3(kRouteThreads), 0, s, a);
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
   const int64_t TK = (int64_t)a.T * a.K;
@@ -324,6 +457,16 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
   // lanes per token: the smallest power of two >= E between 8 and 64; keys
   // per lane: ceil(E / lanes) (E <= 1024)
   const int E = a.E;
+  if (a.grouped) {
+    // one wave (64 lanes) per token, ceil(E/64) keys per lane
+    if (E <= 64) launch_shape<64, 1, true>(a, nblk, s);
+    else if (E <= 128) launch_shape<64, 2, true>(a, nblk, s);
+    else if (E <= 256) launch_shape<64, 4, true>(a, nblk, s);
+    else if (E <= 512) launch_shape<64, 8, true>(a, nblk, s);
+    else if (E <= 1024) launch_shape<64, 16, true>(a, nblk, s);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (E <= 8) launch_shape<8, 1>(a, nblk, s);
   else if (E <= 16) launch_shape<16, 1>(a, nblk, s);
   else if (E <= 32) launch_shape<32, 1>(a, nblk, s);

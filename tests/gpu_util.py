@@ -26,7 +26,7 @@ _DEFAULT = object()
 class Built:
     """A workload on the GPU: inputs, uploaded weights and a MoELayer."""
 
-    def __init__(self, cfg, T=None, layout=None, M_max=None, p2l=_DEFAULT, packed=False):
+    def __init__(self, cfg, T=None, layout=None, M_max=None, p2l=_DEFAULT, packed=False, grouped=None):
         if layout is not None:
             cfg = cfg.with_(layout=layout)
         if M_max is not None:
@@ -51,7 +51,16 @@ class Built:
         self.x = self.inp.x.to(DEV)
         self.wr = self.inp.w_router.to(DEV)
         self.bias = None if self.inp.bias is None else self.inp.bias.to(DEV)
-        self.layer = B.MoELayer(self.d, self.weights, self.wr, self.bias, self.l2p, self.rcount, DEV)
+        # grouped: grouped_topk_route's keyword arguments (score_bias as numpy)
+        self.grouped = grouped
+        router = None
+        if grouped is not None:
+            sb = grouped.get("score_bias")
+            router = B.GroupedRouter(grouped["n_group"], grouped["topk_group"], grouped["group_k"],
+                                     grouped.get("renormalize", True), grouped.get("scale", 1.0),
+                                     None if sb is None else torch.from_numpy(np.asarray(sb, np.float32)).to(DEV))
+        self.layer = B.MoELayer(self.d, self.weights, self.wr, self.bias, self.l2p, self.rcount, DEV,
+                                router=router)
 
     def oracle_logits(self) -> np.ndarray:
         return O.router_logits(to_f64(self.inp.x), to_f64(self.inp.w_router),
@@ -64,7 +73,7 @@ class Built:
         return out
 
     def oracle(self, logits_np=None, tokens=None):
-        return oracle_forward(self.inp, logits=logits_np, tokens=tokens)
+        return oracle_forward(self.inp, logits=logits_np, tokens=tokens, grouped=self.grouped)
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:

@@ -25,7 +25,7 @@ def expert_f64(ew, w_dtype: str):
             O.dequant_block128(ew.w2.numpy(), ew.s2.numpy()))
 
 
-def oracle_forward(inp, logits=None, tokens=None, layout=None):
+def oracle_forward(inp, logits=None, tokens=None, layout=None, grouped=None):
     """Runs the reference on workload inputs ``inp`` (workloads.generate)."""
     cfg = inp.cfg
     cache = {}
@@ -44,4 +44,4 @@ def oracle_forward(inp, logits=None, tokens=None, layout=None):
         None if inp.bias is None else inp.bias.numpy(),
         cfg.K, cfg.E_phys, slot_weights, shared, p2l=inp.p2l,
         layout=layout or cfg.layout, M_max=cfg.M_max, BM=cfg.BM,
-        logits=logits, tokens=tokens)
+        logits=logits, tokens=tokens, grouped=grouped)

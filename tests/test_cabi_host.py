@@ -70,6 +70,16 @@ def test_calls_reject_bad_arguments_before_enqueueing():
     assert L.moe_route(dc, fake, 4, null, null, ctypes.byref(rt2), fake, 1, null) == B.MOE_ERR_WORKSPACE
     # only one of the two replica arrays
     assert L.moe_route(dc, fake, 4, fake, null, ctypes.byref(rt2), fake, 1 << 20, null) == B.MOE_ERR_ARG
+    # grouped router parameters are checked on the host (E = 8 here)
+    for bad in ((0, 1, 1), (3, 1, 1), (4, 5, 1), (4, 2, 3), (1, 1, 9)):
+        g = B.moe_grouped_router_t(None, bad[0], bad[1], bad[2], 1, 1.0)
+        assert L.moe_route_grouped(dc, fake, 4, ctypes.byref(g), null, null, ctypes.byref(rt2), fake,
+                                   1 << 20, null) == B.MOE_ERR_ARG, bad
+    g = B.moe_grouped_router_t(None, 8, 1, 1, 1, 1.0)     # one group of 1 kept, K = 2
+    assert L.moe_route_grouped(dc, fake, 4, ctypes.byref(g), null, null, ctypes.byref(rt2), fake,
+                               1 << 20, null) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_route_grouped(dc, fake, 4, null, null, null, ctypes.byref(rt2), fake, 1 << 20,
+                               null) == B.MOE_ERR_ARG
     # the fused gather needs bf16 activations (the tiny descriptor's are fp32)
     w0 = B.moe_weights_t(fake, fake, fake, None, None, None, None, None, None, None, None, None)
     assert L.moe_expert_gate_up_x(dc, ctypes.byref(w0), ctypes.byref(rt2), 4, fake, fake,
