@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU reference timing")
     ap.add_argument("--row-major", action="store_true",
                     help="stream the row-major weights instead of the packed layout")
+    ap.add_argument("--router", choices=("softmax", "grouped"), default="softmax",
+                    help="softmax top-K (default) or the grouped sigmoid router with "
+                         "8 groups, 4 kept, group score = sum of the 2 best, weights x2.5")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 512 MiB device copy three times (a kernel of known "
                          "traffic for scaling hardware byte counters)")
@@ -59,8 +62,11 @@ def weight_bytes_per_slot(cfg):
     return 3 * cfg.H * cfg.I + 3 * (cfg.H // 128) * (cfg.I // 128) * 4
 
 
+GROUPED_ROUTER = dict(n_group=8, topk_group=4, group_k=2, renormalize=True, scale=2.5)
+
+
 class Setup:
-    def __init__(self, cfg, packed=True):
+    def __init__(self, cfg, packed=True, router="softmax"):
         import torch
         from routing_grouped_expert_router_amd import binding as B
         from workloads import generate
@@ -84,14 +90,23 @@ class Setup:
         self.x = self.inp.x.cuda()
         self.wr = self.inp.w_router.cuda()
         self.bias = None if self.inp.bias is None else self.inp.bias.cuda()
-        self.layer = B.MoELayer(self.d, self.w, self.wr, self.bias, l2p, rc, "cuda")
+        self.grouped = None
+        gr = None
+        if router == "grouped":
+            sb = generate.make_score_bias(cfg)
+            self.grouped = dict(GROUPED_ROUTER, score_bias=sb.numpy())
+            gr = B.GroupedRouter(score_bias=sb.cuda(), **GROUPED_ROUTER)
+        self.layer = B.MoELayer(self.d, self.w, self.wr, self.bias, l2p, rc, "cuda", router=gr)
         self.B = B
         torch.cuda.synchronize()
 
     def step(self, ev=None):
         B, L, d, T = self.B, self.layer, self.d, self.cfg.T
         B.moe_router_logits(d, self.x, self.wr, self.bias, T, L.logits)
-        B.moe_route(d, L.logits, T, L.rt, L.ws, L.l2p, L.rcount)
+        if L.router is None:
+            B.moe_route(d, L.logits, T, L.rt, L.ws, L.l2p, L.rcount)
+        else:
+            B.moe_route_grouped(d, L.logits, T, L.rt, L.ws, L.router, L.l2p, L.rcount)
         gather = d.act_dtype == B.MOE_BF16     # the gate/up kernel gathers rows from x itself
         if not gather:
             B.moe_permute(d, self.x, T, L.rt, L.xg)
@@ -133,12 +148,12 @@ class Setup:
         return slots, routed, gu, total
 
 
-def time_workload(cfg, steps, warmup, packed=True):
+def time_workload(cfg, steps, warmup, packed=True, router="softmax"):
     """Eager steps (HIP events around the gate/up kernel on the launch
     stream), then the same step captured once in a HIP graph and replayed
     ``steps`` times (the layer latency reported)."""
     import torch
-    s = Setup(cfg, packed)
+    s = Setup(cfg, packed, router)
     for _ in range(warmup):
         s.step()
     torch.cuda.synchronize()
@@ -247,15 +262,23 @@ def cpu_baseline(s, budget_s=30.0):
     inp = s.inp
     # copy every expert the batch touches to host memory first (not timed)
     counts = s.layer.rt.counts.cpu().numpy()
+    print(f"# cpu reference: copying {int((counts > 0).sum())} experts to host memory",
+          file=sys.stderr, flush=True)
     inp.prefetch(sorted({inp.slot_logical(p) for p in np.nonzero(counts)[0]}))
     T = cfg.T
-    for n in (T, max(1, T // 4), max(1, T // 16), 1):
+    # double the token sample from 1 while the last run stayed under a quarter
+    # of the budget (the cost per token is not known beforehand: it is set by
+    # the distinct experts the sample touches)
+    n = 1
+    while True:
         toks = np.arange(0, T, max(1, T // n))[:n]
         t0 = time.perf_counter()
-        oracle_forward(inp, tokens=toks)
+        oracle_forward(inp, tokens=toks, grouped=s.grouped)
         dt = time.perf_counter() - t0
-        if dt <= budget_s or n == 1:
+        print(f"# cpu reference: {len(toks)} of {T} tokens in {dt:.1f} s", file=sys.stderr, flush=True)
+        if n >= T or dt * 4 > budget_s:
             break
+        n = min(T, 2 * n)
     # scale: routing is over the full batch; the FFN part is per token
     frac = len(toks) / T
     est = dt / frac if frac > 0 else dt
@@ -290,7 +313,8 @@ def main():
     results = {}
     for n in names:
         c = configs.by_name(n)
-        r = time_workload(c, args.steps, args.warmup, packed=not args.row_major)
+        r = time_workload(c, args.steps, args.warmup, packed=not args.row_major,
+                          router=args.router)
         results[n] = r
         print(f"# {n}: {r['ms']*1e3:.1f} us/layer (graph), {r['eager_ms']*1e3:.1f} eager, "
               f"gate/up {r['gu_ms']*1e3:.1f} us ({r['gu_flops']/(r['gu_ms']*1e-3)/1e12:.0f} TFLOP/s), "
@@ -325,7 +349,9 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
                    "E_phys": cfg.E_phys, "K": cfg.K, "n_shared": cfg.n_shared,
                    "layout": cfg.layout, "M_max": cfg.M_max, "w_dtype": cfg.w_dtype,
-                   "weights": "row-major" if args.row_major else "packed"},
+                   "weights": "row-major" if args.row_major else "packed",
+                   "router": args.router if args.router == "softmax" else
+                   "grouped sigmoid (8 groups, 4 kept, top-2 group score, x2.5)"},
         "expert_weight_hbm_gbs": round(gb_s, 1),
         "layer_tflops": round(head["layer_flops"] / (head["ms"] * 1e-3) / 1e12, 2),
         "touched_slots": head["slots"],

@@ -113,6 +113,12 @@ def make_bias(cfg: MoEConfig) -> torch.Tensor | None:
     raise ValueError(cfg.bias)
 
 
+def make_score_bias(cfg: MoEConfig, std: float = 0.05) -> torch.Tensor:
+    """Per-expert selection bias [E] of the grouped sigmoid router, seeded
+    ~N(0, std) (the load-balancing correction a trained model carries)."""
+    return _normal((cfg.E,), std, cfg.seed, _TAG_BIAS, 2)
+
+
 def make_p2l(cfg: MoEConfig) -> np.ndarray | None:
     """physical_to_logical map [E_phys]: slots [0, E) are home slots; each
     redundant slot replicates the logical expert with the largest
