@@ -31,6 +31,8 @@
 //  * Each output element accumulates its K range in 32-wide MFMA steps in
 //    ascending order, exactly as the streaming kernel does, so the split of
 //    groups between the two kernels does not change any bit of the result.
+#include <cstdlib>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -65,26 +67,31 @@ __device__ __forceinline__ int swz(int lane, int j) {
   return (lane & 48) | (((lane & 15) + 2 * c) & 15);
 }
 
-template <int MODE, bool PACKED>
-__global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(TiledArgs ta) {
-  const StreamArgs& a = ta.s;
-  __shared__ __attribute__((aligned(16))) char xsm[2 * kXStage];   // activation tile, 2 stages
+// One work item of the tiled kernels: group g, weight-row tile nt, row tile mt
+// and the group's row segments (s0, c0 rows, then s1, c1 spill rows).
+struct TileWork {
+  int g, nt, mt, c0, c1, R;
+  int64_t s0, s1;
+  bool shared;
+};
 
-  // ---- work item.  The hardware deals workgroups round-robin over the 8 XCDs
-  // (linear id L goes to XCD L % 8).  The live work list -- tile_off's
-  // ceil(rows/128) tiles per group times the weight-row tiles -- is cut into 8
-  // contiguous chunks, one per XCD, ordered (group, weight tile, row tile), so
-  // the workgroups an XCD runs together share one group's weight and
-  // activation tiles in that XCD's L2.
+// The hardware deals workgroups round-robin over the 8 XCDs (linear id L goes
+// to XCD L % 8).  The live work list -- tile_off's ceil(rows/128) tiles per
+// group times the weight-row tiles -- is cut into 8 contiguous chunks, one per
+// XCD, ordered (group, weight tile, row tile), so the workgroups an XCD runs
+// together share one group's weight and activation tiles in that XCD's L2.
+// Returns false when this workgroup has no work.
+__device__ __forceinline__ bool decode_work(const TiledArgs& ta, TileWork& w) {
+  const StreamArgs& a = ta.s;
   const int ngroups = a.E_phys + 1;
   const int ntiles_n = gridDim.x;
   const int64_t work = (int64_t)ta.tile_off[ngroups] * ntiles_n;
   const int64_t L = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
   const int64_t chunk = (work + 7) / 8;
   const int64_t k_in = L / 8;
-  if (k_in >= chunk) return;
+  if (k_in >= chunk) return false;
   const int64_t wi = (L % 8) * chunk + k_in;
-  if (wi >= work) return;
+  if (wi >= work) return false;
   int lo = 0, hi = ngroups;                  // largest g with tile_off[g] * ntiles_n <= wi
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -93,21 +100,34 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(TiledArgs ta) {
   const int g = lo;
   const int mtiles = ta.tile_off[g + 1] - ta.tile_off[g];
   const int64_t o = wi - (int64_t)ta.tile_off[g] * ntiles_n;
-  const int nt = int(o / mtiles);            // weight-row tile
-  const int mt = int(o % mtiles);            // row tile within the group
-  int64_t s0 = 0, s1 = 0;
-  int c0 = 0, c1 = 0;
-  const bool shared = g == a.E_phys;
-  if (shared) { s0 = a.shared_base; c0 = a.T; }
+  w.g = g;
+  w.nt = int(o / mtiles);                    // weight-row tile
+  w.mt = int(o % mtiles);                    // row tile within the group
+  w.s0 = w.s1 = 0;
+  w.c0 = w.c1 = 0;
+  w.shared = g == a.E_phys;
+  if (w.shared) { w.s0 = a.shared_base; w.c0 = a.T; }
   else if (a.layout == MOE_MASKED) {
     const int mm = a.masked_m[g];
-    s0 = (int64_t)g * a.M_max; c0 = mm;
-    s1 = (int64_t)a.E_phys * a.M_max + a.spill_off[g]; c1 = a.counts[g] - mm;
+    w.s0 = (int64_t)g * a.M_max; w.c0 = mm;
+    w.s1 = (int64_t)a.E_phys * a.M_max + a.spill_off[g]; w.c1 = a.counts[g] - mm;
   } else {
-    s0 = a.pad_off[g]; c0 = a.counts[g];
+    w.s0 = a.pad_off[g]; w.c0 = a.counts[g];
   }
-  const int R = c0 + c1;
-  if (R <= ta.min_rows) return;           // the streaming kernel owns this group
+  w.R = w.c0 + w.c1;
+  return w.R > ta.min_rows;                  // else the streaming kernel owns this group
+}
+
+template <int MODE, bool PACKED>
+__global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(TiledArgs ta) {
+  const StreamArgs& a = ta.s;
+  __shared__ __attribute__((aligned(16))) char xsm[2 * kXStage];   // activation tile, 2 stages
+
+  TileWork tw;
+  if (!decode_work(ta, tw)) return;
+  const int g = tw.g, nt = tw.nt, mt = tw.mt, c0 = tw.c0, R = tw.R;
+  const int64_t s0 = tw.s0, s1 = tw.s1;
+  const bool shared = tw.shared;
   const int m0 = mt * kTM;                 // first row of the tile within the group
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -280,6 +300,214 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(TiledArgs ta) {
   }
 }
 
+// ---- wide variant: 128 token rows x 512 weight rows per workgroup ----------
+//
+// Each wave owns all 128 token rows x 128 weight rows (8 x 8 MFMA tiles, the
+// 256 accumulator registers of a wave running alone on its SIMD), so every
+// activation fragment read from LDS feeds eight MFMAs instead of four: the
+// LDS operand traffic per MFMA is half the narrow kernel's.  K advances in
+// 32-wide steps (one MFMA K); the activation step (8 KiB, fragment order, one
+// ds_read_b128 per 16-row tile) is double-buffered in LDS, and the global
+// loads of weights and activations run kWBanks - 1 steps ahead through
+// kWBanks register banks.
+constexpr int kWN = 512;                 // weight rows per tile
+constexpr int kWBanks = 4;
+constexpr int kWStage = kTM * 32 * 2;    // 8 KiB: 128 rows x 32 K
+
+// Raw buffer resource over [p, p + bytes): loads take a 32-bit per-lane
+// offset and a wave-uniform 32-bit offset, so the K step moves a scalar only
+// (no per-load 64-bit address arithmetic or address registers), and a load
+// past `bytes` returns zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+template <int MODE, bool PACKED>
+__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ffn_wide_kernel(TiledArgs ta) {
+  const StreamArgs& a = ta.s;
+  __shared__ __attribute__((aligned(16))) char xsm[2 * kWStage];
+
+  TileWork tw;
+  if (!decode_work(ta, tw)) return;
+  const int g = tw.g, nt = tw.nt, c0 = tw.c0, R = tw.R;
+  const int64_t s0 = tw.s0, s1 = tw.s1;
+  const bool shared = tw.shared;
+  const int m0 = tw.mt * kTM;               // first row of the tile within the group
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int Kdim = a.Kdim;
+  const int ks = blockIdx.z;
+  const int kper = Kdim / a.ksplit;
+  const int kc0 = ks * kper / 32;           // first 32-wide K chunk
+  const int nsteps = kper / 32;
+
+  // ---- weight rows: wave w owns eight 16-row weight tiles
+  //   GATEUP: W1 rows n0 + 64w .. +64 (tiles 0..3) and the same W3 rows (tiles 4..7)
+  //   DOWN:   W2 rows n0 + 128w .. +128
+  const int n0 = MODE == MODE_GATEUP ? nt * (kWN / 2) : nt * kWN;
+  const char* Wa;
+  const char* Wb = nullptr;
+  if (shared) { Wa = static_cast<const char*>(a.SW); Wb = static_cast<const char*>(a.SW3); }
+  else {
+    Wa = static_cast<const char*>(a.W) + (int64_t)g * a.N * Kdim * 2;
+    if (MODE == MODE_GATEUP) Wb = static_cast<const char*>(a.W3) + (int64_t)g * a.N * Kdim * 2;
+  }
+  // buffer resources over one weight matrix (N x Kdim) and the activation rows
+  const uint32_t wbytes = (uint32_t)a.N * Kdim * 2;
+  const __amdgpu_buffer_rsrc_t wra = buffer_rsrc(Wa, wbytes);
+  const __amdgpu_buffer_rsrc_t wrb = buffer_rsrc(MODE == MODE_GATEUP ? Wb : Wa, wbytes);
+  const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(a.X, (uint32_t)ta.x_bytes);
+  //   weight tile n: byte offset of this lane's piece at K = 0 within its matrix
+  uint32_t woff[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const int row0 = MODE == MODE_GATEUP ? n0 + 64 * wave + 16 * (n & 3) : n0 + 128 * wave + 16 * n;
+    if (PACKED) woff[n] = (uint32_t)(row0 / 16) * 16 * 128 * 2 + lane * 16;
+    else woff[n] = (uint32_t)(row0 + (lane & 15)) * Kdim * 2 + 16 * (lane >> 4);
+  }
+  auto wk = [&](int kc) -> uint32_t {    // byte offset of 32-wide K chunk kc
+    if (PACKED) return (uint32_t)(kc >> 2) * (a.N / 16) * 4096 + (kc & 3) * 1024;   // step-major
+    return (uint32_t)kc * 64;
+  };
+
+  // ---- activations: thread t stages 16-row tile wave + 4q, row t % 16, 16-byte
+  // K column (t / 16) % 4 of each step, i.e. fragment slot t % 64 of that tile
+  uint32_t xoff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int gr = m0 + (wave + 4 * q) * 16 + (lane & 15);   // row within the group
+    int64_t row = gr < c0 ? s0 + gr : (gr < R ? s1 + (gr - c0) : s0);   // pad rows read a valid row
+    if (a.gather_src) {
+      const int rank = gr < R ? gr : 0;
+      row = shared ? rank : a.gather_src[a.gather_off[g] + rank];
+    }
+    xoff[q] = (uint32_t)(row * a.ldx * 2) + 16 * (lane >> 4);
+  }
+
+  const int rows_here = min(kTM, R - m0);
+  const int mv = ((rows_here + 31) / 32) * 2;
+  auto run = [&](auto mvc) {
+    constexpr int MV = decltype(mvc)::value;    // non-empty 16-row tiles (even)
+    // weights run kWBanks - 1 steps ahead; activations, which the workgroups
+    // of a weight tile share through L2, two steps ahead (bank = step % 2)
+    u32x4 xr[2][2], wr[kWBanks][8];
+    // (every wave stages both of its tiles, also the empty ones past MV, which
+    // read a valid row: loads that depend on the wave would be branches, and
+    // the compiler then waits for every outstanding load once per pass)
+    auto gload_x = [&](int bank, int step) {
+      const uint32_t so = (uint32_t)(kc0 + step) * 64;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) xr[bank][q] = buffer_load16(xrs, xoff[q], so);
+    };
+    auto gload_w = [&](int bank, int step) {
+      const uint32_t so = wk(kc0 + step);
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+        wr[bank][n] = buffer_load16(MODE == MODE_GATEUP && n >= 4 ? wrb : wra, woff[n], so);
+    };
+    auto lstore = [&](int bank, int buf) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        *reinterpret_cast<u32x4*>(xsm + buf * kWStage + ((wave + 4 * q) * 64 + lane) * 16) = xr[bank][q];
+    };
+
+    f32x4 acc[MV][8];
+#pragma unroll
+    for (int m = 0; m < MV; ++m)
+#pragma unroll
+      for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0, 0, 0, 0};
+
+    // Per step st: the activations of step st + 2 and the weights of step
+    // st + kWBanks - 1 are issued into the banks steps st and st - 1 freed;
+    // the MFMAs of step st run on weight bank st % kWBanks and LDS buffer
+    // st % 2; step st + 1's activations go to the other buffer (last read
+    // before the previous barrier); barrier.  Steps past the end re-load the
+    // last step (clamped) instead of branching around loads.
+    const int slast = nsteps - 1;
+#pragma unroll
+    for (int p = 0; p < kWBanks - 1; ++p) {
+      if (p < 2) gload_x(p, min(p, slast));
+      gload_w(p, min(p, slast));
+    }
+    lstore(0, 0);
+    __syncthreads();
+    for (int sb = 0; sb < nsteps; sb += kWBanks) {   // kWBanks is even: st % 2 == u % 2
+#pragma unroll
+      for (int u = 0; u < kWBanks; ++u) {
+        const int st = sb + u;
+        if (st < nsteps) {
+          gload_x(u & 1, min(st + 2, slast));
+          gload_w((u + kWBanks - 1) % kWBanks, min(st + kWBanks - 1, slast));
+          // (scheduling fences keep each step's loads, reads and MFMAs in their
+          // step: hoisted across steps they outgrow the register file)
+          __builtin_amdgcn_sched_barrier(0);
+          const char* xb = xsm + (u & 1) * kWStage;
+          bf16x8 xf[MV];
+#pragma unroll
+          for (int m = 0; m < MV; ++m) xf[m] = *reinterpret_cast<const bf16x8*>(xb + (m * 64 + lane) * 16);
+#pragma unroll
+          for (int m = 0; m < MV; ++m)
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+              acc[m][n] = mfma16x16x32(__builtin_bit_cast(bf16x8, wr[u][n]), xf[m], acc[m][n]);
+          // order: the reads of tiles 0 and 1, then per tile m its 8 MFMAs
+          // followed by the read of tile m + 2, so each read has a tile's
+          // MFMAs (8 x 16 cycles) to land
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+          for (int m = 0; m < MV; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            if (m + 2 < MV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          lstore((u + 1) & 1, (u + 1) & 1);
+          __syncthreads();
+        }
+      }
+    }
+
+    // ---- epilogue: acc[m][n] holds D[w-row 4*(lane/16)+j of tile n][token lane%16 of tile m]
+    const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+      const int gr = m0 + m * 16 + lr;
+      if (gr >= R) continue;
+      const int64_t row = gr < c0 ? s0 + gr : s1 + (gr - c0);
+      if (MODE == MODE_GATEUP) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const f32x4 gt = acc[m][n], up = acc[m][n + 4];
+          const int ncol = n0 + 64 * wave + 16 * n + 4 * lg;
+          u32x2 o = {pack_bf16x2(silu_t(gt.x) * up.x, silu_t(gt.y) * up.y),
+                     pack_bf16x2(silu_t(gt.z) * up.z, silu_t(gt.w) * up.w)};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          const int ncol = n0 + 128 * wave + 16 * n + 4 * lg;
+          if (a.out_f32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ks * a.split_stride + row * a.ldo + ncol) = acc[m][n];
+          } else {
+            u32x2 o = {pack_bf16x2(acc[m][n].x, acc[m][n].y), pack_bf16x2(acc[m][n].z, acc[m][n].w)};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
+          }
+        }
+      }
+    }
+  };
+  switch (mv) {
+    case 2: run(IntC<2>{}); break;
+    case 4: run(IntC<4>{}); break;
+    case 6: run(IntC<6>{}); break;
+    default: run(IntC<8>{}); break;
+  }
+}
+
 bool tiled_supported(int mode, int fp8, int N, int Kdim, int ksplit) {
   if (fp8) return false;
   if (mode == MODE_GATEUP) { if (N % 128) return false; }
@@ -287,14 +515,35 @@ bool tiled_supported(int mode, int fp8, int N, int Kdim, int ksplit) {
   return (Kdim / ksplit) % kTK == 0;
 }
 
+// The wide kernel addresses one weight matrix and the activation rows through
+// 32-bit buffer offsets: both must stay below 2 GiB.
+bool wide_supported(int mode, const TiledArgs& a) {
+  if (a.s.N % (mode == MODE_GATEUP ? kWN / 2 : kWN)) return false;
+  if ((a.s.Kdim / a.s.ksplit) % (32 * kWBanks)) return false;   // whole passes of kWBanks steps
+  return (int64_t)a.s.N * a.s.Kdim * 2 < (int64_t(1) << 31) && a.x_bytes > 0 &&
+         a.x_bytes < (int64_t(1) << 31);
+}
+
 hipError_t launch_ffn_tiled(const TiledArgs& a, int fp8, int packed, int mode, int max_tiles, hipStream_t s) {
   if (!tiled_supported(mode, fp8, a.s.N, a.s.Kdim, a.s.ksplit)) return hipErrorInvalidValue;
   if (max_tiles <= 0) return hipSuccess;
+  // MOE_TILED_WIDE=0 selects the narrow kernel where the wide one applies
+  const char* env = getenv("MOE_TILED_WIDE");
+  const bool wide = wide_supported(mode, a) && !(env && env[0] == '0');
   // grid.y covers the static bound on row tiles (the live count is read on the
   // device) plus 8, so that the XCD remap's largest linear id, which can pass
   // the live work count by up to 7, always has a workgroup
-  const dim3 grid(mode == MODE_GATEUP ? a.s.N / 128 : a.s.N / kTN, max_tiles + 8, a.s.ksplit);
-  if (mode == MODE_GATEUP) {
+  const int wn = wide ? (mode == MODE_GATEUP ? kWN / 2 : kWN) : (mode == MODE_GATEUP ? 128 : kTN);
+  const dim3 grid(a.s.N / wn, max_tiles + 8, a.s.ksplit);
+  if (wide) {
+    if (mode == MODE_GATEUP) {
+      if (packed) hipLaunchKernelGGL((ffn_wide_kernel<MODE_GATEUP, true>), grid, dim3(kTThreads), 0, s, a);
+      else hipLaunchKernelGGL((ffn_wide_kernel<MODE_GATEUP, false>), grid, dim3(kTThreads), 0, s, a);
+    } else {
+      if (packed) hipLaunchKernelGGL((ffn_wide_kernel<MODE_DOWN, true>), grid, dim3(kTThreads), 0, s, a);
+      else hipLaunchKernelGGL((ffn_wide_kernel<MODE_DOWN, false>), grid, dim3(kTThreads), 0, s, a);
+    }
+  } else if (mode == MODE_GATEUP) {
     if (packed) hipLaunchKernelGGL((ffn_tiled_kernel<MODE_GATEUP, true>), grid, dim3(kTThreads), 0, s, a);
     else hipLaunchKernelGGL((ffn_tiled_kernel<MODE_GATEUP, false>), grid, dim3(kTThreads), 0, s, a);
   } else {

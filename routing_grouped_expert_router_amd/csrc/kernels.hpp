@@ -99,6 +99,7 @@ struct TiledArgs {
   StreamArgs s;
   const int32_t* tile_off;   // [E_phys + 2] prefix of ceil(rows / 128) per group
   int min_rows;              // groups with at most this many rows are skipped
+  int64_t x_bytes;           // bytes of the activation rows X addresses (rows * ldx * 2)
 };
 bool tiled_supported(int mode, int fp8, int N, int Kdim, int ksplit);
 hipError_t launch_ffn_tiled(const TiledArgs& a, int fp8, int packed, int mode, int max_tiles,

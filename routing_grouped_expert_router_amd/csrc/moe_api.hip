@@ -301,6 +301,8 @@ moe_status_t launch_expert_gemm(const moe_desc_t* d, const moe_route_t* r, int32
   ta.s = a;
   ta.tile_off = r->tile_off;
   ta.min_rows = (mt < 4) ? 64 : a_max;
+  // X holds the layer input (T rows) when gathering, else the grouped buffer
+  ta.x_bytes = (a.gather_src ? (int64_t)T : moe_buffer_rows(d)) * a.ldx * 2;
   const int64_t TK = (int64_t)T * d->K;
   const int64_t max_tiles = (TK + kTileRows - 1) / kTileRows + d->E_phys +
                             (d->n_shared ? (T + kTileRows - 1) / kTileRows : 0);

@@ -55,6 +55,10 @@ def small_configs():
         # tiles (the large-group class) and a shared expert split over chunks
         base.with_(name="fp8_skewed_classes", T=100, H=512, I=256, E=32, E_phys=32, K=2, n_shared=1,
                    act_dtype="bf16", w_dtype="fp8", M_max=64, bias="zipf1.1"),
+        # groups of ~300 rows with shapes the wide tiled kernel takes for both
+        # projections (gate/up and down), masked with spill, shared expert
+        base.with_(name="tiled_wide", T=600, H=512, I=512, E=4, E_phys=4, K=2, n_shared=1,
+                   act_dtype="bf16", M_max=200),
     ]
 
 
@@ -311,6 +315,26 @@ def test_block_walk_gives_identical_outputs(nblk, monkeypatch):
             finally:
                 monkeypatch.delenv("MOE_STREAM_NBLK")
             assert torch.equal(ref, out), (cfg.name, packed, nblk)
+
+
+@pytest.mark.parametrize("name", ["tiled_masked_spill", "tiled_contig_shared", "tiled_wide"])
+def test_wide_tiled_kernel_matches_narrow(name, monkeypatch):
+    """The wide tiled kernel (128 weight rows per wave) and the narrow one
+    (64) reduce every output over the same 32-wide K steps in the same order
+    with the same MFMA: bit-identical outputs (MOE_TILED_WIDE=0 forces the
+    narrow kernel), row-major and packed weights, gathered or permuted rows."""
+    cfg = next(c for c in SMALL if c.name == name)
+    for packed in (False, True):
+        b = Built(cfg, packed=packed)
+        lg = b.oracle_logits()
+        for fused in (True, False):
+            ref = b.run(lg, fused_gather=fused).clone()
+            monkeypatch.setenv("MOE_TILED_WIDE", "0")
+            try:
+                out = b.run(lg, fused_gather=fused).clone()
+            finally:
+                monkeypatch.delenv("MOE_TILED_WIDE")
+            assert torch.equal(ref, out), (name, packed, fused)
 
 
 def test_pack_layout_matches_definition():
