@@ -26,11 +26,13 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 }
 
 // fp32 -> bf16, round to nearest even; NaN stays NaN (quiet).
+// (a select, not a branch: in unrolled epilogues a branch per element splits
+// the code into blocks that the register allocator handles badly)
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t rne = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t qnan = (u >> 16) | 0x40u;
+  return uint16_t((u & 0x7fffffffu) > 0x7f800000u ? qnan : rne);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {

@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kTThreads) void ffn_tiled_kernel(TiledArgs ta) {
 // loads of weights and activations run kWBanks - 1 steps ahead through
 // kWBanks register banks.
 constexpr int kWN = 512;                 // weight rows per tile
-constexpr int kWBanks = 4;
+constexpr int kWBanks = 3;
 constexpr int kWStage = kTM * 32 * 2;    // 8 KiB: 128 rows x 32 K
 
 // Raw buffer resource over [p, p + bytes): loads take a 32-bit per-lane
@@ -325,7 +325,10 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
-template <int MODE, bool PACKED>
+// OUTF32 (down projection only): fp32 partial planes of a K split, else bf16
+// (a template argument: with both epilogues in one kernel the accumulators
+// are copied out and spilled ahead of the branch)
+template <int MODE, bool PACKED, bool OUTF32>
 __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void ffn_wide_kernel(TiledArgs ta) {
   const StreamArgs& a = ta.s;
@@ -392,9 +395,8 @@ void ffn_wide_kernel(TiledArgs ta) {
   const int mv = ((rows_here + 31) / 32) * 2;
   auto run = [&](auto mvc) {
     constexpr int MV = decltype(mvc)::value;    // non-empty 16-row tiles (even)
-    // weights run kWBanks - 1 steps ahead; activations, which the workgroups
-    // of a weight tile share through L2, two steps ahead (bank = step % 2)
-    u32x4 xr[2][2], wr[kWBanks][8];
+    // weights and activations run kWBanks - 1 steps ahead (bank = step % kWBanks)
+    u32x4 xr[kWBanks][2], wr[kWBanks][8];
     // (every wave stages both of its tiles, also the empty ones past MV, which
     // read a valid row: loads that depend on the wave would be branches, and
     // the compiler then waits for every outstanding load once per pass)
@@ -421,31 +423,31 @@ void ffn_wide_kernel(TiledArgs ta) {
 #pragma unroll
       for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0, 0, 0, 0};
 
-    // Per step st: the activations of step st + 2 and the weights of step
-    // st + kWBanks - 1 are issued into the banks steps st and st - 1 freed;
-    // the MFMAs of step st run on weight bank st % kWBanks and LDS buffer
-    // st % 2; step st + 1's activations go to the other buffer (last read
-    // before the previous barrier); barrier.  Steps past the end re-load the
-    // last step (clamped) instead of branching around loads.
+    // Per step st: the activations and weights of step st + kWBanks - 1 are
+    // issued into the bank step st - 1 freed; the MFMAs of step st run on
+    // bank st % kWBanks and LDS buffer st % 2; step st + 1's activations go to
+    // the other buffer (last read before the previous barrier); barrier.
+    // Steps past the end re-load the last step (clamped) instead of branching
+    // around loads.
     const int slast = nsteps - 1;
 #pragma unroll
     for (int p = 0; p < kWBanks - 1; ++p) {
-      if (p < 2) gload_x(p, min(p, slast));
+      gload_x(p, min(p, slast));
       gload_w(p, min(p, slast));
     }
     lstore(0, 0);
     __syncthreads();
-    for (int sb = 0; sb < nsteps; sb += kWBanks) {   // kWBanks is even: st % 2 == u % 2
+    for (int sb = 0; sb < nsteps; sb += kWBanks) {
 #pragma unroll
       for (int u = 0; u < kWBanks; ++u) {
         const int st = sb + u;
         if (st < nsteps) {
-          gload_x(u & 1, min(st + 2, slast));
+          gload_x((u + kWBanks - 1) % kWBanks, min(st + kWBanks - 1, slast));
           gload_w((u + kWBanks - 1) % kWBanks, min(st + kWBanks - 1, slast));
           // (scheduling fences keep each step's loads, reads and MFMAs in their
           // step: hoisted across steps they outgrow the register file)
           __builtin_amdgcn_sched_barrier(0);
-          const char* xb = xsm + (u & 1) * kWStage;
+          const char* xb = xsm + (st & 1) * kWStage;
           bf16x8 xf[MV];
 #pragma unroll
           for (int m = 0; m < MV; ++m) xf[m] = *reinterpret_cast<const bf16x8*>(xb + (m * 64 + lane) * 16);
@@ -464,7 +466,7 @@ void ffn_wide_kernel(TiledArgs ta) {
             if (m + 2 < MV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
-          lstore((u + 1) & 1, (u + 1) & 1);
+          lstore((u + 1) % kWBanks, (st + 1) & 1);
           __syncthreads();
         }
       }
@@ -490,7 +492,7 @@ void ffn_wide_kernel(TiledArgs ta) {
 #pragma unroll
         for (int n = 0; n < 8; ++n) {
           const int ncol = n0 + 128 * wave + 16 * n + 4 * lg;
-          if (a.out_f32) {
+          if constexpr (OUTF32) {
             *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ks * a.split_stride + row * a.ldo + ncol) = acc[m][n];
           } else {
             u32x2 o = {pack_bf16x2(acc[m][n].x, acc[m][n].y), pack_bf16x2(acc[m][n].z, acc[m][n].w)};
@@ -537,11 +539,14 @@ hipError_t launch_ffn_tiled(const TiledArgs& a, int fp8, int packed, int mode, i
   const dim3 grid(a.s.N / wn, max_tiles + 8, a.s.ksplit);
   if (wide) {
     if (mode == MODE_GATEUP) {
-      if (packed) hipLaunchKernelGGL((ffn_wide_kernel<MODE_GATEUP, true>), grid, dim3(kTThreads), 0, s, a);
-      else hipLaunchKernelGGL((ffn_wide_kernel<MODE_GATEUP, false>), grid, dim3(kTThreads), 0, s, a);
+      if (packed) hipLaunchKernelGGL((ffn_wide_kernel<MODE_GATEUP, true, false>), grid, dim3(kTThreads), 0, s, a);
+      else hipLaunchKernelGGL((ffn_wide_kernel<MODE_GATEUP, false, false>), grid, dim3(kTThreads), 0, s, a);
+    } else if (a.s.out_f32) {
+      if (packed) hipLaunchKernelGGL((ffn_wide_kernel<MODE_DOWN, true, true>), grid, dim3(kTThreads), 0, s, a);
+      else hipLaunchKernelGGL((ffn_wide_kernel<MODE_DOWN, false, true>), grid, dim3(kTThreads), 0, s, a);
     } else {
-      if (packed) hipLaunchKernelGGL((ffn_wide_kernel<MODE_DOWN, true>), grid, dim3(kTThreads), 0, s, a);
-      else hipLaunchKernelGGL((ffn_wide_kernel<MODE_DOWN, false>), grid, dim3(kTThreads), 0, s, a);
+      if (packed) hipLaunchKernelGGL((ffn_wide_kernel<MODE_DOWN, true, false>), grid, dim3(kTThreads), 0, s, a);
+      else hipLaunchKernelGGL((ffn_wide_kernel<MODE_DOWN, false, false>), grid, dim3(kTThreads), 0, s, a);
     }
   } else if (mode == MODE_GATEUP) {
     if (packed) hipLaunchKernelGGL((ffn_tiled_kernel<MODE_GATEUP, true>), grid, dim3(kTThreads), 0, s, a);
