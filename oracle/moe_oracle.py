@@ -54,6 +54,27 @@ design notes with its reason):
      the lower expert id), in descending key order.
   R15 the weights are the chosen unbiased scores, divided by their sum when
      renormalising, times a scale factor (the routed scaling factor).
+  R16 expert-parallel share of one GPU ([vllbc] EP section: expert_map, -1 =
+     "not this rank's", zero local contribution, not a drop): a local map
+     over the global physical slots gives each slot's local slot or -1; a
+     choice whose slot is remote gets no row (row_of = slot_of = -1) and adds
+     nothing to this GPU's output.  Replicas (R7) are taken over the global
+     slots first.  An invalid local map (an entry outside [-1, E_phys) or a
+     local slot listed twice) leaves no choice local and sets status bit 3.
+  R17 EPLB replication ([eplb] section 1.3; [infra5] EPLB): each redundant
+     slot goes, one at a time, to the logical expert with the largest load
+     per replica (ties to the lower id).
+  R18 EPLB packing ([infra5] EPLB: longest-processing-time bin packing): the
+     replicas, each carrying load / replicas of its expert, are placed in
+     descending load (ties: lower expert, then replica order) on the rank
+     with the least load among those with a free slot and no replica of the
+     same expert yet (if every rank with a free slot holds one, any rank with
+     a free slot); ties to the lower rank.  Rank r owns global slots
+     [r*S, (r+1)*S), S = (E + redundant) / ranks, filled in placement order.
+  R19 received counts ([infra5] DeepGEMM section: the dispatch's received
+     count per local expert is masked_m): rows of local slot p sit at
+     p*M_max + i, i < count; counts above M_max are an error (status bit 0),
+     the excess rows are not computed.
 
 Parity pins: see tests/test_oracle_pins.py (brute force, a third-party
 Mixtral MoE block, textbook sorts, page worked examples, closed forms).
@@ -65,6 +86,7 @@ import numpy as np
 STATUS_SPILL = 1        # bit 0: masked overflow went to the spill region
 STATUS_BAD_REPLICA = 2  # bit 1: replica map entry invalid, home slot used
 STATUS_NONFINITE = 4    # bit 2: a logit was NaN or infinite
+STATUS_BAD_EP_MAP = 8   # bit 3: local map invalid, no choice is local
 
 
 # --------------------------------------------------------------------------
@@ -237,6 +259,7 @@ def replica_map_valid(l2p: np.ndarray, count: np.ndarray, E_phys: int) -> bool:
 
 def assign_physical(ids: np.ndarray, E_phys: int, l2p: np.ndarray | None = None,
                     count: np.ndarray | None = None):
+    # (E_phys: the slots the map may name -- the global slots under R16)
     """Physical slot of every (token, k) choice.  Without a map the slot is
     the logical id.  With a map (R7): the tokens that chose logical expert l,
     taken in ascending token order, are numbered j = 0, 1, ...; choice j goes
@@ -259,6 +282,95 @@ def assign_physical(ids: np.ndarray, E_phys: int, l2p: np.ndarray | None = None,
 
 
 # --------------------------------------------------------------------------
+# Expert-parallel share of one GPU and the EPLB plan  (R16 - R18)
+# --------------------------------------------------------------------------
+
+def ep_local_map(n_global: int, ep_size: int, rank: int, layout: str = "linear") -> np.ndarray:
+    """[vllbc] EP section: the expert map of one rank over n_global slots --
+    local slots numbered 0.. in slot order, -1 elsewhere.  "linear" cuts
+    contiguous runs and the first n_global % ep_size ranks take one extra;
+    "round_robin" deals slot p to rank p % ep_size."""
+    local = np.full(n_global, -1, dtype=np.int32)
+    if layout == "linear":
+        base, rem = divmod(n_global, ep_size)
+        start = rank * base + min(rank, rem)
+        n = base + (1 if rank < rem else 0)
+        local[start:start + n] = np.arange(n, dtype=np.int32)
+    elif layout == "round_robin":
+        mine = np.arange(rank, n_global, ep_size)
+        local[mine] = np.arange(len(mine), dtype=np.int32)
+    else:
+        raise ValueError(layout)
+    return local
+
+
+def ep_map_valid(local_of: np.ndarray, E_phys: int) -> bool:
+    """R16: entries in [-1, E_phys), no local slot named twice."""
+    v = np.asarray(local_of, dtype=np.int64)
+    if ((v < -1) | (v >= E_phys)).any():
+        return False
+    used = v[v >= 0]
+    return len(np.unique(used)) == len(used)
+
+
+def localize(phys_global: np.ndarray, local_of: np.ndarray, E_phys: int):
+    """R16: each choice's local slot (-1 = another rank's)."""
+    if not ep_map_valid(local_of, E_phys):
+        return np.full_like(phys_global, -1, dtype=np.int32), STATUS_BAD_EP_MAP
+    return np.asarray(local_of, dtype=np.int32)[phys_global], 0
+
+
+def eplb_replicas(load: np.ndarray, n_redundant: int) -> np.ndarray:
+    """R17: replica count per logical expert after handing out the redundant
+    slots one at a time to the largest load per replica."""
+    load = np.asarray(load, dtype=np.float64)
+    rep = np.ones(len(load), dtype=np.int64)
+    for _ in range(n_redundant):
+        per = load / rep
+        rep[int(np.argmax(per))] += 1        # argmax: first (lowest id) of the ties
+    return rep
+
+
+def eplb_plan(load: np.ndarray, n_redundant: int, ep_size: int) -> np.ndarray:
+    """R17 + R18: physical_to_logical map over E + n_redundant global slots,
+    rank r owning slots [r*S, (r+1)*S)."""
+    load = np.asarray(load, dtype=np.float64)
+    E = len(load)
+    n = E + n_redundant
+    if n % ep_size:
+        raise ValueError("E + redundant must divide by the number of ranks")
+    S = n // ep_size
+    rep = eplb_replicas(load, n_redundant)
+    items = [(load[l] / rep[l], l, j) for l in range(E) for j in range(rep[l])]
+    items.sort(key=lambda it: (-it[0], it[1], it[2]))
+    slots = [[] for _ in range(ep_size)]
+    total = [0.0] * ep_size
+    for wgt, l, _ in items:
+        free = [r for r in range(ep_size) if len(slots[r]) < S]
+        fresh = [r for r in free if l not in slots[r]]
+        pool = fresh if fresh else free
+        r = min(pool, key=lambda q: (total[q], q))
+        slots[r].append(l)
+        total[r] += wgt
+    return np.array([l for r in range(ep_size) for l in slots[r]], dtype=np.int32)
+
+
+def received_tables(counts: np.ndarray, M_max: int, tile_rows: int = 128):
+    """R19: the masked tables of a buffer a dispatch filled -- masked_m =
+    counts (an error above M_max), offsets = exclusive prefix of masked_m,
+    no spill, and the prefix of ceil(rows / tile_rows) tiles."""
+    counts = np.asarray(counts, dtype=np.int64)
+    status = STATUS_SPILL if (counts > M_max).any() else 0
+    mm = np.minimum(counts, M_max)
+    offsets = np.zeros(len(mm) + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(mm)
+    tiles = np.zeros(len(mm) + 1, dtype=np.int64)
+    tiles[1:] = np.cumsum((mm + tile_rows - 1) // tile_rows)
+    return dict(masked_m=mm.astype(np.int32), offsets=offsets.astype(np.int32),
+                tile_off=tiles.astype(np.int32), status=status)
+
+
+# --------------------------------------------------------------------------
 # Counts, offsets and the expert-grouped order
 # --------------------------------------------------------------------------
 
@@ -267,16 +379,20 @@ def group_rows(phys: np.ndarray, E_phys: int):
     (E_phys + 1 entries, the cu_seqlens of [moonep] online plan);
     src_of[row] = token of each row of the expert-grouped order, a stable sort
     by slot (R3); row_of[t, k] = the row of choice (t, k).  [vllbc] vLLM
-    forward path: sort token/expert pairs by expert."""
+    forward path: sort token/expert pairs by expert.  Remote choices
+    (phys = -1, R16) have no row: row_of = -1, and src_of holds the local
+    rows only."""
     T, K = phys.shape
     flat = phys.reshape(-1).astype(np.int64)
-    counts = np.bincount(flat, minlength=E_phys).astype(np.int32)
+    local = flat >= 0
+    counts = np.bincount(flat[local], minlength=E_phys).astype(np.int32)
     offsets = np.zeros(E_phys + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(counts)
-    order = np.argsort(flat, kind="stable")
+    idx = np.nonzero(local)[0]
+    order = idx[np.argsort(flat[idx], kind="stable")]
     src_of = (order // K).astype(np.int32)
-    row_of = np.empty(T * K, dtype=np.int32)
-    row_of[order] = np.arange(T * K, dtype=np.int32)
+    row_of = np.full(T * K, -1, dtype=np.int32)
+    row_of[order] = np.arange(len(order), dtype=np.int32)
     return counts, offsets.astype(np.int32), row_of.reshape(T, K), src_of
 
 
@@ -290,9 +406,11 @@ def layout_masked(counts, offsets, row_of, phys, M_max: int, E_phys: int):
     spill_m = counts - masked_m
     spill_off = np.zeros(E_phys + 1, dtype=np.int64)
     spill_off[1:] = np.cumsum(spill_m)
-    rank = row_of - offsets[phys]
-    slot = np.where(rank < M_max, phys.astype(np.int64) * M_max + rank,
-                    E_phys * M_max + spill_off[phys] + rank - M_max)
+    pl = np.maximum(phys, 0)                  # remote choices (R16): slot -1 below
+    rank = row_of - offsets[pl]
+    slot = np.where(rank < M_max, pl.astype(np.int64) * M_max + rank,
+                    E_phys * M_max + spill_off[pl] + rank - M_max)
+    slot = np.where(phys >= 0, slot, -1)
     status = STATUS_SPILL if spill_m.sum() > 0 else 0
     return (masked_m.astype(np.int32), spill_off.astype(np.int32),
             slot.astype(np.int32), status)
@@ -306,8 +424,9 @@ def layout_contig(counts, offsets, row_of, phys, BM: int):
     padded = (counts + BM - 1) // BM * BM
     pad_off = np.zeros(len(counts) + 1, dtype=np.int64)
     pad_off[1:] = np.cumsum(padded)
-    rank = row_of - offsets[phys]
-    slot = pad_off[phys] + rank
+    pl = np.maximum(phys, 0)
+    rank = row_of - offsets[pl]
+    slot = np.where(phys >= 0, pad_off[pl] + rank, -1)
     return pad_off.astype(np.int32), slot.astype(np.int32)
 
 
@@ -329,7 +448,7 @@ def swiglu_expert(X: np.ndarray, W1: np.ndarray, W3: np.ndarray, W2: np.ndarray)
 
 def moe_forward(x, w_router, bias, K, E_phys, expert_weights, shared_weights=None,
                 p2l=None, layout="contig", M_max=0, BM=16, logits=None,
-                tokens=None, grouped=None):
+                tokens=None, grouped=None, local_of=None):
     """The layer forward as defined: returns a dict with every intermediate.
 
     x [T, H] (values exactly as the layer receives them); w_router [E, H];
@@ -340,7 +459,10 @@ def moe_forward(x, w_router, bias, K, E_phys, expert_weights, shared_weights=Non
     token ids (routing still covers every token, as it must).  ``grouped``,
     a dict of grouped_topk_route's keyword arguments (n_group, topk_group,
     group_k, score_bias, renormalize, scale), selects the grouped sigmoid
-    router instead of the softmax top-K.
+    router instead of the softmax top-K.  ``local_of`` (R16), a local map
+    over the global physical slots (the p2l slots, or the logical ids without
+    one), makes this the output of one GPU's expert-parallel share: E_phys is
+    then the number of local slots.
 
     out[t] = S[t] + sum_k w[t, k] * Y[row_of[t, k]]   ([vllbc] combine:
     weight by g_i then sum the K results; R4 for S)."""
@@ -356,8 +478,12 @@ def moe_forward(x, w_router, bias, K, E_phys, expert_weights, shared_weights=Non
     l2p = count = None
     if p2l is not None:
         l2p, count = replica_tables(p2l, E)
-    phys, st = assign_physical(ids, E_phys, l2p, count)
+    n_slots = E_phys if local_of is None else len(local_of)
+    phys, st = assign_physical(ids, n_slots, l2p, count)
     status |= st
+    if local_of is not None:
+        phys, st = localize(phys, local_of, E_phys)
+        status |= st
     counts, offsets, row_of, src_of = group_rows(phys, E_phys)
     res = dict(logits=logits, ids=ids, w=w, phys=phys, counts=counts,
                offsets=offsets, row_of=row_of, src_of=src_of)
@@ -388,7 +514,8 @@ def moe_forward(x, w_router, bias, K, E_phys, expert_weights, shared_weights=Non
     if shared_weights is not None:
         out += swiglu_expert(x[want], *shared_weights)
     for k in range(K):
-        out += w[want, k][:, None] * Y[row_of[want, k]]
+        r = row_of[want, k]
+        out += np.where((r >= 0)[:, None], w[want, k][:, None] * Y[np.maximum(r, 0)], 0.0)
     res["out"] = out
     res["tokens"] = want
     return res

@@ -25,12 +25,24 @@ def expert_f64(ew, w_dtype: str):
             O.dequant_block128(ew.w2.numpy(), ew.s2.numpy()))
 
 
-def oracle_forward(inp, logits=None, tokens=None, layout=None, grouped=None):
-    """Runs the reference on workload inputs ``inp`` (workloads.generate)."""
+def oracle_forward(inp, logits=None, tokens=None, layout=None, grouped=None, local_of=None,
+                   E_local=None):
+    """Runs the reference on workload inputs ``inp`` (workloads.generate).
+    ``local_of`` (over the workload's physical slots) makes it one rank's
+    expert-parallel share with ``E_local`` local slots (default: the number
+    of local entries)."""
     cfg = inp.cfg
     cache = {}
+    E_phys = cfg.E_phys
+    glob = None
+    if local_of is not None:
+        local_of = np.asarray(local_of, dtype=np.int32)
+        E_phys = int((local_of >= 0).sum()) if E_local is None else E_local
+        glob = {int(q): p for p, q in enumerate(local_of) if q >= 0}
 
     def slot_weights(p):
+        if glob is not None:
+            p = glob[p]
         l = inp.slot_logical(p)
         if l not in cache:
             if len(cache) > 2:
@@ -42,6 +54,6 @@ def oracle_forward(inp, logits=None, tokens=None, layout=None, grouped=None):
     return O.moe_forward(
         to_f64(inp.x), to_f64(inp.w_router),
         None if inp.bias is None else inp.bias.numpy(),
-        cfg.K, cfg.E_phys, slot_weights, shared, p2l=inp.p2l,
+        cfg.K, E_phys, slot_weights, shared, p2l=inp.p2l,
         layout=layout or cfg.layout, M_max=cfg.M_max, BM=cfg.BM,
-        logits=logits, tokens=tokens, grouped=grouped)
+        logits=logits, tokens=tokens, grouped=grouped, local_of=local_of)

@@ -499,3 +499,135 @@ def test_grouped_router_keeps_only_the_best_groups():
         gs = [np.sort(key[t, g * 4:(g + 1) * 4])[::-1][:gk].sum() for g in range(G)]
         best = max(itertools.combinations(range(G), TG), key=lambda c: sum(gs[g] for g in c))
         assert {int(e) // 4 for e in ids[t]} <= set(best), t
+
+
+# ------------------------------------------------- expert parallelism (R16-R19)
+
+def test_ep_local_map_page_examples():
+    """[vllbc] EP section: 4 experts on 2 ranks -- linear gives rank 0 experts
+    0, 1 and rank 1 experts 2, 3; round_robin gives rank 0 experts 0, 2 and
+    rank 1 experts 1, 3; local ids count 0.. in expert order, -1 elsewhere.
+    Uneven splits give the first remainder ranks one extra expert."""
+    assert O.ep_local_map(4, 2, 0).tolist() == [0, 1, -1, -1]
+    assert O.ep_local_map(4, 2, 1).tolist() == [-1, -1, 0, 1]
+    assert O.ep_local_map(4, 2, 0, "round_robin").tolist() == [0, -1, 1, -1]
+    assert O.ep_local_map(4, 2, 1, "round_robin").tolist() == [-1, 0, -1, 1]
+    assert O.ep_local_map(5, 2, 0).tolist() == [0, 1, 2, -1, -1]
+    assert O.ep_local_map(5, 2, 1).tolist() == [-1, -1, -1, 0, 1]
+    assert O.ep_local_map(7, 3, 2).tolist() == [-1, -1, -1, -1, -1, 0, 1]
+
+
+@pytest.mark.parametrize("layout", ["linear", "round_robin"])
+def test_ep_local_maps_partition_the_slots(layout):
+    for n, ep in [(8, 2), (9, 4), (256, 8), (5, 5), (3, 4)]:
+        maps = np.stack([O.ep_local_map(n, ep, r, layout) for r in range(ep)])
+        assert ((maps >= 0).sum(0) == 1).all()           # each slot on exactly one rank
+        for m in maps:                                    # local ids 0..n_r-1 in slot order
+            loc = m[m >= 0]
+            assert loc.tolist() == list(range(len(loc)))
+
+
+@pytest.mark.parametrize("layout", ["linear", "round_robin"])
+@pytest.mark.parametrize("replicas", [False, True])
+def test_ep_shares_sum_to_the_full_layer(layout, replicas):
+    """R16: a remote choice contributes zero locally and is computed by the
+    rank that owns its slot, so the ranks' outputs sum to the full layer's,
+    and each rank's rows are exactly its local choices."""
+    cfg = configs.tiny().with_(E=6, E_phys=9 if replicas else 6, K=2, T=24, layout="contig", BM=4)
+    inp = generate.make_inputs(cfg)
+    if replicas:
+        inp.p2l = np.array([0, 1, 2, 3, 4, 5, 2, 2, 0], np.int32)
+    full = oracle_forward(inp)
+    ep = 3
+    total = np.zeros_like(full["out"])
+    rows = 0
+    for r in range(ep):
+        loc = O.ep_local_map(cfg.E_phys, ep, r, layout)
+        res = oracle_forward(inp, local_of=loc)
+        assert res["status"] == 0
+        total += res["out"]
+        local = loc[full["phys"]] >= 0
+        assert ((res["row_of"] >= 0) == local).all()
+        assert (res["slot_of"][~local] == -1).all()
+        assert res["counts"].sum() == local.sum() == res["offsets"][-1]
+        rows += res["counts"].sum()
+    assert rows == cfg.T * cfg.K
+    assert np.allclose(total, full["out"], rtol=1e-12, atol=1e-14)
+
+
+def test_ep_rank_without_experts_and_invalid_map():
+    cfg = configs.tiny().with_(E=4, E_phys=4, K=2, T=8)
+    inp = generate.make_inputs(cfg)
+    none = np.full(4, -1, np.int32)
+    res = oracle_forward(inp, local_of=none, E_local=2)
+    assert res["counts"].sum() == 0 and (res["row_of"] == -1).all()
+    assert np.array_equal(res["out"], np.zeros_like(res["out"]))
+    bad = np.array([0, 0, -1, 1], np.int32)                # local slot 0 named twice
+    res = oracle_forward(inp, local_of=bad, E_local=2)
+    assert res["status"] & O.STATUS_BAD_EP_MAP and res["counts"].sum() == 0
+
+
+def test_eplb_replicas_minimise_the_largest_load_per_replica():
+    """R17 against brute force: handing redundant slots one at a time to the
+    largest load per replica reaches the least possible largest load per
+    replica, on every small instance."""
+    rng = np.random.default_rng(0)
+    for _ in range(150):
+        E, nr = int(rng.integers(2, 6)), int(rng.integers(0, 5))
+        load = rng.integers(1, 50, size=E).astype(np.float64)
+        rep = O.eplb_replicas(load, nr)
+        assert rep.sum() == E + nr and (rep >= 1).all()
+        best = min(max(load / np.array(r)) for r in itertools.product(range(1, nr + 2), repeat=E)
+                   if sum(r) == E + nr)
+        assert max(load / rep) == best
+
+
+def test_eplb_plan_worked_examples():
+    """[eplb] section 1.3: four experts, two redundant slots; with E0 and E2
+    hot the redundant slots hold E0 and E2.  Worked by hand: replicas
+    E0 x2, E2 x2 at 15 each, E1, E3 at 5; LPT puts the two copies of an
+    expert on different ranks and balances 35 / 35."""
+    p2l = O.eplb_plan(np.array([30.0, 5.0, 30.0, 5.0]), 2, 2)
+    assert p2l.tolist() == [0, 2, 1, 0, 2, 3]
+    # no redundancy: 8, 4, 2, 2 on two ranks of two slots -> {8, 2}, {4, 2}
+    assert O.eplb_plan(np.array([8.0, 4.0, 2.0, 2.0]), 0, 2).tolist() == [0, 3, 1, 2]
+    # every rank holds S slots and every expert at least one replica
+    rng = np.random.default_rng(1)
+    for _ in range(50):
+        ep = int(rng.integers(1, 6)); S = int(rng.integers(1, 6))
+        E = int(rng.integers(max(1, ep * S - 4), ep * S + 1))
+        p2l = O.eplb_plan(rng.random(E) + 0.01, ep * S - E, ep)
+        assert len(p2l) == ep * S and set(p2l.tolist()) == set(range(E))
+
+
+def test_eplb_flattens_routing_hot_spots():
+    """[infra5] EPLB: replicating hot experts and LPT packing bring the
+    busiest rank's load back to about 1.1 x the mean under routing hot
+    spots.  Zipf(1.1) loads over 256 experts, 32 redundant slots: linear
+    placement without replicas is far above that, the plan within it."""
+    E = 256
+    ranks = np.random.default_rng(2).permutation(E) + 1
+    load = ranks ** -1.1
+    for ep in (8, 16, 32):
+        S = (E + 32) // ep
+        p2l = O.eplb_plan(load, 32, ep)
+        rep = np.bincount(p2l, minlength=E)
+        w = load[p2l] / rep[p2l]
+        per_rank = w.reshape(ep, S).sum(1)
+        assert per_rank.max() / per_rank.mean() <= 1.1
+        lin = load.reshape(ep, E // ep).sum(1)
+        assert lin.max() / lin.mean() > 1.5
+
+
+def test_received_tables_match_routed_masked_tables():
+    """R19 against the routing path: counts taken from a routed batch give
+    back its masked_m and the 128-row tile prefix (no spill)."""
+    inp = _tiny_inputs(T=40, M_max=40)
+    res = oracle_forward(inp, layout="masked")
+    rt = O.received_tables(res["counts"], inp.cfg.M_max)
+    assert np.array_equal(rt["masked_m"], res["masked_m"]) and rt["status"] == 0
+    assert np.array_equal(rt["offsets"], res["offsets"])
+    tiles = np.concatenate([[0], np.cumsum(-(-res["counts"] // 128))])
+    assert np.array_equal(rt["tile_off"], tiles)
+    over = O.received_tables(np.array([3, 50]), 40)
+    assert over["status"] & O.STATUS_SPILL and over["masked_m"].tolist() == [3, 40]
