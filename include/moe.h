@@ -78,6 +78,12 @@ typedef enum {
                                       below every number, output unspecified */
 #define MOE_STATUS_INTERNAL    8u  /* an index fell outside its buffer and the
                                       access was skipped (never expected) */
+#define MOE_STATUS_BAD_EP_MAP  16u /* moe_route_ep: local map invalid (an entry
+                                      outside [-1, E_phys) or a local slot
+                                      named twice): no choice is local */
+#define MOE_STATUS_RECV_OVERFLOW 32u /* moe_route_received: a count outside
+                                      [0, M_max]; only min(count, M_max) rows
+                                      of that slot are computed */
 
 /* Layer description (host struct, copied by value into every call). */
 typedef struct {
@@ -85,7 +91,9 @@ typedef struct {
   int32_t H;            /* hidden size; multiple of 128 */
   int32_t I;            /* expert intermediate size; multiple of 128 */
   int32_t E;            /* logical routed experts, 1..1024 */
-  int32_t E_phys;       /* physical slots (>= E; == E without replicas) */
+  int32_t E_phys;       /* physical slots (>= E; == E without replicas); for
+                           one rank's expert-parallel share (moe_route_ep) the
+                           local slots, >= 1 */
   int32_t K;            /* experts per token, 1..min(E, 16) */
   int32_t n_shared;     /* 0 or 1 always-on shared expert */
   int32_t max_replicas; /* columns of logical_to_physical_map (>= 1) */
@@ -215,6 +223,81 @@ moe_status_t moe_route_grouped(const moe_desc_t* d, const float* logits, int32_t
                                const int32_t* l2p, const int32_t* replica_count,
                                const moe_route_t* r, void* ws, size_t ws_bytes,
                                hipStream_t stream);
+
+/* ---- expert-parallel share of one GPU ------------------------------------
+ * (vllbc blog, EP section: an expert map gives each global expert its local
+ * slot on this rank, -1 for another rank's; -1 is not a drop: the choice adds
+ * nothing here and is computed by the rank that owns it.  "推理 INFRA 方法论(5)",
+ * DeepGEMM section: the dispatch's received count per local expert is the
+ * masked GEMM's masked_m.) */
+
+typedef struct {
+  const int32_t* local_of;   /* [n_global] device: global physical slot ->
+                                local slot in [0, E_phys), or -1 */
+  int32_t n_global;          /* global physical slots: the slots l2p names,
+                                or >= E without a replica map (slot = expert
+                                id); <= 4096 */
+} moe_ep_map_t;
+
+/* moe_route (g == NULL) or moe_route_grouped (g != NULL) for one rank's share.
+ * Top-K over all E experts as usual; each choice takes its global slot
+ * (through the replica map if given, whose entries are global slots in
+ * [0, n_global)), then its local slot local_of[global].  A choice with local
+ * slot -1 gets topk_phys = row_of = slot_of = -1 (moe_permute and
+ * moe_combine skip it); counts, offsets and the layout tables cover the local
+ * slots only, so offsets[E_phys] <= T*K.  topk_ids and topk_w are those of
+ * the full routing.  An invalid local map (an entry outside [-1, E_phys) or a
+ * local slot named twice) leaves no choice local and sets
+ * MOE_STATUS_BAD_EP_MAP.  Other conventions and errors as moe_route; also
+ * MOE_ERR_ARG for a NULL ep or local_of, or n_global outside the range above. */
+moe_status_t moe_route_ep(const moe_desc_t* d, const float* logits, int32_t T,
+                          const moe_grouped_router_t* g, const moe_ep_map_t* ep,
+                          const int32_t* l2p, const int32_t* replica_count,
+                          const moe_route_t* r, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Route tables for a masked buffer that a dispatch has filled: rows of local
+ * slot p at p*M_max + i, i < counts[p] (counts: [E_phys] device int32, the
+ * received count per local expert).  Writes r->counts and r->masked_m
+ * (min(max(counts, 0), M_max)), r->offsets (their exclusive prefix), r->
+ * spill_off (zeros), r->tile_off (prefix of ceil(rows/128) tiles; the shared
+ * expert's ceil(T/128) last when d->n_shared) and r->status
+ * (MOE_STATUS_RECV_OVERFLOW if a count is outside [0, M_max]); the other
+ * tables are left as they are.  moe_expert_gate_up / moe_expert_down then run
+ * on the buffer as after moe_route + moe_permute (shared-expert rows, if any,
+ * at moe_buffer_rows' routed capacity + t for t < T).  Masked layout only
+ * (else MOE_ERR_UNSUPPORTED); one workgroup, enqueue-only, no host sync. */
+moe_status_t moe_route_received(const moe_desc_t* d, const int32_t* counts, int32_t T,
+                                const moe_route_t* r, hipStream_t stream);
+
+typedef enum {
+  MOE_EP_LINEAR = 0,         /* contiguous runs of slots per rank */
+  MOE_EP_ROUND_ROBIN = 1     /* slot p on rank p % ep_size */
+} moe_ep_layout_t;
+
+/* Host helper: rank's local map over n_global slots (vllbc blog, EP section:
+ * linear cuts contiguous runs and the first n_global % ep_size ranks take one
+ * extra slot; round-robin deals the slots out in turn).  Local slots are
+ * numbered 0.. in global slot order; local_of [n_global] (host) receives the
+ * map, n_local (may be NULL) the number of local slots.  MOE_ERR_ARG for
+ * n_global < 1, ep_size < 1, rank outside [0, ep_size) or an unknown layout. */
+moe_status_t moe_ep_local_map(int32_t n_global, int32_t ep_size, int32_t rank, int32_t layout,
+                              int32_t* local_of, int32_t* n_local);
+
+/* Host helper: EPLB placement (vLLM EPLB explainer, section 1.3: redundant
+ * slots replicate the hot experts; "推理 INFRA 方法论(5)", EPLB section:
+ * replicate hot experts, then longest-processing-time bin packing).  load [E]
+ * (host, finite, >= 0) is each logical expert's load.  Each of the n_redundant
+ * extra slots goes to the expert with the largest load per replica (lowest id
+ * on ties); then the replicas, each carrying load / replicas, are placed in
+ * descending order (lower expert, then replica order, on ties) on the least
+ * loaded rank that has a free slot, preferring ranks without a copy of that
+ * expert (lowest rank on ties).  p2l [E + n_redundant] (host) receives the
+ * physical_to_logical map with rank r owning slots [r*S, (r+1)*S), S =
+ * (E + n_redundant) / ep_size, in placement order.  MOE_ERR_ARG for bad sizes,
+ * E + n_redundant not divisible by ep_size or above 4096, or a bad load. */
+moe_status_t moe_eplb_plan(const double* load, int32_t E, int32_t n_redundant, int32_t ep_size,
+                           int32_t* p2l);
 
 /* a5. Gathers token rows into the grouped buffer: xg[slot_of[t*K+k]] = x[t]
  * (cast to bf16 if x is fp32) and, with a shared expert,

@@ -60,7 +60,7 @@ design notes with its reason):
      choice whose slot is remote gets no row (row_of = slot_of = -1) and adds
      nothing to this GPU's output.  Replicas (R7) are taken over the global
      slots first.  An invalid local map (an entry outside [-1, E_phys) or a
-     local slot listed twice) leaves no choice local and sets status bit 3.
+     local slot listed twice) leaves no choice local and sets status bit 4.
   R17 EPLB replication ([eplb] section 1.3; [infra5] EPLB): each redundant
      slot goes, one at a time, to the logical expert with the largest load
      per replica (ties to the lower id).
@@ -73,8 +73,8 @@ design notes with its reason):
      [r*S, (r+1)*S), S = (E + redundant) / ranks, filled in placement order.
   R19 received counts ([infra5] DeepGEMM section: the dispatch's received
      count per local expert is masked_m): rows of local slot p sit at
-     p*M_max + i, i < count; counts above M_max are an error (status bit 0),
-     the excess rows are not computed.
+     p*M_max + i, i < count; counts outside [0, M_max] are an error (status
+     bit 5) and only min(count, M_max) rows are computed.
 
 Parity pins: see tests/test_oracle_pins.py (brute force, a third-party
 Mixtral MoE block, textbook sorts, page worked examples, closed forms).
@@ -86,7 +86,9 @@ import numpy as np
 STATUS_SPILL = 1        # bit 0: masked overflow went to the spill region
 STATUS_BAD_REPLICA = 2  # bit 1: replica map entry invalid, home slot used
 STATUS_NONFINITE = 4    # bit 2: a logit was NaN or infinite
-STATUS_BAD_EP_MAP = 8   # bit 3: local map invalid, no choice is local
+STATUS_BAD_EP_MAP = 16  # bit 4: local map invalid, no choice is local (bit 3
+                        # is the library's internal-index bit)
+STATUS_RECV_OVERFLOW = 32  # bit 5: a received count above M_max
 
 
 # --------------------------------------------------------------------------
@@ -360,8 +362,8 @@ def received_tables(counts: np.ndarray, M_max: int, tile_rows: int = 128):
     counts (an error above M_max), offsets = exclusive prefix of masked_m,
     no spill, and the prefix of ceil(rows / tile_rows) tiles."""
     counts = np.asarray(counts, dtype=np.int64)
-    status = STATUS_SPILL if (counts > M_max).any() else 0
-    mm = np.minimum(counts, M_max)
+    status = STATUS_RECV_OVERFLOW if ((counts > M_max) | (counts < 0)).any() else 0
+    mm = np.clip(counts, 0, M_max)
     offsets = np.zeros(len(mm) + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(mm)
     tiles = np.zeros(len(mm) + 1, dtype=np.int64)

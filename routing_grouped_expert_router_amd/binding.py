@@ -20,6 +20,8 @@ MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range
 MOE_F32, MOE_BF16, MOE_FP8E4M3_B128 = 0, 1, 2
 MOE_CONTIG, MOE_MASKED = 0, 1
 MOE_STATUS_SPILL, MOE_STATUS_BAD_REPLICA, MOE_STATUS_NONFINITE, MOE_STATUS_INTERNAL = 1, 2, 4, 8
+MOE_STATUS_BAD_EP_MAP, MOE_STATUS_RECV_OVERFLOW = 16, 32
+MOE_EP_LINEAR, MOE_EP_ROUND_ROBIN = 0, 1
 
 EXPORTED = [
     "moe_status_string", "moe_check_desc", "moe_route_workspace_bytes", "moe_buffer_rows",
@@ -27,7 +29,8 @@ EXPORTED = [
     "moe_route_grouped",
     "moe_permute", "moe_expert_gate_up", "moe_expert_gate_up_x", "moe_expert_down",
     "moe_grouped_ffn", "moe_grouped_ffn_x", "moe_combine", "moe_forward", "moe_pack_weights",
-    "moe_replica_map_from_p2l",
+    "moe_replica_map_from_p2l", "moe_route_ep", "moe_route_received", "moe_ep_local_map",
+    "moe_eplb_plan",
 ]
 
 
@@ -44,6 +47,10 @@ class moe_route_t(ctypes.Structure):
     _fields_ = [(n, _P) for n in (
         "topk_ids", "topk_w", "topk_phys", "row_of", "slot_of", "src_of", "counts",
         "offsets", "masked_m", "spill_off", "pad_off", "tile_off", "status")]
+
+
+class moe_ep_map_t(ctypes.Structure):
+    _fields_ = [("local_of", _P), ("n_global", ctypes.c_int32)]
 
 
 class moe_grouped_router_t(ctypes.Structure):
@@ -94,6 +101,11 @@ def lib() -> ctypes.CDLL:
                                            _P, _P, _P, _P, _P]),
             "moe_pack_weights": (ctypes.c_int, [D, i32, i32, _P, _P, _P]),
             "moe_replica_map_from_p2l": (ctypes.c_int, [_P, i32, i32, i32, _P, _P]),
+            "moe_route_ep": (ctypes.c_int, [D, _P, i32, _P, ctypes.POINTER(moe_ep_map_t), _P, _P, R,
+                                            _P, sz, _P]),
+            "moe_route_received": (ctypes.c_int, [D, _P, i32, R, _P]),
+            "moe_ep_local_map": (ctypes.c_int, [i32, i32, i32, i32, _P, _P]),
+            "moe_eplb_plan": (ctypes.c_int, [_P, i32, i32, i32, _P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -301,6 +313,47 @@ def pack_expert_weights(d: Desc, weights: dict) -> dict:
     return out
 
 
+class EPMap:
+    """One rank's local map (moe_ep_map_t): ``local_of`` a device int32
+    tensor over the n_global global physical slots."""
+
+    def __init__(self, local_of, n_global=None):
+        self.local_of = local_of
+        self.c = moe_ep_map_t(_ptr(local_of), int(local_of.numel() if n_global is None else n_global))
+
+
+def moe_route_ep(d: Desc, logits, T, rt: RouteTables, ws, ep: EPMap, router: "GroupedRouter | None" = None,
+                 l2p=None, replica_count=None, stream=None):
+    _check(lib().moe_route_ep(ctypes.byref(d.c()), _ptr(logits), T,
+                              None if router is None else ctypes.byref(router.c), ctypes.byref(ep.c),
+                              _ptr(l2p), _ptr(replica_count), ctypes.byref(rt.c), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(stream)), "moe_route_ep")
+
+
+def moe_route_received(d: Desc, counts, T, rt: RouteTables, stream=None):
+    _check(lib().moe_route_received(ctypes.byref(d.c()), _ptr(counts), T, ctypes.byref(rt.c),
+                                    _stream(stream)), "moe_route_received")
+
+
+def moe_ep_local_map(n_global: int, ep_size: int, rank: int, layout: int = MOE_EP_LINEAR):
+    """Host helper: (local_of [n_global] CPU int32 tensor, local slot count)."""
+    out = torch.empty(n_global, dtype=torch.int32)
+    n = ctypes.c_int32(0)
+    _check(lib().moe_ep_local_map(n_global, ep_size, rank, layout, _ptr(out), ctypes.byref(n)),
+           "moe_ep_local_map")
+    return out, n.value
+
+
+def moe_eplb_plan(load, n_redundant: int, ep_size: int):
+    """Host helper: physical_to_logical map [E + n_redundant] (CPU int32) of
+    the EPLB placement for per-expert ``load`` (float64)."""
+    load = torch.as_tensor(load, dtype=torch.float64).contiguous()
+    E = load.numel()
+    out = torch.empty(E + n_redundant, dtype=torch.int32)
+    _check(lib().moe_eplb_plan(_ptr(load), E, n_redundant, ep_size, _ptr(out)), "moe_eplb_plan")
+    return out
+
+
 def moe_replica_map_from_p2l(p2l, E: int, max_replicas: int):
     """Host helper: physical_to_logical_map -> (logical_to_physical_map,
     logical_replica_count) as CPU int32 tensors."""
@@ -319,9 +372,11 @@ class MoELayer:
     the shared expert, if any, is the last slot."""
 
     def __init__(self, d: Desc, weights: dict, w_router, bias=None, l2p=None,
-                 replica_count=None, device="cuda", router: GroupedRouter | None = None):
+                 replica_count=None, device="cuda", router: GroupedRouter | None = None,
+                 ep: "EPMap | None" = None):
         self.d = d
         self.router = router           # None: softmax top-K (moe_route)
+        self.ep = ep                   # one rank's expert-parallel share (moe_route_ep)
         self.device = device
         self.rt = RouteTables(d, device)
         self.ws = torch.zeros(route_workspace_bytes(d), dtype=torch.uint8, device=device)
@@ -358,7 +413,10 @@ class MoELayer:
         if logits is None:
             moe_router_logits(d, x, self.w_router, self.bias, T, self.logits, stream)
             logits = self.logits
-        if self.router is None:
+        if self.ep is not None:
+            moe_route_ep(d, logits, T, self.rt, self.ws, self.ep, self.router, self.l2p, self.rcount,
+                         stream)
+        elif self.router is None:
             moe_route(d, logits, T, self.rt, self.ws, self.l2p, self.rcount, stream)
         else:
             moe_route_grouped(d, logits, T, self.rt, self.ws, self.router, self.l2p, self.rcount, stream)

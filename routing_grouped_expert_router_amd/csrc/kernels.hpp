@@ -15,12 +15,16 @@ struct RouteWs {            // views into the caller's route workspace
   int32_t* blk;             // [nblk*E] per-block counts -> exclusive prefixes
   int32_t* blk_flags;       // [nblk] non-finite flag per block
   int32_t* tok_flag;        // [T_max] non-finite flag per token
-  int32_t* map_valid;       // [1] 1 when a replica map is given and valid
+  int32_t* map_valid;       // [1] bit 0: a replica map is given and valid;
+                            //     bit 1: the local map is valid
 };
 
 struct RouteArgs {
   const float* logits; int T, E, E_phys, K;
   const int32_t* l2p; const int32_t* rcount; int max_replicas;
+  // expert-parallel share: global physical slot -> local slot or -1 (null:
+  // every slot local, n_global == E_phys)
+  const int32_t* local_of; int n_global;
   int layout, M_max, BM;
   int64_t routed_cap;       // rows of the routed part of the grouped buffer
   // outputs
@@ -35,6 +39,13 @@ struct RouteArgs {
 };
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+struct ReceivedArgs {
+  const int32_t* counts_in; int E_phys, M_max, T, n_shared;
+  int32_t* counts; int32_t* masked_m; int32_t* offsets; int32_t* spill_off; int32_t* tile_off;
+  uint32_t* status;
+};
+hipError_t launch_route_received(const ReceivedArgs& a, hipStream_t s);
 
 // ---- permute / combine -------------------------------------------------------
 

@@ -4,7 +4,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <cmath>
+#include <vector>
 #include <cstdlib>
 
 #include "common.hpp"
@@ -85,7 +87,8 @@ const char* moe_status_string(moe_status_t s) {
 moe_status_t moe_check_desc(const moe_desc_t* d) {
   if (!d) return MOE_ERR_ARG;
   if (d->T_max < 0 || d->H <= 0 || d->I <= 0 || d->E < 1 || d->K < 1 || d->K > d->E) return MOE_ERR_ARG;
-  if (d->E_phys < d->E || d->n_shared < 0 || d->n_shared > 1 || d->max_replicas < 1) return MOE_ERR_ARG;
+  // E_phys < E only for one rank's expert-parallel share (moe_route_ep)
+  if (d->E_phys < 1 || d->n_shared < 0 || d->n_shared > 1 || d->max_replicas < 1) return MOE_ERR_ARG;
   if (d->act_dtype != MOE_F32 && d->act_dtype != MOE_BF16) return MOE_ERR_ARG;
   if (d->w_dtype != MOE_BF16 && d->w_dtype != MOE_FP8E4M3_B128) return MOE_ERR_ARG;
   if (d->w_packed != 0 && d->w_packed != 1) return MOE_ERR_ARG;
@@ -147,10 +150,17 @@ moe_status_t moe_router_logits(const moe_desc_t* d, const void* x, const void* w
 namespace {
 
 moe_status_t route_impl(const moe_desc_t* d, const float* logits, int32_t T, const moe_grouped_router_t* g,
-                        const int32_t* l2p, const int32_t* replica_count, const moe_route_t* r, void* ws,
-                        size_t ws_bytes, hipStream_t stream) {
+                        const moe_ep_map_t* ep, const int32_t* l2p, const int32_t* replica_count,
+                        const moe_route_t* r, void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status_t st = moe_check_desc(d);
   if (st != MOE_OK) return st;
+  if (ep) {
+    // global slots: the replica map's, or the logical ids without one
+    if (!ep->local_of || ep->n_global < 1 || ep->n_global > kMaxE) return MOE_ERR_ARG;
+    if (!l2p && ep->n_global < d->E) return MOE_ERR_ARG;
+  } else if (d->E_phys < d->E) {
+    return MOE_ERR_ARG;                    // every expert needs a local slot
+  }
   if (g) {
     const int G = g->n_group;
     if (G < 1 || d->E % G) return MOE_ERR_ARG;
@@ -169,6 +179,7 @@ moe_status_t route_impl(const moe_desc_t* d, const float* logits, int32_t T, con
   RouteArgs a = {};
   a.logits = logits; a.T = T; a.E = d->E; a.E_phys = d->E_phys; a.K = d->K;
   a.l2p = l2p; a.rcount = replica_count; a.max_replicas = d->max_replicas;
+  if (ep) { a.local_of = ep->local_of; a.n_global = ep->n_global; }
   a.layout = d->layout; a.M_max = d->M_max; a.BM = d->BM; a.routed_cap = routed_cap(d);
   a.topk_ids = r->topk_ids; a.topk_w = r->topk_w; a.topk_phys = r->topk_phys;
   a.row_of = r->row_of; a.slot_of = r->slot_of; a.src_of = r->src_of;
@@ -194,7 +205,7 @@ extern "C" {
 moe_status_t moe_route(const moe_desc_t* d, const float* logits, int32_t T, const int32_t* l2p,
                        const int32_t* replica_count, const moe_route_t* r, void* ws,
                        size_t ws_bytes, hipStream_t stream) {
-  return route_impl(d, logits, T, nullptr, l2p, replica_count, r, ws, ws_bytes, stream);
+  return route_impl(d, logits, T, nullptr, nullptr, l2p, replica_count, r, ws, ws_bytes, stream);
 }
 
 moe_status_t moe_route_grouped(const moe_desc_t* d, const float* logits, int32_t T,
@@ -202,7 +213,30 @@ moe_status_t moe_route_grouped(const moe_desc_t* d, const float* logits, int32_t
                                const int32_t* replica_count, const moe_route_t* r, void* ws,
                                size_t ws_bytes, hipStream_t stream) {
   if (!g) return MOE_ERR_ARG;
-  return route_impl(d, logits, T, g, l2p, replica_count, r, ws, ws_bytes, stream);
+  return route_impl(d, logits, T, g, nullptr, l2p, replica_count, r, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_route_ep(const moe_desc_t* d, const float* logits, int32_t T,
+                          const moe_grouped_router_t* g, const moe_ep_map_t* ep, const int32_t* l2p,
+                          const int32_t* replica_count, const moe_route_t* r, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  if (!ep) return MOE_ERR_ARG;
+  return route_impl(d, logits, T, g, ep, l2p, replica_count, r, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_route_received(const moe_desc_t* d, const int32_t* counts, int32_t T,
+                                const moe_route_t* r, hipStream_t stream) {
+  moe_status_t st = moe_check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->layout != MOE_MASKED) return MOE_ERR_UNSUPPORTED;
+  if (!counts || T < 0 || T > d->T_max || !r || !r->counts || !r->masked_m || !r->offsets ||
+      !r->spill_off || !r->tile_off || !r->status)
+    return MOE_ERR_ARG;
+  ReceivedArgs a = {};
+  a.counts_in = counts; a.E_phys = d->E_phys; a.M_max = d->M_max; a.T = T; a.n_shared = d->n_shared;
+  a.counts = r->counts; a.masked_m = r->masked_m; a.offsets = r->offsets;
+  a.spill_off = r->spill_off; a.tile_off = r->tile_off; a.status = r->status;
+  return hip_status(launch_route_received(a, stream));
 }
 
 moe_status_t moe_permute(const moe_desc_t* d, const void* x, int32_t T, const moe_route_t* r,
@@ -433,6 +467,78 @@ moe_status_t moe_pack_weights(const moe_desc_t* d, int32_t which, int32_t G, con
   if ((which != 0 && which != 1) || G < 0 || (G > 0 && (!src || !dst)) || src == dst) return MOE_ERR_ARG;
   const int N = which == 0 ? d->I : d->H, Kdim = which == 0 ? d->H : d->I;
   return hip_status(launch_pack(src, dst, G, N, Kdim, d->w_dtype == MOE_FP8E4M3_B128, stream));
+}
+
+moe_status_t moe_ep_local_map(int32_t n_global, int32_t ep_size, int32_t rank, int32_t layout,
+                              int32_t* local_of, int32_t* n_local) {
+  if (!local_of || n_global < 1 || ep_size < 1 || rank < 0 || rank >= ep_size) return MOE_ERR_ARG;
+  if (layout != MOE_EP_LINEAR && layout != MOE_EP_ROUND_ROBIN) return MOE_ERR_ARG;
+  int n = 0;
+  if (layout == MOE_EP_LINEAR) {
+    // contiguous runs; the first n_global % ep_size ranks take one more slot
+    const int base = n_global / ep_size, rem = n_global % ep_size;
+    const int first = rank * base + (rank < rem ? rank : rem);
+    const int count = base + (rank < rem ? 1 : 0);
+    for (int p = 0; p < n_global; ++p) local_of[p] = (p >= first && p < first + count) ? p - first : -1;
+    n = count;
+  } else {
+    for (int p = 0; p < n_global; ++p) local_of[p] = (p % ep_size == rank) ? n++ : -1;
+  }
+  if (n_local) *n_local = n;
+  return MOE_OK;
+}
+
+moe_status_t moe_eplb_plan(const double* load, int32_t E, int32_t n_redundant, int32_t ep_size,
+                           int32_t* p2l) {
+  if (!load || !p2l || E < 1 || n_redundant < 0 || ep_size < 1) return MOE_ERR_ARG;
+  const int64_t n = (int64_t)E + n_redundant;
+  if (n % ep_size || n > kMaxE) return MOE_ERR_ARG;
+  for (int l = 0; l < E; ++l)
+    if (!(load[l] >= 0.0) || !std::isfinite(load[l])) return MOE_ERR_ARG;
+  // replicas: each redundant slot to the largest load per replica (lowest id on ties)
+  std::vector<int> rep(E, 1);
+  for (int i = 0; i < n_redundant; ++i) {
+    int best = 0;
+    double bv = load[0] / rep[0];
+    for (int l = 1; l < E; ++l) {
+      const double v = load[l] / rep[l];
+      if (v > bv) { bv = v; best = l; }
+    }
+    ++rep[best];
+  }
+  // longest processing time first: replicas in descending load per replica
+  // (lower expert, then replica order, on ties), each to the least loaded
+  // rank with a free slot, preferring ranks without a copy of that expert
+  struct Item { double w; int l, j; };
+  std::vector<Item> items;
+  items.reserve(n);
+  for (int l = 0; l < E; ++l)
+    for (int j = 0; j < rep[l]; ++j) items.push_back({load[l] / rep[l], l, j});
+  std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) {
+    if (x.w != y.w) return x.w > y.w;
+    if (x.l != y.l) return x.l < y.l;
+    return x.j < y.j;
+  });
+  const int S = int(n / ep_size);
+  std::vector<std::vector<int>> slots(ep_size);
+  std::vector<double> total(ep_size, 0.0);
+  for (const Item& it : items) {
+    int pick = -1;
+    bool pick_fresh = false;
+    for (int r = 0; r < ep_size; ++r) {
+      if ((int)slots[r].size() >= S) continue;
+      const bool fresh = std::find(slots[r].begin(), slots[r].end(), it.l) == slots[r].end();
+      if (pick < 0 || (fresh && !pick_fresh) || (fresh == pick_fresh && total[r] < total[pick])) {
+        pick = r;
+        pick_fresh = fresh;
+      }
+    }
+    slots[pick].push_back(it.l);
+    total[pick] += it.w;
+  }
+  for (int r = 0; r < ep_size; ++r)
+    for (int i = 0; i < S; ++i) p2l[(int64_t)r * S + i] = slots[r][i];
+  return MOE_OK;
 }
 
 moe_status_t moe_replica_map_from_p2l(const int32_t* p2l, int32_t E, int32_t E_phys,

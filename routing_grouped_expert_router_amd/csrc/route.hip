@@ -275,11 +275,15 @@ __device__ __forceinline__ void scan_all(const RouteArgs& a) {
   __shared__ int tl_s[1024];
   __shared__ int tmp[kScanThreads / 64 + 1];
   __shared__ int bad_s, nonfinite_s;
+  __shared__ int bad_ep_s;
   const int tid = threadIdx.x;
   const int E = a.E, P = a.E_phys;
+  const bool ep = a.local_of != nullptr;
+  const int NG = ep ? a.n_global : P;       // slots the replica map may name
+  const int NC = NG > P ? NG : P;
   const int nblk = (a.T + kBlockTokens - 1) / kBlockTokens;
-  if (tid == 0) { bad_s = 0; nonfinite_s = 0; }
-  for (int p = tid; p <= P; p += kScanThreads) { cnt[p] = 0; aux[p] = 0; }
+  if (tid == 0) { bad_s = 0; nonfinite_s = 0; bad_ep_s = 0; }
+  for (int p = tid; p <= NC; p += kScanThreads) { cnt[p] = 0; aux[p] = 0; }
   __syncthreads();
   // per logical expert: exclusive prefix over blocks, and total T_l
   for (int l = tid; l < E; l += kScanThreads) {
@@ -302,14 +306,14 @@ __device__ __forceinline__ void scan_all(const RouteArgs& a) {
       if (R < 1 || R > a.max_replicas) { atomicOr(&bad_s, 1); continue; }
       for (int r = 0; r < R; ++r) {
         const int p = a.l2p[(int64_t)l * a.max_replicas + r];
-        if (p < 0 || p >= P) atomicOr(&bad_s, 1);
+        if (p < 0 || p >= NG) atomicOr(&bad_s, 1);
         else atomicAdd(&aux[p], 1);
       }
     }
   }
   __syncthreads();
   if (has_map)
-    for (int p = tid; p < P; p += kScanThreads)
+    for (int p = tid; p < NG; p += kScanThreads)
       if (aux[p] > 1) atomicOr(&bad_s, 1);
   __syncthreads();
   const bool valid = has_map && bad_s == 0;
@@ -325,6 +329,34 @@ __device__ __forceinline__ void scan_all(const RouteArgs& a) {
     }
   }
   __syncthreads();
+  bool ep_ok = true;
+  if (ep) {
+    // local map: entries in [-1, P), each local slot named at most once; the
+    // local counts take the counts of their global slots (remote: dropped
+    // here, counted by their own rank)
+    for (int q = tid; q < NC; q += kScanThreads) aux[q] = 0;
+    __syncthreads();
+    for (int p = tid; p < NG; p += kScanThreads) {
+      const int q = a.local_of[p];
+      if (q < -1 || q >= P) atomicOr(&bad_ep_s, 1);
+      else if (q >= 0) atomicAdd(&aux[q], 1);
+    }
+    __syncthreads();
+    for (int q = tid; q < P; q += kScanThreads)
+      if (aux[q] > 1) atomicOr(&bad_ep_s, 1);
+    __syncthreads();
+    ep_ok = bad_ep_s == 0;
+    for (int q = tid; q < P; q += kScanThreads) aux[q] = 0;
+    __syncthreads();
+    if (ep_ok)
+      for (int p = tid; p < NG; p += kScanThreads) {
+        const int q = a.local_of[p];
+        if (q >= 0) aux[q] = cnt[p];
+      }
+    __syncthreads();
+    for (int q = tid; q < P; q += kScanThreads) cnt[q] = aux[q];
+    __syncthreads();
+  }
   const bool masked = a.layout == MOE_MASKED;
   for (int p = tid; p < P; p += kScanThreads) {
     const int c = cnt[p];
@@ -365,8 +397,9 @@ __device__ __forceinline__ void scan_all(const RouteArgs& a) {
     if (nonfinite_s) st |= MOE_STATUS_NONFINITE;
     if (masked && total2 > 0) st |= MOE_STATUS_SPILL;
     if (has_map && !valid) st |= MOE_STATUS_BAD_REPLICA;
+    if (!ep_ok) st |= MOE_STATUS_BAD_EP_MAP;
     a.status[0] = st;
-    a.ws.map_valid[0] = valid ? 1 : 0;
+    a.ws.map_valid[0] = (valid ? 1 : 0) | (ep && ep_ok ? 2 : 0);
   }
 }
 
@@ -380,10 +413,22 @@ __device__ __forceinline__ void assign_one(const RouteArgs& a, int64_t i) {
   const int b = t / kBlockTokens;
   const int j = a.ws.blk[(int64_t)b * a.E + l] + a.ws.local_rank[i];
   int p = l, rank = j;
-  if (a.ws.map_valid[0]) {
+  const int mv = a.ws.map_valid[0];
+  if (mv & 1) {
     const int R = a.rcount[l];
     p = a.l2p[(int64_t)l * a.max_replicas + j % R];
     rank = j / R;
+  }
+  if (a.local_of) {
+    // the rank inside a slot counts the tokens of that global slot, all of
+    // which are local when the slot is
+    p = (mv & 2) ? a.local_of[p] : -1;
+    if (p < 0) {                      // another rank's choice: no local row
+      a.topk_phys[i] = -1;
+      a.row_of[i] = -1;
+      a.slot_of[i] = -1;
+      return;
+    }
   }
   const int row = a.offsets[p] + rank;
   int64_t slot;
@@ -450,6 +495,47 @@ static void launch_shape(const RouteArgs& a, int nblk, hipStream_t s) {
   if (TK > 0)
     hipLaunchKernelGGL(route_assign_kernel, dim3((TK + kRouteThreads - 1) / kRouteThreads), dim3(kRouteThreads),
                        0, s, a);
+}
+
+// Received counts (a dispatch filled rows p*M_max + i, i < counts[p], of the
+// masked buffer): the masked tables the expert kernels read, no spill.
+__global__ __launch_bounds__(kScanThreads) void route_received_kernel(ReceivedArgs a) {
+  __shared__ int cnt[kMaxE + 1];
+  __shared__ int aux[kMaxE + 1];
+  __shared__ int tmp[kScanThreads / 64 + 1];
+  __shared__ int over_s;
+  const int tid = threadIdx.x, P = a.E_phys;
+  if (tid == 0) over_s = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += kScanThreads) {
+    const int c = a.counts_in[p];
+    if (c < 0 || c > a.M_max) atomicOr(&over_s, 1);
+    const int mm = c < 0 ? 0 : (c < a.M_max ? c : a.M_max);
+    cnt[p] = mm;
+    aux[p] = (mm + kTileRows - 1) / kTileRows;
+    a.counts[p] = mm;
+    a.masked_m[p] = mm;
+    a.spill_off[p] = 0;
+  }
+  __syncthreads();
+  const int total = block_exclusive_scan(cnt, P, tmp);
+  const int ttotal = block_exclusive_scan(aux, P, tmp);
+  for (int p = tid; p < P; p += kScanThreads) {
+    a.offsets[p] = cnt[p];
+    a.tile_off[p] = aux[p];
+  }
+  if (tid == 0) {
+    a.offsets[P] = total;
+    a.spill_off[P] = 0;
+    a.tile_off[P] = ttotal;
+    a.tile_off[P + 1] = ttotal + (a.n_shared ? (a.T + kTileRows - 1) / kTileRows : 0);
+    a.status[0] = over_s ? MOE_STATUS_RECV_OVERFLOW : 0u;
+  }
+}
+
+hipError_t launch_route_received(const ReceivedArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(route_received_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {

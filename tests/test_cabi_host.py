@@ -40,7 +40,7 @@ def _d(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(K=0), B.MOE_ERR_ARG), (dict(K=9), B.MOE_ERR_ARG), (dict(E_phys=7), B.MOE_ERR_ARG),
+    (dict(K=0), B.MOE_ERR_ARG), (dict(K=9), B.MOE_ERR_ARG), (dict(E_phys=0), B.MOE_ERR_ARG),
     (dict(n_shared=2), B.MOE_ERR_ARG), (dict(act_dtype=7), B.MOE_ERR_ARG),
     (dict(layout=5), B.MOE_ERR_ARG), (dict(M_max=0), B.MOE_ERR_ARG),
     (dict(H=100), B.MOE_ERR_UNSUPPORTED), (dict(I=200), B.MOE_ERR_UNSUPPORTED),
@@ -68,6 +68,9 @@ def test_calls_reject_bad_arguments_before_enqueueing():
     fake = ctypes.c_void_p(16)
     rt2 = B.moe_route_t(*([fake] * len(B.moe_route_t._fields_)))
     assert L.moe_route(dc, fake, 4, null, null, ctypes.byref(rt2), fake, 1, null) == B.MOE_ERR_WORKSPACE
+    # fewer slots than experts: only for an expert-parallel share
+    d7 = ctypes.byref(_d(E_phys=7).c())
+    assert L.moe_route(d7, fake, 4, null, null, ctypes.byref(rt2), fake, 1 << 20, null) == B.MOE_ERR_ARG
     # only one of the two replica arrays
     assert L.moe_route(dc, fake, 4, fake, null, ctypes.byref(rt2), fake, 1 << 20, null) == B.MOE_ERR_ARG
     # grouped router parameters are checked on the host (E = 8 here)
@@ -80,6 +83,18 @@ def test_calls_reject_bad_arguments_before_enqueueing():
                                1 << 20, null) == B.MOE_ERR_UNSUPPORTED
     assert L.moe_route_grouped(dc, fake, 4, null, null, null, ctypes.byref(rt2), fake, 1 << 20,
                                null) == B.MOE_ERR_ARG
+    # expert-parallel routing: a map is required; without a replica map the
+    # global slots must cover the E experts (E = 8 here); received counts
+    # need the masked layout
+    assert L.moe_route_ep(dc, fake, 4, null, null, null, null, ctypes.byref(rt2), fake, 1 << 20,
+                          null) == B.MOE_ERR_ARG
+    for bad in (B.moe_ep_map_t(None, 8), B.moe_ep_map_t(fake, 7), B.moe_ep_map_t(fake, 0),
+                B.moe_ep_map_t(fake, 4097)):
+        assert L.moe_route_ep(dc, fake, 4, null, ctypes.byref(bad), null, null, ctypes.byref(rt2), fake,
+                              1 << 20, null) == B.MOE_ERR_ARG
+    dcon = ctypes.byref(_d(layout=B.MOE_CONTIG, BM=16).c())
+    assert L.moe_route_received(dcon, fake, 4, ctypes.byref(rt2), null) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_route_received(dc, null, 4, ctypes.byref(rt2), null) == B.MOE_ERR_ARG
     # the fused gather needs bf16 activations (the tiny descriptor's are fp32)
     w0 = B.moe_weights_t(fake, fake, fake, None, None, None, None, None, None, None, None, None)
     assert L.moe_expert_gate_up_x(dc, ctypes.byref(w0), ctypes.byref(rt2), 4, fake, fake,
@@ -122,3 +137,34 @@ def test_replica_map_helper_matches_reference_and_page():
         B.moe_replica_map_from_p2l([0, 0, 1], 3, 2)      # logical expert 2 has no slot
     with pytest.raises(B.MoEError):
         B.moe_replica_map_from_p2l([0, 0, 0, 1, 2], 3, 2)  # more than max_replicas
+
+
+def test_ep_local_map_helper_matches_reference():
+    for layout, name in ((B.MOE_EP_LINEAR, "linear"), (B.MOE_EP_ROUND_ROBIN, "round_robin")):
+        for n, ep in ((4, 2), (5, 2), (7, 3), (256, 8), (544, 32), (3, 5)):
+            for r in range(ep):
+                got, nl = B.moe_ep_local_map(n, ep, r, layout)
+                ref = O.ep_local_map(n, ep, r, name)
+                assert got.tolist() == ref.tolist() and nl == int((ref >= 0).sum())
+    for args in ((0, 2, 0, 0), (4, 0, 0, 0), (4, 2, 2, 0), (4, 2, -1, 0), (4, 2, 0, 7)):
+        with pytest.raises(B.MoEError):
+            B.moe_ep_local_map(*args)
+
+
+def test_eplb_plan_helper_matches_reference():
+    assert B.moe_eplb_plan([30.0, 5.0, 30.0, 5.0], 2, 2).tolist() == [0, 2, 1, 0, 2, 3]
+    rng = np.random.default_rng(5)
+    for _ in range(60):
+        ep = int(rng.integers(1, 9)); S = int(rng.integers(1, 9))
+        E = int(rng.integers(max(1, ep * S - 6), ep * S + 1))
+        load = rng.integers(0, 20, size=E).astype(np.float64)      # ties on purpose
+        got = B.moe_eplb_plan(load, ep * S - E, ep)
+        assert got.tolist() == O.eplb_plan(load, ep * S - E, ep).tolist()
+    E = 256
+    load = (np.random.default_rng(2).permutation(E) + 1.0) ** -1.1
+    for ep in (8, 32):
+        assert B.moe_eplb_plan(load, 32, ep).tolist() == O.eplb_plan(load, 32, ep).tolist()
+    for load, nr, ep in (([1.0, 2.0, 3.0], 0, 2), ([1.0, float("nan")], 0, 1), ([1.0, -1.0], 0, 1),
+                         ([], 0, 1), ([1.0], -1, 1)):
+        with pytest.raises(B.MoEError):
+            B.moe_eplb_plan(load, nr, ep)

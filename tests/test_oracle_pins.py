@@ -630,4 +630,4 @@ def test_received_tables_match_routed_masked_tables():
     tiles = np.concatenate([[0], np.cumsum(-(-res["counts"] // 128))])
     assert np.array_equal(rt["tile_off"], tiles)
     over = O.received_tables(np.array([3, 50]), 40)
-    assert over["status"] & O.STATUS_SPILL and over["masked_m"].tolist() == [3, 40]
+    assert over["status"] & O.STATUS_RECV_OVERFLOW and over["masked_m"].tolist() == [3, 40]
