@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--router", choices=("softmax", "grouped"), default="softmax",
                     help="softmax top-K (default) or the grouped sigmoid router with "
                          "8 groups, 4 kept, group score = sum of the 2 best, weights x2.5")
+    ap.add_argument("--ep-ranks", type=int, default=1,
+                    help="time rank 0's expert-parallel share of the layer: the linear map over "
+                         "the physical slots, E_phys / N local slots (routing of every token, "
+                         "experts and combine of the local choices)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 512 MiB device copy three times (a kernel of known "
                          "traffic for scaling hardware byte counters)")
@@ -66,13 +70,31 @@ GROUPED_ROUTER = dict(n_group=8, topk_group=4, group_k=2, renormalize=True, scal
 
 
 class Setup:
-    def __init__(self, cfg, packed=True, router="softmax"):
+    def __init__(self, cfg, packed=True, router="softmax", ep_ranks=1):
+        import numpy as np
         import torch
         from routing_grouped_expert_router_amd import binding as B
         from workloads import generate
         self.cfg = cfg
         self.inp = generate.make_inputs(cfg, wdevice="cuda")
-        self.w = generate.upload_weights(self.inp, "cuda")
+        # expert-parallel share: rank 0 of ep_ranks under the linear map over
+        # the physical slots holds only its local slots' weights
+        self.local_of = None
+        ep = None
+        if ep_ranks > 1:
+            lo, n_local = B.moe_ep_local_map(cfg.E_phys, ep_ranks, 0, B.MOE_EP_LINEAR)
+            self.local_of = lo.numpy()
+            slots = [p for p in range(cfg.E_phys) if self.local_of[p] >= 0]
+            w = generate.upload_weights(self.inp, "cuda", slots=slots + ([cfg.E_phys] if cfg.n_shared else []))
+            idx = torch.tensor(slots + ([cfg.E_phys] if cfg.n_shared else []), device="cuda")
+            self.w = {k: v[idx].contiguous() for k, v in w.items()}
+            del w
+            torch.cuda.empty_cache()
+            ep = B.EPMap(lo.cuda())
+            cfg = cfg.with_(E_phys=n_local)
+            self.cfg = cfg
+        else:
+            self.w = generate.upload_weights(self.inp, "cuda")
         l2p = rc = None
         max_rep = 1
         if self.inp.p2l is not None:
@@ -96,14 +118,16 @@ class Setup:
             sb = generate.make_score_bias(cfg)
             self.grouped = dict(GROUPED_ROUTER, score_bias=sb.numpy())
             gr = B.GroupedRouter(score_bias=sb.cuda(), **GROUPED_ROUTER)
-        self.layer = B.MoELayer(self.d, self.w, self.wr, self.bias, l2p, rc, "cuda", router=gr)
+        self.layer = B.MoELayer(self.d, self.w, self.wr, self.bias, l2p, rc, "cuda", router=gr, ep=ep)
         self.B = B
         torch.cuda.synchronize()
 
     def step(self, ev=None):
         B, L, d, T = self.B, self.layer, self.d, self.cfg.T
         B.moe_router_logits(d, self.x, self.wr, self.bias, T, L.logits)
-        if L.router is None:
+        if L.ep is not None:
+            B.moe_route_ep(d, L.logits, T, L.rt, L.ws, L.ep, L.router, L.l2p, L.rcount)
+        elif L.router is None:
             B.moe_route(d, L.logits, T, L.rt, L.ws, L.l2p, L.rcount)
         else:
             B.moe_route_grouped(d, L.logits, T, L.rt, L.ws, L.router, L.l2p, L.rcount)
@@ -148,12 +172,13 @@ class Setup:
         return slots, routed, gu, total
 
 
-def time_workload(cfg, steps, warmup, packed=True, router="softmax"):
+def time_workload(cfg, steps, warmup, packed=True, router="softmax", ep_ranks=1):
     """Eager steps (HIP events around the gate/up kernel on the launch
     stream), then the same step captured once in a HIP graph and replayed
     ``steps`` times (the layer latency reported)."""
     import torch
-    s = Setup(cfg, packed, router)
+    s = Setup(cfg, packed, router, ep_ranks)
+    cfg = s.cfg
     for _ in range(warmup):
         s.step()
     torch.cuda.synchronize()
@@ -273,7 +298,8 @@ def cpu_baseline(s, budget_s=30.0):
     while True:
         toks = np.arange(0, T, max(1, T // n))[:n]
         t0 = time.perf_counter()
-        oracle_forward(inp, tokens=toks, grouped=s.grouped)
+        oracle_forward(inp, tokens=toks, grouped=s.grouped, local_of=s.local_of,
+                       E_local=None if s.local_of is None else cfg.E_phys)
         dt = time.perf_counter() - t0
         print(f"# cpu reference: {len(toks)} of {T} tokens in {dt:.1f} s", file=sys.stderr, flush=True)
         if n >= T or dt * 4 > budget_s:
@@ -314,7 +340,7 @@ def main():
     for n in names:
         c = configs.by_name(n)
         r = time_workload(c, args.steps, args.warmup, packed=not args.row_major,
-                          router=args.router)
+                          router=args.router, ep_ranks=args.ep_ranks)
         results[n] = r
         print(f"# {n}: {r['ms']*1e3:.1f} us/layer (graph), {r['eager_ms']*1e3:.1f} eager, "
               f"gate/up {r['gu_ms']*1e3:.1f} us ({r['gu_flops']/(r['gu_ms']*1e-3)/1e12:.0f} TFLOP/s), "
@@ -351,7 +377,10 @@ def main():
                    "layout": cfg.layout, "M_max": cfg.M_max, "w_dtype": cfg.w_dtype,
                    "weights": "row-major" if args.row_major else "packed",
                    "router": args.router if args.router == "softmax" else
-                   "grouped sigmoid (8 groups, 4 kept, top-2 group score, x2.5)"},
+                   "grouped sigmoid (8 groups, 4 kept, top-2 group score, x2.5)",
+                   "ep": None if args.ep_ranks == 1 else
+                   {"ranks": args.ep_ranks, "rank": 0, "map": "linear",
+                    "local_slots": head["cfg"].E_phys}},
         "expert_weight_hbm_gbs": round(gb_s, 1),
         "layer_tflops": round(head["layer_flops"] / (head["ms"] * 1e-3) / 1e12, 2),
         "touched_slots": head["slots"],
