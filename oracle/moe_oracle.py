@@ -71,6 +71,18 @@ design notes with its reason):
      same expert yet (if every rank with a free slot holds one, any rank with
      a free slot); ties to the lower rank.  Rank r owns global slots
      [r*S, (r+1)*S), S = (E + redundant) / ranks, filled in placement order.
+  R20 W8A8 activations ([infra5] DeepGEMM section: FP8 operands with
+     per-128 scales and two-level accumulation): each row's 128-wide K block
+     is scaled by s = fp32(amax / 448) (1 for an all-zero block) and coded as
+     E4M3FN of fp32(x / s), round to nearest even; the amax element codes to
+     exactly +-448.
+  R21 W8A8 product: y[t, n] = sum over K blocks b of sa[t, b] * sw[n/128, b]
+     * (sum over k in b of dec(qa[t, k]) * dec(qw[n, k])) -- the per-block
+     sum promoted to fp32 and scaled, then accumulated (two-level
+     accumulation); the reference takes it exactly.
+  R22 W8A8 layer: x is quantized per token (R20), gate/up use R21, h is
+     rounded to bf16 (the layer's intermediate format) and quantized per row
+     the same way for the down projection.
   R19 received counts ([infra5] DeepGEMM section: the dispatch's received
      count per local expert is masked_m): rows of local slot p sit at
      p*M_max + i, i < count; counts outside [0, M_max] are an error (status
@@ -123,6 +135,74 @@ def dequant_block128(q: np.ndarray, s: np.ndarray) -> np.ndarray:
     v = decode_e4m3fn(q)
     sf = np.asarray(s, dtype=np.float64)
     return v * np.repeat(np.repeat(sf, 128, axis=0), 128, axis=1)
+
+
+# --------------------------------------------------------------------------
+# W8A8: activation quantization and the two-level product  (R20 - R22)
+# --------------------------------------------------------------------------
+
+_E4M3_POS = None
+
+
+def encode_e4m3fn(v: np.ndarray) -> np.ndarray:
+    """Finite values -> OCP E4M3FN bytes: the nearest of the 127 non-negative
+    finite codes (ties to the even code, i.e. even mantissa), magnitudes
+    above 448 saturate to 448, the sign bit copied (-0 -> 0x80)."""
+    global _E4M3_POS
+    if _E4M3_POS is None:
+        _E4M3_POS = decode_e4m3fn(np.arange(127))          # ascending: 0 .. 448
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    dlo = a - _E4M3_POS[lo]
+    dhi = _E4M3_POS[hi] - a
+    code = np.where(dhi < dlo, hi, np.where(dlo < dhi, lo, np.where(hi % 2 == 0, hi, lo)))
+    return (code | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def quant_1x128(x: np.ndarray):
+    """R20: rows of fp32-exact values [R, C] (C a multiple of 128) -> (codes
+    uint8 [R, C], scales fp32 [R, C/128])."""
+    x = np.asarray(x, dtype=np.float32)
+    R, C = x.shape
+    blk = x.reshape(R, C // 128, 128)
+    amax = np.abs(blk).max(axis=2)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    v = (blk / s[:, :, None]).astype(np.float32)
+    return encode_e4m3fn(v).reshape(R, C), s
+
+
+def w8a8_matmul(qa: np.ndarray, sa: np.ndarray, qw: np.ndarray, sw: np.ndarray) -> np.ndarray:
+    """R21: qa [T, K] codes with sa [T, K/128]; qw [N, K] codes with sw
+    [N/128, K/128].  Per-block sums, each scaled by sa * sw, then summed."""
+    T, K = qa.shape
+    N = qw.shape[0]
+    A = decode_e4m3fn(qa).reshape(T, K // 128, 128).transpose(1, 0, 2)     # [b, T, 128]
+    W = decode_e4m3fn(qw).reshape(N, K // 128, 128).transpose(1, 2, 0)     # [b, 128, N]
+    part = np.matmul(A, W)                                                  # [b, T, N] block sums
+    scale = (np.asarray(sa, np.float64).T[:, :, None] *
+             np.repeat(np.asarray(sw, np.float64), 128, axis=0).T[:, None, :])
+    return (part * scale).sum(axis=0)
+
+
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """Values -> nearest bf16 (ties to even), as float64, via fp32."""
+    u = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def swiglu_expert_w8a8(X: np.ndarray, codes) -> np.ndarray:
+    """R22: codes = (q1, s1, q3, s3, q2, s2) of one expert (E4M3FN bytes and
+    128x128 block scales)."""
+    q1, s1, q3, s3, q2, s2 = codes
+    qx, sx = quant_1x128(X)
+    G = w8a8_matmul(qx, sx, q1, s1)
+    U = w8a8_matmul(qx, sx, q3, s3)
+    Hh = round_bf16(silu(G) * U)
+    qh, sh = quant_1x128(Hh)
+    return w8a8_matmul(qh, sh, q2, s2)
 
 
 # --------------------------------------------------------------------------
@@ -450,7 +530,7 @@ def swiglu_expert(X: np.ndarray, W1: np.ndarray, W3: np.ndarray, W2: np.ndarray)
 
 def moe_forward(x, w_router, bias, K, E_phys, expert_weights, shared_weights=None,
                 p2l=None, layout="contig", M_max=0, BM=16, logits=None,
-                tokens=None, grouped=None, local_of=None):
+                tokens=None, grouped=None, local_of=None, expert_codes=None, shared_codes=None):
     """The layer forward as defined: returns a dict with every intermediate.
 
     x [T, H] (values exactly as the layer receives them); w_router [E, H];
@@ -464,7 +544,9 @@ def moe_forward(x, w_router, bias, K, E_phys, expert_weights, shared_weights=Non
     router instead of the softmax top-K.  ``local_of`` (R16), a local map
     over the global physical slots (the p2l slots, or the logical ids without
     one), makes this the output of one GPU's expert-parallel share: E_phys is
-    then the number of local slots.
+    then the number of local slots.  ``expert_codes(p)`` (and ``shared_codes``),
+    the fp8 codes and block scales of slot p, select the W8A8 experts (R22)
+    instead of the fp64 products of the dequantized weights.
 
     out[t] = S[t] + sum_k w[t, k] * Y[row_of[t, k]]   ([vllbc] combine:
     weight by g_i then sum the K results; R4 for S)."""
@@ -510,10 +592,15 @@ def moe_forward(x, w_router, bias, K, E_phys, expert_weights, shared_weights=Non
         rows = rows[need[src_of[lo:hi]]]
         if rows.size == 0:
             continue
-        W1, W3, W2 = expert_weights(p)
-        Y[rows] = swiglu_expert(x[src_of[rows]], W1, W3, W2)
+        if expert_codes is not None:
+            Y[rows] = swiglu_expert_w8a8(x[src_of[rows]], expert_codes(p))
+        else:
+            W1, W3, W2 = expert_weights(p)
+            Y[rows] = swiglu_expert(x[src_of[rows]], W1, W3, W2)
     out = np.zeros((len(want), H), dtype=np.float64)
-    if shared_weights is not None:
+    if shared_codes is not None:
+        out += swiglu_expert_w8a8(x[want], shared_codes)
+    elif shared_weights is not None:
         out += swiglu_expert(x[want], *shared_weights)
     for k in range(K):
         r = row_of[want, k]

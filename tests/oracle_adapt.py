@@ -57,3 +57,39 @@ def oracle_forward(inp, logits=None, tokens=None, layout=None, grouped=None, loc
         cfg.K, E_phys, slot_weights, shared, p2l=inp.p2l,
         layout=layout or cfg.layout, M_max=cfg.M_max, BM=cfg.BM,
         logits=logits, tokens=tokens, grouped=grouped, local_of=local_of)
+
+
+def expert_codes(ew):
+    """fp8 weights -> (q1, s1, q3, s3, q2, s2) as numpy (W8A8 reference)."""
+    return (ew.w1.numpy(), ew.s1.numpy(), ew.w3.numpy(), ew.s3.numpy(), ew.w2.numpy(), ew.s2.numpy())
+
+
+def oracle_forward_w8a8(inp, logits=None, tokens=None, layout=None, local_of=None, E_local=None):
+    """oracle_forward with the W8A8 experts (fp8 weights only)."""
+    cfg = inp.cfg
+    assert cfg.w_dtype == "fp8"
+    cache = {}
+    E_phys = cfg.E_phys
+    glob = None
+    if local_of is not None:
+        local_of = np.asarray(local_of, dtype=np.int32)
+        E_phys = int((local_of >= 0).sum()) if E_local is None else E_local
+        glob = {int(q): p for p, q in enumerate(local_of) if q >= 0}
+
+    def codes(p):
+        if glob is not None:
+            p = glob[p]
+        l = inp.slot_logical(p)
+        if l not in cache:
+            if len(cache) > 2:
+                cache.pop(next(iter(cache)))
+            cache[l] = expert_codes(inp.expert(l))
+        return cache[l]
+
+    shared = expert_codes(inp.shared()) if cfg.n_shared else None
+    return O.moe_forward(
+        to_f64(inp.x), to_f64(inp.w_router),
+        None if inp.bias is None else inp.bias.numpy(),
+        cfg.K, E_phys, None, None, p2l=inp.p2l,
+        layout=layout or cfg.layout, M_max=cfg.M_max, BM=cfg.BM,
+        logits=logits, tokens=tokens, local_of=local_of, expert_codes=codes, shared_codes=shared)

@@ -631,3 +631,78 @@ def test_received_tables_match_routed_masked_tables():
     assert np.array_equal(rt["tile_off"], tiles)
     over = O.received_tables(np.array([3, 50]), 40)
     assert over["status"] & O.STATUS_RECV_OVERFLOW and over["masked_m"].tolist() == [3, 40]
+
+
+# ------------------------------------------------------------------ W8A8 (R20-R22)
+
+def test_e4m3_encoder_matches_torch_cast():
+    """The reference's E4M3FN encoder against torch's float8_e4m3fn cast
+    (round to nearest even) on a dense grid of fp32 values in [-448, 448],
+    every midpoint between adjacent codes, subnormals and signed zeros; and
+    every finite code decodes and re-encodes to itself."""
+    pos = O.decode_e4m3fn(np.arange(127))
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+    v = np.concatenate([np.linspace(-448, 448, 100001).astype(np.float32), mids, -mids,
+                        np.float32([0.0, -0.0, 2 ** -10, 2 ** -11, 3 * 2 ** -11, -2 ** -9])])
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.encode_e4m3fn(v), ref)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    assert np.array_equal(O.encode_e4m3fn(O.decode_e4m3fn(codes)), codes)
+    assert O.encode_e4m3fn(np.array([500.0, -1e9])).tolist() == [0x7E, 0xFE]   # saturate
+
+
+def test_quant_1x128_scales_and_error_bound():
+    """R20: per row and 128-wide block the largest magnitude codes to exactly
+    +-448; every value dequantizes within half a code step (2^-4 relative
+    for normals, s * 2^-10 absolute below); an all-zero block has scale 1."""
+    rng = np.random.default_rng(0)
+    x = (rng.standard_normal((5, 384)) * np.exp(rng.normal(0, 2, (5, 1)))).astype(np.float32)
+    x[2, 128:256] = 0.0
+    q, s = O.quant_1x128(x)
+    assert q.shape == x.shape and s.shape == (5, 3) and s.dtype == np.float32
+    dq = O.decode_e4m3fn(q).reshape(5, 3, 128) * s[:, :, None]
+    xb = x.reshape(5, 3, 128).astype(np.float64)
+    for r in range(5):
+        for b in range(3):
+            if r == 2 and b == 1:
+                assert s[r, b] == 1.0 and not q[r, 128:256].any()
+                continue
+            k = int(np.argmax(np.abs(xb[r, b])))
+            assert (q.reshape(5, 3, 128)[r, b, k] & 0x7F) == 0x7E          # |code| = 448
+    bound = np.maximum(np.abs(xb) * 2.0 ** -4, s[:, :, None] * 2.0 ** -10) * (1 + 1e-6)
+    assert (np.abs(dq - xb) <= bound).all()
+
+
+def test_w8a8_product_equals_dequantized_matmul():
+    """R21 against the plain product of the dequantized operands (block
+    scales applied elementwise first, one matmul after)."""
+    rng = np.random.default_rng(1)
+    T, N, K = 7, 256, 384
+    qa, sa = O.quant_1x128(rng.standard_normal((T, K)).astype(np.float32))
+    w = torch.from_numpy(rng.standard_normal((N, K)).astype(np.float32) * 0.02)
+    qw, sw = generate.quantize_e4m3_block128(w)
+    qw, sw = qw.numpy(), sw.numpy()
+    A = O.decode_e4m3fn(qa) * np.repeat(sa, 128, axis=1)
+    W = O.dequant_block128(qw, sw)
+    assert np.allclose(O.w8a8_matmul(qa, sa, qw, sw), A @ W.T, rtol=1e-12, atol=1e-15)
+
+
+def test_round_bf16_matches_torch():
+    v = np.random.default_rng(2).standard_normal(10000) * 10.0 ** np.random.default_rng(3).integers(-5, 5, 10000)
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).float().numpy().astype(np.float64)
+    assert np.array_equal(O.round_bf16(v), ref)
+
+
+def test_w8a8_layer_against_w8a16_layer():
+    """R22: quantizing the activations moves the fp8-weight layer by a few
+    percent of its largest output (the 1x128 activation code steps); the
+    routing is untouched."""
+    from oracle_adapt import oracle_forward_w8a8
+    cfg = configs.tiny().with_(T=20, H=512, I=256, E=8, E_phys=8, K=2, n_shared=1,
+                               act_dtype="bf16", w_dtype="fp8", M_max=20)
+    inp = generate.make_inputs(cfg)
+    a = oracle_forward(inp)
+    b = oracle_forward_w8a8(inp)
+    e = np.abs(a["out"] - b["out"]).max() / np.abs(a["out"]).max()
+    assert 5e-3 < e < 6e-2, e
+    assert np.array_equal(a["row_of"], b["row_of"])
