@@ -347,6 +347,46 @@ moe_status_t moe_grouped_ffn_x(const moe_desc_t* d, const moe_weights_t* w,
                                const moe_route_t* r, int32_t T, const void* x,
                                void* h, void* y, hipStream_t stream);
 
+/* ---- W8A8: fp8 activations on fp8 MFMA ------------------------------------
+ * ("推理 INFRA 方法论(5)", DeepGEMM section: FP8 operands with per-128 scales
+ * and two-level accumulation -- each 128-wide K block summed by the matrix
+ * unit, promoted to fp32, scaled and accumulated.)  For fp8 weights
+ * (MOE_FP8E4M3_B128; else MOE_ERR_UNSUPPORTED).  The W8A8 layer differs from
+ * the W8A16 one (moe_grouped_ffn_x) by the activation quantization: a few
+ * percent of the largest output on DeepSeek-V3 shapes, more than the 3e-2
+ * bound of the fp8 path, so it is a separate, opt-in path. */
+
+/* Each row's 128-wide blocks of a bf16 matrix [rows, C] (row stride ld
+ * elements, C a multiple of 128): s = amax / 448 (1 for an all-zero block),
+ * codes = E4M3FN of x / s (IEEE fp32 division, round to nearest even, clamped
+ * to +-448).  q: device [rows, C] bytes (row stride C), natural K order; s:
+ * device fp32 [rows, C/128].  Non-finite inputs give unspecified codes. */
+moe_status_t moe_quantize_1x128(const void* src, int64_t ld, int64_t rows, int32_t C, void* q,
+                                float* s, hipStream_t stream);
+
+/* a6 with fp8 activations: xq / xs = moe_quantize_1x128 of the layer input x
+ * [T, H]; rows are gathered by token (src_of) as moe_expert_gate_up_x does.
+ * h as moe_expert_gate_up.  Decode-sized groups: a group's rows run in passes
+ * of 16 (at most 16 rows) or 64, each pass streaming the group's weights. */
+moe_status_t moe_expert_gate_up_a8(const moe_desc_t* d, const moe_weights_t* w,
+                                   const moe_route_t* r, int32_t T, const void* xq,
+                                   const float* xs, void* h, hipStream_t stream);
+
+/* a7 with fp8 activations: hq / hs = moe_quantize_1x128 of h over its
+ * moe_buffer_rows(d) rows (C = I).  y as moe_expert_down (same K split). */
+moe_status_t moe_expert_down_a8(const moe_desc_t* d, const moe_weights_t* w,
+                                const moe_route_t* r, int32_t T, const void* hq,
+                                const float* hs, void* y, hipStream_t stream);
+
+/* a6-a8 with fp8 activations: quantize x, gate/up, quantize h, down.
+ * Caller-owned scratch: xq [T_max, H] bytes, xs [T_max, H/128] fp32, hq
+ * [moe_buffer_rows, I] bytes, hs [moe_buffer_rows, I/128] fp32; bf16
+ * activations only (else MOE_ERR_UNSUPPORTED). */
+moe_status_t moe_grouped_ffn_a8(const moe_desc_t* d, const moe_weights_t* w,
+                                const moe_route_t* r, int32_t T, const void* x, void* xq,
+                                float* xs, void* h, void* hq, float* hs, void* y,
+                                hipStream_t stream);
+
 /* a9. out[t] = sum_k topk_w[t,k] * y[slot_of[t*K+k]] (+ y[shared_base + t]),
  * in fp32 with k ascending, then rounded to act_dtype (RNE).
  * (vllbc blog, combine: weight by g_i, then sum the K results.)

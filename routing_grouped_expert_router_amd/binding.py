@@ -30,7 +30,8 @@ EXPORTED = [
     "moe_permute", "moe_expert_gate_up", "moe_expert_gate_up_x", "moe_expert_down",
     "moe_grouped_ffn", "moe_grouped_ffn_x", "moe_combine", "moe_forward", "moe_pack_weights",
     "moe_replica_map_from_p2l", "moe_route_ep", "moe_route_received", "moe_ep_local_map",
-    "moe_eplb_plan",
+    "moe_eplb_plan", "moe_quantize_1x128", "moe_expert_gate_up_a8", "moe_expert_down_a8",
+    "moe_grouped_ffn_a8",
 ]
 
 
@@ -106,6 +107,10 @@ def lib() -> ctypes.CDLL:
             "moe_route_received": (ctypes.c_int, [D, _P, i32, R, _P]),
             "moe_ep_local_map": (ctypes.c_int, [i32, i32, i32, i32, _P, _P]),
             "moe_eplb_plan": (ctypes.c_int, [_P, i32, i32, i32, _P]),
+            "moe_quantize_1x128": (ctypes.c_int, [_P, i64, i64, i32, _P, _P, _P]),
+            "moe_expert_gate_up_a8": (ctypes.c_int, [D, W, R, i32, _P, _P, _P, _P]),
+            "moe_expert_down_a8": (ctypes.c_int, [D, W, R, i32, _P, _P, _P, _P]),
+            "moe_grouped_ffn_a8": (ctypes.c_int, [D, W, R, i32, _P, _P, _P, _P, _P, _P, _P, _P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -354,6 +359,30 @@ def moe_eplb_plan(load, n_redundant: int, ep_size: int):
     return out
 
 
+def moe_quantize_1x128(src, rows: int, q, s, stream=None):
+    """src bf16 [>=rows, >=C] (row stride src.stride(0)) -> q uint8 [rows, C],
+    s fp32 [rows, C/128]; C = q.shape[1]."""
+    C = q.shape[1]
+    _check(lib().moe_quantize_1x128(_ptr(src), src.stride(0), rows, C, _ptr(q), _ptr(s),
+                                    _stream(stream)), "moe_quantize_1x128")
+
+
+def moe_expert_gate_up_a8(d: Desc, w: Weights, rt: RouteTables, T, xq, xs, h, stream=None):
+    _check(lib().moe_expert_gate_up_a8(ctypes.byref(d.c()), ctypes.byref(w.c), ctypes.byref(rt.c), T,
+                                       _ptr(xq), _ptr(xs), _ptr(h), _stream(stream)), "moe_expert_gate_up_a8")
+
+
+def moe_expert_down_a8(d: Desc, w: Weights, rt: RouteTables, T, hq, hs, y, stream=None):
+    _check(lib().moe_expert_down_a8(ctypes.byref(d.c()), ctypes.byref(w.c), ctypes.byref(rt.c), T,
+                                    _ptr(hq), _ptr(hs), _ptr(y), _stream(stream)), "moe_expert_down_a8")
+
+
+def moe_grouped_ffn_a8(d: Desc, w: Weights, rt: RouteTables, T, x, xq, xs, h, hq, hs, y, stream=None):
+    _check(lib().moe_grouped_ffn_a8(ctypes.byref(d.c()), ctypes.byref(w.c), ctypes.byref(rt.c), T,
+                                    _ptr(x), _ptr(xq), _ptr(xs), _ptr(h), _ptr(hq), _ptr(hs), _ptr(y),
+                                    _stream(stream)), "moe_grouped_ffn_a8")
+
+
 def moe_replica_map_from_p2l(p2l, E: int, max_replicas: int):
     """Host helper: physical_to_logical_map -> (logical_to_physical_map,
     logical_replica_count) as CPU int32 tensors."""
@@ -373,8 +402,9 @@ class MoELayer:
 
     def __init__(self, d: Desc, weights: dict, w_router, bias=None, l2p=None,
                  replica_count=None, device="cuda", router: GroupedRouter | None = None,
-                 ep: "EPMap | None" = None):
+                 ep: "EPMap | None" = None, a8: bool = False):
         self.d = d
+        self.a8 = a8                   # fp8 activations (moe_grouped_ffn_a8), fp8 weights only
         self.router = router           # None: softmax top-K (moe_route)
         self.ep = ep                   # one rank's expert-parallel share (moe_route_ep)
         self.device = device
@@ -399,6 +429,12 @@ class MoELayer:
         self.weights = Weights(routed, shared)
         odt = torch.float32 if d.act_dtype == MOE_F32 else torch.bfloat16
         self.out = torch.zeros((max(1, d.T_max), d.H), dtype=odt, device=device)
+        if a8:
+            T1 = max(1, d.T_max)
+            self.xq = torch.zeros((T1, d.H), dtype=torch.uint8, device=device)
+            self.xs = torch.zeros((T1, d.H // 128), dtype=torch.float32, device=device)
+            self.hq = torch.zeros((rows, d.I), dtype=torch.uint8, device=device)
+            self.hs = torch.zeros((rows, d.I // 128), dtype=torch.float32, device=device)
 
     def y_for(self, T: int) -> torch.Tensor:
         return self.y[: y_bytes(self.d, T)]
@@ -420,7 +456,10 @@ class MoELayer:
             moe_route(d, logits, T, self.rt, self.ws, self.l2p, self.rcount, stream)
         else:
             moe_route_grouped(d, logits, T, self.rt, self.ws, self.router, self.l2p, self.rcount, stream)
-        if fused_gather and d.act_dtype == MOE_BF16:
+        if self.a8:
+            moe_grouped_ffn_a8(d, self.weights, self.rt, T, x, self.xq, self.xs, self.h, self.hq, self.hs,
+                               self.y, stream)
+        elif fused_gather and d.act_dtype == MOE_BF16:
             moe_grouped_ffn_x(d, self.weights, self.rt, T, x, self.h, self.y, stream)
         else:
             moe_permute(d, x, T, self.rt, self.xg, stream)

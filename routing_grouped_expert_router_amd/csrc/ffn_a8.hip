@@ -1,0 +1,233 @@
+// W8A8 expert projections on gfx950: fp8 (E4M3FN) weights and activations,
+// fp8 MFMA, per-128 block scales, two-level accumulation.
+//
+// ("推理 INFRA 方法论(5)", DeepGEMM section: FP8 operands with per-128 scales;
+// the matrix unit sums one 128-wide K block, the block sum is promoted to fp32,
+// multiplied by its scales and accumulated.)
+//
+//  * quant_1x128_kernel: each row's 128-wide K block gets s = amax / 448
+//    (1 for an all-zero block) and E4M3FN codes of x / s (IEEE fp32 division,
+//    round to nearest even, clamped to +-448), stored in natural K order.
+//  * ffn_a8_kernel: a streaming kernel for decode-sized groups.  A workgroup
+//    owns 64 weight rows of one group (wave w: the 16-row panel n0 + 16w, and
+//    for gate/up the same rows of W3); the group's token rows run in passes
+//    of MT tiles of 16.  Per 128-wide K step each lane holds 32 weight bytes
+//    -- the packed layout's two 16-byte pieces, K offsets 16g..16g+15 and
+//    64+16g..64+16g+15 for lane group g -- and the same 32 K of its token row,
+//    so one v_mfma_scale_f32_16x16x128_f8f6f4 (unit E8M0 scales) gives the
+//    block sum; it is scaled by the weight block's scale times the token's
+//    and added to the fp32 accumulator.  Weights and activations run NB - 1
+//    steps ahead in registers.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float a8_silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// E4M3FN codes of four fp32 values, bytes in order
+__device__ __forceinline__ uint32_t a8_pack4(float a, float b, float c, float d) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+__global__ __launch_bounds__(256) void quant_1x128_kernel(QuantArgs a) {
+  const int nb = a.C / 128;
+  const int64_t blk = ((int64_t)blockIdx.x * 256 + threadIdx.x) / 16;   // (row, block)
+  const int sub = threadIdx.x & 15;                                    // 8 values each
+  const bool live = blk < a.rows * nb;
+  const int64_t row = live ? blk / nb : 0;
+  const int b = live ? int(blk % nb) : 0;
+  const u32x4 v = *reinterpret_cast<const u32x4*>(a.src + row * a.ld + b * 128 + sub * 8);
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+#pragma unroll
+  for (int d = 8; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d, 16));
+  const float s = m > 0.f ? m / 448.0f : 1.0f;
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(f[i] / s, -448.0f), 448.0f);
+  const uint32_t lo = a8_pack4(q[0], q[1], q[2], q[3]);
+  const uint32_t hi = a8_pack4(q[4], q[5], q[6], q[7]);
+  if (live) {
+    *reinterpret_cast<u32x2*>(a.q + row * a.C + b * 128 + sub * 8) = u32x2{lo, hi};
+    if (sub == 0) a.s[row * nb + b] = s;
+  }
+}
+
+hipError_t launch_quant_1x128(const QuantArgs& a, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  const int64_t threads = a.rows * (a.C / 128) * 16;
+  hipLaunchKernelGGL(quant_1x128_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int MODE, int MT, bool PACKED>
+__global__ __launch_bounds__(256) void ffn_a8_kernel(A8Args a) {
+  constexpr bool GU = MODE == MODE_GATEUP;
+  // register stages (NB - 1 steps in flight), as many as the registers allow
+  constexpr int NB = MT == 1 ? (GU ? 4 : 8) : 3;
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: weight scales load as scalars
+  const bool shared = g == a.E_phys;
+  int64_t s0 = 0, s1 = 0;
+  int c0 = 0, c1 = 0;
+  if (shared) { s0 = a.shared_base; c0 = a.T; }
+  else if (a.layout == MOE_MASKED) {
+    const int mm = a.masked_m[g];
+    s0 = (int64_t)g * a.M_max; c0 = mm;
+    s1 = (int64_t)a.E_phys * a.M_max + a.spill_off[g]; c1 = a.counts[g] - mm;
+  } else {
+    s0 = a.pad_off[g]; c0 = a.counts[g];
+  }
+  const int R = c0 + c1;
+  if (R <= a.min_rows || R > a.max_rows) return;   // the other launch's class
+  const int N = a.N, Kdim = a.Kdim;
+  const int nkb = Kdim / 128;
+  const int kper = nkb / a.ksplit;
+  const int kb0 = blockIdx.z * kper;
+  const int n0 = blockIdx.x * 64 + 16 * wave;       // this wave's 16 weight rows
+  const int lr = lane & 15, lg = lane >> 4;
+  const uint8_t* Wa = shared ? a.SW : a.W + (int64_t)g * N * Kdim;
+  const uint8_t* Wb = GU ? (shared ? a.SW3 : a.W3 + (int64_t)g * N * Kdim) : nullptr;
+  const float* Sa = (shared ? a.SS : a.S + (int64_t)g * (N / 128) * nkb) + (int64_t)(n0 / 128) * nkb;
+  const float* Sb = GU ? (shared ? a.SS3 : a.S3 + (int64_t)g * (N / 128) * nkb) + (int64_t)(n0 / 128) * nkb
+                       : nullptr;
+  // byte offset of this lane's 16-byte weight piece `instr` of K step kb
+  auto woff = [&](int kb, int instr) -> int64_t {
+    if (PACKED) return ((int64_t)kb * (N / 16) + n0 / 16) * 2048 + instr * 1024 + lane * 16;
+    return (int64_t)(n0 + lr) * Kdim + kb * 128 + 64 * instr + 16 * lg;
+  };
+  const int ntiles = (R + 15) / 16;
+  for (int t0 = 0; t0 < ntiles; t0 += MT) {
+    const uint8_t* xrow[MT];
+    const float* srow[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int gr = (t0 + i) * 16 + lr;
+      const int rank = gr < R ? gr : 0;              // rows past the group read a valid row
+      int64_t row;
+      if (a.gather_src) row = shared ? rank : a.gather_src[a.gather_off[g] + rank];
+      else row = rank < c0 ? s0 + rank : s1 + (rank - c0);
+      xrow[i] = a.X + row * a.ldx + 16 * lg;
+      srow[i] = a.XS + row * nkb;
+    }
+    u32x4 wr[NB][2], w3r[NB][2], xr[NB][MT][2];
+    float sx[NB][MT], swa[NB], swb[NB];
+    auto load = [&](int bank, int kb) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        wr[bank][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wa + woff(kb, j)));
+        if constexpr (GU) w3r[bank][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wb + woff(kb, j)));
+      }
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        xr[bank][i][0] = *reinterpret_cast<const u32x4*>(xrow[i] + kb * 128);
+        xr[bank][i][1] = *reinterpret_cast<const u32x4*>(xrow[i] + kb * 128 + 64);
+        sx[bank][i] = srow[i][kb];
+      }
+      swa[bank] = Sa[kb];
+      if constexpr (GU) swb[bank] = Sb[kb];
+    };
+    f32x4 acc[MT], acc3[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) { acc[i] = f32x4{0, 0, 0, 0}; acc3[i] = f32x4{0, 0, 0, 0}; }
+    auto compute = [&](int bank, bool valid) {
+      const v8i w = __builtin_bit_cast(v8i, u32x8{wr[bank][0].x, wr[bank][0].y, wr[bank][0].z, wr[bank][0].w,
+                                                  wr[bank][1].x, wr[bank][1].y, wr[bank][1].z, wr[bank][1].w});
+      v8i w3 = w;
+      if constexpr (GU)
+        w3 = __builtin_bit_cast(v8i, u32x8{w3r[bank][0].x, w3r[bank][0].y, w3r[bank][0].z, w3r[bank][0].w,
+                                           w3r[bank][1].x, w3r[bank][1].y, w3r[bank][1].z, w3r[bank][1].w});
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const u32x4 x0 = xr[bank][i][0], x1 = xr[bank][i][1];
+        const v8i x = __builtin_bit_cast(v8i, u32x8{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w});
+        const f32x4 zero = {0, 0, 0, 0};
+        const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, zero, 0, 0, 0, 127, 0, 127);
+        // padding steps (past the K range) add d * 0
+        const float sc = valid ? swa[bank] * sx[bank][i] : 0.0f;
+        acc[i] += d * sc;
+        if constexpr (GU) {
+          const f32x4 d3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w3, x, zero, 0, 0, 0, 127, 0, 127);
+          acc3[i] += d3 * (valid ? swb[bank] * sx[bank][i] : 0.0f);
+        }
+      }
+    };
+    // The step count is padded to whole passes of NB so that the loop body
+    // has no branches (a guarded step makes the compiler wait for every
+    // outstanding load); loads past the end re-read the last step.
+    const int slast = kper - 1;
+    const int npad = (kper + NB - 1) / NB * NB;
+#pragma unroll
+    for (int p = 0; p < NB - 1; ++p) load(p, kb0 + min(p, slast));
+    for (int sb = 0; sb < npad; sb += NB) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int st = sb + u;
+        load((u + NB - 1) % NB, kb0 + min(st + NB - 1, slast));
+        // (fences keep each step's loads in their step: hoisted together the
+        // loads of a pass serialise the pipeline)
+        __builtin_amdgcn_sched_barrier(0);
+        compute(u, st < kper);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // acc[i] holds D[w-row 4*lg + j][token lr of tile i]
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int gr = (t0 + i) * 16 + lr;
+      if (gr >= R) continue;
+      const int64_t row = gr < c0 ? s0 + gr : s1 + (gr - c0);
+      const int col = n0 + 4 * lg;
+      if constexpr (GU) {
+        const f32x4 gt = acc[i], up = acc3[i];
+        const u32x2 o = {pack_bf16x2(a8_silu(gt.x) * up.x, a8_silu(gt.y) * up.y),
+                         pack_bf16x2(a8_silu(gt.z) * up.z, a8_silu(gt.w) * up.w)};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + col) = o;
+      } else if (a.out_f32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + blockIdx.z * a.split_stride + row * a.ldo + col) = acc[i];
+      } else {
+        const u32x2 o = {pack_bf16x2(acc[i].x, acc[i].y), pack_bf16x2(acc[i].z, acc[i].w)};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + col) = o;
+      }
+    }
+  }
+}
+
+template <int MODE, int MT>
+static void launch_a8_mt(const A8Args& a, int packed, dim3 grid, hipStream_t s) {
+  if (packed) hipLaunchKernelGGL((ffn_a8_kernel<MODE, MT, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ffn_a8_kernel<MODE, MT, false>), grid, dim3(256), 0, s, a);
+}
+
+// Two launches split the groups by row count: up to 16 rows one tile per
+// pass (deeper load pipeline), larger groups four tiles per pass.
+hipError_t launch_ffn_a8(const A8Args& a0, int packed, int mode, hipStream_t s) {
+  if (a0.N % 64 || a0.Kdim % 128 || (a0.Kdim / 128) % a0.ksplit) return hipErrorInvalidValue;
+  const dim3 grid(a0.N / 64, a0.E_phys + a0.n_shared, a0.ksplit);
+  A8Args a = a0;
+  a.min_rows = 0; a.max_rows = 16;
+  if (mode == MODE_GATEUP) launch_a8_mt<MODE_GATEUP, 1>(a, packed, grid, s);
+  else launch_a8_mt<MODE_DOWN, 1>(a, packed, grid, s);
+  if (a0.T > 16) {
+    a.min_rows = 16; a.max_rows = 0x7fffffff;
+    if (mode == MODE_GATEUP) launch_a8_mt<MODE_GATEUP, 4>(a, packed, grid, s);
+    else launch_a8_mt<MODE_DOWN, 4>(a, packed, grid, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -119,6 +119,27 @@ hipError_t launch_ffn_tiled(const TiledArgs& a, int fp8, int packed, int mode, i
 // row-major [G, N, Kdim] weights -> the packed layout the kernels stream
 hipError_t launch_pack(const void* src, void* dst, int G, int N, int Kdim, int fp8, hipStream_t s);
 
+// ---- W8A8 (fp8 activations) ----------------------------------------------------
+
+struct QuantArgs {            // rows of bf16 [rows, C] (row stride ld) -> E4M3FN codes
+  const uint16_t* src; int64_t ld; int64_t rows; int C;   //   [rows, C] and fp32 scales
+  uint8_t* q; float* s;                                     //   [rows, C / 128]
+};
+hipError_t launch_quant_1x128(const QuantArgs& a, hipStream_t s);
+
+struct A8Args {
+  const uint8_t* X; int64_t ldx; const float* XS;   // fp8 rows (natural K order), scales [rows, Kdim/128]
+  const int32_t* gather_src; const int32_t* gather_off;   // as StreamArgs (gate/up only)
+  int Kdim, N;
+  int E_phys, T, layout, M_max, n_shared; int64_t shared_base;
+  const int32_t* counts; const int32_t* masked_m; const int32_t* spill_off; const int32_t* pad_off;
+  const uint8_t* W; const uint8_t* W3; const float* S; const float* S3;        // routed
+  const uint8_t* SW; const uint8_t* SW3; const float* SS; const float* SS3;    // shared
+  void* out; int64_t ldo; int64_t split_stride; int out_f32; int ksplit;
+  int min_rows, max_rows;                           // set by the launcher
+};
+hipError_t launch_ffn_a8(const A8Args& a, int packed, int mode, hipStream_t s);
+
 // ---- router logits --------------------------------------------------------------
 
 struct RouterArgs {

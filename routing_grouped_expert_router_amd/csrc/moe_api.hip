@@ -422,6 +422,96 @@ moe_status_t moe_grouped_ffn_x(const moe_desc_t* d, const moe_weights_t* w, cons
   return moe_expert_down(d, w, r, T, h, y, stream);
 }
 
+moe_status_t moe_quantize_1x128(const void* src, int64_t ld, int64_t rows, int32_t C, void* q,
+                                float* s, hipStream_t stream) {
+  if (rows < 0 || C < 128 || C % 128 || ld < C) return MOE_ERR_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!src || !q || !s) return MOE_ERR_ARG;
+  QuantArgs a;
+  a.src = static_cast<const uint16_t*>(src); a.ld = ld; a.rows = rows; a.C = C;
+  a.q = static_cast<uint8_t*>(q); a.s = s;
+  return hip_status(launch_quant_1x128(a, stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+moe_status_t a8_checks(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r, int32_t T) {
+  moe_status_t st = ffn_common_checks(d, w, r, T);
+  if (st != MOE_OK) return st;
+  if (d->w_dtype != MOE_FP8E4M3_B128) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+A8Args a8_base_args(const moe_desc_t* d, const moe_route_t* r, int32_t T) {
+  A8Args a = {};
+  a.E_phys = d->E_phys; a.T = T; a.layout = d->layout; a.M_max = d->M_max; a.n_shared = d->n_shared;
+  a.shared_base = routed_cap(d);
+  a.counts = r->counts; a.masked_m = r->masked_m; a.spill_off = r->spill_off; a.pad_off = r->pad_off;
+  a.ksplit = 1;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_expert_gate_up_a8(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
+                                   int32_t T, const void* xq, const float* xs, void* h,
+                                   hipStream_t stream) {
+  moe_status_t st = a8_checks(d, w, r, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!xq || !xs || !h || !w->w1 || !w->w3 || !w->s1 || !w->s3) return MOE_ERR_ARG;
+  if (d->n_shared && (!w->sw1 || !w->sw3)) return MOE_ERR_ARG;
+  A8Args a = a8_base_args(d, r, T);
+  a.X = static_cast<const uint8_t*>(xq); a.ldx = d->H; a.XS = xs;
+  a.gather_src = r->src_of; a.gather_off = r->offsets;
+  a.Kdim = d->H; a.N = d->I;
+  a.W = static_cast<const uint8_t*>(w->w1); a.W3 = static_cast<const uint8_t*>(w->w3);
+  a.S = w->s1; a.S3 = w->s3;
+  a.SW = static_cast<const uint8_t*>(w->sw1); a.SW3 = static_cast<const uint8_t*>(w->sw3);
+  a.SS = w->ss1; a.SS3 = w->ss3;
+  a.out = h; a.ldo = d->I;
+  return hip_status(launch_ffn_a8(a, d->w_packed, MODE_GATEUP, stream));
+}
+
+moe_status_t moe_expert_down_a8(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
+                                int32_t T, const void* hq, const float* hs, void* y,
+                                hipStream_t stream) {
+  moe_status_t st = a8_checks(d, w, r, T);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!hq || !hs || !y || !w->w2 || !w->s2) return MOE_ERR_ARG;
+  if (d->n_shared && !w->sw2) return MOE_ERR_ARG;
+  const int splits = moe_down_splits(d, T);
+  A8Args a = a8_base_args(d, r, T);
+  a.X = static_cast<const uint8_t*>(hq); a.ldx = d->I; a.XS = hs;
+  a.Kdim = d->I; a.N = d->H;
+  a.W = static_cast<const uint8_t*>(w->w2); a.S = w->s2;
+  a.SW = static_cast<const uint8_t*>(w->sw2); a.SS = w->ss2;
+  a.out = y; a.ldo = d->H; a.ksplit = splits; a.out_f32 = splits > 1;
+  a.split_stride = moe_buffer_rows(d) * d->H;
+  return hip_status(launch_ffn_a8(a, d->w_packed, MODE_DOWN, stream));
+}
+
+moe_status_t moe_grouped_ffn_a8(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
+                                int32_t T, const void* x, void* xq, float* xs, void* h, void* hq,
+                                float* hs, void* y, hipStream_t stream) {
+  moe_status_t st = a8_checks(d, w, r, T);
+  if (st != MOE_OK) return st;
+  if (d->act_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  st = moe_quantize_1x128(x, d->H, T, d->H, xq, xs, stream);
+  if (st != MOE_OK) return st;
+  st = moe_expert_gate_up_a8(d, w, r, T, xq, xs, h, stream);
+  if (st != MOE_OK) return st;
+  st = moe_quantize_1x128(h, d->I, moe_buffer_rows(d), d->I, hq, hs, stream);
+  if (st != MOE_OK) return st;
+  return moe_expert_down_a8(d, w, r, T, hq, hs, y, stream);
+}
+
 moe_status_t moe_combine(const moe_desc_t* d, const moe_route_t* r, int32_t T, const void* y,
                          void* out, hipStream_t stream) {
   moe_status_t st = moe_check_desc(d);

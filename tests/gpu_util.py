@@ -26,7 +26,8 @@ _DEFAULT = object()
 class Built:
     """A workload on the GPU: inputs, uploaded weights and a MoELayer."""
 
-    def __init__(self, cfg, T=None, layout=None, M_max=None, p2l=_DEFAULT, packed=False, grouped=None):
+    def __init__(self, cfg, T=None, layout=None, M_max=None, p2l=_DEFAULT, packed=False, grouped=None,
+                 a8=False):
         if layout is not None:
             cfg = cfg.with_(layout=layout)
         if M_max is not None:
@@ -59,8 +60,9 @@ class Built:
             router = B.GroupedRouter(grouped["n_group"], grouped["topk_group"], grouped["group_k"],
                                      grouped.get("renormalize", True), grouped.get("scale", 1.0),
                                      None if sb is None else torch.from_numpy(np.asarray(sb, np.float32)).to(DEV))
+        self.a8 = a8
         self.layer = B.MoELayer(self.d, self.weights, self.wr, self.bias, self.l2p, self.rcount, DEV,
-                                router=router)
+                                router=router, a8=a8)
 
     def oracle_logits(self) -> np.ndarray:
         return O.router_logits(to_f64(self.inp.x), to_f64(self.inp.w_router),
@@ -73,6 +75,10 @@ class Built:
         return out
 
     def oracle(self, logits_np=None, tokens=None):
+        if self.a8:
+            from oracle_adapt import oracle_forward_w8a8
+            assert self.grouped is None
+            return oracle_forward_w8a8(self.inp, logits=logits_np, tokens=tokens)
         return oracle_forward(self.inp, logits=logits_np, tokens=tokens, grouped=self.grouped)
 
 

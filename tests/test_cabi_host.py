@@ -95,6 +95,12 @@ def test_calls_reject_bad_arguments_before_enqueueing():
     dcon = ctypes.byref(_d(layout=B.MOE_CONTIG, BM=16).c())
     assert L.moe_route_received(dcon, fake, 4, ctypes.byref(rt2), null) == B.MOE_ERR_UNSUPPORTED
     assert L.moe_route_received(dc, null, 4, ctypes.byref(rt2), null) == B.MOE_ERR_ARG
+    # W8A8 needs fp8 weights; the quantizer needs C a multiple of 128 and ld >= C
+    assert L.moe_expert_gate_up_a8(dc, ctypes.byref(B.moe_weights_t(*([fake] * 12))), ctypes.byref(rt2), 4,
+                                   fake, fake, fake, null) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_quantize_1x128(fake, 200, 4, 200, fake, fake, null) == B.MOE_ERR_ARG
+    assert L.moe_quantize_1x128(fake, 64, 4, 128, fake, fake, null) == B.MOE_ERR_ARG
+    assert L.moe_quantize_1x128(fake, 128, 0, 128, null, null, null) == B.MOE_OK
     # the fused gather needs bf16 activations (the tiny descriptor's are fp32)
     w0 = B.moe_weights_t(fake, fake, fake, None, None, None, None, None, None, None, None, None)
     assert L.moe_expert_gate_up_x(dc, ctypes.byref(w0), ctypes.byref(rt2), 4, fake, fake,
