@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--router", choices=("softmax", "grouped"), default="softmax",
                     help="softmax top-K (default) or the grouped sigmoid router with "
                          "8 groups, 4 kept, group score = sum of the 2 best, weights x2.5")
+    ap.add_argument("--a8", action="store_true",
+                    help="fp8 weights only: quantize the activations per 1x128 block and run the "
+                         "W8A8 expert kernels (fp8 MFMA)")
     ap.add_argument("--ep-ranks", type=int, default=1,
                     help="time rank 0's expert-parallel share of the layer: the linear map over "
                          "the physical slots, E_phys / N local slots (routing of every token, "
@@ -70,7 +73,7 @@ GROUPED_ROUTER = dict(n_group=8, topk_group=4, group_k=2, renormalize=True, scal
 
 
 class Setup:
-    def __init__(self, cfg, packed=True, router="softmax", ep_ranks=1):
+    def __init__(self, cfg, packed=True, router="softmax", ep_ranks=1, a8=False):
         import numpy as np
         import torch
         from routing_grouped_expert_router_amd import binding as B
@@ -118,7 +121,10 @@ class Setup:
             sb = generate.make_score_bias(cfg)
             self.grouped = dict(GROUPED_ROUTER, score_bias=sb.numpy())
             gr = B.GroupedRouter(score_bias=sb.cuda(), **GROUPED_ROUTER)
-        self.layer = B.MoELayer(self.d, self.w, self.wr, self.bias, l2p, rc, "cuda", router=gr, ep=ep)
+        if a8 and cfg.w_dtype != "fp8":
+            raise SystemExit("--a8 needs an fp8-weight workload")
+        self.a8 = a8
+        self.layer = B.MoELayer(self.d, self.w, self.wr, self.bias, l2p, rc, "cuda", router=gr, ep=ep, a8=a8)
         self.B = B
         torch.cuda.synchronize()
 
@@ -131,6 +137,17 @@ class Setup:
             B.moe_route(d, L.logits, T, L.rt, L.ws, L.l2p, L.rcount)
         else:
             B.moe_route_grouped(d, L.logits, T, L.rt, L.ws, L.router, L.l2p, L.rcount)
+        if self.a8:
+            B.moe_quantize_1x128(self.x, T, L.xq, L.xs)
+            if ev is not None:
+                ev[0].record()
+            B.moe_expert_gate_up_a8(d, L.weights, L.rt, T, L.xq, L.xs, L.h)
+            if ev is not None:
+                ev[1].record()
+            B.moe_quantize_1x128(L.h, B.buffer_rows(d), L.hq, L.hs)
+            B.moe_expert_down_a8(d, L.weights, L.rt, T, L.hq, L.hs, L.y)
+            B.moe_combine(d, L.rt, T, L.y, L.out)
+            return
         gather = d.act_dtype == B.MOE_BF16     # the gate/up kernel gathers rows from x itself
         if not gather:
             B.moe_permute(d, self.x, T, L.rt, L.xg)
@@ -172,12 +189,12 @@ class Setup:
         return slots, routed, gu, total
 
 
-def time_workload(cfg, steps, warmup, packed=True, router="softmax", ep_ranks=1):
+def time_workload(cfg, steps, warmup, packed=True, router="softmax", ep_ranks=1, a8=False):
     """Eager steps (HIP events around the gate/up kernel on the launch
     stream), then the same step captured once in a HIP graph and replayed
     ``steps`` times (the layer latency reported)."""
     import torch
-    s = Setup(cfg, packed, router, ep_ranks)
+    s = Setup(cfg, packed, router, ep_ranks, a8)
     cfg = s.cfg
     for _ in range(warmup):
         s.step()
@@ -298,8 +315,13 @@ def cpu_baseline(s, budget_s=30.0):
     while True:
         toks = np.arange(0, T, max(1, T // n))[:n]
         t0 = time.perf_counter()
-        oracle_forward(inp, tokens=toks, grouped=s.grouped, local_of=s.local_of,
-                       E_local=None if s.local_of is None else cfg.E_phys)
+        if s.a8:
+            from oracle_adapt import oracle_forward_w8a8
+            oracle_forward_w8a8(inp, tokens=toks, local_of=s.local_of,
+                                E_local=None if s.local_of is None else cfg.E_phys)
+        else:
+            oracle_forward(inp, tokens=toks, grouped=s.grouped, local_of=s.local_of,
+                           E_local=None if s.local_of is None else cfg.E_phys)
         dt = time.perf_counter() - t0
         print(f"# cpu reference: {len(toks)} of {T} tokens in {dt:.1f} s", file=sys.stderr, flush=True)
         if n >= T or dt * 4 > budget_s:
@@ -340,7 +362,7 @@ def main():
     for n in names:
         c = configs.by_name(n)
         r = time_workload(c, args.steps, args.warmup, packed=not args.row_major,
-                          router=args.router, ep_ranks=args.ep_ranks)
+                          router=args.router, ep_ranks=args.ep_ranks, a8=args.a8)
         results[n] = r
         print(f"# {n}: {r['ms']*1e3:.1f} us/layer (graph), {r['eager_ms']*1e3:.1f} eager, "
               f"gate/up {r['gu_ms']*1e3:.1f} us ({r['gu_flops']/(r['gu_ms']*1e-3)/1e12:.0f} TFLOP/s), "
@@ -370,7 +392,9 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.w_dtype == "bf16" else "fp8-e4m3-b128 weights, bf16 activations",
+        "dtype": "bf16" if cfg.w_dtype == "bf16" else (
+            "fp8-e4m3-b128 weights, fp8-e4m3 1x128 activations (W8A8)" if args.a8
+            else "fp8-e4m3-b128 weights, bf16 activations"),
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
                    "E_phys": cfg.E_phys, "K": cfg.K, "n_shared": cfg.n_shared,

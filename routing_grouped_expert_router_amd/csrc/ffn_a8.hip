@@ -74,11 +74,10 @@ hipError_t launch_quant_1x128(const QuantArgs& a, hipStream_t s) {
 }
 
 template <int MODE, int MT, bool PACKED>
-__global__ __launch_bounds__(256) void ffn_a8_kernel(A8Args a) {
+__device__ __forceinline__ void ffn_a8_body(const A8Args& a, int g, bool big_class) {
   constexpr bool GU = MODE == MODE_GATEUP;
   // register stages (NB - 1 steps in flight), as many as the registers allow
   constexpr int NB = MT == 1 ? (GU ? 4 : 8) : 3;
-  const int g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: weight scales load as scalars
   const bool shared = g == a.E_phys;
@@ -93,7 +92,7 @@ __global__ __launch_bounds__(256) void ffn_a8_kernel(A8Args a) {
     s0 = a.pad_off[g]; c0 = a.counts[g];
   }
   const int R = c0 + c1;
-  if (R <= a.min_rows || R > a.max_rows) return;   // the other launch's class
+  if (R <= 0 || (big_class ? R <= 16 : R > 16)) return;   // the other class's group
   const int N = a.N, Kdim = a.Kdim;
   const int nkb = Kdim / 128;
   const int kper = nkb / a.ksplit;
@@ -207,25 +206,39 @@ __global__ __launch_bounds__(256) void ffn_a8_kernel(A8Args a) {
   }
 }
 
-template <int MODE, int MT>
-static void launch_a8_mt(const A8Args& a, int packed, dim3 grid, hipStream_t s) {
-  if (packed) hipLaunchKernelGGL((ffn_a8_kernel<MODE, MT, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((ffn_a8_kernel<MODE, MT, false>), grid, dim3(256), 0, s, a);
+// One launch: groups of up to 16 rows take one tile per pass (the deeper
+// load pipeline), larger ones four; the large-group workgroups come first in
+// the grid (grid.y row 0 .. n_big-1 re-reads group ids from the top) so that
+// their longer streams start early.  BIG = false: every group takes the
+// one-tile path (T <= 16, no group can be larger).
+template <int MODE, bool PACKED, bool BIG>
+__global__ __launch_bounds__(256) void ffn_a8_kernel(A8Args a) {
+  if constexpr (BIG) {
+    const int groups = a.E_phys + a.n_shared;
+    if ((int)blockIdx.y < groups) { ffn_a8_body<MODE, 4, PACKED>(a, blockIdx.y, true); return; }
+    ffn_a8_body<MODE, 1, PACKED>(a, blockIdx.y - groups, false);
+  } else {
+    ffn_a8_body<MODE, 1, PACKED>(a, blockIdx.y, false);
+  }
 }
 
-// Two launches split the groups by row count: up to 16 rows one tile per
-// pass (deeper load pipeline), larger groups four tiles per pass.
-hipError_t launch_ffn_a8(const A8Args& a0, int packed, int mode, hipStream_t s) {
-  if (a0.N % 64 || a0.Kdim % 128 || (a0.Kdim / 128) % a0.ksplit) return hipErrorInvalidValue;
-  const dim3 grid(a0.N / 64, a0.E_phys + a0.n_shared, a0.ksplit);
-  A8Args a = a0;
-  a.min_rows = 0; a.max_rows = 16;
-  if (mode == MODE_GATEUP) launch_a8_mt<MODE_GATEUP, 1>(a, packed, grid, s);
-  else launch_a8_mt<MODE_DOWN, 1>(a, packed, grid, s);
-  if (a0.T > 16) {
-    a.min_rows = 16; a.max_rows = 0x7fffffff;
-    if (mode == MODE_GATEUP) launch_a8_mt<MODE_GATEUP, 4>(a, packed, grid, s);
-    else launch_a8_mt<MODE_DOWN, 4>(a, packed, grid, s);
+template <int MODE, bool BIG>
+static void launch_a8_big(const A8Args& a, int packed, dim3 grid, hipStream_t s) {
+  if (packed) hipLaunchKernelGGL((ffn_a8_kernel<MODE, true, BIG>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((ffn_a8_kernel<MODE, false, BIG>), grid, dim3(256), 0, s, a);
+}
+
+hipError_t launch_ffn_a8(const A8Args& a, int packed, int mode, hipStream_t s) {
+  if (a.N % 64 || a.Kdim % 128 || (a.Kdim / 128) % a.ksplit) return hipErrorInvalidValue;
+  const int groups = a.E_phys + a.n_shared;
+  const bool big = a.T > 16;
+  const dim3 grid(a.N / 64, big ? 2 * groups : groups, a.ksplit);
+  if (mode == MODE_GATEUP) {
+    if (big) launch_a8_big<MODE_GATEUP, true>(a, packed, grid, s);
+    else launch_a8_big<MODE_GATEUP, false>(a, packed, grid, s);
+  } else {
+    if (big) launch_a8_big<MODE_DOWN, true>(a, packed, grid, s);
+    else launch_a8_big<MODE_DOWN, false>(a, packed, grid, s);
   }
   return hipGetLastError();
 }

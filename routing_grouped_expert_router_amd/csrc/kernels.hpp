@@ -136,7 +136,6 @@ struct A8Args {
   const uint8_t* W; const uint8_t* W3; const float* S; const float* S3;        // routed
   const uint8_t* SW; const uint8_t* SW3; const float* SS; const float* SS3;    // shared
   void* out; int64_t ldo; int64_t split_stride; int out_f32; int ksplit;
-  int min_rows, max_rows;                           // set by the launcher
 };
 hipError_t launch_ffn_a8(const A8Args& a, int packed, int mode, hipStream_t s);
 
