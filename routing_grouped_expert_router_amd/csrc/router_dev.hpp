@@ -1,0 +1,138 @@
+// Device functions of the router-logits kernels, shared with the persistent
+// decode kernel.  The method is described in router.hip.
+#pragma once
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+// Logits of token t for experts ey*EB .. ey*EB + EB - 1 by one 256-thread
+// workgroup.  Each expert's sum runs in the same order for every EB.
+template <bool XF32, int EB>
+__device__ __forceinline__ void router_small_item(const RouterArgs& a, int t, int ey) {
+  __shared__ float red[4][EB];
+  const int eb = ey * EB;                      // first expert of this workgroup
+  const int ne = min(EB, a.E - eb);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float part[EB];
+#pragma unroll
+  for (int e = 0; e < EB; ++e) part[e] = 0.f;
+  for (int h0 = tid * 8; h0 < a.H; h0 += 256 * 8) {
+    float xv[8];
+    if (XF32) {
+      const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + (int64_t)t * a.H + h0);
+      const f32x4 lo = p[0], hi = p[1];
+      xv[0] = lo.x; xv[1] = lo.y; xv[2] = lo.z; xv[3] = lo.w;
+      xv[4] = hi.x; xv[5] = hi.y; xv[6] = hi.z; xv[7] = hi.w;
+    } else {
+      const u32x4 u = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) + (int64_t)t * a.H + h0);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { xv[2 * q] = __uint_as_float(w[q] << 16); xv[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u); }
+    }
+    // every W_r load is issued (rows past E re-read the last row, their sums
+    // are never stored), so none waits behind a branch
+#pragma unroll
+    for (int e = 0; e < EB; ++e) {
+      const u32x4 u = *reinterpret_cast<const u32x4*>(a.w + (int64_t)(eb + min(e, ne - 1)) * a.H + h0);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      float s = part[e];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        s += xv[2 * q] * __uint_as_float(w[q] << 16);
+        s += xv[2 * q + 1] * __uint_as_float(w[q] & 0xffff0000u);
+      }
+      part[e] = s;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EB; ++e) {
+    float v = part[e];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    if (lane == 0) red[wave][e] = v;
+  }
+  __syncthreads();
+  if (tid < ne) {
+    const float v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    a.logits[(int64_t)t * a.E + eb + tid] = v + (a.bias ? a.bias[eb + tid] : 0.f);
+  }
+}
+
+constexpr int kRouterWaves = 16;   // H slices of the MFMA router (one per wave)
+
+// Slice `slice` (of kRouterWaves) of H for experts e0 .. e0+15 and tokens
+// t0 .. t0 + 16*MR - 1, summed from zero in 64-wide chunks by one wave with
+// v_mfma_f32_16x16x32_bf16; lane l returns experts e0 + 4*(l/16) + j of
+// token t0 + 16*m + l%16 in acc[m][j].
+template <int MR>
+__device__ __forceinline__ void router_mfma_slice(const RouterArgs& a, int e0, int t0, int slice, f32x4* acc) {
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int erow = e0 + lr;
+  const bool eok = erow < a.E;
+  const uint16_t* wrow = a.w + (int64_t)(eok ? erow : 0) * a.H;
+  const uint16_t* xrow[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const int t = t0 + 16 * m + lr;
+    xrow[m] = static_cast<const uint16_t*>(a.x) + (int64_t)(t < a.T ? t : 0) * a.H;
+  }
+  const int kw = a.H / kRouterWaves;          // multiple of 64 (H % 1024 == 0)
+  const int kbeg = slice * kw;
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = f32x4{0, 0, 0, 0};
+  u32x4 wc[2], xc[MR][2];
+  auto load = [&](int k0, u32x4* wv, u32x4 (*xv)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int k = k0 + 32 * j + 8 * lg;
+      // rows past E or T read row 0; their results are never written
+      wv[j] = *reinterpret_cast<const u32x4*>(wrow + k);
+#pragma unroll
+      for (int m = 0; m < MR; ++m) xv[m][j] = *reinterpret_cast<const u32x4*>(xrow[m] + k);
+    }
+  };
+  load(kbeg, wc, xc);
+  for (int k0 = kbeg; k0 < kbeg + kw; k0 += 64) {
+    u32x4 wn[2], xn[MR][2];
+    const bool more = k0 + 64 < kbeg + kw;
+    if (more) load(k0 + 64, wn, xn);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+        acc[m] = mfma16x16x32(__builtin_bit_cast(bf16x8, wc[j]), __builtin_bit_cast(bf16x8, xc[m][j]), acc[m]);
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        wc[j] = wn[j];
+#pragma unroll
+        for (int m = 0; m < MR; ++m) xc[m][j] = xn[m][j];
+      }
+    }
+  }
+}
+
+// The kRouterWaves slice sums red[0..15][m][l], added in slice order, stored
+// with the bias (threads tid < 64*MR).
+template <int MR>
+__device__ __forceinline__ void router_mfma_store(const RouterArgs& a, int e0, int t0, const f32x4 (*red)[MR][64]) {
+  const int tid = threadIdx.x;
+  if (tid < 64 * MR) {
+    const int m = tid >> 6, l = tid & 63;
+    f32x4 s = red[0][m][l];
+    for (int w = 1; w < kRouterWaves; ++w) s += red[w][m][l];
+    const int t = t0 + 16 * m + (l & 15);
+    if (t < a.T) {
+      const float v[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = e0 + 4 * (l >> 4) + j;
+        if (e < a.E) a.logits[(int64_t)t * a.E + e] = v[j] + (a.bias ? a.bias[e] : 0.f);
+      }
+    }
+  }
+}
+
+}  // namespace moe
