@@ -84,6 +84,11 @@ typedef enum {
 #define MOE_STATUS_RECV_OVERFLOW 32u /* moe_route_received: a count outside
                                       [0, M_max]; only min(count, M_max) rows
                                       of that slot are computed */
+#define MOE_STATUS_SYNC_TIMEOUT 64u /* moe_decode_fused: a grid-barrier wait
+                                      exceeded its bound (the grid was not
+                                      resident at once); the call's outputs
+                                      are incomplete and its fused workspace
+                                      must be zero-filled again */
 
 /* Layer description (host struct, copied by value into every call). */
 typedef struct {
@@ -402,6 +407,39 @@ moe_status_t moe_forward(const moe_desc_t* d, const void* x, const void* w_route
                          const moe_weights_t* w, int32_t T, float* logits,
                          const moe_route_t* r, void* ws, size_t ws_bytes,
                          void* xg, void* h, void* y, void* out, hipStream_t stream);
+
+/* Bytes of the fused workspace moe_decode_fused needs: grid-barrier words and
+ * the list of slots with tokens (0 if the descriptor is invalid). */
+size_t moe_decode_fused_workspace_bytes(const moe_desc_t* d);
+
+/* The whole decode layer (router logits, routing, gate/up, down, combine) in
+ * ONE persistent launch, for T <= 16 tokens: every buffer is the caller's and
+ * preallocated, so the call can be recorded into a graph and replayed (the
+ * low-latency decode path on fixed buffers: "推理 INFRA 方法论(5)", DeepEP
+ * section; vllbc blog, Table 4-2).  Outputs -- logits, the route tables, h, y
+ * and out -- are bit-identical to moe_router_logits, moe_route (g NULL) or
+ * moe_route_grouped (g given), moe_grouped_ffn_x and moe_combine called with
+ * the same arguments.
+ *   x [T, H] bf16, w_router [E, H] bf16, bias [E] fp32 or NULL, g, l2p and
+ *   replica_count as moe_route_grouped, w as moe_grouped_ffn, logits
+ *   [T_max, E] fp32, r / ws / ws_bytes as moe_route, h [moe_buffer_rows, I]
+ *   bf16, y moe_y_bytes(d, T), out [T, H] bf16: all device memory.
+ *   fws: device, fws_bytes >= moe_decode_fused_workspace_bytes(d); zero-filled
+ *   by the caller before the first call (and after a call whose status word
+ *   has MOE_STATUS_SYNC_TIMEOUT), then left alone: each call leaves it ready
+ *   for the next.  Calls that may overlap need workspaces of their own.
+ * Requires bf16 activations and packed weights (w_packed = 1), and E <= 512
+ * (softmax) or E <= 256 (grouped router); else MOE_ERR_UNSUPPORTED, as for
+ * T > 16.  The launch holds every compute unit of the device until it ends;
+ * its workgroups wait for one another, with each wait bounded (about a
+ * second), so work on other streams can only delay it. */
+moe_status_t moe_decode_fused(const moe_desc_t* d, const void* x, const void* w_router,
+                              const float* bias, const moe_grouped_router_t* g,
+                              const int32_t* l2p, const int32_t* replica_count,
+                              const moe_weights_t* w, int32_t T, float* logits,
+                              const moe_route_t* r, void* ws, size_t ws_bytes, void* h,
+                              void* y, void* out, void* fws, size_t fws_bytes,
+                              hipStream_t stream);
 
 /* ---- weight layout ------------------------------------------------------ */
 

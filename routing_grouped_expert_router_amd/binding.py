@@ -20,7 +20,7 @@ MOE_OK, MOE_ERR_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range
 MOE_F32, MOE_BF16, MOE_FP8E4M3_B128 = 0, 1, 2
 MOE_CONTIG, MOE_MASKED = 0, 1
 MOE_STATUS_SPILL, MOE_STATUS_BAD_REPLICA, MOE_STATUS_NONFINITE, MOE_STATUS_INTERNAL = 1, 2, 4, 8
-MOE_STATUS_BAD_EP_MAP, MOE_STATUS_RECV_OVERFLOW = 16, 32
+MOE_STATUS_BAD_EP_MAP, MOE_STATUS_RECV_OVERFLOW, MOE_STATUS_SYNC_TIMEOUT = 16, 32, 64
 MOE_EP_LINEAR, MOE_EP_ROUND_ROBIN = 0, 1
 
 EXPORTED = [
@@ -31,7 +31,7 @@ EXPORTED = [
     "moe_grouped_ffn", "moe_grouped_ffn_x", "moe_combine", "moe_forward", "moe_pack_weights",
     "moe_replica_map_from_p2l", "moe_route_ep", "moe_route_received", "moe_ep_local_map",
     "moe_eplb_plan", "moe_quantize_1x128", "moe_expert_gate_up_a8", "moe_expert_down_a8",
-    "moe_grouped_ffn_a8",
+    "moe_grouped_ffn_a8", "moe_decode_fused_workspace_bytes", "moe_decode_fused",
 ]
 
 
@@ -111,6 +111,9 @@ def lib() -> ctypes.CDLL:
             "moe_expert_gate_up_a8": (ctypes.c_int, [D, W, R, i32, _P, _P, _P, _P]),
             "moe_expert_down_a8": (ctypes.c_int, [D, W, R, i32, _P, _P, _P, _P]),
             "moe_grouped_ffn_a8": (ctypes.c_int, [D, W, R, i32, _P, _P, _P, _P, _P, _P, _P, _P]),
+            "moe_decode_fused_workspace_bytes": (sz, [D]),
+            "moe_decode_fused": (ctypes.c_int, [D, _P, _P, _P, GR, _P, _P, W, i32, _P, R, _P, sz, _P, _P,
+                                                _P, _P, sz, _P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -394,6 +397,23 @@ def moe_replica_map_from_p2l(p2l, E: int, max_replicas: int):
     return l2p, cnt
 
 
+def moe_decode_fused_workspace_bytes(d: Desc) -> int:
+    return int(lib().moe_decode_fused_workspace_bytes(ctypes.byref(d.c())))
+
+
+def moe_decode_fused(d: Desc, x, w_router, bias, T, logits, rt: RouteTables, ws, w: Weights, h, y, out, fws,
+                     router: "GroupedRouter | None" = None, l2p=None, replica_count=None, stream=None):
+    """The whole decode layer in one launch (T <= 16); ``fws`` is a device
+    uint8 tensor of moe_decode_fused_workspace_bytes(d) bytes, zero-filled
+    once before the first call."""
+    _check(lib().moe_decode_fused(ctypes.byref(d.c()), _ptr(x), _ptr(w_router), _ptr(bias),
+                                  ctypes.byref(router.c) if router is not None else None, _ptr(l2p),
+                                  _ptr(replica_count), ctypes.byref(w.c), T, _ptr(logits), ctypes.byref(rt.c),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _ptr(h), _ptr(y), _ptr(out),
+                                  _ptr(fws), fws.numel() * fws.element_size(), _stream(stream)),
+           "moe_decode_fused")
+
+
 class MoELayer:
     """One layer's device buffers and the C calls in order.  Weights are a
     dict of device tensors as produced for the C ABI layout
@@ -429,6 +449,8 @@ class MoELayer:
         self.weights = Weights(routed, shared)
         odt = torch.float32 if d.act_dtype == MOE_F32 else torch.bfloat16
         self.out = torch.zeros((max(1, d.T_max), d.H), dtype=odt, device=device)
+        # fused decode workspace: zero-filled once, then kept by every call
+        self.fws = torch.zeros(moe_decode_fused_workspace_bytes(d), dtype=torch.uint8, device=device)
         if a8:
             T1 = max(1, d.T_max)
             self.xq = torch.zeros((T1, d.H), dtype=torch.uint8, device=device)
@@ -465,4 +487,12 @@ class MoELayer:
             moe_permute(d, x, T, self.rt, self.xg, stream)
             moe_grouped_ffn(d, self.weights, self.rt, T, self.xg, self.h, self.y, stream)
         moe_combine(d, self.rt, T, self.y, self.out, stream)
+        return self.out[:T]
+
+    def forward_fused(self, x, T=None, stream=None):
+        """The same layer in one persistent launch (moe_decode_fused): bf16
+        activations, packed weights, T <= 16.  Returns the output view [T, H]."""
+        T = x.shape[0] if T is None else T
+        moe_decode_fused(self.d, x, self.w_router, self.bias, T, self.logits, self.rt, self.ws, self.weights,
+                         self.h, self.y, self.out, self.fws, self.router, self.l2p, self.rcount, stream)
         return self.out[:T]

@@ -145,5 +145,21 @@ struct RouterArgs {
   const void* x; int x_f32; const uint16_t* w; const float* bias; int T, E, H; float* logits;
 };
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
+bool router_uses_mfma(int E, int H, int x_f32);
+
+// ---- persistent single-launch decode layer --------------------------------------
+
+struct FusedArgs {
+  RouterArgs router; int router_mfma;   // logits phase (bf16 x)
+  RouteArgs route; int route_variant;   // select shape: decode_fused_variant(E, grouped)
+  StreamArgs g1, g2;                    // gate/up (gathering from x) and down, nblk = 1
+  CombineArgs comb;
+  uint32_t* sync;                       // barrier words (3 lines of 64), zero-filled once
+  int32_t* act;                         // [1 + E_phys] slots with tokens
+  int grid, spin_limit;                 // set by the launcher
+};
+// -1: E (or the grouped router's E) too large for the single-workgroup route
+int decode_fused_variant(int E, int grouped);
+hipError_t launch_decode_fused(FusedArgs f, int fp8, hipStream_t s);
 
 }  // namespace moe

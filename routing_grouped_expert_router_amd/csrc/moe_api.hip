@@ -53,6 +53,9 @@ bool route_ptrs_ok(const moe_desc_t* d, const moe_route_t* r) {
   return r->pad_off != nullptr;
 }
 
+constexpr size_t kFusedSyncBytes = 768;   // three 256-byte lines of barrier words
+constexpr int kFusedMaxTokens = 16;
+
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Row tiles held in registers per pass of the streaming GEMM for the bulk of
@@ -149,9 +152,10 @@ moe_status_t moe_router_logits(const moe_desc_t* d, const void* x, const void* w
 
 namespace {
 
-moe_status_t route_impl(const moe_desc_t* d, const float* logits, int32_t T, const moe_grouped_router_t* g,
+// Checks the routing arguments and fills the kernels' view of them.
+moe_status_t route_args(const moe_desc_t* d, const float* logits, int32_t T, const moe_grouped_router_t* g,
                         const moe_ep_map_t* ep, const int32_t* l2p, const int32_t* replica_count,
-                        const moe_route_t* r, void* ws, size_t ws_bytes, hipStream_t stream) {
+                        const moe_route_t* r, void* ws, size_t ws_bytes, RouteArgs& a) {
   moe_status_t st = moe_check_desc(d);
   if (st != MOE_OK) return st;
   if (ep) {
@@ -176,7 +180,7 @@ moe_status_t route_impl(const moe_desc_t* d, const float* logits, int32_t T, con
   const WsLayout wl = ws_layout(d);
   if (!ws || ws_bytes < wl.total) return MOE_ERR_WORKSPACE;
   char* base = static_cast<char*>(ws);
-  RouteArgs a = {};
+  a = RouteArgs{};
   a.logits = logits; a.T = T; a.E = d->E; a.E_phys = d->E_phys; a.K = d->K;
   a.l2p = l2p; a.rcount = replica_count; a.max_replicas = d->max_replicas;
   if (ep) { a.local_of = ep->local_of; a.n_global = ep->n_global; }
@@ -195,6 +199,15 @@ moe_status_t route_impl(const moe_desc_t* d, const float* logits, int32_t T, con
     a.grouped = 1; a.n_group = g->n_group; a.topk_group = g->topk_group; a.group_k = g->group_k;
     a.renormalize = g->renormalize; a.score_bias = g->score_bias; a.scale = g->scale;
   }
+  return MOE_OK;
+}
+
+moe_status_t route_impl(const moe_desc_t* d, const float* logits, int32_t T, const moe_grouped_router_t* g,
+                        const moe_ep_map_t* ep, const int32_t* l2p, const int32_t* replica_count,
+                        const moe_route_t* r, void* ws, size_t ws_bytes, hipStream_t stream) {
+  RouteArgs a;
+  const moe_status_t st = route_args(d, logits, T, g, ep, l2p, replica_count, r, ws, ws_bytes, a);
+  if (st != MOE_OK) return st;
   return hip_status(launch_route(a, stream));
 }
 
@@ -353,6 +366,39 @@ StreamArgs ffn_base_args(const moe_desc_t* d, const moe_route_t* r, int32_t T) {
   return a;
 }
 
+StreamArgs gate_up_args(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r, int32_t T,
+                        const void* X, bool gather, void* h) {
+  StreamArgs g1 = ffn_base_args(d, r, T);
+  g1.X = static_cast<const uint16_t*>(X); g1.ldx = d->H; g1.Kdim = d->H; g1.N = d->I;
+  if (gather) { g1.gather_src = r->src_of; g1.gather_off = r->offsets; }
+  g1.W = w->w1; g1.W3 = w->w3; g1.S = w->s1; g1.S3 = w->s3;
+  g1.SW = w->sw1; g1.SW3 = w->sw3; g1.SS = w->ss1; g1.SS3 = w->ss3;
+  g1.out = h; g1.ldo = d->I;
+  return g1;
+}
+
+StreamArgs down_args(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r, int32_t T,
+                     const void* h, void* y) {
+  const int splits = moe_down_splits(d, T);
+  StreamArgs g2 = ffn_base_args(d, r, T);
+  g2.X = static_cast<const uint16_t*>(h); g2.ldx = d->I; g2.Kdim = d->I; g2.N = d->H;
+  g2.W = w->w2; g2.S = w->s2; g2.SW = w->sw2; g2.SS = w->ss2;
+  g2.out = y; g2.ldo = d->H; g2.ksplit = splits; g2.out_f32 = splits > 1;
+  g2.split_stride = moe_buffer_rows(d) * d->H;
+  return g2;
+}
+
+CombineArgs combine_args(const moe_desc_t* d, const moe_route_t* r, int32_t T, const void* y, void* out) {
+  const int splits = moe_down_splits(d, T);
+  CombineArgs a = {};
+  a.y = y; a.y_f32 = splits > 1; a.splits = splits; a.split_stride = moe_buffer_rows(d) * d->H;
+  a.T = T; a.K = d->K; a.H = d->H; a.rows = moe_buffer_rows(d);
+  a.slot_of = r->slot_of; a.topk_w = r->topk_w;
+  a.n_shared = d->n_shared; a.shared_base = routed_cap(d);
+  a.out = out; a.out_f32 = d->act_dtype == MOE_F32;
+  return a;
+}
+
 // gate/up from the grouped buffer (gather = false: X = xg, by slot) or
 // straight from the layer input (gather = true: X = x, by token)
 moe_status_t gate_up_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_route_t* r,
@@ -365,12 +411,7 @@ moe_status_t gate_up_impl(const moe_desc_t* d, const moe_weights_t* w, const moe
   if (!X || !h || !w->w1 || !w->w3) return MOE_ERR_ARG;
   if (fp8 && (!w->s1 || !w->s3)) return MOE_ERR_ARG;
   if (d->n_shared && (!w->sw1 || !w->sw3)) return MOE_ERR_ARG;
-  StreamArgs g1 = ffn_base_args(d, r, T);
-  g1.X = static_cast<const uint16_t*>(X); g1.ldx = d->H; g1.Kdim = d->H; g1.N = d->I;
-  if (gather) { g1.gather_src = r->src_of; g1.gather_off = r->offsets; }
-  g1.W = w->w1; g1.W3 = w->w3; g1.S = w->s1; g1.S3 = w->s3;
-  g1.SW = w->sw1; g1.SW3 = w->sw3; g1.SS = w->ss1; g1.SS3 = w->ss3;
-  g1.out = h; g1.ldo = d->I;
+  const StreamArgs g1 = gate_up_args(d, w, r, T, X, gather, h);
   return launch_expert_gemm(d, r, T, g1, fp8, MODE_GATEUP, dim3(d->I / 64, d->E_phys + d->n_shared, 1),
                             stream);
 }
@@ -398,13 +439,8 @@ moe_status_t moe_expert_down(const moe_desc_t* d, const moe_weights_t* w, const 
   if (!h || !y || !w->w2) return MOE_ERR_ARG;
   if (fp8 && !w->s2) return MOE_ERR_ARG;
   if (d->n_shared && !w->sw2) return MOE_ERR_ARG;
-  const int splits = moe_down_splits(d, T);
-  StreamArgs g2 = ffn_base_args(d, r, T);
-  g2.X = static_cast<const uint16_t*>(h); g2.ldx = d->I; g2.Kdim = d->I; g2.N = d->H;
-  g2.W = w->w2; g2.S = w->s2; g2.SW = w->sw2; g2.SS = w->ss2;
-  g2.out = y; g2.ldo = d->H; g2.ksplit = splits; g2.out_f32 = splits > 1;
-  g2.split_stride = moe_buffer_rows(d) * d->H;
-  return launch_expert_gemm(d, r, T, g2, fp8, MODE_DOWN, dim3(d->H / 64, d->E_phys + d->n_shared, splits),
+  const StreamArgs g2 = down_args(d, w, r, T, h, y);
+  return launch_expert_gemm(d, r, T, g2, fp8, MODE_DOWN, dim3(d->H / 64, d->E_phys + d->n_shared, g2.ksplit),
                             stream);
 }
 
@@ -519,14 +555,7 @@ moe_status_t moe_combine(const moe_desc_t* d, const moe_route_t* r, int32_t T, c
   if (T < 0 || T > d->T_max || !route_ptrs_ok(d, r)) return MOE_ERR_ARG;
   if (T == 0) return MOE_OK;
   if (!y || !out) return MOE_ERR_ARG;
-  const int splits = moe_down_splits(d, T);
-  CombineArgs a = {};
-  a.y = y; a.y_f32 = splits > 1; a.splits = splits; a.split_stride = moe_buffer_rows(d) * d->H;
-  a.T = T; a.K = d->K; a.H = d->H; a.rows = moe_buffer_rows(d);
-  a.slot_of = r->slot_of; a.topk_w = r->topk_w;
-  a.n_shared = d->n_shared; a.shared_base = routed_cap(d);
-  a.out = out; a.out_f32 = d->act_dtype == MOE_F32;
-  return hip_status(launch_combine(a, stream));
+  return hip_status(launch_combine(combine_args(d, r, T, y, out), stream));
 }
 
 moe_status_t moe_forward(const moe_desc_t* d, const void* x, const void* w_router,
@@ -548,6 +577,48 @@ moe_status_t moe_forward(const moe_desc_t* d, const void* x, const void* w_route
   }
   if (st != MOE_OK) return st;
   return moe_combine(d, r, T, y, out, stream);
+}
+
+size_t moe_decode_fused_workspace_bytes(const moe_desc_t* d) {
+  if (moe_check_desc(d) != MOE_OK) return 0;
+  const size_t act = sizeof(int32_t) * (1 + (size_t)d->E_phys);
+  return kFusedSyncBytes + (act + 255) / 256 * 256;
+}
+
+moe_status_t moe_decode_fused(const moe_desc_t* d, const void* x, const void* w_router, const float* bias,
+                              const moe_grouped_router_t* g, const int32_t* l2p,
+                              const int32_t* replica_count, const moe_weights_t* w, int32_t T,
+                              float* logits, const moe_route_t* r, void* ws, size_t ws_bytes, void* h,
+                              void* y, void* out, void* fws, size_t fws_bytes, hipStream_t stream) {
+  moe_status_t st = moe_check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->act_dtype != MOE_BF16 || d->w_packed != 1) return MOE_ERR_UNSUPPORTED;
+  if (T < 0 || T > d->T_max) return MOE_ERR_ARG;
+  if (T > kFusedMaxTokens) return MOE_ERR_UNSUPPORTED;
+  if (!x || !w_router || !logits || !h || !y || !out || !fws) return MOE_ERR_ARG;
+  RouteArgs ra;
+  st = route_args(d, logits, T, g, nullptr, l2p, replica_count, r, ws, ws_bytes, ra);
+  if (st != MOE_OK) return st;
+  st = ffn_common_checks(d, w, r, T);
+  if (st != MOE_OK) return st;
+  const bool fp8 = d->w_dtype == MOE_FP8E4M3_B128;
+  if (!w->w1 || !w->w3 || !w->w2) return MOE_ERR_ARG;
+  if (fp8 && (!w->s1 || !w->s3 || !w->s2)) return MOE_ERR_ARG;
+  if (d->n_shared && (!w->sw1 || !w->sw3 || !w->sw2)) return MOE_ERR_ARG;
+  const int variant = decode_fused_variant(d->E, g != nullptr);
+  if (variant < 0) return MOE_ERR_UNSUPPORTED;
+  if (fws_bytes < moe_decode_fused_workspace_bytes(d)) return MOE_ERR_WORKSPACE;
+  FusedArgs f = {};
+  f.router = RouterArgs{x, 0, static_cast<const uint16_t*>(w_router), bias, T, d->E, d->H, logits};
+  f.router_mfma = router_uses_mfma(d->E, d->H, 0);
+  f.route = ra;
+  f.route_variant = variant;
+  f.g1 = gate_up_args(d, w, r, T, x, true, h);
+  f.g2 = down_args(d, w, r, T, h, y);
+  f.comb = combine_args(d, r, T, y, out);
+  f.sync = static_cast<uint32_t*>(fws);
+  f.act = reinterpret_cast<int32_t*>(static_cast<char*>(fws) + kFusedSyncBytes);
+  return hip_status(launch_decode_fused(f, fp8, stream));
 }
 
 moe_status_t moe_pack_weights(const moe_desc_t* d, int32_t which, int32_t G, const void* src,

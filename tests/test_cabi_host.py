@@ -112,6 +112,36 @@ def test_calls_reject_bad_arguments_before_enqueueing():
                              fake, null) == B.MOE_ERR_ARG
 
 
+def test_decode_fused_rejects_before_launch():
+    """moe_decode_fused decides every refusal on the host: activations and
+    weight layout it does not take, T above 16, null buffers, a too-small
+    fused workspace, E too large for the single-workgroup route."""
+    L = B.lib()
+    fake = ctypes.c_void_p(16)
+    rt2 = B.moe_route_t(*([fake] * len(B.moe_route_t._fields_)))
+    w = B.moe_weights_t(*([fake] * 12))
+
+    def call(d, T=4, fws_bytes=1 << 20, x=fake, g=None):
+        return L.moe_decode_fused(ctypes.byref(d.c()), x, fake, None, g, None, None, ctypes.byref(w), T, fake,
+                                  ctypes.byref(rt2), fake, 1 << 24, fake, fake, fake, fake, fws_bytes, None)
+
+    bf = _d(act_dtype=B.MOE_BF16, w_packed=1, T_max=32)
+    assert call(_d(w_packed=1)) == B.MOE_ERR_UNSUPPORTED                    # fp32 activations
+    assert call(_d(act_dtype=B.MOE_BF16)) == B.MOE_ERR_UNSUPPORTED          # row-major weights
+    assert call(bf, T=17) == B.MOE_ERR_UNSUPPORTED
+    assert call(bf, T=33) == B.MOE_ERR_ARG                                   # above T_max
+    assert call(bf, x=None) == B.MOE_ERR_ARG
+    need = L.moe_decode_fused_workspace_bytes(ctypes.byref(bf.c()))
+    assert need >= 768 + 4 * (1 + bf.E_phys)
+    assert call(bf, fws_bytes=need - 1) == B.MOE_ERR_WORKSPACE
+    big = _d(act_dtype=B.MOE_BF16, w_packed=1, E=1024, E_phys=1024, M_max=4)
+    assert call(big) == B.MOE_ERR_UNSUPPORTED                                # softmax route above E = 512
+    g = B.moe_grouped_router_t(None, 64, 8, 2, 1, 1.0)                       # E = 512 grouped
+    assert call(_d(act_dtype=B.MOE_BF16, w_packed=1, E=512, E_phys=512, M_max=4),
+                g=ctypes.byref(g)) == B.MOE_ERR_UNSUPPORTED
+    assert L.moe_decode_fused_workspace_bytes(ctypes.byref(_d(K=0).c())) == 0
+
+
 @pytest.mark.parametrize("cfg", configs.all_configs(), ids=lambda c: c.name)
 def test_buffer_sizing_formulas(cfg):
     d = B.Desc.from_config(cfg)
