@@ -162,6 +162,17 @@ class Setup:
         B.moe_expert_down(d, L.weights, L.rt, T, L.h, L.y)
         B.moe_combine(d, L.rt, T, L.y, L.out)
 
+    def fused_ok(self):
+        """The single-launch decode layer takes this step: bf16 activations,
+        packed weights, T <= 16, bf16 expert activations (not W8A8), no
+        expert-parallel map."""
+        B, d = self.B, self.d
+        return (d.act_dtype == B.MOE_BF16 and d.w_packed == 1 and self.cfg.T <= 16 and not self.a8
+                and self.layer.ep is None)
+
+    def step_fused(self):
+        self.layer.forward_fused(self.x, self.cfg.T)
+
     def gate_up_flops(self):
         """Algorithmic FLOPs of the gate/up kernel: 2 * rows * 2I * H over the
         token rows (T*K routed + n_shared*T shared); pad rows not counted."""
@@ -234,14 +245,50 @@ def time_workload(cfg, steps, warmup, packed=True, router="softmax", ep_ranks=1,
                routed_bytes=routed, gu_bytes=gu_bytes, total_bytes=total, status=status, setup=s,
                gu_flops=s.gate_up_flops(), layer_flops=s.layer_flops())
     del graph
+    if s.fused_ok():
+        res.update(time_fused(s, steps, warmup, ref))
     return res
+
+
+def time_fused(s, steps, warmup, ref):
+    """The same layer step as one persistent launch (moe_decode_fused):
+    checked bit for bit against the multi-launch step, then timed launched
+    directly and as a replayed HIP graph."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        s.step_fused()
+    torch.cuda.synchronize()
+    assert torch.equal(s.layer.out, ref), "the single-launch step differs from the multi-launch step"
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        s.step_fused()
+    end.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = start.elapsed_time(end) / steps
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        s.step_fused()
+    for _ in range(warmup):
+        graph.replay()
+    start.record(stream)
+    for _ in range(steps):
+        graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    assert torch.equal(s.layer.out, ref), "graph replay of the single-launch step differs"
+    status = int(s.layer.rt.status.item())
+    assert not status & s.B.MOE_STATUS_SYNC_TIMEOUT, "grid barrier timed out"
+    del graph
+    return dict(fused_ms=start.elapsed_time(end) / steps, fused_eager_ms=eager_ms)
 
 
 PREFILL_MIN_T = 1024   # token counts from here on are timed against the MFMA peak
 
 # sources of the decode gate/up kernel and its launch (the decode path never
 # launches the tiled kernel)
-KERNEL_SOURCES = ("common.hpp", "kernels.hpp", "ffn_stream.hip", "moe_api.hip")
+KERNEL_SOURCES = ("common.hpp", "kernels.hpp", "stream_dev.hpp", "ffn_stream.hip", "moe_api.hip")
 
 
 def kernel_sources_hash() -> str:
@@ -368,7 +415,9 @@ def main():
               f"gate/up {r['gu_ms']*1e3:.1f} us ({r['gu_flops']/(r['gu_ms']*1e-3)/1e12:.0f} TFLOP/s), "
               f"layer {r['layer_flops']/(r['ms']*1e-3)/1e12:.0f} TFLOP/s, "
               f"slots {r['slots']}, touched {r['total_bytes']/1e9:.3f} GB -> "
-              f"{r['total_bytes']/(r['ms']*1e-3)/1e9:.0f} GB/s, status {r['status']}",
+              f"{r['total_bytes']/(r['ms']*1e-3)/1e9:.0f} GB/s, status {r['status']}"
+              + (f"; single launch {r['fused_ms']*1e3:.1f} us (graph), {r['fused_eager_ms']*1e3:.1f} eager"
+                 if "fused_ms" in r else ""),
               file=sys.stderr, flush=True)
         if n != cfg.name:
             del r["setup"]
@@ -418,7 +467,9 @@ def main():
                         "eager_latency_us": round(r["eager_ms"] * 1e3, 2),
                         "gbs": round(r["total_bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
                         "gate_up_us": round(r["gu_ms"] * 1e3, 2),
-                        "touched_slots": r["slots"]} for n, r in results.items()},
+                        "touched_slots": r["slots"],
+                        "single_launch_latency_us": round(r["fused_ms"] * 1e3, 2) if "fused_ms" in r else None}
+                    for n, r in results.items()},
     }
     print(json.dumps(out), flush=True)
 

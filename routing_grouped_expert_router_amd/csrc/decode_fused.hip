@@ -1,11 +1,9 @@
 // The whole decode layer in one persistent launch on gfx950 (CDNA4): router
 // logits, routing, the expert gate/up and down projections and the combine.
 //
-// At decode sizes (T <= 16 tokens) the layer is five short launches around
-// about a hundred microseconds of weight streaming; each boundary drains the
-// chip, refills it and adds the gap between launches.  The pages' decode
-// path keeps every buffer preallocated so a step can be recorded and replayed
-// as a unit ("推理 INFRA 方法论(5)", DeepEP section: low-latency kernels on
+// At decode sizes (T <= 16 tokens) the layer is five launches around about a
+// hundred microseconds of weight streaming.  The pages' decode path keeps
+// every buffer preallocated so a step can be recorded and replayed as a unit ("推理 INFRA 方法论(5)", DeepEP section: low-latency kernels on
 // fixed buffers; vllbc blog, Table 4-2: the decode backend with graph capture
 // and the masked layout).  Here the step is one launch of G workgroups, all
 // resident at once (G = compute units x workgroups that fit on one), each
@@ -26,16 +24,20 @@
 // moe_router_logits + moe_route / moe_route_grouped + moe_grouped_ffn_x +
 // moe_combine.
 //
-// Grid barrier: an arrival counter and a generation word, on separate
-// 256-byte lines of the caller's fused workspace (zero-filled once; every
-// completed launch leaves the counter at zero).  Thread 0 of each workgroup
-// arrives with an agent-scope atomic after a release fence and spins on the
-// generation with agent-scope loads, then an acquire fence, so each phase's
-// global writes are visible to the next phase on every XCD.  Every wait is
-// bounded: a workgroup whose wait exceeds the spin limit, or that sees the
-// abort word, sets the abort word and MOE_STATUS_SYNC_TIMEOUT in the status
-// word and leaves; no item of a phase starts before the previous barrier has
+// Grid barrier (grid_sync below): arrival counters and one release flag per
+// workgroup in the caller's fused workspace (zero-filled once; every
+// completed launch leaves the counters at zero).  Outputs read by later
+// phases (logits, h, y) are stored at agent scope, past the XCD's L2, and
+// each XCD's L2 is written back once per barrier, so each phase's global
+// writes are visible to the next phase on every XCD.  Every wait is bounded:
+// a workgroup whose wait exceeds the spin limit, or that sees the abort word,
+// sets the abort word and MOE_STATUS_SYNC_TIMEOUT in the status word and
+// leaves; no item of a phase starts before the previous barrier has
 // completed, so an abort only leaves outputs unwritten.
+//
+// Measured on MI355X, this single launch is slower than the five launches
+// replayed from a HIP graph (whose launch boundaries cost about nothing):
+// a grid barrier costs ~5 us, the L2 writeback it needs stalls an XCD's L2.
 #include "combine_dev.hpp"
 #include "route_dev.hpp"
 #include "router_dev.hpp"
@@ -44,41 +46,111 @@
 namespace moe {
 
 constexpr int kFusedMaxT = 16;           // one 16-row tile per slot and pass
-constexpr int kSyncLine = 64;            // words per 256-byte line
 constexpr int kSpinLimit = 1 << 20;      // polls per wait (about a second)
 
+// The XCD this wave runs on (each XCD has its own L2).
+__device__ __forceinline__ int xcd_id() {
+  unsigned v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return (int)(v & (kFusedGroups - 1));
+}
+
+// Per-workgroup barrier state, held by thread 0: its XCD, the workgroups on
+// that XCD and the XCDs in use (known after the first barrier).
+struct BarState {
+  int xcd;
+  uint32_t xsize, nx;
+};
+
 // Returns false (in every thread of the workgroup) when the grid aborts.
-__device__ __forceinline__ bool grid_sync(const FusedArgs& f) {
-  __shared__ int go_s;
-  __threadfence();   // every wave releases its own writes of the phase
+//
+// An L2 writeback (the release half of an agent-scope fence) stalls the
+// XCD's L2 for several microseconds whatever it holds, so it is done once
+// per XCD and barrier, not once per workgroup.  Every wave first waits until
+// its own stores have reached its XCD's L2; arrival is then counted per XCD,
+// and the XCD's last arrival writes that L2 back for all of them before
+// adding the XCD to the top counter.  The first barrier, before the
+// workgroups know how many of them share an XCD, counts groups wg % 8 instead
+// and each workgroup that wrote anything writes its own L2 back.  The last
+// arrival of all resets the counters and releases every workgroup by writing
+// the new generation into each one's own flag line, so the waiting
+// workgroups poll different memory channels; polls are agent-scope relaxed
+// loads (past the L2, without invalidating it), and one acquire fence per
+// workgroup follows the wait.
+__device__ __forceinline__ bool grid_sync(const FusedArgs& f, BarState& bs, int bar, bool wrote) {
+  __shared__ int go_s, last_s;
+  __shared__ uint32_t gen_s;
+  const int wg = blockIdx.x, G = f.grid;
+  uint32_t* const top = f.sync;
+  uint32_t* const abort_w = f.sync + kFusedLine;
+  uint32_t* const flag = f.sync + kFusedFlagsOff + (size_t)wg * kFusedFlagStride;
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t* count = f.sync;
-    uint32_t* gen = f.sync + kSyncLine;
-    uint32_t* abort_w = f.sync + 2 * kSyncLine;
-    int go = 1;
-    const uint32_t g0 = __hip_atomic_load(gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t old = __hip_atomic_fetch_add(count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (old + 1u == (uint32_t)f.grid) {
-      // last arrival: reset the counter, then open the barrier
-      __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t* grp;
+    uint32_t gsize, ngroups;
+    if (bar == 0) {
+      const int ng = G < kFusedGroups ? G : kFusedGroups;
+      const int gi = wg % ng;
+      grp = f.sync + (2 + gi) * kFusedLine;
+      gsize = (uint32_t)((G - gi + ng - 1) / ng);
+      ngroups = (uint32_t)ng;
+      if (wrote) __threadfence();
     } else {
-      int n = 0;
-      while (__hip_atomic_load(gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == g0) {
-        if (__hip_atomic_load(abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u || ++n > f.spin_limit) {
-          go = 0;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
+      grp = f.sync + (2 + kFusedGroups + bs.xcd) * kFusedLine;
+      gsize = bs.xsize;
+      ngroups = bs.nx;
+    }
+    const uint32_t g0 = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int last = 0;
+    if (__hip_atomic_fetch_add(grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u == gsize) {
+      __hip_atomic_store(grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // every arrival of the group has its stores in this L2 (or, first
+      // barrier, already written back): write it back, and order the reset
+      __threadfence();
+      if (__hip_atomic_fetch_add(top, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u == ngroups) {
+        __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __threadfence();   // every group's writes acquired, the reset ordered before the flags
+        last = 1;
       }
     }
+    last_s = last;
+    gen_s = g0 + 1u;
+  }
+  __syncthreads();
+  int go = 1;
+  if (last_s) {
+    __threadfence();   // release, by every thread that writes a flag
+    for (int w = threadIdx.x; w < G; w += kThreads)
+      __hip_atomic_store(f.sync + kFusedFlagsOff + (size_t)w * kFusedFlagStride, gen_s, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  } else if (threadIdx.x == 0) {
+    const uint32_t g0 = gen_s - 1u;
+    int n = 0;
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
+      if ((++n & 63) == 0 &&
+          (__hip_atomic_load(abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u || n > f.spin_limit)) {
+        go = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(8);
+    }
+  }
+  if (threadIdx.x == 0) {
     if (go && __hip_atomic_load(abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) go = 0;
     if (!go) {
       __hip_atomic_fetch_or(abort_w, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_fetch_or(f.route.status, MOE_STATUS_SYNC_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (bar == 0) {
+      // every workgroup counted itself on its XCD before arriving
+      uint32_t* const members = f.sync + (2 + 2 * kFusedGroups) * kFusedLine;
+      bs.xsize = __hip_atomic_load(members + bs.xcd * kFusedLine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bs.nx = 0;
+      for (int x = 0; x < kFusedGroups; ++x)
+        bs.nx += __hip_atomic_load(members + x * kFusedLine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+    }
     go_s = go;
   }
   __syncthreads();
@@ -96,7 +168,7 @@ __device__ __forceinline__ void router_mfma_item4(const RouterArgs& a, int e0) {
     red[sl][0][lane] = acc[0];
   }
   __syncthreads();
-  router_mfma_store<1>(a, e0, 0, red);
+  router_mfma_store<1, true>(a, e0, 0, red);
 }
 
 // Routing by one workgroup of kThreads, then the list of slots with tokens:
@@ -147,12 +219,12 @@ __device__ __forceinline__ void route_phase(const FusedArgs& f) {
 
 template <bool FP8>
 __device__ __forceinline__ void gate_up_item(const FusedArgs& f, int g, int bx, uint16_t* xs) {
-  stream_group<FP8, MODE_GATEUP, 1, true, banks_a<FP8, MODE_GATEUP>(), true>(f.g1, g, 0, 0, 1, 0, 0, xs, bx);
+  stream_group<FP8, MODE_GATEUP, 1, true, banks_a<FP8, MODE_GATEUP>(), true, false, true>(f.g1, g, 0, 0, 1, 0, 0, xs, bx);
 }
 
 template <bool FP8>
 __device__ __forceinline__ void down_item(const FusedArgs& f, int g, int bx, int ks, uint16_t* xs) {
-  stream_group<FP8, MODE_DOWN, 1, true, banks_a<FP8, MODE_DOWN>(), true>(f.g2, g, ks, 0, 1, 0, 0, xs, bx);
+  stream_group<FP8, MODE_DOWN, 1, true, banks_a<FP8, MODE_DOWN>(), true, false, true>(f.g2, g, ks, 0, 1, 0, 0, xs, bx);
 }
 
 template <bool FP8>
@@ -161,28 +233,38 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs f) {
   const int wg = blockIdx.x, G = f.grid;
   const int T = f.route.T;
   const int P = f.route.E_phys;
+  uint32_t* const members = f.sync + (2 + 2 * kFusedGroups) * kFusedLine;
+  BarState bs{0, 0, 0};
+  if (threadIdx.x == 0) {
+    bs.xcd = xcd_id();
+    __hip_atomic_fetch_add(members + bs.xcd * kFusedLine, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   // R: router logits
+  int items = 0;
   if (T > 0 && f.router_mfma) {
     const int nb = (f.router.E + 15) / 16;
-    for (int i = wg; i < nb; i += G) {
+    for (int i = wg; i < nb; i += G, ++items) {
       router_mfma_item4(f.router, 16 * i);
       __syncthreads();
     }
   } else if (T > 0) {
     const int ne = (f.router.E + 7) / 8;
-    for (int i = wg; i < T * ne; i += G) {
-      router_small_item<false, 8>(f.router, i / ne, i % ne);
+    for (int i = wg; i < T * ne; i += G, ++items) {
+      router_small_item<false, 8, true>(f.router, i / ne, i % ne);
       __syncthreads();
     }
   }
-  if (!grid_sync(f)) return;
+  if (!grid_sync(f, bs, 0, items > 0)) return;
   // A: routing (workgroup 0); the shared expert's gate/up (the others)
   const int nbx1 = f.g1.N / kBN, nbx2 = f.g2.N / kBN, ns = f.g2.ksplit;
   const bool shared = f.route.n_shared != 0;
   if (wg == 0) route_phase(f);
   else if (shared)
     for (int i = wg - 1; i < nbx1; i += G - 1) gate_up_item<FP8>(f, P, i, xs);
-  if (!grid_sync(f)) return;
+  if (!grid_sync(f, bs, 1, true)) return;
+  // the XCD counts were read after the first barrier and are no longer needed
+  if (wg == 0 && threadIdx.x < kFusedGroups)
+    __hip_atomic_store(members + threadIdx.x * kFusedLine, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // G: routed gate/up, then the shared expert's down projection
   const int na = f.act[0];
   const int n_gu = na * nbx1;
@@ -195,13 +277,13 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs f) {
       down_item<FP8>(f, P, j % nbx2, j / nbx2, xs);
     }
   }
-  if (!grid_sync(f)) return;
+  if (!grid_sync(f, bs, 2, true)) return;
   // D: routed down projections
   for (int i = wg; i < na * nbx2 * ns; i += G) {
     const int r = i / nbx2;
     down_item<FP8>(f, f.act[1 + r % na], i % nbx2, r / na, xs);
   }
-  if (!grid_sync(f)) return;
+  if (!grid_sync(f, bs, 3, true)) return;
   // C: combine
   const int nv = f.comb.H / 8;
   const int nvc = (nv + kThreads - 1) / kThreads;
@@ -243,7 +325,7 @@ hipError_t launch_decode_fused(FusedArgs f, int fp8, hipStream_t s) {
     return hipErrorInvalidValue;
   if (f.g1.nblk != 1 || f.g2.nblk != 1 || f.g1.N % kBN || f.g2.N % kBN) return hipErrorInvalidValue;
   f.grid = decode_fused_grid(fp8);
-  if (f.grid < 2) return hipErrorInvalidConfiguration;
+  if (f.grid < 2 || f.grid > kFusedMaxGrid) return hipErrorInvalidConfiguration;
   f.spin_limit = kSpinLimit;
   if (fp8) hipLaunchKernelGGL(decode_fused_kernel<true>, dim3(f.grid), dim3(kThreads), 0, s, f);
   else hipLaunchKernelGGL(decode_fused_kernel<false>, dim3(f.grid), dim3(kThreads), 0, s, f);

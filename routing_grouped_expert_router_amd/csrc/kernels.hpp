@@ -149,12 +149,26 @@ bool router_uses_mfma(int E, int H, int x_f32);
 
 // ---- persistent single-launch decode layer --------------------------------------
 
+// Fused workspace: barrier words, then the slot list.  Lines of 64 words:
+// line 0 the top arrival counter, line 1 the abort word, lines 2..9 the
+// first barrier's arrival counters (workgroup groups wg % 8), lines 10..17
+// the later barriers' counters (one per XCD), lines 18..25 the number of
+// workgroups on each XCD, then one 128-byte release flag per workgroup
+// (kFusedMaxGrid of them), so that waiting workgroups poll different memory
+// channels.
+constexpr int kFusedMaxGrid = 2048;
+constexpr int kFusedGroups = 8;                // XCDs (and first-barrier groups)
+constexpr int kFusedLine = 64;                 // uint32 words per 256-byte line
+constexpr int kFusedFlagStride = 32;           // uint32 words per release flag (128 bytes)
+constexpr int kFusedFlagsOff = (2 + 3 * kFusedGroups) * kFusedLine;
+constexpr size_t kFusedSyncBytes = sizeof(uint32_t) * ((size_t)kFusedFlagsOff + (size_t)kFusedMaxGrid * kFusedFlagStride);
+
 struct FusedArgs {
   RouterArgs router; int router_mfma;   // logits phase (bf16 x)
   RouteArgs route; int route_variant;   // select shape: decode_fused_variant(E, grouped)
   StreamArgs g1, g2;                    // gate/up (gathering from x) and down, nblk = 1
   CombineArgs comb;
-  uint32_t* sync;                       // barrier words (3 lines of 64), zero-filled once
+  uint32_t* sync;                       // barrier words (kFusedSyncBytes), zero-filled once
   int32_t* act;                         // [1 + E_phys] slots with tokens
   int grid, spin_limit;                 // set by the launcher
 };

@@ -53,7 +53,6 @@ bool route_ptrs_ok(const moe_desc_t* d, const moe_route_t* r) {
   return r->pad_off != nullptr;
 }
 
-constexpr size_t kFusedSyncBytes = 768;   // three 256-byte lines of barrier words
 constexpr int kFusedMaxTokens = 16;
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }

@@ -8,7 +8,15 @@ namespace moe {
 
 // Logits of token t for experts ey*EB .. ey*EB + EB - 1 by one 256-thread
 // workgroup.  Each expert's sum runs in the same order for every EB.
-template <bool XF32, int EB>
+// WT: agent-scope stores (written through the XCD's L2) for a reader on
+// another XCD later in the same launch.
+template <bool WT>
+__device__ __forceinline__ void store_logit(float* p, float v) {
+  if constexpr (WT) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+
+template <bool XF32, int EB, bool WT = false>
 __device__ __forceinline__ void router_small_item(const RouterArgs& a, int t, int ey) {
   __shared__ float red[4][EB];
   const int eb = ey * EB;                      // first expert of this workgroup
@@ -55,7 +63,7 @@ __device__ __forceinline__ void router_small_item(const RouterArgs& a, int t, in
   __syncthreads();
   if (tid < ne) {
     const float v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
-    a.logits[(int64_t)t * a.E + eb + tid] = v + (a.bias ? a.bias[eb + tid] : 0.f);
+    store_logit<WT>(a.logits + (int64_t)t * a.E + eb + tid, v + (a.bias ? a.bias[eb + tid] : 0.f));
   }
 }
 
@@ -116,7 +124,7 @@ __device__ __forceinline__ void router_mfma_slice(const RouterArgs& a, int e0, i
 
 // The kRouterWaves slice sums red[0..15][m][l], added in slice order, stored
 // with the bias (threads tid < 64*MR).
-template <int MR>
+template <int MR, bool WT = false>
 __device__ __forceinline__ void router_mfma_store(const RouterArgs& a, int e0, int t0, const f32x4 (*red)[MR][64]) {
   const int tid = threadIdx.x;
   if (tid < 64 * MR) {
@@ -129,7 +137,7 @@ __device__ __forceinline__ void router_mfma_store(const RouterArgs& a, int e0, i
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int e = e0 + 4 * (l >> 4) + j;
-        if (e < a.E) a.logits[(int64_t)t * a.E + e] = v[j] + (a.bias ? a.bias[e] : 0.f);
+        if (e < a.E) store_logit<WT>(a.logits + (int64_t)t * a.E + e, v[j] + (a.bias ? a.bias[e] : 0.f));
       }
     }
   }

@@ -112,7 +112,27 @@ constexpr int banks_xl() { return FP8 ? 12 : 6; }
 // K range (at most kXlSteps steps) are staged once into LDS, in MFMA fragment
 // order, before the weight stream starts; the stream then carries weights
 // only and never synchronises.
-template <bool FP8, int MODE, int MT, bool PACKED, int NB, bool NT, bool XL = false>
+// Output stores.  WT: agent-scope stores (written through the XCD's L2), for
+// outputs that workgroups on other XCDs read later in the same launch.
+template <bool WT>
+__device__ __forceinline__ void store_u32x2(void* p, u32x2 v) {
+  if constexpr (WT)
+    __hip_atomic_store(static_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *static_cast<u32x2*>(p) = v;
+}
+template <bool WT>
+__device__ __forceinline__ void store_f32x4(float* p, f32x4 v) {
+  if constexpr (WT) {
+    store_u32x2<true>(p, u32x2{__float_as_uint(v.x), __float_as_uint(v.y)});
+    store_u32x2<true>(p + 2, u32x2{__float_as_uint(v.z), __float_as_uint(v.w)});
+  } else {
+    *reinterpret_cast<f32x4*>(p) = v;
+  }
+}
+
+template <bool FP8, int MODE, int MT, bool PACKED, int NB, bool NT, bool XL = false, bool WT = false>
 __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks, int mc, int mch, int lo,
                                              int hi, uint16_t* __restrict__ xs_raw, int bx) {
   constexpr bool TWO = MODE == MODE_GATEUP;
@@ -292,13 +312,12 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
             const f32x4 gt = acc[m], up = acc3[m];
             u32x2 o = {pack_bf16x2(silu(gt.x) * up.x, silu(gt.y) * up.y),
                        pack_bf16x2(silu(gt.z) * up.z, silu(gt.w) * up.w)};
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
+            store_u32x2<WT>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol, o);
           } else if (a.out_f32) {
-            float* o = static_cast<float*>(a.out) + ks * a.split_stride + row * a.ldo + ncol;
-            *reinterpret_cast<f32x4*>(o) = acc[m];
+            store_f32x4<WT>(static_cast<float*>(a.out) + ks * a.split_stride + row * a.ldo + ncol, acc[m]);
           } else {
             u32x2 o = {pack_bf16x2(acc[m].x, acc[m].y), pack_bf16x2(acc[m].z, acc[m].w)};
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
+            store_u32x2<WT>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol, o);
           }
         }
         acc[m] = f32x4{0, 0, 0, 0};
