@@ -262,10 +262,18 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
     for (int m = 0; m < MT; ++m) { acc[m] = f32x4{0, 0, 0, 0}; acc3[m] = f32x4{0, 0, 0, 0}; }
 
     // one K step: multiply the weights in (wa, wb) with the step's activations
-    auto compute = [&](const WFrag<FP8>& wa, const WFrag<FP8>& wb, const u32x4* xr, int buf, int j, int kstep) {
+    // fp8 block scales of the down projection travel with their step's
+    // weights (SCALE_AHEAD): loaded at compute time, the wait for a scale
+    // (vector-memory counters drain in order) also waits for every weight
+    // load in flight.  Measured: the down projection (short K ranges, XL
+    // activations) gains; gate/up at three waves per SIMD loses, and keeps
+    // loading its scales at compute time.
+    constexpr bool SCALE_AHEAD = FP8 && MODE == MODE_DOWN;
+    auto compute = [&](const WFrag<FP8>& wa, const WFrag<FP8>& wb, const u32x4* xr, int buf, float s1a,
+                       float s3a, int j, int kstep) {
       if (FP8) {
-        const float sc1 = Sg[sb_row(j) + kstep];
-        const float sc3 = TWO ? S3g[sb_row(j) + kstep] : 0.f;
+        const float sc1 = SCALE_AHEAD ? s1a : Sg[sb_row(j) + kstep];
+        const float sc3 = SCALE_AHEAD ? s3a : (TWO ? S3g[sb_row(j) + kstep] : 0.f);
         bf16x8 a1[4], a3[4];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -341,6 +349,7 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
     const int span = FLAT ? nblk : 1;       // blocks per stream
     const int vsteps = span * steps;
     WFrag<FP8> w1b[NB], w3b[NB];
+    float s1b[NB], s3b[NB];   // SCALE_AHEAD: the banks' block scales
     u32x4 xb[NB][XV];
     for (int jb = 0; jb < nblk; jb += span) {
       int lj = jb, lk = 0;   // block and K step of the next loads
@@ -349,6 +358,10 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
         const int j = in ? lj : jb + span - 1;
         const int k = kstep0 + (in ? lk : steps - 1);
         load_x(k, xb[bank]);
+        if constexpr (SCALE_AHEAD) {
+          s1b[bank] = Sg[sb_row(j) + k];
+          s3b[bank] = TWO ? S3g[sb_row(j) + k] : 0.f;
+        }
         load_w<FP8, NT>(w1b[bank], w1s, j, k);
         if (TWO) load_w<FP8, NT>(w3b[bank], w3s, j, k);
         if (++lk == steps) { lk = 0; ++lj; }
@@ -388,7 +401,8 @@ __device__ __forceinline__ void stream_group(const StreamArgs& a, int g, int ks,
           const int v = v0 + u;
           if (v < vsteps) {
             issue((u + NB - 1) % NB);
-            compute(w1b[u], w3b[u], xb[u], v & 1, cj, kstep0 + ck);
+            compute(w1b[u], w3b[u], xb[u], v & 1, SCALE_AHEAD ? s1b[u] : 0.f, SCALE_AHEAD ? s3b[u] : 0.f, cj,
+                    kstep0 + ck);
             if constexpr (!XDIRECT) {
               store_x((v + 1) & 1, xb[(u + 1) % NB]);
               __syncthreads();
