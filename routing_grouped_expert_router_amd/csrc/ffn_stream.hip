@@ -41,10 +41,10 @@ namespace moe {
 
 // grid (N / 64, b_rows + E_phys + n_shared, ksplit); region B exists only
 // when region A takes fewer than four tiles per pass.
-// fp8 single-tile launches fit three waves per SIMD (168 registers) once the
-// compiler is asked to
+// fp8 single-tile launches run two waves per SIMD (three measured slower
+// with the gate/up scales held in registers)
 template <bool FP8, int MTA>
-constexpr int min_waves() { return (FP8 && MTA == 1) ? 3 : 1; }
+constexpr int min_waves() { return (FP8 && MTA == 1) ? 2 : 1; }
 
 // XLK: region A keeps its activations in LDS (dynamic shared memory sized by
 // the launch to cover both the K range and region B's tiles).
