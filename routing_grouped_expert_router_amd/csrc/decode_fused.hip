@@ -324,8 +324,9 @@ hipError_t launch_decode_fused(FusedArgs f, int fp8, hipStream_t s) {
   if (f.route.T < 0 || f.route.T > kFusedMaxT || f.route_variant < 0 || f.g2.ksplit > kMaxSplits)
     return hipErrorInvalidValue;
   if (f.g1.nblk != 1 || f.g2.nblk != 1 || f.g1.N % kBN || f.g2.N % kBN) return hipErrorInvalidValue;
-  f.grid = decode_fused_grid(fp8);
-  if (f.grid < 2 || f.grid > kFusedMaxGrid) return hipErrorInvalidConfiguration;
+  // fewer workgroups than fit are resident all the same
+  f.grid = std::min(decode_fused_grid(fp8), kFusedMaxGrid);
+  if (f.grid < 2) return hipErrorInvalidConfiguration;
   f.spin_limit = kSpinLimit;
   if (fp8) hipLaunchKernelGGL(decode_fused_kernel<true>, dim3(f.grid), dim3(kThreads), 0, s, f);
   else hipLaunchKernelGGL(decode_fused_kernel<false>, dim3(f.grid), dim3(kThreads), 0, s, f);
