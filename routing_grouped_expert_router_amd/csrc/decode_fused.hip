@@ -9,8 +9,8 @@
 // resident at once (G = compute units x workgroups that fit on one), each
 // walking the work items of five phases, in item order, separated by grid
 // barriers:
-//   R  router logits: (token, 8 experts) items, or (16 experts) items on
-//      MFMA when E > 64;
+//   R  router logits: (token, expert) items, or (16 experts) items on MFMA
+//      when E > 64;
 //   A  workgroup 0 routes (select, rank, scan, assign) and lists the slots
 //      that received tokens; the other workgroups meanwhile run the shared
 //      expert's gate/up, which needs no routing;
@@ -248,9 +248,9 @@ __global__ __launch_bounds__(kThreads) void decode_fused_kernel(FusedArgs f) {
       __syncthreads();
     }
   } else if (T > 0) {
-    const int ne = (f.router.E + 7) / 8;
+    const int ne = f.router.E;
     for (int i = wg; i < T * ne; i += G, ++items) {
-      router_small_item<false, 8, true>(f.router, i / ne, i % ne);
+      router_small_item<false, 1, true>(f.router, i / ne, i % ne);
       __syncthreads();
     }
   }

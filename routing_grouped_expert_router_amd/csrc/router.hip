@@ -4,7 +4,8 @@
 //
 // Two kernels, both with a fixed summation order (bit-reproducible):
 //  * router_small (any E, fp32 or bf16 x): one workgroup per token and group of
-//    up to 64 experts; thread i takes 8 consecutive h per 2048-wide stride and
+//    up to 64 experts (one expert when T * E <= 1024, so that few tokens still
+//    spread over many workgroups); thread i takes 8 consecutive h per 2048-wide stride and
 //    keeps one partial sum per expert, then a wave butterfly and a fixed-order
 //    sum over the four waves.  W_r rows are read from L2 by every workgroup.
 //  * router_mfma (E > 64, bf16 x): a workgroup owns 16 experts x 16*MR tokens
@@ -36,6 +37,8 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_mfma_kernel(RouterAr
 
 bool router_uses_mfma(int E, int H, int x_f32) { return E > 64 && !x_f32 && H % 1024 == 0; }
 
+constexpr int kRouterOneExpertMax = 1024;   // T * E up to which each workgroup takes one expert
+
 hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   if (router_uses_mfma(a.E, a.H, a.x_f32)) {
@@ -49,6 +52,12 @@ hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
       hipLaunchKernelGGL(router_mfma_kernel<2>, dim3(eb, (a.T + 31) / 32), dim3(kRouterWaves * 64), 0, s, a);
     else
       hipLaunchKernelGGL(router_mfma_kernel<1>, dim3(eb, (a.T + 15) / 16), dim3(kRouterWaves * 64), 0, s, a);
+  } else if ((int64_t)a.T * a.E <= kRouterOneExpertMax) {
+    // few tokens: one workgroup per (token, expert), so the W_r rows are read
+    // in parallel (each expert's sum runs in the same order for any EB)
+    const dim3 g(a.T, a.E), b(256);
+    if (a.x_f32) hipLaunchKernelGGL((router_small_kernel<true, 1>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((router_small_kernel<false, 1>), g, b, 0, s, a);
   } else {
     const dim3 g(a.T, a.E > 32 ? (a.E + 63) / 64 : 1), b(256);
     if (a.x_f32) {
