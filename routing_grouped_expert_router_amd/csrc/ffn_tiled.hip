@@ -521,7 +521,7 @@ bool tiled_supported(int mode, int fp8, int N, int Kdim, int ksplit) {
 // 32-bit buffer offsets: both must stay below 2 GiB.
 bool wide_supported(int mode, const TiledArgs& a) {
   if (a.s.N % (mode == MODE_GATEUP ? kWN / 2 : kWN)) return false;
-  if ((a.s.Kdim / a.s.ksplit) % (32 * kWBanks)) return false;   // whole passes of kWBanks steps
+  if ((a.s.Kdim / a.s.ksplit) % 32) return false;   // whole 32-wide steps (a pass may end early)
   return (int64_t)a.s.N * a.s.Kdim * 2 < (int64_t(1) << 31) && a.x_bytes > 0 &&
          a.x_bytes < (int64_t(1) << 31);
 }
