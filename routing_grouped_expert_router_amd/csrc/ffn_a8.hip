@@ -97,18 +97,22 @@ __device__ __forceinline__ void ffn_a8_body(const A8Args& a, int g, bool big_cla
   const int nkb = Kdim / 128;
   const int kper = nkb / a.ksplit;
   const int kb0 = blockIdx.z * kper;
-  const int n0 = blockIdx.x * 64 + 16 * wave;       // this wave's 16 weight rows
+  // the workgroup owns a.nblk consecutive 64-row blocks; this wave's 16
+  // weight rows in block j start at n0(j)
+  const int nblk = a.nblk;
+  auto n0_of = [&](int j) { return (blockIdx.x * nblk + j) * 64 + 16 * wave; };
   const int lr = lane & 15, lg = lane >> 4;
   const uint8_t* Wa = shared ? a.SW : a.W + (int64_t)g * N * Kdim;
   const uint8_t* Wb = GU ? (shared ? a.SW3 : a.W3 + (int64_t)g * N * Kdim) : nullptr;
-  const float* Sa = (shared ? a.SS : a.S + (int64_t)g * (N / 128) * nkb) + (int64_t)(n0 / 128) * nkb;
-  const float* Sb = GU ? (shared ? a.SS3 : a.S3 + (int64_t)g * (N / 128) * nkb) + (int64_t)(n0 / 128) * nkb
-                       : nullptr;
-  // byte offset of this lane's 16-byte weight piece `instr` of K step kb
-  auto woff = [&](int kb, int instr) -> int64_t {
+  const float* Sa0 = shared ? a.SS : a.S + (int64_t)g * (N / 128) * nkb;
+  const float* Sb0 = GU ? (shared ? a.SS3 : a.S3 + (int64_t)g * (N / 128) * nkb) : nullptr;
+  // byte offset of this lane's 16-byte weight piece `instr` of K step kb, block j
+  auto woff = [&](int j, int kb, int instr) -> int64_t {
+    const int n0 = n0_of(j);
     if (PACKED) return ((int64_t)kb * (N / 16) + n0 / 16) * 2048 + instr * 1024 + lane * 16;
     return (int64_t)(n0 + lr) * Kdim + kb * 128 + 64 * instr + 16 * lg;
   };
+  auto srow_w = [&](int j) { return (int64_t)(n0_of(j) / 128) * nkb; };
   const int ntiles = (R + 15) / 16;
   for (int t0 = 0; t0 < ntiles; t0 += MT) {
     const uint8_t* xrow[MT];
@@ -125,11 +129,12 @@ __device__ __forceinline__ void ffn_a8_body(const A8Args& a, int g, bool big_cla
     }
     u32x4 wr[NB][2], w3r[NB][2], xr[NB][MT][2];
     float sx[NB][MT], swa[NB], swb[NB];
-    auto load = [&](int bank, int kb) {
+    auto load = [&](int bank, int jw, int kb) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        wr[bank][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wa + woff(kb, j)));
-        if constexpr (GU) w3r[bank][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wb + woff(kb, j)));
+        wr[bank][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wa + woff(jw, kb, j)));
+        if constexpr (GU)
+          w3r[bank][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wb + woff(jw, kb, j)));
       }
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
@@ -137,8 +142,8 @@ __device__ __forceinline__ void ffn_a8_body(const A8Args& a, int g, bool big_cla
         xr[bank][i][1] = *reinterpret_cast<const u32x4*>(xrow[i] + kb * 128 + 64);
         sx[bank][i] = srow[i][kb];
       }
-      swa[bank] = Sa[kb];
-      if constexpr (GU) swb[bank] = Sb[kb];
+      swa[bank] = Sa0[srow_w(jw) + kb];
+      if constexpr (GU) swb[bank] = Sb0[srow_w(jw) + kb];
     };
     f32x4 acc[MT], acc3[MT];
 #pragma unroll
@@ -165,42 +170,65 @@ __device__ __forceinline__ void ffn_a8_body(const A8Args& a, int g, bool big_cla
         }
       }
     };
-    // The step count is padded to whole passes of NB so that the loop body
-    // has no branches (a guarded step makes the compiler wait for every
-    // outstanding load); loads past the end re-read the last step.
-    const int slast = kper - 1;
-    const int npad = (kper + NB - 1) / NB * NB;
+    // acc[i] holds D[w-row 4*lg + j][token lr of tile i] of block jo
+    auto epilogue = [&](int jo) {
 #pragma unroll
-    for (int p = 0; p < NB - 1; ++p) load(p, kb0 + min(p, slast));
-    for (int sb = 0; sb < npad; sb += NB) {
-#pragma unroll
-      for (int u = 0; u < NB; ++u) {
-        const int st = sb + u;
-        load((u + NB - 1) % NB, kb0 + min(st + NB - 1, slast));
-        // (fences keep each step's loads in their step: hoisted together the
-        // loads of a pass serialise the pipeline)
-        __builtin_amdgcn_sched_barrier(0);
-        compute(u, st < kper);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < MT; ++i) {
+        const int gr = (t0 + i) * 16 + lr;
+        if (gr < R) {
+          const int64_t row = gr < c0 ? s0 + gr : s1 + (gr - c0);
+          const int col = n0_of(jo) + 4 * lg;
+          if constexpr (GU) {
+            const f32x4 gt = acc[i], up = acc3[i];
+            const u32x2 o = {pack_bf16x2(a8_silu(gt.x) * up.x, a8_silu(gt.y) * up.y),
+                             pack_bf16x2(a8_silu(gt.z) * up.z, a8_silu(gt.w) * up.w)};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + col) = o;
+          } else if (a.out_f32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + blockIdx.z * a.split_stride + row * a.ldo + col) =
+                acc[i];
+          } else {
+            const u32x2 o = {pack_bf16x2(acc[i].x, acc[i].y), pack_bf16x2(acc[i].z, acc[i].w)};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + col) = o;
+          }
+        }
+        acc[i] = f32x4{0, 0, 0, 0};
+        acc3[i] = f32x4{0, 0, 0, 0};
       }
-    }
-    // acc[i] holds D[w-row 4*lg + j][token lr of tile i]
+    };
+    // Single-tile passes walk the workgroup's blocks as one stream of
+    // nblk * kper steps (loads run NB - 1 steps ahead across block
+    // boundaries); multi-tile passes run one stream per block.  The step
+    // count of a stream is padded to whole passes of NB so that the loop
+    // body has no branches around loads (a guarded step makes the compiler
+    // wait for every outstanding load); loads past the end re-read the last
+    // step, and padding steps add d * 0.
+    const int span = MT == 1 ? nblk : 1;
+    const int vsteps = span * kper;
+    const int npad = (vsteps + NB - 1) / NB * NB;
+    for (int jb = 0; jb < nblk; jb += span) {
+      auto load_v = [&](int bank, int v) {
+        const int vc = min(v, vsteps - 1);
+        load(bank, jb + vc / kper, kb0 + vc % kper);
+      };
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int gr = (t0 + i) * 16 + lr;
-      if (gr >= R) continue;
-      const int64_t row = gr < c0 ? s0 + gr : s1 + (gr - c0);
-      const int col = n0 + 4 * lg;
-      if constexpr (GU) {
-        const f32x4 gt = acc[i], up = acc3[i];
-        const u32x2 o = {pack_bf16x2(a8_silu(gt.x) * up.x, a8_silu(gt.y) * up.y),
-                         pack_bf16x2(a8_silu(gt.z) * up.z, a8_silu(gt.w) * up.w)};
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + col) = o;
-      } else if (a.out_f32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + blockIdx.z * a.split_stride + row * a.ldo + col) = acc[i];
-      } else {
-        const u32x2 o = {pack_bf16x2(acc[i].x, acc[i].y), pack_bf16x2(acc[i].z, acc[i].w)};
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + col) = o;
+      for (int p = 0; p < NB - 1; ++p) load_v(p, p);
+      int cj = jb, ck = 0;   // block and step being multiplied
+      for (int sb = 0; sb < npad; sb += NB) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const int st = sb + u;
+          load_v((u + NB - 1) % NB, st + NB - 1);
+          // (fences keep each step's loads in their step: hoisted together the
+          // loads of a pass serialise the pipeline)
+          __builtin_amdgcn_sched_barrier(0);
+          compute(u, st < vsteps);
+          __builtin_amdgcn_sched_barrier(0);
+          if (st < vsteps && ++ck == kper) {
+            epilogue(cj);
+            ck = 0;
+            ++cj;
+          }
+        }
       }
     }
   }
@@ -232,7 +260,8 @@ hipError_t launch_ffn_a8(const A8Args& a, int packed, int mode, hipStream_t s) {
   if (a.N % 64 || a.Kdim % 128 || (a.Kdim / 128) % a.ksplit) return hipErrorInvalidValue;
   const int groups = a.E_phys + a.n_shared;
   const bool big = a.T > 16;
-  const dim3 grid(a.N / 64, big ? 2 * groups : groups, a.ksplit);
+  if (a.nblk < 1 || a.nblk > 8 || (a.N / 64) % a.nblk) return hipErrorInvalidValue;
+  const dim3 grid(a.N / (64 * a.nblk), big ? 2 * groups : groups, a.ksplit);
   if (mode == MODE_GATEUP) {
     if (big) launch_a8_big<MODE_GATEUP, true>(a, packed, grid, s);
     else launch_a8_big<MODE_GATEUP, false>(a, packed, grid, s);

@@ -136,6 +136,7 @@ struct A8Args {
   const uint8_t* W; const uint8_t* W3; const float* S; const float* S3;        // routed
   const uint8_t* SW; const uint8_t* SW3; const float* SS; const float* SS3;    // shared
   void* out; int64_t ldo; int64_t split_stride; int out_f32; int ksplit;
+  int nblk;           // consecutive 64-row output blocks per workgroup (1..8); grid.x = N / (64 * nblk)
 };
 hipError_t launch_ffn_a8(const A8Args& a, int packed, int mode, hipStream_t s);
 

@@ -485,7 +485,27 @@ A8Args a8_base_args(const moe_desc_t* d, const moe_route_t* r, int32_t T) {
   a.shared_base = routed_cap(d);
   a.counts = r->counts; a.masked_m = r->masked_m; a.spill_off = r->spill_off; a.pad_off = r->pad_off;
   a.ksplit = 1;
+  a.nblk = 1;
   return a;
+}
+
+// 64-row output blocks per W8A8 workgroup: as the streaming kernel's fp8 rule
+// (stream_nblk), several blocks walked as one pipeline of at most 64 K steps
+// while at least 6144 workgroups remain.  MOE_STREAM_NBLK overrides it.
+int a8_nblk(const moe_desc_t* d, int32_t T, const A8Args& a) {
+  const int nblocks = a.N / 64;
+  const int steps = a.Kdim / 128 / a.ksplit;
+  if (const char* env = getenv("MOE_STREAM_NBLK")) {
+    const int v = atoi(env);
+    if (v >= 1 && v <= 8 && nblocks % v == 0) return v;
+  }
+  const int64_t TK = (int64_t)T * d->K;
+  const int64_t groups = (TK < d->E_phys ? TK : d->E_phys) + d->n_shared;
+  int nb = 1;
+  while (nb < 8 && steps * nb * 2 <= 64 && nblocks % (nb * 2) == 0 &&
+         groups * (nblocks / (nb * 2)) * a.ksplit >= 6144)
+    nb *= 2;
+  return nb;
 }
 
 }  // namespace
@@ -509,6 +529,7 @@ moe_status_t moe_expert_gate_up_a8(const moe_desc_t* d, const moe_weights_t* w, 
   a.SW = static_cast<const uint8_t*>(w->sw1); a.SW3 = static_cast<const uint8_t*>(w->sw3);
   a.SS = w->ss1; a.SS3 = w->ss3;
   a.out = h; a.ldo = d->I;
+  a.nblk = a8_nblk(d, T, a);
   return hip_status(launch_ffn_a8(a, d->w_packed, MODE_GATEUP, stream));
 }
 
@@ -528,6 +549,7 @@ moe_status_t moe_expert_down_a8(const moe_desc_t* d, const moe_weights_t* w, con
   a.SW = static_cast<const uint8_t*>(w->sw2); a.SS = w->ss2;
   a.out = y; a.ldo = d->H; a.ksplit = splits; a.out_f32 = splits > 1;
   a.split_stride = moe_buffer_rows(d) * d->H;
+  a.nblk = a8_nblk(d, T, a);
   return hip_status(launch_ffn_a8(a, d->w_packed, MODE_DOWN, stream));
 }
 
