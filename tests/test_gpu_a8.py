@@ -98,3 +98,19 @@ def test_two_level_accumulation_at_k16k_all_positive():
     e = float(np.abs(got - ref[rows]).max() / np.abs(ref).max())
     say(f"  K=16384 all-positive: max rel err {e:.3e} (bf16 rounding {2.0 ** -9:.3e})")
     assert (ref > 0).all() and e <= 2.0 ** -8
+
+
+@pytest.mark.parametrize("nblk", [2, 4])
+def test_a8_block_walk_gives_identical_outputs(nblk, monkeypatch):
+    """1, 2 or 4 output blocks per W8A8 workgroup (MOE_STREAM_NBLK) reduce
+    every output over the same K steps in the same order: bit-identical
+    layer outputs, both size classes (T > 16)."""
+    cfg = A8_CASES[0]
+    b = Built(cfg, packed=True, a8=True)
+    lg = b.oracle_logits()
+    monkeypatch.setenv("MOE_STREAM_NBLK", "1")
+    ref = b.run(lg).clone()
+    monkeypatch.setenv("MOE_STREAM_NBLK", str(nblk))
+    out = b.run(lg).clone()
+    monkeypatch.delenv("MOE_STREAM_NBLK")
+    assert torch.equal(ref, out), nblk
