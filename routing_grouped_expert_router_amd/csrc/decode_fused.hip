@@ -38,6 +38,8 @@
 // Measured on MI355X, this single launch is slower than the five launches
 // replayed from a HIP graph (whose launch boundaries cost about nothing):
 // a grid barrier costs ~5 us, the L2 writeback it needs stalls an XCD's L2.
+#include <cstdlib>
+
 #include "combine_dev.hpp"
 #include "route_dev.hpp"
 #include "router_dev.hpp"
@@ -128,8 +130,8 @@ __device__ __forceinline__ bool grid_sync(const FusedArgs& f, BarState& bs, int 
     const uint32_t g0 = gen_s - 1u;
     int n = 0;
     while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
-      if ((++n & 63) == 0 &&
-          (__hip_atomic_load(abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u || n > f.spin_limit)) {
+      if (++n > f.spin_limit ||
+          ((n & 63) == 0 && __hip_atomic_load(abort_w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)) {
         go = 0;
         break;
       }
@@ -327,7 +329,14 @@ hipError_t launch_decode_fused(FusedArgs f, int fp8, hipStream_t s) {
   // fewer workgroups than fit are resident all the same
   f.grid = std::min(decode_fused_grid(fp8), kFusedMaxGrid);
   if (f.grid < 2) return hipErrorInvalidConfiguration;
+  // MOE_FUSED_SPIN_LIMIT (polls per wait, >= 0) shortens the bound, so that
+  // tests can take the timeout path: a workgroup that must wait longer
+  // aborts the launch instead
   f.spin_limit = kSpinLimit;
+  if (const char* env = getenv("MOE_FUSED_SPIN_LIMIT")) {
+    const int v = atoi(env);
+    if (v >= 0 && v < kSpinLimit) f.spin_limit = v;
+  }
   if (fp8) hipLaunchKernelGGL(decode_fused_kernel<true>, dim3(f.grid), dim3(kThreads), 0, s, f);
   else hipLaunchKernelGGL(decode_fused_kernel<false>, dim3(f.grid), dim3(kThreads), 0, s, f);
   return hipGetLastError();

@@ -174,3 +174,23 @@ def test_fused_decode_full_size(cfg, gp):
     e = rel_err(got["out"][toks].astype(np.float64), res["out"])
     say(f"  {cfg.name}: bit-identical to the chain, sampled tokens {list(toks)} rel err {e:.3e}")
     assert e <= TOL[cfg.w_dtype]
+
+
+def test_fused_decode_timeout_path_and_recovery(monkeypatch):
+    """The bounded wait's failure path, forced from the host: with a spin
+    limit of zero polls every workgroup that has to wait at a barrier aborts
+    the launch, which ends normally with MOE_STATUS_SYNC_TIMEOUT in the
+    status word.  After the fused workspace is zero-filled again the next
+    call equals the multi-launch chain bit for bit."""
+    cfg, gp = CASES[0]
+    b = Built(cfg, grouped=gp, packed=True)
+    ref = _multi(b, b.T)
+    monkeypatch.setenv("MOE_FUSED_SPIN_LIMIT", "0")
+    _zero(b)
+    b.layer.forward_fused(b.x, b.T)
+    torch.cuda.synchronize()
+    status = int(b.layer.rt.status.cpu().numpy()[0])
+    assert status & B.MOE_STATUS_SYNC_TIMEOUT, status
+    monkeypatch.delenv("MOE_FUSED_SPIN_LIMIT")
+    b.layer.fws.zero_()
+    _same(ref, _fused(b, b.T), "after recovery")
