@@ -432,7 +432,8 @@ size_t moe_decode_fused_workspace_bytes(const moe_desc_t* d);
  * (softmax) or E <= 256 (grouped router); else MOE_ERR_UNSUPPORTED, as for
  * T > 16.  The launch holds every compute unit of the device until it ends;
  * its workgroups wait for one another, with each wait bounded (about a
- * second), so work on other streams can only delay it. */
+ * second; the environment variable MOE_FUSED_SPIN_LIMIT, in polls, lowers
+ * the bound), so work on other streams can only delay it. */
 moe_status_t moe_decode_fused(const moe_desc_t* d, const void* x, const void* w_router,
                               const float* bias, const moe_grouped_router_t* g,
                               const int32_t* l2p, const int32_t* replica_count,
