@@ -73,9 +73,19 @@ hipError_t launch_quant_1x128(const QuantArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int MODE, int MT, bool PACKED>
+// XL (down projection, single-tile passes, K range of at most kA8XlSteps
+// steps): the tile's activation codes and scales for the whole K range are
+// staged once into LDS, in the lane order the MFMA reads them, and shared by
+// the four waves and every output block the workgroup walks; the loads then
+// carry weights only.
+constexpr int kA8XlSteps = 16;
+
+template <int MODE, int MT, bool PACKED, bool XL>
 __device__ __forceinline__ void ffn_a8_body(const A8Args& a, int g, bool big_class) {
   constexpr bool GU = MODE == MODE_GATEUP;
+  static_assert(!XL || (MT == 1 && !GU), "LDS-staged activations: single-tile down projection");
+  __shared__ __attribute__((aligned(16))) u32x4 xl_s[XL ? kA8XlSteps * 64 * 2 : 1];   // [step][lane][2]
+  __shared__ float sxl_s[XL ? kA8XlSteps * 16 : 1];                                   // [step][row]
   // register stages (NB - 1 steps in flight), as many as the registers allow
   constexpr int NB = MT == 1 ? (GU ? 4 : 8) : 3;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -129,6 +139,7 @@ __device__ __forceinline__ void ffn_a8_body(const A8Args& a, int g, bool big_cla
     }
     u32x4 wr[NB][2], w3r[NB][2], xr[NB][MT][2];
     float sx[NB][MT], swa[NB], swb[NB];
+    int kbk[NB];   // XL: the bank's K step
     auto load = [&](int bank, int jw, int kb) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -136,11 +147,15 @@ __device__ __forceinline__ void ffn_a8_body(const A8Args& a, int g, bool big_cla
         if constexpr (GU)
           w3r[bank][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Wb + woff(jw, kb, j)));
       }
+      if constexpr (XL) {
+        kbk[bank] = kb - kb0;
+      } else {
 #pragma unroll
-      for (int i = 0; i < MT; ++i) {
-        xr[bank][i][0] = *reinterpret_cast<const u32x4*>(xrow[i] + kb * 128);
-        xr[bank][i][1] = *reinterpret_cast<const u32x4*>(xrow[i] + kb * 128 + 64);
-        sx[bank][i] = srow[i][kb];
+        for (int i = 0; i < MT; ++i) {
+          xr[bank][i][0] = *reinterpret_cast<const u32x4*>(xrow[i] + kb * 128);
+          xr[bank][i][1] = *reinterpret_cast<const u32x4*>(xrow[i] + kb * 128 + 64);
+          sx[bank][i] = srow[i][kb];
+        }
       }
       swa[bank] = Sa0[srow_w(jw) + kb];
       if constexpr (GU) swb[bank] = Sb0[srow_w(jw) + kb];
@@ -157,16 +172,26 @@ __device__ __forceinline__ void ffn_a8_body(const A8Args& a, int g, bool big_cla
                                            w3r[bank][1].x, w3r[bank][1].y, w3r[bank][1].z, w3r[bank][1].w});
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        const u32x4 x0 = xr[bank][i][0], x1 = xr[bank][i][1];
+        u32x4 x0, x1;
+        float sxi;
+        if constexpr (XL) {
+          x0 = xl_s[(kbk[bank] * 64 + lane) * 2];
+          x1 = xl_s[(kbk[bank] * 64 + lane) * 2 + 1];
+          sxi = sxl_s[kbk[bank] * 16 + lr];
+        } else {
+          x0 = xr[bank][i][0];
+          x1 = xr[bank][i][1];
+          sxi = sx[bank][i];
+        }
         const v8i x = __builtin_bit_cast(v8i, u32x8{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w});
         const f32x4 zero = {0, 0, 0, 0};
         const f32x4 d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w, x, zero, 0, 0, 0, 127, 0, 127);
         // padding steps (past the K range) add d * 0
-        const float sc = valid ? swa[bank] * sx[bank][i] : 0.0f;
+        const float sc = valid ? swa[bank] * sxi : 0.0f;
         acc[i] += d * sc;
         if constexpr (GU) {
           const f32x4 d3 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w3, x, zero, 0, 0, 0, 127, 0, 127);
-          acc3[i] += d3 * (valid ? swb[bank] * sx[bank][i] : 0.0f);
+          acc3[i] += d3 * (valid ? swb[bank] * sxi : 0.0f);
         }
       }
     };
@@ -205,6 +230,30 @@ __device__ __forceinline__ void ffn_a8_body(const A8Args& a, int g, bool big_cla
     const int span = MT == 1 ? nblk : 1;
     const int vsteps = span * kper;
     const int npad = (vsteps + NB - 1) / NB * NB;
+    // XL: piece p = (s * 64 + l) * 2 + j of the LDS tile is the 16 bytes j of
+    // K step s lane l reads (row l % 16, K bytes 16 (l / 16) + 64 j); thread
+    // t moves pieces t + 256 i.  Issued before the first weights, so the
+    // wait for them leaves the weight loads in flight.
+    u32x4 xst[XL ? 8 : 1];
+    float sxst = 0.f;
+    if constexpr (XL) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int pc = tid + 256 * i, st = pc >> 7, l = (pc >> 1) & 63, j = pc & 1;
+        const int gr = t0 * 16 + (l & 15);
+        const int rank = gr < R ? gr : 0;
+        const int64_t row = rank < c0 ? s0 + rank : s1 + (rank - c0);
+        const int k = kb0 + (st < kper ? st : 0);
+        xst[i] = *reinterpret_cast<const u32x4*>(a.X + row * a.ldx + k * 128 + 16 * (l >> 4) + 64 * j);
+      }
+      {
+        const int st = tid >> 4, r = tid & 15;
+        const int gr = t0 * 16 + r;
+        const int rank = gr < R ? gr : 0;
+        const int64_t row = rank < c0 ? s0 + rank : s1 + (rank - c0);
+        sxst = a.XS[row * nkb + kb0 + (st < kper ? st : 0)];
+      }
+    }
     for (int jb = 0; jb < nblk; jb += span) {
       auto load_v = [&](int bank, int v) {
         const int vc = min(v, vsteps - 1);
@@ -212,6 +261,15 @@ __device__ __forceinline__ void ffn_a8_body(const A8Args& a, int g, bool big_cla
       };
 #pragma unroll
       for (int p = 0; p < NB - 1; ++p) load_v(p, p);
+      if constexpr (XL) {
+        if (jb == 0) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (((tid + 256 * i) >> 7) < kper) xl_s[tid + 256 * i] = xst[i];
+          if ((tid >> 4) < kper) sxl_s[tid] = sxst;
+          __syncthreads();
+        }
+      }
       int cj = jb, ck = 0;   // block and step being multiplied
       for (int sb = 0; sb < npad; sb += NB) {
 #pragma unroll
@@ -231,6 +289,7 @@ __device__ __forceinline__ void ffn_a8_body(const A8Args& a, int g, bool big_cla
         }
       }
     }
+    if constexpr (XL) __syncthreads();   // the LDS tile is restaged by the next pass
   }
 }
 
@@ -239,21 +298,30 @@ __device__ __forceinline__ void ffn_a8_body(const A8Args& a, int g, bool big_cla
 // the grid (grid.y row 0 .. n_big-1 re-reads group ids from the top) so that
 // their longer streams start early.  BIG = false: every group takes the
 // one-tile path (T <= 16, no group can be larger).
-template <int MODE, bool PACKED, bool BIG>
+// XL: the single-tile class of the down projection stages its activations
+// in LDS (K range of at most kA8XlSteps steps).
+template <int MODE, bool PACKED, bool BIG, bool XL>
 __global__ __launch_bounds__(256) void ffn_a8_kernel(A8Args a) {
   if constexpr (BIG) {
     const int groups = a.E_phys + a.n_shared;
-    if ((int)blockIdx.y < groups) { ffn_a8_body<MODE, 4, PACKED>(a, blockIdx.y, true); return; }
-    ffn_a8_body<MODE, 1, PACKED>(a, blockIdx.y - groups, false);
+    if ((int)blockIdx.y < groups) { ffn_a8_body<MODE, 4, PACKED, false>(a, blockIdx.y, true); return; }
+    ffn_a8_body<MODE, 1, PACKED, XL>(a, blockIdx.y - groups, false);
   } else {
-    ffn_a8_body<MODE, 1, PACKED>(a, blockIdx.y, false);
+    ffn_a8_body<MODE, 1, PACKED, XL>(a, blockIdx.y, false);
   }
 }
 
 template <int MODE, bool BIG>
 static void launch_a8_big(const A8Args& a, int packed, dim3 grid, hipStream_t s) {
-  if (packed) hipLaunchKernelGGL((ffn_a8_kernel<MODE, true, BIG>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((ffn_a8_kernel<MODE, false, BIG>), grid, dim3(256), 0, s, a);
+  constexpr bool kXl = MODE == MODE_DOWN;
+  const bool xl = kXl && a.Kdim / 128 / a.ksplit <= kA8XlSteps;
+  if (xl) {
+    if (packed) hipLaunchKernelGGL((ffn_a8_kernel<MODE, true, BIG, kXl>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((ffn_a8_kernel<MODE, false, BIG, kXl>), grid, dim3(256), 0, s, a);
+  } else {
+    if (packed) hipLaunchKernelGGL((ffn_a8_kernel<MODE, true, BIG, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((ffn_a8_kernel<MODE, false, BIG, false>), grid, dim3(256), 0, s, a);
+  }
 }
 
 hipError_t launch_ffn_a8(const A8Args& a, int packed, int mode, hipStream_t s) {
