@@ -510,6 +510,209 @@ void ffn_wide_kernel(TiledArgs ta) {
   }
 }
 
+// ---- wide tile with operands staged by direct-to-LDS loads ------------------
+//
+// The tile, the waves' outputs and the MFMA order are ffn_wide_kernel's (so
+// the results are the same bit for bit), but weights and activations go from
+// memory straight into a ring of kDStages LDS stages (buffer_load ... lds,
+// each lane's 16 bytes landing at stage base + 16 * lane), so kDStages - 1
+// 32-wide K steps are in flight without holding registers.  Each wave then
+// reads its 8 weight fragments and the step's activation fragments from LDS
+// (ds_read_b128 of 1 KiB lane-contiguous panels, free of bank conflicts).
+// Fragment reads are software-pipelined: step st multiplies the fragments
+// read from LDS during step st - 1 while reading those of step st + 1, so the
+// LDS reads run under the MFMAs even at one wave per SIMD.  Per step: wait
+// for the wave's own loads of stage st + 1 (vector-memory counters drain in
+// order) and its fragment reads of step st, barrier (every wave's loads of
+// stage st + 1 have landed and every wave has finished reading stage st - 1),
+// issue the loads of step st + kDStages - 1 into stage st - 1, read stage
+// st + 1, multiply.  Loads run kDStages - 2 steps ahead.  Packed weights only.
+constexpr int kDStages = 4;
+constexpr int kDW = kWN * 32 * 2;   // 32 KiB: 512 weight rows x 32 K
+constexpr int kDX = kTM * 32 * 2;   // 8 KiB: 128 token rows x 32 K
+constexpr int kDLoads = 10;         // loads per wave and step: 8 weight panels, 2 activation tiles
+
+template <int MODE, bool OUTF32>
+__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ffn_wdma_kernel(TiledArgs ta) {
+  const StreamArgs& a = ta.s;
+  __shared__ __attribute__((aligned(16))) char w0s[kDW];
+  __shared__ __attribute__((aligned(16))) char w1s[kDW];
+  __shared__ __attribute__((aligned(16))) char w2s[kDW];
+  __shared__ __attribute__((aligned(16))) char w3s[kDW];
+  __shared__ __attribute__((aligned(16))) char x0s[kDX];
+  __shared__ __attribute__((aligned(16))) char x1s[kDX];
+  __shared__ __attribute__((aligned(16))) char x2s[kDX];
+  __shared__ __attribute__((aligned(16))) char x3s[kDX];
+
+  TileWork tw;
+  if (!decode_work(ta, tw)) return;
+  const int g = tw.g, nt = tw.nt, c0 = tw.c0, R = tw.R;
+  const int64_t s0 = tw.s0, s1 = tw.s1;
+  const bool shared = tw.shared;
+  const int m0 = tw.mt * kTM;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Kdim = a.Kdim;
+  const int ks = blockIdx.z;
+  const int kper = Kdim / a.ksplit;
+  const int kc0 = ks * kper / 32;
+  const int nsteps = kper / 32;
+
+  const int n0 = MODE == MODE_GATEUP ? nt * (kWN / 2) : nt * kWN;
+  const char* Wa;
+  const char* Wb = nullptr;
+  if (shared) { Wa = static_cast<const char*>(a.SW); Wb = static_cast<const char*>(a.SW3); }
+  else {
+    Wa = static_cast<const char*>(a.W) + (int64_t)g * a.N * Kdim * 2;
+    if (MODE == MODE_GATEUP) Wb = static_cast<const char*>(a.W3) + (int64_t)g * a.N * Kdim * 2;
+  }
+  const uint32_t wbytes = (uint32_t)a.N * Kdim * 2;
+  // the weight panels this wave loads: p = 8 * wave + i; for gate/up panels
+  // 0..15 are W1 rows n0 + 16 p, panels 16..31 the same rows of W3
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(MODE == MODE_GATEUP && wave >= 2 ? Wb : Wa, wbytes);
+  const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(a.X, (uint32_t)ta.x_bytes);
+  uint32_t pw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int p = 8 * wave + i;
+    const int row0 = MODE == MODE_GATEUP ? n0 + 16 * (p & 15) : n0 + 16 * p;
+    pw[i] = (uint32_t)(row0 / 16) * 16 * 128 * 2 + lane * 16;
+  }
+  auto wk = [&](int kc) -> uint32_t { return (uint32_t)(kc >> 2) * (a.N / 16) * 4096 + (kc & 3) * 1024; };
+  // activation tiles this wave loads: wave + 4 q (row m0 + 16 (wave + 4 q) + lane % 16)
+  uint32_t xoff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int gr = m0 + (wave + 4 * q) * 16 + (lane & 15);
+    int64_t row = gr < c0 ? s0 + gr : (gr < R ? s1 + (gr - c0) : s0);   // pad rows read a valid row
+    if (a.gather_src) {
+      const int rank = gr < R ? gr : 0;
+      row = shared ? rank : a.gather_src[a.gather_off[g] + rank];
+    }
+    xoff[q] = (uint32_t)(row * a.ldx * 2) + 16 * (lane >> 4);
+  }
+
+  const int rows_here = min(kTM, R - m0);
+  const int mv = ((rows_here + 31) / 32) * 2;
+  auto run = [&](auto mvc) {
+    constexpr int MV = decltype(mvc)::value;
+    // loads of step st (clamped past the end: re-read, never multiplied) into stage S
+    auto issue = [&](auto sc, int st) {
+      constexpr int S = decltype(sc)::value;
+      char* ws = S == 0 ? w0s : S == 1 ? w1s : S == 2 ? w2s : w3s;
+      char* xs = S == 0 ? x0s : S == 1 ? x1s : S == 2 ? x2s : x3s;
+      const int stc = st < nsteps ? st : nsteps - 1;
+      const uint32_t wso = wk(kc0 + stc);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, ws + (8 * wave + i) * 1024, 16, pw[i], wso, 0, 0);
+      const uint32_t xso = (uint32_t)(kc0 + stc) * 64;
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, xs + (wave + 4 * q) * 1024, 16, xoff[q], xso, 0, 0);
+    };
+    f32x4 acc[MV][8];
+#pragma unroll
+    for (int m = 0; m < MV; ++m)
+#pragma unroll
+      for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0, 0, 0, 0};
+    // fragments of one stage: 8 weight panels, then MV activation tiles
+    bf16x8 fa[8 + MV], fb[8 + MV];
+    auto readf = [&](auto sc, bf16x8* f) {
+      constexpr int S = decltype(sc)::value;
+      const char* ws = S == 0 ? w0s : S == 1 ? w1s : S == 2 ? w2s : w3s;
+      const char* xs = S == 0 ? x0s : S == 1 ? x1s : S == 2 ? x2s : x3s;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const int p = MODE == MODE_GATEUP ? (n < 4 ? 4 * wave + n : 16 + 4 * wave + (n - 4)) : 8 * wave + n;
+        f[n] = *reinterpret_cast<const bf16x8*>(ws + p * 1024 + lane * 16);
+      }
+#pragma unroll
+      for (int m = 0; m < MV; ++m) f[8 + m] = *reinterpret_cast<const bf16x8*>(xs + m * 1024 + lane * 16);
+    };
+    auto mma = [&](const bf16x8* f) {
+#pragma unroll
+      for (int m = 0; m < MV; ++m)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[m][n] = mfma16x16x32(f[n], f[8 + m], acc[m][n]);
+    };
+    // s_waitcnt immediates (gfx9): vmcnt in bits 3:0 and 15:14, expcnt 6:4
+    // and lgkmcnt 11:8 left at their maxima
+    constexpr int kVm0 = (kDStages - 2) * kDLoads;   // stage 0 landed, stages 1 and 2 may run
+    constexpr int kVm = (kDStages - 3) * kDLoads;    // the next stage landed, the one after may run
+    constexpr int kWait0 = (kVm0 & 15) | ((kVm0 >> 4) << 14) | 0x70 | 0xF00;
+    constexpr int kWaitNext = (kVm & 15) | ((kVm >> 4) << 14) | 0x70 | 0xF00;
+    issue(IntC<0>{}, 0);
+    issue(IntC<1>{}, 1);
+    issue(IntC<2>{}, 2);
+    __builtin_amdgcn_s_waitcnt(kWait0);
+    __builtin_amdgcn_s_barrier();
+    readf(IntC<0>{}, fa);
+    // step st: its fragments are in registers (read during the previous
+    // step); read the next stage's fragments while its MFMAs run
+    // (the scheduling barriers keep each step's MFMAs between its own
+    // s_barrier and the next one: MFMAs touch no memory, and the scheduler
+    // would otherwise sink them below the next wait)
+    auto step = [&](auto nc, auto rc, bf16x8* cur, bf16x8* nxt, int st) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kWaitNext);   // this wave's loads of stage st + 1 landed
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): fragments of step st are in registers
+      __builtin_amdgcn_s_barrier();            // every wave's: stage st + 1 readable, stage st - 1 free
+      issue(nc, st + kDStages - 1);
+      if (st + 1 < nsteps) readf(rc, nxt);
+      if (st < nsteps) mma(cur);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int sb = 0; sb < nsteps; sb += kDStages) {
+      step(IntC<3>{}, IntC<1>{}, fa, fb, sb);
+      step(IntC<0>{}, IntC<2>{}, fb, fa, sb + 1);
+      step(IntC<1>{}, IntC<3>{}, fa, fb, sb + 2);
+      step(IntC<2>{}, IntC<0>{}, fb, fa, sb + 3);
+    }
+    // no load may land in LDS after the workgroup has ended
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+
+    // ---- epilogue: acc[m][n] holds D[w-row 4*(lane/16)+j of tile n][token lane%16 of tile m]
+    const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+      const int gr = m0 + m * 16 + lr;
+      if (gr >= R) continue;
+      const int64_t row = gr < c0 ? s0 + gr : s1 + (gr - c0);
+      if (MODE == MODE_GATEUP) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const f32x4 gt = acc[m][n], up = acc[m][n + 4];
+          const int ncol = n0 + 64 * wave + 16 * n + 4 * lg;
+          u32x2 o = {pack_bf16x2(silu_t(gt.x) * up.x, silu_t(gt.y) * up.y),
+                     pack_bf16x2(silu_t(gt.z) * up.z, silu_t(gt.w) * up.w)};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          const int ncol = n0 + 128 * wave + 16 * n + 4 * lg;
+          if constexpr (OUTF32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ks * a.split_stride + row * a.ldo + ncol) = acc[m][n];
+          } else {
+            u32x2 o = {pack_bf16x2(acc[m][n].x, acc[m][n].y), pack_bf16x2(acc[m][n].z, acc[m][n].w)};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
+          }
+        }
+      }
+    }
+  };
+  switch (mv) {
+    case 2: run(IntC<2>{}); break;
+    case 4: run(IntC<4>{}); break;
+    case 6: run(IntC<6>{}); break;
+    default: run(IntC<8>{}); break;
+  }
+}
+
 bool tiled_supported(int mode, int fp8, int N, int Kdim, int ksplit) {
   if (fp8) return false;
   if (mode == MODE_GATEUP) { if (N % 128) return false; }
@@ -537,6 +740,15 @@ hipError_t launch_ffn_tiled(const TiledArgs& a, int fp8, int packed, int mode, i
   // the live work count by up to 7, always has a workgroup
   const int wn = wide ? (mode == MODE_GATEUP ? kWN / 2 : kWN) : (mode == MODE_GATEUP ? 128 : kTN);
   const dim3 grid(a.s.N / wn, max_tiles + 8, a.s.ksplit);
+  // packed weights take the wide tile with operands staged by direct-to-LDS
+  // loads; MOE_TILED_DMA=0 selects the register-staged wide kernel instead
+  const char* denv = getenv("MOE_TILED_DMA");
+  if (wide && packed && !(denv && denv[0] == '0')) {
+    if (mode == MODE_GATEUP) hipLaunchKernelGGL((ffn_wdma_kernel<MODE_GATEUP, false>), grid, dim3(kTThreads), 0, s, a);
+    else if (a.s.out_f32) hipLaunchKernelGGL((ffn_wdma_kernel<MODE_DOWN, true>), grid, dim3(kTThreads), 0, s, a);
+    else hipLaunchKernelGGL((ffn_wdma_kernel<MODE_DOWN, false>), grid, dim3(kTThreads), 0, s, a);
+    return hipGetLastError();
+  }
   if (wide) {
     if (mode == MODE_GATEUP) {
       if (packed) hipLaunchKernelGGL((ffn_wide_kernel<MODE_GATEUP, true, false>), grid, dim3(kTThreads), 0, s, a);

@@ -322,19 +322,23 @@ def test_wide_tiled_kernel_matches_narrow(name, monkeypatch):
     """The wide tiled kernel (128 weight rows per wave) and the narrow one
     (64) reduce every output over the same 32-wide K steps in the same order
     with the same MFMA: bit-identical outputs (MOE_TILED_WIDE=0 forces the
-    narrow kernel), row-major and packed weights, gathered or permuted rows."""
+    narrow kernel), row-major and packed weights, gathered or permuted rows.
+    With packed weights the default wide kernel stages its operands by
+    direct-to-LDS loads; MOE_TILED_DMA=0 forces the register-staged one,
+    which must agree as well."""
     cfg = next(c for c in SMALL if c.name == name)
     for packed in (False, True):
         b = Built(cfg, packed=packed)
         lg = b.oracle_logits()
         for fused in (True, False):
             ref = b.run(lg, fused_gather=fused).clone()
-            monkeypatch.setenv("MOE_TILED_WIDE", "0")
-            try:
-                out = b.run(lg, fused_gather=fused).clone()
-            finally:
-                monkeypatch.delenv("MOE_TILED_WIDE")
-            assert torch.equal(ref, out), (name, packed, fused)
+            for var in ("MOE_TILED_WIDE", "MOE_TILED_DMA"):
+                monkeypatch.setenv(var, "0")
+                try:
+                    out = b.run(lg, fused_gather=fused).clone()
+                finally:
+                    monkeypatch.delenv(var)
+                assert torch.equal(ref, out), (name, packed, fused, var)
 
 
 def test_pack_layout_matches_definition():
