@@ -340,13 +340,20 @@ moe_status_t launch_expert_gemm(const moe_desc_t* d, const moe_route_t* r, int32
     a.b_rows = d->E_phys + d->n_shared * a.shared_chunks;
     grid.y += a.b_rows;
   }
-  hipError_t e = launch_ffn_stream(a, fp8, d->w_packed, mode, mt, grid, stream);
-  if (e != hipSuccess) return hip_status(e);
+  // Groups large on average with region A alone streaming (no region B):
+  // the few groups of at most a_max rows join the tiled launch, where they
+  // overlap the large ones, instead of a streaming launch too small to fill
+  // the GPU (DeepSeek-V3-shaped prefill T=8192: about 5 such experts)
+  const bool all_tiled = need_c && !need_b;
+  if (!all_tiled) {
+    hipError_t e = launch_ffn_stream(a, fp8, d->w_packed, mode, mt, grid, stream);
+    if (e != hipSuccess) return hip_status(e);
+  }
   if (!need_c) return MOE_OK;
   TiledArgs ta;
   ta.s = a;
   ta.tile_off = r->tile_off;
-  ta.min_rows = (mt < 4) ? 64 : a_max;
+  ta.min_rows = all_tiled ? 0 : (mt < 4) ? 64 : a_max;
   // X holds the layer input (T rows) when gathering, else the grouped buffer
   ta.x_bytes = (a.gather_src ? (int64_t)T : moe_buffer_rows(d)) * a.ldx * 2;
   const int64_t TK = (int64_t)T * d->K;
