@@ -13,6 +13,8 @@
 //    its 16 waves split H, each runs v_mfma_f32_16x16x32_bf16 over its slice
 //    with operands loaded straight to registers (next slice in flight), and
 //    the 16 partial tiles are summed in wave order through LDS.
+//  * router_block (the same, when 64-expert x 64-token blocks give at least
+//    256 workgroups): 64 experts x 64 tokens per workgroup, 8 H slices.
 #include "router_dev.hpp"
 
 namespace moe {
@@ -37,11 +39,106 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_mfma_kernel(RouterAr
 
 bool router_uses_mfma(int E, int H, int x_f32) { return E > 64 && !x_f32 && H % 1024 == 0; }
 
+// ---- many tokens: 64 experts x 64 tokens per workgroup ----------------------
+//
+// A 16-expert block re-reads every activation row once per block (16 times
+// for 256 experts); with many tokens that operand traffic, not HBM, bounds
+// router_mfma.  Here a workgroup owns 64 experts x 64 tokens, so each
+// activation row is read E/64 times and each W_r row T/64 times.  Its 8
+// waves split H into 8 slices; wave w sums slice w in 64-wide chunks
+// (two v_mfma_f32_16x16x32_bf16 per chunk and tile, the next chunk's
+// operands in flight), then the 8 partial tiles are added in wave order
+// through LDS.  Summation order is fixed: bit-reproducible.
+constexpr int kRouterBlockWaves = 8;
+
+__global__ __launch_bounds__(kRouterBlockWaves * 64) void router_block_kernel(RouterArgs a) {
+  __shared__ f32x4 red[kRouterBlockWaves][16][64];   // 128 KiB: [wave][4 expert x 4 token tiles][lane]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int e0 = blockIdx.x * 64, t0 = blockIdx.y * 64;
+  // rows past E or T read row 0; their results are never written
+  const uint16_t* wrow[4];
+  const uint16_t* xrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = e0 + 16 * i + lr, t = t0 + 16 * i + lr;
+    wrow[i] = a.w + (int64_t)(e < a.E ? e : 0) * a.H;
+    xrow[i] = static_cast<const uint16_t*>(a.x) + (int64_t)(t < a.T ? t : 0) * a.H;
+  }
+  const int kw = a.H / kRouterBlockWaves;   // multiple of 64
+  const int kbeg = wave * kw;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[n][m] = f32x4{0, 0, 0, 0};
+  u32x4 wc[4][2], xc[4][2];
+  auto load = [&](int k0, u32x4 (*wv)[2], u32x4 (*xv)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int k = k0 + 32 * j + 8 * lg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wv[i][j] = *reinterpret_cast<const u32x4*>(wrow[i] + k);
+        xv[i][j] = *reinterpret_cast<const u32x4*>(xrow[i] + k);
+      }
+    }
+  };
+  load(kbeg, wc, xc);
+  for (int k0 = kbeg; k0 < kbeg + kw; k0 += 64) {
+    u32x4 wn[4][2], xn[4][2];
+    const bool more = k0 + 64 < kbeg + kw;
+    if (more) load(k0 + 64, wn, xn);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          acc[n][m] = mfma16x16x32(__builtin_bit_cast(bf16x8, wc[n][j]), __builtin_bit_cast(bf16x8, xc[m][j]),
+                                   acc[n][m]);
+    if (more) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { wc[i][j] = wn[i][j]; xc[i][j] = xn[i][j]; }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) red[wave][4 * n + m][lane] = acc[n][m];
+  __syncthreads();
+  // thread tid sums tiles tid / 64 and tid / 64 + 8 (lane tid % 64) over the waves in order;
+  // lane l of tile (n, m) holds experts e0 + 16 n + 4 (l / 16) + j of token t0 + 16 m + l % 16
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int tile = (tid >> 6) + 8 * h, l = tid & 63;
+    f32x4 s = red[0][tile][l];
+    for (int w = 1; w < kRouterBlockWaves; ++w) s += red[w][tile][l];
+    const int n = tile >> 2, m = tile & 3;
+    const int t = t0 + 16 * m + (l & 15);
+    if (t < a.T) {
+      const float v[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = e0 + 16 * n + 4 * (l >> 4) + j;
+        if (e < a.E) a.logits[(int64_t)t * a.E + e] = v[j] + (a.bias ? a.bias[e] : 0.f);
+      }
+    }
+  }
+}
+
 constexpr int kRouterOneExpertMax = 1024;   // T * E up to which each workgroup takes one expert
 
 hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  if (router_uses_mfma(a.E, a.H, a.x_f32)) {
+  const int64_t blocks = (int64_t)((a.E + 63) / 64) * ((a.T + 63) / 64);
+  if (router_uses_mfma(a.E, a.H, a.x_f32) && blocks >= 256 && !(a.H % (64 * kRouterBlockWaves))) {
+    hipLaunchKernelGGL(router_block_kernel, dim3((a.E + 63) / 64, (a.T + 63) / 64), dim3(kRouterBlockWaves * 64),
+                       0, s, a);
+  } else if (router_uses_mfma(a.E, a.H, a.x_f32)) {
     // 16*MR tokens per workgroup: the largest MR that still gives >= 256
     // workgroups (weights are re-read once per token block, activations once
     // per 16-expert block either way)

@@ -123,6 +123,36 @@ def test_router_logits(cfg):
     assert (np.abs(got - ref) <= bound).all(), float((np.abs(got - ref) / bound).max())
 
 
+# many tokens and more than 64 experts: the 64-expert x 64-token block
+# router (ragged token and expert counts: partial blocks on both axes)
+ROUTER_BLOCK = [
+    configs.tiny().with_(name="router_block_e256_t4100", T=4100, H=1024, I=128, E=256, E_phys=256, K=8,
+                         act_dtype="bf16", layout="contig", BM=128, bias="normal0.5"),
+    configs.tiny().with_(name="router_block_e200_t5000", T=5000, H=2048, I=128, E=200, E_phys=200, K=8,
+                         act_dtype="bf16", layout="contig", BM=128, bias="normal0.5"),
+]
+
+
+@pytest.mark.parametrize("cfg", ROUTER_BLOCK, ids=lambda c: c.name)
+def test_router_block_logits(cfg):
+    """Same bound as test_router_logits: |got - exact| within H ulps of the
+    sum of |x||w| (fp32 accumulation) plus one of the result."""
+    b = Built(cfg)
+    ref = b.oracle_logits().astype(np.float64)
+    b.layer.logits.fill_(float("nan"))
+    B.moe_router_logits(b.d, b.x, b.wr, b.bias, b.T, b.layer.logits)
+    got = b.layer.logits[: b.T].cpu().numpy().astype(np.float64)
+    from oracle_adapt import to_f64
+    absdot = np.abs(to_f64(b.inp.x)) @ np.abs(to_f64(b.inp.w_router)).T
+    bound = cfg.H * 2.0 ** -24 * absdot + 2.0 ** -24 * np.abs(ref) + 1e-30
+    assert np.isfinite(got).all()
+    assert (np.abs(got - ref) <= bound).all(), float((np.abs(got - ref) / bound).max())
+    # deterministic: a second call gives the same bits
+    first = b.layer.logits[: b.T].clone()
+    B.moe_router_logits(b.d, b.x, b.wr, b.bias, b.T, b.layer.logits)
+    assert torch.equal(first, b.layer.logits[: b.T])
+
+
 def test_permute_copies_rows_exactly():
     cfg = SMALL[3]   # fp8 + shared + masked
     b = Built(cfg)
