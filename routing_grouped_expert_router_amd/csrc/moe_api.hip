@@ -294,7 +294,9 @@ moe_status_t ffn_common_checks(const moe_desc_t* d, const moe_weights_t* w, cons
 // least 6144 workgroups (about eight rounds of the chip) remain; fewer,
 // longer workgroups would leave the chip idle at the end of the launch.
 // Measured: it pays for fp8 down projections with K = 2048 and costs time for
-// bf16 ones.  MOE_STREAM_NBLK (1..8, dividing N/64) overrides the choice.
+// bf16 ones with long K ranges; a bf16 K range of at most 8 steps (a 128 KiB
+// stream per block) walks two blocks.  MOE_STREAM_NBLK (1..8, dividing N/64)
+// overrides the choice.
 int stream_nblk(const moe_desc_t* d, int32_t T, const StreamArgs& a, bool fp8) {
   const int nblocks = a.N / 64;
   const int steps = a.Kdim / 128 / a.ksplit;
@@ -302,9 +304,10 @@ int stream_nblk(const moe_desc_t* d, int32_t T, const StreamArgs& a, bool fp8) {
     const int v = atoi(env);
     if (v >= 1 && v <= 8 && nblocks % v == 0) return v;
   }
-  if (!fp8) return 1;
   const int64_t TK = (int64_t)T * d->K;
   const int64_t groups = (TK < d->E_phys ? TK : d->E_phys) + d->n_shared;
+  if (!fp8)
+    return (steps <= 8 && nblocks % 2 == 0 && groups * (nblocks / 2) * a.ksplit >= 6144) ? 2 : 1;
   int nb = 1;
   while (nb < 8 && steps * nb * 2 <= 64 && nblocks % (nb * 2) == 0 &&
          groups * (nblocks / (nb * 2)) * a.ksplit >= 6144)
