@@ -59,6 +59,11 @@ def small_configs():
         # projections (gate/up and down), masked with spill, shared expert
         base.with_(name="tiled_wide", T=600, H=512, I=512, E=4, E_phys=4, K=2, n_shared=1,
                    act_dtype="bf16", M_max=200),
+        # groups large on average (T*K = 64*E) but skewed: rows per expert
+        # 253, 6, 0, 165, 4, 58, 24, 2 and a 256-row shared expert, every
+        # group (the empty one aside) in the tiled launch, tiny ones included
+        base.with_(name="tiled_skewed_small_groups", T=256, H=512, I=512, E=8, E_phys=8, K=2, n_shared=1,
+                   act_dtype="bf16", layout="contig", BM=128, bias="zipf1.1"),
     ]
 
 
@@ -347,7 +352,8 @@ def test_block_walk_gives_identical_outputs(nblk, monkeypatch):
             assert torch.equal(ref, out), (cfg.name, packed, nblk)
 
 
-@pytest.mark.parametrize("name", ["tiled_masked_spill", "tiled_contig_shared", "tiled_wide"])
+@pytest.mark.parametrize("name", ["tiled_masked_spill", "tiled_contig_shared", "tiled_wide",
+                                  "tiled_skewed_small_groups"])
 def test_wide_tiled_kernel_matches_narrow(name, monkeypatch):
     """The wide tiled kernel (128 weight rows per wave) and the narrow one
     (64) reduce every output over the same 32-wide K steps in the same order
