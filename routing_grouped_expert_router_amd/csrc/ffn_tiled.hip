@@ -713,6 +713,188 @@ void ffn_wdma_kernel(TiledArgs ta) {
   }
 }
 
+// ---- wide tile, weights straight to registers, activations through LDS --------
+//
+// The tile, the waves' outputs and the MFMA order are ffn_wdma_kernel's (so
+// the results are the same bit for bit).  A weight fragment is read by one
+// wave only, so weights skip LDS: each wave loads its 8 weight fragments of a
+// step into one of two register banks, two steps ahead.  Only the activation
+// tile, which all four waves read, goes through LDS, by direct-to-LDS loads
+// into a ring of kHStages stages (three steps ahead); the MFMAs of each
+// activation tile wait only for that tile's LDS read.  LDS traffic per step
+// and workgroup falls from 104 KiB (40 KiB written, 64 KiB read) to 40 KiB.
+// The launch guarantees nsteps % 4 == 0.  Packed weights only.
+constexpr int kHStages = 4;
+
+template <int MODE, bool OUTF32>
+__global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ffn_whyb_kernel(TiledArgs ta) {
+  const StreamArgs& a = ta.s;
+  __shared__ __attribute__((aligned(16))) char x0s[kDX];
+  __shared__ __attribute__((aligned(16))) char x1s[kDX];
+  __shared__ __attribute__((aligned(16))) char x2s[kDX];
+  __shared__ __attribute__((aligned(16))) char x3s[kDX];
+
+  TileWork tw;
+  if (!decode_work(ta, tw)) return;
+  const int g = tw.g, nt = tw.nt, c0 = tw.c0, R = tw.R;
+  const int64_t s0 = tw.s0, s1 = tw.s1;
+  const bool shared = tw.shared;
+  const int m0 = tw.mt * kTM;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int Kdim = a.Kdim;
+  const int ks = blockIdx.z;
+  const int kper = Kdim / a.ksplit;
+  const int kc0 = ks * kper / 32;
+  const int nsteps = kper / 32;
+
+  const int n0 = MODE == MODE_GATEUP ? nt * (kWN / 2) : nt * kWN;
+  const char* Wa;
+  const char* Wb = nullptr;
+  if (shared) { Wa = static_cast<const char*>(a.SW); Wb = static_cast<const char*>(a.SW3); }
+  else {
+    Wa = static_cast<const char*>(a.W) + (int64_t)g * a.N * Kdim * 2;
+    if (MODE == MODE_GATEUP) Wb = static_cast<const char*>(a.W3) + (int64_t)g * a.N * Kdim * 2;
+  }
+  const uint32_t wbytes = (uint32_t)a.N * Kdim * 2;
+  const __amdgpu_buffer_rsrc_t wra = buffer_rsrc(Wa, wbytes);
+  const __amdgpu_buffer_rsrc_t wrb = buffer_rsrc(MODE == MODE_GATEUP ? Wb : Wa, wbytes);
+  const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(a.X, (uint32_t)ta.x_bytes);
+  // weight fragment n of this wave: GATEUP n < 4 W1 rows n0 + 64 w + 16 n,
+  // n >= 4 the same rows of W3; DOWN W2 rows n0 + 128 w + 16 n
+  uint32_t pw[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const int row0 = MODE == MODE_GATEUP ? n0 + 64 * wave + 16 * (n & 3) : n0 + 128 * wave + 16 * n;
+    pw[n] = (uint32_t)(row0 / 16) * 16 * 128 * 2 + lane * 16;
+  }
+  auto wk = [&](int kc) -> uint32_t { return (uint32_t)(kc >> 2) * (a.N / 16) * 4096 + (kc & 3) * 1024; };
+  uint32_t xoff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int gr = m0 + (wave + 4 * q) * 16 + (lane & 15);
+    int64_t row = gr < c0 ? s0 + gr : (gr < R ? s1 + (gr - c0) : s0);   // pad rows read a valid row
+    if (a.gather_src) {
+      const int rank = gr < R ? gr : 0;
+      row = shared ? rank : a.gather_src[a.gather_off[g] + rank];
+    }
+    xoff[q] = (uint32_t)(row * a.ldx * 2) + 16 * (lane >> 4);
+  }
+
+  const int rows_here = min(kTM, R - m0);
+  const int mv = ((rows_here + 31) / 32) * 2;
+  auto run = [&](auto mvc) {
+    constexpr int MV = decltype(mvc)::value;
+    // activation loads of step st (clamped past the end) into stage S
+    auto issue_x = [&](auto sc, int st) {
+      constexpr int S = decltype(sc)::value;
+      char* xs = S == 0 ? x0s : S == 1 ? x1s : S == 2 ? x2s : x3s;
+      const int stc = st < nsteps ? st : nsteps - 1;
+      const uint32_t xso = (uint32_t)(kc0 + stc) * 64;
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, xs + (wave + 4 * q) * 1024, 16, xoff[q], xso, 0, 0);
+    };
+    // weight fragments of step st (clamped) into a register bank
+    auto load_w = [&](bf16x8* wb, int st) {
+      const int stc = st < nsteps ? st : nsteps - 1;
+      const uint32_t wso = wk(kc0 + stc);
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+        wb[n] = __builtin_bit_cast(bf16x8, buffer_load16(MODE == MODE_GATEUP && n >= 4 ? wrb : wra, pw[n], wso));
+    };
+    auto read_x = [&](auto sc, bf16x8* f) {
+      constexpr int S = decltype(sc)::value;
+      const char* xs = S == 0 ? x0s : S == 1 ? x1s : S == 2 ? x2s : x3s;
+#pragma unroll
+      for (int m = 0; m < MV; ++m) f[m] = *reinterpret_cast<const bf16x8*>(xs + m * 1024 + lane * 16);
+    };
+    f32x4 acc[MV][8];
+#pragma unroll
+    for (int m = 0; m < MV; ++m)
+#pragma unroll
+      for (int n = 0; n < 8; ++n) acc[m][n] = f32x4{0, 0, 0, 0};
+    bf16x8 w0[8], w1[8];   // weight banks of steps st and st + 1
+    bf16x8 xf[MV];         // activation fragments of step st
+    // Issue order: A0 A1 W0 A2 W1 (A: a step's activation stage, W: its
+    // weights), then per step st: A(st + 3), and after its MFMAs W(st + 2).
+    // At the top of step st the loads issued after A(st) are at most W(st-1)
+    // A(st+1) W(st) A(st+2) W(st+1), of which W(st-1) has already been
+    // waited for: vmcnt(20) means stage st has landed (exactly so at st = 0).
+    issue_x(IntC<0>{}, 0);
+    issue_x(IntC<1>{}, 1);
+    load_w(w0, 0);
+    issue_x(IntC<2>{}, 2);
+    load_w(w1, 1);
+    constexpr int kVm = 2 * 8 + 2 * 2;
+    constexpr int kWait = (kVm & 15) | ((kVm >> 4) << 14) | 0x70 | 0xF00;
+    auto step = [&](auto sc, auto nc, bf16x8* wc, int st) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kWait);       // this wave's loads of stage st landed
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): its reads of stage st - 1 are done
+      __builtin_amdgcn_s_barrier();            // every wave's: stage st readable, stage st - 1 free
+      issue_x(nc, st + kHStages - 1);
+      read_x(sc, xf);
+      __builtin_amdgcn_sched_barrier(0);       // every read issued before the first MFMA
+#pragma unroll
+      for (int m = 0; m < MV; ++m)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[m][n] = mfma16x16x32(wc[n], xf[m], acc[m][n]);
+      // the bank's next weights only after its last MFMA (else a third bank)
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(wc, st + 2);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int sb = 0; sb < nsteps; sb += 4) {
+      step(IntC<0>{}, IntC<3>{}, w0, sb);
+      step(IntC<1>{}, IntC<0>{}, w1, sb + 1);
+      step(IntC<2>{}, IntC<1>{}, w0, sb + 2);
+      step(IntC<3>{}, IntC<2>{}, w1, sb + 3);
+    }
+    // no load may land in LDS after the workgroup has ended
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+
+    // ---- epilogue: acc[m][n] holds D[w-row 4*(lane/16)+j of tile n][token lane%16 of tile m]
+    const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+      const int gr = m0 + m * 16 + lr;
+      if (gr >= R) continue;
+      const int64_t row = gr < c0 ? s0 + gr : s1 + (gr - c0);
+      if (MODE == MODE_GATEUP) {
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const f32x4 gt = acc[m][n], up = acc[m][n + 4];
+          const int ncol = n0 + 64 * wave + 16 * n + 4 * lg;
+          u32x2 o = {pack_bf16x2(silu_t(gt.x) * up.x, silu_t(gt.y) * up.y),
+                     pack_bf16x2(silu_t(gt.z) * up.z, silu_t(gt.w) * up.w)};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          const int ncol = n0 + 128 * wave + 16 * n + 4 * lg;
+          if constexpr (OUTF32) {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + ks * a.split_stride + row * a.ldo + ncol) = acc[m][n];
+          } else {
+            u32x2 o = {pack_bf16x2(acc[m][n].x, acc[m][n].y), pack_bf16x2(acc[m][n].z, acc[m][n].w)};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + row * a.ldo + ncol) = o;
+          }
+        }
+      }
+    }
+  };
+  switch (mv) {
+    case 2: run(IntC<2>{}); break;
+    case 4: run(IntC<4>{}); break;
+    case 6: run(IntC<6>{}); break;
+    default: run(IntC<8>{}); break;
+  }
+}
+
 bool tiled_supported(int mode, int fp8, int N, int Kdim, int ksplit) {
   if (fp8) return false;
   if (mode == MODE_GATEUP) { if (N % 128) return false; }
@@ -740,10 +922,20 @@ hipError_t launch_ffn_tiled(const TiledArgs& a, int fp8, int packed, int mode, i
   // the live work count by up to 7, always has a workgroup
   const int wn = wide ? (mode == MODE_GATEUP ? kWN / 2 : kWN) : (mode == MODE_GATEUP ? 128 : kTN);
   const dim3 grid(a.s.N / wn, max_tiles + 8, a.s.ksplit);
-  // packed weights take the wide tile with operands staged by direct-to-LDS
-  // loads; MOE_TILED_DMA=0 selects the register-staged wide kernel instead
+  // packed weights: by default the hybrid tile (weights to registers,
+  // activations by direct-to-LDS loads) where the K range is whole blocks of
+  // four 32-wide steps, else the all-LDS one; MOE_TILED_HYB=0 selects the
+  // all-LDS tile, MOE_TILED_DMA=0 the register-staged wide kernel
   const char* denv = getenv("MOE_TILED_DMA");
-  if (wide && packed && !(denv && denv[0] == '0')) {
+  const char* henv = getenv("MOE_TILED_HYB");
+  const bool dma_off = denv && denv[0] == '0';
+  if (wide && packed && !dma_off && !(henv && henv[0] == '0') && (a.s.Kdim / a.s.ksplit) % 128 == 0) {
+    if (mode == MODE_GATEUP) hipLaunchKernelGGL((ffn_whyb_kernel<MODE_GATEUP, false>), grid, dim3(kTThreads), 0, s, a);
+    else if (a.s.out_f32) hipLaunchKernelGGL((ffn_whyb_kernel<MODE_DOWN, true>), grid, dim3(kTThreads), 0, s, a);
+    else hipLaunchKernelGGL((ffn_whyb_kernel<MODE_DOWN, false>), grid, dim3(kTThreads), 0, s, a);
+    return hipGetLastError();
+  }
+  if (wide && packed && !dma_off) {
     if (mode == MODE_GATEUP) hipLaunchKernelGGL((ffn_wdma_kernel<MODE_GATEUP, false>), grid, dim3(kTThreads), 0, s, a);
     else if (a.s.out_f32) hipLaunchKernelGGL((ffn_wdma_kernel<MODE_DOWN, true>), grid, dim3(kTThreads), 0, s, a);
     else hipLaunchKernelGGL((ffn_wdma_kernel<MODE_DOWN, false>), grid, dim3(kTThreads), 0, s, a);

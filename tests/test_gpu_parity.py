@@ -359,16 +359,17 @@ def test_wide_tiled_kernel_matches_narrow(name, monkeypatch):
     (64) reduce every output over the same 32-wide K steps in the same order
     with the same MFMA: bit-identical outputs (MOE_TILED_WIDE=0 forces the
     narrow kernel), row-major and packed weights, gathered or permuted rows.
-    With packed weights the default wide kernel stages its operands by
-    direct-to-LDS loads; MOE_TILED_DMA=0 forces the register-staged one,
-    which must agree as well."""
+    With packed weights the default wide kernel loads weights into registers
+    and stages activations by direct-to-LDS loads; MOE_TILED_HYB=0 forces
+    the one that stages both through LDS, MOE_TILED_DMA=0 the
+    register-staged one: all must agree."""
     cfg = next(c for c in SMALL if c.name == name)
     for packed in (False, True):
         b = Built(cfg, packed=packed)
         lg = b.oracle_logits()
         for fused in (True, False):
             ref = b.run(lg, fused_gather=fused).clone()
-            for var in ("MOE_TILED_WIDE", "MOE_TILED_DMA"):
+            for var in ("MOE_TILED_WIDE", "MOE_TILED_DMA", "MOE_TILED_HYB"):
                 monkeypatch.setenv(var, "0")
                 try:
                     out = b.run(lg, fused_gather=fused).clone()
