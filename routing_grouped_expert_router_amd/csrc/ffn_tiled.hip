@@ -23,7 +23,7 @@
 //    dealt to the XCDs in contiguous chunks, so the row tiles that share a
 //    weight tile run back to back on one XCD and the later ones find it in
 //    that XCD's L2.  Groups with at most `min_rows` rows are left to the
-//    streaming kernel.
+//    streaming kernel (none are when groups are large on average).
 //  * A group's last row tile is usually partly empty (groups are 28..961
 //    rows at the prefill workload): the tile is run with only its non-empty
 //    32-row sub-tiles (a compile-time count, one instance per count), so no
@@ -31,6 +31,14 @@
 //  * Each output element accumulates its K range in 32-wide MFMA steps in
 //    ascending order, exactly as the streaming kernel does, so the split of
 //    groups between the two kernels does not change any bit of the result.
+//
+// Four kernels share the work list and that MFMA order (bit-identical
+// outputs): ffn_tiled_kernel, the tile above; ffn_wide_kernel, 128 token rows
+// x 512 weight rows with one wave per SIMD owning 128 x 128 outputs, operands
+// staged through registers; ffn_wdma_kernel, the wide tile with both operands
+// staged by direct-to-LDS loads; ffn_whyb_kernel, the wide tile with weights
+// straight to registers and only activations through LDS (the default for
+// packed weights whose K range is whole blocks of four 32-wide steps).
 #include <cstdlib>
 
 #include "common.hpp"
