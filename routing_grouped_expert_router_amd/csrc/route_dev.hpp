@@ -255,13 +255,19 @@ __device__ __forceinline__ void scan_all(const RouteArgs& a) {
   if (tid == 0) { bad_s = 0; nonfinite_s = 0; bad_ep_s = 0; }
   for (int p = tid; p <= NC; p += nth) { cnt[p] = 0; aux[p] = 0; }
   __syncthreads();
-  // per logical expert: exclusive prefix over blocks, and total T_l
+  // per logical expert: exclusive prefix over blocks, and total T_l (16
+  // blocks' counts loaded before any is overwritten, so the loads overlap)
   for (int l = tid; l < E; l += nth) {
     int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int c = a.ws.blk[(int64_t)b * E + l];
-      a.ws.blk[(int64_t)b * E + l] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) c[j] = b0 + j < nblk ? a.ws.blk[(int64_t)(b0 + j) * E + l] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (b0 + j < nblk) a.ws.blk[(int64_t)(b0 + j) * E + l] = run;
+        run += c[j];
+      }
     }
     tl_s[l] = run;
   }
