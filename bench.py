@@ -7,18 +7,25 @@ one stream, with inputs and weights already resident in HBM.  With bf16
 activations the permute is done by the gate/up kernel itself (it gathers
 each group's rows from x through the route tables).
 
-Default workload: the Mixtral-8x7B-shaped decode layer (E=8, K=2, H=4096,
-I=14336, bf16) at B=64 tokens; the other batch sizes of that workload are
-timed too and reported under "batches".  ``--workload`` picks another one.
+Default run: every workload at its full size -- the Mixtral-8x7B-shaped
+decode layer at B = 1, 8, 32, 64; the DeepSeek-V3-shaped fp8 decode layer at
+B = 32, 128, 256; the DeepSeek-V3-shaped bf16 prefill layer at T = 8192; the
+544-slot replica decode layer at B = 256 -- each under "batches" with its own
+roofline and diagnostics.  The headline value is the Mixtral-shaped B = 64
+decode layer.  ``--workload NAME`` times one workload only.
 
 Metric: decode MoE-layer latency (us), lower is better, with the expert-weight
-HBM bandwidth it implies: touched weight bytes (slots with >= 1 token, plus
-the shared expert and the router) / latency.  The roofline object is for the
-dominant kernel (expert gate/up): algorithmic bytes per launch (W1 + W3 of
-every touched slot) / its mean duration, measured with HIP events on the
-launch stream over the timed region.
+HBM bandwidth it implies (touched weight bytes -- slots with >= 1 token, plus
+the shared expert and the router -- over the latency); prefill TFLOP/s.  Each
+workload's roofline object is for its dominant kernel, expert gate/up:
+algorithmic bytes per launch (W1 + W3 of every touched slot) over its mean
+duration for decode, against 8 TB/s; algorithmic FLOPs per launch over its
+mean duration for prefill, against 2.5 PFLOP/s bf16.  Durations come from HIP
+events on the launch stream over the timed region.  The achievable peaks of
+the same device (a streaming read and a matrix-core loop, include/moe_probe.h)
+are measured in the same run and reported beside the spec peaks.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload NAME]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
 """
 from __future__ import annotations
 
@@ -38,10 +45,9 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mixtral_decode_b64")
-    ap.add_argument("--no-sweep", action="store_true", help="time only the named workload")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="time this workload only (default: all)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU reference timing")
     ap.add_argument("--row-major", action="store_true",
                     help="stream the row-major weights instead of the packed layout")
@@ -58,6 +64,7 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 512 MiB device copy three times (a kernel of known "
                          "traffic for scaling hardware byte counters)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak probes")
     return ap.parse_args()
 
 
@@ -146,6 +153,8 @@ class Setup:
                 ev[1].record()
             B.moe_quantize_1x128(L.h, B.buffer_rows(d), L.hq, L.hs)
             B.moe_expert_down_a8(d, L.weights, L.rt, T, L.hq, L.hs, L.y)
+            if ev is not None:
+                ev[2].record()
             B.moe_combine(d, L.rt, T, L.y, L.out)
             return
         gather = d.act_dtype == B.MOE_BF16     # the gate/up kernel gathers rows from x itself
@@ -160,6 +169,8 @@ class Setup:
         if ev is not None:
             ev[1].record()
         B.moe_expert_down(d, L.weights, L.rt, T, L.h, L.y)
+        if ev is not None:
+            ev[2].record()
         B.moe_combine(d, L.rt, T, L.y, L.out)
 
     def fused_ok(self):
@@ -201,9 +212,9 @@ class Setup:
 
 
 def time_workload(cfg, steps, warmup, packed=True, router="softmax", ep_ranks=1, a8=False):
-    """Eager steps (HIP events around the gate/up kernel on the launch
-    stream), then the same step captured once in a HIP graph and replayed
-    ``steps`` times (the layer latency reported)."""
+    """Eager steps (HIP events around the gate/up and down kernels on the
+    launch stream), then the same step captured once in a HIP graph and
+    replayed ``steps`` times (the layer latency reported)."""
     import torch
     s = Setup(cfg, packed, router, ep_ranks, a8)
     cfg = s.cfg
@@ -211,8 +222,7 @@ def time_workload(cfg, steps, warmup, packed=True, router="softmax", ep_ranks=1,
         s.step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -221,7 +231,8 @@ def time_workload(cfg, steps, warmup, packed=True, router="softmax", ep_ranks=1,
     end.record(stream)
     torch.cuda.synchronize()
     eager_ms = start.elapsed_time(end) / steps
-    gu_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
+    gu_ms = sum(a.elapsed_time(b) for a, b, _ in evs) / steps
+    down_ms = sum(b.elapsed_time(c) for _, b, c in evs) / steps
     ref = s.layer.out.clone()
 
     graph = torch.cuda.CUDAGraph()
@@ -241,9 +252,11 @@ def time_workload(cfg, steps, warmup, packed=True, router="softmax", ep_ranks=1,
     ms = start.elapsed_time(end) / steps
     slots, routed, gu_bytes, total = s.touched()
     status = int(s.layer.rt.status.item())
-    res = dict(cfg=cfg, ms=ms, eager_ms=eager_ms, gu_ms=gu_ms, wall=wall, slots=slots,
+    res = dict(cfg=cfg, ms=ms, eager_ms=eager_ms, gu_ms=gu_ms, down_ms=down_ms, wall=wall, slots=slots,
                routed_bytes=routed, gu_bytes=gu_bytes, total_bytes=total, status=status, setup=s,
-               gu_flops=s.gate_up_flops(), layer_flops=s.layer_flops())
+               gu_flops=s.gate_up_flops(), layer_flops=s.layer_flops(),
+               counts=s.layer.rt.counts.cpu().numpy(),
+               gu_kernel=s.B.expert_kernel(s.d, cfg.T, 0), down_kernel=s.B.expert_kernel(s.d, cfg.T, 1))
     del graph
     if s.fused_ok():
         # the single-launch step is reported beside the multi-launch one; a
@@ -291,17 +304,54 @@ def time_fused(s, steps, warmup, ref):
     return dict(fused_ms=start.elapsed_time(end) / steps, fused_eager_ms=eager_ms)
 
 
+def achievable_peaks(reps=5):
+    """Streaming-read GB/s over a 4 GiB buffer (16x the last-level cache) and
+    bf16 matrix-core TFLOP/s of a loop with no memory traffic, measured on
+    this device with HIP events (include/moe_probe.h)."""
+    import torch
+    from routing_grouped_expert_router_amd import binding as B
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(B.MOE_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        B.moe_probe_read(buf, sink)
+    start.record(stream)
+    for _ in range(reps):
+        B.moe_probe_read(buf, sink)
+    end.record(stream)
+    torch.cuda.synchronize()
+    read_gbs = buf.numel() * reps / (start.elapsed_time(end) * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs, iters = min(8 * cus, B.MOE_PROBE_SINK_WORDS), 10000
+    B.moe_probe_mfma_bf16(iters, wgs, sink)
+    start.record(stream)
+    for _ in range(reps):
+        B.moe_probe_mfma_bf16(iters, wgs, sink)
+    end.record(stream)
+    torch.cuda.synchronize()
+    flops = wgs * 4.0 * iters * 8 * 16384 * reps
+    mfma_tf = flops / (start.elapsed_time(end) * 1e-3) / 1e12
+    return {"hbm_read_gbs": round(read_gbs, 1), "mfma_bf16_tflops": round(mfma_tf, 1),
+            "how": "moe_probe_read: one non-temporal 16-byte-load pass over 4 GiB; moe_probe_mfma_bf16: "
+                   f"{wgs} workgroups x 4 waves x {iters} x 8 independent v_mfma_f32_16x16x32_bf16; "
+                   f"mean of {reps} launches timed with HIP events"}
+
+
 PREFILL_MIN_T = 1024   # token counts from here on are timed against the MFMA peak
 
-# sources of the decode gate/up kernel and its launch (the decode path never
-# launches the tiled kernel)
-KERNEL_SOURCES = ("common.hpp", "kernels.hpp", "stream_dev.hpp", "ffn_stream.hip", "moe_api.hip")
+DEFAULT_WORKLOADS = ["mixtral_decode_b1", "mixtral_decode_b8", "mixtral_decode_b32", "mixtral_decode_b64",
+                     "dsv3_decode_b32", "dsv3_decode_b128", "dsv3_decode_b256", "dsv3_prefill_t8192",
+                     "replica_decode_b256"]
+HEADLINE = "mixtral_decode_b64"
 
 
-def kernel_sources_hash() -> str:
+def kernel_sources_hash(files) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "routing_grouped_expert_router_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -311,17 +361,19 @@ def measured_traffic(workload: str):
     """HBM bytes per launch of the gate/up kernel from the committed counter
     summary (profiles/gate_up_traffic_<workload>.md: FETCH_SIZE and
     WRITE_SIZE passes scaled by a plain copy of known size), or None when
-    there is none or the kernel sources changed since it was taken."""
+    there is none or the kernel's sources (listed in the summary) changed
+    since it was taken."""
     path = os.path.join(ROOT, "profiles", f"gate_up_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
     vals = {}
     with open(path) as fh:
         for line in fh:
-            if ":" in line and not line.startswith((" ", "*", "#")):
+            if ":" in line and not line.startswith((" ", "*", "#", "|")):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_sources_sha256_16") != kernel_sources_hash():
+    files = vals.get("kernel_sources", "").split()
+    if not files or vals.get("kernel_sources_sha256_16") != kernel_sources_hash(files):
         return None
     try:
         return int(vals["traffic_bytes_per_launch"])
@@ -329,27 +381,66 @@ def measured_traffic(workload: str):
         return None
 
 
-def roofline(cfg, r):
+def roofline(cfg, r, peaks):
     """The dominant kernel (expert gate/up + SwiGLU) against its bound: HBM
     bytes for decode, bf16 MFMA FLOPs for prefill."""
-    kernel = "ffn_stream gate/up (W1+W3, SwiGLU)"
+    kernel = f"{r['gu_kernel']} gate/up (W1+W3, SwiGLU)"
     if cfg.T >= PREFILL_MIN_T:
         tf = r["gu_flops"] / (r["gu_ms"] * 1e-3) / 1e12
-        return {"bound": "mfma", "kernel": kernel, "achieved": round(tf, 1),
-                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                "traffic": None, "kernel_us": round(r["gu_ms"] * 1e3, 2),
-                "algorithmic_flops": r["gu_flops"]}
+        out = {"bound": "mfma", "kernel": kernel, "achieved": round(tf, 1),
+               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+               "traffic": measured_traffic(cfg.name), "kernel_us": round(r["gu_ms"] * 1e3, 2),
+               "algorithmic_flops": r["gu_flops"]}
+        if peaks:
+            out["achievable_peak"] = peaks["mfma_bf16_tflops"]
+            out["frac_of_achievable"] = round(tf / peaks["mfma_bf16_tflops"], 4)
+        return out
     gbs = r["gu_bytes"] / (r["gu_ms"] * 1e-3) / 1e9
-    return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(cfg.name),
-            "kernel_us": round(r["gu_ms"] * 1e3, 2), "algorithmic_bytes": r["gu_bytes"]}
+    out = {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+           "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+           "traffic": measured_traffic(cfg.name),
+           "kernel_us": round(r["gu_ms"] * 1e3, 2), "algorithmic_bytes": r["gu_bytes"]}
+    if peaks:
+        out["achievable_peak"] = peaks["hbm_read_gbs"]
+        out["frac_of_achievable"] = round(gbs / peaks["hbm_read_gbs"], 4)
+    return out
+
+
+def diagnostics(cfg, r, splits):
+    """The pages' cost terms for this batch ("推理 INFRA 方法论(5)", DeepGEMM
+    and C(B) sections): pad-row FLOP waste ceil(M_e/BM)*BM/M_e summed over
+    the groups at the row granularity the expert kernel skips empty rows at
+    (16-row MFMA tiles when streaming, 32-row sub-tiles in the large-group
+    kernels), rows sent to the spill region of a masked buffer, the
+    activation bytes the step moves (reported apart from the weight bytes),
+    and the expected distinct experts E*C(B) of a uniform router,
+    C(B) = 1 - (1 - K/E)^B, beside the slots the batch touched."""
+    import numpy as np
+    counts = np.asarray(r["counts"], dtype=np.int64)
+    T, K, H, I = cfg.T, cfg.K, cfg.H, cfg.I
+    gran = 16 if r["gu_kernel"] == "ffn_stream_kernel" else 32
+    rows = np.concatenate([counts[counts > 0], [T] * cfg.n_shared])
+    waste = float((-(-rows // gran) * gran).sum() / max(1, rows.sum()))
+    spill = int(np.maximum(counts - cfg.M_max, 0).sum()) if cfg.layout == "masked" else 0
+    grouped = T * K + cfg.n_shared * T
+    ybytes = 2 if splits == 1 else 4 * splits
+    act = (T * H * 2                    # x read by the router
+           + T * cfg.E * 4 * 2          # logits written and read
+           + grouped * H * 2            # rows gathered by gate/up
+           + grouped * I * 2 * 2        # h written and read
+           + grouped * H * ybytes * 2   # y written and read
+           + T * H * 2)                 # out
+    cb = 1.0 - (1.0 - K / cfg.E) ** T
+    return {"pad_flop_waste": round(waste, 4), "pad_rows_granularity": gran, "spill_rows": spill,
+            "activation_bytes": int(act), "weight_bytes": int(r["total_bytes"]),
+            "expected_experts_uniform": round(cfg.E * cb, 2), "touched_slots": r["slots"]}
 
 
 def cpu_baseline(s, budget_s=30.0):
     """The CPU reference, as it stands, on a bounded sample of the workload:
     all routing for the whole batch plus the expert FFN and combine for a
-    sample of tokens.  Returns (us per full layer call, sample description)."""
+    sample of tokens.  Returns (us per full layer call, sample description,
+    threads)."""
     import numpy as np
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from oracle import moe_oracle as O
@@ -393,6 +484,30 @@ def cpu_baseline(s, budget_s=30.0):
                       f"measured {dt:.1f} s, scaled by tokens", cores
 
 
+def batch_entry(r, peaks):
+    cfg = r["cfg"]
+    B = r["setup"].B
+    splits = B.down_splits(r["setup"].d, cfg.T)
+    e = {"latency_us": round(r["ms"] * 1e3, 2),
+         "eager_latency_us": round(r["eager_ms"] * 1e3, 2),
+         "gbs": round(r["total_bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
+         "layer_tflops": round(r["layer_flops"] / (r["ms"] * 1e-3) / 1e12, 2),
+         "gate_up_us": round(r["gu_ms"] * 1e3, 2),
+         "down_us": round(r["down_ms"] * 1e3, 2),
+         "down_kernel": r["down_kernel"],
+         "touched_slots": r["slots"],
+         "touched_bytes": r["total_bytes"],
+         "w_dtype": cfg.w_dtype,
+         "status": r["status"],
+         "roofline": roofline(cfg, r, peaks),
+         "diagnostics": diagnostics(cfg, r, splits),
+         "single_launch_latency_us": round(r["fused_ms"] * 1e3, 2) if "fused_ms" in r else None}
+    if cfg.T >= PREFILL_MIN_T:
+        down_flops = r["layer_flops"] - r["gu_flops"] - 2.0 * cfg.T * cfg.E * cfg.H
+        e["down_tflops"] = round(down_flops / (r["down_ms"] * 1e-3) / 1e12, 1)
+    return e
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -408,28 +523,34 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    cfg = configs.by_name(args.workload)
-    names = [cfg.name]
-    if not args.no_sweep and cfg.name.startswith("mixtral_decode_b"):
-        names = [f"mixtral_decode_b{b}" for b in (1, 8, 32, 64)]
+    names = [configs.by_name(args.workload).name] if args.workload else list(DEFAULT_WORKLOADS)
+    head_name = HEADLINE if HEADLINE in names else names[0]
+    peaks = None
+    if not args.no_peaks:
+        peaks = achievable_peaks()
+        print(f"# achievable: streaming read {peaks['hbm_read_gbs']:.0f} GB/s, "
+              f"bf16 MFMA {peaks['mfma_bf16_tflops']:.0f} TFLOP/s", file=sys.stderr, flush=True)
     results = {}
     for n in names:
         c = configs.by_name(n)
         r = time_workload(c, args.steps, args.warmup, packed=not args.row_major,
                           router=args.router, ep_ranks=args.ep_ranks, a8=args.a8)
         results[n] = r
+        r["entry"] = batch_entry(r, peaks)
         print(f"# {n}: {r['ms']*1e3:.1f} us/layer (graph), {r['eager_ms']*1e3:.1f} eager, "
-              f"gate/up {r['gu_ms']*1e3:.1f} us ({r['gu_flops']/(r['gu_ms']*1e-3)/1e12:.0f} TFLOP/s), "
+              f"gate/up {r['gu_ms']*1e3:.1f} us ({r['gu_flops']/(r['gu_ms']*1e-3)/1e12:.0f} TFLOP/s, "
+              f"{r['gu_kernel']}), down {r['down_ms']*1e3:.1f} us, "
               f"layer {r['layer_flops']/(r['ms']*1e-3)/1e12:.0f} TFLOP/s, "
               f"slots {r['slots']}, touched {r['total_bytes']/1e9:.3f} GB -> "
               f"{r['total_bytes']/(r['ms']*1e-3)/1e9:.0f} GB/s, status {r['status']}"
               + (f"; single launch {r['fused_ms']*1e3:.1f} us (graph), {r['fused_eager_ms']*1e3:.1f} eager"
                  if "fused_ms" in r else ""),
               file=sys.stderr, flush=True)
-        if n != cfg.name:
+        if n != head_name:
             del r["setup"]
             torch.cuda.empty_cache()
-    head = results[cfg.name]
+    head = results[head_name]
+    cfg = head["cfg"]
     lat_us = head["ms"] * 1e3
     gb_s = head["total_bytes"] / (head["ms"] * 1e-3) / 1e9
     cpu = None
@@ -437,6 +558,7 @@ def main():
         us, sample, cores = cpu_baseline(head["setup"])
         cpu = {"value": round(us, 1), "unit": "us", "cores": cores, "kind": "oracle",
                "sample": sample}
+    prefill = next((results[n] for n in names if configs.by_name(n).T >= PREFILL_MIN_T), None)
     out = {
         "metric": "decode MoE-layer latency (us) + expert-weight HBM GB/s; prefill TFLOP/s",
         "value": round(lat_us, 2),
@@ -463,20 +585,18 @@ def main():
                     "local_slots": head["cfg"].E_phys}},
         "expert_weight_hbm_gbs": round(gb_s, 1),
         "layer_tflops": round(head["layer_flops"] / (head["ms"] * 1e-3) / 1e12, 2),
+        "prefill_tflops": None if prefill is None else
+        round(prefill["layer_flops"] / (prefill["ms"] * 1e-3) / 1e12, 1),
         "touched_slots": head["slots"],
         "touched_bytes": head["total_bytes"],
-        "roofline": roofline(cfg, head),
+        "roofline": head["entry"]["roofline"],
         "cpu_baseline": cpu,
+        "achievable_peaks": peaks,
         "eager_latency_us": round(head["eager_ms"] * 1e3, 2),
         "timing": "HIP graph of one layer step replayed `steps` times between HIP events "
-                  "on the launch stream; eager_latency_us is the same step launched directly",
-        "batches": {n: {"latency_us": round(r["ms"] * 1e3, 2),
-                        "eager_latency_us": round(r["eager_ms"] * 1e3, 2),
-                        "gbs": round(r["total_bytes"] / (r["ms"] * 1e-3) / 1e9, 1),
-                        "gate_up_us": round(r["gu_ms"] * 1e3, 2),
-                        "touched_slots": r["slots"],
-                        "single_launch_latency_us": round(r["fused_ms"] * 1e3, 2) if "fused_ms" in r else None}
-                    for n, r in results.items()},
+                  "on the launch stream; eager_latency_us is the same step launched directly; "
+                  "kernel times from HIP events around each expert kernel in the eager steps",
+        "batches": {n: r["entry"] for n, r in results.items()},
     }
     print(json.dumps(out), flush=True)
 

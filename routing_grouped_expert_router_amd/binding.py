@@ -22,23 +22,28 @@ MOE_CONTIG, MOE_MASKED = 0, 1
 MOE_STATUS_SPILL, MOE_STATUS_BAD_REPLICA, MOE_STATUS_NONFINITE, MOE_STATUS_INTERNAL = 1, 2, 4, 8
 MOE_STATUS_BAD_EP_MAP, MOE_STATUS_RECV_OVERFLOW, MOE_STATUS_SYNC_TIMEOUT = 16, 32, 64
 MOE_EP_LINEAR, MOE_EP_ROUND_ROBIN = 0, 1
+MOE_DEBUG_NBLK_MASK, MOE_DEBUG_TILED_SHIFT, MOE_DEBUG_FUSED_NO_WAIT = 0xF, 4, 0x100
+MOE_DEBUG_TILED_NARROW, MOE_DEBUG_TILED_WIDE_REGS, MOE_DEBUG_TILED_WIDE_LDS, MOE_DEBUG_TILED_WIDE_HYB = 1, 2, 3, 4
 
 EXPORTED = [
     "moe_status_string", "moe_check_desc", "moe_route_workspace_bytes", "moe_buffer_rows",
-    "moe_shared_base", "moe_down_splits", "moe_y_bytes", "moe_router_logits", "moe_route",
+    "moe_shared_base", "moe_down_splits", "moe_y_bytes", "moe_y_bytes_max", "moe_workspace_bytes",
+    "moe_router_logits", "moe_route",
     "moe_route_grouped",
     "moe_permute", "moe_expert_gate_up", "moe_expert_gate_up_x", "moe_expert_down",
     "moe_grouped_ffn", "moe_grouped_ffn_x", "moe_combine", "moe_forward", "moe_pack_weights",
     "moe_replica_map_from_p2l", "moe_route_ep", "moe_route_received", "moe_ep_local_map",
     "moe_eplb_plan", "moe_quantize_1x128", "moe_expert_gate_up_a8", "moe_expert_down_a8",
     "moe_grouped_ffn_a8", "moe_decode_fused_workspace_bytes", "moe_decode_fused",
+    "moe_expert_kernel", "moe_probe_read", "moe_probe_mfma_bf16",
 ]
+MOE_PROBE_SINK_WORDS = 8192
 
 
 class moe_desc_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T_max", "H", "I", "E", "E_phys", "K", "n_shared", "max_replicas",
-        "act_dtype", "w_dtype", "layout", "M_max", "BM", "w_packed")]
+        "act_dtype", "w_dtype", "layout", "M_max", "BM", "w_packed", "debug_flags")]
 
 
 _P = ctypes.c_void_p
@@ -88,6 +93,8 @@ def lib() -> ctypes.CDLL:
             "moe_shared_base": (i64, [D]),
             "moe_down_splits": (i32, [D, i32]),
             "moe_y_bytes": (sz, [D, i32]),
+            "moe_y_bytes_max": (sz, [D]),
+            "moe_workspace_bytes": (sz, [D]),
             "moe_router_logits": (ctypes.c_int, [D, _P, _P, _P, i32, _P, _P]),
             "moe_route": (ctypes.c_int, [D, _P, i32, _P, _P, R, _P, sz, _P]),
             "moe_route_grouped": (ctypes.c_int, [D, _P, i32, GR, _P, _P, R, _P, sz, _P]),
@@ -112,6 +119,9 @@ def lib() -> ctypes.CDLL:
             "moe_expert_down_a8": (ctypes.c_int, [D, W, R, i32, _P, _P, _P, _P]),
             "moe_grouped_ffn_a8": (ctypes.c_int, [D, W, R, i32, _P, _P, _P, _P, _P, _P, _P, _P]),
             "moe_decode_fused_workspace_bytes": (sz, [D]),
+            "moe_expert_kernel": (ctypes.c_char_p, [D, i32, i32]),
+            "moe_probe_read": (ctypes.c_int, [_P, sz, _P, _P]),
+            "moe_probe_mfma_bf16": (ctypes.c_int, [i32, i32, _P, _P]),
             "moe_decode_fused": (ctypes.c_int, [D, _P, _P, _P, GR, _P, _P, W, i32, _P, R, _P, sz, _P, _P,
                                                 _P, _P, sz, _P]),
         }
@@ -159,6 +169,7 @@ class Desc:
     M_max: int = 1
     BM: int = 16
     w_packed: int = 0
+    debug_flags: int = 0
 
     def c(self) -> moe_desc_t:
         return moe_desc_t(*[int(getattr(self, f)) for f, _ in moe_desc_t._fields_])
@@ -197,6 +208,34 @@ def down_splits(d: Desc, T: int) -> int:
 
 def y_bytes(d: Desc, T: int) -> int:
     return lib().moe_y_bytes(ctypes.byref(d.c()), T)
+
+
+def y_bytes_max(d: Desc) -> int:
+    return lib().moe_y_bytes_max(ctypes.byref(d.c()))
+
+
+def workspace_bytes(d: Desc) -> int:
+    return lib().moe_workspace_bytes(ctypes.byref(d.c()))
+
+
+def expert_kernel(d: Desc, T: int, which: int) -> str:
+    """Name of the kernel the expert call runs for the largest groups
+    (which = 0 gate/up, 1 down)."""
+    return lib().moe_expert_kernel(ctypes.byref(d.c()), T, which).decode()
+
+
+# ---- measurement probes (include/moe_probe.h) ---------------------------------
+
+def moe_probe_read(buf, sink, stream=None):
+    """One non-temporal streaming read of the device tensor ``buf``."""
+    _check(lib().moe_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)),
+           "moe_probe_read")
+
+
+def moe_probe_mfma_bf16(iters: int, workgroups: int, sink, stream=None):
+    """``workgroups`` x 4 waves x ``iters`` x 8 bf16 16x16x32 matrix-core
+    products (16384 FLOP each), no memory traffic."""
+    _check(lib().moe_probe_mfma_bf16(iters, workgroups, _ptr(sink), _stream(stream)), "moe_probe_mfma_bf16")
 
 
 # ---- buffers ------------------------------------------------------------------
@@ -299,6 +338,16 @@ def moe_expert_down(d: Desc, w: Weights, rt: RouteTables, T, h, y, stream=None):
 def moe_combine(d: Desc, rt: RouteTables, T, y, out, stream=None):
     _check(lib().moe_combine(ctypes.byref(d.c()), ctypes.byref(rt.c), T, _ptr(y), _ptr(out),
                              _stream(stream)), "moe_combine")
+
+
+def moe_forward(d: Desc, x, w_router, bias, w: Weights, T, logits, rt: RouteTables, ws, xg, h, y, out,
+                l2p=None, replica_count=None, stream=None):
+    """The five steps in one C call (router logits, moe_route, permute or the
+    fused gather, grouped FFN, combine)."""
+    _check(lib().moe_forward(ctypes.byref(d.c()), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(l2p),
+                             _ptr(replica_count), ctypes.byref(w.c), T, _ptr(logits), ctypes.byref(rt.c),
+                             _ptr(ws), ws.numel() * ws.element_size(), _ptr(xg), _ptr(h), _ptr(y), _ptr(out),
+                             _stream(stream)), "moe_forward")
 
 
 def moe_pack_weights(d: Desc, which: int, src, dst, stream=None):
@@ -433,9 +482,8 @@ class MoELayer:
         rows = buffer_rows(d)
         self.xg = torch.zeros((rows, d.H), dtype=torch.bfloat16, device=device)
         self.h = torch.zeros((rows, d.I), dtype=torch.bfloat16, device=device)
-        # the down projection splits K more for fewer tokens: size y for the worst T
-        ymax = max(y_bytes(d, t) for t in {1, d.T_max} if t <= max(1, d.T_max))
-        self.y = torch.zeros(ymax, dtype=torch.uint8, device=device)
+        # the down projection splits K more for fewer tokens: size y for every T
+        self.y = torch.zeros(y_bytes_max(d), dtype=torch.uint8, device=device)
         self.logits = torch.zeros((max(1, d.T_max), d.E), dtype=torch.float32, device=device)
         self.w_router = w_router
         self.bias = bias

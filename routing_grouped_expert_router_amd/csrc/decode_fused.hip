@@ -329,14 +329,10 @@ hipError_t launch_decode_fused(FusedArgs f, int fp8, hipStream_t s) {
   // fewer workgroups than fit are resident all the same
   f.grid = std::min(decode_fused_grid(fp8), kFusedMaxGrid);
   if (f.grid < 2) return hipErrorInvalidConfiguration;
-  // MOE_FUSED_SPIN_LIMIT (polls per wait, >= 0) shortens the bound, so that
-  // tests can take the timeout path: a workgroup that must wait longer
-  // aborts the launch instead
-  f.spin_limit = kSpinLimit;
-  if (const char* env = getenv("MOE_FUSED_SPIN_LIMIT")) {
-    const int v = atoi(env);
-    if (v >= 0 && v < kSpinLimit) f.spin_limit = v;
-  }
+  // MOE_DEBUG_FUSED_NO_WAIT (f.no_wait) bounds every wait at zero polls, so
+  // that tests can take the timeout path: a workgroup that must wait aborts
+  // the launch instead
+  f.spin_limit = f.no_wait ? 0 : kSpinLimit;
   if (fp8) hipLaunchKernelGGL(decode_fused_kernel<true>, dim3(f.grid), dim3(kThreads), 0, s, f);
   else hipLaunchKernelGGL(decode_fused_kernel<false>, dim3(f.grid), dim3(kThreads), 0, s, f);
   return hipGetLastError();

@@ -100,6 +100,10 @@ moe_status_t moe_check_desc(const moe_desc_t* d) {
   if (d->H % 128 || d->I % 128) return MOE_ERR_UNSUPPORTED;
   if (d->E > 1024 || d->E_phys > kMaxE || d->K > kMaxK) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)d->T_max * d->K > (int64_t)INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  const uint32_t dbg = (uint32_t)d->debug_flags;
+  if (dbg & ~(MOE_DEBUG_NBLK_MASK | MOE_DEBUG_TILED_MASK | MOE_DEBUG_FUSED_NO_WAIT)) return MOE_ERR_ARG;
+  if ((dbg & MOE_DEBUG_NBLK_MASK) > 8 || ((dbg & MOE_DEBUG_TILED_MASK) >> MOE_DEBUG_TILED_SHIFT) > kTiledVariants)
+    return MOE_ERR_ARG;
   return MOE_OK;
 }
 
@@ -107,6 +111,8 @@ size_t moe_route_workspace_bytes(const moe_desc_t* d) {
   if (moe_check_desc(d) != MOE_OK) return 0;
   return ws_layout(d).total;
 }
+
+size_t moe_workspace_bytes(const moe_desc_t* d) { return moe_route_workspace_bytes(d); }
 
 int64_t moe_shared_base(const moe_desc_t* d) {
   if (moe_check_desc(d) != MOE_OK) return -1;
@@ -133,6 +139,22 @@ size_t moe_y_bytes(const moe_desc_t* d, int32_t T) {
   if (s <= 0) return 0;
   const size_t plane = (size_t)moe_buffer_rows(d) * d->H;
   return s == 1 ? plane * 2 : plane * 4 * s;
+}
+
+size_t moe_y_bytes_max(const moe_desc_t* d) {
+  if (moe_check_desc(d) != MOE_OK) return 0;
+  // T enters the split rule only through min(T*K, E_phys), so the token
+  // counts up to ceil(E_phys / K) cover every case
+  const int32_t tcap = std::min<int64_t>(d->T_max > 0 ? d->T_max : 1, ((int64_t)d->E_phys + d->K - 1) / d->K);
+  size_t best = 0;
+  int32_t last = -1;
+  for (int32_t T = 1; T <= std::max<int32_t>(1, tcap); ++T) {
+    const int32_t s = moe_down_splits(d, T);
+    if (s == last) continue;           // same split, same size
+    last = s;
+    best = std::max(best, moe_y_bytes(d, T));
+  }
+  return best;
 }
 
 moe_status_t moe_router_logits(const moe_desc_t* d, const void* x, const void* w_router,
@@ -295,15 +317,17 @@ moe_status_t ffn_common_checks(const moe_desc_t* d, const moe_weights_t* w, cons
 // longer workgroups would leave the chip idle at the end of the launch.
 // Measured: it pays for fp8 down projections with K = 2048 and costs time for
 // bf16 ones with long K ranges; a bf16 K range of at most 8 steps (a 128 KiB
-// stream per block) walks two blocks.  MOE_STREAM_NBLK (1..8, dividing N/64)
+// stream per block) walks two blocks.  moe_desc_t.debug_flags (MOE_DEBUG_NBLK_MASK)
 // overrides the choice.
+int debug_nblk(const moe_desc_t* d, int nblocks) {
+  const int v = (int)((uint32_t)d->debug_flags & MOE_DEBUG_NBLK_MASK);
+  return (v >= 1 && v <= 8 && nblocks % v == 0) ? v : 0;
+}
+
 int stream_nblk(const moe_desc_t* d, int32_t T, const StreamArgs& a, bool fp8) {
   const int nblocks = a.N / 64;
   const int steps = a.Kdim / 128 / a.ksplit;
-  if (const char* env = getenv("MOE_STREAM_NBLK")) {
-    const int v = atoi(env);
-    if (v >= 1 && v <= 8 && nblocks % v == 0) return v;
-  }
+  if (const int v = debug_nblk(d, nblocks)) return v;
   const int64_t TK = (int64_t)T * d->K;
   const int64_t groups = (TK < d->E_phys ? TK : d->E_phys) + d->n_shared;
   if (!fp8)
@@ -315,19 +339,41 @@ int stream_nblk(const moe_desc_t* d, int32_t T, const StreamArgs& a, bool fp8) {
   return nb;
 }
 
-moe_status_t launch_expert_gemm(const moe_desc_t* d, const moe_route_t* r, int32_t T, StreamArgs a,
-                                bool fp8, int mode, dim3 stream_grid, hipStream_t stream) {
-  const int mt = stream_mt(d, T);
-  a.nblk = stream_nblk(d, T, a, fp8);
-  stream_grid.x = a.N / (64 * a.nblk);
+// Which size classes a launch has (see launch_expert_gemm).
+struct GemmPlan {
+  int mt;          // row tiles per pass of region A
+  int a_max;       // rows region A takes
+  bool need_b;     // region B (streamed in passes of several tiles)
+  bool need_c;     // the tiled kernel for large groups
+  bool all_tiled;  // every group in the tiled launch, no streaming launch
+};
+
+GemmPlan plan_expert_gemm(const moe_desc_t* d, int32_t T, const StreamArgs& a, bool fp8, int mode) {
+  GemmPlan p;
+  p.mt = stream_mt(d, T);
   const bool tiled = tiled_supported(mode, fp8, a.N, a.Kdim, a.ksplit);
-  const int a_max = 16 * mt;
-  const bool need_b = mt < 4 && T > a_max;   // a group may outgrow region A
+  p.a_max = 16 * p.mt;
+  p.need_b = p.mt < 4 && T > p.a_max;   // a group may outgrow region A
   // The tiled kernel pays only when groups are large on average (T*K/E_phys
   // >= 64 rows, prefill); at decode sizes a few hot groups above 64 rows
   // occupy too few workgroups in a launch of their own (measured on the
   // replica workload: 1036 -> 970 us), so region B streams them, in passes.
-  const bool need_c = tiled && T > 64 && (int64_t)T * d->K >= (int64_t)64 * d->E_phys;
+  p.need_c = tiled && T > 64 && (int64_t)T * d->K >= (int64_t)64 * d->E_phys;
+  // Groups large on average with region A alone streaming (no region B):
+  // the few groups of at most a_max rows join the tiled launch, where they
+  // overlap the large ones, instead of a streaming launch too small to fill
+  // the GPU (DeepSeek-V3-shaped prefill T=8192: about 5 such experts)
+  p.all_tiled = p.need_c && !p.need_b;
+  return p;
+}
+
+moe_status_t launch_expert_gemm(const moe_desc_t* d, const moe_route_t* r, int32_t T, StreamArgs a,
+                                bool fp8, int mode, dim3 stream_grid, hipStream_t stream) {
+  const GemmPlan pl = plan_expert_gemm(d, T, a, fp8, mode);
+  const int mt = pl.mt, a_max = pl.a_max;
+  const bool need_b = pl.need_b, need_c = pl.need_c;
+  a.nblk = stream_nblk(d, T, a, fp8);
+  stream_grid.x = a.N / (64 * a.nblk);
   a.max_rows = (need_b || need_c) ? a_max : 0;
   a.b_rows = 0;
   a.shared_chunks = 1;
@@ -343,11 +389,7 @@ moe_status_t launch_expert_gemm(const moe_desc_t* d, const moe_route_t* r, int32
     a.b_rows = d->E_phys + d->n_shared * a.shared_chunks;
     grid.y += a.b_rows;
   }
-  // Groups large on average with region A alone streaming (no region B):
-  // the few groups of at most a_max rows join the tiled launch, where they
-  // overlap the large ones, instead of a streaming launch too small to fill
-  // the GPU (DeepSeek-V3-shaped prefill T=8192: about 5 such experts)
-  const bool all_tiled = need_c && !need_b;
+  const bool all_tiled = pl.all_tiled;
   if (!all_tiled) {
     hipError_t e = launch_ffn_stream(a, fp8, d->w_packed, mode, mt, grid, stream);
     if (e != hipSuccess) return hip_status(e);
@@ -356,12 +398,18 @@ moe_status_t launch_expert_gemm(const moe_desc_t* d, const moe_route_t* r, int32
   TiledArgs ta;
   ta.s = a;
   ta.tile_off = r->tile_off;
+  ta.variant = (int)(((uint32_t)d->debug_flags & MOE_DEBUG_TILED_MASK) >> MOE_DEBUG_TILED_SHIFT);
   ta.min_rows = all_tiled ? 0 : (mt < 4) ? 64 : a_max;
   // X holds the layer input (T rows) when gathering, else the grouped buffer
   ta.x_bytes = (a.gather_src ? (int64_t)T : moe_buffer_rows(d)) * a.ldx * 2;
+  // static bound on the live row tiles: a routed layout holds T*K rows in
+  // at most E_phys groups; received counts (moe_route_received) fill up to
+  // M_max rows of every slot whatever T*K is
   const int64_t TK = (int64_t)T * d->K;
-  const int64_t max_tiles = (TK + kTileRows - 1) / kTileRows + d->E_phys +
-                            (d->n_shared ? (T + kTileRows - 1) / kTileRows : 0);
+  int64_t routed_tiles = (TK + kTileRows - 1) / kTileRows + d->E_phys;
+  if (d->layout == MOE_MASKED)
+    routed_tiles = std::max(routed_tiles, (int64_t)d->E_phys * ((d->M_max + kTileRows - 1) / kTileRows));
+  const int64_t max_tiles = routed_tiles + (d->n_shared ? (T + kTileRows - 1) / kTileRows : 0);
   return hip_status(launch_ffn_tiled(ta, fp8, d->w_packed, mode, (int)max_tiles, stream));
 }
 
@@ -467,6 +515,23 @@ moe_status_t moe_grouped_ffn_x(const moe_desc_t* d, const moe_weights_t* w, cons
   return moe_expert_down(d, w, r, T, h, y, stream);
 }
 
+const char* moe_expert_kernel(const moe_desc_t* d, int32_t T, int32_t which) {
+  if (moe_check_desc(d) != MOE_OK || T <= 0 || T > d->T_max || (which != 0 && which != 1)) return "none";
+  const bool fp8 = d->w_dtype == MOE_FP8E4M3_B128;
+  moe_route_t r = {};                          // table pointers are not read here
+  moe_weights_t w = {};
+  const bool gather = d->act_dtype == MOE_BF16;
+  const StreamArgs a = which == 0 ? gate_up_args(d, &w, &r, T, nullptr, gather, nullptr)
+                                  : down_args(d, &w, &r, T, nullptr, nullptr);
+  const GemmPlan pl = plan_expert_gemm(d, T, a, fp8, which == 0 ? MODE_GATEUP : MODE_DOWN);
+  if (!pl.need_c) return "ffn_stream_kernel";
+  TiledArgs ta = {};
+  ta.s = a;
+  ta.x_bytes = (which == 0 && gather ? (int64_t)T : moe_buffer_rows(d)) * a.ldx * 2;
+  ta.variant = (int)(((uint32_t)d->debug_flags & MOE_DEBUG_TILED_MASK) >> MOE_DEBUG_TILED_SHIFT);
+  return tiled_kernel_name(tiled_choice(ta, d->w_packed, which == 0 ? MODE_GATEUP : MODE_DOWN));
+}
+
 moe_status_t moe_quantize_1x128(const void* src, int64_t ld, int64_t rows, int32_t C, void* q,
                                 float* s, hipStream_t stream) {
   if (rows < 0 || C < 128 || C % 128 || ld < C) return MOE_ERR_ARG;
@@ -501,14 +566,11 @@ A8Args a8_base_args(const moe_desc_t* d, const moe_route_t* r, int32_t T) {
 
 // 64-row output blocks per W8A8 workgroup: as the streaming kernel's fp8 rule
 // (stream_nblk), several blocks walked as one pipeline of at most 64 K steps
-// while at least 6144 workgroups remain.  MOE_STREAM_NBLK overrides it.
+// while at least 6144 workgroups remain.  MOE_DEBUG_NBLK_MASK overrides it.
 int a8_nblk(const moe_desc_t* d, int32_t T, const A8Args& a) {
   const int nblocks = a.N / 64;
   const int steps = a.Kdim / 128 / a.ksplit;
-  if (const char* env = getenv("MOE_STREAM_NBLK")) {
-    const int v = atoi(env);
-    if (v >= 1 && v <= 8 && nblocks % v == 0) return v;
-  }
+  if (const int v = debug_nblk(d, nblocks)) return v;
   const int64_t TK = (int64_t)T * d->K;
   const int64_t groups = (TK < d->E_phys ? TK : d->E_phys) + d->n_shared;
   int nb = 1;
@@ -647,6 +709,7 @@ moe_status_t moe_decode_fused(const moe_desc_t* d, const void* x, const void* w_
   f.g1 = gate_up_args(d, w, r, T, x, true, h);
   f.g2 = down_args(d, w, r, T, h, y);
   f.comb = combine_args(d, r, T, y, out);
+  f.no_wait = ((uint32_t)d->debug_flags & MOE_DEBUG_FUSED_NO_WAIT) ? 1 : 0;
   f.sync = static_cast<uint32_t*>(fws);
   f.act = reinterpret_cast<int32_t*>(static_cast<char*>(fws) + kFusedSyncBytes);
   return hip_status(launch_decode_fused(f, fp8, stream));

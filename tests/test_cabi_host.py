@@ -16,7 +16,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    txt = open(os.path.join(ROOT, "include", "moe.h")).read()
+    inc = os.path.join(ROOT, "include")
+    txt = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
     return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", txt)))
 
@@ -48,6 +49,18 @@ def _d(**kw):
 ])
 def test_desc_validation(kw, code):
     assert B.check_desc(_d(**kw)) == code
+
+
+@pytest.mark.parametrize("flags,code", [
+    (0, B.MOE_OK), (8, B.MOE_OK), (9, B.MOE_ERR_ARG),
+    (B.MOE_DEBUG_TILED_WIDE_HYB << B.MOE_DEBUG_TILED_SHIFT, B.MOE_OK),
+    (15 << B.MOE_DEBUG_TILED_SHIFT, B.MOE_ERR_ARG), (B.MOE_DEBUG_FUSED_NO_WAIT, B.MOE_OK),
+    (0x200, B.MOE_ERR_ARG), (-1, B.MOE_ERR_ARG),
+])
+def test_debug_flags_validation(flags, code):
+    """The test switches in moe_desc_t.debug_flags are checked like every
+    other field: unknown bits and out-of-range values are argument errors."""
+    assert B.check_desc(_d(debug_flags=flags)) == code
 
 
 def test_calls_reject_bad_arguments_before_enqueueing():
@@ -156,6 +169,12 @@ def test_buffer_sizing_formulas(cfg):
     plane = B.buffer_rows(d) * cfg.H
     assert B.y_bytes(d, cfg.T) == (plane * 2 if s == 1 else plane * 4 * s)
     assert B.route_workspace_bytes(d) >= 4 * cfg.T * cfg.K
+    assert B.workspace_bytes(d) == B.route_workspace_bytes(d)
+    # one y buffer for every T: moe_y_bytes_max bounds moe_y_bytes at each T
+    ymax = B.y_bytes_max(d)
+    ts = sorted({1, 2, 3, cfg.T} | set(range(1, cfg.T + 1, max(1, cfg.T // 64))))
+    assert ymax == max(B.y_bytes(d, t) for t in range(1, cfg.T + 1)) if cfg.T <= 512 else \
+        ymax >= max(B.y_bytes(d, t) for t in ts)
 
 
 def test_replica_map_helper_matches_reference_and_page():
@@ -204,3 +223,28 @@ def test_eplb_plan_helper_matches_reference():
                          ([], 0, 1), ([1.0], -1, 1)):
         with pytest.raises(B.MoEError):
             B.moe_eplb_plan(load, nr, ep)
+
+
+def test_expert_kernel_names_follow_the_size_classes():
+    """The kernel a call runs for its largest groups: the streaming kernel
+    for decode-sized groups, a large-group kernel for the prefill batch
+    (packed weights, fused gather), the narrow tile when forced."""
+    dec = B.Desc.from_config(configs.mixtral_decode(64), w_packed=1)
+    assert B.expert_kernel(dec, 64, 0) == "ffn_stream_kernel"
+    pre = B.Desc.from_config(configs.dsv3_prefill(), w_packed=1)
+    assert B.expert_kernel(pre, 8192, 0) != "ffn_stream_kernel"
+    assert B.expert_kernel(pre, 8192, 1) != "ffn_stream_kernel"
+    pre.debug_flags = B.MOE_DEBUG_TILED_NARROW << B.MOE_DEBUG_TILED_SHIFT
+    assert B.expert_kernel(pre, 8192, 0) == "ffn_tiled_kernel"
+    assert B.expert_kernel(pre, 0, 0) == "none" and B.expert_kernel(pre, 8192, 2) == "none"
+
+
+def test_probes_reject_bad_arguments():
+    L = B.lib()
+    fake = ctypes.c_void_p(256)
+    assert L.moe_probe_read(fake, 100, fake, None) == B.MOE_ERR_ARG          # not a multiple of 16
+    assert L.moe_probe_read(None, 1024, fake, None) == B.MOE_ERR_ARG
+    assert L.moe_probe_read(fake, 0, fake, None) == B.MOE_ERR_ARG
+    assert L.moe_probe_mfma_bf16(0, 8, fake, None) == B.MOE_ERR_ARG
+    assert L.moe_probe_mfma_bf16(10, B.MOE_PROBE_SINK_WORDS + 1, fake, None) == B.MOE_ERR_ARG
+    assert L.moe_probe_mfma_bf16(10, 8, None, None) == B.MOE_ERR_ARG

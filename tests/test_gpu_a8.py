@@ -101,16 +101,18 @@ def test_two_level_accumulation_at_k16k_all_positive():
 
 
 @pytest.mark.parametrize("nblk", [2, 4])
-def test_a8_block_walk_gives_identical_outputs(nblk, monkeypatch):
-    """1, 2 or 4 output blocks per W8A8 workgroup (MOE_STREAM_NBLK) reduce
-    every output over the same K steps in the same order: bit-identical
-    layer outputs, both size classes (T > 16)."""
+def test_a8_block_walk_gives_identical_outputs(nblk):
+    """1, 2 or 4 output blocks per W8A8 workgroup (MOE_DEBUG_NBLK_MASK)
+    reduce every output over the same K steps in the same order:
+    bit-identical layer outputs, both size classes (T > 16)."""
     cfg = A8_CASES[0]
     b = Built(cfg, packed=True, a8=True)
     lg = b.oracle_logits()
-    monkeypatch.setenv("MOE_STREAM_NBLK", "1")
-    ref = b.run(lg).clone()
-    monkeypatch.setenv("MOE_STREAM_NBLK", str(nblk))
-    out = b.run(lg).clone()
-    monkeypatch.delenv("MOE_STREAM_NBLK")
+    try:
+        b.d.debug_flags = 1
+        ref = b.run(lg).clone()
+        b.d.debug_flags = nblk
+        out = b.run(lg).clone()
+    finally:
+        b.d.debug_flags = 0
     assert torch.equal(ref, out), nblk

@@ -181,3 +181,47 @@ def test_received_counts_run_the_dispatched_buffer(name):
     torch.cuda.synchronize()
     assert int(rt2.status.item()) & B.MOE_STATUS_RECV_OVERFLOW
     assert int(rt2.masked_m[0].item()) == cfg.M_max
+
+
+@pytest.mark.parametrize("packed", [False, True], ids=["rowmajor", "packed"])
+def test_received_counts_above_routed_total(packed):
+    """A dispatch can deliver more rows to a rank than its own batch routed
+    (T*K): here the slots of a masked buffer receive up to M_max rows, about
+    six times T*K in all, with T*K = 64*E_phys so the large-group kernel
+    runs.  Every received row's expert output must match the reference
+    SwiGLU of that row (no row tile left out of the launch: 31 row tiles of
+    128 against the 12 a routed batch of this size can have)."""
+    cfg = _BASE.with_(name="recv_many", T=256, H=512, I=512, E=8, E_phys=8, K=2, act_dtype="bf16",
+                      M_max=640)
+    b = Built(cfg, packed=packed)
+    d, L, T = b.d, b.layer, b.T
+    counts = torch.tensor([640, 600, 513, 400, 390, 300, 257, 129], dtype=torch.int32, device=DEV)
+    assert int(counts.sum()) > T * cfg.K and T * cfg.K >= 64 * cfg.E_phys
+    rows_n = B.buffer_rows(d)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    xg = torch.randn((rows_n, d.H), generator=g).to(torch.bfloat16).to(DEV)
+    rt2 = B.RouteTables(d, DEV)
+    B.moe_route_received(d, counts, T, rt2)
+    h = torch.zeros_like(L.h)
+    y = torch.zeros_like(L.y)
+    B.moe_expert_gate_up(d, L.weights, rt2, T, xg, h)
+    B.moe_expert_down(d, L.weights, rt2, T, h, y)
+    torch.cuda.synchronize()
+    assert int(rt2.status.item()) == 0
+    splits = B.down_splits(d, T)
+    ysz = B.y_bytes(d, T)
+    if splits == 1:
+        yv = y[:ysz].view(torch.bfloat16).view(-1, d.H).float()
+    else:
+        yv = y[:ysz].view(torch.float32).view(splits, -1, d.H).sum(0)
+    xs = to_f64(xg.cpu())
+    worst = 0.0
+    for p in range(cfg.E_phys):
+        ew = b.inp.expert(b.inp.slot_logical(p))
+        W1, W3, W2 = to_f64(ew.w1), to_f64(ew.w3), to_f64(ew.w2)
+        rows = np.arange(p * cfg.M_max, p * cfg.M_max + int(counts[p]))
+        ref = O.swiglu_expert(xs[rows], W1, W3, W2)
+        got = yv[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
+        worst = max(worst, rel_err(got, ref))
+    say(f"  received {int(counts.sum())} rows (T*K = {T * cfg.K}): rel err {worst:.3e}")
+    assert worst <= TOL["bf16"]

@@ -176,21 +176,24 @@ def test_fused_decode_full_size(cfg, gp):
     assert e <= TOL[cfg.w_dtype]
 
 
-def test_fused_decode_timeout_path_and_recovery(monkeypatch):
-    """The bounded wait's failure path, forced from the host: with a spin
-    limit of zero polls every workgroup that has to wait at a barrier aborts
-    the launch, which ends normally with MOE_STATUS_SYNC_TIMEOUT in the
-    status word.  After the fused workspace is zero-filled again the next
-    call equals the multi-launch chain bit for bit."""
+def test_fused_decode_timeout_path_and_recovery():
+    """The bounded wait's failure path, forced from the host: with a wait
+    bound of zero polls (MOE_DEBUG_FUSED_NO_WAIT) every workgroup that has to
+    wait at a barrier aborts the launch, which ends normally with
+    MOE_STATUS_SYNC_TIMEOUT in the status word.  After the fused workspace is
+    zero-filled again the next call equals the multi-launch chain bit for
+    bit."""
     cfg, gp = CASES[0]
     b = Built(cfg, grouped=gp, packed=True)
     ref = _multi(b, b.T)
-    monkeypatch.setenv("MOE_FUSED_SPIN_LIMIT", "0")
-    _zero(b)
-    b.layer.forward_fused(b.x, b.T)
-    torch.cuda.synchronize()
+    b.d.debug_flags = B.MOE_DEBUG_FUSED_NO_WAIT
+    try:
+        _zero(b)
+        b.layer.forward_fused(b.x, b.T)
+        torch.cuda.synchronize()
+    finally:
+        b.d.debug_flags = 0
     status = int(b.layer.rt.status.cpu().numpy()[0])
     assert status & B.MOE_STATUS_SYNC_TIMEOUT, status
-    monkeypatch.delenv("MOE_FUSED_SPIN_LIMIT")
     b.layer.fws.zero_()
     _same(ref, _fused(b, b.T), "after recovery")

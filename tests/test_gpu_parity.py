@@ -15,7 +15,8 @@ import torch
 from oracle import moe_oracle as O
 from routing_grouped_expert_router_amd import binding as B
 from workloads import configs, generate
-from gpu_util import Built, TOL, rel_err, out_np, route_np, say, tile_off_expected, weight_tol, DEV
+from gpu_util import (Built, TOL, rel_err, out_np, route_np, say, tile_off_expected, weight_tol, DEV,
+                      covering_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -68,9 +69,13 @@ def small_configs():
 
 
 SMALL = small_configs()
-FULL = [configs.mixtral_decode(1), configs.mixtral_decode(8), configs.mixtral_decode(64),
-        configs.dsv3_decode(32), configs.dsv3_decode(256), configs.dsv3_prefill(),
-        configs.replica_decode()]
+# every workload at its full size
+FULL = [configs.mixtral_decode(1), configs.mixtral_decode(8), configs.mixtral_decode(32),
+        configs.mixtral_decode(64), configs.dsv3_decode(32), configs.dsv3_decode(128),
+        configs.dsv3_decode(256), configs.dsv3_prefill(), configs.replica_decode()]
+
+TILED_VARIANTS = (B.MOE_DEBUG_TILED_NARROW, B.MOE_DEBUG_TILED_WIDE_REGS, B.MOE_DEBUG_TILED_WIDE_LDS,
+                  B.MOE_DEBUG_TILED_WIDE_HYB)
 
 ROUTE_KEYS = ["ids", "phys", "row_of", "slot_of", "src_of", "counts", "offsets"]
 
@@ -335,46 +340,45 @@ def test_fused_gather_gives_identical_outputs():
 
 
 @pytest.mark.parametrize("nblk", [2, 4])
-def test_block_walk_gives_identical_outputs(nblk, monkeypatch):
+def test_block_walk_gives_identical_outputs(nblk):
     """A streaming workgroup that walks several 64-row output blocks as one
-    pipelined stream (MOE_STREAM_NBLK forces the count) reduces every output
-    over the same K steps in the same order: bit-identical outputs."""
+    pipelined stream (MOE_DEBUG_NBLK_MASK forces the count) reduces every
+    output over the same K steps in the same order: bit-identical outputs."""
     for cfg in (SMALL[1], SMALL[3], SMALL[9]):
         for packed in (False, True):
             b = Built(cfg, packed=packed)
             lg = b.oracle_logits()
             ref = b.run(lg).clone()
-            monkeypatch.setenv("MOE_STREAM_NBLK", str(nblk))
+            b.d.debug_flags = nblk
             try:
                 out = b.run(lg).clone()
             finally:
-                monkeypatch.delenv("MOE_STREAM_NBLK")
+                b.d.debug_flags = 0
             assert torch.equal(ref, out), (cfg.name, packed, nblk)
 
 
 @pytest.mark.parametrize("name", ["tiled_masked_spill", "tiled_contig_shared", "tiled_wide",
                                   "tiled_skewed_small_groups"])
-def test_wide_tiled_kernel_matches_narrow(name, monkeypatch):
-    """The wide tiled kernel (128 weight rows per wave) and the narrow one
-    (64) reduce every output over the same 32-wide K steps in the same order
-    with the same MFMA: bit-identical outputs (MOE_TILED_WIDE=0 forces the
-    narrow kernel), row-major and packed weights, gathered or permuted rows.
-    With packed weights the default wide kernel loads weights into registers
-    and stages activations by direct-to-LDS loads; MOE_TILED_HYB=0 forces
-    the one that stages both through LDS, MOE_TILED_DMA=0 the
-    register-staged one: all must agree."""
+def test_wide_tiled_kernel_matches_narrow(name):
+    """Every kernel for large groups reduces each output over the same
+    32-wide K steps in the same order with the same MFMA: bit-identical
+    outputs, row-major and packed weights, gathered or permuted rows.
+    MOE_DEBUG_TILED_* in the descriptor forces each one: the narrow tile
+    (64 weight rows per wave), the wide tile with operands staged through
+    registers, with both operands by direct-to-LDS loads, and with weights
+    to registers and activations through LDS."""
     cfg = next(c for c in SMALL if c.name == name)
     for packed in (False, True):
         b = Built(cfg, packed=packed)
         lg = b.oracle_logits()
         for fused in (True, False):
             ref = b.run(lg, fused_gather=fused).clone()
-            for var in ("MOE_TILED_WIDE", "MOE_TILED_DMA", "MOE_TILED_HYB"):
-                monkeypatch.setenv(var, "0")
+            for var in TILED_VARIANTS:
+                b.d.debug_flags = var << B.MOE_DEBUG_TILED_SHIFT
                 try:
                     out = b.run(lg, fused_gather=fused).clone()
                 finally:
-                    monkeypatch.delenv(var)
+                    b.d.debug_flags = 0
                 assert torch.equal(ref, out), (name, packed, fused, var)
 
 
@@ -516,18 +520,56 @@ def _sample(T, n, seed=0):
     return np.unique(np.concatenate([[0, T - 1], rng.choice(T, size=min(n, T), replace=False)]))
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("cfg", FULL, ids=lambda c: c.name)
-def test_full_size_sampled(cfg):
+def test_full_size(cfg):
+    """Each workload at full size in the launch configuration the benchmark
+    times (packed weights, fused gather).  Routing tables bit-exact on the
+    whole batch.  Outputs: every token of a decode batch (every touched slot
+    and every masked/spill boundary included); for the prefill batch, the
+    tokens on the first and last row of every group and on both sides of
+    every 128- and 256-row tile boundary of every group and of the shared
+    expert, so that each expert, each K loop and each partial last tile is
+    compared against the reference."""
     b = Built(cfg, packed=True)          # the layout the benchmark times
     say(f"  built {cfg.name}")
     lg = b.oracle_logits()
     out = out_np(b.run(lg))
-    toks = _sample(b.T, 6 if cfg.T > 64 else 4)
-    res = b.oracle(lg, tokens=toks)
+    g = route_np(b.layer.rt, b.T, cfg.K)
+    if b.T <= 256:
+        toks = np.arange(b.T)
+    else:
+        toks = covering_tokens(g["counts"], g["offsets"], g["src_of"], b.T, cfg.n_shared)
+    slots = sorted({int(p) for p in g["phys"][toks].ravel() if p >= 0})
+    res = b.oracle(lg, tokens=toks, slots=slots)
     check_route(b, res)
     e = rel_err(out[toks], res["out"])
-    say(f"  {cfg.name}: sampled tokens {list(toks)} rel err {e:.3e} status {res['status']}")
+    say(f"  {cfg.name}: {len(toks)} tokens over {len(slots)} slots, rel err {e:.3e} status {res['status']}")
     assert e <= TOL[cfg.w_dtype]
+
+
+@pytest.mark.parametrize("name", ["tiny_t16", "dsv3_small_fp8", "replica_small", "tiled_contig_shared"])
+def test_c_forward_chain(name):
+    """moe_forward, the C ABI's one-call chain (router logits, route,
+    permute or fused gather, grouped FFN, combine): its output matches the
+    reference on every token and equals the step-by-step calls bit for bit
+    (fp32 activations take the permute; bf16 ones the fused gather)."""
+    cfg = next(c for c in SMALL if c.name == name)
+    b = Built(cfg, packed=cfg.act_dtype == "bf16")
+    L = b.layer
+    out = torch.zeros_like(L.out)
+    B.moe_forward(b.d, b.x, b.wr, b.bias, L.weights, b.T, L.logits, L.rt, L.ws, L.xg, L.h, L.y, out,
+                  b.l2p, b.rcount)
+    torch.cuda.synchronize()
+    got = out_np(out[: b.T])
+    res = b.oracle(L.logits[: b.T].cpu().numpy())
+    check_route(b, res)
+    e = rel_err(got, res["out"])
+    say(f"  {name}: rel err {e:.3e}")
+    assert e <= TOL[cfg.w_dtype]
+    steps = L.forward(b.x, b.T).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(steps, out[: b.T])
 
 
 def test_graph_replays_match_eager():

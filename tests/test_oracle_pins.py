@@ -706,3 +706,86 @@ def test_w8a8_layer_against_w8a16_layer():
     e = np.abs(a["out"] - b["out"]).max() / np.abs(a["out"]).max()
     assert 5e-3 < e < 6e-2, e
     assert np.array_equal(a["row_of"], b["row_of"])
+
+
+def _torch_q1x128(a: torch.Tensor):
+    """Rows of fp32 values -> (E4M3FN codes as float64 values, fp32 scales
+    [R, C/128]), written from R20 with torch's own float8_e4m3fn cast: per
+    row and 128-wide block s = fp32(amax / 448) (1 for an all-zero block),
+    codes = cast(fp32(x / s)) clamped to +-448."""
+    R, C = a.shape
+    blk = a.reshape(R, C // 128, 128)
+    amax = blk.abs().amax(dim=2)
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    v = (blk / s[:, :, None]).clamp(-448.0, 448.0)
+    codes = v.to(torch.float8_e4m3fn).to(torch.float64).reshape(R, C)
+    return codes, s
+
+
+def _torch_block_product(ca, sa, cw, sw):
+    """R21 with torch matmuls, one per 128-wide K block: the block's sum of
+    code products, times the row's and the weight block's scales, added to
+    a float64 total."""
+    T, K = ca.shape
+    N = cw.shape[0]
+    out = torch.zeros((T, N), dtype=torch.float64)
+    for b in range(K // 128):
+        part = ca[:, 128 * b:128 * (b + 1)] @ cw[:, 128 * b:128 * (b + 1)].T
+        wscale = torch.repeat_interleave(sw[:, b].to(torch.float64), 128)      # [N]
+        out += part * sa[:, b].to(torch.float64)[:, None] * wscale[None, :]
+    return out
+
+
+def _torch_w8a8_expert(x, ew, round_h=True, h_blocks_by_row=True):
+    """R22 composed independently of the reference: x (bf16 values) coded per
+    token, gate and up by R21, h = SiLU(g) * u rounded to bf16 through fp32,
+    h coded per row, down by R21.  The switches plant the two mistakes the
+    pin must catch: no bf16 rounding of h, and h coded with one scale per
+    128-wide block shared by all rows (the weights' block rule) instead of
+    one per row."""
+    dec = lambda q: q.view(torch.float8_e4m3fn).to(torch.float64)
+    cx, sx = _torch_q1x128(x.to(torch.float32))
+    g = _torch_block_product(cx, sx, dec(ew.w1), ew.s1)
+    u = _torch_block_product(cx, sx, dec(ew.w3), ew.s3)
+    h = torch.nn.functional.silu(g) * u
+    if round_h:
+        h = h.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+    h32 = h.to(torch.float32)
+    if h_blocks_by_row:
+        ch, sh = _torch_q1x128(h32)
+    else:                                   # one scale per block for all rows
+        R, C = h32.shape
+        blk = h32.reshape(R, C // 128, 128)
+        amax = blk.abs().amax(dim=(0, 2))
+        s1 = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        ch = (blk / s1[None, :, None]).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).to(torch.float64)
+        ch = ch.reshape(R, C)
+        sh = s1[None, :].expand(R, -1)
+    return _torch_block_product(ch, sh, dec(ew.w2), ew.s2)
+
+
+def test_w8a8_expert_against_independent_torch_composition():
+    """swiglu_expert_w8a8 (R20-R22) against the same composition written
+    independently with torch: torch's float8_e4m3fn cast for both
+    quantizations, one torch matmul per 128-wide K block, and the bf16
+    rounding of h made explicit.  Agreement is to float64 rounding.  The
+    same composition with the bf16 rounding of h dropped, or with h coded in
+    blocks along the wrong axis, lies far outside that tolerance, so the pin
+    catches either mistake in the reference."""
+    cfg = configs.tiny().with_(T=6, H=384, I=256, E=1, E_phys=1, K=1, act_dtype="bf16", w_dtype="fp8")
+    inp = generate.make_inputs(cfg)
+    ew = inp.expert(0)
+    x = inp.x.to(torch.float64)
+    # rows of different magnitudes, one all-zero 128-block (scale 1)
+    x = x * torch.tensor([1.0, 3.0, 0.25, 10.0, 1.0, 0.5], dtype=torch.float64)[:, None]
+    x[4, 128:256] = 0.0
+    x = x.to(torch.bfloat16)
+    ref = O.swiglu_expert_w8a8(to_f64(x), (ew.w1.numpy(), ew.s1.numpy(), ew.w3.numpy(), ew.s3.numpy(),
+                                           ew.w2.numpy(), ew.s2.numpy()))
+    got = _torch_w8a8_expert(x, ew).numpy()
+    scale = np.abs(ref).max()
+    assert np.abs(got - ref).max() <= 1e-12 * scale
+    no_round = _torch_w8a8_expert(x, ew, round_h=False).numpy()
+    wrong_axis = _torch_w8a8_expert(x, ew, h_blocks_by_row=False).numpy()
+    assert np.abs(no_round - ref).max() > 1e-6 * scale
+    assert np.abs(wrong_axis - ref).max() > 1e-6 * scale
