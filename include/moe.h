@@ -110,7 +110,25 @@ typedef struct {
   int32_t BM;           /* segment padding, >= 1 (MOE_CONTIG) */
   int32_t w_packed;     /* 0: expert weights row-major [out, in];
                            1: packed by moe_pack_weights */
+  int32_t debug_flags;  /* 0 in normal use.  Test and ablation switches
+                           (MOE_DEBUG_*): each selects a kernel variant
+                           whose outputs are bit-identical to the default
+                           choice, or forces a failure path from the host */
 } moe_desc_t;
+
+/* moe_desc_t.debug_flags.  Bits 0-3: 64-row output blocks per streaming or
+ * W8A8 workgroup (1..8 and dividing N/64; 0 = the library's choice).
+ * Bits 4-7: the kernel for large groups (MOE_DEBUG_TILED_*; 0 = the
+ * library's choice).  Bit 8: moe_decode_fused bounds every grid-barrier wait
+ * at zero polls, so a call aborts with MOE_STATUS_SYNC_TIMEOUT. */
+#define MOE_DEBUG_NBLK_MASK        0xFu
+#define MOE_DEBUG_TILED_SHIFT      4
+#define MOE_DEBUG_TILED_MASK       0xF0u
+#define MOE_DEBUG_TILED_NARROW     1  /* 128 x 256 tile, operands via registers */
+#define MOE_DEBUG_TILED_WIDE_REGS  2  /* 128 x 512 tile, operands via registers */
+#define MOE_DEBUG_TILED_WIDE_LDS   3  /* 128 x 512 tile, both operands by direct-to-LDS loads */
+#define MOE_DEBUG_TILED_WIDE_HYB   4  /* 128 x 512 tile, weights to registers, activations via LDS */
+#define MOE_DEBUG_FUSED_NO_WAIT    0x100u
 
 /* Routing tables, all device int32/float/uint32 arrays, caller-allocated.
  * Sizes: TK = T_max*K.  Choice i = t*K + k (k-th choice of token t). */
@@ -156,10 +174,19 @@ const char* moe_status_string(moe_status_t s);
 /* Validates a description; MOE_OK or the error the calls would return. */
 moe_status_t moe_check_desc(const moe_desc_t* d);
 
-/* Bytes of scratch device memory moe_route needs (for T = T_max). */
+/* Bytes of scratch device memory moe_route needs (for T = T_max): per
+ * 64-token block, the counts of each expert and the rank of each choice
+ * inside its block (the counting pass before the offsets; MoonEP online-plan
+ * data flow: counts -> token offsets -> expert-grouped slots). */
 size_t moe_route_workspace_bytes(const moe_desc_t* d);
 
-/* Rows of the grouped buffers xg [rows, H], h [rows, I] and y: routed rows
+/* The same number under the name the boundary's description uses. */
+size_t moe_workspace_bytes(const moe_desc_t* d);
+
+/* Rows of the grouped buffers xg [rows, H], h [rows, I] and y ("推理 INFRA
+ * 方法论(5)", DeepGEMM section: a static [E_loc, M_max, K] buffer whose valid
+ * rows per expert masked_m gives at run time; vllbc blog, vLLM forward path:
+ * contiguous groups padded to a block size): routed rows
  * (masked: E_phys*M_max + K*max(0, T_max - M_max) spill rows; contiguous:
  * T_max*K + E_phys*(BM-1)), then n_shared*T_max shared-expert rows. */
 int64_t moe_buffer_rows(const moe_desc_t* d);
@@ -169,11 +196,19 @@ int64_t moe_shared_base(const moe_desc_t* d);
 
 /* Number of K-splits the down projection uses for T tokens.  With 1 split
  * y is bf16 [rows, H]; with S > 1 it is S fp32 partial sums [S, rows, H],
- * summed in split order by moe_combine. */
+ * summed in split order by moe_combine.  Fewer tokens touch fewer slots, so
+ * the split grows as T shrinks ("推理 INFRA 方法论(5)", C(B) section: the
+ * decode batch reads the weights of the slots it touches). */
 int32_t moe_down_splits(const moe_desc_t* d, int32_t T);
 
-/* Bytes of y for T tokens. */
+/* Bytes of y for T tokens.  This is not monotone in T: fewer tokens may use
+ * more fp32 split planes.  A y buffer that serves calls with different T must
+ * hold moe_y_bytes_max(d). */
 size_t moe_y_bytes(const moe_desc_t* d, int32_t T);
+
+/* The largest moe_y_bytes(d, T) over 1 <= T <= T_max (0 for an invalid
+ * descriptor): the size of a y buffer allocated once for every call. */
+size_t moe_y_bytes_max(const moe_desc_t* d);
 
 /* ---- the hot path -------------------------------------------------------- */
 
@@ -307,7 +342,11 @@ moe_status_t moe_eplb_plan(const double* load, int32_t E, int32_t n_redundant, i
 /* a5. Gathers token rows into the grouped buffer: xg[slot_of[t*K+k]] = x[t]
  * (cast to bf16 if x is fp32) and, with a shared expert,
  * xg[moe_shared_base + t] = x[t].  x: device [T, H] act_dtype;
- * xg: device [moe_buffer_rows, H] bf16. */
+ * xg: device [moe_buffer_rows, H] bf16.
+ * (vllbc blog, vLLM forward-path section: after top-K the token rows are
+ * sorted by expert and block-aligned before the first expert GEMM; MoonEP,
+ * online-plan section: each token row is written to its slot of the
+ * expert-grouped buffer at the offset the counts give.) */
 moe_status_t moe_permute(const moe_desc_t* d, const void* x, int32_t T,
                          const moe_route_t* r, void* xg, hipStream_t stream);
 
@@ -337,20 +376,34 @@ moe_status_t moe_expert_gate_up_x(const moe_desc_t* d, const moe_weights_t* w,
 
 /* a7 (+a8). Down projection y[row] = h[row] W2^T for the same rows.
  * y: device, moe_y_bytes(d, T) bytes: bf16 [moe_buffer_rows, H] when
- * moe_down_splits(d, T) == 1, else that many fp32 partial planes. */
+ * moe_down_splits(d, T) == 1, else that many fp32 partial planes (a buffer
+ * reused across calls with different T: moe_y_bytes_max(d) bytes). */
 moe_status_t moe_expert_down(const moe_desc_t* d, const moe_weights_t* w,
                              const moe_route_t* r, int32_t T, const void* h, void* y,
                              hipStream_t stream);
 
-/* a6-a8 in one call: moe_expert_gate_up then moe_expert_down. */
+/* a6-a8 in one call: moe_expert_gate_up then moe_expert_down (vllbc blog,
+ * vLLM forward-path section: GEMM1, activation, GEMM2 over the
+ * expert-grouped rows; "推理 INFRA 方法论(5)", DeepGEMM section: one grouped
+ * launch serves every expert, empty experts skipped). */
 moe_status_t moe_grouped_ffn(const moe_desc_t* d, const moe_weights_t* w,
                              const moe_route_t* r, int32_t T, const void* xg,
                              void* h, void* y, hipStream_t stream);
 
-/* a5-a8 in one call: moe_expert_gate_up_x then moe_expert_down. */
+/* a5-a8 in one call: moe_expert_gate_up_x then moe_expert_down (the same
+ * passages as moe_grouped_ffn, with the gather of moe_permute inside). */
 moe_status_t moe_grouped_ffn_x(const moe_desc_t* d, const moe_weights_t* w,
                                const moe_route_t* r, int32_t T, const void* x,
                                void* h, void* y, hipStream_t stream);
+
+/* Name of the kernel that moe_expert_gate_up_x / moe_expert_gate_up (which
+ * = 0) or moe_expert_down (which = 1) runs for the largest groups of a
+ * T-token call: "ffn_stream_kernel" (decode-sized groups, weights streamed
+ * once per group) or one of the large-group kernels ("ffn_whyb_kernel" ...).
+ * A static string; "none" for an invalid descriptor, T outside [1, T_max]
+ * or another `which`.  Host only, pure: profiles and benchmarks use it to
+ * name the kernel they time. */
+const char* moe_expert_kernel(const moe_desc_t* d, int32_t T, int32_t which);
 
 /* ---- W8A8: fp8 activations on fp8 MFMA ------------------------------------
  * ("推理 INFRA 方法论(5)", DeepGEMM section: FP8 operands with per-128 scales
@@ -399,9 +452,13 @@ moe_status_t moe_grouped_ffn_a8(const moe_desc_t* d, const moe_weights_t* w,
 moe_status_t moe_combine(const moe_desc_t* d, const moe_route_t* r, int32_t T,
                          const void* y, void* out, hipStream_t stream);
 
-/* All five steps in order on one stream (same arguments as above).  With
- * bf16 activations the permute is fused into the expert kernel
- * (moe_grouped_ffn_x) and xg is not used (may be NULL). */
+/* All five steps in order on one stream (same arguments as above): the
+ * MoE layer forward of vllbc blog's routing / expert-FFN section (router,
+ * top-K with renormalised softmax, SwiGLU experts, weighted sum) along the
+ * vLLM forward path of the same page (topk -> align/sort -> GEMM1 -> act ->
+ * GEMM2 -> moe_sum).  With bf16 activations the permute is fused into the
+ * expert kernel (moe_grouped_ffn_x) and xg is not used (may be NULL).  y
+ * must hold moe_y_bytes(d, T) bytes (moe_y_bytes_max(d) if T varies). */
 moe_status_t moe_forward(const moe_desc_t* d, const void* x, const void* w_router,
                          const float* bias, const int32_t* l2p, const int32_t* replica_count,
                          const moe_weights_t* w, int32_t T, float* logits,
@@ -432,8 +489,13 @@ size_t moe_decode_fused_workspace_bytes(const moe_desc_t* d);
  * (softmax) or E <= 256 (grouped router); else MOE_ERR_UNSUPPORTED, as for
  * T > 16.  The launch holds every compute unit of the device until it ends;
  * its workgroups wait for one another, with each wait bounded (about a
- * second; the environment variable MOE_FUSED_SPIN_LIMIT, in polls, lowers
- * the bound), so work on other streams can only delay it. */
+ * second; MOE_DEBUG_FUSED_NO_WAIT in desc->debug_flags sets the bound to zero
+ * polls), so work on other streams can only delay it.  Its grid barriers
+ * write each XCD's L2 back once per barrier, from the XCD's last arrival,
+ * relying on that writeback covering the stores of every workgroup on that
+ * XCD (a property of gfx950's cache operations rather than of the HIP memory
+ * model); the multi-launch chain relies on no such property and stays the
+ * default path. */
 moe_status_t moe_decode_fused(const moe_desc_t* d, const void* x, const void* w_router,
                               const float* bias, const moe_grouped_router_t* g,
                               const int32_t* l2p, const int32_t* replica_count,

@@ -919,31 +919,48 @@ bool wide_supported(int mode, const TiledArgs& a) {
          a.x_bytes < (int64_t(1) << 31);
 }
 
+// Which kernel takes a launch.  a.variant (moe_desc_t.debug_flags) can force
+// one; where the forced one does not apply to the shape the choice falls to
+// the next one down.  Packed weights: by default the hybrid tile (weights to
+// registers, activations by direct-to-LDS loads) where the K range is whole
+// blocks of four 32-wide steps, else the all-LDS one; row-major weights: the
+// register-staged wide tile; shapes the wide tile does not divide: the
+// narrow one.
+int tiled_choice(const TiledArgs& a, int packed, int mode) {
+  const bool wide = wide_supported(mode, a) && a.variant != MOE_DEBUG_TILED_NARROW;
+  if (!wide) return MOE_DEBUG_TILED_NARROW;
+  if (!packed || a.variant == MOE_DEBUG_TILED_WIDE_REGS) return MOE_DEBUG_TILED_WIDE_REGS;
+  if (a.variant != MOE_DEBUG_TILED_WIDE_LDS && (a.s.Kdim / a.s.ksplit) % 128 == 0) return MOE_DEBUG_TILED_WIDE_HYB;
+  return MOE_DEBUG_TILED_WIDE_LDS;
+}
+
+const char* tiled_kernel_name(int choice) {
+  switch (choice) {
+    case MOE_DEBUG_TILED_NARROW: return "ffn_tiled_kernel";
+    case MOE_DEBUG_TILED_WIDE_REGS: return "ffn_wide_kernel";
+    case MOE_DEBUG_TILED_WIDE_LDS: return "ffn_wdma_kernel";
+    case MOE_DEBUG_TILED_WIDE_HYB: return "ffn_whyb_kernel";
+  }
+  return "none";
+}
+
 hipError_t launch_ffn_tiled(const TiledArgs& a, int fp8, int packed, int mode, int max_tiles, hipStream_t s) {
   if (!tiled_supported(mode, fp8, a.s.N, a.s.Kdim, a.s.ksplit)) return hipErrorInvalidValue;
   if (max_tiles <= 0) return hipSuccess;
-  // MOE_TILED_WIDE=0 selects the narrow kernel where the wide one applies
-  const char* env = getenv("MOE_TILED_WIDE");
-  const bool wide = wide_supported(mode, a) && !(env && env[0] == '0');
+  const int choice = tiled_choice(a, packed, mode);
+  const bool wide = choice != MOE_DEBUG_TILED_NARROW;
   // grid.y covers the static bound on row tiles (the live count is read on the
   // device) plus 8, so that the XCD remap's largest linear id, which can pass
   // the live work count by up to 7, always has a workgroup
   const int wn = wide ? (mode == MODE_GATEUP ? kWN / 2 : kWN) : (mode == MODE_GATEUP ? 128 : kTN);
   const dim3 grid(a.s.N / wn, max_tiles + 8, a.s.ksplit);
-  // packed weights: by default the hybrid tile (weights to registers,
-  // activations by direct-to-LDS loads) where the K range is whole blocks of
-  // four 32-wide steps, else the all-LDS one; MOE_TILED_HYB=0 selects the
-  // all-LDS tile, MOE_TILED_DMA=0 the register-staged wide kernel
-  const char* denv = getenv("MOE_TILED_DMA");
-  const char* henv = getenv("MOE_TILED_HYB");
-  const bool dma_off = denv && denv[0] == '0';
-  if (wide && packed && !dma_off && !(henv && henv[0] == '0') && (a.s.Kdim / a.s.ksplit) % 128 == 0) {
+  if (choice == MOE_DEBUG_TILED_WIDE_HYB) {
     if (mode == MODE_GATEUP) hipLaunchKernelGGL((ffn_whyb_kernel<MODE_GATEUP, false>), grid, dim3(kTThreads), 0, s, a);
     else if (a.s.out_f32) hipLaunchKernelGGL((ffn_whyb_kernel<MODE_DOWN, true>), grid, dim3(kTThreads), 0, s, a);
     else hipLaunchKernelGGL((ffn_whyb_kernel<MODE_DOWN, false>), grid, dim3(kTThreads), 0, s, a);
     return hipGetLastError();
   }
-  if (wide && packed && !dma_off) {
+  if (choice == MOE_DEBUG_TILED_WIDE_LDS) {
     if (mode == MODE_GATEUP) hipLaunchKernelGGL((ffn_wdma_kernel<MODE_GATEUP, false>), grid, dim3(kTThreads), 0, s, a);
     else if (a.s.out_f32) hipLaunchKernelGGL((ffn_wdma_kernel<MODE_DOWN, true>), grid, dim3(kTThreads), 0, s, a);
     else hipLaunchKernelGGL((ffn_wdma_kernel<MODE_DOWN, false>), grid, dim3(kTThreads), 0, s, a);

@@ -108,11 +108,17 @@ constexpr int kTileRows = 128;     // token rows per tile of the tiled kernel
 
 struct TiledArgs {
   StreamArgs s;
-  const int32_t* tile_off;   // [E_phys + 2] prefix of ceil(rows / 128) per group
+  const int32_t* tile_off;   // [E_phys + 2] prefix of ceil(rows / kTileRows) per group
   int min_rows;              // groups with at most this many rows are skipped
   int64_t x_bytes;           // bytes of the activation rows X addresses (rows * ldx * 2)
+  int variant;               // 0: the launcher's choice; else a MOE_DEBUG_TILED_* kernel
 };
+// largest MOE_DEBUG_TILED_* value
+constexpr int kTiledVariants = 4;
 bool tiled_supported(int mode, int fp8, int N, int Kdim, int ksplit);
+// the MOE_DEBUG_TILED_* kernel a launch with these arguments runs, and its name
+int tiled_choice(const TiledArgs& a, int packed, int mode);
+const char* tiled_kernel_name(int choice);
 hipError_t launch_ffn_tiled(const TiledArgs& a, int fp8, int packed, int mode, int max_tiles,
                             hipStream_t s);
 
@@ -171,6 +177,7 @@ struct FusedArgs {
   CombineArgs comb;
   uint32_t* sync;                       // barrier words (kFusedSyncBytes), zero-filled once
   int32_t* act;                         // [1 + E_phys] slots with tokens
+  int no_wait;                          // MOE_DEBUG_FUSED_NO_WAIT: waits bounded at zero polls
   int grid, spin_limit;                 // set by the launcher
 };
 // -1: E (or the grouped router's E) too large for the single-workgroup route
