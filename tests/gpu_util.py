@@ -74,12 +74,12 @@ class Built:
         torch.cuda.synchronize()
         return out
 
-    def oracle(self, logits_np=None, tokens=None):
+    def oracle(self, logits_np=None, tokens=None, slots=None):
         if self.a8:
             from oracle_adapt import oracle_forward_w8a8
             assert self.grouped is None
             return oracle_forward_w8a8(self.inp, logits=logits_np, tokens=tokens)
-        return oracle_forward(self.inp, logits=logits_np, tokens=tokens, grouped=self.grouped)
+        return oracle_forward(self.inp, logits=logits_np, tokens=tokens, grouped=self.grouped, slots=slots)
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
@@ -119,3 +119,30 @@ def weight_tol(K: int) -> float:
     fp32 exponentials carries <= 2 ulp, the sum K-1 roundings, the quotient
     one: (K + 4) * 2^-23 relative, on weights <= 1."""
     return (K + 4) * 2.0 ** -23
+
+
+def covering_tokens(counts, offsets, src_of, T: int, n_shared: int, tiles=(128, 256)):
+    """Token ids whose outputs cover every group of a routed batch at the
+    places a tiled kernel can get wrong: the first and the last row of every
+    slot with tokens, and the rows on both sides of every boundary between
+    row tiles of the given heights (the last, partial tile of each group
+    included); the shared expert's group is the tokens in order, so its
+    boundaries are token ids."""
+    counts = np.asarray(counts)
+    offsets = np.asarray(offsets)
+    src_of = np.asarray(src_of)
+    toks = {0, T - 1}
+
+    def ranks(R):
+        r = {0, R - 1}
+        for h in tiles:
+            for j in range(1, (R - 1) // h + 1):
+                r |= {h * j - 1, h * j}
+        return r
+
+    for p in np.nonzero(counts)[0]:
+        for r in ranks(int(counts[p])):
+            toks.add(int(src_of[offsets[p] + r]))
+    if n_shared:
+        toks |= ranks(T)
+    return np.array(sorted(toks), dtype=np.int64)
