@@ -65,6 +65,9 @@ def parse():
                     help="first run a plain 512 MiB device copy three times (a kernel of known "
                          "traffic for scaling hardware byte counters)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak probes")
+    ap.add_argument("--debug-flags", type=int, default=0,
+                    help="moe_desc_t.debug_flags for an ablation (MOE_DEBUG_* in include/moe.h: e.g. "
+                         "a forced large-group kernel); outputs stay bit-identical")
     return ap.parse_args()
 
 
@@ -80,7 +83,7 @@ GROUPED_ROUTER = dict(n_group=8, topk_group=4, group_k=2, renormalize=True, scal
 
 
 class Setup:
-    def __init__(self, cfg, packed=True, router="softmax", ep_ranks=1, a8=False):
+    def __init__(self, cfg, packed=True, router="softmax", ep_ranks=1, a8=False, debug_flags=0):
         import numpy as np
         import torch
         from routing_grouped_expert_router_amd import binding as B
@@ -114,6 +117,7 @@ class Setup:
             l2p_t, rc_t = B.moe_replica_map_from_p2l(self.inp.p2l, cfg.E, max_rep)
             l2p, rc = l2p_t.cuda(), rc_t.cuda()
         self.d = B.Desc.from_config(cfg, max_replicas=max_rep, w_packed=int(packed))
+        self.d.debug_flags = debug_flags
         if packed:   # one-time repack into the streamed layout; free the row-major copy
             w = B.pack_expert_weights(self.d, self.w)
             del self.w
@@ -211,12 +215,12 @@ class Setup:
         return slots, routed, gu, total
 
 
-def time_workload(cfg, steps, warmup, packed=True, router="softmax", ep_ranks=1, a8=False):
+def time_workload(cfg, steps, warmup, packed=True, router="softmax", ep_ranks=1, a8=False, debug_flags=0):
     """Eager steps (HIP events around the gate/up and down kernels on the
     launch stream), then the same step captured once in a HIP graph and
     replayed ``steps`` times (the layer latency reported)."""
     import torch
-    s = Setup(cfg, packed, router, ep_ranks, a8)
+    s = Setup(cfg, packed, router, ep_ranks, a8, debug_flags)
     cfg = s.cfg
     for _ in range(warmup):
         s.step()
@@ -534,7 +538,8 @@ def main():
     for n in names:
         c = configs.by_name(n)
         r = time_workload(c, args.steps, args.warmup, packed=not args.row_major,
-                          router=args.router, ep_ranks=args.ep_ranks, a8=args.a8)
+                          router=args.router, ep_ranks=args.ep_ranks, a8=args.a8,
+                          debug_flags=args.debug_flags)
         results[n] = r
         r["entry"] = batch_entry(r, peaks)
         print(f"# {n}: {r['ms']*1e3:.1f} us/layer (graph), {r['eager_ms']*1e3:.1f} eager, "
@@ -578,6 +583,7 @@ def main():
                    "E_phys": cfg.E_phys, "K": cfg.K, "n_shared": cfg.n_shared,
                    "layout": cfg.layout, "M_max": cfg.M_max, "w_dtype": cfg.w_dtype,
                    "weights": "row-major" if args.row_major else "packed",
+                   "debug_flags": args.debug_flags,
                    "router": args.router if args.router == "softmax" else
                    "grouped sigmoid (8 groups, 4 kept, top-2 group score, x2.5)",
                    "ep": None if args.ep_ranks == 1 else

@@ -128,6 +128,7 @@ typedef struct {
 #define MOE_DEBUG_TILED_WIDE_REGS  2  /* 128 x 512 tile, operands via registers */
 #define MOE_DEBUG_TILED_WIDE_LDS   3  /* 128 x 512 tile, both operands by direct-to-LDS loads */
 #define MOE_DEBUG_TILED_WIDE_HYB   4  /* 128 x 512 tile, weights to registers, activations via LDS */
+#define MOE_DEBUG_TILED_TALL       5  /* 256 x 256 tile, every wave all 256 token rows */
 #define MOE_DEBUG_FUSED_NO_WAIT    0x100u
 
 /* Routing tables, all device int32/float/uint32 arrays, caller-allocated.
@@ -145,9 +146,10 @@ typedef struct {
   int32_t* masked_m;   /* [E_phys] min(T_p, M_max)   (MOE_MASKED; else NULL ok) */
   int32_t* spill_off;  /* [E_phys+1] prefix sum of T_p - masked_m (MOE_MASKED) */
   int32_t* pad_off;    /* [E_phys+1] prefix sum of ceil(T_p/BM)*BM (MOE_CONTIG) */
-  int32_t* tile_off;   /* [E_phys+2] work list of the tiled expert kernel:
-                          prefix sum of ceil(T_p/128) over slots, then the
-                          shared expert's ceil(T/128) tiles (n_shared = 1) */
+  int32_t* tile_off;   /* [E_phys+2] work list of the large-group expert
+                          kernels: prefix sum of ceil(T_p/256) over slots,
+                          then the shared expert's ceil(T/256) tiles
+                          (n_shared = 1) */
   uint32_t* status;    /* [1] MOE_STATUS_* bits of the last moe_route */
 } moe_route_t;
 
@@ -300,8 +302,8 @@ moe_status_t moe_route_ep(const moe_desc_t* d, const float* logits, int32_t T,
  * slot p at p*M_max + i, i < counts[p] (counts: [E_phys] device int32, the
  * received count per local expert).  Writes r->counts and r->masked_m
  * (min(max(counts, 0), M_max)), r->offsets (their exclusive prefix), r->
- * spill_off (zeros), r->tile_off (prefix of ceil(rows/128) tiles; the shared
- * expert's ceil(T/128) last when d->n_shared) and r->status
+ * spill_off (zeros), r->tile_off (prefix of ceil(rows/256) tiles; the shared
+ * expert's ceil(T/256) last when d->n_shared) and r->status
  * (MOE_STATUS_RECV_OVERFLOW if a count is outside [0, M_max]); the other
  * tables are left as they are.  moe_expert_gate_up / moe_expert_down then run
  * on the buffer as after moe_route + moe_permute (shared-expert rows, if any,

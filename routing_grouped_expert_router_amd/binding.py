@@ -24,6 +24,7 @@ MOE_STATUS_BAD_EP_MAP, MOE_STATUS_RECV_OVERFLOW, MOE_STATUS_SYNC_TIMEOUT = 16, 3
 MOE_EP_LINEAR, MOE_EP_ROUND_ROBIN = 0, 1
 MOE_DEBUG_NBLK_MASK, MOE_DEBUG_TILED_SHIFT, MOE_DEBUG_FUSED_NO_WAIT = 0xF, 4, 0x100
 MOE_DEBUG_TILED_NARROW, MOE_DEBUG_TILED_WIDE_REGS, MOE_DEBUG_TILED_WIDE_LDS, MOE_DEBUG_TILED_WIDE_HYB = 1, 2, 3, 4
+MOE_DEBUG_TILED_TALL = 5
 
 EXPORTED = [
     "moe_status_string", "moe_check_desc", "moe_route_workspace_bytes", "moe_buffer_rows",

@@ -104,7 +104,7 @@ hipError_t launch_ffn_stream(const StreamArgs& a, int fp8, int packed, int mode,
 
 // ---- LDS-tiled grouped GEMM (large groups) ------------------------------------
 
-constexpr int kTileRows = 128;     // token rows per tile of the tiled kernel
+constexpr int kTileRows = 256;     // token rows per work item of the large-group kernels
 
 struct TiledArgs {
   StreamArgs s;
@@ -112,9 +112,11 @@ struct TiledArgs {
   int min_rows;              // groups with at most this many rows are skipped
   int64_t x_bytes;           // bytes of the activation rows X addresses (rows * ldx * 2)
   int variant;               // 0: the launcher's choice; else a MOE_DEBUG_TILED_* kernel
+  int cluster_size;          // persistent tall kernel: workgroups per cluster (= weight-row tiles)
+  int clusters_per_xcd;      //   and clusters on each XCD (set by the launcher)
 };
 // largest MOE_DEBUG_TILED_* value
-constexpr int kTiledVariants = 4;
+constexpr int kTiledVariants = 5;
 bool tiled_supported(int mode, int fp8, int N, int Kdim, int ksplit);
 // the MOE_DEBUG_TILED_* kernel a launch with these arguments runs, and its name
 int tiled_choice(const TiledArgs& a, int packed, int mode);

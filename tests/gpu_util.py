@@ -101,13 +101,13 @@ def route_np(rt: B.RouteTables, T: int, K: int) -> dict:
                 tile_off=rt.tile_off.cpu().numpy(), status=int(rt.status.cpu().numpy()[0]))
 
 
-TILE_ROWS = 128   # token rows per tile of the tiled expert kernel (moe_route_t.tile_off)
+TILE_ROWS = 256   # token rows per work item of the large-group kernels (moe_route_t.tile_off)
 
 
 def tile_off_expected(counts, T: int, n_shared: int):
-    """tile_off as moe.h defines it: exclusive prefix sum of ceil(count/128)
+    """tile_off as moe.h defines it: exclusive prefix sum of ceil(count/256)
     over the slots, the total, then the total plus the shared expert's
-    ceil(T/128) tiles."""
+    ceil(T/256) tiles."""
     t = -(-np.asarray(counts, dtype=np.int64) // TILE_ROWS)
     pre = np.concatenate([[0], np.cumsum(t)])
     shared = -(-T // TILE_ROWS) if n_shared else 0

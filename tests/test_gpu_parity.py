@@ -75,7 +75,7 @@ FULL = [configs.mixtral_decode(1), configs.mixtral_decode(8), configs.mixtral_de
         configs.dsv3_decode(256), configs.dsv3_prefill(), configs.replica_decode()]
 
 TILED_VARIANTS = (B.MOE_DEBUG_TILED_NARROW, B.MOE_DEBUG_TILED_WIDE_REGS, B.MOE_DEBUG_TILED_WIDE_LDS,
-                  B.MOE_DEBUG_TILED_WIDE_HYB)
+                  B.MOE_DEBUG_TILED_WIDE_HYB, B.MOE_DEBUG_TILED_TALL)
 
 ROUTE_KEYS = ["ids", "phys", "row_of", "slot_of", "src_of", "counts", "offsets"]
 
@@ -365,8 +365,9 @@ def test_wide_tiled_kernel_matches_narrow(name):
     outputs, row-major and packed weights, gathered or permuted rows.
     MOE_DEBUG_TILED_* in the descriptor forces each one: the narrow tile
     (64 weight rows per wave), the wide tile with operands staged through
-    registers, with both operands by direct-to-LDS loads, and with weights
-    to registers and activations through LDS."""
+    registers, with both operands by direct-to-LDS loads, with weights to
+    registers and activations through LDS, and the tall 256-row tile (where
+    a kernel does not apply to a shape the launch takes the next one)."""
     cfg = next(c for c in SMALL if c.name == name)
     for packed in (False, True):
         b = Built(cfg, packed=packed)
