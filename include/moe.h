@@ -236,6 +236,23 @@ moe_status_t moe_route(const moe_desc_t* d, const float* logits, int32_t T,
                        const moe_route_t* r, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* moe_route for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument.  The route workspace is a static device array of
+ * MOE_NOALLOC_WORKSPACE_BYTES in the library, one copy per GPU, held until
+ * the process ends; the call allocates and frees nothing.  Same tables,
+ * conventions and errors as moe_route, plus MOE_ERR_WORKSPACE when
+ * moe_route_workspace_bytes(d) exceeds that size and MOE_ERR_HIP when the
+ * array's device address cannot be looked up.  The address is looked up on
+ * a device's first call, with that device current: make that first call
+ * outside graph capture.  Every call on one GPU shares that GPU's array, so
+ * calls that may overlap on one GPU (different streams, graphs replayed
+ * concurrently) race and must be serialised by the caller. */
+#define MOE_NOALLOC_WORKSPACE_BYTES ((size_t)4 << 20)
+moe_status_t moe_route_noalloc(const moe_desc_t* d, const float* logits, int32_t T,
+                               const int32_t* l2p, const int32_t* replica_count,
+                               const moe_route_t* r, hipStream_t stream);
+
 /* Grouped sigmoid router (DeepSeek style; vllbc blog, routing section and
  * Table 3-1: sigmoid scores, a correction bias used only to choose experts,
  * weights from the unbiased scores, best groups first, then experts inside

@@ -36,8 +36,9 @@ EXPORTED = [
     "moe_replica_map_from_p2l", "moe_route_ep", "moe_route_received", "moe_ep_local_map",
     "moe_eplb_plan", "moe_quantize_1x128", "moe_expert_gate_up_a8", "moe_expert_down_a8",
     "moe_grouped_ffn_a8", "moe_decode_fused_workspace_bytes", "moe_decode_fused",
-    "moe_expert_kernel", "moe_probe_read", "moe_probe_mfma_bf16",
+    "moe_expert_kernel", "moe_probe_read", "moe_probe_mfma_bf16", "moe_route_noalloc",
 ]
+MOE_NOALLOC_WORKSPACE_BYTES = 4 << 20
 MOE_PROBE_SINK_WORDS = 8192
 
 
@@ -99,6 +100,7 @@ def lib() -> ctypes.CDLL:
             "moe_router_logits": (ctypes.c_int, [D, _P, _P, _P, i32, _P, _P]),
             "moe_route": (ctypes.c_int, [D, _P, i32, _P, _P, R, _P, sz, _P]),
             "moe_route_grouped": (ctypes.c_int, [D, _P, i32, GR, _P, _P, R, _P, sz, _P]),
+            "moe_route_noalloc": (ctypes.c_int, [D, _P, i32, _P, _P, R, _P]),
             "moe_permute": (ctypes.c_int, [D, _P, i32, R, _P, _P]),
             "moe_expert_gate_up": (ctypes.c_int, [D, W, R, i32, _P, _P, _P]),
             "moe_expert_gate_up_x": (ctypes.c_int, [D, W, R, i32, _P, _P, _P]),
@@ -287,6 +289,13 @@ def moe_route(d: Desc, logits, T, rt: RouteTables, ws, l2p=None, replica_count=N
     _check(lib().moe_route(ctypes.byref(d.c()), _ptr(logits), T, _ptr(l2p), _ptr(replica_count),
                            ctypes.byref(rt.c), _ptr(ws), ws.numel() * ws.element_size(),
                            _stream(stream)), "moe_route")
+
+
+def moe_route_noalloc(d: Desc, logits, T, rt: RouteTables, l2p=None, replica_count=None, stream=None):
+    """moe_route with the library's static per-GPU workspace (no workspace
+    argument, nothing allocated)."""
+    _check(lib().moe_route_noalloc(ctypes.byref(d.c()), _ptr(logits), T, _ptr(l2p), _ptr(replica_count),
+                                   ctypes.byref(rt.c), _stream(stream)), "moe_route_noalloc")
 
 
 class GroupedRouter:

@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <vector>
 #include <cstdlib>
 
@@ -13,6 +14,13 @@
 #include "kernels.hpp"
 
 using namespace moe;
+
+// Route workspace of moe_route_noalloc: one copy per GPU the library runs on,
+// held until the process ends.  Host code never uses this name as an address
+// (here it stands for the symbol only); each device's address comes from
+// hipGetSymbolAddress, looked up once per device (scratch_on_device).
+constexpr size_t kNoallocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -223,6 +231,25 @@ moe_status_t route_args(const moe_desc_t* d, const float* logits, int32_t T, con
   return MOE_OK;
 }
 
+// The current device's copy of `scratch`: its address is looked up on the
+// device's first call, with that device current, and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+moe_status_t scratch_on_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return MOE_OK;
+}
+
 moe_status_t route_impl(const moe_desc_t* d, const float* logits, int32_t T, const moe_grouped_router_t* g,
                         const moe_ep_map_t* ep, const int32_t* l2p, const int32_t* replica_count,
                         const moe_route_t* r, void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -240,6 +267,19 @@ moe_status_t moe_route(const moe_desc_t* d, const float* logits, int32_t T, cons
                        const int32_t* replica_count, const moe_route_t* r, void* ws,
                        size_t ws_bytes, hipStream_t stream) {
   return route_impl(d, logits, T, nullptr, nullptr, l2p, replica_count, r, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_route_noalloc(const moe_desc_t* d, const float* logits, int32_t T, const int32_t* l2p,
+                               const int32_t* replica_count, const moe_route_t* r, hipStream_t stream) {
+  const moe_status_t st = moe_check_desc(d);
+  if (st != MOE_OK) return st;
+  // every word of the workspace is written before it is read, so the array
+  // needs no clearing between calls
+  if (ws_layout(d).total > kNoallocScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const moe_status_t sst = scratch_on_device(&ws);
+  if (sst != MOE_OK) return sst;
+  return route_impl(d, logits, T, nullptr, nullptr, l2p, replica_count, r, ws, kNoallocScratchBytes, stream);
 }
 
 moe_status_t moe_route_grouped(const moe_desc_t* d, const float* logits, int32_t T,

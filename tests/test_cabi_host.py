@@ -248,3 +248,18 @@ def test_probes_reject_bad_arguments():
     assert L.moe_probe_mfma_bf16(0, 8, fake, None) == B.MOE_ERR_ARG
     assert L.moe_probe_mfma_bf16(10, B.MOE_PROBE_SINK_WORDS + 1, fake, None) == B.MOE_ERR_ARG
     assert L.moe_probe_mfma_bf16(10, 8, None, None) == B.MOE_ERR_ARG
+
+
+def test_route_noalloc_rejects_a_workspace_beyond_its_array():
+    """moe_route_noalloc's static workspace holds MOE_NOALLOC_WORKSPACE_BYTES;
+    a descriptor needing more is refused on the host, before any device
+    call."""
+    L = B.lib()
+    fake = ctypes.c_void_p(16)
+    rt2 = B.moe_route_t(*([fake] * len(B.moe_route_t._fields_)))
+    big = _d(T_max=200000, E=256, E_phys=256, K=8, M_max=64)
+    assert B.route_workspace_bytes(big) > B.MOE_NOALLOC_WORKSPACE_BYTES
+    assert L.moe_route_noalloc(ctypes.byref(big.c()), fake, 4, None, None, ctypes.byref(rt2),
+                               None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_route_noalloc(ctypes.byref(_d(K=0).c()), fake, 4, None, None, ctypes.byref(rt2),
+                               None) == B.MOE_ERR_ARG
