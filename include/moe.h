@@ -151,7 +151,15 @@ typedef struct {
                           then the shared expert's ceil(T/256) tiles
                           (n_shared = 1) */
   uint32_t* status;    /* [1] MOE_STATUS_* bits of the last moe_route */
+  uint32_t* claim;     /* [MOE_CLAIM_WORDS] work-claim counters of the
+                          large-group expert kernels (NULL: those kernels
+                          run one workgroup per work item instead).
+                          moe_route* zero them; every expert call leaves
+                          them zero when it ends, so expert calls that
+                          share route tables must not overlap */
 } moe_route_t;
+
+#define MOE_CLAIM_WORDS 256
 
 /* Expert weights, device memory.  Row-major layout [out, in] (row = output
  * feature), or the packed layout of moe_pack_weights when desc->w_packed:

@@ -40,6 +40,7 @@ EXPORTED = [
 ]
 MOE_NOALLOC_WORKSPACE_BYTES = 4 << 20
 MOE_PROBE_SINK_WORDS = 8192
+MOE_CLAIM_WORDS = 256
 
 
 class moe_desc_t(ctypes.Structure):
@@ -54,7 +55,7 @@ _P = ctypes.c_void_p
 class moe_route_t(ctypes.Structure):
     _fields_ = [(n, _P) for n in (
         "topk_ids", "topk_w", "topk_phys", "row_of", "slot_of", "src_of", "counts",
-        "offsets", "masked_m", "spill_off", "pad_off", "tile_off", "status")]
+        "offsets", "masked_m", "spill_off", "pad_off", "tile_off", "status", "claim")]
 
 
 class moe_ep_map_t(ctypes.Structure):
@@ -262,6 +263,7 @@ class RouteTables:
         self.pad_off = torch.zeros(d.E_phys + 1, **i32)
         self.tile_off = torch.zeros(d.E_phys + 2, **i32)
         self.status = torch.zeros(1, **i32)
+        self.claim = torch.zeros(MOE_CLAIM_WORDS, **i32)
         self.c = moe_route_t(*[_ptr(getattr(self, f)) for f, _ in moe_route_t._fields_])
 
 

@@ -976,23 +976,30 @@ constexpr int kQStages = 4;           // LDS ring of 64-wide K stages
 constexpr int kQStage = kQM * 64 * 2; // 32 KiB a stage
 constexpr int kQN = 256;              // weight rows per tile
 constexpr int kQAhead = 2;            // row tiles whose fragments are read ahead of their MFMAs
-// cache policy of the weight loads (buffer instruction aux bits; 2 = nt on
-// gfx950): weights are read by one tile only, activations by every tile of
-// their rows, so the weight stream should not evict the activations
+// cache policy of the weight loads (buffer instruction aux bits; 0 = the
+// default, cached; 2 = nt on gfx950).  A group's row tiles read the same
+// weights close together in time, and the later reads find them in L2 or in
+// the memory-side cache only if the first read allocated them there.
 #ifndef MOE_TALL_WEIGHT_POLICY
-#define MOE_TALL_WEIGHT_POLICY 2
+#define MOE_TALL_WEIGHT_POLICY 0
 #endif
 constexpr int kWeightPolicy = MOE_TALL_WEIGHT_POLICY;
 static_assert(kQM == 256, "the tall tile is one work item");
+
+struct NoHook {
+  __device__ void operator()() const {}
+};
 
 // One work item: rows m0 = 256 mt .. of group g against weight-row tile nt.
 // The activation ring is four LDS arrays, one per stage slot, rather than one
 // array with offsets: the compiler then tells a direct-to-LDS load into one
 // slot from a read of another and does not make the read wait for every
-// load in flight.
-template <int MODE, bool OUTF32>
+// load in flight.  at_loop_end() runs once the K loop is done, before the
+// epilogue (the persistent schedule claims its next unit there, so the
+// claim's latency overlaps the epilogue's arithmetic).
+template <int MODE, bool OUTF32, typename Hook = NoHook>
 __device__ __forceinline__ void tall_tile(const TiledArgs& ta, const TileWork& tw, char* x0s, char* x1s,
-                                          char* x2s, char* x3s) {
+                                          char* x2s, char* x3s, Hook at_loop_end = Hook{}) {
   const StreamArgs& a = ta.s;
   const int g = tw.g, nt = tw.nt, c0 = tw.c0, R = tw.R;
   const int64_t s0 = tw.s0, s1 = tw.s1;
@@ -1079,7 +1086,7 @@ __device__ __forceinline__ void tall_tile(const TiledArgs& ta, const TileWork& t
       }
     };
     // weights of stage st (clamped) into a bank: fragment 2 n + j = panel n,
-    // step j; read once per tile, so streamed past the caches (kWeightPolicy)
+    // step j (cache policy kWeightPolicy)
     auto load_w = [&](bf16x8* wb, int st) -> void {
       const int stc = st < nst ? st : nst - 1;
 #pragma unroll
@@ -1174,6 +1181,7 @@ __device__ __forceinline__ void tall_tile(const TiledArgs& ta, const TileWork& t
     __builtin_amdgcn_s_waitcnt(0);
     __builtin_amdgcn_s_barrier();
     acc_fence();
+    at_loop_end();
 
     // ---- epilogue: acc[m][n] holds D[w-row 4*(lane/16)+j of panel n][token lane%16 of tile m]
     const int lr = lane & 15, lg = lane >> 4;
@@ -1254,21 +1262,27 @@ __device__ __forceinline__ void tall_tile(const TiledArgs& ta, const TileWork& t
   }
 }
 
-// Persistent schedule of the tall kernel (ffn_tall_kernel<..., true>): the
-// launch holds kQClusters clusters of C workgroups, C = the weight-row tiles,
-// each cluster on one XCD (the hardware deals linear workgroup ids to XCD
-// id % 8), workgroup j of a cluster always on weight tile j.  A cluster walks
-// row tiles: its C workgroups take the same row tile at the same time, so
-// the tile's activations come from memory once and from that XCD's L2 for
-// the rest, and the two clusters of an XCD take neighbouring tiles, which
-// share their weights when they belong to one group.  Row tiles are ordered
-// by size (full tiles first, then by 32-row class, each class in (group,
-// tile) order) and dealt to the clusters in snake order (round r forward,
-// round r + 1 backward), which balances the clusters' work to about 1% on
-// the prefill workload.  Every workgroup computes the same order from
-// tile_off and the group sizes, in LDS, at start.
-constexpr int kPlanGroups = 768;    // largest E_phys + 2 the schedule holds
-constexpr int kClasses = kQM / 32;  // size classes: 32-row sub-tiles in the last tile
+// Persistent schedule of the tall kernel (ffn_tall_kernel<..., true>): one
+// workgroup per compute unit, workgroup b serving first the work list of
+// XCD x = b % 8 (the hardware deals linear workgroup ids to the XCDs in
+// turn).  List x holds whole groups: first an eighth of the shared expert's
+// row tiles, then slots x, x + 8, x + 16, ...  Its units are (row tile,
+// weight tile) pairs, group by group, and inside a group weight tile major,
+// row tile minor, so the row tiles of one group that read the same weights
+// run side by side on one XCD and the weights come from memory about once
+// (the other reads hit that XCD's L2 or the memory-side cache), while the
+// weight tiles of one row tile follow each other and share its activations
+// in L2.  A workgroup claims its next unit with an atomic add on its list's
+// counter, so faster compute units take more units; once its list is empty
+// it claims from the other lists in turn.  The last workgroup to finish sets
+// the counters back to zero.  Every workgroup computes the lists' prefix of
+// row tiles from tile_off, in LDS, at start.
+constexpr int kClaimLists = 8;
+constexpr int kClaimStride = 16;                     // words between list counters (64-byte lines)
+constexpr int kClaimDone = kClaimLists * kClaimStride;
+static_assert(kClaimDone < MOE_CLAIM_WORDS, "claim counters fit the route table");
+constexpr int kPlanGroups = 768;                     // largest E_phys the schedule holds
+constexpr int kListChunks = kPlanGroups / kClaimLists + 1;   // groups per list (shared part first)
 
 template <int MODE, bool OUTF32, bool PERSIST>
 __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -1283,54 +1297,90 @@ void ffn_tall_kernel(TiledArgs ta) {
     if (!decode_work(ta, tw)) return;
     tall_tile<MODE, OUTF32>(ta, tw, x0s, x1s, x2s, x3s);
   } else {
-    __shared__ int plan[kClasses * kPlanGroups];   // per class: exclusive prefix of its tiles over the groups
+    // lt[x * L + c]: row tiles of chunk c of list x (chunk 0 the shared
+    // expert's part, chunk c > 0 slot x + 8 (c - 1)), then their exclusive
+    // prefix over all lists
+    __shared__ int lt[kClaimLists * kListChunks + 1];
     __shared__ int scan_tmp[kTThreads / 64 + 1];
+    __shared__ int claim_s;
     const StreamArgs& a = ta.s;
-    const int ng = a.E_phys + 1;                   // the slots, then the shared expert's group
-    for (int g = threadIdx.x; g < ng; g += kTThreads) {
-      const int tiles = ta.tile_off[g + 1] - ta.tile_off[g];
-      int full = 0, lc = -1;
-      if (tiles > 0) {
-        TileWork w;
-        group_rows(a, g, w);
-        const int last = w.R - kQM * (tiles - 1);      // rows of the last tile, 1..256
-        lc = (last + 31) / 32 - 1;                     // its class, kClasses - 1 = full
-        full = tiles - 1 + (lc == kClasses - 1 ? 1 : 0);
+    const int P = a.E_phys;
+    const int L = (P + kClaimLists - 1) / kClaimLists + 1;
+    const int ts = ta.tile_off[P + 1] - ta.tile_off[P];          // the shared expert's row tiles
+    const int cs = (ts + kClaimLists - 1) / kClaimLists;          // of them per list
+    for (int i = threadIdx.x; i < kClaimLists * L; i += kTThreads) {
+      const int x = i / L, c = i - x * L;
+      int t;
+      if (c == 0) {
+        t = ts - x * cs;
+        t = t < 0 ? 0 : (t > cs ? cs : t);
+      } else {
+        const int g = x + kClaimLists * (c - 1);
+        t = g < P ? ta.tile_off[g + 1] - ta.tile_off[g] : 0;
       }
-#pragma unroll
-      for (int c = 0; c < kClasses; ++c)
-        plan[c * kPlanGroups + g] = c == kClasses - 1 ? full : (c == lc ? 1 : 0);
+      lt[i] = t;
     }
     __syncthreads();
-    int class_total[kClasses];
-#pragma unroll
-    for (int c = 0; c < kClasses; ++c) class_total[c] = block_exclusive_scan(plan + c * kPlanGroups, ng, scan_tmp);
-    const int n_items = ta.tile_off[ng];
-    const int C = ta.cluster_size;
-    const int cpx = ta.clusters_per_xcd;
-    const int ncl = 8 * cpx;
-    const int local = blockIdx.x / 8;
-    const int k = (blockIdx.x % 8) * cpx + local / C;  // cluster
-    const int nt = local % C;                         // weight-row tile
-    for (int r = 0;; ++r) {
-      const int p = r * ncl + ((r & 1) ? ncl - 1 - k : k);
-      if (p >= n_items) break;
-      // class of sorted position p (largest class first), then its group
-      int c = kClasses - 1, base = 0;
-      while (c > 0 && p >= base + class_total[c]) { base += class_total[c]; --c; }
-      const int idx = p - base;
-      const int* pc = plan + c * kPlanGroups;
-      int lo = 0, hi = ng;                             // largest g with pc[g] <= idx
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pc[mid] <= idx) lo = mid; else hi = mid;
+    const int total = block_exclusive_scan(lt, kClaimLists * L, scan_tmp);
+    if (threadIdx.x == 0) lt[kClaimLists * L] = total;
+    __syncthreads();
+    const int ntn = a.N / (MODE == MODE_GATEUP ? kQN / 2 : kQN);   // weight tiles per row tile
+
+    auto claim = [&](int x) -> int {                 // thread 0's claim on list x
+      return (int)__hip_atomic_fetch_add(ta.claim + x * kClaimStride, 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    };
+    auto broadcast = [&](int v) -> int {             // thread 0's value to the workgroup
+      if (threadIdx.x == 0) claim_s = v;
+      __syncthreads();
+      const int r = __builtin_amdgcn_readfirstlane(claim_s);
+      __syncthreads();                               // claim_s is rewritten only after every read
+      return r;
+    };
+    const int home = blockIdx.x % kClaimLists;
+    int s = 0, x = home;
+    int u = broadcast(threadIdx.x == 0 ? claim(x) : 0);
+    for (;;) {
+      const int* pl = lt + x * L;                    // list x: chunk prefixes pl[0..L], pl[L] its end
+      const int base = pl[0];
+      if (u >= (pl[L] - base) * ntn) {               // list x is empty: the next one
+        if (++s == kClaimLists) break;
+        x = (home + s) % kClaimLists;
+        u = broadcast(threadIdx.x == 0 ? claim(x) : 0);
+        continue;
       }
+      int lo = 0, hi = L;                            // the chunk holding unit u: largest c with
+      while (hi - lo > 1) {                          // (pl[c] - base) * ntn <= u
+        const int mid = (lo + hi) >> 1;
+        if ((pl[mid] - base) * ntn <= u) lo = mid; else hi = mid;
+      }
+      const int tc = pl[lo + 1] - pl[lo];            // row tiles of the chunk (> 0: it holds u)
+      const int v = u - (pl[lo] - base) * ntn;
+      const int nt = v / tc;                         // weight tile major,
+      const int t = v - nt * tc;                     // row tile minor
       TileWork tw;
-      group_rows(a, lo, tw);
-      const int tiles = ta.tile_off[lo + 1] - ta.tile_off[lo];
-      tw.mt = c == kClasses - 1 ? idx - pc[lo] : tiles - 1;
+      if (lo == 0) {
+        group_rows(a, P, tw);
+        tw.mt = x * cs + t;
+      } else {
+        group_rows(a, x + kClaimLists * (lo - 1), tw);
+        tw.mt = t;
+      }
       tw.nt = nt;
-      tall_tile<MODE, OUTF32>(ta, tw, x0s, x1s, x2s, x3s);
+      int next = 0;
+      tall_tile<MODE, OUTF32>(ta, tw, x0s, x1s, x2s, x3s, [&]() -> void {
+        if (threadIdx.x == 0) next = claim(x);
+      });
+      u = broadcast(next);
+    }
+    // every workgroup has made its last claim once the done count reaches the
+    // grid; the last one zeroes the counters for the next launch
+    if (threadIdx.x == 0 &&
+        __hip_atomic_fetch_add(ta.claim + kClaimDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            gridDim.x - 1) {
+      for (int xx = 0; xx < kClaimLists; ++xx)
+        __hip_atomic_store(ta.claim + xx * kClaimStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ta.claim + kClaimDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -1376,11 +1426,11 @@ bool wide_supported(int mode, const TiledArgs& a) {
 
 // Which kernel takes a launch.  a.variant (moe_desc_t.debug_flags) can force
 // one; where the forced one does not apply to the shape the choice falls to
-// the next one down.  Packed weights: by default the hybrid tile (weights to
-// registers, activations by direct-to-LDS loads) where the K range is whole
-// blocks of four 32-wide steps, else the all-LDS one; row-major weights: the
-// register-staged wide tile; shapes the wide tile does not divide: the
-// narrow one.
+// the next one down.  Packed weights: by default the tall tile where it
+// applies, then the hybrid tile (weights to registers, activations by
+// direct-to-LDS loads) where the K range is whole blocks of four 32-wide
+// steps, else the all-LDS one; row-major weights: the register-staged wide
+// tile; shapes the wide tile does not divide: the narrow one.
 int tiled_choice(const TiledArgs& a, int packed, int mode) {
   if (packed && (a.variant == 0 || a.variant == MOE_DEBUG_TILED_TALL) && tall_supported(mode, a))
     return MOE_DEBUG_TILED_TALL;
@@ -1408,17 +1458,15 @@ hipError_t launch_ffn_tiled(const TiledArgs& a, int fp8, int packed, int mode, i
   const int choice = tiled_choice(a, packed, mode);
   if (choice == MOE_DEBUG_TILED_TALL) {
     const int ntn = a.s.N / (mode == MODE_GATEUP ? kQN / 2 : kQN);
-    // persistent clusters where an XCD holds at least one cluster of ntn
-    // workgroups and the schedule fits its LDS; else one workgroup per item
+    // the persistent schedule (one workgroup per compute unit, work claimed
+    // through the route table's counters) where there are counters, no K
+    // split, and the order fits its LDS; else one workgroup per work item
     const int cus = device_cus();
-    TiledArgs pa = a;
-    pa.cluster_size = ntn;
-    pa.clusters_per_xcd = cus > 0 && cus % 8 == 0 ? (cus / 8) / ntn : 0;
-    if (a.s.ksplit == 1 && pa.clusters_per_xcd >= 1 && a.s.E_phys + 2 <= kPlanGroups) {
-      const dim3 grid(8 * pa.clusters_per_xcd * ntn);
-      if (mode == MODE_GATEUP) hipLaunchKernelGGL((ffn_tall_kernel<MODE_GATEUP, false, true>), grid, dim3(kTThreads), 0, s, pa);
-      else if (a.s.out_f32) hipLaunchKernelGGL((ffn_tall_kernel<MODE_DOWN, true, true>), grid, dim3(kTThreads), 0, s, pa);
-      else hipLaunchKernelGGL((ffn_tall_kernel<MODE_DOWN, false, true>), grid, dim3(kTThreads), 0, s, pa);
+    if (a.claim && a.s.ksplit == 1 && a.s.E_phys <= kPlanGroups && cus >= kClaimLists) {
+      const dim3 grid(cus);
+      if (mode == MODE_GATEUP) hipLaunchKernelGGL((ffn_tall_kernel<MODE_GATEUP, false, true>), grid, dim3(kTThreads), 0, s, a);
+      else if (a.s.out_f32) hipLaunchKernelGGL((ffn_tall_kernel<MODE_DOWN, true, true>), grid, dim3(kTThreads), 0, s, a);
+      else hipLaunchKernelGGL((ffn_tall_kernel<MODE_DOWN, false, true>), grid, dim3(kTThreads), 0, s, a);
       return hipGetLastError();
     }
     const dim3 grid(ntn, max_tiles + 8, a.s.ksplit);

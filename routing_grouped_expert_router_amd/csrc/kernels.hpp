@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe.h"
+
 namespace moe {
 
 // ---- routing ----------------------------------------------------------------
@@ -31,6 +33,7 @@ struct RouteArgs {
   int32_t* topk_ids; float* topk_w; int32_t* topk_phys; int32_t* row_of;
   int32_t* slot_of; int32_t* src_of; int32_t* counts; int32_t* offsets;
   int32_t* masked_m; int32_t* spill_off; int32_t* pad_off; int32_t* tile_off; uint32_t* status;
+  uint32_t* claim;          // [MOE_CLAIM_WORDS] zeroed here (may be null)
   int n_shared;
   RouteWs ws;
   // grouped sigmoid router (selection phase only); grouped == 0: softmax top-K
@@ -44,6 +47,7 @@ struct ReceivedArgs {
   const int32_t* counts_in; int E_phys, M_max, T, n_shared;
   int32_t* counts; int32_t* masked_m; int32_t* offsets; int32_t* spill_off; int32_t* tile_off;
   uint32_t* status;
+  uint32_t* claim;          // [MOE_CLAIM_WORDS] zeroed here (may be null)
 };
 hipError_t launch_route_received(const ReceivedArgs& a, hipStream_t s);
 
@@ -112,8 +116,8 @@ struct TiledArgs {
   int min_rows;              // groups with at most this many rows are skipped
   int64_t x_bytes;           // bytes of the activation rows X addresses (rows * ldx * 2)
   int variant;               // 0: the launcher's choice; else a MOE_DEBUG_TILED_* kernel
-  int cluster_size;          // persistent tall kernel: workgroups per cluster (= weight-row tiles)
-  int clusters_per_xcd;      //   and clusters on each XCD (set by the launcher)
+  uint32_t* claim;           // [MOE_CLAIM_WORDS] work-claim counters, zero on entry and on
+                             // exit (null: one workgroup per work item)
 };
 // largest MOE_DEBUG_TILED_* value
 constexpr int kTiledVariants = 5;

@@ -218,7 +218,7 @@ moe_status_t route_args(const moe_desc_t* d, const float* logits, int32_t T, con
   a.row_of = r->row_of; a.slot_of = r->slot_of; a.src_of = r->src_of;
   a.counts = r->counts; a.offsets = r->offsets; a.masked_m = r->masked_m;
   a.spill_off = r->spill_off; a.pad_off = r->pad_off; a.tile_off = r->tile_off;
-  a.status = r->status; a.n_shared = d->n_shared;
+  a.status = r->status; a.claim = r->claim; a.n_shared = d->n_shared;
   a.ws.local_rank = reinterpret_cast<int32_t*>(base + wl.local_rank);
   a.ws.blk = reinterpret_cast<int32_t*>(base + wl.blk);
   a.ws.blk_flags = reinterpret_cast<int32_t*>(base + wl.flags);
@@ -309,7 +309,7 @@ moe_status_t moe_route_received(const moe_desc_t* d, const int32_t* counts, int3
   ReceivedArgs a = {};
   a.counts_in = counts; a.E_phys = d->E_phys; a.M_max = d->M_max; a.T = T; a.n_shared = d->n_shared;
   a.counts = r->counts; a.masked_m = r->masked_m; a.offsets = r->offsets;
-  a.spill_off = r->spill_off; a.tile_off = r->tile_off; a.status = r->status;
+  a.spill_off = r->spill_off; a.tile_off = r->tile_off; a.status = r->status; a.claim = r->claim;
   return hip_status(launch_route_received(a, stream));
 }
 
@@ -435,9 +435,10 @@ moe_status_t launch_expert_gemm(const moe_desc_t* d, const moe_route_t* r, int32
     if (e != hipSuccess) return hip_status(e);
   }
   if (!need_c) return MOE_OK;
-  TiledArgs ta;
+  TiledArgs ta = {};
   ta.s = a;
   ta.tile_off = r->tile_off;
+  ta.claim = r->claim;
   ta.variant = (int)(((uint32_t)d->debug_flags & MOE_DEBUG_TILED_MASK) >> MOE_DEBUG_TILED_SHIFT);
   ta.min_rows = all_tiled ? 0 : (mt < 4) ? 64 : a_max;
   // X holds the layer input (T rows) when gathering, else the grouped buffer

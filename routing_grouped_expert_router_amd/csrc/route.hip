@@ -120,6 +120,8 @@ __global__ __launch_bounds__(kScanThreads) void route_received_kernel(ReceivedAr
     a.offsets[p] = cnt[p];
     a.tile_off[p] = aux[p];
   }
+  if (a.claim)
+    for (int i = tid; i < MOE_CLAIM_WORDS; i += kScanThreads) a.claim[i] = 0u;
   if (tid == 0) {
     a.offsets[P] = total;
     a.spill_off[P] = 0;

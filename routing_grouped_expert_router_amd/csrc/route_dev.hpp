@@ -363,6 +363,8 @@ __device__ __forceinline__ void scan_all(const RouteArgs& a) {
   __syncthreads();
   const int ttotal = block_exclusive_scan(aux, P, tmp);
   for (int p = tid; p < P; p += nth) a.tile_off[p] = aux[p];
+  if (a.claim)
+    for (int i = tid; i < MOE_CLAIM_WORDS; i += nth) a.claim[i] = 0u;
   if (tid == 0) {
     a.tile_off[P] = ttotal;
     a.tile_off[P + 1] = ttotal + (a.n_shared ? (a.T + kTileRows - 1) / kTileRows : 0);

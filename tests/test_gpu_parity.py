@@ -383,6 +383,30 @@ def test_wide_tiled_kernel_matches_narrow(name):
                 assert torch.equal(ref, out), (name, packed, fused, var)
 
 
+@pytest.mark.parametrize("name", ["tiled_contig_shared", "tiled_wide", "tiled_skewed_small_groups"])
+def test_claim_counters(name):
+    """The large-group kernels' persistent schedule claims work through the
+    route table's counters.  Routing zeroes them (here over a poisoned
+    table), every expert call leaves them zero, and the outputs equal those
+    of the one-workgroup-per-item schedule (no counter table) bit for bit."""
+    cfg = next(c for c in SMALL if c.name == name)
+    b = Built(cfg, packed=True)
+    lg = b.oracle_logits()
+    rt = b.layer.rt
+    rt.claim.fill_(12345)
+    ref = b.run(lg).clone()
+    assert not rt.claim.any(), name
+    ref2 = b.run(lg, fused_gather=False).clone()
+    assert not rt.claim.any(), name
+    assert torch.equal(ref, ref2)
+    rt.c.claim = None
+    try:
+        out = b.run(lg).clone()
+    finally:
+        rt.c.claim = rt.claim.data_ptr()
+    assert torch.equal(ref, out), name
+
+
 def test_pack_layout_matches_definition():
     """moe_pack_weights places element (n, k) where the layout definition
     says: K block k/128, panel n/16 (step-major), then the lane piece of
@@ -536,6 +560,7 @@ def test_full_size(cfg):
     say(f"  built {cfg.name}")
     lg = b.oracle_logits()
     out = out_np(b.run(lg))
+    assert not b.layer.rt.claim.any()    # the large-group kernels leave their counters zero
     g = route_np(b.layer.rt, b.T, cfg.K)
     if b.T <= 256:
         toks = np.arange(b.T)
