@@ -65,6 +65,10 @@ def parse():
                     help="first run a plain 512 MiB device copy three times (a kernel of known "
                          "traffic for scaling hardware byte counters)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak probes")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no timing: turn the counter_collection.csv files of a FETCH_SIZE and a "
+                         "WRITE_SIZE rocprofv3 pass over `bench.py --workload W --copy-calibration` "
+                         "into profiles/gate_up_traffic_W.md (needs --workload)")
     ap.add_argument("--debug-flags", type=int, default=0,
                     help="moe_desc_t.debug_flags for an ablation (MOE_DEBUG_* in include/moe.h: e.g. "
                          "a forced large-group kernel); outputs stay bit-identical")
@@ -361,12 +365,12 @@ def kernel_sources_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch of the gate/up kernel from the committed counter
     summary (profiles/gate_up_traffic_<workload>.md: FETCH_SIZE and
     WRITE_SIZE passes scaled by a plain copy of known size), or None when
-    there is none or the kernel's sources (listed in the summary) changed
-    since it was taken."""
+    there is none, it was taken of another kernel, or the kernel's sources
+    (listed in the summary) changed since it was taken."""
     path = os.path.join(ROOT, "profiles", f"gate_up_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
@@ -377,12 +381,96 @@ def measured_traffic(workload: str):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
     files = vals.get("kernel_sources", "").split()
-    if not files or vals.get("kernel_sources_sha256_16") != kernel_sources_hash(files):
+    if vals.get("kernel") != kernel or not files or \
+            vals.get("kernel_sources_sha256_16") != kernel_sources_hash(files):
         return None
     try:
         return int(vals["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+KERNEL_FILE = {"ffn_stream_kernel": "ffn_stream.hip", "ffn_tall_kernel": "ffn_tiled.hip",
+               "ffn_whyb_kernel": "ffn_tiled.hip", "ffn_wdma_kernel": "ffn_tiled.hip",
+               "ffn_wide_kernel": "ffn_tiled.hip", "ffn_tiled_kernel": "ffn_tiled.hip"}
+
+
+def kernel_sources(kernel: str) -> list:
+    """The csrc files a kernel is compiled from: its translation unit and the
+    local headers it includes, recursively."""
+    import re
+    csrc = os.path.join(ROOT, "routing_grouped_expert_router_amd", "csrc")
+    seen, todo = [], [KERNEL_FILE[kernel]]
+    while todo:
+        f = todo.pop(0)
+        if f in seen or not os.path.exists(os.path.join(csrc, f)):
+            continue
+        seen.append(f)
+        with open(os.path.join(csrc, f)) as fh:
+            todo += re.findall(r'^#include "([^"]+)"', fh.read(), re.M)
+    return sorted(seen)
+
+
+def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, cmd_prefix: str):
+    """profiles/gate_up_traffic_<workload>.md from two counter passes: the
+    first three device copies (the 512 MiB calibration of --copy-calibration)
+    give the factor from counter units to bytes, the gate/up kernel's
+    dispatches the bytes per launch."""
+    import csv
+    import re
+    from workloads import configs
+    from routing_grouped_expert_router_amd import binding as B
+    cfg = configs.by_name(workload)
+    d = B.Desc.from_config(cfg, w_packed=1)
+    kernel = B.expert_kernel(d, cfg.T, 0)
+    mode0 = (re.compile(r"ffn_stream_kernel<(true|false), 0,") if kernel == "ffn_stream_kernel"
+             else re.compile(re.escape(kernel) + r"<0,"))
+    cal_bytes = 512 << 20
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        with open(path) as fh:
+            rows = [r for r in csv.DictReader(fh) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        cal = [float(r["Counter_Value"]) for r in rows if r["Kernel_Name"] == "__amd_rocclr_copyBuffer"][:3]
+        ker = [float(r["Counter_Value"]) for r in rows if mode0.search(r["Kernel_Name"])]
+        names = sorted({r["Kernel_Name"] for r in rows if mode0.search(r["Kernel_Name"])})
+        if len(cal) < 3 or max(cal) > 1.05 * min(cal) or not ker:
+            raise SystemExit(f"{path}: calibration copies {cal} / {len(ker)} gate/up dispatches unusable")
+        factor = cal_bytes / 1024 / (sum(cal) / 3)
+        out[counter] = dict(cal=sum(cal) / 3, factor=factor, n=len(ker), kib=sum(ker) / len(ker),
+                            bytes=int(round(sum(ker) / len(ker) * 1024 * factor)), names=names)
+    rd, wr = out["FETCH_SIZE"], out["WRITE_SIZE"]
+    files = kernel_sources(kernel)
+    lines = [
+        f"# HBM traffic of the expert gate/up kernel, workload {workload}",
+        "",
+        "Two counter passes, one counter each, over the bench with a 512 MiB plain device copy run "
+        "three times first as the calibration kernel of known traffic (repository root on the GPU "
+        "box, `R=$PWD`):",
+        "",
+        f"    {cmd_prefix} --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/FETCH_SIZE -o run -- "
+        f"python3 $R/bench.py --workload {workload} --no-cpu --no-peaks --steps 3 --warmup 1 --copy-calibration",
+        f"    {cmd_prefix} --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/WRITE_SIZE -o run -- "
+        f"python3 $R/bench.py --workload {workload} --no-cpu --no-peaks --steps 3 --warmup 1 --copy-calibration",
+        f"    python3 bench.py --workload {workload} --summarize-traffic "
+        "gpurun_out/prof/FETCH_SIZE/run_counter_collection.csv gpurun_out/prof/WRITE_SIZE/run_counter_collection.csv",
+        "",
+        f"* calibration copy (512 MiB each way): FETCH_SIZE {rd['cal']:.0f} KiB -> factor {rd['factor']:.4f}; "
+        f"WRITE_SIZE {wr['cal']:.0f} KiB -> factor {wr['factor']:.4f}",
+        f"* kernel `{', '.join(rd['names'])}` ({rd['n']} dispatches): FETCH_SIZE {rd['kib']:.0f} KiB, "
+        f"WRITE_SIZE {wr['kib']:.0f} KiB per dispatch",
+        f"* scaled HBM bytes per launch: read {rd['bytes']} + write {wr['bytes']} = {rd['bytes'] + wr['bytes']}",
+        "",
+        f"traffic_bytes_per_launch: {rd['bytes'] + wr['bytes']}",
+        f"kernel: {kernel}",
+        f"kernel_sources: {' '.join(files)}",
+        f"kernel_sources_sha256_16: {kernel_sources_hash(files)}",
+        "",
+    ]
+    path = os.path.join(ROOT, "profiles", f"gate_up_traffic_{workload}.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines))
+    print(f"wrote {path}: {rd['bytes'] + wr['bytes']} bytes per launch")
 
 
 def roofline(cfg, r, peaks):
@@ -393,7 +481,7 @@ def roofline(cfg, r, peaks):
         tf = r["gu_flops"] / (r["gu_ms"] * 1e-3) / 1e12
         out = {"bound": "mfma", "kernel": kernel, "achieved": round(tf, 1),
                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-               "traffic": measured_traffic(cfg.name), "kernel_us": round(r["gu_ms"] * 1e3, 2),
+               "traffic": measured_traffic(cfg.name, r["gu_kernel"]), "kernel_us": round(r["gu_ms"] * 1e3, 2),
                "algorithmic_flops": r["gu_flops"]}
         if peaks:
             out["achievable_peak"] = peaks["mfma_bf16_tflops"]
@@ -402,7 +490,7 @@ def roofline(cfg, r, peaks):
     gbs = r["gu_bytes"] / (r["gu_ms"] * 1e-3) / 1e9
     out = {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-           "traffic": measured_traffic(cfg.name),
+           "traffic": measured_traffic(cfg.name, r["gu_kernel"]),
            "kernel_us": round(r["gu_ms"] * 1e3, 2), "algorithmic_bytes": r["gu_bytes"]}
     if peaks:
         out["achievable_peak"] = peaks["hbm_read_gbs"]
@@ -518,6 +606,12 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the MoE layer here runs on a single MI355X)", file=sys.stderr)
         sys.exit(2)
+    if args.summarize_traffic:
+        if not args.workload:
+            raise SystemExit("--summarize-traffic needs --workload")
+        summarize_traffic(args.workload, *args.summarize_traffic,
+                          "cd /tmp && TMPDIR=/tmp timeout -s KILL 150 rocprofv3")
+        return
     import torch
     from workloads import configs
     if args.copy_calibration:

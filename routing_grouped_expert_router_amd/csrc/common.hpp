@@ -69,6 +69,31 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8 a, const bf16x8 b, f3
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// D += A * B of v_mfma_f32_16x16x32_bf16 on an accumulator that stays in its
+// accumulation registers: the operand is tied, so the register allocator
+// cannot rotate the 256 accumulators of a wave through copies between loop
+// stages (it does with the builtin's separate source and result at this
+// register count, and the overlapping copies serialise the matrix core).
+// Every use accumulates into exactly the registers it reads, which the
+// matrix core chains back to back; the operands come from loads and LDS
+// reads the compiler waits for.  The compiler does not know the statement is
+// a multi-pass product, so it inserts no wait states before instructions
+// that read its result: acc_fence() must separate the last product from any
+// read of the accumulators, including moves the compiler adds at the exit of
+// the loop holding the products.
+__device__ __forceinline__ void mfma_acc(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// wait states between the last product and the first read of its result
+// (more than the longest product's passes); the scheduling barriers keep the
+// compiler from moving reads of the accumulators above it
+__device__ __forceinline__ void acc_fence() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+
 // ---- ordering key for top-K ------------------------------------------------
 // Monotone map fp32 -> u32 with -0 == +0 and NaN below -inf (key 0).
 __device__ __forceinline__ uint32_t order_key(float v) {

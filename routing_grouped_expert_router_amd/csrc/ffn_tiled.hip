@@ -951,25 +951,6 @@ void ffn_whyb_kernel(TiledArgs ta) {
 //    results are the same bit for bit.
 // The launch needs packed weights and a K range of whole blocks of four
 // 64-wide stages.
-// D += A * B of v_mfma_f32_16x16x32_bf16 on an accumulator that stays in its
-// accumulation registers: the operand is tied, so the register allocator
-// cannot rotate the 256 accumulators of a wave through copies between loop
-// stages (it does with the builtin's separate source and result at this
-// register count, and the overlapping copies serialise the matrix core).
-// Every use accumulates into exactly the registers it reads, which the
-// matrix core chains back to back; the operands come from loads and LDS
-// reads the compiler waits for.  The compiler does not know the statement is
-// a multi-pass product, so it inserts no wait states before instructions
-// that read its result: acc_fence() must separate the last product from any
-// read of the accumulators, including moves the compiler adds at the exit of
-// the loop holding the products.
-__device__ __forceinline__ void mfma_acc(f32x4& acc, const bf16x8& a, const bf16x8& b) {
-  asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-// wait states between the last product and the first read of its result
-// (more than the longest product's passes)
-__device__ __forceinline__ void acc_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"); }
-
 constexpr int kQM = kTileRows;        // token rows per tile (256)
 constexpr int kQMT = kQM / 16;        // 16-row MFMA tiles per tile
 constexpr int kQStages = 4;           // LDS ring of 64-wide K stages
@@ -1269,10 +1250,9 @@ __device__ __forceinline__ void tall_tile(const TiledArgs& ta, const TileWork& t
 // row tiles, then slots x, x + 8, x + 16, ...  Its units are (row tile,
 // weight tile) pairs, group by group, and inside a group weight tile major,
 // row tile minor, so the row tiles of one group that read the same weights
-// run side by side on one XCD and the weights come from memory about once
-// (the other reads hit that XCD's L2 or the memory-side cache), while the
-// weight tiles of one row tile follow each other and share its activations
-// in L2.  A workgroup claims its next unit with an atomic add on its list's
+// run close together on one XCD and the repeated weight reads can hit the
+// memory-side cache, while the weight tiles of one row tile follow each
+// other and share its activations in L2.  A workgroup claims its next unit with an atomic add on its list's
 // counter, so faster compute units take more units; once its list is empty
 // it claims from the other lists in turn.  The last workgroup to finish sets
 // the counters back to zero.  Every workgroup computes the lists' prefix of

@@ -31,8 +31,9 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4* 
   if (acc == kNeverDigest) sink[blockIdx.x] = acc;
 }
 
-// eight independent accumulators per wave, operands derived from the lane so
-// nothing folds; one store of a digest that is, in practice, never taken
+// eight independent accumulators per wave (tied, as in the expert kernels),
+// operands derived from the lane so nothing folds; one store of a digest
+// that is, in practice, never taken
 __global__ __launch_bounds__(kProbeThreads) void probe_mfma_kernel(int iters, uint32_t* __restrict__ sink) {
   const int lane = threadIdx.x & 63;
   bf16x8 a, b;
@@ -46,8 +47,12 @@ __global__ __launch_bounds__(kProbeThreads) void probe_mfma_kernel(int iters, ui
   for (int j = 0; j < 8; ++j) acc[j] = f32x4{0, 0, 0, 0};
   for (int i = 0; i < iters; ++i) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = mfma16x16x32(a, b, acc[j]);
+    for (int j = 0; j < 8; ++j) mfma_acc(acc[j], a, b);
   }
+  // the wait states, tied to every accumulator so that no read comes first
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+a"(acc[4]), "+a"(acc[5]),
+                 "+a"(acc[6]), "+a"(acc[7]));
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) s += acc[j].x + acc[j].y + acc[j].z + acc[j].w;
