@@ -145,13 +145,14 @@ class Setup:
 
     def step(self, ev=None):
         B, L, d, T = self.B, self.layer, self.d, self.cfg.T
-        B.moe_router_logits(d, self.x, self.wr, self.bias, T, L.logits)
-        if L.ep is not None:
-            B.moe_route_ep(d, L.logits, T, L.rt, L.ws, L.ep, L.router, L.l2p, L.rcount)
-        elif L.router is None:
-            B.moe_route(d, L.logits, T, L.rt, L.ws, L.l2p, L.rcount)
+        if L.ep is None and L.router is None:
+            B.moe_router_route(d, self.x, self.wr, self.bias, T, L.logits, L.rt, L.ws, L.l2p, L.rcount)
         else:
-            B.moe_route_grouped(d, L.logits, T, L.rt, L.ws, L.router, L.l2p, L.rcount)
+            B.moe_router_logits(d, self.x, self.wr, self.bias, T, L.logits)
+            if L.ep is not None:
+                B.moe_route_ep(d, L.logits, T, L.rt, L.ws, L.ep, L.router, L.l2p, L.rcount)
+            else:
+                B.moe_route_grouped(d, L.logits, T, L.rt, L.ws, L.router, L.l2p, L.rcount)
         if self.a8:
             B.moe_quantize_1x128(self.x, T, L.xq, L.xs)
             if ev is not None:

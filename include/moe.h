@@ -244,6 +244,18 @@ moe_status_t moe_route(const moe_desc_t* d, const float* logits, int32_t T,
                        const moe_route_t* r, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* a1-a4 in one call: moe_router_logits (writing logits) then moe_route on
+ * them, with the arguments, results and errors of the two calls.  With few
+ * tokens and experts (T * E <= 16, E <= 64, the router's one-logit-per-
+ * workgroup summation) both run in one workgroup of one launch, which saves
+ * a launch on the decode path; the logits and every table are bit-identical
+ * to the two calls.  (vllbc blog, routing section and Table 3-1.) */
+moe_status_t moe_router_route(const moe_desc_t* d, const void* x, const void* w_router,
+                              const float* bias, int32_t T, float* logits,
+                              const int32_t* l2p, const int32_t* replica_count,
+                              const moe_route_t* r, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
 /* moe_route for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc): no
  * workspace argument.  The route workspace is a static device array of

@@ -36,7 +36,7 @@ EXPORTED = [
     "moe_replica_map_from_p2l", "moe_route_ep", "moe_route_received", "moe_ep_local_map",
     "moe_eplb_plan", "moe_quantize_1x128", "moe_expert_gate_up_a8", "moe_expert_down_a8",
     "moe_grouped_ffn_a8", "moe_decode_fused_workspace_bytes", "moe_decode_fused",
-    "moe_expert_kernel", "moe_probe_read", "moe_probe_mfma_bf16", "moe_route_noalloc",
+    "moe_expert_kernel", "moe_probe_read", "moe_probe_mfma_bf16", "moe_route_noalloc", "moe_router_route",
 ]
 MOE_NOALLOC_WORKSPACE_BYTES = 4 << 20
 MOE_PROBE_SINK_WORDS = 8192
@@ -102,6 +102,7 @@ def lib() -> ctypes.CDLL:
             "moe_route": (ctypes.c_int, [D, _P, i32, _P, _P, R, _P, sz, _P]),
             "moe_route_grouped": (ctypes.c_int, [D, _P, i32, GR, _P, _P, R, _P, sz, _P]),
             "moe_route_noalloc": (ctypes.c_int, [D, _P, i32, _P, _P, R, _P]),
+            "moe_router_route": (ctypes.c_int, [D, _P, _P, _P, i32, _P, _P, _P, R, _P, sz, _P]),
             "moe_permute": (ctypes.c_int, [D, _P, i32, R, _P, _P]),
             "moe_expert_gate_up": (ctypes.c_int, [D, W, R, i32, _P, _P, _P]),
             "moe_expert_gate_up_x": (ctypes.c_int, [D, W, R, i32, _P, _P, _P]),
@@ -291,6 +292,14 @@ def moe_route(d: Desc, logits, T, rt: RouteTables, ws, l2p=None, replica_count=N
     _check(lib().moe_route(ctypes.byref(d.c()), _ptr(logits), T, _ptr(l2p), _ptr(replica_count),
                            ctypes.byref(rt.c), _ptr(ws), ws.numel() * ws.element_size(),
                            _stream(stream)), "moe_route")
+
+
+def moe_router_route(d: Desc, x, w_router, bias, T, logits, rt: RouteTables, ws, l2p=None, replica_count=None,
+                     stream=None):
+    """moe_router_logits then moe_route in one call (one launch for tiny T * E)."""
+    _check(lib().moe_router_route(ctypes.byref(d.c()), _ptr(x), _ptr(w_router), _ptr(bias), T, _ptr(logits),
+                                  _ptr(l2p), _ptr(replica_count), ctypes.byref(rt.c), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)), "moe_router_route")
 
 
 def moe_route_noalloc(d: Desc, logits, T, rt: RouteTables, l2p=None, replica_count=None, stream=None):
@@ -528,16 +537,21 @@ class MoELayer:
         Returns the output view [T, H]."""
         d = self.d
         T = x.shape[0] if T is None else T
-        if logits is None:
-            moe_router_logits(d, x, self.w_router, self.bias, T, self.logits, stream)
-            logits = self.logits
-        if self.ep is not None:
-            moe_route_ep(d, logits, T, self.rt, self.ws, self.ep, self.router, self.l2p, self.rcount,
-                         stream)
-        elif self.router is None:
-            moe_route(d, logits, T, self.rt, self.ws, self.l2p, self.rcount, stream)
+        if logits is None and self.ep is None and self.router is None:
+            # router logits and routing in one call (one launch for tiny T * E)
+            moe_router_route(d, x, self.w_router, self.bias, T, self.logits, self.rt, self.ws, self.l2p,
+                             self.rcount, stream)
         else:
-            moe_route_grouped(d, logits, T, self.rt, self.ws, self.router, self.l2p, self.rcount, stream)
+            if logits is None:
+                moe_router_logits(d, x, self.w_router, self.bias, T, self.logits, stream)
+                logits = self.logits
+            if self.ep is not None:
+                moe_route_ep(d, logits, T, self.rt, self.ws, self.ep, self.router, self.l2p, self.rcount,
+                             stream)
+            elif self.router is None:
+                moe_route(d, logits, T, self.rt, self.ws, self.l2p, self.rcount, stream)
+            else:
+                moe_route_grouped(d, logits, T, self.rt, self.ws, self.router, self.l2p, self.rcount, stream)
         if self.a8:
             moe_grouped_ffn_a8(d, self.weights, self.rt, T, x, self.xq, self.xs, self.h, self.hq, self.hs,
                                self.y, stream)

@@ -160,6 +160,12 @@ struct RouterArgs {
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 bool router_uses_mfma(int E, int H, int x_f32);
 
+// router logits, then routing: one launch when T * E <= kTinyRouterItems
+// (softmax top-K, E <= 64, no expert-parallel map), else the two launches
+constexpr int kTinyRouterItems = 16;
+bool router_route_fits(const RouterArgs& ra, const RouteArgs& a);
+hipError_t launch_router_route(const RouterArgs& ra, const RouteArgs& a, hipStream_t s);
+
 // ---- persistent single-launch decode layer --------------------------------------
 
 // Fused workspace: barrier words, then the slot list.  Lines of 64 words:

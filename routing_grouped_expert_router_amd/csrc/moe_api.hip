@@ -269,6 +269,21 @@ moe_status_t moe_route(const moe_desc_t* d, const float* logits, int32_t T, cons
   return route_impl(d, logits, T, nullptr, nullptr, l2p, replica_count, r, ws, ws_bytes, stream);
 }
 
+moe_status_t moe_router_route(const moe_desc_t* d, const void* x, const void* w_router, const float* bias,
+                              int32_t T, float* logits, const int32_t* l2p, const int32_t* replica_count,
+                              const moe_route_t* r, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = moe_check_desc(d);
+  if (st != MOE_OK) return st;
+  if (T > 0 && (!x || !w_router)) return MOE_ERR_ARG;
+  RouteArgs a;
+  st = route_args(d, logits, T, nullptr, nullptr, l2p, replica_count, r, ws, ws_bytes, a);
+  if (st != MOE_OK) return st;
+  if (T == 0) return hip_status(launch_route(a, stream));   // no logits to compute
+  const RouterArgs ra = {x, d->act_dtype == MOE_F32, static_cast<const uint16_t*>(w_router), bias,
+                         T, d->E, d->H, logits};
+  return hip_status(launch_router_route(ra, a, stream));
+}
+
 moe_status_t moe_route_noalloc(const moe_desc_t* d, const float* logits, int32_t T, const int32_t* l2p,
                                const int32_t* replica_count, const moe_route_t* r, hipStream_t stream) {
   const moe_status_t st = moe_check_desc(d);
@@ -697,9 +712,8 @@ moe_status_t moe_forward(const moe_desc_t* d, const void* x, const void* w_route
                          const moe_weights_t* w, int32_t T, float* logits, const moe_route_t* r,
                          void* ws, size_t ws_bytes, void* xg, void* h, void* y, void* out,
                          hipStream_t stream) {
-  moe_status_t st = moe_router_logits(d, x, w_router, bias, T, logits, stream);
-  if (st != MOE_OK) return st;
-  st = moe_route(d, logits, T, l2p, replica_count, r, ws, ws_bytes, stream);
+  moe_status_t st = moe_router_route(d, x, w_router, bias, T, logits, l2p, replica_count, r, ws, ws_bytes,
+                                     stream);
   if (st != MOE_OK) return st;
   if (d->act_dtype == MOE_BF16) {
     // the expert kernel gathers its rows from x; xg is not used

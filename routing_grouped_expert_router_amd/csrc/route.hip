@@ -22,7 +22,10 @@
 //     its logical expert, its replica l2p[l][j mod R] and rank j / R inside
 //     that slot, its row, its buffer slot, and src_of.
 //   For T <= 64 (one block) the four run back to back in one workgroup.
+#include <type_traits>
+
 #include "route_dev.hpp"
+#include "router_dev.hpp"
 
 namespace moe {
 
@@ -51,7 +54,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_assign_kernel(RouteArgs a
 // The barrier between phases orders the global-memory tables each phase
 // writes before the next one reads them.
 template <int LPT, int NPL, bool GROUPED>
-__global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(RouteArgs a) {
+__device__ __forceinline__ void route_one_workgroup(const RouteArgs& a) {
   if (a.T > 0) {
     if constexpr (GROUPED) select_tokens_grouped<NPL>(a, 0, a.T, threadIdx.x / kWave, kFusedThreads / kWave);
     else select_tokens<LPT, NPL>(a, 0, a.T, threadIdx.x / kWave, kFusedThreads / kWave);
@@ -63,6 +66,54 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(RouteArgs a)
   __syncthreads();
   const int64_t TK = (int64_t)a.T * a.K;
   for (int64_t i = threadIdx.x; i < TK; i += kFusedThreads) assign_one(a, i);
+}
+
+template <int LPT, int NPL, bool GROUPED>
+__global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(RouteArgs a) {
+  route_one_workgroup<LPT, NPL, GROUPED>(a);
+}
+
+// A few tokens and experts (T * E <= kTinyRouterItems, E <= 64): the router
+// logits and the routing in one workgroup, one launch instead of two.  Its
+// four groups of 256 threads take the (token, expert) items in turn, each
+// summed exactly as the router kernel's one-item workgroups sum it, so the
+// logits, and with them the tables, are bit-identical to the two launches.
+constexpr int kRouterGroups = kFusedThreads / 256;
+
+template <bool XF32, int LPT>
+__global__ __launch_bounds__(kFusedThreads) void router_route_kernel(RouterArgs ra, RouteArgs a) {
+  __shared__ float red[kRouterGroups][4][1];
+  const int grp = threadIdx.x >> 8, gtid = threadIdx.x & 255;
+  const int items = ra.T * ra.E;
+  for (int i0 = 0; i0 < items; i0 += kRouterGroups) {
+    const int i = i0 + grp;
+    router_small_group<XF32, 1>(ra, i < items ? i / ra.E : -1, i < items ? i % ra.E : 0, gtid, red[grp]);
+  }
+  __syncthreads();        // the logits this workgroup wrote are read back by the routing
+  route_one_workgroup<LPT, 1, false>(a);
+}
+
+bool router_route_fits(const RouterArgs& ra, const RouteArgs& a) {
+  return !a.grouped && !a.local_of && a.E <= 64 && ra.E == a.E && ra.T == a.T && a.T >= 1 &&
+         a.T * a.E <= kTinyRouterItems && !router_uses_mfma(ra.E, ra.H, ra.x_f32);
+}
+
+hipError_t launch_router_route(const RouterArgs& ra, const RouteArgs& a, hipStream_t s) {
+  if (!router_route_fits(ra, a)) {
+    const hipError_t e = launch_router(ra, s);
+    return e != hipSuccess ? e : launch_route(a, s);
+  }
+  const dim3 g(1), b(kFusedThreads);
+  auto go = [&](auto xf, auto lpt) -> void {
+    hipLaunchKernelGGL((router_route_kernel<decltype(xf)::value, decltype(lpt)::value>), g, b, 0, s, ra, a);
+  };
+  using F = std::false_type;
+  using Tr = std::true_type;
+  if (a.E <= 8) ra.x_f32 ? go(Tr{}, std::integral_constant<int, 8>{}) : go(F{}, std::integral_constant<int, 8>{});
+  else if (a.E <= 16) ra.x_f32 ? go(Tr{}, std::integral_constant<int, 16>{}) : go(F{}, std::integral_constant<int, 16>{});
+  else if (a.E <= 32) ra.x_f32 ? go(Tr{}, std::integral_constant<int, 32>{}) : go(F{}, std::integral_constant<int, 32>{});
+  else ra.x_f32 ? go(Tr{}, std::integral_constant<int, 64>{}) : go(F{}, std::integral_constant<int, 64>{});
+  return hipGetLastError();
 }
 
 template <int LPT, int NPL, bool GROUPED = false>

@@ -16,16 +16,18 @@ __device__ __forceinline__ void store_logit(float* p, float v) {
   else *p = v;
 }
 
+// The same by a group of 256 threads inside a larger workgroup: tid is the
+// thread's index in its group, red the group's LDS partials, and a group
+// with t < 0 only takes part in the workgroup barrier.
 template <bool XF32, int EB, bool WT = false>
-__device__ __forceinline__ void router_small_item(const RouterArgs& a, int t, int ey) {
-  __shared__ float red[4][EB];
-  const int eb = ey * EB;                      // first expert of this workgroup
+__device__ __forceinline__ void router_small_group(const RouterArgs& a, int t, int ey, int tid, float (*red)[EB]) {
+  const int eb = ey * EB;                      // first expert of this item
   const int ne = min(EB, a.E - eb);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   float part[EB];
 #pragma unroll
   for (int e = 0; e < EB; ++e) part[e] = 0.f;
-  for (int h0 = tid * 8; h0 < a.H; h0 += 256 * 8) {
+  for (int h0 = tid * 8; t >= 0 && h0 < a.H; h0 += 256 * 8) {
     float xv[8];
     if (XF32) {
       const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + (int64_t)t * a.H + h0);
@@ -61,10 +63,16 @@ __device__ __forceinline__ void router_small_item(const RouterArgs& a, int t, in
     if (lane == 0) red[wave][e] = v;
   }
   __syncthreads();
-  if (tid < ne) {
+  if (t >= 0 && tid < ne) {
     const float v = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
     store_logit<WT>(a.logits + (int64_t)t * a.E + eb + tid, v + (a.bias ? a.bias[eb + tid] : 0.f));
   }
+}
+
+template <bool XF32, int EB, bool WT = false>
+__device__ __forceinline__ void router_small_item(const RouterArgs& a, int t, int ey) {
+  __shared__ float red[4][EB];
+  router_small_group<XF32, EB, WT>(a, t, ey, threadIdx.x, red);
 }
 
 constexpr int kRouterWaves = 16;   // H slices of the MFMA router (one per wave)

@@ -263,3 +263,19 @@ def test_route_noalloc_rejects_a_workspace_beyond_its_array():
                                None) == B.MOE_ERR_WORKSPACE
     assert L.moe_route_noalloc(ctypes.byref(_d(K=0).c()), fake, 4, None, None, ctypes.byref(rt2),
                                None) == B.MOE_ERR_ARG
+
+
+def test_router_route_rejects_bad_arguments():
+    """moe_router_route checks the router's and the routing's arguments on the
+    host, before any device call."""
+    L = B.lib()
+    fake = ctypes.c_void_p(16)
+    rt2 = B.moe_route_t(*([fake] * len(B.moe_route_t._fields_)))
+    d = _d(T_max=4)
+    ws_ok = B.route_workspace_bytes(d)
+    args = lambda T, x, ws_bytes: (ctypes.byref(d.c()), x, fake, None, T, fake, None, None, ctypes.byref(rt2),
+                                   fake, ws_bytes, None)
+    assert L.moe_router_route(*args(5, fake, ws_ok)) == B.MOE_ERR_ARG        # T > T_max
+    assert L.moe_router_route(*args(-1, fake, ws_ok)) == B.MOE_ERR_ARG
+    assert L.moe_router_route(*args(2, None, ws_ok)) == B.MOE_ERR_ARG        # no x
+    assert L.moe_router_route(*args(2, fake, ws_ok - 1)) == B.MOE_ERR_WORKSPACE

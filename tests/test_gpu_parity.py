@@ -133,6 +133,46 @@ def test_router_logits(cfg):
     assert (np.abs(got - ref) <= bound).all(), float((np.abs(got - ref) / bound).max())
 
 
+# few tokens and experts: moe_router_route runs the router and the routing
+# in one launch while T * E <= 16 (the last case takes the two launches)
+ROUTER_ROUTE = [
+    configs.tiny().with_(name="rr_e8_t1_masked", T=1, H=4096, I=128, E=8, E_phys=8, K=2, act_dtype="bf16",
+                         M_max=1, bias="normal0.5"),
+    configs.tiny().with_(name="rr_e8_t2_f32_contig", T=2, H=1024, I=128, E=8, E_phys=8, K=2, act_dtype="f32",
+                         layout="contig", BM=16),
+    configs.tiny().with_(name="rr_e16_t1_replicas", T=1, H=512, I=128, E=16, E_phys=20, K=4, act_dtype="bf16",
+                         layout="contig", BM=16, bias="zipf1.1"),
+    configs.tiny().with_(name="rr_e8_t16_two_launches", T=16, H=512, I=128, E=8, E_phys=8, K=2,
+                         act_dtype="bf16", M_max=16, bias="normal0.5"),
+]
+RR_KEYS = ("ids", "w", "phys", "row_of", "slot_of", "src_of", "counts", "offsets", "masked_m", "spill_off",
+           "pad_off", "tile_off", "status")
+
+
+@pytest.mark.parametrize("cfg", ROUTER_ROUTE, ids=lambda c: c.name)
+def test_router_route_matches_two_calls(cfg):
+    """moe_router_route equals moe_router_logits + moe_route bit for bit:
+    the logits and every routing table, at T and at T = 0; its claim
+    counters end zero."""
+    b = Built(cfg)
+    d, L = b.d, b.layer
+    for T in (b.T, 0):
+        B.moe_router_logits(d, b.x, b.wr, b.bias, T, L.logits)
+        B.moe_route(d, L.logits, T, L.rt, L.ws, b.l2p, b.rcount)
+        rt2 = B.RouteTables(d, DEV)
+        rt2.claim.fill_(7)
+        lg2 = torch.full_like(L.logits, float("nan"))
+        ws2 = torch.empty_like(L.ws)
+        B.moe_router_route(d, b.x, b.wr, b.bias, T, lg2, rt2, ws2, b.l2p, b.rcount)
+        torch.cuda.synchronize()
+        assert torch.equal(L.logits[:T], lg2[:T]), (cfg.name, T)
+        ref, got = route_np(L.rt, T, cfg.K), route_np(rt2, T, cfg.K)
+        for k in RR_KEYS:
+            assert np.array_equal(np.asarray(ref[k]), np.asarray(got[k])), (cfg.name, T, k)
+        assert not rt2.claim.any()
+        say(f"  {cfg.name} T={T}: logits and tables bit-identical, status {got['status']}")
+
+
 # many tokens and more than 64 experts: the 64-expert x 64-token block
 # router (ragged token and expert counts: partial blocks on both axes)
 ROUTER_BLOCK = [
