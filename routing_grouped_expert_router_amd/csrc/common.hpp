@@ -116,15 +116,41 @@ __device__ __forceinline__ uint64_t topk_key(float v, int id) {
   return (uint64_t(order_key(v)) << 32) | uint64_t(0xffffffffu - uint32_t(id));
 }
 
+// One step of a max-scan across lanes by a DPP move (row shift or row
+// broadcast; lanes the move does not reach read 0, which every key exceeds)
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, ROW_MASK, 0xf, true);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, ROW_MASK, 0xf, true);
+  const uint64_t o = (uint64_t(hi) << 32) | lo;
+  return o > v ? o : v;
+}
+
+// The largest 64-bit value over the 64 lanes, returned to every lane: row
+// shifts by 1, 2, 4 and 8 leave each 16-lane row's maximum in its lane 15,
+// the row broadcasts of lanes 15 and 31 carry them on to lane 63, which is
+// read back.  No lane exchange goes through LDS (as __shfl_xor does), so a
+// step costs a few ALU cycles instead of an LDS round trip.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor((unsigned)(v & 0xffffffffu), off, kWave);
-    uint32_t hi = __shfl_xor((unsigned)(v >> 32), off, kWave);
-    uint64_t o = (uint64_t(hi) << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+  v = dpp_max_step<0x111, 0xf>(v);   // row_shr:1
+  v = dpp_max_step<0x112, 0xf>(v);   // row_shr:2
+  v = dpp_max_step<0x114, 0xf>(v);   // row_shr:4
+  v = dpp_max_step<0x118, 0xf>(v);   // row_shr:8
+  v = dpp_max_step<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_max_step<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
+  return (uint64_t(hi) << 32) | lo;
+}
+
+// A workgroup barrier that orders LDS accesses only: it waits for the
+// wave's LDS operations, not for its outstanding global stores, which
+// __syncthreads() also waits for (an L2 round trip).  For phases that hand
+// each other data in LDS alone.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Exclusive scan of n (<= 4 * blockDim.x) ints in LDS `a`, in place, by the
@@ -144,17 +170,17 @@ __device__ inline int block_exclusive_scan(int* a, int n, int* tmp) {
     if (lane >= off) x += y;
   }
   if (lane == 63) tmp[wv] = x;
-  __syncthreads();
+  lds_barrier();
   if (tid == 0) {
     int run = 0;
     for (int w = 0; w < nt / 64; ++w) { int c = tmp[w]; tmp[w] = run; run += c; }
     tmp[nt / 64] = run;
   }
-  __syncthreads();
+  lds_barrier();
   int base = tmp[wv] + x - s;
   for (int i = lo; i < hi; ++i) { int c = a[i]; a[i] = base; base += c; }
   int total = tmp[nt / 64];
-  __syncthreads();
+  lds_barrier();
   return total;
 }
 

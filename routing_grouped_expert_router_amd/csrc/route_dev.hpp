@@ -51,11 +51,15 @@ __device__ __forceinline__ void select_tokens(const RouteArgs& a, int t0, int co
     uint64_t my_key = 0ull;
     for (int k = 0; k < K; ++k) {
       uint64_t best = keys[0];
+      if constexpr (LPT == kWave) {
+        best = wave_max_u64(best);
+      } else {
 #pragma unroll
-      for (int off = LPT >> 1; off >= 1; off >>= 1) {
-        const uint32_t lo = __shfl_xor((unsigned)(best & 0xffffffffu), off, kWave);
-        const uint32_t hi = __shfl_xor((unsigned)(best >> 32), off, kWave);
-        best = max_u64(best, (uint64_t(hi) << 32) | lo);
+        for (int off = LPT >> 1; off >= 1; off >>= 1) {
+          const uint32_t lo = __shfl_xor((unsigned)(best & 0xffffffffu), off, kWave);
+          const uint32_t hi = __shfl_xor((unsigned)(best >> 32), off, kWave);
+          best = max_u64(best, (uint64_t(hi) << 32) | lo);
+        }
       }
       if (sl == k) my_key = best;
       // the lane holding the winner pops it (best == 0: nothing left, a no-op)
@@ -215,14 +219,14 @@ __device__ __forceinline__ void rank_block(const RouteArgs& a, int b) {
   const int nt = min(kBlockTokens, a.T - t0);
   for (int e = tid; e < E; e += nth) mask[e] = 0ull;
   if (tid == 0) flag_s = 0;
-  __syncthreads();
+  lds_barrier();
   for (int i = tid; i < nt * K; i += nth) {
     const int id = a.topk_ids[(int64_t)t0 * K + i];
     atomicOr(&mask[id], 1ull << (i / K));
   }
   for (int tl = tid; tl < nt; tl += nth)
     if (a.ws.tok_flag[t0 + tl]) atomicOr(&flag_s, 1);
-  __syncthreads();
+  lds_barrier();
   for (int i = tid; i < nt * K; i += nth) {
     const int tl = i / K;
     const int id = a.topk_ids[(int64_t)t0 * K + i];
@@ -238,7 +242,9 @@ constexpr int kScanThreads = 1024;
 static_assert(kScanThreads == kFusedThreads, "the fused route kernel runs every phase in one workgroup");
 
 // Any workgroup size (the loops stride by blockDim.x); the routing kernels run
-// it with kScanThreads.
+// it with kScanThreads.  Its phases hand each other data in LDS only (their
+// barriers order LDS alone); its global outputs are read after the caller's
+// next full barrier or by the next kernel.
 __device__ __forceinline__ void scan_all(const RouteArgs& a) {
   __shared__ int cnt[kMaxE + 1];
   __shared__ int aux[kMaxE + 1];
@@ -254,7 +260,7 @@ __device__ __forceinline__ void scan_all(const RouteArgs& a) {
   const int nblk = (a.T + kBlockTokens - 1) / kBlockTokens;
   if (tid == 0) { bad_s = 0; nonfinite_s = 0; bad_ep_s = 0; }
   for (int p = tid; p <= NC; p += nth) { cnt[p] = 0; aux[p] = 0; }
-  __syncthreads();
+  lds_barrier();
   // per logical expert: exclusive prefix over blocks, and total T_l (16
   // blocks' counts loaded before any is overwritten, so the loads overlap)
   for (int l = tid; l < E; l += nth) {
@@ -287,11 +293,11 @@ __device__ __forceinline__ void scan_all(const RouteArgs& a) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (has_map)
     for (int p = tid; p < NG; p += nth)
       if (aux[p] > 1) atomicOr(&bad_s, 1);
-  __syncthreads();
+  lds_barrier();
   const bool valid = has_map && bad_s == 0;
   // physical counts: replica r of l gets the j = r, r+R, ... tokens
   for (int l = tid; l < E; l += nth) {
@@ -304,34 +310,34 @@ __device__ __forceinline__ void scan_all(const RouteArgs& a) {
       cnt[l] = Tl;
     }
   }
-  __syncthreads();
+  lds_barrier();
   bool ep_ok = true;
   if (ep) {
     // local map: entries in [-1, P), each local slot named at most once; the
     // local counts take the counts of their global slots (remote: dropped
     // here, counted by their own rank)
     for (int q = tid; q < NC; q += nth) aux[q] = 0;
-    __syncthreads();
+    lds_barrier();
     for (int p = tid; p < NG; p += nth) {
       const int q = a.local_of[p];
       if (q < -1 || q >= P) atomicOr(&bad_ep_s, 1);
       else if (q >= 0) atomicAdd(&aux[q], 1);
     }
-    __syncthreads();
+    lds_barrier();
     for (int q = tid; q < P; q += nth)
       if (aux[q] > 1) atomicOr(&bad_ep_s, 1);
-    __syncthreads();
+    lds_barrier();
     ep_ok = bad_ep_s == 0;
     for (int q = tid; q < P; q += nth) aux[q] = 0;
-    __syncthreads();
+    lds_barrier();
     if (ep_ok)
       for (int p = tid; p < NG; p += nth) {
         const int q = a.local_of[p];
         if (q >= 0) aux[q] = cnt[p];
       }
-    __syncthreads();
+    lds_barrier();
     for (int q = tid; q < P; q += nth) cnt[q] = aux[q];
-    __syncthreads();
+    lds_barrier();
   }
   const bool masked = a.layout == MOE_MASKED;
   for (int p = tid; p < P; p += nth) {
@@ -345,7 +351,7 @@ __device__ __forceinline__ void scan_all(const RouteArgs& a) {
       aux[p] = (c + a.BM - 1) / a.BM * a.BM;
     }
   }
-  __syncthreads();
+  lds_barrier();
   const int total = block_exclusive_scan(cnt, P, tmp);
   const int total2 = block_exclusive_scan(aux, P, tmp);
   for (int p = tid; p < P; p += nth) {
@@ -353,14 +359,14 @@ __device__ __forceinline__ void scan_all(const RouteArgs& a) {
     if (masked) a.spill_off[p] = aux[p];
     else a.pad_off[p] = aux[p];
   }
-  __syncthreads();
+  lds_barrier();
   // tiles of kTileRows rows per slot for the tiled expert kernel (aux reused;
   // cnt holds the exclusive offsets, so slot p has cnt[p+1] - cnt[p] rows)
   for (int p = tid; p < P; p += nth) {
     const int rows = (p + 1 < P ? cnt[p + 1] : total) - cnt[p];
     aux[p] = (rows + kTileRows - 1) / kTileRows;
   }
-  __syncthreads();
+  lds_barrier();
   const int ttotal = block_exclusive_scan(aux, P, tmp);
   for (int p = tid; p < P; p += nth) a.tile_off[p] = aux[p];
   if (a.claim)
