@@ -69,10 +69,32 @@ void ffn_stream_kernel(StreamArgs a) {
     }
     y -= a.b_rows;
   }
-  if constexpr (XLK)
-    stream_group<FP8, MODE, 1, PACKED, banks_xl<FP8>(), true, true>(a, y, ks, 0, 1, 0, a.max_rows, xs_raw, blockIdx.x);
-  else
-    stream_group<FP8, MODE, MTA, PACKED, banks_a<FP8, MODE>(), true>(a, y, ks, 0, 1, 0, a.max_rows, xs_raw, blockIdx.x);
+  auto group = [&](int g) -> void {
+    if constexpr (XLK)
+      stream_group<FP8, MODE, 1, PACKED, banks_xl<FP8>(), true, true>(a, g, ks, 0, 1, 0, a.max_rows, xs_raw, blockIdx.x);
+    else
+      stream_group<FP8, MODE, MTA, PACKED, banks_a<FP8, MODE>(), true>(a, g, ks, 0, 1, 0, a.max_rows, xs_raw, blockIdx.x);
+  };
+  const int rows = a.compact_rows;
+  if (rows == 0) {
+    group(y);
+    return;
+  }
+  if (y >= rows) {                       // the shared expert
+    group(a.E_phys + (y - rows));
+    return;
+  }
+  // the y-th, (y + rows)-th, ... slots with tokens: one forward scan of the
+  // counts (few tokens, so far fewer launched rows than slots)
+  int p = 0, k = -1;
+  for (int j = y;; j += rows) {
+    for (; p < a.E_phys; ++p)
+      if (a.counts[p] > 0 && ++k == j) break;
+    if (p >= a.E_phys) return;
+    if (j != y) __syncthreads();         // the previous group is done with the LDS
+    group(p);
+    ++p;
+  }
 }
 
 template <bool FP8, int MODE, bool PACKED>

@@ -98,6 +98,11 @@ struct StreamArgs {
   // Region A, the rest: groups with at most max_rows rows (0 = no limit).
   int max_rows;
   int b_rows, shared_chunks, b_max_rows;
+  // compact_rows > 0 (no region B): region A's first compact_rows workgroup
+  // rows take the slots with tokens, in slot order, row y the y-th, the
+  // (y + compact_rows)-th, ... (any number of them), and the next n_shared
+  // rows the shared expert; 0: row y is slot y
+  int compact_rows;
 };
 
 // row tiles per pass of region B

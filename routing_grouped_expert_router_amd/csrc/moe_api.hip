@@ -433,6 +433,16 @@ moe_status_t launch_expert_gemm(const moe_desc_t* d, const moe_route_t* r, int32
   a.b_rows = 0;
   a.shared_chunks = 1;
   a.b_max_rows = 0;
+  a.compact_rows = 0;
+  // Few tokens (T*K below the slot count): launch T*K rows for the routed
+  // slots instead of one per slot, most of which would find no tokens; each
+  // row walks the slots that have tokens (received counts may fill more
+  // slots than T*K, and the walk covers them too)
+  const int64_t TKc = (int64_t)T * d->K;
+  if (!need_b && !need_c && TKc >= 1 && TKc < d->E_phys && stream_grid.y == (unsigned)(d->E_phys + d->n_shared)) {
+    a.compact_rows = (int)TKc;
+    stream_grid.y = (unsigned)(TKc + d->n_shared);
+  }
   dim3 grid = stream_grid;
   if (need_b) {
     a.b_max_rows = need_c ? 64 : 0;

@@ -76,6 +76,10 @@ __device__ __forceinline__ void router_small_item(const RouterArgs& a, int t, in
 }
 
 constexpr int kRouterWaves = 16;   // H slices of the MFMA router (one per wave)
+// 64-wide chunks of a slice in flight (register sets of weights and MR
+// token tiles, within a 1024-thread workgroup's 128 registers per lane)
+template <int MR>
+constexpr int router_ahead() { return MR >= 4 ? 2 : 4; }
 
 // Slice `slice` (of kRouterWaves) of H for experts e0 .. e0+15 and tokens
 // t0 .. t0 + 16*MR - 1, summed from zero in 64-wide chunks by one wave with
@@ -98,8 +102,7 @@ __device__ __forceinline__ void router_mfma_slice(const RouterArgs& a, int e0, i
   const int kbeg = slice * kw;
 #pragma unroll
   for (int m = 0; m < MR; ++m) acc[m] = f32x4{0, 0, 0, 0};
-  u32x4 wc[2], xc[MR][2];
-  auto load = [&](int k0, u32x4* wv, u32x4 (*xv)[2]) {
+  auto load = [&](int k0, u32x4* wv, u32x4 (*xv)[2]) -> void {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int k = k0 + 32 * j + 8 * lg;
@@ -109,22 +112,26 @@ __device__ __forceinline__ void router_mfma_slice(const RouterArgs& a, int e0, i
       for (int m = 0; m < MR; ++m) xv[m][j] = *reinterpret_cast<const u32x4*>(xrow[m] + k);
     }
   };
-  load(kbeg, wc, xc);
-  for (int k0 = kbeg; k0 < kbeg + kw; k0 += 64) {
-    u32x4 wn[2], xn[MR][2];
-    const bool more = k0 + 64 < kbeg + kw;
-    if (more) load(k0 + 64, wn, xn);
+  // router_ahead<MR>() 64-wide chunks in flight in a ring of register sets (a
+  // slice has a few chunks: one at a time left the wave waiting a full
+  // memory latency per chunk); the MFMAs run in chunk order
+  constexpr int D = router_ahead<MR>();
+  u32x4 wv[D][2], xv[D][MR][2];
+  const int nch = kw / 64;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int d = 0; d < D; ++d)
+    if (d < nch) load(kbeg + 64 * d, wv[d], xv[d]);
+  for (int c0 = 0; c0 < nch; c0 += D) {
 #pragma unroll
-      for (int m = 0; m < MR; ++m)
-        acc[m] = mfma16x16x32(__builtin_bit_cast(bf16x8, wc[j]), __builtin_bit_cast(bf16x8, xc[m][j]), acc[m]);
-    if (more) {
+    for (int d = 0; d < D; ++d) {
+      const int c = c0 + d;
+      if (c < nch) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        wc[j] = wn[j];
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int m = 0; m < MR; ++m) xc[m][j] = xn[m][j];
+          for (int m = 0; m < MR; ++m)
+            acc[m] = mfma16x16x32(__builtin_bit_cast(bf16x8, wv[d][j]), __builtin_bit_cast(bf16x8, xv[d][m][j]), acc[m]);
+        if (c + D < nch) load(kbeg + 64 * (c + D), wv[d], xv[d]);
       }
     }
   }

@@ -225,3 +225,47 @@ def test_received_counts_above_routed_total(packed):
         worst = max(worst, rel_err(got, ref))
     say(f"  received {int(counts.sum())} rows (T*K = {T * cfg.K}): rel err {worst:.3e}")
     assert worst <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_received_counts_on_more_slots_than_routed_choices(T):
+    """Few tokens (T*K below the slot count) make the streaming launch run
+    T*K workgroup rows over the slots that hold tokens instead of one row
+    per slot; received counts can fill more slots than T*K, so each row then
+    walks several slots.  Every slot's rows (M_max each, and an empty slot)
+    must match the reference SwiGLU of those rows."""
+    cfg = _BASE.with_(name=f"recv_t{T}", T=T, H=512, I=256, E=16, E_phys=16, K=2, act_dtype="bf16", M_max=4)
+    b = Built(cfg, packed=True)
+    d, L = b.d, b.layer
+    counts = torch.tensor([4, 1, 0, 3, 2, 4, 1, 1, 4, 0, 2, 3, 4, 1, 2, 4], dtype=torch.int32, device=DEV)
+    assert (counts > 0).sum() > T * cfg.K
+    rows_n = B.buffer_rows(d)
+    g = torch.Generator(device="cpu").manual_seed(11)
+    xg = torch.randn((rows_n, d.H), generator=g).to(torch.bfloat16).to(DEV)
+    rt2 = B.RouteTables(d, DEV)
+    B.moe_route_received(d, counts, T, rt2)
+    h = torch.zeros_like(L.h)
+    y = torch.zeros_like(L.y)
+    B.moe_expert_gate_up(d, L.weights, rt2, T, xg, h)
+    B.moe_expert_down(d, L.weights, rt2, T, h, y)
+    torch.cuda.synchronize()
+    assert int(rt2.status.item()) == 0
+    splits = B.down_splits(d, T)
+    ysz = B.y_bytes(d, T)
+    if splits == 1:
+        yv = y[:ysz].view(torch.bfloat16).view(-1, d.H).float()
+    else:
+        yv = y[:ysz].view(torch.float32).view(splits, -1, d.H).sum(0)
+    xs = to_f64(xg.cpu())
+    worst = 0.0
+    for p in range(cfg.E_phys):
+        if int(counts[p]) == 0:
+            continue
+        ew = b.inp.expert(b.inp.slot_logical(p))
+        W1, W3, W2 = to_f64(ew.w1), to_f64(ew.w3), to_f64(ew.w2)
+        rows = np.arange(p * cfg.M_max, p * cfg.M_max + int(counts[p]))
+        ref = O.swiglu_expert(xs[rows], W1, W3, W2)
+        got = yv[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64)
+        worst = max(worst, rel_err(got, ref))
+    say(f"  T={T}: {int((counts > 0).sum())} slots with rows (T*K = {T * cfg.K}): rel err {worst:.3e}")
+    assert worst <= TOL["bf16"]
