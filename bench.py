@@ -69,6 +69,10 @@ def parse():
                     help="no timing: turn the counter_collection.csv files of a FETCH_SIZE and a "
                          "WRITE_SIZE rocprofv3 pass over `bench.py --workload W --copy-calibration` "
                          "into profiles/gate_up_traffic_W.md (needs --workload)")
+    ap.add_argument("--summarize-stats", nargs=2, metavar=("STATS_CSV", "LOG"),
+                    help="no timing: turn a rocprofv3 --kernel-trace --stats run_kernel_stats.csv of "
+                         "`bench.py --workload W` (and that run's stderr log, for its bench line) into "
+                         "profiles/W_kernel_stats.md (needs --workload)")
     ap.add_argument("--debug-flags", type=int, default=0,
                     help="moe_desc_t.debug_flags for an ablation (MOE_DEBUG_* in include/moe.h: e.g. "
                          "a forced large-group kernel); outputs stay bit-identical")
@@ -474,6 +478,48 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, cmd_prefix:
     print(f"wrote {path}: {rd['bytes'] + wr['bytes']} bytes per launch")
 
 
+def summarize_stats(workload: str, stats_csv: str, log: str, steps: int, warmup: int):
+    """profiles/<workload>_kernel_stats.md from the per-kernel statistics of a
+    kernel-trace run of the bench on that workload (the library's kernels)."""
+    import csv
+    from workloads import configs
+    cfg = configs.by_name(workload)
+    with open(stats_csv) as fh:
+        rows = [r for r in csv.DictReader(fh) if "moe::" in r["Name"] and "pack_kernel" not in r["Name"]]
+    total = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
+    bench_lines = []
+    with open(log) as fh:
+        bench_lines = [ln.rstrip() for ln in fh if ln.startswith(f"# {workload}:")]
+    name = lambda n: n.replace("void ", "").replace("moe::", "").split("(")[0]
+    lines = [
+        f"# rocprofv3 kernel statistics: workload {workload}",
+        "",
+        f"T={cfg.T}, H={cfg.H}, I={cfg.I}, E={cfg.E}, E_phys={cfg.E_phys}, K={cfg.K}, n_shared={cfg.n_shared}, "
+        f"weights {cfg.w_dtype}, layout {cfg.layout}.  Command (repository root on the GPU box, `R=$PWD`):",
+        "",
+        f"    cd /tmp && TMPDIR=/tmp timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv "
+        f"-d $R/gpurun_out/prof/{workload} -o run -- python3 $R/bench.py --workload {workload} --no-cpu --no-peaks "
+        f"--steps {steps} --warmup {warmup} 2> $R/gpurun_out/prof/{workload}.log",
+        f"    python3 bench.py --workload {workload} --summarize-stats "
+        f"gpurun_out/prof/{workload}/run_kernel_stats.csv gpurun_out/prof/{workload}.log",
+        "",
+        "The library's kernels (the one-time weight packing left out); durations in microseconds, over the "
+        "eager and graph-replayed steps of the run.",
+        "",
+        "| kernel | calls | avg us | min us | max us | share of these kernels |",
+        "|---|---|---|---|---|---|",
+    ]
+    for r in rows:
+        lines.append(f"| `{name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{100 * float(r['TotalDurationNs']) / total:.1f}% |")
+    lines += ["", "Bench line printed by the same run:", ""] + [f"    {ln}" for ln in bench_lines] + [""]
+    path = os.path.join(ROOT, "profiles", f"{workload}_kernel_stats.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines))
+    print(f"wrote {path}")
+
+
 def roofline(cfg, r, peaks):
     """The dominant kernel (expert gate/up + SwiGLU) against its bound: HBM
     bytes for decode, bf16 MFMA FLOPs for prefill."""
@@ -607,6 +653,11 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the MoE layer here runs on a single MI355X)", file=sys.stderr)
         sys.exit(2)
+    if args.summarize_stats:
+        if not args.workload:
+            raise SystemExit("--summarize-stats needs --workload")
+        summarize_stats(args.workload, *args.summarize_stats, args.steps, args.warmup)
+        return
     if args.summarize_traffic:
         if not args.workload:
             raise SystemExit("--summarize-traffic needs --workload")

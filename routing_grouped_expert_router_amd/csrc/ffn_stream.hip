@@ -69,40 +69,50 @@ void ffn_stream_kernel(StreamArgs a) {
     }
     y -= a.b_rows;
   }
-  auto group = [&](int g) -> void {
+  if constexpr (XLK || FP8) {
+    // fp8 launches are never compacted (stream_compacts): the loop below
+    // costs their variants the registers of a wave per SIMD
     if constexpr (XLK)
-      stream_group<FP8, MODE, 1, PACKED, banks_xl<FP8>(), true, true>(a, g, ks, 0, 1, 0, a.max_rows, xs_raw, blockIdx.x);
+      stream_group<FP8, MODE, 1, PACKED, banks_xl<FP8>(), true, true>(a, y, ks, 0, 1, 0, a.max_rows, xs_raw, blockIdx.x);
     else
-      stream_group<FP8, MODE, MTA, PACKED, banks_a<FP8, MODE>(), true>(a, g, ks, 0, 1, 0, a.max_rows, xs_raw, blockIdx.x);
-  };
+      stream_group<FP8, MODE, MTA, PACKED, banks_a<FP8, MODE>(), true>(a, y, ks, 0, 1, 0, a.max_rows, xs_raw, blockIdx.x);
+    return;
+  }
+  // compact rows (a.compact_rows > 0): row y takes the y-th, (y + rows)-th,
+  // ... slots with tokens, found by one forward scan of the counts (few
+  // tokens, so far fewer launched rows than slots); the rows after them are
+  // the shared expert.  One call site of the group body (three inlined
+  // copies raised the register count and halved the occupancy).
   const int rows = a.compact_rows;
-  if (rows == 0) {
-    group(y);
-    return;
-  }
-  if (y >= rows) {                       // the shared expert
-    group(a.E_phys + (y - rows));
-    return;
-  }
-  // the y-th, (y + rows)-th, ... slots with tokens: one forward scan of the
-  // counts (few tokens, so far fewer launched rows than slots)
-  int p = 0, k = -1;
-  for (int j = y;; j += rows) {
+  int p = 0, k = -1, j = y;
+  auto next_slot = [&]() -> int {
     for (; p < a.E_phys; ++p)
-      if (a.counts[p] > 0 && ++k == j) break;
-    if (p >= a.E_phys) return;
-    if (j != y) __syncthreads();         // the previous group is done with the LDS
-    group(p);
+      if (a.counts[p] > 0 && ++k == j) return p;
+    return -1;
+  };
+  int g = rows == 0 ? y : (y >= rows ? a.E_phys + (y - rows) : next_slot());
+  while (g >= 0) {
+    stream_group<FP8, MODE, MTA, PACKED, banks_a<FP8, MODE>(), true>(a, g, ks, 0, 1, 0, a.max_rows, xs_raw, blockIdx.x);
+    if (rows == 0 || y >= rows) return;
     ++p;
+    j += rows;
+    g = next_slot();
+    if (g >= 0) __syncthreads();         // the previous group is done with the LDS
   }
+}
+
+// fp8 down projections with one row tile per pass and a K range of at most
+// kXlSteps steps keep their activations in LDS (measured: pays for fp8 with
+// K = 2048, costs time for bf16)
+bool stream_uses_xl(int fp8, int mode, int mt, const StreamArgs& a) {
+  return fp8 && mode == MODE_DOWN && mt == 1 && a.Kdim / kKS / a.ksplit <= kXlSteps;
 }
 
 template <bool FP8, int MODE, bool PACKED>
 static hipError_t launch_mt(const StreamArgs& a, int mt, dim3 grid, hipStream_t s) {
   if constexpr (MODE == MODE_DOWN && FP8) {
-    // measured: pays for fp8 down projections (K = 2048), costs time for bf16
     const int steps = a.Kdim / kKS / a.ksplit;
-    if (mt == 1 && steps <= kXlSteps) {
+    if (stream_uses_xl(FP8, MODE, mt, a)) {
       // bytes: the K range's activation pieces, and region B's LDS tiles
       constexpr int TB = tiles_b<FP8>();
       const size_t lds = std::max<size_t>((size_t)steps * 256 * 16, sizeof(uint16_t) * lds_elems<TB>());
@@ -125,9 +135,12 @@ static hipError_t launch_mode(const StreamArgs& a, int fp8, int packed, int mt, 
   return packed ? launch_mt<false, MODE, true>(a, mt, grid, s) : launch_mt<false, MODE, false>(a, mt, grid, s);
 }
 
+bool stream_compacts(int fp8) { return !fp8; }
+
 hipError_t launch_ffn_stream(const StreamArgs& a, int fp8, int packed, int mode, int mt, dim3 grid,
                              hipStream_t s) {
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return hipSuccess;
+  if (a.compact_rows != 0 && !stream_compacts(fp8)) return hipErrorInvalidValue;
   if (a.nblk < 1 || a.nblk > 8 || (int64_t)grid.x * 64 * a.nblk != a.N) return hipErrorInvalidValue;
   if (mt == 4 && a.b_rows != 0) return hipErrorInvalidValue;
   if (a.b_rows != 0 && a.b_rows < a.E_phys) return hipErrorInvalidValue;

@@ -107,6 +107,10 @@ struct StreamArgs {
 
 // row tiles per pass of region B
 inline int stream_tiles_b(int fp8) { return fp8 ? 2 : 4; }
+// whether a launch with these arguments keeps its activations in LDS, and
+// whether launches of this weight type take compact rows (StreamArgs)
+bool stream_uses_xl(int fp8, int mode, int mt, const StreamArgs& a);
+bool stream_compacts(int fp8);
 // mt: row tiles per pass of region A (1, 2 or 4); grid.x = N / (64 * nblk)
 hipError_t launch_ffn_stream(const StreamArgs& a, int fp8, int packed, int mode, int mt, dim3 grid,
                              hipStream_t s);

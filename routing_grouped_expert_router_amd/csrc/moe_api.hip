@@ -439,7 +439,8 @@ moe_status_t launch_expert_gemm(const moe_desc_t* d, const moe_route_t* r, int32
   // row walks the slots that have tokens (received counts may fill more
   // slots than T*K, and the walk covers them too)
   const int64_t TKc = (int64_t)T * d->K;
-  if (!need_b && !need_c && TKc >= 1 && TKc < d->E_phys && stream_grid.y == (unsigned)(d->E_phys + d->n_shared)) {
+  if (!need_b && !need_c && TKc >= 1 && TKc < d->E_phys && stream_compacts(fp8) &&
+      stream_grid.y == (unsigned)(d->E_phys + d->n_shared)) {
     a.compact_rows = (int)TKc;
     stream_grid.y = (unsigned)(TKc + d->n_shared);
   }
