@@ -453,12 +453,13 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, cmd_prefix:
         "three times first as the calibration kernel of known traffic (repository root on the GPU "
         "box, `R=$PWD`):",
         "",
-        f"    {cmd_prefix} --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/FETCH_SIZE -o run -- "
+        f"    {cmd_prefix} --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/{workload}_FETCH_SIZE -o run -- "
         f"python3 $R/bench.py --workload {workload} --no-cpu --no-peaks --steps 3 --warmup 1 --copy-calibration",
-        f"    {cmd_prefix} --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/WRITE_SIZE -o run -- "
+        f"    {cmd_prefix} --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/{workload}_WRITE_SIZE -o run -- "
         f"python3 $R/bench.py --workload {workload} --no-cpu --no-peaks --steps 3 --warmup 1 --copy-calibration",
         f"    python3 bench.py --workload {workload} --summarize-traffic "
-        "gpurun_out/prof/FETCH_SIZE/run_counter_collection.csv gpurun_out/prof/WRITE_SIZE/run_counter_collection.csv",
+        f"gpurun_out/prof/{workload}_FETCH_SIZE/run_counter_collection.csv "
+        f"gpurun_out/prof/{workload}_WRITE_SIZE/run_counter_collection.csv",
         "",
         f"* calibration copy (512 MiB each way): FETCH_SIZE {rd['cal']:.0f} KiB -> factor {rd['factor']:.4f}; "
         f"WRITE_SIZE {wr['cal']:.0f} KiB -> factor {wr['factor']:.4f}",
