@@ -51,21 +51,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_assign_kernel(RouteArgs a
 }
 
 // T <= 64: the four phases in one workgroup (one launch instead of four).
-// The barrier between phases orders the global-memory tables each phase
-// writes before the next one reads them.
+// The selected ids and the non-finite flag stay in LDS for the other phases
+// (route_block_tables), so no phase waits on global memory written by
+// another.
 template <int LPT, int NPL, bool GROUPED>
 __device__ __forceinline__ void route_one_workgroup(const RouteArgs& a) {
+  __shared__ int ids[kBlockTokens * kMaxK];
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  lds_barrier();
   if (a.T > 0) {
-    if constexpr (GROUPED) select_tokens_grouped<NPL>(a, 0, a.T, threadIdx.x / kWave, kFusedThreads / kWave);
-    else select_tokens<LPT, NPL>(a, 0, a.T, threadIdx.x / kWave, kFusedThreads / kWave);
-    __syncthreads();
-    rank_block(a, 0);
+    if constexpr (GROUPED) select_tokens_grouped<NPL>(a, 0, a.T, threadIdx.x / kWave, kFusedThreads / kWave, ids, &bad);
+    else select_tokens<LPT, NPL>(a, 0, a.T, threadIdx.x / kWave, kFusedThreads / kWave, ids, &bad);
   }
-  __syncthreads();
-  scan_all(a);
-  __syncthreads();
-  const int64_t TK = (int64_t)a.T * a.K;
-  for (int64_t i = threadIdx.x; i < TK; i += kFusedThreads) assign_one(a, i);
+  lds_barrier();
+  route_block_tables(a, ids, bad != 0);
 }
 
 template <int LPT, int NPL, bool GROUPED>

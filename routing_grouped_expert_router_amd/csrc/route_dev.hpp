@@ -15,8 +15,12 @@ __device__ __forceinline__ uint64_t max_u64(uint64_t x, uint64_t y) { return x >
 
 // Top-K of tokens t0 .. t0+count-1 (clamped to T), by `nwaves` waves of which
 // this is `wave`.  Writes topk_ids, topk_w and the per-token non-finite flag.
+// lds_ids / lds_flag (single-workgroup routing): the ids also go to LDS at
+// (t - t0) * K + k, and a token with a non-finite logit ORs 1 into *lds_flag
+// instead of writing its global flag.
 template <int LPT, int NPL>
-__device__ __forceinline__ void select_tokens(const RouteArgs& a, int t0, int count, int wave, int nwaves) {
+__device__ __forceinline__ void select_tokens(const RouteArgs& a, int t0, int count, int wave, int nwaves,
+                                              int* lds_ids = nullptr, int* lds_flag = nullptr) {
   constexpr int TPW = kWave / LPT;   // tokens per wave and pass
   const int E = a.E, K = a.K;
   const int lane = threadIdx.x & (kWave - 1);
@@ -82,9 +86,13 @@ __device__ __forceinline__ void select_tokens(const RouteArgs& a, int t0, int co
       const int id = (my_id >= 0 && my_id < E) ? my_id : 0;
       a.topk_ids[(int64_t)t * K + sl] = id;
       a.topk_w[(int64_t)t * K + sl] = ek / sum;
+      if (lds_ids) lds_ids[(t - t0) * K + sl] = id;
     }
-    if (valid && sl == 0)
-      a.ws.tok_flag[t] = ((badm >> sbase) & (LPT == 64 ? ~0ull : ((1ull << LPT) - 1ull))) ? 1 : 0;
+    if (valid && sl == 0) {
+      const int fl = ((badm >> sbase) & (LPT == 64 ? ~0ull : ((1ull << LPT) - 1ull))) ? 1 : 0;
+      if (!lds_flag) a.ws.tok_flag[t] = fl;
+      else if (fl) atomicOr(lds_flag, 1);
+    }
   }
 }
 
@@ -104,7 +112,8 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
 //   K largest keys among their experts (ties to the lower id)
 //   weight = s of the choice (/ sum of the K chosen s) * scale
 template <int NPL>
-__device__ __forceinline__ void select_tokens_grouped(const RouteArgs& a, int t0, int count, int wave, int nwaves) {
+__device__ __forceinline__ void select_tokens_grouped(const RouteArgs& a, int t0, int count, int wave, int nwaves,
+                                                      int* lds_ids = nullptr, int* lds_flag = nullptr) {
   const int E = a.E, K = a.K, G = a.n_group;
   const int gs = E / G;
   const int lane = threadIdx.x & (kWave - 1);
@@ -201,8 +210,12 @@ __device__ __forceinline__ void select_tokens_grouped(const RouteArgs& a, int t0
       const int id = (my_id >= 0 && my_id < E) ? my_id : 0;
       a.topk_ids[(int64_t)t * K + lane] = id;
       a.topk_w[(int64_t)t * K + lane] = (a.renormalize ? ek / sum : ek) * a.scale;
+      if (lds_ids) lds_ids[(t - t0) * K + lane] = id;
     }
-    if (valid && lane == 0) a.ws.tok_flag[t] = badm ? 1 : 0;
+    if (valid && lane == 0) {
+      if (!lds_flag) a.ws.tok_flag[t] = badm ? 1 : 0;
+      else if (badm) atomicOr(lds_flag, 1);
+    }
   }
 }
 
@@ -430,5 +443,179 @@ __device__ __forceinline__ void assign_one(const RouteArgs& a, int64_t i) {
   if (!ok) atomicOr(a.status, MOE_STATUS_INTERNAL);
 }
 
+
+// ---- one workgroup, T <= 64 (one token block) ------------------------------
+//
+// rank, scan and assign of one 64-token block, handing each other their
+// tables in LDS: the phases' barriers order LDS only, so no phase waits for
+// another's global stores, and nothing is read back from global memory
+// except the maps.  The tables are the ones rank_block + scan_all + assign_one
+// compute for a single block (a block's exclusive prefix is then 0, so a
+// choice's rank among its logical expert's tokens is its rank in the block),
+// and the status word is written once, at the end, by thread 0.
+//   ids: LDS [T * K] selected logical ids (select_tokens' lds_ids);
+//   tok_bad: any selected token had a non-finite logit.
+// Any workgroup size that is a multiple of 64 and at most kScanThreads.
+__device__ __forceinline__ void route_block_tables(const RouteArgs& a, const int* ids, bool tok_bad) {
+  __shared__ unsigned long long mask[1024];      // E <= 1024 on the routing paths
+  __shared__ int cnt[kMaxE + 1];
+  __shared__ int aux[kMaxE + 1];
+  __shared__ int pad[kMaxE + 1];                 // spill (masked) or padded (contiguous) offsets
+  __shared__ int rk[kBlockTokens * kMaxK];
+  __shared__ int tmp[kScanThreads / 64 + 1];
+  __shared__ int bad_s, bad_ep_s, st_s;
+  const int tid = threadIdx.x, nth = blockDim.x;
+  const int E = a.E, P = a.E_phys, K = a.K;
+  const int TK = a.T * K;
+  const bool ep = a.local_of != nullptr;
+  const int NG = ep ? a.n_global : P;
+  const int NC = NG > P ? NG : P;
+  for (int e = tid; e < E; e += nth) mask[e] = 0ull;
+  for (int p = tid; p <= NC; p += nth) { cnt[p] = 0; aux[p] = 0; }
+  if (tid == 0) { bad_s = 0; bad_ep_s = 0; st_s = 0; }
+  lds_barrier();
+  // rank: one bit per token in its chosen experts' masks
+  for (int i = tid; i < TK; i += nth) atomicOr(&mask[ids[i]], 1ull << (i / K));
+  // replica map validation: counts in [1, max_replicas], slots in range,
+  // every slot listed at most once
+  const bool has_map = a.l2p != nullptr;
+  if (has_map) {
+    for (int l = tid; l < E; l += nth) {
+      const int R = a.rcount[l];
+      if (R < 1 || R > a.max_replicas) { atomicOr(&bad_s, 1); continue; }
+      for (int r = 0; r < R; ++r) {
+        const int p = a.l2p[(int64_t)l * a.max_replicas + r];
+        if (p < 0 || p >= NG) atomicOr(&bad_s, 1);
+        else atomicAdd(&aux[p], 1);
+      }
+    }
+  }
+  lds_barrier();
+  // rank of choice i among the earlier tokens that chose the same expert
+  for (int i = tid; i < TK; i += nth) {
+    const int tl = i / K;
+    rk[i] = tl ? __popcll(mask[ids[i]] & ((1ull << tl) - 1ull)) : 0;
+  }
+  if (has_map)
+    for (int p = tid; p < NG; p += nth)
+      if (aux[p] > 1) atomicOr(&bad_s, 1);
+  lds_barrier();
+  const bool valid = has_map && bad_s == 0;
+  // physical counts: replica r of l gets the j = r, r+R, ... tokens
+  for (int l = tid; l < E; l += nth) {
+    const int Tl = __popcll(mask[l]);
+    if (valid) {
+      const int R = a.rcount[l];
+      for (int r = 0; r < R; ++r)
+        cnt[a.l2p[(int64_t)l * a.max_replicas + r]] = (Tl - r + R - 1) / R;
+    } else {
+      cnt[l] = Tl;
+    }
+  }
+  lds_barrier();
+  bool ep_ok = true;
+  if (ep) {
+    // local map: entries in [-1, P), each local slot named at most once; the
+    // local counts take the counts of their global slots
+    for (int q = tid; q < NC; q += nth) aux[q] = 0;
+    lds_barrier();
+    for (int p = tid; p < NG; p += nth) {
+      const int q = a.local_of[p];
+      if (q < -1 || q >= P) atomicOr(&bad_ep_s, 1);
+      else if (q >= 0) atomicAdd(&aux[q], 1);
+    }
+    lds_barrier();
+    for (int q = tid; q < P; q += nth)
+      if (aux[q] > 1) atomicOr(&bad_ep_s, 1);
+    lds_barrier();
+    ep_ok = bad_ep_s == 0;
+    for (int q = tid; q < P; q += nth) aux[q] = 0;
+    lds_barrier();
+    if (ep_ok)
+      for (int p = tid; p < NG; p += nth) {
+        const int q = a.local_of[p];
+        if (q >= 0) aux[q] = cnt[p];
+      }
+    lds_barrier();
+    for (int q = tid; q < P; q += nth) cnt[q] = aux[q];
+    lds_barrier();
+  }
+  const bool masked = a.layout == MOE_MASKED;
+  for (int p = tid; p < P; p += nth) {
+    const int c = cnt[p];
+    a.counts[p] = c;
+    if (masked) {
+      const int mm = c < a.M_max ? c : a.M_max;
+      a.masked_m[p] = mm;
+      pad[p] = c - mm;
+    } else {
+      pad[p] = (c + a.BM - 1) / a.BM * a.BM;
+    }
+    aux[p] = c;                      // kept: the tile counts need the rows per slot
+  }
+  lds_barrier();
+  const int total = block_exclusive_scan(cnt, P, tmp);
+  const int total2 = block_exclusive_scan(pad, P, tmp);
+  for (int p = tid; p < P; p += nth) {
+    a.offsets[p] = cnt[p];
+    if (masked) a.spill_off[p] = pad[p];
+    else a.pad_off[p] = pad[p];
+    aux[p] = (aux[p] + kTileRows - 1) / kTileRows;   // row tiles of the tiled expert kernel
+  }
+  lds_barrier();
+  const int ttotal = block_exclusive_scan(aux, P, tmp);
+  for (int p = tid; p < P; p += nth) a.tile_off[p] = aux[p];
+  if (a.claim)
+    for (int i = tid; i < MOE_CLAIM_WORDS; i += nth) a.claim[i] = 0u;
+  if (tid == 0) {
+    a.tile_off[P] = ttotal;
+    a.tile_off[P + 1] = ttotal + (a.n_shared ? (a.T + kTileRows - 1) / kTileRows : 0);
+    a.offsets[P] = total;
+    if (masked) a.spill_off[P] = total2;
+    else a.pad_off[P] = total2;
+    uint32_t st = 0;
+    if (tok_bad) st |= MOE_STATUS_NONFINITE;
+    if (masked && total2 > 0) st |= MOE_STATUS_SPILL;
+    if (has_map && !valid) st |= MOE_STATUS_BAD_REPLICA;
+    if (!ep_ok) st |= MOE_STATUS_BAD_EP_MAP;
+    atomicOr(&st_s, (int)st);
+  }
+  // assign: choice i's replica, row and buffer slot (as assign_one)
+  for (int i = tid; i < TK; i += nth) {
+    const int t = i / K;
+    const int l = ids[i];
+    const int j = rk[i];
+    int p = l, rank = j;
+    if (valid) {
+      const int R = a.rcount[l];
+      p = a.l2p[(int64_t)l * a.max_replicas + j % R];
+      rank = j / R;
+    }
+    if (ep) {
+      p = ep_ok ? a.local_of[p] : -1;
+      if (p < 0) {                    // another rank's choice: no local row
+        a.topk_phys[i] = -1;
+        a.row_of[i] = -1;
+        a.slot_of[i] = -1;
+        continue;
+      }
+    }
+    const int row = cnt[p] + rank;
+    int64_t slot;
+    if (masked)
+      slot = rank < a.M_max ? (int64_t)p * a.M_max + rank : (int64_t)P * a.M_max + pad[p] + (rank - a.M_max);
+    else
+      slot = (int64_t)pad[p] + rank;
+    a.topk_phys[i] = p;
+    a.row_of[i] = row;
+    bool ok = true;
+    if (row >= 0 && row < TK) a.src_of[row] = t; else ok = false;
+    if (slot < 0 || slot >= a.routed_cap) { slot = -1; ok = false; }
+    a.slot_of[i] = int32_t(slot);
+    if (!ok) atomicOr(&st_s, (int)MOE_STATUS_INTERNAL);
+  }
+  lds_barrier();
+  if (tid == 0) a.status[0] = (uint32_t)st_s;
+}
 
 }  // namespace moe
