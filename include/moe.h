@@ -193,6 +193,13 @@ size_t moe_route_workspace_bytes(const moe_desc_t* d);
 /* The same number under the name the boundary's description uses. */
 size_t moe_workspace_bytes(const moe_desc_t* d);
 
+/* Bytes of ws that let moe_router_route split the router of T <= 64
+ * tokens over more workgroups: moe_route_workspace_bytes(d), then the split
+ * router's per-tile arrival counts and partial tiles (zero-filled by the
+ * caller before first use; left zero by every call).  Equals
+ * moe_route_workspace_bytes(d) when the split router never applies. */
+size_t moe_router_route_workspace_bytes(const moe_desc_t* d);
+
 /* Rows of the grouped buffers xg [rows, H], h [rows, I] and y ("推理 INFRA
  * 方法论(5)", DeepGEMM section: a static [E_loc, M_max, K] buffer whose valid
  * rows per expert masked_m gives at run time; vllbc blog, vLLM forward path:
@@ -249,7 +256,14 @@ moe_status_t moe_route(const moe_desc_t* d, const float* logits, int32_t T,
  * tokens and experts (T * E <= 16, E <= 64, the router's one-logit-per-
  * workgroup summation) both run in one workgroup of one launch, which saves
  * a launch on the decode path; the logits and every table are bit-identical
- * to the two calls.  (vllbc blog, routing section and Table 3-1.) */
+ * to the two calls.  (vllbc blog, routing section and Table 3-1.)
+ * With ws_bytes >= moe_router_route_workspace_bytes(d), T <= 64 and the
+ * MFMA router (E > 64, bf16 x, H % 1024 == 0), the router spreads each
+ * 16 x 16 logit tile over several workgroups and adds their partial sums in
+ * the single-launch order, so the logits stay bit-identical; the part of ws
+ * past moe_route_workspace_bytes(d) bytes must then be zero-filled before
+ * the first call, and every call leaves it zero again.  A smaller ws (at
+ * least moe_route_workspace_bytes(d)) runs the plain router. */
 moe_status_t moe_router_route(const moe_desc_t* d, const void* x, const void* w_router,
                               const float* bias, int32_t T, float* logits,
                               const int32_t* l2p, const int32_t* replica_count,

@@ -29,6 +29,7 @@ MOE_DEBUG_TILED_TALL = 5
 EXPORTED = [
     "moe_status_string", "moe_check_desc", "moe_route_workspace_bytes", "moe_buffer_rows",
     "moe_shared_base", "moe_down_splits", "moe_y_bytes", "moe_y_bytes_max", "moe_workspace_bytes",
+    "moe_router_route_workspace_bytes",
     "moe_router_logits", "moe_route",
     "moe_route_grouped",
     "moe_permute", "moe_expert_gate_up", "moe_expert_gate_up_x", "moe_expert_down",
@@ -98,6 +99,7 @@ def lib() -> ctypes.CDLL:
             "moe_y_bytes": (sz, [D, i32]),
             "moe_y_bytes_max": (sz, [D]),
             "moe_workspace_bytes": (sz, [D]),
+            "moe_router_route_workspace_bytes": (sz, [D]),
             "moe_router_logits": (ctypes.c_int, [D, _P, _P, _P, i32, _P, _P]),
             "moe_route": (ctypes.c_int, [D, _P, i32, _P, _P, R, _P, sz, _P]),
             "moe_route_grouped": (ctypes.c_int, [D, _P, i32, GR, _P, _P, R, _P, sz, _P]),
@@ -221,6 +223,12 @@ def y_bytes_max(d: Desc) -> int:
 
 def workspace_bytes(d: Desc) -> int:
     return lib().moe_workspace_bytes(ctypes.byref(d.c()))
+
+
+def router_route_workspace_bytes(d: Desc) -> int:
+    """moe_router_route_workspace_bytes: the route workspace plus the split
+    router's zero-filled counts and partial tiles."""
+    return lib().moe_router_route_workspace_bytes(ctypes.byref(d.c()))
 
 
 def expert_kernel(d: Desc, T: int, which: int) -> str:
@@ -499,7 +507,7 @@ class MoELayer:
         self.ep = ep                   # one rank's expert-parallel share (moe_route_ep)
         self.device = device
         self.rt = RouteTables(d, device)
-        self.ws = torch.zeros(route_workspace_bytes(d), dtype=torch.uint8, device=device)
+        self.ws = torch.zeros(router_route_workspace_bytes(d), dtype=torch.uint8, device=device)
         rows = buffer_rows(d)
         self.xg = torch.zeros((rows, d.H), dtype=torch.bfloat16, device=device)
         self.h = torch.zeros((rows, d.I), dtype=torch.bfloat16, device=device)

@@ -14,6 +14,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// a compile-time int as a type, for generic lambdas that unroll over it
+template <int V>
+struct IntC { static constexpr int value = V; };
+
 constexpr int kWave = 64;
 constexpr int kMaxK = 16;      // experts per token supported by the router
 constexpr int kMaxE = 4096;    // logical / physical experts supported
@@ -141,6 +145,38 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, 63);
   const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63);
   return (uint64_t(hi) << 32) | lo;
+}
+
+// The largest 32-bit value over the 64 lanes, to every lane (the same row
+// shifts and broadcasts as wave_max_u64 on one word).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_max_step32(uint32_t v) {
+  const uint32_t o = __builtin_amdgcn_update_dpp(0u, v, CTRL, ROW_MASK, 0xf, true);
+  return o > v ? o : v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max_step32<0x111, 0xf>(v);
+  v = dpp_max_step32<0x112, 0xf>(v);
+  v = dpp_max_step32<0x114, 0xf>(v);
+  v = dpp_max_step32<0x118, 0xf>(v);
+  v = dpp_max_step32<0x142, 0xa>(v);
+  v = dpp_max_step32<0x143, 0xc>(v);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// wave_max_u64 by 32-bit steps: the maximum of the high words; then, if one
+// lane holds it, that lane's low word, else the maximum low word among the
+// lanes that hold it.  Same result, about a third of the instructions when
+// high words rarely tie (the top-K keys: a tie is two equal logits).
+// Every lane of the wave must be active.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  const uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
+  const uint32_t mh = wave_max_u32(hi);
+  const uint64_t tie = __ballot(hi == mh);
+  uint32_t ml;
+  if (__popcll(tie) == 1) ml = __builtin_amdgcn_readlane(lo, __builtin_ctzll(tie));
+  else ml = wave_max_u32(hi == mh ? lo : 0u);
+  return (uint64_t(mh) << 32) | ml;
 }
 
 // A workgroup barrier that orders LDS accesses only: it waits for the

@@ -46,9 +46,6 @@
 
 namespace moe {
 
-template <int V>
-struct IntC { static constexpr int value = V; };
-
 constexpr int kTM = 128;     // token rows per tile
 constexpr int kTN = 256;     // weight rows per tile
 constexpr int kTK = 64;      // K per stage

@@ -169,11 +169,18 @@ struct RouterArgs {
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 bool router_uses_mfma(int E, int H, int x_f32);
 
+// the router for T <= 64 with each tile's H slices over several workgroups;
+// ws: its arrival counts (zero on entry, left zero), then the partial tiles
+int router_split_count(int E, int H, int x_f32, int T);
+size_t router_split_bytes(int E, int H, int x_f32, int T_max);
+hipError_t launch_router_split(const RouterArgs& a, void* ws, int T_max, hipStream_t s);
+
 // router logits, then routing: one launch when T * E <= kTinyRouterItems
 // (softmax top-K, E <= 64, no expert-parallel map), else the two launches
 constexpr int kTinyRouterItems = 16;
 bool router_route_fits(const RouterArgs& ra, const RouteArgs& a);
-hipError_t launch_router_route(const RouterArgs& ra, const RouteArgs& a, hipStream_t s);
+// split_ws: the split router's workspace (router_split_bytes for T_max), or null
+hipError_t launch_router_route(const RouterArgs& ra, const RouteArgs& a, void* split_ws, int T_max, hipStream_t s);
 
 // ---- persistent single-launch decode layer --------------------------------------
 

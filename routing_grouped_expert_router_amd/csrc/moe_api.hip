@@ -122,6 +122,11 @@ size_t moe_route_workspace_bytes(const moe_desc_t* d) {
 
 size_t moe_workspace_bytes(const moe_desc_t* d) { return moe_route_workspace_bytes(d); }
 
+size_t moe_router_route_workspace_bytes(const moe_desc_t* d) {
+  if (moe_check_desc(d) != MOE_OK) return 0;
+  return ws_layout(d).total + router_split_bytes(d->E, d->H, d->act_dtype == MOE_F32, d->T_max);
+}
+
 int64_t moe_shared_base(const moe_desc_t* d) {
   if (moe_check_desc(d) != MOE_OK) return -1;
   return routed_cap(d);
@@ -281,7 +286,11 @@ moe_status_t moe_router_route(const moe_desc_t* d, const void* x, const void* w_
   if (T == 0) return hip_status(launch_route(a, stream));   // no logits to compute
   const RouterArgs ra = {x, d->act_dtype == MOE_F32, static_cast<const uint16_t*>(w_router), bias,
                          T, d->E, d->H, logits};
-  return hip_status(launch_router_route(ra, a, stream));
+  // the split router's counts and partials follow the route's workspace
+  const size_t route_bytes = ws_layout(d).total;
+  const size_t split_bytes = router_split_bytes(d->E, d->H, d->act_dtype == MOE_F32, d->T_max);
+  void* split_ws = split_bytes && ws_bytes >= route_bytes + split_bytes ? static_cast<char*>(ws) + route_bytes : nullptr;
+  return hip_status(launch_router_route(ra, a, split_ws, d->T_max, stream));
 }
 
 moe_status_t moe_route_noalloc(const moe_desc_t* d, const float* logits, int32_t T, const int32_t* l2p,

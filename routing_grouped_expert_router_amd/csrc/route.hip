@@ -98,9 +98,11 @@ bool router_route_fits(const RouterArgs& ra, const RouteArgs& a) {
          a.T * a.E <= kTinyRouterItems && !router_uses_mfma(ra.E, ra.H, ra.x_f32);
 }
 
-hipError_t launch_router_route(const RouterArgs& ra, const RouteArgs& a, hipStream_t s) {
+hipError_t launch_router_route(const RouterArgs& ra, const RouteArgs& a, void* split_ws, int T_max, hipStream_t s) {
   if (!router_route_fits(ra, a)) {
-    const hipError_t e = launch_router(ra, s);
+    const hipError_t e = split_ws && router_split_count(ra.E, ra.H, ra.x_f32, ra.T)
+                             ? launch_router_split(ra, split_ws, T_max, s)
+                             : launch_router(ra, s);
     return e != hipSuccess ? e : launch_route(a, s);
   }
   const dim3 g(1), b(kFusedThreads);

@@ -56,7 +56,7 @@ __device__ __forceinline__ void select_tokens(const RouteArgs& a, int t0, int co
     for (int k = 0; k < K; ++k) {
       uint64_t best = keys[0];
       if constexpr (LPT == kWave) {
-        best = wave_max_u64(best);
+        best = wave_max_key(best);
       } else {
 #pragma unroll
         for (int off = LPT >> 1; off >= 1; off >>= 1) {
@@ -170,7 +170,7 @@ __device__ __forceinline__ void select_tokens_grouped(const RouteArgs& a, int t0
     uint64_t gkey = (valid && lane < G) ? topk_key(my_g, lane) : 0ull;
     uint64_t gmask = 0ull;
     for (int r = 0; r < a.topk_group; ++r) {
-      const uint64_t best = wave_max_u64(gkey);
+      const uint64_t best = wave_max_key(gkey);
       gmask |= 1ull << (int(0xffffffffu - uint32_t(best & 0xffffffffu)) & 63);
       gkey = gkey == best ? 0ull : gkey;
     }
@@ -192,7 +192,7 @@ __device__ __forceinline__ void select_tokens_grouped(const RouteArgs& a, int t0
     uint64_t my_key = 0ull;
     float my_s = 0.f;
     for (int k = 0; k < K; ++k) {
-      const uint64_t best = wave_max_u64(key[0]);
+      const uint64_t best = wave_max_key(key[0]);
       const int id = int(0xffffffffu - uint32_t(best & 0xffffffffu));
       const float sb = __shfl(sc[0], id & (kWave - 1), kWave);   // the winner's lane is id % 64
       if (lane == k) { my_key = best; my_s = sb; }

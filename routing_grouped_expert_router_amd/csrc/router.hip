@@ -39,6 +39,123 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_mfma_kernel(RouterAr
 
 bool router_uses_mfma(int E, int H, int x_f32) { return E > 64 && !x_f32 && H % 1024 == 0; }
 
+// ---- few tokens: a tile's 16 H slices over S workgroups ---------------------
+//
+// With T <= 64 the router_mfma grid has E/16 * ceil(T/16) workgroups, a few
+// dozen for 256 experts, each reading 16 W_r rows and 16 activation rows
+// whole: a few compute units stream everything.  Here the 16 slices of a
+// (16-expert, 16-token) tile go to S = 16 / W workgroups of W waves, each
+// wave computing its slice exactly as router_mfma_kernel<1>'s wave of the
+// same index does.  Every wave writes its partial tile to part; the last
+// workgroup of a tile to arrive (an atomic count per tile in `arrive`, left
+// at zero again) adds the 16 partials in slice order, as router_mfma_store
+// does, so the logits are bit-identical to router_mfma_kernel<1>'s.
+// part: [tiles][16][64] f32x4; arrive: [tiles], zero on entry.
+//
+// The partials cross workgroups, possibly on other XCDs, without an L2
+// writeback (an agent-scope release fence writes a whole L2 back and stalls
+// it for microseconds, once per workgroup here): they are stored at agent
+// scope, which writes them past the XCD's L2, each wave waits until its
+// stores have completed before its workgroup arrives, and the last arrival
+// reads them with agent-scope loads, which do not stop at its own L2 (the
+// same protocol as the grid barrier of the persistent decode kernel).
+template <int W>
+__global__ __launch_bounds__(W * 64) void router_mfma_split_kernel(RouterArgs a, float* part, uint32_t* arrive) {
+  __shared__ int last_s;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e0 = blockIdx.x * 16, t0 = blockIdx.y * 16;
+  const int tile = blockIdx.y * gridDim.x + blockIdx.x;
+  const int slice = blockIdx.z * W + wave;
+  float* tp = part + (size_t)tile * kRouterWaves * 64 * 4;
+  f32x4 acc[1];
+  router_mfma_slice<1>(a, e0, t0, slice, acc);
+  {
+    float* p = tp + (slice * 64 + lane) * 4;
+    __hip_atomic_store(p + 0, acc[0].x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p + 1, acc[0].y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p + 2, acc[0].z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p + 3, acc[0].w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);     // this wave's partial stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last_s = __hip_atomic_fetch_add(arrive + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             gridDim.z - 1u;
+  __syncthreads();
+  if (!last_s) return;
+  if (threadIdx.x < 64) {
+    auto ld = [&](int w) -> f32x4 {
+      const float* p = tp + (w * 64 + lane) * 4;
+      return f32x4{__hip_atomic_load(p + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                   __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                   __hip_atomic_load(p + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                   __hip_atomic_load(p + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+    };
+    f32x4 sum = ld(0);
+    for (int w = 1; w < kRouterWaves; ++w) sum += ld(w);
+    const int t = t0 + (lane & 15);
+    if (t < a.T) {
+      const float v[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = e0 + 4 * (lane >> 4) + j;
+        if (e < a.E) a.logits[(int64_t)t * a.E + e] = v[j] + (a.bias ? a.bias[e] : 0.f);
+      }
+    }
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(arrive + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int kRouterSplitMaxT = 64;
+
+// Workgroups per tile of the split router for T tokens (0: not used): the
+// smallest power of two that brings the grid to 256 workgroups, at most 16.
+// Used from 4 chunks per wave (H >= 4096) on: measured on MI355X at E = 256,
+// the split router takes 7.4 us against 15 us at H = 7168, but its partial
+// round trip makes it slower than the one-workgroup tiles at H <= 2048.
+constexpr int kRouterSplitMinH = 4096;
+int router_split_count(int E, int H, int x_f32, int T) {
+  if (!router_uses_mfma(E, H, x_f32) || H < kRouterSplitMinH || T < 1 || T > kRouterSplitMaxT) return 0;
+  const int tiles = ((E + 15) / 16) * ((T + 15) / 16);
+  int S = 2;
+  while (S < 16 && tiles * S < 256) S *= 2;
+  return tiles * 2 <= 256 ? S : 0;
+}
+
+// Bytes of the split router's arrival counts and partial tiles for up to
+// T_max tokens (0 when the split router is never used).
+// The workspace holds the counts, then the partials, of the largest tile
+// count any call may have (T = min(T_max, 64)); a call uses the first tiles
+// of each, so calls with fewer tokens keep the same layout.
+static size_t split_tiles_max(int E, int T_max) {
+  const int T = T_max < kRouterSplitMaxT ? T_max : kRouterSplitMaxT;
+  return (size_t)((E + 15) / 16) * ((T + 15) / 16);
+}
+
+static size_t split_part_offset(size_t tiles_max) { return (tiles_max * sizeof(uint32_t) + 255) / 256 * 256; }
+
+size_t router_split_bytes(int E, int H, int x_f32, int T_max) {
+  const int T = T_max < kRouterSplitMaxT ? T_max : kRouterSplitMaxT;
+  if (!router_split_count(E, H, x_f32, T)) return 0;
+  const size_t tiles = split_tiles_max(E, T_max);
+  return split_part_offset(tiles) + tiles * kRouterWaves * 64 * sizeof(f32x4);
+}
+
+hipError_t launch_router_split(const RouterArgs& a, void* ws, int T_max, hipStream_t s) {
+  const int S = router_split_count(a.E, a.H, a.x_f32, a.T);
+  if (!S || a.T > T_max) return hipErrorInvalidValue;
+  uint32_t* arrive = static_cast<uint32_t*>(ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + split_part_offset(split_tiles_max(a.E, T_max)));
+  const dim3 g((a.E + 15) / 16, (a.T + 15) / 16, S);
+  switch (S) {
+    case 2: hipLaunchKernelGGL(router_mfma_split_kernel<8>, g, dim3(8 * 64), 0, s, a, part, arrive); break;
+    case 4: hipLaunchKernelGGL(router_mfma_split_kernel<4>, g, dim3(4 * 64), 0, s, a, part, arrive); break;
+    case 8: hipLaunchKernelGGL(router_mfma_split_kernel<2>, g, dim3(2 * 64), 0, s, a, part, arrive); break;
+    default: hipLaunchKernelGGL(router_mfma_split_kernel<1>, g, dim3(64), 0, s, a, part, arrive); break;
+  }
+  return hipGetLastError();
+}
+
 // ---- many tokens: 64 experts x 64 tokens per workgroup ----------------------
 //
 // A 16-expert block re-reads every activation row once per block (16 times

@@ -114,24 +114,52 @@ __device__ __forceinline__ void router_mfma_slice(const RouterArgs& a, int e0, i
   };
   // router_ahead<MR>() 64-wide chunks in flight in a ring of register sets (a
   // slice has a few chunks: one at a time left the wave waiting a full
-  // memory latency per chunk); the MFMAs run in chunk order
+  // memory latency per chunk); the MFMAs run in chunk order.  Slices of up
+  // to 8 chunks (H <= 8192) run fully unrolled: with every load at a fixed
+  // place the compiler waits for the oldest chunk only, where a loop made it
+  // wait for every load in flight once per turn.
   constexpr int D = router_ahead<MR>();
   u32x4 wv[D][2], xv[D][MR][2];
   const int nch = kw / 64;
+  auto step = [&](int c, int d) -> void {
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (d < nch) load(kbeg + 64 * d, wv[d], xv[d]);
-  for (int c0 = 0; c0 < nch; c0 += D) {
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int c = c0 + d;
-      if (c < nch) {
+      for (int m = 0; m < MR; ++m)
+        acc[m] = mfma16x16x32(__builtin_bit_cast(bf16x8, wv[d][j]), __builtin_bit_cast(bf16x8, xv[d][m][j]), acc[m]);
+  };
+  auto unrolled = [&](auto nc) -> void {
+    constexpr int NCH = decltype(nc)::value;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+    for (int d = 0; d < D; ++d)
+      if (d < NCH) load(kbeg + 64 * d, wv[d], xv[d]);
 #pragma unroll
-          for (int m = 0; m < MR; ++m)
-            acc[m] = mfma16x16x32(__builtin_bit_cast(bf16x8, wv[d][j]), __builtin_bit_cast(bf16x8, xv[d][m][j]), acc[m]);
-        if (c + D < nch) load(kbeg + 64 * (c + D), wv[d], xv[d]);
+    for (int c = 0; c < NCH; ++c) {
+      step(c, c % D);
+      if (c + D < NCH) load(kbeg + 64 * (c + D), wv[c % D], xv[c % D]);
+    }
+  };
+  switch (nch) {
+    case 1: unrolled(IntC<1>{}); break;
+    case 2: unrolled(IntC<2>{}); break;
+    case 3: unrolled(IntC<3>{}); break;
+    case 4: unrolled(IntC<4>{}); break;
+    case 5: unrolled(IntC<5>{}); break;
+    case 6: unrolled(IntC<6>{}); break;
+    case 7: unrolled(IntC<7>{}); break;
+    case 8: unrolled(IntC<8>{}); break;
+    default: {
+      // every step issues its loads, past the slice's end re-reading its
+      // last chunk (never used), so that no load sits under a branch
+#pragma unroll
+      for (int d = 0; d < D; ++d) load(kbeg + 64 * d, wv[d], xv[d]);
+      for (int c0 = 0; c0 < nch; c0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          const int c = c0 + d;
+          if (c < nch) step(c, d);
+          load(kbeg + 64 * min(c + D, nch - 1), wv[d], xv[d]);
+        }
       }
     }
   }

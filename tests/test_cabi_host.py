@@ -170,6 +170,13 @@ def test_buffer_sizing_formulas(cfg):
     assert B.y_bytes(d, cfg.T) == (plane * 2 if s == 1 else plane * 4 * s)
     assert B.route_workspace_bytes(d) >= 4 * cfg.T * cfg.K
     assert B.workspace_bytes(d) == B.route_workspace_bytes(d)
+    # the split router's arrival counts and partial 16 x 16 tiles (16 slices
+    # of 64 lanes x 16 bytes) for up to 64 tokens, when it applies
+    tiles = -(-cfg.E // 16) * -(-min(cfg.T, 64) // 16)
+    split = (cfg.E > 64 and cfg.act_dtype == "bf16" and cfg.H % 1024 == 0 and cfg.H >= 4096
+             and tiles * 2 <= 256)
+    extra = (-(-4 * tiles // 256) * 256 + tiles * 16 * 64 * 16) if split else 0
+    assert B.router_route_workspace_bytes(d) == B.route_workspace_bytes(d) + extra
     # one y buffer for every T: moe_y_bytes_max bounds moe_y_bytes at each T
     ymax = B.y_bytes_max(d)
     ts = sorted({1, 2, 3, cfg.T} | set(range(1, cfg.T + 1, max(1, cfg.T // 64))))

@@ -173,6 +173,49 @@ def test_router_route_matches_two_calls(cfg):
         say(f"  {cfg.name} T={T}: logits and tables bit-identical, status {got['status']}")
 
 
+# up to 64 tokens and more than 64 experts: with the larger workspace the
+# router spreads each 16 x 16 logit tile over 2..16 workgroups
+ROUTER_SPLIT = [
+    configs.tiny().with_(name="split_e256_t32_masked", T=32, H=7168, I=128, E=256, E_phys=256, K=8,
+                         act_dtype="bf16", M_max=4, bias="normal0.5"),
+    configs.tiny().with_(name="split_e256_t5_h4096", T=5, H=4096, I=128, E=256, E_phys=256, K=8,
+                         act_dtype="bf16", M_max=4),
+    configs.tiny().with_(name="split_e200_t37_contig", T=37, H=5120, I=128, E=200, E_phys=200, K=6,
+                         act_dtype="bf16", layout="contig", BM=16, bias="zipf1.1"),
+    configs.tiny().with_(name="split_e512_t64_contig", T=64, H=4096, I=128, E=512, E_phys=512, K=10,
+                         act_dtype="bf16", layout="contig", BM=16),
+]
+
+
+@pytest.mark.parametrize("cfg", ROUTER_SPLIT, ids=lambda c: c.name)
+def test_split_router_matches_two_calls(cfg):
+    """moe_router_route with moe_router_route_workspace_bytes of zeroed ws
+    (the split router) equals moe_router_logits + moe_route bit for bit, at
+    T, at a smaller T right after, at T again (the arrival counts were left
+    zero, the layout does not depend on T) and at T = 0."""
+    b = Built(cfg)
+    d, L = b.d, b.layer
+    rbytes = B.route_workspace_bytes(d)
+    assert B.router_route_workspace_bytes(d) > rbytes, cfg.name      # the split router applies
+    ws_plain = torch.zeros(rbytes, dtype=torch.uint8, device=DEV)
+    ws_split = torch.zeros(B.router_route_workspace_bytes(d), dtype=torch.uint8, device=DEV)
+    rt2 = B.RouteTables(d, DEV)
+    for T in (b.T, max(1, b.T // 3), b.T, 0):
+        lg1 = torch.full_like(L.logits, float("nan"))
+        B.moe_router_logits(d, b.x, b.wr, b.bias, T, lg1)
+        B.moe_route(d, lg1, T, L.rt, ws_plain, b.l2p, b.rcount)
+        lg2 = torch.full_like(L.logits, float("nan"))
+        B.moe_router_route(d, b.x, b.wr, b.bias, T, lg2, rt2, ws_split, b.l2p, b.rcount)
+        torch.cuda.synchronize()
+        assert torch.equal(lg1[:T], lg2[:T]), (cfg.name, T)
+        ref, got = route_np(L.rt, T, cfg.K), route_np(rt2, T, cfg.K)
+        for k in RR_KEYS:
+            assert np.array_equal(np.asarray(ref[k]), np.asarray(got[k])), (cfg.name, T, k)
+        ncount = 4 * ((cfg.E + 15) // 16) * ((min(b.T, 64) + 15) // 16)
+        assert not ws_split[rbytes:rbytes + ncount].any(), (cfg.name, T)   # arrival counts back at zero
+        say(f"  {cfg.name} T={T}: split router logits and tables bit-identical")
+
+
 # many tokens and more than 64 experts: the 64-expert x 64-token block
 # router (ragged token and expert counts: partial blocks on both axes)
 ROUTER_BLOCK = [
