@@ -189,35 +189,66 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Exclusive scans of N arrays of n (<= 4 * blockDim.x) ints each in LDS
+// (arr[0..N-1]), in place, by the whole workgroup, sharing one set of
+// barriers; total[q] = the sum of arr[q].  `tmp` needs N * (blockDim.x/64 + 1)
+// ints.  Integer sums: the results do not depend on the grouping.
+template <int N>
+__device__ inline void block_exclusive_scan_n(int* const (&arr)[N], int n, int* tmp, int (&total)[N]) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int nw = nt / 64;
+  const int per = (n + nt - 1) / nt;
+  const int lo = tid * per, hi = min(lo + per, n);
+  const int lane = tid & 63, wv = tid >> 6;
+  int s[N], x[N];
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    s[q] = 0;
+    for (int i = lo; i < hi; ++i) s[q] += arr[q][i];
+    // inclusive scan of s across the wave
+    x[q] = s[q];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x[q], off, kWave);
+      if (lane >= off) x[q] += y;
+    }
+    if (lane == 63) tmp[q * (nw + 1) + wv] = x[q];
+  }
+  lds_barrier();
+  // the waves' totals (at most 16 per array) scanned by the first wave's lanes
+  if (wv == 0) {
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      int* t = tmp + q * (nw + 1);
+      const int c = lane < nw ? t[lane] : 0;
+      int r = c;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(r, off, kWave);
+        if (lane >= off) r += y;
+      }
+      if (lane < nw) t[lane] = r - c;
+      if (lane == nw - 1) t[nw] = r;
+    }
+  }
+  lds_barrier();
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    const int* t = tmp + q * (nw + 1);
+    int base = t[wv] + x[q] - s[q];
+    for (int i = lo; i < hi; ++i) { const int c = arr[q][i]; arr[q][i] = base; base += c; }
+    total[q] = t[nw];
+  }
+  lds_barrier();
+}
+
 // Exclusive scan of n (<= 4 * blockDim.x) ints in LDS `a`, in place, by the
 // whole workgroup; returns the total.  `tmp` needs blockDim.x/64 + 1 ints.
 __device__ inline int block_exclusive_scan(int* a, int n, int* tmp) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const int per = (n + nt - 1) / nt;
-  const int lo = tid * per, hi = min(lo + per, n);
-  int s = 0;
-  for (int i = lo; i < hi; ++i) s += a[i];
-  // inclusive scan of s across the workgroup
-  const int lane = tid & 63, wv = tid >> 6;
-  int x = s;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(x, off, kWave);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) tmp[wv] = x;
-  lds_barrier();
-  if (tid == 0) {
-    int run = 0;
-    for (int w = 0; w < nt / 64; ++w) { int c = tmp[w]; tmp[w] = run; run += c; }
-    tmp[nt / 64] = run;
-  }
-  lds_barrier();
-  int base = tmp[wv] + x - s;
-  for (int i = lo; i < hi; ++i) { int c = a[i]; a[i] = base; base += c; }
-  int total = tmp[nt / 64];
-  lds_barrier();
-  return total;
+  int* const arr[1] = {a};
+  int total[1];
+  block_exclusive_scan_n<1>(arr, n, tmp, total);
+  return total[0];
 }
 
 }  // namespace moe

@@ -73,6 +73,26 @@ __global__ __launch_bounds__(kFusedThreads) void route_fused_kernel(RouteArgs a)
   route_one_workgroup<LPT, NPL, GROUPED>(a);
 }
 
+// T <= 64 with more tokens than the fused workgroup selects in one pass:
+// the selection runs in its own launch over workgroups of four waves (one
+// token per wave for E > 32, on as many compute units: in one workgroup the
+// rounds of several tokens per wave queue on four SIMDs), then this
+// workgroup reads the ids and the per-token non-finite flags back and
+// builds the tables as the fused kernel does.
+__global__ __launch_bounds__(kFusedThreads) void route_tables_kernel(RouteArgs a) {
+  __shared__ int ids[kBlockTokens * kMaxK];
+  __shared__ int bad;
+  if (threadIdx.x == 0) bad = 0;
+  lds_barrier();
+  const int TK = a.T * a.K;
+  for (int i = threadIdx.x; i < TK; i += kFusedThreads) ids[i] = a.topk_ids[i];
+  for (int t = threadIdx.x; t < a.T; t += kFusedThreads)
+    if (a.ws.tok_flag[t]) atomicOr(&bad, 1);
+  lds_barrier();
+  route_block_tables(a, ids, bad != 0);
+}
+
+
 // A few tokens and experts (T * E <= kTinyRouterItems, E <= 64): the router
 // logits and the routing in one workgroup, one launch instead of two.  Its
 // four groups of 256 threads take the (token, expert) items in turn, each
@@ -123,7 +143,10 @@ static void launch_shape(const RouteArgs& a, int nblk, hipStream_t s) {
   // one block: a single launch, unless 16 keys per lane would not fit the
   // registers of a 1024-thread workgroup
   constexpr bool kFusedFits = GROUPED ? NPL <= 4 : NPL <= 8;
-  if (nblk <= 1 && kFusedFits) {
+  const bool one_block = nblk <= 1 && kFusedFits;
+  // tokens the fused workgroup selects in one pass (one per LPT lanes)
+  constexpr int kFusedPass = (kFusedThreads / kWave) * (GROUPED ? 1 : kWave / LPT);
+  if (one_block && a.T <= kFusedPass) {
     hipLaunchKernelGGL((route_fused_kernel<LPT, NPL, GROUPED>), dim3(1), dim3(kFusedThreads), 0, s, a);
     return;
   }
@@ -137,6 +160,10 @@ static void launch_shape(const RouteArgs& a, int nblk, hipStream_t s) {
       hipLaunchKernelGGL((route_select_kernel<LPT, NPL>), dim3((a.T + per_wg - 1) / per_wg), dim3(kSelectThreads),
                          0, s, a);
     }
+  }
+  if (one_block) {
+    hipLaunchKernelGGL(route_tables_kernel, dim3(1), dim3(kFusedThreads), 0, s, a);
+    return;
   }
   hipLaunchKernelGGL(route_rank_kernel, dim3(nblk > 0 ? nblk : 1), dim3(kRouteThreads), 0, s, a);
   hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);

@@ -25,14 +25,24 @@ __device__ __forceinline__ void select_tokens(const RouteArgs& a, int t0, int co
   const int E = a.E, K = a.K;
   const int lane = threadIdx.x & (kWave - 1);
   const int sub = lane / LPT, sl = lane % LPT, sbase = sub * LPT;
+  // a token's logits; loads issued unconditionally (clamped row and column),
+  // masked afterwards.  The next pass's token is loaded while this one is
+  // selected, so a wave with several tokens waits for memory once.
+  auto load_row = [&](int bse, float* dst) -> void {
+    const int tt = t0 + bse + sub;
+    const float* row = a.logits + (int64_t)((bse + sub < count && tt < a.T) ? tt : 0) * E;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) dst[j] = row[min(sl + j * LPT, E - 1)];
+  };
+  float nxt[NPL];
+  load_row(wave * TPW, nxt);
   for (int base = wave * TPW; base < count; base += nwaves * TPW) {
     const int t = t0 + base + sub;
     const bool valid = base + sub < count && t < a.T;
-    const float* row = a.logits + (int64_t)(valid ? t : 0) * E;
-    // all loads issued unconditionally (clamped column), masked afterwards
     float lv[NPL];
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) lv[j] = row[min(sl + j * LPT, E - 1)];
+    for (int j = 0; j < NPL; ++j) lv[j] = nxt[j];
+    load_row(base + nwaves * TPW, nxt);
     uint64_t keys[NPL];
     bool bad = false;
 #pragma unroll
@@ -446,23 +456,210 @@ __device__ __forceinline__ void assign_one(const RouteArgs& a, int64_t i) {
 
 // ---- one workgroup, T <= 64 (one token block) ------------------------------
 //
-// rank, scan and assign of one 64-token block, handing each other their
-// tables in LDS: the phases' barriers order LDS only, so no phase waits for
-// another's global stores, and nothing is read back from global memory
-// except the maps.  The tables are the ones rank_block + scan_all + assign_one
+// rank, scan and assign of one 64-token block with the tables in LDS: no
+// phase waits on global memory written by another, nothing is read back
+// from global memory except the maps, and the status word is written once,
+// at the end.  The tables are the ones rank_block + scan_all + assign_one
 // compute for a single block (a block's exclusive prefix is then 0, so a
-// choice's rank among its logical expert's tokens is its rank in the block),
-// and the status word is written once, at the end, by thread 0.
-//   ids: LDS [T * K] selected logical ids (select_tokens' lds_ids);
+// choice's rank among its logical expert's tokens is its rank in the
+// block).  With at most 64 experts and slots the workgroup's first wave
+// does it alone (route_tables_wave: no workgroup barrier at all, its LDS
+// operations complete in order; the other waves return at once); with
+// more, the whole workgroup, with LDS-only barriers between phases
+// (route_tables_wg).
+//   ids: LDS [T * K] selected logical ids (select_tokens' lds_ids), visible
+//   to every wave (a workgroup barrier after the select);
 //   tok_bad: any selected token had a non-finite logit.
-// Any workgroup size that is a multiple of 64 and at most kScanThreads.
-__device__ __forceinline__ void route_block_tables(const RouteArgs& a, const int* ids, bool tok_bad) {
-  __shared__ unsigned long long mask[1024];      // E <= 1024 on the routing paths
-  __shared__ int cnt[kMaxE + 1];
-  __shared__ int aux[kMaxE + 1];
-  __shared__ int pad[kMaxE + 1];                 // spill (masked) or padded (contiguous) offsets
-  __shared__ int rk[kBlockTokens * kMaxK];
-  __shared__ int tmp[kScanThreads / 64 + 1];
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Exclusive scans, in place, of N LDS arrays of n ints by one wave: lane l
+// takes elements [l c, l c + c) with c = ceil(n / 64); returns the totals.
+template <int N>
+__device__ __forceinline__ void wave_exclusive_scan_n(int* const (&arr)[N], int n, int (&total)[N]) {
+  const int lane = threadIdx.x & 63;
+  const int c = (n + 63) / 64;
+  const int lo = lane * c, hi = min(lo + c, n);
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) sum += arr[q][i];
+    int x = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, kWave);
+      if (lane >= off) x += y;
+    }
+    int base = x - sum;
+    for (int i = lo; i < hi; ++i) { const int v = arr[q][i]; arr[q][i] = base; base += v; }
+    total[q] = __shfl(x, 63, kWave);
+  }
+}
+
+__device__ __forceinline__ void route_tables_wave(const RouteArgs& a, const int* ids, bool tok_bad,
+                                                  unsigned long long* mask, int* cnt, int* aux, int* pad, int* rk) {
+  if (threadIdx.x >= kWave) return;
+  const int lane = threadIdx.x;
+  const int E = a.E, P = a.E_phys, K = a.K;
+  const int TK = a.T * K;
+  const bool ep = a.local_of != nullptr;
+  const int NG = ep ? a.n_global : P;
+  const int NC = NG > P ? NG : P;
+  for (int e = lane; e < E; e += kWave) mask[e] = 0ull;
+  for (int p = lane; p <= NC; p += kWave) { cnt[p] = 0; aux[p] = 0; }
+  wave_lds_sync();
+  // rank: one bit per token in its chosen experts' masks
+  for (int i = lane; i < TK; i += kWave) atomicOr(&mask[ids[i]], 1ull << (i / K));
+  // replica map validation: counts in [1, max_replicas], slots in range,
+  // every slot listed at most once
+  const bool has_map = a.l2p != nullptr;
+  bool bad = false;
+  if (has_map) {
+    for (int l = lane; l < E; l += kWave) {
+      const int R = a.rcount[l];
+      if (R < 1 || R > a.max_replicas) { bad = true; continue; }
+      for (int r = 0; r < R; ++r) {
+        const int p = a.l2p[(int64_t)l * a.max_replicas + r];
+        if (p < 0 || p >= NG) bad = true;
+        else atomicAdd(&aux[p], 1);
+      }
+    }
+  }
+  wave_lds_sync();
+  // rank of choice i among the earlier tokens that chose the same expert
+  for (int i = lane; i < TK; i += kWave) {
+    const int tl = i / K;
+    rk[i] = tl ? __popcll(mask[ids[i]] & ((1ull << tl) - 1ull)) : 0;
+  }
+  if (has_map)
+    for (int p = lane; p < NG; p += kWave)
+      if (aux[p] > 1) bad = true;
+  const bool valid = has_map && __ballot(bad) == 0ull;
+  // physical counts: replica r of l gets the j = r, r+R, ... tokens
+  for (int l = lane; l < E; l += kWave) {
+    const int Tl = __popcll(mask[l]);
+    if (valid) {
+      const int R = a.rcount[l];
+      for (int r = 0; r < R; ++r)
+        cnt[a.l2p[(int64_t)l * a.max_replicas + r]] = (Tl - r + R - 1) / R;
+    } else {
+      cnt[l] = Tl;
+    }
+  }
+  wave_lds_sync();
+  bool ep_ok = true;
+  if (ep) {
+    // local map: entries in [-1, P), each local slot named at most once; the
+    // local counts take the counts of their global slots
+    for (int q = lane; q < NC; q += kWave) aux[q] = 0;
+    wave_lds_sync();
+    bool bad_ep = false;
+    for (int p = lane; p < NG; p += kWave) {
+      const int q = a.local_of[p];
+      if (q < -1 || q >= P) bad_ep = true;
+      else if (q >= 0) atomicAdd(&aux[q], 1);
+    }
+    wave_lds_sync();
+    for (int q = lane; q < P; q += kWave)
+      if (aux[q] > 1) bad_ep = true;
+    ep_ok = __ballot(bad_ep) == 0ull;
+    wave_lds_sync();
+    for (int q = lane; q < P; q += kWave) aux[q] = 0;
+    wave_lds_sync();
+    if (ep_ok)
+      for (int p = lane; p < NG; p += kWave) {
+        const int q = a.local_of[p];
+        if (q >= 0) aux[q] = cnt[p];
+      }
+    wave_lds_sync();
+    for (int q = lane; q < P; q += kWave) cnt[q] = aux[q];
+    wave_lds_sync();
+  }
+  const bool masked = a.layout == MOE_MASKED;
+  for (int p = lane; p < P; p += kWave) {
+    const int c = cnt[p];
+    a.counts[p] = c;
+    if (masked) {
+      const int mm = c < a.M_max ? c : a.M_max;
+      a.masked_m[p] = mm;
+      pad[p] = c - mm;
+    } else {
+      pad[p] = (c + a.BM - 1) / a.BM * a.BM;
+    }
+    aux[p] = (c + kTileRows - 1) / kTileRows;   // row tiles of the tiled expert kernel
+  }
+  wave_lds_sync();
+  // offsets, spill or padded offsets, and tile offsets in one pass
+  int* const arrs[3] = {cnt, pad, aux};
+  int tots[3];
+  wave_exclusive_scan_n<3>(arrs, P, tots);
+  wave_lds_sync();
+  const int total = tots[0], total2 = tots[1], ttotal = tots[2];
+  for (int p = lane; p < P; p += kWave) {
+    a.offsets[p] = cnt[p];
+    if (masked) a.spill_off[p] = pad[p];
+    else a.pad_off[p] = pad[p];
+    a.tile_off[p] = aux[p];
+  }
+  if (a.claim)
+    for (int i = lane; i < MOE_CLAIM_WORDS; i += kWave) a.claim[i] = 0u;
+  uint32_t st = 0;
+  if (tok_bad) st |= MOE_STATUS_NONFINITE;
+  if (masked && total2 > 0) st |= MOE_STATUS_SPILL;
+  if (has_map && !valid) st |= MOE_STATUS_BAD_REPLICA;
+  if (!ep_ok) st |= MOE_STATUS_BAD_EP_MAP;
+  if (lane == 0) {
+    a.tile_off[P] = ttotal;
+    a.tile_off[P + 1] = ttotal + (a.n_shared ? (a.T + kTileRows - 1) / kTileRows : 0);
+    a.offsets[P] = total;
+    if (masked) a.spill_off[P] = total2;
+    else a.pad_off[P] = total2;
+  }
+  // assign: choice i's replica, row and buffer slot (as assign_one)
+  bool internal = false;
+  for (int i = lane; i < TK; i += kWave) {
+    const int t = i / K;
+    const int l = ids[i];
+    const int j = rk[i];
+    int p = l, rank = j;
+    if (valid) {
+      const int R = a.rcount[l];
+      p = a.l2p[(int64_t)l * a.max_replicas + j % R];
+      rank = j / R;
+    }
+    if (ep) {
+      p = ep_ok ? a.local_of[p] : -1;
+      if (p < 0) {                    // another rank's choice: no local row
+        a.topk_phys[i] = -1;
+        a.row_of[i] = -1;
+        a.slot_of[i] = -1;
+        continue;
+      }
+    }
+    const int row = cnt[p] + rank;
+    int64_t slot;
+    if (masked)
+      slot = rank < a.M_max ? (int64_t)p * a.M_max + rank : (int64_t)P * a.M_max + pad[p] + (rank - a.M_max);
+    else
+      slot = (int64_t)pad[p] + rank;
+    a.topk_phys[i] = p;
+    a.row_of[i] = row;
+    bool ok = true;
+    if (row >= 0 && row < TK) a.src_of[row] = t; else ok = false;
+    if (slot < 0 || slot >= a.routed_cap) { slot = -1; ok = false; }
+    a.slot_of[i] = int32_t(slot);
+    internal |= !ok;
+  }
+  if (__ballot(internal)) st |= MOE_STATUS_INTERNAL;
+  if (lane == 0) a.status[0] = st;
+}
+
+__device__ __forceinline__ void route_tables_wg(const RouteArgs& a, const int* ids, bool tok_bad,
+                                                unsigned long long* mask, int* cnt, int* aux, int* pad, int* rk) {
+  __shared__ int tmp[3 * (kScanThreads / 64 + 1)];
   __shared__ int bad_s, bad_ep_s, st_s;
   const int tid = threadIdx.x, nth = blockDim.x;
   const int E = a.E, P = a.E_phys, K = a.K;
@@ -551,20 +748,20 @@ __device__ __forceinline__ void route_block_tables(const RouteArgs& a, const int
     } else {
       pad[p] = (c + a.BM - 1) / a.BM * a.BM;
     }
-    aux[p] = c;                      // kept: the tile counts need the rows per slot
+    aux[p] = (c + kTileRows - 1) / kTileRows;   // row tiles of the tiled expert kernel
   }
   lds_barrier();
-  const int total = block_exclusive_scan(cnt, P, tmp);
-  const int total2 = block_exclusive_scan(pad, P, tmp);
+  // offsets, spill or padded offsets, and tile offsets in one pass
+  int* const arrs[3] = {cnt, pad, aux};
+  int tots[3];
+  block_exclusive_scan_n<3>(arrs, P, tmp, tots);
+  const int total = tots[0], total2 = tots[1], ttotal = tots[2];
   for (int p = tid; p < P; p += nth) {
     a.offsets[p] = cnt[p];
     if (masked) a.spill_off[p] = pad[p];
     else a.pad_off[p] = pad[p];
-    aux[p] = (aux[p] + kTileRows - 1) / kTileRows;   // row tiles of the tiled expert kernel
+    a.tile_off[p] = aux[p];
   }
-  lds_barrier();
-  const int ttotal = block_exclusive_scan(aux, P, tmp);
-  for (int p = tid; p < P; p += nth) a.tile_off[p] = aux[p];
   if (a.claim)
     for (int i = tid; i < MOE_CLAIM_WORDS; i += nth) a.claim[i] = 0u;
   if (tid == 0) {
@@ -616,6 +813,17 @@ __device__ __forceinline__ void route_block_tables(const RouteArgs& a, const int
   }
   lds_barrier();
   if (tid == 0) a.status[0] = (uint32_t)st_s;
+}
+
+__device__ __forceinline__ void route_block_tables(const RouteArgs& a, const int* ids, bool tok_bad) {
+  __shared__ unsigned long long mask[1024];      // E <= 1024 on the routing paths
+  __shared__ int cnt[kMaxE + 1];
+  __shared__ int aux[kMaxE + 1];
+  __shared__ int pad[kMaxE + 1];                 // spill (masked) or padded (contiguous) offsets
+  __shared__ int rk[kBlockTokens * kMaxK];
+  const int ng = a.local_of ? a.n_global : a.E_phys;
+  if (a.E <= kWave && a.E_phys <= kWave && ng <= kWave) route_tables_wave(a, ids, tok_bad, mask, cnt, aux, pad, rk);
+  else route_tables_wg(a, ids, tok_bad, mask, cnt, aux, pad, rk);
 }
 
 }  // namespace moe
