@@ -55,14 +55,14 @@ __global__ __launch_bounds__(kRouteThreads) void route_assign_kernel(RouteArgs a
 // (route_block_tables), so no phase waits on global memory written by
 // another.
 template <int LPT, int NPL, bool GROUPED>
-__device__ __forceinline__ void route_one_workgroup(const RouteArgs& a) {
+__device__ __forceinline__ void route_one_workgroup(const RouteArgs& a, const float* lds_logits = nullptr) {
   __shared__ int ids[kBlockTokens * kMaxK];
   __shared__ int bad;
   if (threadIdx.x == 0) bad = 0;
   lds_barrier();
   if (a.T > 0) {
     if constexpr (GROUPED) select_tokens_grouped<NPL>(a, 0, a.T, threadIdx.x / kWave, kFusedThreads / kWave, ids, &bad);
-    else select_tokens<LPT, NPL>(a, 0, a.T, threadIdx.x / kWave, kFusedThreads / kWave, ids, &bad);
+    else select_tokens<LPT, NPL>(a, 0, a.T, threadIdx.x / kWave, kFusedThreads / kWave, ids, &bad, lds_logits);
   }
   lds_barrier();
   route_block_tables(a, ids, bad != 0);
@@ -100,17 +100,37 @@ __global__ __launch_bounds__(kFusedThreads) void route_tables_kernel(RouteArgs a
 // logits, and with them the tables, are bit-identical to the two launches.
 constexpr int kRouterGroups = kFusedThreads / 256;
 
+// Group g takes items g, g + 4, g + 8, g + 12 (item i: token i / E, expert
+// i % E), all of them in one pass with their loads issued together; the
+// logits also go to LDS, from where the routing reads them.
 template <bool XF32, int LPT>
 __global__ __launch_bounds__(kFusedThreads) void router_route_kernel(RouterArgs ra, RouteArgs a) {
-  __shared__ float red[kRouterGroups][4][1];
+  constexpr int NI = (kTinyRouterItems + kRouterGroups - 1) / kRouterGroups;
+  __shared__ float red[kRouterGroups][4 * NI];
+  __shared__ float lg[kRouterGroups * NI];        // logit of item g + 4 q at [g * NI + q]
+  __shared__ float lgt[kTinyRouterItems];         // the same in [t, e] order
   const int grp = threadIdx.x >> 8, gtid = threadIdx.x & 255;
   const int items = ra.T * ra.E;
-  for (int i0 = 0; i0 < items; i0 += kRouterGroups) {
-    const int i = i0 + grp;
-    router_small_group<XF32, 1>(ra, i < items ? i / ra.E : -1, i < items ? i % ra.E : 0, gtid, red[grp]);
+  int ts[NI], es[NI];
+#pragma unroll
+  for (int q = 0; q < NI; ++q) {
+    const int i = grp + kRouterGroups * q;
+    ts[q] = i < items ? i / ra.E : -1;
+    es[q] = i < items ? i % ra.E : 0;
   }
-  __syncthreads();        // the logits this workgroup wrote are read back by the routing
-  route_one_workgroup<LPT, 1, false>(a);
+  const int ni = (items - grp + kRouterGroups - 1) / kRouterGroups;   // this group's items
+  // every group runs exactly one of these (each has one workgroup barrier)
+  switch (ni) {
+    case 0:
+    case 1: router_small_group_n<XF32, 1>(ra, ts, es, gtid, red[grp], lg + grp * NI); break;
+    case 2: router_small_group_n<XF32, 2>(ra, ts, es, gtid, red[grp], lg + grp * NI); break;
+    case 3: router_small_group_n<XF32, 3>(ra, ts, es, gtid, red[grp], lg + grp * NI); break;
+    default: router_small_group_n<XF32, NI>(ra, ts, es, gtid, red[grp], lg + grp * NI); break;
+  }
+  lds_barrier();
+  if (threadIdx.x < items) lgt[threadIdx.x] = lg[(threadIdx.x % kRouterGroups) * NI + threadIdx.x / kRouterGroups];
+  lds_barrier();
+  route_one_workgroup<LPT, 1, false>(a, lgt);
 }
 
 bool router_route_fits(const RouterArgs& ra, const RouteArgs& a) {

@@ -18,9 +18,12 @@ __device__ __forceinline__ uint64_t max_u64(uint64_t x, uint64_t y) { return x >
 // lds_ids / lds_flag (single-workgroup routing): the ids also go to LDS at
 // (t - t0) * K + k, and a token with a non-finite logit ORs 1 into *lds_flag
 // instead of writing its global flag.
+// lds_logits: the logits [T, E] in LDS instead of a.logits (they were
+// computed by this workgroup).
 template <int LPT, int NPL>
 __device__ __forceinline__ void select_tokens(const RouteArgs& a, int t0, int count, int wave, int nwaves,
-                                              int* lds_ids = nullptr, int* lds_flag = nullptr) {
+                                              int* lds_ids = nullptr, int* lds_flag = nullptr,
+                                              const float* lds_logits = nullptr) {
   constexpr int TPW = kWave / LPT;   // tokens per wave and pass
   const int E = a.E, K = a.K;
   const int lane = threadIdx.x & (kWave - 1);
@@ -30,7 +33,7 @@ __device__ __forceinline__ void select_tokens(const RouteArgs& a, int t0, int co
   // selected, so a wave with several tokens waits for memory once.
   auto load_row = [&](int bse, float* dst) -> void {
     const int tt = t0 + bse + sub;
-    const float* row = a.logits + (int64_t)((bse + sub < count && tt < a.T) ? tt : 0) * E;
+    const float* row = (lds_logits ? lds_logits : a.logits) + (int64_t)((bse + sub < count && tt < a.T) ? tt : 0) * E;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) dst[j] = row[min(sl + j * LPT, E - 1)];
   };

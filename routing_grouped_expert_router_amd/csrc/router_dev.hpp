@@ -69,6 +69,87 @@ __device__ __forceinline__ void router_small_group(const RouterArgs& a, int t, i
   }
 }
 
+// NI (token, expert) logits by one group of 256 threads, each summed in
+// exactly the order router_small_group<XF32, 1> sums it, with the loads of
+// all NI items issued together (one memory latency for the NI items rather
+// than one each).  Item q is (ts[q], es[q]); ts[q] < 0: no item (es[q]
+// must still name a row of W_r).  Each logit is also written to lds_out[q].
+// red: this group's LDS partials, 4 * NI floats.
+template <bool XF32, int NI>
+__device__ __forceinline__ void router_small_group_n(const RouterArgs& a, const int* ts, const int* es, int tid,
+                                                     float* red, float* lds_out) {
+  const int lane = tid & 63, wave = tid >> 6;
+  float part[NI];
+#pragma unroll
+  for (int q = 0; q < NI; ++q) part[q] = 0.f;
+  // the 16 bytes of x and of W_r one item takes at h0; the next step's are
+  // loaded before this step is summed (past the end: the last step again,
+  // never used), so the group waits for memory about once
+  u32x4 xr[NI][2], wr[NI];
+  auto load = [&](int h0, u32x4 (*xd)[2], u32x4* wd) -> void {
+    const int hc = min(h0, a.H - 8);
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      const int t = ts[q] >= 0 ? ts[q] : 0;
+      if (XF32) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const float*>(a.x) + (int64_t)t * a.H + hc);
+        xd[q][0] = p[0];
+        xd[q][1] = p[1];
+      } else {
+        xd[q][0] = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) + (int64_t)t * a.H + hc);
+      }
+      wd[q] = *reinterpret_cast<const u32x4*>(a.w + (int64_t)es[q] * a.H + hc);
+    }
+  };
+  load(tid * 8, xr, wr);
+  for (int h0 = tid * 8; h0 < a.H; h0 += 256 * 8) {
+    u32x4 xc[NI][2], wc[NI];
+#pragma unroll
+    for (int q = 0; q < NI; ++q) { xc[q][0] = xr[q][0]; xc[q][1] = xr[q][1]; wc[q] = wr[q]; }
+    load(h0 + 256 * 8, xr, wr);
+#pragma unroll
+    for (int q = 0; q < NI; ++q) {
+      float xv[8];
+      if (XF32) {
+        xv[0] = __uint_as_float(xc[q][0].x); xv[1] = __uint_as_float(xc[q][0].y);
+        xv[2] = __uint_as_float(xc[q][0].z); xv[3] = __uint_as_float(xc[q][0].w);
+        xv[4] = __uint_as_float(xc[q][1].x); xv[5] = __uint_as_float(xc[q][1].y);
+        xv[6] = __uint_as_float(xc[q][1].z); xv[7] = __uint_as_float(xc[q][1].w);
+      } else {
+        const uint32_t w[4] = {xc[q][0].x, xc[q][0].y, xc[q][0].z, xc[q][0].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          xv[2 * k] = __uint_as_float(w[k] << 16);
+          xv[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        }
+      }
+      const uint32_t w[4] = {wc[q].x, wc[q].y, wc[q].z, wc[q].w};
+      float s = part[q];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        s += xv[2 * k] * __uint_as_float(w[k] << 16);
+        s += xv[2 * k + 1] * __uint_as_float(w[k] & 0xffff0000u);
+      }
+      part[q] = s;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NI; ++q) {
+    float v = part[q];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+    if (lane == 0) red[q * 4 + wave] = v;
+  }
+  __syncthreads();
+  if (tid < NI && ts[tid] >= 0) {
+    const int q = tid;
+    const float v = ((red[q * 4] + red[q * 4 + 1]) + red[q * 4 + 2]) + red[q * 4 + 3];
+    const float o = v + (a.bias ? a.bias[es[q]] : 0.f);
+    a.logits[(int64_t)ts[q] * a.E + es[q]] = o;
+    lds_out[q] = o;
+  }
+}
+
 template <bool XF32, int EB, bool WT = false>
 __device__ __forceinline__ void router_small_item(const RouterArgs& a, int t, int ey) {
   __shared__ float red[4][EB];
