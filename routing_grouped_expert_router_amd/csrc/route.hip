@@ -21,7 +21,10 @@
 //   assign, one thread per choice: the choice's rank j among all tokens of
 //     its logical expert, its replica l2p[l][j mod R] and rank j / R inside
 //     that slot, its row, its buffer slot, and src_of.
-//   For T <= 64 (one block) the four run back to back in one workgroup.
+//   For T <= 64 (one block) rank, scan and assign run in one workgroup that
+//     keeps their tables in LDS (by its first wave alone when experts and
+//     slots are at most 64), after the selection in the same workgroup, or,
+//     past the tokens it selects in one pass, in a launch of its own.
 #include <type_traits>
 
 #include "route_dev.hpp"

@@ -13,6 +13,9 @@
 //    its 16 waves split H, each runs v_mfma_f32_16x16x32_bf16 over its slice
 //    with operands loaded straight to registers (next slice in flight), and
 //    the 16 partial tiles are summed in wave order through LDS.
+//  * router_mfma_split (T <= 64, H >= 4096, with a workspace): the same
+//    16 slices of a tile spread over 2-16 workgroups, the partials added by
+//    the tile's last workgroup in the same order (bit-identical logits).
 //  * router_block (the same, when 64-expert x 64-token blocks give at least
 //    256 workgroups): 64 experts x 64 tokens per workgroup, 8 H slices.
 #include "router_dev.hpp"
