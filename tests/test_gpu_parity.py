@@ -144,6 +144,11 @@ ROUTER_ROUTE = [
                          layout="contig", BM=16, bias="zipf1.1"),
     configs.tiny().with_(name="rr_e8_t16_two_launches", T=16, H=512, I=128, E=8, E_phys=8, K=2,
                          act_dtype="bf16", M_max=16, bias="normal0.5"),
+    # 12 and 4 items: router groups of three items and of one
+    configs.tiny().with_(name="rr_e12_t1_three_items", T=1, H=2560, I=128, E=12, E_phys=12, K=3,
+                         act_dtype="f32", layout="contig", BM=16, bias="normal0.5"),
+    configs.tiny().with_(name="rr_e4_t1_one_item", T=1, H=768, I=128, E=4, E_phys=4, K=2,
+                         act_dtype="bf16", M_max=1),
 ]
 RR_KEYS = ("ids", "w", "phys", "row_of", "slot_of", "src_of", "counts", "offsets", "masked_m", "spill_off",
            "pad_off", "tile_off", "status")
