@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, vendor figure
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA, vendor figure
 
 
 def parse():
@@ -269,7 +270,7 @@ def time_workload(cfg, steps, warmup, packed=True, router="softmax", ep_ranks=1,
                routed_bytes=routed, gu_bytes=gu_bytes, total_bytes=total, status=status, setup=s,
                gu_flops=s.gate_up_flops(), layer_flops=s.layer_flops(),
                counts=s.layer.rt.counts.cpu().numpy(),
-               gu_kernel=s.B.expert_kernel(s.d, cfg.T, 0), down_kernel=s.B.expert_kernel(s.d, cfg.T, 1))
+               gu_kernel=kernel_name(s, 0), down_kernel=kernel_name(s, 1), a8=s.a8)
     del graph
     if s.fused_ok():
         # the single-launch step is reported beside the multi-launch one; a
@@ -281,6 +282,12 @@ def time_workload(cfg, steps, warmup, packed=True, router="softmax", ep_ranks=1,
             s.layer.fws.zero_()
             torch.cuda.synchronize()
     return res
+
+
+def kernel_name(s, which):
+    """The expert kernel the step runs for its largest groups (which = 0
+    gate/up, 1 down)."""
+    return (s.B.expert_kernel_a8 if s.a8 else s.B.expert_kernel)(s.d, s.cfg.T, which)
 
 
 def time_fused(s, steps, warmup, ref):
@@ -357,7 +364,9 @@ PREFILL_MIN_T = 1024   # token counts from here on are timed against the MFMA pe
 
 DEFAULT_WORKLOADS = ["mixtral_decode_b1", "mixtral_decode_b8", "mixtral_decode_b32", "mixtral_decode_b64",
                      "dsv3_decode_b32", "dsv3_decode_b128", "dsv3_decode_b256", "dsv3_prefill_t8192",
-                     "replica_decode_b256"]
+                     "dsv3_prefill_t8192_fp8", "replica_decode_b256"]
+# workloads timed on the W8A8 path (fp8 activations on fp8 MFMA) whatever --a8 says
+A8_WORKLOADS = {"dsv3_prefill_t8192_fp8"}
 HEADLINE = "mixtral_decode_b64"
 
 
@@ -396,6 +405,7 @@ def measured_traffic(workload: str, kernel: str):
 
 
 KERNEL_FILE = {"ffn_stream_kernel": "ffn_stream.hip", "ffn_tall_kernel": "ffn_tiled.hip",
+               "ffn_a8_tall_kernel": "ffn_a8_tall.hip", "ffn_a8_kernel": "ffn_a8.hip",
                "ffn_whyb_kernel": "ffn_tiled.hip", "ffn_wdma_kernel": "ffn_tiled.hip",
                "ffn_wide_kernel": "ffn_tiled.hip", "ffn_tiled_kernel": "ffn_tiled.hip"}
 
@@ -427,9 +437,9 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, cmd_prefix:
     from routing_grouped_expert_router_amd import binding as B
     cfg = configs.by_name(workload)
     d = B.Desc.from_config(cfg, w_packed=1)
-    kernel = B.expert_kernel(d, cfg.T, 0)
+    kernel = (B.expert_kernel_a8 if workload in A8_WORKLOADS else B.expert_kernel)(d, cfg.T, 0)
     mode0 = (re.compile(r"ffn_stream_kernel<(true|false), 0,") if kernel == "ffn_stream_kernel"
-             else re.compile(re.escape(kernel) + r"<0,"))
+             else re.compile(re.escape(kernel) + r"<0[,>]"))
     cal_bytes = 512 << 20
     out = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -527,11 +537,13 @@ def roofline(cfg, r, peaks):
     kernel = f"{r['gu_kernel']} gate/up (W1+W3, SwiGLU)"
     if cfg.T >= PREFILL_MIN_T:
         tf = r["gu_flops"] / (r["gu_ms"] * 1e-3) / 1e12
+        peak = FP8_PEAK_TFLOPS if r.get("a8") else BF16_PEAK_TFLOPS   # the MFMA type the kernel runs
         out = {"bound": "mfma", "kernel": kernel, "achieved": round(tf, 1),
-               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+               "peak": peak, "unit": "TFLOP/s", "frac": round(tf / peak, 4),
+               "mfma_dtype": "fp8" if r.get("a8") else "bf16",
                "traffic": measured_traffic(cfg.name, r["gu_kernel"]), "kernel_us": round(r["gu_ms"] * 1e3, 2),
                "algorithmic_flops": r["gu_flops"]}
-        if peaks:
+        if peaks and not r.get("a8"):
             out["achievable_peak"] = peaks["mfma_bf16_tflops"]
             out["frac_of_achievable"] = round(tf / peaks["mfma_bf16_tflops"], 4)
         return out
@@ -638,6 +650,7 @@ def batch_entry(r, peaks):
          "touched_slots": r["slots"],
          "touched_bytes": r["total_bytes"],
          "w_dtype": cfg.w_dtype,
+         "activations": "fp8-e4m3 1x128 (W8A8)" if r.get("a8") else "bf16",
          "status": r["status"],
          "roofline": roofline(cfg, r, peaks),
          "diagnostics": diagnostics(cfg, r, splits),
@@ -685,7 +698,7 @@ def main():
     for n in names:
         c = configs.by_name(n)
         r = time_workload(c, args.steps, args.warmup, packed=not args.row_major,
-                          router=args.router, ep_ranks=args.ep_ranks, a8=args.a8,
+                          router=args.router, ep_ranks=args.ep_ranks, a8=args.a8 or n in A8_WORKLOADS,
                           debug_flags=args.debug_flags)
         results[n] = r
         r["entry"] = batch_entry(r, peaks)

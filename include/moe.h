@@ -118,9 +118,10 @@ typedef struct {
 
 /* moe_desc_t.debug_flags.  Bits 0-3: 64-row output blocks per streaming or
  * W8A8 workgroup (1..8 and dividing N/64; 0 = the library's choice).
- * Bits 4-7: the kernel for large groups (MOE_DEBUG_TILED_*; 0 = the
- * library's choice).  Bit 8: moe_decode_fused bounds every grid-barrier wait
- * at zero polls, so a call aborts with MOE_STATUS_SYNC_TIMEOUT. */
+ * Bits 4-7: the kernel for large groups (MOE_DEBUG_TILED_* for bf16
+ * activations, MOE_DEBUG_A8_STREAM for W8A8; 0 = the library's choice).
+ * Bit 8: moe_decode_fused bounds every grid-barrier wait at zero polls, so a
+ * call aborts with MOE_STATUS_SYNC_TIMEOUT. */
 #define MOE_DEBUG_NBLK_MASK        0xFu
 #define MOE_DEBUG_TILED_SHIFT      4
 #define MOE_DEBUG_TILED_MASK       0xF0u
@@ -129,6 +130,7 @@ typedef struct {
 #define MOE_DEBUG_TILED_WIDE_LDS   3  /* 128 x 512 tile, both operands by direct-to-LDS loads */
 #define MOE_DEBUG_TILED_WIDE_HYB   4  /* 128 x 512 tile, weights to registers, activations via LDS */
 #define MOE_DEBUG_TILED_TALL       5  /* 256 x 256 tile, every wave all 256 token rows */
+#define MOE_DEBUG_A8_STREAM        6  /* W8A8: the streaming kernel for every group */
 #define MOE_DEBUG_FUSED_NO_WAIT    0x100u
 
 /* Routing tables, all device int32/float/uint32 arrays, caller-allocated.
@@ -458,6 +460,12 @@ moe_status_t moe_grouped_ffn_x(const moe_desc_t* d, const moe_weights_t* w,
  * name the kernel they time. */
 const char* moe_expert_kernel(const moe_desc_t* d, int32_t T, int32_t which);
 
+/* The same for moe_expert_gate_up_a8 (which = 0) and moe_expert_down_a8
+ * (which = 1) with route tables that hold claim counters:
+ * "ffn_a8_tall_kernel" or "ffn_a8_kernel"; "none" as above and for weights
+ * that are not fp8. */
+const char* moe_expert_kernel_a8(const moe_desc_t* d, int32_t T, int32_t which);
+
 /* ---- W8A8: fp8 activations on fp8 MFMA ------------------------------------
  * ("推理 INFRA 方法论(5)", DeepGEMM section: FP8 operands with per-128 scales
  * and two-level accumulation -- each 128-wide K block summed by the matrix
@@ -478,13 +486,21 @@ moe_status_t moe_quantize_1x128(const void* src, int64_t ld, int64_t rows, int32
 /* a6 with fp8 activations: xq / xs = moe_quantize_1x128 of the layer input x
  * [T, H]; rows are gathered by token (src_of) as moe_expert_gate_up_x does.
  * h as moe_expert_gate_up.  Decode-sized groups: a group's rows run in passes
- * of 16 (at most 16 rows) or 64, each pass streaming the group's weights. */
+ * of 16 (at most 16 rows) or 64, each pass streaming the group's weights.
+ * Groups large on average (T > 64 and T*K >= 64 E_phys, the prefill case),
+ * with packed weights, route tables holding claim counters, H a multiple of
+ * 512 (at most 16384) and I of 128: one persistent launch over 256-row tiles
+ * of every group, each weight tile read once per 256 rows (the DeepGEMM
+ * section's contiguous layout with large tiles).  Both kernels give the same
+ * bits. */
 moe_status_t moe_expert_gate_up_a8(const moe_desc_t* d, const moe_weights_t* w,
                                    const moe_route_t* r, int32_t T, const void* xq,
                                    const float* xs, void* h, hipStream_t stream);
 
 /* a7 with fp8 activations: hq / hs = moe_quantize_1x128 of h over its
- * moe_buffer_rows(d) rows (C = I).  y as moe_expert_down (same K split). */
+ * moe_buffer_rows(d) rows (C = I).  y as moe_expert_down (same K split).
+ * The large-group kernel as for gate/up, where the call has no K split, I
+ * is a multiple of 512 and H of 128. */
 moe_status_t moe_expert_down_a8(const moe_desc_t* d, const moe_weights_t* w,
                                 const moe_route_t* r, int32_t T, const void* hq,
                                 const float* hs, void* y, hipStream_t stream);

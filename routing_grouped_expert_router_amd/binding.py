@@ -25,6 +25,7 @@ MOE_EP_LINEAR, MOE_EP_ROUND_ROBIN = 0, 1
 MOE_DEBUG_NBLK_MASK, MOE_DEBUG_TILED_SHIFT, MOE_DEBUG_FUSED_NO_WAIT = 0xF, 4, 0x100
 MOE_DEBUG_TILED_NARROW, MOE_DEBUG_TILED_WIDE_REGS, MOE_DEBUG_TILED_WIDE_LDS, MOE_DEBUG_TILED_WIDE_HYB = 1, 2, 3, 4
 MOE_DEBUG_TILED_TALL = 5
+MOE_DEBUG_A8_STREAM = 6
 
 EXPORTED = [
     "moe_status_string", "moe_check_desc", "moe_route_workspace_bytes", "moe_buffer_rows",
@@ -37,7 +38,7 @@ EXPORTED = [
     "moe_replica_map_from_p2l", "moe_route_ep", "moe_route_received", "moe_ep_local_map",
     "moe_eplb_plan", "moe_quantize_1x128", "moe_expert_gate_up_a8", "moe_expert_down_a8",
     "moe_grouped_ffn_a8", "moe_decode_fused_workspace_bytes", "moe_decode_fused",
-    "moe_expert_kernel", "moe_probe_read", "moe_probe_mfma_bf16", "moe_route_noalloc", "moe_router_route",
+    "moe_expert_kernel", "moe_expert_kernel_a8", "moe_probe_read", "moe_probe_mfma_bf16", "moe_route_noalloc", "moe_router_route",
 ]
 MOE_NOALLOC_WORKSPACE_BYTES = 4 << 20
 MOE_PROBE_SINK_WORDS = 8192
@@ -127,6 +128,7 @@ def lib() -> ctypes.CDLL:
             "moe_grouped_ffn_a8": (ctypes.c_int, [D, W, R, i32, _P, _P, _P, _P, _P, _P, _P, _P]),
             "moe_decode_fused_workspace_bytes": (sz, [D]),
             "moe_expert_kernel": (ctypes.c_char_p, [D, i32, i32]),
+            "moe_expert_kernel_a8": (ctypes.c_char_p, [D, i32, i32]),
             "moe_probe_read": (ctypes.c_int, [_P, sz, _P, _P]),
             "moe_probe_mfma_bf16": (ctypes.c_int, [i32, i32, _P, _P]),
             "moe_decode_fused": (ctypes.c_int, [D, _P, _P, _P, GR, _P, _P, W, i32, _P, R, _P, sz, _P, _P,
@@ -235,6 +237,11 @@ def expert_kernel(d: Desc, T: int, which: int) -> str:
     """Name of the kernel the expert call runs for the largest groups
     (which = 0 gate/up, 1 down)."""
     return lib().moe_expert_kernel(ctypes.byref(d.c()), T, which).decode()
+
+
+def expert_kernel_a8(d: Desc, T: int, which: int) -> str:
+    """The same for the W8A8 expert calls."""
+    return lib().moe_expert_kernel_a8(ctypes.byref(d.c()), T, which).decode()
 
 
 # ---- measurement probes (include/moe_probe.h) ---------------------------------

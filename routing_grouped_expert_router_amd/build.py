@@ -25,6 +25,16 @@ HIP_FLAGS = [
 ]
 
 
+# extra flags of single translation units
+FILE_FLAGS = {
+    # MFMA results in ordinary VGPRs: the W8A8 large-group kernel scales every
+    # 128-wide block sum with VALU instructions, which cannot read the
+    # accumulation registers the compiler otherwise gives the results (each
+    # would take a copy first)
+    "ffn_a8_tall.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -40,7 +50,7 @@ def build(verbose: bool = False) -> str:
     procs = []
     for s in srcs:
         o = os.path.join(objdir, os.path.basename(s) + ".o")
-        cmd = [hipcc(), *HIP_FLAGS, "-c", s, "-o", o]
+        cmd = [hipcc(), *HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(s), []), "-c", s, "-o", o]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((s, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

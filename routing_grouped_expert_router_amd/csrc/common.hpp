@@ -64,6 +64,14 @@ __device__ __forceinline__ void fp8x16_to_bf16(const u32x4 q, bf16x8& a0, bf16x8
   a1 = __builtin_bit_cast(bf16x8, v1);
 }
 
+// Raw buffer resource over [p, p + bytes): loads take a 32-bit per-lane
+// offset and a wave-uniform 32-bit offset, so the K step moves a scalar only
+// (no per-load 64-bit address arithmetic or address registers), and a load
+// past `bytes` returns zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 // ---- MFMA ---------------------------------------------------------------
 // v_mfma_f32_16x16x32_bf16: D[16x16] += A[16x32] * B[32x16].
 // Lane l supplies A row (l % 16), B column (l % 16), each with 8 K values

@@ -1,0 +1,357 @@
+// W8A8 expert projections for large groups (prefill) on gfx950: fp8
+// (E4M3FN) weights and activations, fp8 MFMA, per-128 block scales, the
+// block sums promoted to fp32 ("推理 INFRA 方法论(5)", DeepGEMM section: FP8
+// operands with per-128 scales, each 128-wide K block summed on the matrix
+// unit and accumulated in fp32 after scaling; prefill groups in the
+// contiguous layout with large tiles).
+//
+//  * Work item: 256 token rows of one group x 128 weight rows (MODE_GATEUP:
+//    64 rows of W1 and the same 64 rows of W3, so SiLU(g) * u pairs sit in one
+//    lane; MODE_DOWN: 128 rows of W2), from the persistent claim schedule of
+//    tile_sched.hpp.  Each of the four waves owns all 256 token rows x 32
+//    weight rows (two 16-row panels: W1 and W3 of the same rows, or two of
+//    W2), 16 x 2 MFMA tiles of 16 x 16, so a partly full tile shortens every
+//    wave alike.
+//  * K runs in 128-wide stages.  Per (row tile, panel) and stage one
+//    v_mfma_scale_f32_16x16x128_f8f6f4 with unit E8M0 scales gives the block
+//    sum, which is multiplied by the weight block's scale times the token's
+//    and added to an fp32 accumulator, K blocks in ascending order: the
+//    streaming W8A8 kernel's arithmetic, operand for operand, so both give
+//    the same bits.
+//  * Activation codes (32 KiB a stage, 16-byte pieces in MFMA lane order) and
+//    their scales (1 KiB) go by direct-to-LDS loads into a ring of four
+//    stages, three ahead; every wave reads all 16 row tiles' fragments from
+//    it, each feeding its two panels' products.
+//  * Weights go straight to registers (each fragment is read by one wave),
+//    four banks, three stages ahead.  The item's weight-block scales (a row
+//    of K blocks per matrix) go to LDS by direct loads at its start.
+//  * A stage's 13 loads per wave are issued one after each row tile's
+//    products, so they never queue in a burst behind the MFMAs, and each
+//    tile's promotion runs under the next tile's products.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "tile_sched.hpp"
+
+namespace moe {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kAThreads = 256;
+constexpr int kAM = kTileRows;              // token rows per work item
+constexpr int kAMT = kAM / 16;              // 16-row MFMA tiles per item
+constexpr int kAN = 128;                    // weight rows per item
+constexpr int kAStages = 4;                 // LDS ring slots of 128-wide K stages
+constexpr int kAXBytes = kAM * 128;         // a stage's activation codes (32 KiB)
+constexpr int kASlot = kAXBytes + kAM * 4;  // + their 256 scales
+constexpr int kAMaxKb = 128;                // K blocks a weight-scale row in LDS holds
+constexpr int kALoads = 13;                 // loads per wave and stage: 8 codes, 1 scales, 4 weights
+constexpr int kAAhead = 2;                  // row tiles whose fragments are read ahead of their products
+constexpr int kPromoteValu = 10;            // VALU instructions of a tile's promotion
+static_assert(kAM == 256 && kAMT == 16, "an item is 16 row tiles");
+static_assert(kALoads <= kAMT, "a stage's loads fit its row-tile steps");
+static_assert(kAMaxKb == 128, "two 64-word halves per weight-scale row, one per wave");
+
+__device__ __forceinline__ float a8t_silu(float g) { return g / (1.0f + __expf(-g)); }
+
+__device__ __forceinline__ i32x8 join8(const u32x4 lo, const u32x4 hi) {
+  return __builtin_bit_cast(i32x8, u32x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w});
+}
+
+// One work item: rows m0 = 256 mt .. of group tw.g against weight tile tw.nt.
+// at_loop_end() runs once the K loop is done, before the epilogue.
+template <int MODE, typename Hook>
+__device__ __forceinline__ void a8_tall_tile(const A8TallArgs& ta, const TileWork& tw, char* r0, char* r1,
+                                             char* r2, char* r3, float* wsc, Hook at_loop_end) {
+  constexpr bool GU = MODE == MODE_GATEUP;
+  const A8Args& a = ta.s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lr = lane & 15, lg = lane >> 4;
+  const int g = tw.g, c0 = tw.c0, R = tw.R;
+  const int64_t s0 = tw.s0, s1 = tw.s1;
+  const int m0 = tw.mt * kAM;                  // first row of the item within the group
+  const int N = a.N, Kdim = a.Kdim, nkb = Kdim / 128;
+  const int n0 = GU ? tw.nt * (kAN / 2) : tw.nt * kAN;   // first output column (weight row) of the item
+
+  const uint8_t* Wa;
+  const uint8_t* Wb;
+  const float* Sa;
+  const float* Sb;
+  if (tw.shared) {
+    Wa = a.SW; Wb = GU ? a.SW3 : a.SW;
+    Sa = a.SS; Sb = GU ? a.SS3 : a.SS;
+  } else {
+    Wa = a.W + (int64_t)g * N * Kdim;
+    Wb = GU ? a.W3 + (int64_t)g * N * Kdim : Wa;
+    Sa = a.S + (int64_t)g * (N / 128) * nkb;
+    Sb = GU ? a.S3 + (int64_t)g * (N / 128) * nkb : Sa;
+  }
+  const __amdgpu_buffer_rsrc_t wra = buffer_rsrc(Wa, (uint32_t)N * Kdim);
+  const __amdgpu_buffer_rsrc_t wrb = buffer_rsrc(Wb, (uint32_t)N * Kdim);
+  const __amdgpu_buffer_rsrc_t xrs = buffer_rsrc(a.X, (uint32_t)(ta.x_rows * a.ldx));
+  const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(a.XS, (uint32_t)(ta.x_rows * nkb * 4));
+  // this wave's two 16-row weight panels (packed layout: per K block, panel
+  // p's 2 KiB at p * 2048, lane l's 16 bytes of half j at j * 1024 + 16 l)
+  const int pn0 = GU ? (n0 + 16 * wave) / 16 : (n0 + 32 * wave) / 16;
+  const int pn1 = GU ? pn0 : pn0 + 1;
+  const uint32_t pw[2] = {(uint32_t)pn0 * 2048 + lane * 16, (uint32_t)pn1 * 2048 + lane * 16};
+  const uint32_t kbytes = (uint32_t)N * 128;   // one K block of the packed layout
+
+  // activation rows: the four row tiles of codes this wave loads (wave + 4 q;
+  // lane: row lr, K bytes 16 lg + 64 j), then the row of its scale word
+  // (word p = 64 wave + lane of the slot's scale block is row tile p % 16,
+  // row p / 16 of it, so lane (lr) reads its tiles 4q..4q+3 as one 16
+  // bytes).  Rows past the group read a valid row, never used.  The gather
+  // indices load together, under one wait.
+  int rk[5];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) rk[q] = m0 + (wave + 4 * q) * 16 + lr;
+  rk[4] = m0 + 16 * lr + 4 * wave + lg;
+  int64_t rw[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) rk[i] = rk[i] < R ? rk[i] : 0;
+  if (a.gather_src && !tw.shared) {
+    const int32_t* gs = a.gather_src + a.gather_off[g];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) rw[i] = gs[rk[i]];
+  } else if (a.gather_src) {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) rw[i] = rk[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) rw[i] = rk[i] < c0 ? s0 + rk[i] : s1 + (rk[i] - c0);
+  }
+  uint32_t xoff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) xoff[q] = (uint32_t)(rw[q] * a.ldx) + 16 * lg;
+  const uint32_t soff = (uint32_t)(rw[4] * nkb * 4);
+
+  const int rows_here = min(kAM, R - m0);
+  const int mv = ((rows_here + 31) / 32) * 2;   // non-empty 16-row tiles, in pairs
+  auto run = [&](auto mvc) -> void {
+    constexpr int MV = decltype(mvc)::value;
+    auto slot = [&](auto sc) -> char* {
+      constexpr int S = decltype(sc)::value;
+      return S == 0 ? r0 : S == 1 ? r1 : S == 2 ? r2 : r3;
+    };
+    // load i (0..12) of stage st (clamped past the end: re-read, never used):
+    // 0..7 codes of row tile wave + 4 (i / 2), half i % 2, into ring slot S;
+    // 8 the scales; 9..12 weights of panel (i - 9) / 2, half (i - 9) % 2
+    u32x4 wb[kAStages][2][2];
+    auto issue = [&](int i, char* sl, u32x4 (*b)[2], int st) -> void {
+      const int stc = st < nkb ? st : nkb - 1;
+      if (i < 8) {
+        const int q = i >> 1, j = i & 1;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, sl + ((wave + 4 * q) * 2 + j) * 1024, 16, xoff[q],
+                                                 (uint32_t)stc * 128 + 64 * j, 0, 0);
+      } else if (i == 8) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, sl + kAXBytes + wave * 256, 4, soff, (uint32_t)stc * 4,
+                                                 0, 0);
+      } else if (i < kALoads) {
+        const int n = (i - 9) >> 1, j = (i - 9) & 1;
+        b[n][j] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(n ? wrb : wra, (int)pw[n], (int)(stc * kbytes + j * 1024), 0));
+      }
+    };
+    f32x4 acc[MV][2];
+#pragma unroll
+    for (int m = 0; m < MV; ++m) acc[m][0] = acc[m][1] = f32x4{0, 0, 0, 0};
+    // prologue: stages 0..2, weights first (a wait the compiler places
+    // before the first load into a register then covers the previous
+    // item's stores only), and after stage 0's weights the item's
+    // weight-block scales, one direct load per wave: wsc[k] of W1 (W2),
+    // wsc[kAMaxKb + k] of W3 (for the down projection waves 2 and 3 load the
+    // W2 row again into the unused half)
+#pragma unroll
+    for (int i = 9; i < kALoads; ++i) issue(i, r0, wb[0], 0);
+    {
+      const int mat = wave >> 1, c = (wave & 1) * 64;
+      const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(GU && mat ? Sb : Sa, (uint32_t)(N / 128) * nkb * 4);
+      const uint32_t o = (uint32_t)((n0 / 128) * nkb + min(c + lane, nkb - 1)) * 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, wsc + mat * kAMaxKb + c, 4, o, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 9; ++i) issue(i, r0, wb[0], 0);
+    __builtin_amdgcn_sched_barrier(0);          // each stage's loads before the next stage's
+#pragma unroll
+    for (int i = 9; i < kALoads; ++i) issue(i, r1, wb[1], 1);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) issue(i, r1, wb[1], 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 9; i < kALoads; ++i) issue(i, r2, wb[2], 2);
+#pragma unroll
+    for (int i = 0; i < 9; ++i) issue(i, r2, wb[2], 2);
+    __builtin_amdgcn_sched_barrier(0);
+    // at the top of stage st the loads issued after stage st's are those of
+    // st + 1 and st + 2: vmcnt(2 * kALoads) means this wave's loads of stage
+    // st (and, before stage 0, the weight scales) have landed
+    constexpr int kVm = 2 * kALoads;
+    constexpr int kWait = (kVm & 15) | ((kVm >> 4) << 14) | 0x70 | 0xF00;
+    auto stage = [&](auto sc, auto nc, int st) -> void {
+      constexpr int S = decltype(sc)::value;
+      u32x4 (*wc)[2] = wb[S];
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(kWait);       // this wave's loads of stage st landed
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): its reads of stage st - 1 are done
+      __builtin_amdgcn_s_barrier();            // every wave's: stage st readable, slot of st - 1 free
+      const char* xs = slot(sc);
+      const i32x8 w0 = join8(wc[0][0], wc[0][1]), w1 = join8(wc[1][0], wc[1][1]);
+      const float sw0 = wsc[st], sw1 = GU ? wsc[kAMaxKb + st] : sw0;
+      // activation scale of row tile m (this lane's token), read just before
+      // its promotion
+      auto xscale = [&](int m) -> float {
+        return *reinterpret_cast<const float*>(xs + kAXBytes + (lr * 16 + m) * 4);
+      };
+      auto frag = [&](int m) -> i32x8 {
+        return join8(*reinterpret_cast<const u32x4*>(xs + (m * 2) * 1024 + lane * 16),
+                     *reinterpret_cast<const u32x4*>(xs + (m * 2 + 1) * 1024 + lane * 16));
+      };
+      i32x8 xf[kAAhead + 1];
+#pragma unroll
+      for (int m = 0; m < kAAhead && m < MV; ++m) xf[m] = frag(m);
+      f32x4 dp0, dp1;                          // block sums of the previous row tile
+      const f32x4 zero = {0, 0, 0, 0};
+#pragma unroll
+      for (int m = 0; m < kAMT; ++m) {
+        if (m < MV) {
+          if (m + kAAhead < MV) xf[(m + kAAhead) % (kAAhead + 1)] = frag(m + kAAhead);
+          const i32x8 x = xf[m % (kAAhead + 1)];
+          const f32x4 d0 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w0, x, zero, 0, 0, 0, 127, 0, 127);
+          const f32x4 d1 = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w1, x, zero, 0, 0, 0, 127, 0, 127);
+          if (m > 0) {
+            const float sxp = xscale(m - 1);
+            acc[m - 1][0] += dp0 * (sw0 * sxp);
+            acc[m - 1][1] += dp1 * (sw1 * sxp);
+          }
+          dp0 = d0;
+          dp1 = d1;
+        }
+        if (m < kALoads) issue(m, slot(nc), wb[decltype(nc)::value], st + kAStages - 1);
+      }
+      const float sxl = xscale(MV - 1);
+      acc[MV - 1][0] += dp0 * (sw0 * sxl);
+      acc[MV - 1][1] += dp1 * (sw1 * sxl);
+      // The stage is one scheduling region laid out as a pipeline: the
+      // scale reads, then per row tile its fragment reads (two tiles ahead),
+      // its two products each followed by VALU work -- the promotion of the
+      // tile before, whose products have finished by then -- and one of the
+      // next stage's loads.  (Left to itself the compiler put each tile's
+      // promotion right behind its own products, so the wave waited for the
+      // matrix core and then kept it idle through the promotion.)
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 + 2 * kAAhead, 0);   // DS reads
+#pragma unroll
+      for (int m = 0; m < MV; ++m) {
+        if (m + kAAhead < MV) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // fragment, scale
+        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kPromoteValu / 2, 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kPromoteValu / 2, 0);
+        if (m < kALoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int sb = 0; sb < nkb; sb += kAStages) {
+      stage(IntC<0>{}, IntC<3>{}, sb);
+      stage(IntC<1>{}, IntC<0>{}, sb + 1);
+      stage(IntC<2>{}, IntC<1>{}, sb + 2);
+      stage(IntC<3>{}, IntC<2>{}, sb + 3);
+    }
+    // no load may land in LDS after the workgroup has ended, nor in the
+    // ring once the epilogue reuses it
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    at_loop_end();
+
+    // ---- epilogue: acc[m][n] holds D[row 4 lg + i of panel n][token lr of tile m].
+    // bf16 outputs go through the ring: every lane writes its values, then
+    // the workgroup stores whole 16-byte pieces of the valid rows.
+    constexpr int kOutCols = GU ? kAN / 2 : kAN;          // h: 64, y: 128 columns
+    constexpr int kPieces = kOutCols / 8;                  // 16-byte pieces per row
+    constexpr int kSlotRows = kAXBytes / (kOutCols * 2);   // rows per ring slot
+    auto piece_ptr = [&](int r, int pc) -> uint16_t* {
+      const int sl = r / kSlotRows;
+      char* base = sl == 0 ? r0 : sl == 1 ? r1 : sl == 2 ? r2 : r3;
+      return reinterpret_cast<uint16_t*>(base) + (r % kSlotRows) * kOutCols + ((pc + r) % kPieces) * 8;
+    };
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+      const int r = m * 16 + lr;
+      if constexpr (GU) {
+        const f32x4 gt = acc[m][0], up = acc[m][1];
+        const int col = 16 * wave + 4 * lg;
+        const u32x2 o = {pack_bf16x2(a8t_silu(gt.x) * up.x, a8t_silu(gt.y) * up.y),
+                         pack_bf16x2(a8t_silu(gt.z) * up.z, a8t_silu(gt.w) * up.w)};
+        *reinterpret_cast<u32x2*>(piece_ptr(r, col / 8) + col % 8) = o;
+      } else {
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const int col = 32 * wave + 16 * n + 4 * lg;
+          const u32x2 o = {pack_bf16x2(acc[m][n].x, acc[m][n].y), pack_bf16x2(acc[m][n].z, acc[m][n].w)};
+          *reinterpret_cast<u32x2*>(piece_ptr(r, col / 8) + col % 8) = o;
+        }
+      }
+    }
+    __syncthreads();
+    const int rows = min(rows_here, MV * 16);
+    for (int i = tid; i < rows * kPieces; i += kAThreads) {
+      const int r = i / kPieces, pc = i % kPieces;
+      const int gr = m0 + r;
+      const int64_t row = gr < c0 ? s0 + gr : s1 + (gr - c0);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(piece_ptr(r, pc));
+      *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.out) + row * a.ldo + n0 + pc * 8) = v;
+    }
+    __syncthreads();             // the next item's loads refill this LDS
+  };
+  switch (mv) {
+    case 2: run(IntC<2>{}); break;
+    case 4: run(IntC<4>{}); break;
+    case 6: run(IntC<6>{}); break;
+    case 8: run(IntC<8>{}); break;
+    case 10: run(IntC<10>{}); break;
+    case 12: run(IntC<12>{}); break;
+    case 14: run(IntC<14>{}); break;
+    default: run(IntC<16>{}); break;
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kAThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ffn_a8_tall_kernel(A8TallArgs ta) {
+  __shared__ __attribute__((aligned(16))) char r0[kASlot];
+  __shared__ __attribute__((aligned(16))) char r1[kASlot];
+  __shared__ __attribute__((aligned(16))) char r2[kASlot];
+  __shared__ __attribute__((aligned(16))) char r3[kASlot];
+  __shared__ __attribute__((aligned(16))) float wsc[2 * kAMaxKb];
+  const int ntn = ta.s.N / (MODE == MODE_GATEUP ? kAN / 2 : kAN);   // weight tiles per row tile
+  claim_units<kAThreads>(ta.s, ta.tile_off, ta.claim, ntn, [&](const TileWork& tw, auto at_loop_end) {
+    a8_tall_tile<MODE>(ta, tw, r0, r1, r2, r3, wsc, at_loop_end);
+  });
+}
+
+// Whole 128-row output tiles (64 for gate/up), a K range of whole blocks of
+// four 128-wide stages that the scale rows in LDS hold, no K split, the
+// route table's claim counters, and 32-bit buffer offsets.
+bool a8_tall_supported(int mode, const A8TallArgs& a) {
+  const A8Args& s = a.s;
+  const int wn = mode == MODE_GATEUP ? kAN / 2 : kAN;
+  if (s.N <= 0 || s.N % wn || s.N % 128 || s.Kdim <= 0 || s.Kdim % (128 * kAStages) || s.Kdim / 128 > kAMaxKb)
+    return false;
+  if (s.ksplit != 1 || s.out_f32 || s.ldx < s.Kdim || s.ldx % 16) return false;
+  if (!a.claim || !a.tile_off || s.E_phys > kPlanGroups || a.x_rows <= 0) return false;
+  const int64_t lim = int64_t(1) << 31;
+  return (int64_t)s.N * s.Kdim < lim && a.x_rows * s.ldx < lim && a.x_rows * (s.Kdim / 128) * 4 < lim;
+}
+
+hipError_t launch_ffn_a8_tall(const A8TallArgs& a, int mode, hipStream_t s) {
+  const int cus = device_cus();
+  if (!a8_tall_supported(mode, a) || cus < kClaimLists) return hipErrorInvalidValue;
+  const dim3 grid(cus);
+  if (mode == MODE_GATEUP) hipLaunchKernelGGL((ffn_a8_tall_kernel<MODE_GATEUP>), grid, dim3(kAThreads), 0, s, a);
+  else hipLaunchKernelGGL((ffn_a8_tall_kernel<MODE_DOWN>), grid, dim3(kAThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -43,6 +43,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "tile_sched.hpp"
 
 namespace moe {
 
@@ -70,32 +71,6 @@ __device__ __forceinline__ float silu_t(float g) { return g / (1.0f + __expf(-g)
 __device__ __forceinline__ int swz(int lane, int j) {
   const int c = 4 * j + (lane >> 4);
   return (lane & 48) | (((lane & 15) + 2 * c) & 15);
-}
-
-// One work item of the tiled kernels: group g, weight-row tile nt, row tile mt
-// and the group's row segments (s0, c0 rows, then s1, c1 spill rows).
-struct TileWork {
-  int g, nt, mt, c0, c1, R;
-  int64_t s0, s1;
-  bool shared;
-};
-
-// The rows of group g (slot g, or the shared expert as group E_phys): the
-// segment s0 of c0 rows, then the spill segment s1 of c1 rows.
-__device__ __forceinline__ void group_rows(const StreamArgs& a, int g, TileWork& w) {
-  w.g = g;
-  w.s0 = w.s1 = 0;
-  w.c0 = w.c1 = 0;
-  w.shared = g == a.E_phys;
-  if (w.shared) { w.s0 = a.shared_base; w.c0 = a.T; }
-  else if (a.layout == MOE_MASKED) {
-    const int mm = a.masked_m[g];
-    w.s0 = (int64_t)g * a.M_max; w.c0 = mm;
-    w.s1 = (int64_t)a.E_phys * a.M_max + a.spill_off[g]; w.c1 = a.counts[g] - mm;
-  } else {
-    w.s0 = a.pad_off[g]; w.c0 = a.counts[g];
-  }
-  w.R = w.c0 + w.c1;
 }
 
 // The hardware deals workgroups round-robin over the 8 XCDs (linear id L goes
@@ -330,13 +305,6 @@ constexpr int kWN = 512;                 // weight rows per tile
 constexpr int kWBanks = 3;
 constexpr int kWStage = kTM * 32 * 2;    // 8 KiB: 128 rows x 32 K
 
-// Raw buffer resource over [p, p + bytes): loads take a 32-bit per-lane
-// offset and a wave-uniform 32-bit offset, so the K step moves a scalar only
-// (no per-load 64-bit address arithmetic or address registers), and a load
-// past `bytes` returns zero instead of touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
@@ -1240,27 +1208,8 @@ __device__ __forceinline__ void tall_tile(const TiledArgs& ta, const TileWork& t
   }
 }
 
-// Persistent schedule of the tall kernel (ffn_tall_kernel<..., true>): one
-// workgroup per compute unit, workgroup b serving first the work list of
-// XCD x = b % 8 (the hardware deals linear workgroup ids to the XCDs in
-// turn).  List x holds whole groups: first an eighth of the shared expert's
-// row tiles, then slots x, x + 8, x + 16, ...  Its units are (row tile,
-// weight tile) pairs, group by group, and inside a group weight tile major,
-// row tile minor, so the row tiles of one group that read the same weights
-// run close together on one XCD and the repeated weight reads can hit the
-// memory-side cache, while the weight tiles of one row tile follow each
-// other and share its activations in L2.  A workgroup claims its next unit with an atomic add on its list's
-// counter, so faster compute units take more units; once its list is empty
-// it claims from the other lists in turn.  The last workgroup to finish sets
-// the counters back to zero.  Every workgroup computes the lists' prefix of
-// row tiles from tile_off, in LDS, at start.
-constexpr int kClaimLists = 8;
-constexpr int kClaimStride = 16;                     // words between list counters (64-byte lines)
-constexpr int kClaimDone = kClaimLists * kClaimStride;
-static_assert(kClaimDone < MOE_CLAIM_WORDS, "claim counters fit the route table");
-constexpr int kPlanGroups = 768;                     // largest E_phys the schedule holds
-constexpr int kListChunks = kPlanGroups / kClaimLists + 1;   // groups per list (shared part first)
-
+// PERSIST: the claim schedule of claim_units(), one workgroup per compute
+// unit; else one workgroup per work item (decode_work).
 template <int MODE, bool OUTF32, bool PERSIST>
 __global__ __launch_bounds__(kTThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void ffn_tall_kernel(TiledArgs ta) {
@@ -1274,91 +1223,10 @@ void ffn_tall_kernel(TiledArgs ta) {
     if (!decode_work(ta, tw)) return;
     tall_tile<MODE, OUTF32>(ta, tw, x0s, x1s, x2s, x3s);
   } else {
-    // lt[x * L + c]: row tiles of chunk c of list x (chunk 0 the shared
-    // expert's part, chunk c > 0 slot x + 8 (c - 1)), then their exclusive
-    // prefix over all lists
-    __shared__ int lt[kClaimLists * kListChunks + 1];
-    __shared__ int scan_tmp[kTThreads / 64 + 1];
-    __shared__ int claim_s;
-    const StreamArgs& a = ta.s;
-    const int P = a.E_phys;
-    const int L = (P + kClaimLists - 1) / kClaimLists + 1;
-    const int ts = ta.tile_off[P + 1] - ta.tile_off[P];          // the shared expert's row tiles
-    const int cs = (ts + kClaimLists - 1) / kClaimLists;          // of them per list
-    for (int i = threadIdx.x; i < kClaimLists * L; i += kTThreads) {
-      const int x = i / L, c = i - x * L;
-      int t;
-      if (c == 0) {
-        t = ts - x * cs;
-        t = t < 0 ? 0 : (t > cs ? cs : t);
-      } else {
-        const int g = x + kClaimLists * (c - 1);
-        t = g < P ? ta.tile_off[g + 1] - ta.tile_off[g] : 0;
-      }
-      lt[i] = t;
-    }
-    __syncthreads();
-    const int total = block_exclusive_scan(lt, kClaimLists * L, scan_tmp);
-    if (threadIdx.x == 0) lt[kClaimLists * L] = total;
-    __syncthreads();
-    const int ntn = a.N / (MODE == MODE_GATEUP ? kQN / 2 : kQN);   // weight tiles per row tile
-
-    auto claim = [&](int x) -> int {                 // thread 0's claim on list x
-      return (int)__hip_atomic_fetch_add(ta.claim + x * kClaimStride, 1u, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    };
-    auto broadcast = [&](int v) -> int {             // thread 0's value to the workgroup
-      if (threadIdx.x == 0) claim_s = v;
-      __syncthreads();
-      const int r = __builtin_amdgcn_readfirstlane(claim_s);
-      __syncthreads();                               // claim_s is rewritten only after every read
-      return r;
-    };
-    const int home = blockIdx.x % kClaimLists;
-    int s = 0, x = home;
-    int u = broadcast(threadIdx.x == 0 ? claim(x) : 0);
-    for (;;) {
-      const int* pl = lt + x * L;                    // list x: chunk prefixes pl[0..L], pl[L] its end
-      const int base = pl[0];
-      if (u >= (pl[L] - base) * ntn) {               // list x is empty: the next one
-        if (++s == kClaimLists) break;
-        x = (home + s) % kClaimLists;
-        u = broadcast(threadIdx.x == 0 ? claim(x) : 0);
-        continue;
-      }
-      int lo = 0, hi = L;                            // the chunk holding unit u: largest c with
-      while (hi - lo > 1) {                          // (pl[c] - base) * ntn <= u
-        const int mid = (lo + hi) >> 1;
-        if ((pl[mid] - base) * ntn <= u) lo = mid; else hi = mid;
-      }
-      const int tc = pl[lo + 1] - pl[lo];            // row tiles of the chunk (> 0: it holds u)
-      const int v = u - (pl[lo] - base) * ntn;
-      const int nt = v / tc;                         // weight tile major,
-      const int t = v - nt * tc;                     // row tile minor
-      TileWork tw;
-      if (lo == 0) {
-        group_rows(a, P, tw);
-        tw.mt = x * cs + t;
-      } else {
-        group_rows(a, x + kClaimLists * (lo - 1), tw);
-        tw.mt = t;
-      }
-      tw.nt = nt;
-      int next = 0;
-      tall_tile<MODE, OUTF32>(ta, tw, x0s, x1s, x2s, x3s, [&]() -> void {
-        if (threadIdx.x == 0) next = claim(x);
-      });
-      u = broadcast(next);
-    }
-    // every workgroup has made its last claim once the done count reaches the
-    // grid; the last one zeroes the counters for the next launch
-    if (threadIdx.x == 0 &&
-        __hip_atomic_fetch_add(ta.claim + kClaimDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-            gridDim.x - 1) {
-      for (int xx = 0; xx < kClaimLists; ++xx)
-        __hip_atomic_store(ta.claim + xx * kClaimStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(ta.claim + kClaimDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    const int ntn = ta.s.N / (MODE == MODE_GATEUP ? kQN / 2 : kQN);   // weight tiles per row tile
+    claim_units<kTThreads>(ta.s, ta.tile_off, ta.claim, ntn, [&](const TileWork& tw, auto at_loop_end) {
+      tall_tile<MODE, OUTF32>(ta, tw, x0s, x1s, x2s, x3s, at_loop_end);
+    });
   }
 }
 

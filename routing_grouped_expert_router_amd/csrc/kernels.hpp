@@ -161,6 +161,19 @@ struct A8Args {
 };
 hipError_t launch_ffn_a8(const A8Args& a, int packed, int mode, hipStream_t s);
 
+// W8A8 for large groups: one persistent launch over every group's
+// (256-row tile, weight tile) units, packed weights, no K split.
+struct A8TallArgs {
+  A8Args s;
+  const int32_t* tile_off;   // [E_phys + 2] prefix of ceil(rows / kTileRows) per group
+  uint32_t* claim;           // [MOE_CLAIM_WORDS] work-claim counters, zero on entry and on exit
+  int64_t x_rows;            // rows of X and XS the launch may address
+};
+bool a8_tall_supported(int mode, const A8TallArgs& a);
+// compute units of the current device (0 if the query fails)
+int device_cus();
+hipError_t launch_ffn_a8_tall(const A8TallArgs& a, int mode, hipStream_t s);
+
 // ---- router logits --------------------------------------------------------------
 
 struct RouterArgs {

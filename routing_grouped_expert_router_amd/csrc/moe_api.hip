@@ -110,7 +110,7 @@ moe_status_t moe_check_desc(const moe_desc_t* d) {
   if ((int64_t)d->T_max * d->K > (int64_t)INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
   const uint32_t dbg = (uint32_t)d->debug_flags;
   if (dbg & ~(MOE_DEBUG_NBLK_MASK | MOE_DEBUG_TILED_MASK | MOE_DEBUG_FUSED_NO_WAIT)) return MOE_ERR_ARG;
-  if ((dbg & MOE_DEBUG_NBLK_MASK) > 8 || ((dbg & MOE_DEBUG_TILED_MASK) >> MOE_DEBUG_TILED_SHIFT) > kTiledVariants)
+  if ((dbg & MOE_DEBUG_NBLK_MASK) > 8 || ((dbg & MOE_DEBUG_TILED_MASK) >> MOE_DEBUG_TILED_SHIFT) > MOE_DEBUG_A8_STREAM)
     return MOE_ERR_ARG;
   return MOE_OK;
 }
@@ -418,6 +418,13 @@ struct GemmPlan {
   bool all_tiled;  // every group in the tiled launch, no streaming launch
 };
 
+// The bf16 large-group kernel that debug_flags forces (0: the library's
+// choice; the W8A8 switch MOE_DEBUG_A8_STREAM leaves the choice alone).
+int tiled_variant(const moe_desc_t* d) {
+  const int v = (int)(((uint32_t)d->debug_flags & MOE_DEBUG_TILED_MASK) >> MOE_DEBUG_TILED_SHIFT);
+  return v <= kTiledVariants ? v : 0;
+}
+
 GemmPlan plan_expert_gemm(const moe_desc_t* d, int32_t T, const StreamArgs& a, bool fp8, int mode) {
   GemmPlan p;
   p.mt = stream_mt(d, T);
@@ -480,7 +487,7 @@ moe_status_t launch_expert_gemm(const moe_desc_t* d, const moe_route_t* r, int32
   ta.s = a;
   ta.tile_off = r->tile_off;
   ta.claim = r->claim;
-  ta.variant = (int)(((uint32_t)d->debug_flags & MOE_DEBUG_TILED_MASK) >> MOE_DEBUG_TILED_SHIFT);
+  ta.variant = tiled_variant(d);
   ta.min_rows = all_tiled ? 0 : (mt < 4) ? 64 : a_max;
   // X holds the layer input (T rows) when gathering, else the grouped buffer
   ta.x_bytes = (a.gather_src ? (int64_t)T : moe_buffer_rows(d)) * a.ldx * 2;
@@ -610,7 +617,7 @@ const char* moe_expert_kernel(const moe_desc_t* d, int32_t T, int32_t which) {
   TiledArgs ta = {};
   ta.s = a;
   ta.x_bytes = (which == 0 && gather ? (int64_t)T : moe_buffer_rows(d)) * a.ldx * 2;
-  ta.variant = (int)(((uint32_t)d->debug_flags & MOE_DEBUG_TILED_MASK) >> MOE_DEBUG_TILED_SHIFT);
+  ta.variant = tiled_variant(d);
   return tiled_kernel_name(tiled_choice(ta, d->w_packed, which == 0 ? MODE_GATEUP : MODE_DOWN));
 }
 
@@ -662,6 +669,16 @@ int a8_nblk(const moe_desc_t* d, int32_t T, const A8Args& a) {
   return nb;
 }
 
+// The W8A8 kernel for large groups (ffn_a8_tall_kernel) takes a launch when
+// groups are large on average (the bf16 rule of plan_expert_gemm: T > 64 and
+// T*K >= 64 E_phys), the weights are packed and the route table has its
+// claim counters; MOE_DEBUG_A8_STREAM keeps the streaming kernel.
+bool a8_tall_wanted(const moe_desc_t* d, const moe_route_t* r, int32_t T) {
+  const int v = (int)(((uint32_t)d->debug_flags & MOE_DEBUG_TILED_MASK) >> MOE_DEBUG_TILED_SHIFT);
+  return v != MOE_DEBUG_A8_STREAM && d->w_packed && r->claim && r->tile_off && T > 64 &&
+         (int64_t)T * d->K >= (int64_t)64 * d->E_phys;
+}
+
 }  // namespace
 
 extern "C" {
@@ -683,6 +700,10 @@ moe_status_t moe_expert_gate_up_a8(const moe_desc_t* d, const moe_weights_t* w, 
   a.SW = static_cast<const uint8_t*>(w->sw1); a.SW3 = static_cast<const uint8_t*>(w->sw3);
   a.SS = w->ss1; a.SS3 = w->ss3;
   a.out = h; a.ldo = d->I;
+  if (a8_tall_wanted(d, r, T)) {
+    const A8TallArgs ta = {a, r->tile_off, r->claim, T};
+    if (a8_tall_supported(MODE_GATEUP, ta)) return hip_status(launch_ffn_a8_tall(ta, MODE_GATEUP, stream));
+  }
   a.nblk = a8_nblk(d, T, a);
   return hip_status(launch_ffn_a8(a, d->w_packed, MODE_GATEUP, stream));
 }
@@ -703,6 +724,10 @@ moe_status_t moe_expert_down_a8(const moe_desc_t* d, const moe_weights_t* w, con
   a.SW = static_cast<const uint8_t*>(w->sw2); a.SS = w->ss2;
   a.out = y; a.ldo = d->H; a.ksplit = splits; a.out_f32 = splits > 1;
   a.split_stride = moe_buffer_rows(d) * d->H;
+  if (a8_tall_wanted(d, r, T)) {
+    const A8TallArgs ta = {a, r->tile_off, r->claim, moe_buffer_rows(d)};
+    if (a8_tall_supported(MODE_DOWN, ta)) return hip_status(launch_ffn_a8_tall(ta, MODE_DOWN, stream));
+  }
   a.nblk = a8_nblk(d, T, a);
   return hip_status(launch_ffn_a8(a, d->w_packed, MODE_DOWN, stream));
 }
@@ -721,6 +746,27 @@ moe_status_t moe_grouped_ffn_a8(const moe_desc_t* d, const moe_weights_t* w, con
   st = moe_quantize_1x128(h, d->I, moe_buffer_rows(d), d->I, hq, hs, stream);
   if (st != MOE_OK) return st;
   return moe_expert_down_a8(d, w, r, T, hq, hs, y, stream);
+}
+
+const char* moe_expert_kernel_a8(const moe_desc_t* d, int32_t T, int32_t which) {
+  if (moe_check_desc(d) != MOE_OK || T <= 0 || T > d->T_max || (which != 0 && which != 1)) return "none";
+  if (d->w_dtype != MOE_FP8E4M3_B128) return "none";
+  static int32_t tiles = 0;
+  static uint32_t counters = 0;
+  moe_route_t r = {};
+  r.tile_off = &tiles;                         // only their presence is read here
+  r.claim = &counters;
+  if (!a8_tall_wanted(d, &r, T)) return "ffn_a8_kernel";
+  A8Args a = a8_base_args(d, &r, T);
+  if (which == 0) {
+    a.ldx = d->H; a.Kdim = d->H; a.N = d->I;
+  } else {
+    a.ldx = d->I; a.Kdim = d->I; a.N = d->H;
+    a.ksplit = moe_down_splits(d, T);
+    a.out_f32 = a.ksplit > 1;
+  }
+  const A8TallArgs ta = {a, r.tile_off, r.claim, which == 0 ? (int64_t)T : (int64_t)moe_buffer_rows(d)};
+  return a8_tall_supported(which == 0 ? MODE_GATEUP : MODE_DOWN, ta) ? "ffn_a8_tall_kernel" : "ffn_a8_kernel";
 }
 
 moe_status_t moe_combine(const moe_desc_t* d, const moe_route_t* r, int32_t T, const void* y,

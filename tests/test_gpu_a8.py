@@ -9,7 +9,7 @@ import torch
 from oracle import moe_oracle as O
 from routing_grouped_expert_router_amd import binding as B
 from workloads import configs
-from gpu_util import DEV, TOL, Built, out_np, rel_err, say
+from gpu_util import DEV, TOL, Built, covering_tokens, out_np, rel_err, route_np, say
 
 pytestmark = pytest.mark.gpu
 
@@ -116,3 +116,75 @@ def test_a8_block_walk_gives_identical_outputs(nblk):
     finally:
         b.d.debug_flags = 0
     assert torch.equal(ref, out), nblk
+
+
+# groups large on average (T*K >= 64 E_phys): the W8A8 large-group kernel
+# takes both projections; Zipf-skewed experts fill up to T rows, so groups
+# span two 256-row tiles with a ragged second one, and small groups leave
+# most of their one tile empty
+A8_LARGE = [
+    configs.tiny().with_(name="a8_tall_contig_shared", T=512, H=1024, I=512, E=64, E_phys=64, K=8, n_shared=1,
+                         act_dtype="bf16", w_dtype="fp8", layout="contig", BM=16, bias="zipf1.1"),
+    configs.tiny().with_(name="a8_tall_masked_spill", T=520, H=1024, I=512, E=64, E_phys=64, K=8, n_shared=0,
+                         act_dtype="bf16", w_dtype="fp8", layout="masked", M_max=96, bias="zipf1.1"),
+]
+
+
+def _tall_both(b) -> bool:
+    return all(B.expert_kernel_a8(b.d, b.T, w) == "ffn_a8_tall_kernel" for w in (0, 1))
+
+
+@pytest.mark.parametrize("cfg", A8_LARGE, ids=lambda c: c.name)
+def test_a8_large_groups_against_reference(cfg):
+    """The large-group W8A8 kernel on every token against the reference's
+    W8A8 layer; the claim counters are left zero."""
+    b = Built(cfg, packed=True, a8=True)
+    assert _tall_both(b)
+    lg = b.oracle_logits()
+    out = out_np(b.run(lg))
+    assert not b.layer.rt.claim.any()
+    g = route_np(b.layer.rt, b.T, cfg.K)
+    assert g["counts"].max() > 256                       # some groups span two tiles
+    res = b.oracle(lg)
+    e = rel_err(out, res["out"])
+    say(f"  {cfg.name}: groups {g['counts'].min()}..{g['counts'].max()} rows, rel err {e:.3e}")
+    assert e <= TOL["fp8"]
+
+
+@pytest.mark.parametrize("cfg", A8_LARGE, ids=lambda c: c.name)
+def test_a8_large_group_kernel_matches_streaming(cfg):
+    """The large-group and the streaming W8A8 kernels reduce every output
+    over the same 128-wide K blocks, in the same order, with the same
+    products and scalings: bit-identical layer outputs."""
+    b = Built(cfg, packed=True, a8=True)
+    lg = b.oracle_logits()
+    try:
+        b.d.debug_flags = B.MOE_DEBUG_A8_STREAM << B.MOE_DEBUG_TILED_SHIFT
+        assert B.expert_kernel_a8(b.d, b.T, 0) == "ffn_a8_kernel"
+        ref = b.run(lg).clone()
+        b.d.debug_flags = 0
+        out = b.run(lg).clone()
+    finally:
+        b.d.debug_flags = 0
+    assert _tall_both(b)
+    assert torch.equal(ref, out), cfg.name
+
+
+@pytest.mark.timeout(900)
+def test_a8_prefill_full_size_sampled():
+    """The DeepSeek-V3-shaped prefill (T = 8192) with fp8 weights on the W8A8
+    path, in the launch configuration the benchmark times: routing tables
+    bit-exact, and the tokens on the first and last row of every group and on
+    both sides of every 256-row tile boundary compared with the reference."""
+    cfg = configs.dsv3_prefill().with_(name="dsv3_prefill_t8192_fp8", w_dtype="fp8")
+    b = Built(cfg, packed=True, a8=True)
+    assert _tall_both(b)
+    lg = b.oracle_logits()
+    out = out_np(b.run(lg))
+    assert not b.layer.rt.claim.any()
+    g = route_np(b.layer.rt, b.T, cfg.K)
+    toks = covering_tokens(g["counts"], g["offsets"], g["src_of"], b.T, cfg.n_shared, tiles=(256,))
+    res = b.oracle(lg, tokens=toks)
+    e = rel_err(out[toks], res["out"])
+    say(f"  {cfg.name}: {len(toks)} tokens, rel err {e:.3e}")
+    assert e <= TOL["fp8"]

@@ -88,6 +88,12 @@ def dsv3_prefill(T: int = 8192) -> MoEConfig:
                      layout="contig", M_max=0, BM=128, bias="normal0.5")
 
 
+def dsv3_prefill_fp8(T: int = 8192) -> MoEConfig:
+    """The DeepSeek-V3-shaped prefill with fp8 block-128 weights (timed on the
+    W8A8 path: fp8 activations on fp8 MFMA)."""
+    return dsv3_prefill(T).with_(name=f"dsv3_prefill_t{T}_fp8", w_dtype="fp8")
+
+
 def replica_decode(B: int = 256) -> MoEConfig:
     """512 logical experts in 544 physical slots, K=10, bf16, Zipf(1.1) router
     bias, contiguous layout."""
@@ -99,7 +105,7 @@ def replica_decode(B: int = 256) -> MoEConfig:
 def all_configs() -> list[MoEConfig]:
     return ([tiny()] + [mixtral_decode(b) for b in (1, 8, 32, 64)]
             + [dsv3_decode(b) for b in (32, 128, 256)]
-            + [dsv3_prefill(), replica_decode()])
+            + [dsv3_prefill(), dsv3_prefill_fp8(), replica_decode()])
 
 
 def by_name(name: str) -> MoEConfig:
