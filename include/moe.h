@@ -489,7 +489,7 @@ moe_status_t moe_quantize_1x128(const void* src, int64_t ld, int64_t rows, int32
  * of 16 (at most 16 rows) or 64, each pass streaming the group's weights.
  * Groups large on average (T > 64 and T*K >= 64 E_phys, the prefill case),
  * with packed weights, route tables holding claim counters, H a multiple of
- * 512 (at most 16384) and I of 128: one persistent launch over 256-row tiles
+ * 1024 (at most 16384) and I of 128: one persistent launch over 256-row tiles
  * of every group, each weight tile read once per 256 rows (the DeepGEMM
  * section's contiguous layout with large tiles).  Both kernels give the same
  * bits. */
@@ -500,7 +500,7 @@ moe_status_t moe_expert_gate_up_a8(const moe_desc_t* d, const moe_weights_t* w,
 /* a7 with fp8 activations: hq / hs = moe_quantize_1x128 of h over its
  * moe_buffer_rows(d) rows (C = I).  y as moe_expert_down (same K split).
  * The large-group kernel as for gate/up, where the call has no K split, I
- * is a multiple of 512 and H of 128. */
+ * is a multiple of 1024 (at most 16384) and H of 128. */
 moe_status_t moe_expert_down_a8(const moe_desc_t* d, const moe_weights_t* w,
                                 const moe_route_t* r, int32_t T, const void* hq,
                                 const float* hs, void* y, hipStream_t stream);

@@ -42,14 +42,16 @@ constexpr int kAM = kTileRows;              // token rows per work item
 constexpr int kAMT = kAM / 16;              // 16-row MFMA tiles per item
 constexpr int kAN = 128;                    // weight rows per item
 constexpr int kAStages = 4;                 // LDS ring slots of 128-wide K stages
-constexpr int kAXBytes = kAM * 128;         // a stage's activation codes (32 KiB)
-constexpr int kASlot = kAXBytes + kAM * 4;  // + their 256 scales
+constexpr int kAXBytes = kAM * 128;         // a ring slot: a stage's activation codes (32 KiB)
+constexpr int kAScaleBlock = 4;             // K stages whose activation scales load together
 constexpr int kAMaxKb = 128;                // K blocks a weight-scale row in LDS holds
-constexpr int kALoads = 13;                 // loads per wave and stage: 8 codes, 1 scales, 4 weights
+constexpr int kALoads = 12;                 // loads per wave and stage: 8 codes, 4 weights (+1 scales
+                                            // at every kAScaleBlock-th stage)
 constexpr int kAAhead = 2;                  // row tiles whose fragments are read ahead of their products
 constexpr int kPromoteValu = 10;            // VALU instructions of a tile's promotion
 static_assert(kAM == 256 && kAMT == 16, "an item is 16 row tiles");
-static_assert(kALoads <= kAMT, "a stage's loads fit its row-tile steps");
+static_assert(kALoads + 1 <= kAMT, "a stage's loads fit its row-tile steps");
+static_assert(kAScaleBlock == kAStages, "a scale block is one pass of the ring");
 static_assert(kAMaxKb == 128, "two 64-word halves per weight-scale row, one per wave");
 
 __device__ __forceinline__ float a8t_silu(float g) { return g / (1.0f + __expf(-g)); }
@@ -62,7 +64,8 @@ __device__ __forceinline__ i32x8 join8(const u32x4 lo, const u32x4 hi) {
 // at_loop_end() runs once the K loop is done, before the epilogue.
 template <int MODE, typename Hook>
 __device__ __forceinline__ void a8_tall_tile(const A8TallArgs& ta, const TileWork& tw, char* r0, char* r1,
-                                             char* r2, char* r3, float* wsc, Hook at_loop_end) {
+                                             char* r2, char* r3, float* xs0, float* xs1, float* wsc,
+                                             Hook at_loop_end) {
   constexpr bool GU = MODE == MODE_GATEUP;
   const A8Args& a = ta.s;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -99,15 +102,14 @@ __device__ __forceinline__ void a8_tall_tile(const A8TallArgs& ta, const TileWor
   const uint32_t kbytes = (uint32_t)N * 128;   // one K block of the packed layout
 
   // activation rows: the four row tiles of codes this wave loads (wave + 4 q;
-  // lane: row lr, K bytes 16 lg + 64 j), then the row of its scale word
-  // (word p = 64 wave + lane of the slot's scale block is row tile p % 16,
-  // row p / 16 of it, so lane (lr) reads its tiles 4q..4q+3 as one 16
-  // bytes).  Rows past the group read a valid row, never used.  The gather
+  // lane: row lr, K bytes 16 lg + 64 j), then the row whose scales it loads
+  // (row 64 wave + lane: 16 bytes, the scales of kAScaleBlock consecutive K
+  // stages).  Rows past the group read a valid row, never used.  The gather
   // indices load together, under one wait.
   int rk[5];
 #pragma unroll
   for (int q = 0; q < 4; ++q) rk[q] = m0 + (wave + 4 * q) * 16 + lr;
-  rk[4] = m0 + 16 * lr + 4 * wave + lg;
+  rk[4] = m0 + 64 * wave + lane;
   int64_t rw[5];
 #pragma unroll
   for (int i = 0; i < 5; ++i) rk[i] = rk[i] < R ? rk[i] : 0;
@@ -135,23 +137,26 @@ __device__ __forceinline__ void a8_tall_tile(const A8TallArgs& ta, const TileWor
       constexpr int S = decltype(sc)::value;
       return S == 0 ? r0 : S == 1 ? r1 : S == 2 ? r2 : r3;
     };
-    // load i (0..12) of stage st (clamped past the end: re-read, never used):
-    // 0..7 codes of row tile wave + 4 (i / 2), half i % 2, into ring slot S;
-    // 8 the scales; 9..12 weights of panel (i - 9) / 2, half (i - 9) % 2
+    // load i of stage st (clamped past the end: re-read, never used):
+    // 0..7 codes of row tile wave + 4 (i / 2), half i % 2, into ring slot
+    // sl; 8..11 weights of panel (i - 8) / 2, half (i - 8) % 2, into bank b;
+    // 12 (stages st % kAScaleBlock == 0) the activation scales of stages
+    // st .. st + 3 into the scale buffer sb: word 4 r + k is row r, stage
+    // st + k, so lane (lr) finds row tile m's scale at word 4 (16 m + lr) + k
     u32x4 wb[kAStages][2][2];
-    auto issue = [&](int i, char* sl, u32x4 (*b)[2], int st) -> void {
+    auto issue = [&](int i, char* sl, u32x4 (*b)[2], float* sb, int st) -> void {
       const int stc = st < nkb ? st : nkb - 1;
       if (i < 8) {
         const int q = i >> 1, j = i & 1;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xrs, sl + ((wave + 4 * q) * 2 + j) * 1024, 16, xoff[q],
                                                  (uint32_t)stc * 128 + 64 * j, 0, 0);
-      } else if (i == 8) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, sl + kAXBytes + wave * 256, 4, soff, (uint32_t)stc * 4,
-                                                 0, 0);
       } else if (i < kALoads) {
-        const int n = (i - 9) >> 1, j = (i - 9) & 1;
+        const int n = (i - 8) >> 1, j = (i - 8) & 1;
         b[n][j] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(n ? wrb : wra, (int)pw[n], (int)(stc * kbytes + j * 1024), 0));
+      } else {
+        const int blk = stc / kAScaleBlock * kAScaleBlock;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, sb + wave * 256, 16, soff, (uint32_t)blk * 4, 0, 0);
       }
     };
     f32x4 acc[MV][2];
@@ -164,7 +169,7 @@ __device__ __forceinline__ void a8_tall_tile(const A8TallArgs& ta, const TileWor
     // wsc[kAMaxKb + k] of W3 (for the down projection waves 2 and 3 load the
     // W2 row again into the unused half)
 #pragma unroll
-    for (int i = 9; i < kALoads; ++i) issue(i, r0, wb[0], 0);
+    for (int i = 8; i < kALoads; ++i) issue(i, r0, wb[0], xs0, 0);
     {
       const int mat = wave >> 1, c = (wave & 1) * 64;
       const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(GU && mat ? Sb : Sa, (uint32_t)(N / 128) * nkb * 4);
@@ -172,25 +177,29 @@ __device__ __forceinline__ void a8_tall_tile(const A8TallArgs& ta, const TileWor
       __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, wsc + mat * kAMaxKb + c, 4, o, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 9; ++i) issue(i, r0, wb[0], 0);
+    for (int i = 0; i < 8; ++i) issue(i, r0, wb[0], xs0, 0);
+    issue(kALoads, r0, wb[0], xs0, 0);          // the scales of stages 0..3
     __builtin_amdgcn_sched_barrier(0);          // each stage's loads before the next stage's
 #pragma unroll
-    for (int i = 9; i < kALoads; ++i) issue(i, r1, wb[1], 1);
+    for (int i = 8; i < kALoads; ++i) issue(i, r1, wb[1], xs0, 1);
 #pragma unroll
-    for (int i = 0; i < 9; ++i) issue(i, r1, wb[1], 1);
+    for (int i = 0; i < 8; ++i) issue(i, r1, wb[1], xs0, 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 9; i < kALoads; ++i) issue(i, r2, wb[2], 2);
+    for (int i = 8; i < kALoads; ++i) issue(i, r2, wb[2], xs0, 2);
 #pragma unroll
-    for (int i = 0; i < 9; ++i) issue(i, r2, wb[2], 2);
+    for (int i = 0; i < 8; ++i) issue(i, r2, wb[2], xs0, 2);
     __builtin_amdgcn_sched_barrier(0);
-    // at the top of stage st the loads issued after stage st's are those of
-    // st + 1 and st + 2: vmcnt(2 * kALoads) means this wave's loads of stage
-    // st (and, before stage 0, the weight scales) have landed
-    constexpr int kVm = 2 * kALoads;
-    constexpr int kWait = (kVm & 15) | ((kVm >> 4) << 14) | 0x70 | 0xF00;
-    auto stage = [&](auto sc, auto nc, int st) -> void {
+    // Stage st's loads are issued during stage st - 3 (slot S - 1 mod 4),
+    // kALoads of them, one more for stages st % 4 == 0 (issued from slot 1).
+    // At the top of stage st the loads issued after stage st's are those of
+    // st + 1 and st + 2, so vmcnt(their count) means this wave's loads of
+    // stage st (and, before stage 0, the weight scales) have landed.
+    auto stage = [&](auto sc, auto nc, int st, float* rsb, float* lsb) -> void {
       constexpr int S = decltype(sc)::value;
+      constexpr int kVm = 2 * kALoads + ((S + 1) % kAScaleBlock == 0) + ((S + 2) % kAScaleBlock == 0);
+      constexpr int kWait = (kVm & 15) | ((kVm >> 4) << 14) | 0x70 | 0xF00;
+      constexpr bool kScaleLoad = (S + kAStages - 1) % kAScaleBlock == 0;   // stage st + 3 starts a block
       u32x4 (*wc)[2] = wb[S];
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(kWait);       // this wave's loads of stage st landed
@@ -199,11 +208,9 @@ __device__ __forceinline__ void a8_tall_tile(const A8TallArgs& ta, const TileWor
       const char* xs = slot(sc);
       const i32x8 w0 = join8(wc[0][0], wc[0][1]), w1 = join8(wc[1][0], wc[1][1]);
       const float sw0 = wsc[st], sw1 = GU ? wsc[kAMaxKb + st] : sw0;
-      // activation scale of row tile m (this lane's token), read just before
-      // its promotion
-      auto xscale = [&](int m) -> float {
-        return *reinterpret_cast<const float*>(xs + kAXBytes + (lr * 16 + m) * 4);
-      };
+      // activation scale of row tile m (this lane's token) at stage st,
+      // read just before its promotion
+      auto xscale = [&](int m) -> float { return rsb[4 * (16 * m + lr) + S]; };
       auto frag = [&](int m) -> i32x8 {
         return join8(*reinterpret_cast<const u32x4*>(xs + (m * 2) * 1024 + lane * 16),
                      *reinterpret_cast<const u32x4*>(xs + (m * 2 + 1) * 1024 + lane * 16));
@@ -228,7 +235,8 @@ __device__ __forceinline__ void a8_tall_tile(const A8TallArgs& ta, const TileWor
           dp0 = d0;
           dp1 = d1;
         }
-        if (m < kALoads) issue(m, slot(nc), wb[decltype(nc)::value], st + kAStages - 1);
+        if (m < kALoads || (kScaleLoad && m == kALoads))
+          issue(m, slot(nc), wb[decltype(nc)::value], lsb, st + kAStages - 1);
       }
       const float sxl = xscale(MV - 1);
       acc[MV - 1][0] += dp0 * (sw0 * sxl);
@@ -249,15 +257,23 @@ __device__ __forceinline__ void a8_tall_tile(const A8TallArgs& ta, const TileWor
         __builtin_amdgcn_sched_group_barrier(0x002, kPromoteValu / 2, 0);  // VALU
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, kPromoteValu / 2, 0);
-        if (m < kALoads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
+        if (m < kALoads || (kScaleLoad && m == kALoads))
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // VMEM read
       }
       __builtin_amdgcn_sched_barrier(0);
     };
-    for (int sb = 0; sb < nkb; sb += kAStages) {
-      stage(IntC<0>{}, IntC<3>{}, sb);
-      stage(IntC<1>{}, IntC<0>{}, sb + 1);
-      stage(IntC<2>{}, IntC<1>{}, sb + 2);
-      stage(IntC<3>{}, IntC<2>{}, sb + 3);
+    // two scale blocks per pass, so that each stage's scale buffers are
+    // fixed: stages sb .. sb + 3 read xs0 while slot 1 loads the next
+    // block into xs1, and the other way round
+    for (int sb = 0; sb < nkb; sb += 2 * kAStages) {
+      stage(IntC<0>{}, IntC<3>{}, sb, xs0, xs1);
+      stage(IntC<1>{}, IntC<0>{}, sb + 1, xs0, xs1);
+      stage(IntC<2>{}, IntC<1>{}, sb + 2, xs0, xs1);
+      stage(IntC<3>{}, IntC<2>{}, sb + 3, xs0, xs1);
+      stage(IntC<0>{}, IntC<3>{}, sb + 4, xs1, xs0);
+      stage(IntC<1>{}, IntC<0>{}, sb + 5, xs1, xs0);
+      stage(IntC<2>{}, IntC<1>{}, sb + 6, xs1, xs0);
+      stage(IntC<3>{}, IntC<2>{}, sb + 7, xs1, xs0);
     }
     // no load may land in LDS after the workgroup has ended, nor in the
     // ring once the epilogue reuses it
@@ -320,24 +336,26 @@ __device__ __forceinline__ void a8_tall_tile(const A8TallArgs& ta, const TileWor
 template <int MODE>
 __global__ __launch_bounds__(kAThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void ffn_a8_tall_kernel(A8TallArgs ta) {
-  __shared__ __attribute__((aligned(16))) char r0[kASlot];
-  __shared__ __attribute__((aligned(16))) char r1[kASlot];
-  __shared__ __attribute__((aligned(16))) char r2[kASlot];
-  __shared__ __attribute__((aligned(16))) char r3[kASlot];
+  __shared__ __attribute__((aligned(16))) char r0[kAXBytes];
+  __shared__ __attribute__((aligned(16))) char r1[kAXBytes];
+  __shared__ __attribute__((aligned(16))) char r2[kAXBytes];
+  __shared__ __attribute__((aligned(16))) char r3[kAXBytes];
+  __shared__ __attribute__((aligned(16))) float xs0[kAM * kAScaleBlock];   // activation scales of
+  __shared__ __attribute__((aligned(16))) float xs1[kAM * kAScaleBlock];   // alternate stage blocks
   __shared__ __attribute__((aligned(16))) float wsc[2 * kAMaxKb];
   const int ntn = ta.s.N / (MODE == MODE_GATEUP ? kAN / 2 : kAN);   // weight tiles per row tile
   claim_units<kAThreads>(ta.s, ta.tile_off, ta.claim, ntn, [&](const TileWork& tw, auto at_loop_end) {
-    a8_tall_tile<MODE>(ta, tw, r0, r1, r2, r3, wsc, at_loop_end);
+    a8_tall_tile<MODE>(ta, tw, r0, r1, r2, r3, xs0, xs1, wsc, at_loop_end);
   });
 }
 
 // Whole 128-row output tiles (64 for gate/up), a K range of whole blocks of
-// four 128-wide stages that the scale rows in LDS hold, no K split, the
+// eight 128-wide stages that the scale rows in LDS hold, no K split, the
 // route table's claim counters, and 32-bit buffer offsets.
 bool a8_tall_supported(int mode, const A8TallArgs& a) {
   const A8Args& s = a.s;
   const int wn = mode == MODE_GATEUP ? kAN / 2 : kAN;
-  if (s.N <= 0 || s.N % wn || s.N % 128 || s.Kdim <= 0 || s.Kdim % (128 * kAStages) || s.Kdim / 128 > kAMaxKb)
+  if (s.N <= 0 || s.N % wn || s.N % 128 || s.Kdim <= 0 || s.Kdim % (128 * 2 * kAStages) || s.Kdim / 128 > kAMaxKb)
     return false;
   if (s.ksplit != 1 || s.out_f32 || s.ldx < s.Kdim || s.ldx % 16) return false;
   if (!a.claim || !a.tile_off || s.E_phys > kPlanGroups || a.x_rows <= 0) return false;

@@ -123,9 +123,9 @@ def test_a8_block_walk_gives_identical_outputs(nblk):
 # span two 256-row tiles with a ragged second one, and small groups leave
 # most of their one tile empty
 A8_LARGE = [
-    configs.tiny().with_(name="a8_tall_contig_shared", T=512, H=1024, I=512, E=64, E_phys=64, K=8, n_shared=1,
+    configs.tiny().with_(name="a8_tall_contig_shared", T=512, H=1024, I=1024, E=64, E_phys=64, K=8, n_shared=1,
                          act_dtype="bf16", w_dtype="fp8", layout="contig", BM=16, bias="zipf1.1"),
-    configs.tiny().with_(name="a8_tall_masked_spill", T=520, H=1024, I=512, E=64, E_phys=64, K=8, n_shared=0,
+    configs.tiny().with_(name="a8_tall_masked_spill", T=520, H=1024, I=1024, E=64, E_phys=64, K=8, n_shared=0,
                          act_dtype="bf16", w_dtype="fp8", layout="masked", M_max=96, bias="zipf1.1"),
 ]
 
