@@ -463,9 +463,11 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, cmd_prefix:
         "three times first as the calibration kernel of known traffic (repository root on the GPU "
         "box, `R=$PWD`):",
         "",
-        f"    {cmd_prefix} --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/{workload}_FETCH_SIZE -o run -- "
+        f"    {cmd_prefix} --kernel-include-regex '{kernel}|copyBuffer' --pmc FETCH_SIZE --output-format csv "
+        f"-d $R/gpurun_out/prof/{workload}_FETCH_SIZE -o run -- "
         f"python3 $R/bench.py --workload {workload} --no-cpu --no-peaks --steps 3 --warmup 1 --copy-calibration",
-        f"    {cmd_prefix} --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/{workload}_WRITE_SIZE -o run -- "
+        f"    {cmd_prefix} --kernel-include-regex '{kernel}|copyBuffer' --pmc WRITE_SIZE --output-format csv "
+        f"-d $R/gpurun_out/prof/{workload}_WRITE_SIZE -o run -- "
         f"python3 $R/bench.py --workload {workload} --no-cpu --no-peaks --steps 3 --warmup 1 --copy-calibration",
         f"    python3 bench.py --workload {workload} --summarize-traffic "
         f"gpurun_out/prof/{workload}_FETCH_SIZE/run_counter_collection.csv "
@@ -508,7 +510,8 @@ def summarize_stats(workload: str, stats_csv: str, log: str, steps: int, warmup:
         f"T={cfg.T}, H={cfg.H}, I={cfg.I}, E={cfg.E}, E_phys={cfg.E_phys}, K={cfg.K}, n_shared={cfg.n_shared}, "
         f"weights {cfg.w_dtype}, layout {cfg.layout}.  Command (repository root on the GPU box, `R=$PWD`):",
         "",
-        f"    cd /tmp && TMPDIR=/tmp timeout -k 10 300 rocprofv3 --kernel-trace --stats --output-format csv "
+        f"    cd /tmp && TMPDIR=/tmp timeout -k 10 300 rocprofv3 --kernel-include-regex 'moe' --kernel-trace --stats "
+        f"--output-format csv "
         f"-d $R/gpurun_out/prof/{workload} -o run -- python3 $R/bench.py --workload {workload} --no-cpu --no-peaks "
         f"--steps {steps} --warmup {warmup} 2> $R/gpurun_out/prof/{workload}.log",
         f"    python3 bench.py --workload {workload} --summarize-stats "
