@@ -739,7 +739,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if cfg.w_dtype == "bf16" else (
-            "fp8-e4m3-b128 weights, fp8-e4m3 1x128 activations (W8A8)" if args.a8
+            "fp8-e4m3-b128 weights, fp8-e4m3 1x128 activations (W8A8)" if args.a8 or head_name in A8_WORKLOADS
             else "fp8-e4m3-b128 weights, bf16 activations"),
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E,
