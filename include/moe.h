@@ -117,7 +117,9 @@ typedef struct {
 } moe_desc_t;
 
 /* moe_desc_t.debug_flags.  Bits 0-3: 64-row output blocks per streaming or
- * W8A8 workgroup (1..8 and dividing N/64; 0 = the library's choice).
+ * W8A8 streaming workgroup (1..8 and dividing N/64), and weight tiles per work
+ * item of the W8A8 large-group kernel (1..8 and dividing their number); 0 =
+ * the library's choice.
  * Bits 4-7: the kernel for large groups (MOE_DEBUG_TILED_* for bf16
  * activations, MOE_DEBUG_A8_STREAM for W8A8; 0 = the library's choice).
  * Bit 8: moe_decode_fused bounds every grid-barrier wait at zero polls, so a

@@ -168,6 +168,7 @@ struct A8TallArgs {
   const int32_t* tile_off;   // [E_phys + 2] prefix of ceil(rows / kTileRows) per group
   uint32_t* claim;           // [MOE_CLAIM_WORDS] work-claim counters, zero on entry and on exit
   int64_t x_rows;            // rows of X and XS the launch may address
+  int walk;                  // weight tiles one work item runs as one pipeline (1..8, dividing their count)
 };
 bool a8_tall_supported(int mode, const A8TallArgs& a);
 // compute units of the current device (0 if the query fails)

@@ -679,6 +679,22 @@ bool a8_tall_wanted(const moe_desc_t* d, const moe_route_t* r, int32_t T) {
          (int64_t)T * d->K >= (int64_t)64 * d->E_phys;
 }
 
+// Weight tiles a W8A8 large-group work item walks as one pipeline: doubled
+// while the item runs fewer than 48 K stages (each item pays its set-up and
+// the pipeline's fill once), at most 8, dividing the tile count.  Measured on
+// the DeepSeek-V3-shaped fp8 prefill (one box): down (16 stages a tile)
+// 2396 us unwalked, 2282 walking 2, 2219-2272 walking 4; gate/up (56 stages)
+// 3766 us unwalked, 3801-3918 walking 2 or 4.  MOE_DEBUG_NBLK_MASK overrides
+// it (an override that does not divide the tile count leaves the call on the
+// streaming kernel).
+int a8_walk(const moe_desc_t* d, int mode, int N, int Kdim) {
+  const int tiles = N / (mode == MODE_GATEUP ? 64 : 128);
+  if (const int v = (int)((uint32_t)d->debug_flags & MOE_DEBUG_NBLK_MASK)) return v;
+  int w = 1;
+  while (w < 8 && tiles % (2 * w) == 0 && w * (Kdim / 128) < 48) w *= 2;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -701,7 +717,7 @@ moe_status_t moe_expert_gate_up_a8(const moe_desc_t* d, const moe_weights_t* w, 
   a.SS = w->ss1; a.SS3 = w->ss3;
   a.out = h; a.ldo = d->I;
   if (a8_tall_wanted(d, r, T)) {
-    const A8TallArgs ta = {a, r->tile_off, r->claim, T};
+    const A8TallArgs ta = {a, r->tile_off, r->claim, T, a8_walk(d, MODE_GATEUP, a.N, a.Kdim)};
     if (a8_tall_supported(MODE_GATEUP, ta)) return hip_status(launch_ffn_a8_tall(ta, MODE_GATEUP, stream));
   }
   a.nblk = a8_nblk(d, T, a);
@@ -725,7 +741,7 @@ moe_status_t moe_expert_down_a8(const moe_desc_t* d, const moe_weights_t* w, con
   a.out = y; a.ldo = d->H; a.ksplit = splits; a.out_f32 = splits > 1;
   a.split_stride = moe_buffer_rows(d) * d->H;
   if (a8_tall_wanted(d, r, T)) {
-    const A8TallArgs ta = {a, r->tile_off, r->claim, moe_buffer_rows(d)};
+    const A8TallArgs ta = {a, r->tile_off, r->claim, moe_buffer_rows(d), a8_walk(d, MODE_DOWN, a.N, a.Kdim)};
     if (a8_tall_supported(MODE_DOWN, ta)) return hip_status(launch_ffn_a8_tall(ta, MODE_DOWN, stream));
   }
   a.nblk = a8_nblk(d, T, a);
@@ -765,8 +781,10 @@ const char* moe_expert_kernel_a8(const moe_desc_t* d, int32_t T, int32_t which) 
     a.ksplit = moe_down_splits(d, T);
     a.out_f32 = a.ksplit > 1;
   }
-  const A8TallArgs ta = {a, r.tile_off, r.claim, which == 0 ? (int64_t)T : (int64_t)moe_buffer_rows(d)};
-  return a8_tall_supported(which == 0 ? MODE_GATEUP : MODE_DOWN, ta) ? "ffn_a8_tall_kernel" : "ffn_a8_kernel";
+  const int mode = which == 0 ? MODE_GATEUP : MODE_DOWN;
+  const A8TallArgs ta = {a, r.tile_off, r.claim, which == 0 ? (int64_t)T : (int64_t)moe_buffer_rows(d),
+                         a8_walk(d, mode, a.N, a.Kdim)};
+  return a8_tall_supported(mode, ta) ? "ffn_a8_tall_kernel" : "ffn_a8_kernel";
 }
 
 moe_status_t moe_combine(const moe_desc_t* d, const moe_route_t* r, int32_t T, const void* y,

@@ -188,3 +188,23 @@ def test_a8_prefill_full_size_sampled():
     e = rel_err(out[toks], res["out"])
     say(f"  {cfg.name}: {len(toks)} tokens, rel err {e:.3e}")
     assert e <= TOL["fp8"]
+
+
+@pytest.mark.parametrize("walk", [1, 2])
+def test_a8_large_group_walks_give_identical_outputs(walk):
+    """A large-group W8A8 work item walks several weight tiles as one
+    pipeline (8 at these shapes by default); forcing 1 or 2 per item
+    (MOE_DEBUG_NBLK_MASK) reduces every output over the same K blocks in
+    the same order: bit-identical layer outputs, claim counters left zero."""
+    cfg = A8_LARGE[0]
+    b = Built(cfg, packed=True, a8=True)
+    lg = b.oracle_logits()
+    ref = b.run(lg).clone()
+    try:
+        b.d.debug_flags = walk
+        assert _tall_both(b)
+        out = b.run(lg).clone()
+    finally:
+        b.d.debug_flags = 0
+    assert not b.layer.rt.claim.any()
+    assert torch.equal(ref, out), walk
