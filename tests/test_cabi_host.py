@@ -54,6 +54,7 @@ def test_desc_validation(kw, code):
 @pytest.mark.parametrize("flags,code", [
     (0, B.MOE_OK), (8, B.MOE_OK), (9, B.MOE_ERR_ARG),
     (B.MOE_DEBUG_TILED_WIDE_HYB << B.MOE_DEBUG_TILED_SHIFT, B.MOE_OK),
+    (B.MOE_DEBUG_A8_STREAM << B.MOE_DEBUG_TILED_SHIFT, B.MOE_OK),
     (15 << B.MOE_DEBUG_TILED_SHIFT, B.MOE_ERR_ARG), (B.MOE_DEBUG_FUSED_NO_WAIT, B.MOE_OK),
     (0x200, B.MOE_ERR_ARG), (-1, B.MOE_ERR_ARG),
 ])
@@ -244,6 +245,36 @@ def test_expert_kernel_names_follow_the_size_classes():
     pre.debug_flags = B.MOE_DEBUG_TILED_NARROW << B.MOE_DEBUG_TILED_SHIFT
     assert B.expert_kernel(pre, 8192, 0) == "ffn_tiled_kernel"
     assert B.expert_kernel(pre, 0, 0) == "none" and B.expert_kernel(pre, 8192, 2) == "none"
+
+
+def test_a8_kernel_names_follow_the_size_classes():
+    """The W8A8 calls: the large-group kernel for the fp8 prefill batch
+    (groups large on average, packed weights), the streaming kernel for
+    decode batches, row-major weights, K ranges that are not whole
+    1024-element blocks, walk overrides that do not divide the tile count,
+    and when forced by MOE_DEBUG_A8_STREAM; "none" for bf16 weights.  The
+    bf16 calls ignore the W8A8 switch."""
+    pre = B.Desc.from_config(configs.dsv3_prefill_fp8(), w_packed=1)
+    assert [B.expert_kernel_a8(pre, 8192, w) for w in (0, 1)] == ["ffn_a8_tall_kernel"] * 2
+    assert B.expert_kernel_a8(pre, 64, 0) == "ffn_a8_kernel"           # T*K < 64 E_phys
+    dec = B.Desc.from_config(configs.dsv3_decode(256), w_packed=1)
+    assert B.expert_kernel_a8(dec, 256, 0) == "ffn_a8_kernel"
+    rowmajor = B.Desc.from_config(configs.dsv3_prefill_fp8(), w_packed=0)
+    assert B.expert_kernel_a8(rowmajor, 8192, 0) == "ffn_a8_kernel"
+    odd_k = B.Desc.from_config(configs.dsv3_prefill_fp8().with_(H=7168 - 512), w_packed=1)
+    assert B.expert_kernel_a8(odd_k, 8192, 0) == "ffn_a8_kernel"      # gate/up K = H not whole 1024s
+    assert B.expert_kernel_a8(odd_k, 8192, 1) == "ffn_a8_tall_kernel"
+    pre.debug_flags = 3                                                # walk 3 divides neither tile count
+    assert B.expert_kernel_a8(pre, 8192, 0) == "ffn_a8_kernel"
+    pre.debug_flags = 4
+    assert B.expert_kernel_a8(pre, 8192, 0) == "ffn_a8_tall_kernel"
+    pre.debug_flags = B.MOE_DEBUG_A8_STREAM << B.MOE_DEBUG_TILED_SHIFT
+    assert B.expert_kernel_a8(pre, 8192, 0) == "ffn_a8_kernel"
+    bf = B.Desc.from_config(configs.dsv3_prefill(), w_packed=1)
+    assert B.expert_kernel_a8(bf, 8192, 0) == "none"
+    tall = B.expert_kernel(bf, 8192, 0)
+    bf.debug_flags = B.MOE_DEBUG_A8_STREAM << B.MOE_DEBUG_TILED_SHIFT
+    assert B.expert_kernel(bf, 8192, 0) == tall
 
 
 def test_probes_reject_bad_arguments():
