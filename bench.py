@@ -66,6 +66,9 @@ def parse():
                     help="first run a plain 512 MiB device copy three times (a kernel of known "
                          "traffic for scaling hardware byte counters)")
     ap.add_argument("--no-peaks", action="store_true", help="skip the achievable-peak probes")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="no effect (a named --workload is the only one timed); accepted so that the commands "
+                         "recorded in older profiles still run")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no timing: turn the counter_collection.csv files of a FETCH_SIZE and a "
                          "WRITE_SIZE rocprofv3 pass over `bench.py --workload W --copy-calibration` "
@@ -464,14 +467,14 @@ def summarize_traffic(workload: str, fetch_csv: str, write_csv: str, cmd_prefix:
         "box, `R=$PWD`):",
         "",
         f"    {cmd_prefix} --kernel-include-regex '{kernel}|copyBuffer' --pmc FETCH_SIZE --output-format csv "
-        f"-d $R/gpurun_out/prof/{workload}_FETCH_SIZE -o run -- "
+        f"-d $OUT/{workload}_FETCH_SIZE -o run -- "
         f"python3 $R/bench.py --workload {workload} --no-cpu --no-peaks --steps 3 --warmup 1 --copy-calibration",
         f"    {cmd_prefix} --kernel-include-regex '{kernel}|copyBuffer' --pmc WRITE_SIZE --output-format csv "
-        f"-d $R/gpurun_out/prof/{workload}_WRITE_SIZE -o run -- "
+        f"-d $OUT/{workload}_WRITE_SIZE -o run -- "
         f"python3 $R/bench.py --workload {workload} --no-cpu --no-peaks --steps 3 --warmup 1 --copy-calibration",
         f"    python3 bench.py --workload {workload} --summarize-traffic "
-        f"gpurun_out/prof/{workload}_FETCH_SIZE/run_counter_collection.csv "
-        f"gpurun_out/prof/{workload}_WRITE_SIZE/run_counter_collection.csv",
+        f"$OUT/{workload}_FETCH_SIZE/run_counter_collection.csv "
+        f"$OUT/{workload}_WRITE_SIZE/run_counter_collection.csv",
         "",
         f"* calibration copy (512 MiB each way): FETCH_SIZE {rd['cal']:.0f} KiB -> factor {rd['factor']:.4f}; "
         f"WRITE_SIZE {wr['cal']:.0f} KiB -> factor {wr['factor']:.4f}",
@@ -508,14 +511,14 @@ def summarize_stats(workload: str, stats_csv: str, log: str, steps: int, warmup:
         f"# rocprofv3 kernel statistics: workload {workload}",
         "",
         f"T={cfg.T}, H={cfg.H}, I={cfg.I}, E={cfg.E}, E_phys={cfg.E_phys}, K={cfg.K}, n_shared={cfg.n_shared}, "
-        f"weights {cfg.w_dtype}, layout {cfg.layout}.  Command (repository root on the GPU box, `R=$PWD`):",
+        f"weights {cfg.w_dtype}, layout {cfg.layout}.  Command (`R` the repository root, `OUT` an output folder):",
         "",
         f"    cd /tmp && TMPDIR=/tmp timeout -k 10 300 rocprofv3 --kernel-include-regex 'moe' --kernel-trace --stats "
         f"--output-format csv "
-        f"-d $R/gpurun_out/prof/{workload} -o run -- python3 $R/bench.py --workload {workload} --no-cpu --no-peaks "
-        f"--steps {steps} --warmup {warmup} 2> $R/gpurun_out/prof/{workload}.log",
+        f"-d $OUT/{workload} -o run -- python3 $R/bench.py --workload {workload} --no-cpu --no-peaks "
+        f"--steps {steps} --warmup {warmup} 2> $OUT/{workload}.log",
         f"    python3 bench.py --workload {workload} --summarize-stats "
-        f"gpurun_out/prof/{workload}/run_kernel_stats.csv gpurun_out/prof/{workload}.log",
+        f"$OUT/{workload}/run_kernel_stats.csv $OUT/{workload}.log",
         "",
         "The library's kernels (the one-time weight packing left out); durations in microseconds, over the "
         "eager and graph-replayed steps of the run.",
