@@ -22,16 +22,20 @@
 //    and added to an fp32 accumulator, K blocks in ascending order: the
 //    streaming W8A8 kernel's arithmetic, operand for operand, so both give
 //    the same bits.
-//  * Activation codes (32 KiB a stage, 16-byte pieces in MFMA lane order) and
-//    their scales (1 KiB) go by direct-to-LDS loads into a ring of four
-//    stages, three ahead; every wave reads all 16 row tiles' fragments from
-//    it, each feeding its two panels' products.
+//  * Activation codes (32 KiB a stage, 16-byte pieces in MFMA lane order) go
+//    by direct-to-LDS loads into a ring of four stages, three ahead; every
+//    wave reads all 16 row tiles' fragments from it, each feeding its two
+//    panels' products.  Each row's activation scales for four stages load
+//    as one 16-byte piece into one of two alternating LDS buffers.
 //  * Weights go straight to registers (each fragment is read by one wave),
-//    four banks, three stages ahead.  The item's weight-block scales (a row
-//    of K blocks per matrix) go to LDS by direct loads at its start.
-//  * A stage's 13 loads per wave are issued one after each row tile's
-//    products, so they never queue in a burst behind the MFMAs, and each
-//    tile's promotion runs under the next tile's products.
+//    four banks, three stages ahead.  The weight-block scales of the walk's
+//    tiles (a row of K blocks per matrix and tile) go to LDS by direct loads
+//    at the item's start.
+//  * A stage's 12 loads per wave (13 when it also loads a scale block) are
+//    issued one after each row tile's products, so they never queue in a
+//    burst behind the MFMAs, and each tile's promotion runs under the next
+//    tile's products; the products' results stay in ordinary VGPRs, where
+//    the promotion's VALU instructions read them.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile_sched.hpp"
@@ -44,7 +48,7 @@ typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 constexpr int kAThreads = 256;
 constexpr int kAM = kTileRows;              // token rows per work item
 constexpr int kAMT = kAM / 16;              // 16-row MFMA tiles per item
-constexpr int kAN = 128;                    // weight rows per item
+constexpr int kAN = 128;                    // weight rows per weight tile
 constexpr int kAStages = 4;                 // LDS ring slots of 128-wide K stages
 constexpr int kAXBytes = kAM * 128;         // a ring slot: a stage's activation codes (32 KiB)
 constexpr int kAScaleBlock = 4;             // K stages whose activation scales load together
