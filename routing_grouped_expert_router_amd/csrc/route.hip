@@ -24,7 +24,9 @@
 //   For T <= 64 (one block) rank, scan and assign run in one workgroup that
 //     keeps their tables in LDS (by its first wave alone when experts and
 //     slots are at most 64), after the selection in the same workgroup, or,
-//     past the tokens it selects in one pass, in a launch of its own.
+//     past the tokens it selects in one pass, in a launch of its own.  Up to
+//     four blocks: the three phases one after the other in one workgroup,
+//     after the selection launch.
 #include <type_traits>
 
 #include "route_dev.hpp"
@@ -51,6 +53,43 @@ __global__ __launch_bounds__(kScanThreads) void route_scan_kernel(RouteArgs a) {
 __global__ __launch_bounds__(kRouteThreads) void route_assign_kernel(RouteArgs a) {
   const int64_t i = (int64_t)blockIdx.x * kRouteThreads + threadIdx.x;
   if (i < (int64_t)a.T * a.K) assign_one(a, i);
+}
+
+// A few token blocks (at most kTableBlocks) in one workgroup, one launch
+// instead of three: every block ranked at once (the tables rank_block makes,
+// with one set of expert masks per block in LDS), then scan_all and
+// assign_one, the phases handing each other their tables through global
+// memory across full barriers.
+constexpr int kTableBlocks = 4;
+
+__global__ __launch_bounds__(kScanThreads) void route_blocks_kernel(RouteArgs a) {
+  __shared__ unsigned long long mask[kTableBlocks][1024];   // E <= 1024 on the routing paths
+  __shared__ int flag_s[kTableBlocks];
+  const int E = a.E, K = a.K, T = a.T;
+  const int tid = threadIdx.x;
+  const int nblk = (T + kBlockTokens - 1) / kBlockTokens;
+  const int TK = T * K;
+  for (int i = tid; i < nblk * E; i += kScanThreads) mask[i / E][i - (i / E) * E] = 0ull;
+  if (tid < kTableBlocks) flag_s[tid] = 0;
+  lds_barrier();
+  for (int i = tid; i < TK; i += kScanThreads) {
+    const int t = i / K;
+    atomicOr(&mask[t / kBlockTokens][a.topk_ids[i]], 1ull << (t % kBlockTokens));
+  }
+  for (int t = tid; t < T; t += kScanThreads)
+    if (a.ws.tok_flag[t]) atomicOr(&flag_s[t / kBlockTokens], 1);
+  lds_barrier();
+  for (int i = tid; i < TK; i += kScanThreads) {
+    const int t = i / K, tl = t % kBlockTokens;
+    const unsigned long long below = tl ? (mask[t / kBlockTokens][a.topk_ids[i]] & ((1ull << tl) - 1ull)) : 0ull;
+    a.ws.local_rank[i] = __popcll(below);
+  }
+  for (int i = tid; i < nblk * E; i += kScanThreads) a.ws.blk[i] = __popcll(mask[i / E][i - (i / E) * E]);
+  if (tid < nblk) a.ws.blk_flags[tid] = flag_s[tid];
+  __syncthreads();                           // the block tables are read by every thread below
+  scan_all(a);
+  __syncthreads();                           // and so are the scan's
+  for (int i = tid; i < TK; i += kScanThreads) assign_one(a, i);
 }
 
 // T <= 64: the four phases in one workgroup (one launch instead of four).
@@ -186,6 +225,10 @@ static void launch_shape(const RouteArgs& a, int nblk, hipStream_t s) {
   }
   if (one_block) {
     hipLaunchKernelGGL(route_tables_kernel, dim3(1), dim3(kFusedThreads), 0, s, a);
+    return;
+  }
+  if (nblk <= kTableBlocks) {
+    hipLaunchKernelGGL(route_blocks_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
     return;
   }
   hipLaunchKernelGGL(route_rank_kernel, dim3(nblk > 0 ? nblk : 1), dim3(kRouteThreads), 0, s, a);
